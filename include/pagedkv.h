@@ -1,0 +1,301 @@
+/*
+ * pagedkv.h — C ABI of libpagedkv.so: paged KV cache + PagedAttention decode
+ * for AMD Instinct MI355X (gfx950 / CDNA4).
+ *
+ * Sources (the web pages this library is built from):
+ *   [P1] "LLM inference basics and vLLM internals: KV cache, PagedAttention,
+ *        scheduler" (ttlab.hopto.org), §1 arithmetic intensity, §2 KV cache
+ *        and the size formula, §4 PagedAttention and block management.
+ *   [P2] "vLLM internals (2): why PagedAttention pages the KV cache"
+ *        (youngju.dev), sections "Block table: logically contiguous,
+ *        physically scattered", "Block size tradeoff", "Sharing".
+ *   [P4] "vToken: token-level virtualization of the KV cache"
+ *        (gotosocial.chinng-lab-srv.dev), "KV cache basics" and
+ *        "PagedAttention: block management learned from OS virtual memory".
+ *
+ * What is computed (the operation this ABI exposes):
+ *   The KV cache holds, per layer, the key and value vector of every past
+ *   token; a decode step adds only the new token's K/V and attends over all
+ *   of them ([P1] §2, [P4] "KV cache basics").  The cache is cut into
+ *   fixed-size blocks (16 tokens by default); each request owns a block table
+ *   mapping its logical block j to a physical block id, so a request's blocks
+ *   may sit anywhere in the pool and several requests may point at the same
+ *   physical block ([P1] §4 and its diagram, [P2] "Block table", "Sharing").
+ *   Query heads are grouped: all G = num_heads / num_kv_heads query heads of
+ *   a group read the same K/V head ([P1] §2, MQA/GQA paragraph).
+ *
+ *   For sequence s with context length c (which already counts the token
+ *   being decoded), query head h, kv head g = h / G:
+ *     K_t = dequant(k_cache tile(block_tables[s][t / bs], g), row t % bs)
+ *     out[s,h,:] = sum_t softmax_t(scale * q[s,h,:] . K_t) * V_t,  t < c
+ *   (V_t likewise).  Block size and block-table semantics follow [P1] §4;
+ *   the per-token byte count 2*L*H_kv*d*b follows [P1] §2's formula.
+ *
+ * Conventions shared by every entry point
+ *   - All pointers are device pointers unless stated; all buffers are owned
+ *     by the caller.  The library keeps no pointer beyond a call except inside
+ *     a pkv_pool handle (which only records them).
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = default
+ *     stream) and never synchronise the host, except pkv_check_block_tables.
+ *   - Return 0 on success, a negative PKV_ERR_* code otherwise; the message
+ *     is then available from pkv_last_error() (thread-local).  Nothing is
+ *     launched when an argument check fails.  No C++ exception crosses the ABI.
+ *   - Per-step data (block tables, context lengths, slot mappings) is device
+ *     data; the launch shape depends only on host scalars, so a decode step
+ *     can be captured into a HIP graph.
+ *
+ * ----------------------------------------------------------------------------
+ * KV pool layout (frozen; the oracle reads the pool through this formula)
+ * ----------------------------------------------------------------------------
+ * One layer has one K pool and one V pool, each an array of
+ *     [num_blocks][num_kv_heads] tiles,  tile = block_size tokens x head_dim.
+ * Tile (pb, g) starts at byte  ((int64)pb * num_kv_heads + g) * tile_bytes,
+ *     tile_bytes = block_size * head_dim * E,   E = element bytes (2 or 1).
+ * A tile is block_size/16 sub-tiles of 16 tokens; token t of the block lives
+ * in sub-tile u = t / 16 (byte u * 16 * head_dim * E), as row r = t % 16.
+ * A sub-tile is a sequence of 1 KiB "rows": 64 lanes x 16 bytes, so one
+ * wave-wide 16-byte-per-lane load reads one row, fully contiguous.
+ *
+ *   K element (r, k), 0<=r<16, 0<=k<head_dim:
+ *       c = k / 8,  lane = r + 16 * (c % 4),  kk = c / 4,  e = k % 8,
+ *       n = 2 / E   (8-element groups per 16-byte lane slot),
+ *       byte = 1024*(kk / n) + 16*lane + 8*E*(kk % n) + E*e
+ *   V element (r, k):
+ *       nt = k / 16,  lane = (k % 16) + 16 * (r / 4),  i = r % 4,
+ *       n = 4 / E   (4-element groups per 16-byte lane slot),
+ *       byte = 1024*(nt / n) + 16*lane + 4*E*(nt % n) + E*i
+ *
+ * Why: in K, lane L of a row holds 8 consecutive dims of token L%16 — exactly
+ * the A operand of a 16x16x32 matrix-core product S^T = K.Q^T.  In V, lane L
+ * holds 4 consecutive tokens of dim L%16 — the A operand of a 16x16x16
+ * product O^T = V^T.P^T, whose B operand (P) is in the same lane order as the
+ * S^T result.  head_dim must be a multiple of 64 (128 for every shipped
+ * kernel), block_size 16 or 32.  Element encodings: bf16 / fp16 bit patterns
+ * unchanged; fp8 = OCP OFP8 E4M3 ("e4m3fn": bias 7, max 448, no infinities,
+ * S.1111.111 = NaN) holding round-to-nearest-even(x / scale) saturated to
+ * +-448, and dequantised as code * scale.
+ * Block 0 is the null block ([P1] §4: the block pool reserves block 0); no
+ * kernel reads it unless a block table points at it.
+ */
+#ifndef PAGEDKV_H_
+#define PAGEDKV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of q / out / key / value / KV pool. */
+typedef enum {
+    PKV_BF16 = 0,      /* bfloat16 */
+    PKV_FP16 = 1,      /* IEEE binary16 */
+    PKV_FP8_E4M3 = 2   /* OCP E4M3 with per-tensor fp32 scale (KV pool only) */
+} pkv_dtype;
+
+enum {
+    PKV_OK = 0,
+    PKV_ERR_ARG = -1,          /* null pointer, bad size, inconsistent heads */
+    PKV_ERR_SIZE = -2,         /* workspace / pool / buffer too small */
+    PKV_ERR_HIP = -3,          /* a HIP runtime call or launch failed */
+    PKV_ERR_UNSUPPORTED = -4   /* valid but not built: head_dim, dtype pair */
+};
+
+/* Opaque stream type: a hipStream_t passed through unchanged. */
+typedef void* pkv_stream_t;
+
+/* ---------------------------------------------------------------- errors -- */
+
+/* Message for the last nonzero return on this thread ("" if none).  The
+ * string is owned by the library and valid until the next call. */
+const char* pkv_last_error(void);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int32_t pkv_version(void);
+
+/* ------------------------------------------------------------ pool sizes -- */
+
+/* Bytes of KV per token over all layers: 2 * L * H_kv * d * b ([P1] §2 size
+ * formula; b = 2 for bf16/fp16, 1 for fp8 — [P1] §2 notes that FP8 KV makes
+ * b = 1).  Returns a negative PKV_ERR_* code on a bad argument.
+ * Example: L=28, H_kv=2, d=128, bf16 -> 28672. */
+int64_t pkv_bytes_per_token(int32_t num_layers, int32_t num_kv_heads,
+                            int32_t head_dim, int32_t kv_dtype);
+
+/* Bytes of one tile (block_size x head_dim elements) and of one layer's K
+ * (equivalently V) pool of num_blocks blocks.  Negative on a bad argument. */
+int64_t pkv_tile_bytes(int32_t head_dim, int32_t block_size, int32_t kv_dtype);
+int64_t pkv_layer_pool_bytes(int32_t num_blocks, int32_t num_kv_heads,
+                             int32_t head_dim, int32_t block_size,
+                             int32_t kv_dtype);
+
+/* ------------------------------------------------------------- KV pool -- */
+
+typedef struct {
+    int32_t num_layers;
+    int32_t num_blocks;     /* physical blocks per layer, block 0 = null */
+    int32_t num_kv_heads;
+    int32_t head_dim;
+    int32_t block_size;     /* tokens per block: 16 or 32 */
+    int32_t kv_dtype;       /* pkv_dtype */
+} pkv_pool_desc;
+
+typedef struct pkv_pool pkv_pool;
+
+/* Bind caller-allocated device memory as a paged KV pool ([P1] §4 block
+ * pool; layout above).  k_layers / v_layers are host arrays of num_layers
+ * device pointers, each at least bytes_each bytes, which must be at least
+ * pkv_layer_pool_bytes(desc).  The handle records the pointers; it allocates
+ * no device memory.  Errors: PKV_ERR_ARG (null, bad descriptor),
+ * PKV_ERR_SIZE (bytes_each too small), PKV_ERR_UNSUPPORTED. */
+int32_t kv_pool_create(const pkv_pool_desc* desc, void* const* k_layers,
+                       void* const* v_layers, int64_t bytes_each,
+                       pkv_pool** out);
+int32_t kv_pool_destroy(pkv_pool* pool);
+int32_t kv_pool_get_desc(const pkv_pool* pool, pkv_pool_desc* out);
+/* Device pointers of layer `layer`'s K and V pools. */
+int32_t kv_pool_layer(const pkv_pool* pool, int32_t layer, void** k_cache,
+                      void** v_cache);
+/* Fill the null block (block 0) of every layer's K and V pool with a NaN
+ * pattern of the pool's dtype, so that a stray read of it shows in the
+ * output.  Asynchronous on `stream`. */
+int32_t kv_pool_poison_null_block(const pkv_pool* pool, pkv_stream_t stream);
+
+/* ---------------------------------------------------------- cache write -- */
+
+/* Slot of each sequence's newest token: the token at position c-1 sits in
+ * logical block (c-1)/bs at offset (c-1)%bs, so
+ *     slot_mapping[s] = block_tables[s][(c-1)/bs] * bs + (c-1) % bs
+ * ([P1] §4 diagram: request A's tokens 32-37 live in the block that logical
+ * B2 maps to; [P2] "Block table").  c = context_lens[s] already counts the
+ * new token; c <= 0 or c > max_blocks_per_seq*bs gives slot -1 (no write).
+ * block_tables: [num_seqs][max_blocks_per_seq] int32, row-major. */
+int32_t pkv_decode_slot_mapping(const int32_t* block_tables,
+                                int32_t max_blocks_per_seq,
+                                const int32_t* context_lens, int32_t num_seqs,
+                                int32_t block_size, int32_t* slot_mapping,
+                                pkv_stream_t stream);
+
+/* reshape_and_cache: write the new tokens' K and V into the pool.
+ * key, value: [num_tokens][num_kv_heads][head_dim] of src_dtype (bf16/fp16),
+ * contiguous.  For token t with slot = slot_mapping[t] >= 0, block
+ * pb = slot / block_size, row = slot % block_size, every head g and dim k:
+ *     k_cache element (pb, g, row, k) <- encode(key[t][g][k])
+ * and likewise for V (only new tokens' K/V are added: [P4] "KV cache basics";
+ * [P1] §2).  encode is the identity on bits when kv_dtype == src_dtype; for
+ * fp8 it is e4m3(RNE_satfinite(float(x) * inv)) with inv = 1.0f / k_scale
+ * (resp. v_scale) rounded to fp32 on the host.  Slots < 0 or >= num_blocks *
+ * block_size are skipped (padding tokens).  Tokens must have distinct slots.
+ * Errors: PKV_ERR_ARG, PKV_ERR_UNSUPPORTED (kv bf16/fp16 must equal
+ * src_dtype), PKV_ERR_HIP. */
+int32_t reshape_and_cache(const void* key, const void* value,
+                          int32_t src_dtype, void* k_cache, void* v_cache,
+                          const int32_t* slot_mapping, int32_t num_tokens,
+                          int32_t num_kv_heads, int32_t head_dim,
+                          int32_t block_size, int32_t num_blocks,
+                          int32_t kv_dtype, float k_scale, float v_scale,
+                          pkv_stream_t stream);
+
+/* --------------------------------------------------------------- decode -- */
+
+/* Implementation selector for paged_attention_decode_ex. */
+enum {
+    PKV_IMPL_AUTO = 0,    /* matrix-core kernel */
+    PKV_IMPL_MFMA = 1,    /* GQA group on 16x16 MFMA tiles */
+    PKV_IMPL_VECTOR = 2   /* same math on the vector ALU (for comparison) */
+};
+
+/* Which kernels one call launches (bit mask; default both). */
+enum {
+    PKV_STAGE_PARTITIONS = 1,  /* per-partition attention (+ direct output
+                                  for single-partition sequences) */
+    PKV_STAGE_REDUCE = 2       /* partial-softmax merge of multi-partition
+                                  sequences */
+};
+
+typedef struct {
+    int32_t partition_tokens; /* context split size; 0 = library default
+                                 (512); must be a multiple of block_size */
+    int32_t impl;             /* PKV_IMPL_* */
+    int32_t stages;           /* PKV_STAGE_* mask; 0 = both */
+    int32_t num_blocks;       /* pool size for id clamping; 0 = unchecked */
+} pkv_decode_opts;
+
+/* Workspace bytes for a decode call: per (sequence, query head, partition)
+ * one running max, one normaliser and head_dim fp32 partial outputs, with
+ * P = ceil(max_context_len / partition_tokens).  Zero when P == 1. */
+int64_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_heads,
+                                        int32_t head_dim,
+                                        int32_t max_context_len,
+                                        int32_t partition_tokens);
+
+/* paged_attention_decode: one query token per sequence attends over its
+ * whole context through the block table (operation above; [P1] §4, [P2]
+ * "Block table").
+ *   out, q       : [num_seqs][num_heads][head_dim] of q_dtype (bf16 / fp16),
+ *                  contiguous; out rounded to nearest even.
+ *   k_cache,
+ *   v_cache      : one layer's pools, layout above, kv_dtype.  bf16/fp16 KV
+ *                  must equal q_dtype; fp8 KV works with either q_dtype.
+ *   block_tables : [num_seqs][max_blocks_per_seq] int32; entries at or past
+ *                  ceil(c/bs) are never read.
+ *   context_lens : [num_seqs] int32, c >= 0 (c = 0 gives a zero output).
+ *                  c is clamped to min(max_context_len, max_blocks_per_seq *
+ *                  block_size) so the kernel never reads past the table.
+ *   scale        : logit scale (1/sqrt(head_dim) usually).
+ *   k_scale,
+ *   v_scale      : fp8 dequantisation scales (ignored unless kv fp8).
+ *   workspace    : >= paged_attention_workspace_bytes(...) bytes of device
+ *                  memory (may be NULL when that is 0).
+ * num_heads must be a multiple of num_kv_heads, with G = num_heads /
+ * num_kv_heads <= 16.  Errors: PKV_ERR_ARG, PKV_ERR_SIZE (workspace),
+ * PKV_ERR_UNSUPPORTED (head_dim != 128, dtype pair), PKV_ERR_HIP. */
+int32_t paged_attention_decode(void* out, const void* q, int32_t q_dtype,
+                               const void* k_cache, const void* v_cache,
+                               const int32_t* block_tables,
+                               int32_t max_blocks_per_seq,
+                               const int32_t* context_lens,
+                               int32_t max_context_len, int32_t num_seqs,
+                               int32_t num_heads, int32_t num_kv_heads,
+                               int32_t head_dim, float scale,
+                               int32_t block_size, int32_t kv_dtype,
+                               float k_scale, float v_scale, void* workspace,
+                               int64_t workspace_bytes, pkv_stream_t stream);
+
+/* Same as paged_attention_decode with explicit options (NULL = defaults).
+ * With opts->num_blocks > 0, block ids outside [0, num_blocks) are read as
+ * the null block 0 instead of faulting. */
+int32_t paged_attention_decode_ex(void* out, const void* q, int32_t q_dtype,
+                                  const void* k_cache, const void* v_cache,
+                                  const int32_t* block_tables,
+                                  int32_t max_blocks_per_seq,
+                                  const int32_t* context_lens,
+                                  int32_t max_context_len, int32_t num_seqs,
+                                  int32_t num_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, float scale,
+                                  int32_t block_size, int32_t kv_dtype,
+                                  float k_scale, float v_scale,
+                                  void* workspace, int64_t workspace_bytes,
+                                  const pkv_decode_opts* opts,
+                                  pkv_stream_t stream);
+
+/* ------------------------------------------------------------ validation -- */
+
+/* Count block-table entries that a decode of these context lengths would
+ * read and that fall outside [1, num_blocks) (the null block 0 counts as
+ * invalid), plus context lengths < 0 or > max_blocks_per_seq * block_size.
+ * Synchronous: waits for `stream`, writes the count to *bad_count (host).
+ * Uses 4 bytes of caller scratch device memory `scratch_dev`. */
+int32_t pkv_check_block_tables(const int32_t* block_tables,
+                               int32_t max_blocks_per_seq,
+                               const int32_t* context_lens, int32_t num_seqs,
+                               int32_t block_size, int32_t num_blocks,
+                               int32_t* scratch_dev, int64_t* bad_count,
+                               pkv_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H_ */
