@@ -1,0 +1,289 @@
+#!/usr/bin/env python3
+"""Paged decode attention throughput on one MI355X.
+
+A step is one decode step of the whole path for every layer of the
+workload: decode slot mapping (once, tables are shared by all layers), then
+per layer reshape_and_cache of the batch's new tokens, the partition kernel
+and the partition merge.  Inputs are synthetic and resident in HBM before
+timing starts (workloads/: seeded lengths and block tables, N(0,1) values).
+
+Output: one JSON line.  `value` is achieved GB/s of algorithmic bytes per
+step over step time; bytes per layer = sum_s c_s*2*H_kv*d*b_kv (KV read)
++ S*H*d*(b_q + b_out) (query read, output write) + S*H_kv*d*2*(b_src + b_kv)
+(new-token K/V read and written).  `roofline` covers the partition kernel,
+timed with HIP events on its launch stream inside the timed region.
+`cpu_baseline` times the CPU oracle on a bounded sample of layer 0.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0   # MI355X published HBM3E bandwidth
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="qwen7b",
+                    choices=["tiny", "qwen15b", "qwen7b", "qwen72b", "llama7b"])
+    ap.add_argument("--kv-dtype", default=None, choices=[None, "bf16", "fp16", "fp8"])
+    ap.add_argument("--block-size", type=int, default=None, choices=[None, 16, 32])
+    ap.add_argument("--layers", type=int, default=None)
+    ap.add_argument("--partition-tokens", type=int, default=0)
+    ap.add_argument("--impl", default="auto", choices=["auto", "mfma", "vector"])
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0,
+                    help="target CPU time of the oracle sample (0 disables)")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also run one device copy of this size (counter calibration)")
+    return ap.parse_args()
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("decode.hip", "pkv_device.h"):
+        with open(os.path.join(ROOT, "paged_kv_cache_51_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(config_key):
+    """HBM traffic per launch from committed rocprofv3 counter runs, only if
+    they were taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", "decode_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    rec = data.get(config_key)
+    if not rec or rec.get("kernel_hash") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}),
+              flush=True)
+        sys.exit(2)
+
+    import torch
+    import paged_kv_cache_51_amd as pkv
+    import workloads
+
+    dt_names = {"bf16": pkv.BF16, "fp16": pkv.FP16, "fp8": pkv.FP8_E4M3}
+    cfg, tabs, _, _ = workloads.make(args.config, seed=args.seed, block_size=args.block_size)
+    kv_dtype = dt_names[args.kv_dtype] if args.kv_dtype else cfg.kv_dtype
+    q_dtype = cfg.q_dtype
+    if kv_dtype in (pkv.BF16, pkv.FP16) and kv_dtype != q_dtype:
+        q_dtype = kv_dtype
+    bs = args.block_size or cfg.block_size
+    L = args.layers or cfg.num_layers
+    S, H, Hkv, D = cfg.num_seqs, cfg.num_heads, cfg.num_kv_heads, cfg.head_dim
+    impl = {"auto": pkv.IMPL_AUTO, "mfma": pkv.IMPL_MFMA, "vector": pkv.IMPL_VECTOR}[args.impl]
+    part = args.partition_tokens
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    tq = torch.bfloat16 if q_dtype == pkv.BF16 else torch.float16
+    b_kv = 1 if kv_dtype == pkv.FP8_E4M3 else 2
+    ctx = tabs.context_lens
+    max_ctx = int(ctx.max())
+    nb = tabs.num_blocks
+    fp8_scale = float(np.float32(8.0 / 448.0))
+    ks = vs = fp8_scale if kv_dtype == pkv.FP8_E4M3 else 1.0
+
+    print(f"[bench] {cfg.description}; layers={L} kv={kv_dtype} bs={bs} blocks={nb}",
+          file=sys.stderr, flush=True)
+    t0 = time.time()
+    pool_bytes = pkv.layer_pool_bytes(nb, Hkv, D, bs, kv_dtype)
+    kpools, vpools = [], []
+    for layer in range(L):
+        k = torch.empty(pool_bytes, dtype=torch.uint8, device=dev)
+        v = torch.empty(pool_bytes, dtype=torch.uint8, device=dev)
+        workloads.device_fill_normal(k, kv_dtype, 1000 + layer, scale=fp8_scale)
+        workloads.device_fill_normal(v, kv_dtype, 2000 + layer, scale=fp8_scale)
+        kpools.append(k)
+        vpools.append(v)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(args.seed + 7)
+    qs = [torch.randn(S, H, D, generator=gen, device=dev).to(tq) for _ in range(L)]
+    newk = [torch.randn(S, Hkv, D, generator=gen, device=dev).to(tq) for _ in range(L)]
+    newv = [torch.randn(S, Hkv, D, generator=gen, device=dev).to(tq) for _ in range(L)]
+    outs = [torch.empty(S, H, D, dtype=tq, device=dev) for _ in range(L)]
+    bt = torch.from_numpy(tabs.block_tables).to(dev)
+    cl = torch.from_numpy(ctx).to(dev)
+    slots = torch.empty(S, dtype=torch.int32, device=dev)
+    ws_n = pkv.workspace_bytes(S, H, D, max_ctx, part)
+    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=dev)
+    assert pkv.check_block_tables(bt, cl, bs, nb) == 0
+    torch.cuda.synchronize()
+    print(f"[bench] inputs resident in {time.time() - t0:.1f}s "
+          f"({2 * L * pool_bytes / 2**30:.1f} GiB of pools)", file=sys.stderr, flush=True)
+
+    stream = torch.cuda.current_stream()
+    scale = float(np.float32(1.0 / np.sqrt(D)))
+
+    def step(ev=None):
+        pkv.decode_slot_mapping(bt, cl, bs, slot_mapping=slots, stream=stream)
+        for layer in range(L):
+            pkv.reshape_and_cache(newk[layer], newv[layer], kpools[layer], vpools[layer], slots,
+                                  bs, nb, kv_dtype, ks, vs, stream=stream)
+            if ev is not None:
+                ev[layer][0].record(stream)
+            pkv.paged_attention_decode(outs[layer], qs[layer], kpools[layer], vpools[layer], bt,
+                                       cl, max_ctx, Hkv, bs, kv_dtype, scale, ks, vs,
+                                       workspace=ws, partition_tokens=part, impl=impl,
+                                       stages=pkv.STAGE_PARTITIONS, num_blocks=nb,
+                                       stream=stream)
+            if ev is not None:
+                ev[layer][1].record(stream)
+            pkv.paged_attention_decode(outs[layer], qs[layer], kpools[layer], vpools[layer], bt,
+                                       cl, max_ctx, Hkv, bs, kv_dtype, scale, ks, vs,
+                                       workspace=ws, partition_tokens=part, impl=impl,
+                                       stages=pkv.STAGE_REDUCE, num_blocks=nb, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(L)]
+           for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for k in range(args.steps):
+        step(evs[k])
+    end.record(stream)
+    torch.cuda.synchronize()
+    step_ms = start.elapsed_time(end) / args.steps
+    dec_ms = [evs[k][layer][0].elapsed_time(evs[k][layer][1])
+              for k in range(args.steps) for layer in range(L)]
+    dec_avg_ms = float(np.mean(dec_ms))
+
+    kv_bytes = int(ctx.astype(np.int64).sum()) * 2 * Hkv * D * b_kv
+    qo_bytes = S * H * D * (2 + 2)
+    new_bytes = S * Hkv * D * 2 * (2 + b_kv)
+    step_bytes = L * (kv_bytes + qo_bytes + new_bytes)
+    gbs = step_bytes / (step_ms * 1e-3) / 1e9
+    launch_bytes = kv_bytes + qo_bytes
+    achieved = launch_bytes / (dec_avg_ms * 1e-3) / 1e9
+    traffic_key = f"{args.config}-{kv_dtype}-bs{bs}-part{part}-impl{impl}"
+    traffic = measured_traffic(traffic_key)
+    print(f"[bench] step {step_ms:.3f} ms, {gbs:.0f} GB/s; partition kernel "
+          f"{dec_avg_ms * 1e3:.1f} us avg, {achieved:.0f} GB/s ({achieved / PEAK_HBM_GBS:.1%})",
+          file=sys.stderr, flush=True)
+
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib << 20
+        a = torch.empty(n, dtype=torch.uint8, device=dev)
+        b = torch.empty(n, dtype=torch.uint8, device=dev)
+        a.fill_(1)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    cpu = None
+    if args.cpu_baseline_seconds > 0:
+        cpu = cpu_baseline(args, tabs, kpools[0], vpools[0], qs[0], q_dtype, kv_dtype, Hkv, bs,
+                           scale, ks, vs, b_kv, H, D)
+
+    dt_name = {pkv.BF16: "bf16", pkv.FP16: "fp16", pkv.FP8_E4M3: "fp8"}
+    rec = {
+        "metric": "paged decode attn achieved HBM GB/s (% of MI355X peak) + seq-layers/s",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dt_name[kv_dtype] if kv_dtype == pkv.FP8_E4M3 else dt_name[q_dtype],
+        "data": "synthetic",
+        "config": {
+            "workload": cfg.description,
+            "config": args.config,
+            "layers": L,
+            "num_seqs": S,
+            "num_heads": H,
+            "num_kv_heads": Hkv,
+            "head_dim": D,
+            "block_size": bs,
+            "kv_dtype": dt_name[kv_dtype],
+            "mean_context": float(ctx.mean()),
+            "partition_tokens": part or 512,
+            "impl": args.impl,
+            "parallelism": "single GPU",
+        },
+        "pct_of_peak": round(gbs / PEAK_HBM_GBS, 4),
+        "seq_layers_per_s": round(S * L / (step_ms * 1e-3), 1),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "paged_decode_mfma_kernel" if impl != pkv.IMPL_VECTOR
+                      else "paged_decode_vector_kernel",
+            "achieved": round(achieved, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "traffic": traffic,
+            "avg_launch_us": round(dec_avg_ms * 1e3, 2),
+            "algorithmic_bytes_per_launch": launch_bytes,
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def cpu_baseline(args, tabs, kpool, vpool, q, q_dtype, kv_dtype, Hkv, bs, scale, ks, vs, b_kv,
+                 H, D):
+    """The oracle as it stands, on a bounded sample of layer 0."""
+    import oracle
+    t0 = time.time()
+    kp = kpool.cpu().numpy()
+    vp = vpool.cpu().numpy()
+    qb = q.cpu().view(__import__("torch").int16).numpy().view(np.uint16)
+    ctx = tabs.context_lens
+    bt = tabs.block_tables
+    odt = {0: oracle.BF16, 1: oracle.FP16, 2: oracle.FP8}
+    threads = oracle.max_threads()
+
+    def run(n):
+        t = time.time()
+        oracle.paged_decode(qb[:n], odt[q_dtype], kp, vp, odt[kv_dtype], bt[:n], ctx[:n], Hkv,
+                            bs, scale, ks, vs)
+        return time.time() - t
+
+    t1 = run(1)
+    n = int(min(len(ctx), max(1, args.cpu_baseline_seconds / max(t1, 1e-6))))
+    tn = run(n) if n > 1 else t1
+    kv = int(ctx[:n].astype(np.int64).sum()) * 2 * Hkv * D * b_kv
+    qo = n * H * D * 4
+    print(f"[bench] cpu oracle: {n} seqs in {tn:.1f}s on {threads} threads "
+          f"(host copy {time.time() - t0 - tn - t1:.1f}s)", file=sys.stderr, flush=True)
+    return {
+        "value": round((kv + qo) / tn / 1e9, 4),
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"layer 0, first {n} of {len(ctx)} sequences ({int(ctx[:n].sum())} "
+                  f"context tokens), fp64 C oracle, OpenMP over (seq, head)",
+        "seq_layers_per_s": round(n / tn, 3),
+        "seconds": round(tn, 2),
+    }
+
+
+if __name__ == "__main__":
+    main()

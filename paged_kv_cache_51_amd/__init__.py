@@ -1,0 +1,14 @@
+"""paged_kv_cache_51_amd — paged KV cache + PagedAttention decode for MI355X.
+
+A thin ctypes binding over libpagedkv.so (include/pagedkv.h): every step of
+the decode path runs in the library's HIP kernels; this module only turns
+torch tensors into pointers, sizes and the current HIP stream.  There is no
+fallback: if the library is missing or fails to load, importing the binding
+raises.
+"""
+from ._binding import (  # noqa: F401
+    BF16, FP16, FP8_E4M3, IMPL_AUTO, IMPL_MFMA, IMPL_VECTOR, STAGE_PARTITIONS, STAGE_REDUCE,
+    PagedKVError, KVPool, lib, lib_path, version, last_error, bytes_per_token, tile_bytes,
+    layer_pool_bytes, workspace_bytes, decode_slot_mapping, reshape_and_cache,
+    paged_attention_decode, check_block_tables, torch_dtype, dtype_code, EXPORTS,
+)

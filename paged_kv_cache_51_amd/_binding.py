@@ -1,0 +1,252 @@
+"""ctypes binding of libpagedkv.so — argument marshalling only.
+
+Names follow include/pagedkv.h.  Tensors must be CUDA (HIP) tensors of the
+documented dtypes and layouts; launches go on torch's current stream unless a
+stream is given.  Errors from the library raise PagedKVError with the
+library's message.
+"""
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(HERE, "lib", "libpagedkv.so")
+
+BF16, FP16, FP8_E4M3 = 0, 1, 2
+IMPL_AUTO, IMPL_MFMA, IMPL_VECTOR = 0, 1, 2
+STAGE_PARTITIONS, STAGE_REDUCE = 1, 2
+
+# Every symbol include/pagedkv.h declares.
+EXPORTS = [
+    "pkv_last_error", "pkv_version", "pkv_bytes_per_token", "pkv_tile_bytes",
+    "pkv_layer_pool_bytes", "kv_pool_create", "kv_pool_destroy", "kv_pool_get_desc",
+    "kv_pool_layer", "kv_pool_poison_null_block", "pkv_decode_slot_mapping",
+    "reshape_and_cache", "paged_attention_workspace_bytes", "paged_attention_decode",
+    "paged_attention_decode_ex", "pkv_check_block_tables",
+]
+
+
+class PagedKVError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"libpagedkv error {code}: {msg}")
+        self.code = code
+
+
+class PoolDesc(ctypes.Structure):
+    _fields_ = [("num_layers", ctypes.c_int32), ("num_blocks", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("block_size", ctypes.c_int32), ("kv_dtype", ctypes.c_int32)]
+
+
+class DecodeOpts(ctypes.Structure):
+    _fields_ = [("partition_tokens", ctypes.c_int32), ("impl", ctypes.c_int32),
+                ("stages", ctypes.c_int32), ("num_blocks", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libpagedkv.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(lib_path):
+            raise ImportError(f"{lib_path} is missing: build it with "
+                              "`python -m paged_kv_cache_51_amd.build` (no fallback exists)")
+        L = ctypes.CDLL(lib_path)
+        i32, i64, f32, p = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p
+        sig = {
+            "pkv_last_error": (ctypes.c_char_p, []),
+            "pkv_version": (i32, []),
+            "pkv_bytes_per_token": (i64, [i32, i32, i32, i32]),
+            "pkv_tile_bytes": (i64, [i32, i32, i32]),
+            "pkv_layer_pool_bytes": (i64, [i32, i32, i32, i32, i32]),
+            "kv_pool_create": (i32, [ctypes.POINTER(PoolDesc), p, p, i64, ctypes.POINTER(p)]),
+            "kv_pool_destroy": (i32, [p]),
+            "kv_pool_get_desc": (i32, [p, ctypes.POINTER(PoolDesc)]),
+            "kv_pool_layer": (i32, [p, i32, ctypes.POINTER(p), ctypes.POINTER(p)]),
+            "kv_pool_poison_null_block": (i32, [p, p]),
+            "pkv_decode_slot_mapping": (i32, [p, i32, p, i32, i32, p, p]),
+            "reshape_and_cache": (i32, [p, p, i32, p, p, p, i32, i32, i32, i32, i32, i32, f32,
+                                        f32, p]),
+            "paged_attention_workspace_bytes": (i64, [i32, i32, i32, i32, i32]),
+            "paged_attention_decode": (i32, [p, p, i32, p, p, p, i32, p, i32, i32, i32, i32,
+                                             i32, f32, i32, i32, f32, f32, p, i64, p]),
+            "paged_attention_decode_ex": (i32, [p, p, i32, p, p, p, i32, p, i32, i32, i32, i32,
+                                                i32, f32, i32, i32, f32, f32, p, i64,
+                                                ctypes.POINTER(DecodeOpts), p]),
+            "pkv_check_block_tables": (i32, [p, i32, p, i32, i32, i32, p,
+                                             ctypes.POINTER(ctypes.c_int64), p]),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def last_error():
+    return lib().pkv_last_error().decode()
+
+
+def _check(rc):
+    if rc < 0:
+        raise PagedKVError(int(rc), last_error())
+    return rc
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t, name, dtype=None, device=True):
+    if t is None:
+        return None
+    if device and not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+_TORCH = {BF16: torch.bfloat16, FP16: torch.float16}
+
+
+def torch_dtype(code):
+    return _TORCH[code]
+
+
+def dtype_code(t):
+    if t == torch.bfloat16:
+        return BF16
+    if t == torch.float16:
+        return FP16
+    raise ValueError(f"unsupported dtype {t}")
+
+
+def version():
+    return int(lib().pkv_version())
+
+
+def bytes_per_token(num_layers, num_kv_heads, head_dim, kv_dtype):
+    return _check(lib().pkv_bytes_per_token(num_layers, num_kv_heads, head_dim, kv_dtype))
+
+
+def tile_bytes(head_dim, block_size, kv_dtype):
+    return _check(lib().pkv_tile_bytes(head_dim, block_size, kv_dtype))
+
+
+def layer_pool_bytes(num_blocks, num_kv_heads, head_dim, block_size, kv_dtype):
+    return _check(lib().pkv_layer_pool_bytes(num_blocks, num_kv_heads, head_dim, block_size,
+                                             kv_dtype))
+
+
+def workspace_bytes(num_seqs, num_heads, head_dim, max_context_len, partition_tokens=0):
+    return _check(lib().paged_attention_workspace_bytes(num_seqs, num_heads, head_dim,
+                                                        max_context_len, partition_tokens))
+
+
+class KVPool:
+    """A paged KV pool over caller-owned torch byte tensors (one K and one V
+    tensor of pkv_layer_pool_bytes bytes per layer)."""
+
+    def __init__(self, num_layers, num_blocks, num_kv_heads, head_dim, block_size, kv_dtype,
+                 k_layers, v_layers):
+        self.desc = PoolDesc(num_layers, num_blocks, num_kv_heads, head_dim, block_size,
+                             kv_dtype)
+        self.k_layers, self.v_layers = list(k_layers), list(v_layers)
+        nbytes = min(t.numel() * t.element_size() for t in self.k_layers + self.v_layers)
+        karr = (ctypes.c_void_p * num_layers)(*[t.data_ptr() for t in self.k_layers])
+        varr = (ctypes.c_void_p * num_layers)(*[t.data_ptr() for t in self.v_layers])
+        h = ctypes.c_void_p()
+        _check(lib().kv_pool_create(ctypes.byref(self.desc), karr, varr, nbytes,
+                                    ctypes.byref(h)))
+        self.handle = h
+
+    @classmethod
+    def allocate(cls, num_layers, num_blocks, num_kv_heads, head_dim, block_size, kv_dtype,
+                 device="cuda"):
+        n = layer_pool_bytes(num_blocks, num_kv_heads, head_dim, block_size, kv_dtype)
+        ks = [torch.empty(n, dtype=torch.uint8, device=device) for _ in range(num_layers)]
+        vs = [torch.empty(n, dtype=torch.uint8, device=device) for _ in range(num_layers)]
+        return cls(num_layers, num_blocks, num_kv_heads, head_dim, block_size, kv_dtype, ks, vs)
+
+    def layer(self, i):
+        k, v = ctypes.c_void_p(), ctypes.c_void_p()
+        _check(lib().kv_pool_layer(self.handle, i, ctypes.byref(k), ctypes.byref(v)))
+        return k.value, v.value
+
+    def poison_null_block(self, stream=None):
+        _check(lib().kv_pool_poison_null_block(self.handle, _stream(stream)))
+
+    def close(self):
+        if self.handle:
+            lib().kv_pool_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def decode_slot_mapping(block_tables, context_lens, block_size, slot_mapping=None, stream=None):
+    S = context_lens.shape[0]
+    if slot_mapping is None:
+        slot_mapping = torch.empty(S, dtype=torch.int32, device=context_lens.device)
+    _check(lib().pkv_decode_slot_mapping(
+        _ptr(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+        _ptr(context_lens, "context_lens", torch.int32), S, block_size,
+        _ptr(slot_mapping, "slot_mapping", torch.int32), _stream(stream)))
+    return slot_mapping
+
+
+def reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, block_size, num_blocks,
+                      kv_dtype, k_scale=1.0, v_scale=1.0, stream=None):
+    """key/value: [T][H_kv][d] bf16/fp16; caches: uint8 pool tensors."""
+    T, H, D = key.shape
+    _check(lib().reshape_and_cache(
+        _ptr(key, "key"), _ptr(value, "value"), dtype_code(key.dtype),
+        _ptr(k_cache, "k_cache"), _ptr(v_cache, "v_cache"),
+        _ptr(slot_mapping, "slot_mapping", torch.int32), T, H, D, block_size, num_blocks,
+        kv_dtype, float(k_scale), float(v_scale), _stream(stream)))
+
+
+def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
+                           max_context_len, num_kv_heads, block_size, kv_dtype, scale,
+                           k_scale=1.0, v_scale=1.0, workspace=None, partition_tokens=0,
+                           impl=IMPL_AUTO, stages=0, num_blocks=0, stream=None):
+    """q/out: [S][H][d] bf16/fp16; k/v_cache: uint8 pools of one layer."""
+    S, H, D = q.shape
+    need = workspace_bytes(S, H, D, max_context_len, partition_tokens)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    opts = DecodeOpts(partition_tokens, impl, stages, num_blocks)
+    _check(lib().paged_attention_decode_ex(
+        _ptr(out, "out"), _ptr(q, "q"), dtype_code(q.dtype), _ptr(k_cache, "k_cache"),
+        _ptr(v_cache, "v_cache"), _ptr(block_tables, "block_tables", torch.int32),
+        block_tables.shape[1], _ptr(context_lens, "context_lens", torch.int32),
+        int(max_context_len), S, H, num_kv_heads, D, float(scale), block_size, kv_dtype,
+        float(k_scale), float(v_scale), _ptr(workspace, "workspace"), ws_bytes,
+        ctypes.byref(opts), _stream(stream)))
+    return out
+
+
+def check_block_tables(block_tables, context_lens, block_size, num_blocks, stream=None):
+    """Number of table entries a decode would read outside [1, num_blocks)
+    (plus bad context lengths).  Synchronous."""
+    scratch = torch.empty(1, dtype=torch.int32, device=context_lens.device)
+    bad = ctypes.c_int64()
+    _check(lib().pkv_check_block_tables(
+        _ptr(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+        _ptr(context_lens, "context_lens", torch.int32), context_lens.shape[0], block_size,
+        num_blocks, _ptr(scratch, "scratch"), ctypes.byref(bad), _stream(stream)))
+    return int(bad.value)

@@ -1,0 +1,328 @@
+// api.hip — the extern "C" boundary declared in include/pagedkv.h:
+// argument checks, workspace sizing, kernel selection, error reporting.
+// Every computation runs in the kernels of cache_ops.hip / decode*.hip.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/pagedkv.h"
+#include "pkv_launch.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int32_t fail(int32_t code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+int32_t ok() {
+    g_err.clear();
+    return PKV_OK;
+}
+
+int32_t hip_fail(hipError_t e, const char* what) {
+    return fail(PKV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool valid_dtype(int32_t dt) { return dt == PKV_BF16 || dt == PKV_FP16 || dt == PKV_FP8_E4M3; }
+int32_t elem_size(int32_t dt) { return dt == PKV_FP8_E4M3 ? 1 : 2; }
+bool valid_block_size(int32_t bs) { return bs == 16 || bs == 32; }
+
+constexpr int32_t kDefaultPartitionTokens = 512;
+constexpr int32_t kBuiltHeadDim = 128;
+
+// Kernels are built for head_dim 128; layout sizes accept any multiple of 64.
+int32_t check_layout_args(int32_t head_dim, int32_t block_size, int32_t kv_dtype) {
+    if (!valid_dtype(kv_dtype)) return fail(PKV_ERR_ARG, "kv_dtype %d is not a pkv_dtype", kv_dtype);
+    if (head_dim <= 0 || head_dim % 64) return fail(PKV_ERR_ARG, "head_dim %d is not a positive multiple of 64", head_dim);
+    if (!valid_block_size(block_size)) return fail(PKV_ERR_ARG, "block_size %d must be 16 or 32", block_size);
+    return PKV_OK;
+}
+
+}  // namespace
+
+struct pkv_pool {
+    pkv_pool_desc desc;
+    std::vector<void*> k;
+    std::vector<void*> v;
+    int64_t bytes_each;
+};
+
+extern "C" {
+
+const char* pkv_last_error(void) { return g_err.c_str(); }
+
+int32_t pkv_version(void) { return 100; }
+
+int64_t pkv_bytes_per_token(int32_t num_layers, int32_t num_kv_heads, int32_t head_dim,
+                            int32_t kv_dtype) {
+    if (num_layers <= 0 || num_kv_heads <= 0 || head_dim <= 0)
+        return fail(PKV_ERR_ARG, "layers, kv heads and head_dim must be positive");
+    if (!valid_dtype(kv_dtype)) return fail(PKV_ERR_ARG, "kv_dtype %d is not a pkv_dtype", kv_dtype);
+    ok();
+    return 2LL * num_layers * num_kv_heads * head_dim * elem_size(kv_dtype);
+}
+
+int64_t pkv_tile_bytes(int32_t head_dim, int32_t block_size, int32_t kv_dtype) {
+    if (int32_t e = check_layout_args(head_dim, block_size, kv_dtype)) return e;
+    ok();
+    return (int64_t)block_size * head_dim * elem_size(kv_dtype);
+}
+
+int64_t pkv_layer_pool_bytes(int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
+                             int32_t block_size, int32_t kv_dtype) {
+    if (int32_t e = check_layout_args(head_dim, block_size, kv_dtype)) return e;
+    if (num_blocks <= 0 || num_kv_heads <= 0)
+        return fail(PKV_ERR_ARG, "num_blocks and num_kv_heads must be positive");
+    if ((int64_t)num_blocks * block_size >= (1LL << 31))
+        return fail(PKV_ERR_ARG, "num_blocks * block_size must stay below 2^31 (slot numbers are int32)");
+    ok();
+    return (int64_t)num_blocks * num_kv_heads * block_size * head_dim * elem_size(kv_dtype);
+}
+
+int32_t kv_pool_create(const pkv_pool_desc* desc, void* const* k_layers, void* const* v_layers,
+                       int64_t bytes_each, pkv_pool** out) {
+    if (!desc || !k_layers || !v_layers || !out) return fail(PKV_ERR_ARG, "null argument");
+    *out = nullptr;
+    if (desc->num_layers <= 0) return fail(PKV_ERR_ARG, "num_layers must be positive");
+    const int64_t need = pkv_layer_pool_bytes(desc->num_blocks, desc->num_kv_heads, desc->head_dim,
+                                              desc->block_size, desc->kv_dtype);
+    if (need < 0) return (int32_t)need;
+    if (bytes_each < need)
+        return fail(PKV_ERR_SIZE, "each layer pool needs %lld bytes, got %lld", (long long)need,
+                    (long long)bytes_each);
+    for (int32_t i = 0; i < desc->num_layers; ++i)
+        if (!k_layers[i] || !v_layers[i]) return fail(PKV_ERR_ARG, "layer %d pointer is null", i);
+    pkv_pool* p = new (std::nothrow) pkv_pool;
+    if (!p) return fail(PKV_ERR_ARG, "out of host memory");
+    p->desc = *desc;
+    p->k.assign(k_layers, k_layers + desc->num_layers);
+    p->v.assign(v_layers, v_layers + desc->num_layers);
+    p->bytes_each = bytes_each;
+    *out = p;
+    return ok();
+}
+
+int32_t kv_pool_destroy(pkv_pool* pool) {
+    delete pool;
+    return ok();
+}
+
+int32_t kv_pool_get_desc(const pkv_pool* pool, pkv_pool_desc* out) {
+    if (!pool || !out) return fail(PKV_ERR_ARG, "null argument");
+    *out = pool->desc;
+    return ok();
+}
+
+int32_t kv_pool_layer(const pkv_pool* pool, int32_t layer, void** k_cache, void** v_cache) {
+    if (!pool || !k_cache || !v_cache) return fail(PKV_ERR_ARG, "null argument");
+    if (layer < 0 || layer >= pool->desc.num_layers)
+        return fail(PKV_ERR_ARG, "layer %d outside [0, %d)", layer, pool->desc.num_layers);
+    *k_cache = pool->k[layer];
+    *v_cache = pool->v[layer];
+    return ok();
+}
+
+int32_t kv_pool_poison_null_block(const pkv_pool* pool, pkv_stream_t stream) {
+    if (!pool) return fail(PKV_ERR_ARG, "null pool");
+    const pkv_pool_desc& d = pool->desc;
+    const int64_t bytes = (int64_t)d.num_kv_heads * d.block_size * d.head_dim * elem_size(d.kv_dtype);
+    uint32_t pattern = d.kv_dtype == PKV_BF16 ? 0x7fc0u : (d.kv_dtype == PKV_FP16 ? 0x7e00u : 0x7fu);
+    const int pattern_bytes = elem_size(d.kv_dtype);
+    hipStream_t st = (hipStream_t)stream;
+    for (int32_t i = 0; i < d.num_layers; ++i) {
+        hipError_t e = pkv::launch_fill_pattern(pool->k[i], bytes, pattern, pattern_bytes, st);
+        if (e == hipSuccess) e = pkv::launch_fill_pattern(pool->v[i], bytes, pattern, pattern_bytes, st);
+        if (e != hipSuccess) return hip_fail(e, "null-block fill");
+    }
+    return ok();
+}
+
+int32_t pkv_decode_slot_mapping(const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                const int32_t* context_lens, int32_t num_seqs, int32_t block_size,
+                                int32_t* slot_mapping, pkv_stream_t stream) {
+    if (num_seqs < 0 || max_blocks_per_seq < 0) return fail(PKV_ERR_ARG, "negative size");
+    if (!valid_block_size(block_size)) return fail(PKV_ERR_ARG, "block_size %d must be 16 or 32", block_size);
+    if (num_seqs > 0 && (!block_tables || !context_lens || !slot_mapping))
+        return fail(PKV_ERR_ARG, "null pointer");
+    (void)hipGetLastError();
+    hipError_t e = pkv::launch_decode_slot_mapping(block_tables, max_blocks_per_seq, context_lens,
+                                                   num_seqs, block_size, slot_mapping,
+                                                   (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "decode_slot_mapping launch");
+    return ok();
+}
+
+int32_t reshape_and_cache(const void* key, const void* value, int32_t src_dtype, void* k_cache,
+                          void* v_cache, const int32_t* slot_mapping, int32_t num_tokens,
+                          int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                          int32_t num_blocks, int32_t kv_dtype, float k_scale, float v_scale,
+                          pkv_stream_t stream) {
+    if (int32_t e = check_layout_args(head_dim, block_size, kv_dtype)) return e;
+    if (src_dtype != PKV_BF16 && src_dtype != PKV_FP16)
+        return fail(PKV_ERR_ARG, "src_dtype must be bf16 or fp16");
+    if (num_kv_heads > 65535) return fail(PKV_ERR_UNSUPPORTED, "num_kv_heads must be <= 65535 (grid limit)");
+    if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks <= 0)
+        return fail(PKV_ERR_ARG, "num_tokens >= 0, num_kv_heads > 0 and num_blocks > 0 required");
+    if ((int64_t)num_blocks * block_size >= (1LL << 31))
+        return fail(PKV_ERR_ARG, "num_blocks * block_size must stay below 2^31");
+    if (head_dim != kBuiltHeadDim)
+        return fail(PKV_ERR_UNSUPPORTED, "kernels are built for head_dim 128, got %d", head_dim);
+    if (kv_dtype != PKV_FP8_E4M3 && kv_dtype != src_dtype)
+        return fail(PKV_ERR_UNSUPPORTED, "a 16-bit pool must have the source dtype");
+    if (num_tokens > 0 && (!key || !value || !k_cache || !v_cache || !slot_mapping))
+        return fail(PKV_ERR_ARG, "null pointer");
+    float k_inv = 1.0f, v_inv = 1.0f;
+    if (kv_dtype == PKV_FP8_E4M3) {
+        if (!(std::isfinite(k_scale) && k_scale > 0.f && std::isfinite(v_scale) && v_scale > 0.f))
+            return fail(PKV_ERR_ARG, "fp8 scales must be finite and positive");
+        k_inv = 1.0f / k_scale;   // IEEE fp32 division, correctly rounded
+        v_inv = 1.0f / v_scale;
+    }
+    pkv::RacArgs a{key, value, k_cache, v_cache, slot_mapping, num_tokens, num_kv_heads,
+                   block_size, num_blocks, src_dtype, kv_dtype, k_inv, v_inv};
+    (void)hipGetLastError();
+    hipError_t e = pkv::launch_reshape_and_cache(a, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "reshape_and_cache launch");
+    return ok();
+}
+
+int64_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                        int32_t max_context_len, int32_t partition_tokens) {
+    if (num_seqs < 0 || num_heads <= 0 || head_dim <= 0 || max_context_len < 0 || partition_tokens < 0)
+        return fail(PKV_ERR_ARG, "bad workspace query");
+    const int32_t part = partition_tokens ? partition_tokens : kDefaultPartitionTokens;
+    const int64_t P = (max_context_len + part - 1) / part;
+    ok();
+    if (P <= 1) return 0;
+    return (int64_t)num_seqs * num_heads * P * (head_dim + 2) * (int64_t)sizeof(float);
+}
+
+int32_t paged_attention_decode_ex(void* out, const void* q, int32_t q_dtype, const void* k_cache,
+                                  const void* v_cache, const int32_t* block_tables,
+                                  int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                  int32_t max_context_len, int32_t num_seqs, int32_t num_heads,
+                                  int32_t num_kv_heads, int32_t head_dim, float scale,
+                                  int32_t block_size, int32_t kv_dtype, float k_scale,
+                                  float v_scale, void* workspace, int64_t workspace_bytes,
+                                  const pkv_decode_opts* opts, pkv_stream_t stream) {
+    pkv_decode_opts o{0, PKV_IMPL_AUTO, 0, 0};
+    if (opts) o = *opts;
+    if (int32_t e = check_layout_args(head_dim, block_size, kv_dtype)) return e;
+    if (q_dtype != PKV_BF16 && q_dtype != PKV_FP16) return fail(PKV_ERR_ARG, "q_dtype must be bf16 or fp16");
+    if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || max_context_len < 0 || max_blocks_per_seq < 0)
+        return fail(PKV_ERR_ARG, "bad sizes");
+    if (num_seqs > 65535 || num_kv_heads > 65535) return fail(PKV_ERR_UNSUPPORTED, "num_seqs and num_kv_heads must be <= 65535 (grid limits)");
+    if (num_heads % num_kv_heads) return fail(PKV_ERR_ARG, "num_heads %d is not a multiple of num_kv_heads %d", num_heads, num_kv_heads);
+    const int32_t G = num_heads / num_kv_heads;
+    if (G > 16) return fail(PKV_ERR_UNSUPPORTED, "query heads per kv head %d > 16", G);
+    if (head_dim != kBuiltHeadDim) return fail(PKV_ERR_UNSUPPORTED, "kernels are built for head_dim 128, got %d", head_dim);
+    if (kv_dtype != PKV_FP8_E4M3 && kv_dtype != q_dtype)
+        return fail(PKV_ERR_UNSUPPORTED, "a 16-bit KV pool must have the query dtype");
+    if (!std::isfinite(scale)) return fail(PKV_ERR_ARG, "scale must be finite");
+    if (kv_dtype == PKV_FP8_E4M3 && !(std::isfinite(k_scale) && std::isfinite(v_scale)))
+        return fail(PKV_ERR_ARG, "fp8 scales must be finite");
+    if (o.impl < 0 || o.impl > 2) return fail(PKV_ERR_ARG, "impl %d unknown", o.impl);
+    if (o.impl == PKV_IMPL_VECTOR && G > 8) return fail(PKV_ERR_UNSUPPORTED, "vector kernel supports at most 8 query heads per kv head");
+    const int32_t stages = o.stages ? o.stages : (PKV_STAGE_PARTITIONS | PKV_STAGE_REDUCE);
+    if (stages & ~(PKV_STAGE_PARTITIONS | PKV_STAGE_REDUCE)) return fail(PKV_ERR_ARG, "bad stages mask");
+    const int32_t part_tokens = o.partition_tokens ? o.partition_tokens : kDefaultPartitionTokens;
+    if (part_tokens < block_size || part_tokens % block_size)
+        return fail(PKV_ERR_ARG, "partition_tokens %d must be a positive multiple of block_size %d", part_tokens, block_size);
+    if (o.num_blocks < 0) return fail(PKV_ERR_ARG, "num_blocks < 0");
+    if (num_seqs > 0 && (!out || !q || !k_cache || !v_cache || !context_lens || (max_blocks_per_seq > 0 && !block_tables)))
+        return fail(PKV_ERR_ARG, "null pointer");
+
+    const int64_t table_tokens = (int64_t)max_blocks_per_seq * block_size;
+    const int32_t ctx_cap = (int32_t)(table_tokens < max_context_len ? table_tokens : max_context_len);
+    const int32_t num_parts = (ctx_cap + part_tokens - 1) / part_tokens;
+    const int64_t need = paged_attention_workspace_bytes(num_seqs, num_heads, head_dim, ctx_cap, part_tokens);
+    if (need < 0) return (int32_t)need;
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(PKV_ERR_SIZE, "workspace needs %lld bytes, got %lld", (long long)need, (long long)workspace_bytes);
+
+    pkv::DecodeArgs a{};
+    a.out = out;
+    a.q = q;
+    a.k_cache = (const uint8_t*)k_cache;
+    a.v_cache = (const uint8_t*)v_cache;
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.ws_out = (float*)workspace;
+    a.ws_ml = need > 0 ? (float*)workspace + (int64_t)num_seqs * num_heads * num_parts * head_dim : nullptr;
+    a.max_blocks = max_blocks_per_seq;
+    a.ctx_cap = ctx_cap;
+    a.num_seqs = num_seqs;
+    a.num_heads = num_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.group = G;
+    a.part_blocks = part_tokens / block_size;
+    a.num_parts = num_parts;
+    a.num_blocks = o.num_blocks;
+    const float ks = kv_dtype == PKV_FP8_E4M3 ? k_scale : 1.0f;
+    a.qk_scale_log2 = (float)((double)scale * (double)ks * 1.4426950408889634);
+    a.out_scale = kv_dtype == PKV_FP8_E4M3 ? v_scale : 1.0f;
+
+    hipStream_t st = (hipStream_t)stream;
+    (void)hipGetLastError();
+    if (stages & PKV_STAGE_PARTITIONS) {
+        hipError_t e = pkv::launch_decode_partitions(a, q_dtype, kv_dtype, block_size, o.impl, st);
+        if (e != hipSuccess) return hip_fail(e, "paged decode launch");
+    }
+    if ((stages & PKV_STAGE_REDUCE) && num_parts > 1) {
+        hipError_t e = pkv::launch_decode_reduce(a, q_dtype, block_size, st);
+        if (e != hipSuccess) return hip_fail(e, "partition reduce launch");
+    }
+    return ok();
+}
+
+int32_t paged_attention_decode(void* out, const void* q, int32_t q_dtype, const void* k_cache,
+                               const void* v_cache, const int32_t* block_tables,
+                               int32_t max_blocks_per_seq, const int32_t* context_lens,
+                               int32_t max_context_len, int32_t num_seqs, int32_t num_heads,
+                               int32_t num_kv_heads, int32_t head_dim, float scale,
+                               int32_t block_size, int32_t kv_dtype, float k_scale, float v_scale,
+                               void* workspace, int64_t workspace_bytes, pkv_stream_t stream) {
+    return paged_attention_decode_ex(out, q, q_dtype, k_cache, v_cache, block_tables,
+                                     max_blocks_per_seq, context_lens, max_context_len, num_seqs,
+                                     num_heads, num_kv_heads, head_dim, scale, block_size,
+                                     kv_dtype, k_scale, v_scale, workspace, workspace_bytes,
+                                     nullptr, stream);
+}
+
+int32_t pkv_check_block_tables(const int32_t* block_tables, int32_t max_blocks_per_seq,
+                               const int32_t* context_lens, int32_t num_seqs, int32_t block_size,
+                               int32_t num_blocks, int32_t* scratch_dev, int64_t* bad_count,
+                               pkv_stream_t stream) {
+    if (!bad_count || !scratch_dev) return fail(PKV_ERR_ARG, "null pointer");
+    if (num_seqs < 0 || max_blocks_per_seq < 0 || num_blocks <= 0) return fail(PKV_ERR_ARG, "bad sizes");
+    if (!valid_block_size(block_size)) return fail(PKV_ERR_ARG, "block_size %d must be 16 or 32", block_size);
+    if (num_seqs > 0 && (!context_lens || (max_blocks_per_seq > 0 && !block_tables)))
+        return fail(PKV_ERR_ARG, "null pointer");
+    hipStream_t st = (hipStream_t)stream;
+    (void)hipGetLastError();
+    hipError_t e = pkv::launch_check_tables(block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                                            block_size, num_blocks, scratch_dev, st);
+    if (e != hipSuccess) return hip_fail(e, "table check launch");
+    int32_t host = 0;
+    e = hipMemcpyAsync(&host, scratch_dev, sizeof host, hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return hip_fail(e, "table check readback");
+    *bad_count = host;
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,175 @@
+// cache_ops.hip — writing new tokens into the paged pool, and the small
+// indexing kernels around it.
+//
+// Pages: "LLM inference basics and vLLM internals" (ttlab.hopto.org) §4 —
+// tokens live in fixed 16-token blocks reached through a per-request block
+// table, block 0 is reserved as the null block; vToken page
+// (gotosocial.chinng-lab-srv.dev) "KV cache basics" — each decode step only
+// appends the new token's key and value.
+#include "pkv_device.h"
+#include "pkv_launch.h"
+
+namespace pkv {
+
+// One wave per (token, kv head); lane l owns dims 2l and 2l+1 of the
+// 128-dim row.  K: dims 2l, 2l+1 are adjacent inside one 8-dim group, so one
+// 4-byte (16-bit types) or 2-byte (fp8) store.  V: the two dims live in
+// neighbouring lanes of the V row, so two element stores.
+template <int SRC, int KVT, int BS>
+__global__ __launch_bounds__(64) void reshape_and_cache_kernel(
+    const uint16_t* __restrict__ key, const uint16_t* __restrict__ value,
+    uint8_t* __restrict__ k_cache, uint8_t* __restrict__ v_cache,
+    const int32_t* __restrict__ slot_mapping, int32_t num_kv_heads,
+    int64_t num_slots, float k_inv, float v_inv) {
+    constexpr int EB = elem_bytes(KVT);
+    constexpr int64_t SUB = sub_tile_bytes(KVT);
+    constexpr int64_t TILE = SUB * (BS / kSubTokens);
+    const int t = blockIdx.x, g = blockIdx.y, lane = threadIdx.x;
+    const int64_t slot = slot_mapping[t];
+    if (slot < 0 || slot >= num_slots) return;
+    const int64_t pb = slot / BS;
+    const int row = (int)(slot % BS);
+    const int r = row % kSubTokens;
+    const int64_t base = (pb * num_kv_heads + g) * TILE + (row / kSubTokens) * SUB;
+
+    const int64_t src = ((int64_t)t * num_kv_heads + g) * kHeadDim + 2 * lane;
+    const uint32_t kw = *reinterpret_cast<const uint32_t*>(key + src);
+    const uint32_t vw = *reinterpret_cast<const uint32_t*>(value + src);
+
+    const int k0 = 2 * lane;
+    // K position of (r, k0): group c = k0/8 -> lane r + 16*(c%4), row c/4.
+    const int kc = k0 / 8, kkk = kc / 4;
+    const int k_lane = r + 16 * (kc % 4);
+    const int k_per = 2 / EB;
+    const int64_t k_off = 1024 * (kkk / k_per) + 16 * k_lane + 8 * EB * (kkk % k_per) + EB * (k0 % 8);
+    // V position of (r, k) for k = k0, k0+1: tile nt = k/16, lane k%16 + 16*(r/4).
+    const int v_per = 4 / EB;
+    const int nt = k0 / 16;
+    const int64_t v_off0 = 1024 * (nt / v_per) + 16 * ((k0 % 16) + 16 * (r / 4)) +
+                           4 * EB * (nt % v_per) + EB * (r % 4);
+    const int64_t v_off1 = v_off0 + 16;   // next dim = next lane
+
+    if constexpr (KVT == DT_FP8) {
+        const float k_lo = bits_to_f32<SRC>(kw & 0xffffu) * k_inv;
+        const float k_hi = bits_to_f32<SRC>(kw >> 16) * k_inv;
+        const float v_lo = bits_to_f32<SRC>(vw & 0xffffu) * v_inv;
+        const float v_hi = bits_to_f32<SRC>(vw >> 16) * v_inv;
+        const uint16_t kcode = (uint16_t)(f32_to_e4m3(k_lo) | (f32_to_e4m3(k_hi) << 8));
+        *reinterpret_cast<uint16_t*>(k_cache + base + k_off) = kcode;
+        v_cache[base + v_off0] = (uint8_t)f32_to_e4m3(v_lo);
+        v_cache[base + v_off1] = (uint8_t)f32_to_e4m3(v_hi);
+    } else {
+        *reinterpret_cast<uint32_t*>(k_cache + base + k_off) = kw;
+        *reinterpret_cast<uint16_t*>(v_cache + base + v_off0) = (uint16_t)(vw & 0xffffu);
+        *reinterpret_cast<uint16_t*>(v_cache + base + v_off1) = (uint16_t)(vw >> 16);
+    }
+}
+
+// slot of the newest token (position c-1) of every sequence.
+__global__ __launch_bounds__(256) void decode_slot_mapping_kernel(
+    const int32_t* __restrict__ block_tables, int32_t max_blocks,
+    const int32_t* __restrict__ context_lens, int32_t num_seqs, int32_t block_size,
+    int32_t* __restrict__ slot_mapping) {
+    const int s = blockIdx.x * blockDim.x + threadIdx.x;
+    if (s >= num_seqs) return;
+    const int c = context_lens[s];
+    if (c <= 0 || (int64_t)c > (int64_t)max_blocks * block_size) {
+        slot_mapping[s] = -1;
+        return;
+    }
+    const int pos = c - 1;
+    const int32_t pb = block_tables[(int64_t)s * max_blocks + pos / block_size];
+    slot_mapping[s] = pb * block_size + pos % block_size;
+}
+
+// Count table entries a decode would read that are outside [1, num_blocks),
+// and context lengths outside [0, max_blocks * block_size].
+__global__ __launch_bounds__(256) void check_tables_kernel(
+    const int32_t* __restrict__ block_tables, int32_t max_blocks,
+    const int32_t* __restrict__ context_lens, int32_t block_size, int32_t num_blocks,
+    int32_t* __restrict__ bad) {
+    const int s = blockIdx.y;
+    const int j = blockIdx.x * blockDim.x + threadIdx.x;
+    const int c = context_lens[s];
+    int nbad = 0;
+    if (j == 0 && (c < 0 || (int64_t)c > (int64_t)max_blocks * block_size)) nbad++;
+    const int cc = c < 0 ? 0 : (c > max_blocks * block_size ? max_blocks * block_size : c);
+    const int nblk = (cc + block_size - 1) / block_size;
+    if (j < nblk) {
+        const int32_t id = block_tables[(int64_t)s * max_blocks + j];
+        if (id < 1 || id >= num_blocks) nbad++;
+    }
+    if (nbad) atomicAdd(bad, nbad);
+}
+
+__global__ __launch_bounds__(256) void zero_i32_kernel(int32_t* p) {
+    if (threadIdx.x == 0 && blockIdx.x == 0) p[0] = 0;
+}
+
+// Fill n 16-bit (or n 8-bit when pattern_bytes == 1) elements with a pattern.
+__global__ __launch_bounds__(256) void fill_pattern_kernel(uint8_t* __restrict__ p, int64_t n_bytes,
+                                                           uint32_t pattern, int pattern_bytes) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n_bytes) return;
+    const int byte_in = (int)(i % pattern_bytes);
+    p[i] = (uint8_t)(pattern >> (8 * byte_in));
+}
+
+// ----------------------------------------------------------------- launch --
+
+template <int SRC, int KVT, int BS>
+static hipError_t launch_rac(const RacArgs& a, hipStream_t st) {
+    dim3 grid(a.num_tokens, a.num_kv_heads);
+    hipLaunchKernelGGL((reshape_and_cache_kernel<SRC, KVT, BS>), grid, dim3(64), 0, st,
+                       (const uint16_t*)a.key, (const uint16_t*)a.value, (uint8_t*)a.k_cache,
+                       (uint8_t*)a.v_cache, a.slot_mapping, a.num_kv_heads,
+                       (int64_t)a.num_blocks * BS, a.k_inv, a.v_inv);
+    return hipGetLastError();
+}
+
+template <int SRC, int KVT>
+static hipError_t launch_rac_bs(const RacArgs& a, hipStream_t st) {
+    return a.block_size == 16 ? launch_rac<SRC, KVT, 16>(a, st) : launch_rac<SRC, KVT, 32>(a, st);
+}
+
+hipError_t launch_reshape_and_cache(const RacArgs& a, hipStream_t st) {
+    if (a.num_tokens == 0) return hipSuccess;
+    if (a.src_dtype == DT_BF16) {
+        if (a.kv_dtype == DT_BF16) return launch_rac_bs<DT_BF16, DT_BF16>(a, st);
+        return launch_rac_bs<DT_BF16, DT_FP8>(a, st);
+    }
+    if (a.kv_dtype == DT_FP16) return launch_rac_bs<DT_FP16, DT_FP16>(a, st);
+    return launch_rac_bs<DT_FP16, DT_FP8>(a, st);
+}
+
+hipError_t launch_decode_slot_mapping(const int32_t* bt, int32_t max_blocks, const int32_t* ctx,
+                                      int32_t num_seqs, int32_t bs, int32_t* slots,
+                                      hipStream_t st) {
+    if (num_seqs == 0) return hipSuccess;
+    hipLaunchKernelGGL(decode_slot_mapping_kernel, dim3((num_seqs + 255) / 256), dim3(256), 0, st,
+                       bt, max_blocks, ctx, num_seqs, bs, slots);
+    return hipGetLastError();
+}
+
+hipError_t launch_check_tables(const int32_t* bt, int32_t max_blocks, const int32_t* ctx,
+                               int32_t num_seqs, int32_t bs, int32_t num_blocks, int32_t* bad,
+                               hipStream_t st) {
+    hipLaunchKernelGGL(zero_i32_kernel, dim3(1), dim3(64), 0, st, bad);
+    if (num_seqs > 0 && max_blocks > 0) {
+        dim3 grid((max_blocks + 255) / 256, num_seqs);
+        hipLaunchKernelGGL(check_tables_kernel, grid, dim3(256), 0, st, bt, max_blocks, ctx, bs,
+                           num_blocks, bad);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_pattern(void* p, int64_t n_bytes, uint32_t pattern, int pattern_bytes,
+                               hipStream_t st) {
+    if (n_bytes <= 0) return hipSuccess;
+    const int64_t blocks = (n_bytes + 255) / 256;
+    hipLaunchKernelGGL(fill_pattern_kernel, dim3((unsigned)blocks), dim3(256), 0, st,
+                       (uint8_t*)p, n_bytes, pattern, pattern_bytes);
+    return hipGetLastError();
+}
+
+}  // namespace pkv

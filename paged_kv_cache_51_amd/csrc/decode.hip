@@ -1,0 +1,368 @@
+// decode.hip — PagedAttention decode on gfx950 matrix cores, plus the
+// split-context merge.
+//
+// What is computed ("LLM inference basics and vLLM internals" §4 and "vLLM
+// internals (2)", "Block table"): for each sequence, its one new query token
+// attends over all c context tokens, whose K/V rows are found by looking up
+// the physical block of logical block t / block_size in the request's block
+// table.  GQA ("LLM inference basics..." §2): the G query heads of a group
+// share one K/V head, so one pass over a K/V tile serves all G of them.
+//
+// Work decomposition (one workgroup of NW waves per (partition, kv head,
+// sequence)):
+//   - a partition is part_blocks consecutive logical blocks; the workgroup
+//     walks its 16-token sub-tiles ("units"), wave w taking units w, w+NW, ...
+//   - per unit a wave loads the K and V sub-tiles (4 + 4 rows of 1 KiB for
+//     16-bit KV, 2 + 2 for fp8) straight into registers: the pool stores them
+//     in MFMA operand order, so no LDS staging and no shuffles are needed;
+//   - S^T = K . Q^T on four 16x16x32 MFMAs (rows = 16 tokens, columns = the
+//     G query heads padded to 16), online softmax in fp32 in the log2 domain,
+//     then O^T += V^T . P^T on eight 16x16x16 MFMAs whose B operand is the
+//     S^T result in place (same lane order);
+//   - the next unit's loads are issued before the current unit is computed
+//     (two register sets);
+//   - waves merge through LDS; a sequence that fits one partition writes its
+//     output directly, otherwise (max, normaliser, normalised output) per
+//     partition go to the workspace for decode_reduce_kernel.
+#include "pkv_device.h"
+#include "pkv_launch.h"
+
+namespace pkv {
+
+template <int KVT>
+struct UnitRegs {
+    static constexpr int R = rows_per_sub(KVT);
+    u32x4_t k[R];
+    u32x4_t v[R];
+};
+
+template <int KVT>
+__device__ __forceinline__ void load_unit(UnitRegs<KVT>& u, const uint8_t* kbase,
+                                          const uint8_t* vbase, int lane) {
+    const u32x4_t* kp = reinterpret_cast<const u32x4_t*>(kbase) + lane;
+    const u32x4_t* vp = reinterpret_cast<const u32x4_t*>(vbase) + lane;
+#pragma unroll
+    for (int r = 0; r < UnitRegs<KVT>::R; ++r) u.k[r] = kp[kWave * r];
+#pragma unroll
+    for (int r = 0; r < UnitRegs<KVT>::R; ++r) u.v[r] = vp[kWave * r];
+}
+
+// K fragment kk (dims 8*((lane>>4) + 4kk) .. +7 of token lane&15).
+template <int KVT, int QT>
+__device__ __forceinline__ u32x4_t k_frag(const UnitRegs<KVT>& u, int kk) {
+    if constexpr (KVT == DT_FP8) {
+        const u32x4_t row = u.k[kk >> 1];
+        return (kk & 1) ? e4m3x8_to_16<QT>(row[2], row[3]) : e4m3x8_to_16<QT>(row[0], row[1]);
+    } else {
+        return u.k[kk];
+    }
+}
+
+// V fragment nt (tokens 4*(lane>>4) .. +3 of dim 16*nt + (lane&15)).
+template <int KVT, int QT>
+__device__ __forceinline__ u32x2_t v_frag(const UnitRegs<KVT>& u, int nt) {
+    if constexpr (KVT == DT_FP8) {
+        return e4m3x4_to_16<QT>(u.v[nt >> 2][nt & 3]);
+    } else {
+        const u32x4_t row = u.v[nt >> 1];
+        u32x2_t r;
+        r[0] = (nt & 1) ? row[2] : row[0];
+        r[1] = (nt & 1) ? row[3] : row[1];
+        return r;
+    }
+}
+
+// One 16-token unit: logits, online-softmax update, PV accumulation.
+// tok0 = logical position of the unit's first token; ctx = context length;
+// cs = scale * k_scale * log2(e).  m is in log2 units (already scaled).
+template <int KVT, int QT>
+__device__ __forceinline__ void process_unit(const UnitRegs<KVT>& u, const u32x4_t (&qf)[4],
+                                             f32x4_t (&acc)[8], float& m, float& l, int tok0,
+                                             int ctx, float cs, int lane) {
+    f32x4_t st = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) st = mfma_16x16x32<QT>(k_frag<KVT, QT>(u, kk), qf[kk], st);
+
+    const int tb = tok0 + 4 * (lane >> 4);
+    float t[4];
+    bool valid[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        valid[i] = (tb + i) < ctx;
+        t[i] = valid[i] ? st[i] * cs : -INFINITY;
+    }
+    float bm = fmaxf(fmaxf(t[0], t[1]), fmaxf(t[2], t[3]));
+    bm = fmaxf(bm, xor_shfl(bm, 16));
+    bm = fmaxf(bm, xor_shfl(bm, 32));
+    const float mn = fmaxf(m, bm);       // finite: every unit holds a valid token
+    const float alpha = (m == -INFINITY) ? 0.f : fast_exp2(m - mn);
+    uint32_t pbits[4];
+    float psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float p = valid[i] ? fast_exp2(t[i] - mn) : 0.f;
+        pbits[i] = f32_to_bits<QT>(p);
+        psum += bits_to_f32<QT>(pbits[i]);   // normalise with the rounded weights
+    }
+    l = l * alpha + psum;
+    m = mn;
+    u32x2_t pf;
+    pf[0] = pbits[0] | (pbits[1] << 16);
+    pf[1] = pbits[2] | (pbits[3] << 16);
+    if (tok0 + kSubTokens <= ctx) {
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) {
+            acc[nt] *= alpha;
+            acc[nt] = mfma_16x16x16<QT>(v_frag<KVT, QT>(u, nt), pf, acc[nt]);
+        }
+    } else {
+        // Last unit of the context: rows past the context hold whatever the
+        // slot last held (NaN or stale data); a zero weight times NaN would
+        // still poison the sum, so zero those V elements too.
+        u32x2_t vm;
+        vm[0] = (valid[0] ? 0x0000ffffu : 0u) | (valid[1] ? 0xffff0000u : 0u);
+        vm[1] = (valid[2] ? 0x0000ffffu : 0u) | (valid[3] ? 0xffff0000u : 0u);
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) {
+            acc[nt] *= alpha;
+            acc[nt] = mfma_16x16x16<QT>(v_frag<KVT, QT>(u, nt) & vm, pf, acc[nt]);
+        }
+    }
+}
+
+template <int KVT, int QT, int BS, int NW>
+__global__ __launch_bounds__(NW * kWave) void paged_decode_mfma_kernel(const DecodeArgs a) {
+    constexpr int NSUB = BS / kSubTokens;
+    constexpr int64_t SUB = sub_tile_bytes(KVT);
+    constexpr int64_t TILE = SUB * NSUB;
+    __shared__ float sm_acc[NW][32][kWave];
+    __shared__ float sm_m[NW][16];
+    __shared__ float sm_l[NW][16];
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int part = blockIdx.x, kvh = blockIdx.y, s = blockIdx.z;
+    const int G = a.group;
+
+    int ctx = a.context_lens[s];
+    ctx = ctx < a.ctx_cap ? ctx : a.ctx_cap;
+    if (ctx <= 0) {
+        if (part == 0) {
+            uint16_t* out = reinterpret_cast<uint16_t*>(a.out) +
+                            ((int64_t)s * a.num_heads + (int64_t)kvh * G) * kHeadDim;
+            for (int e = threadIdx.x; e < G * kHeadDim; e += NW * kWave) out[e] = 0;
+        }
+        return;
+    }
+    const int n_units = (ctx + kSubTokens - 1) / kSubTokens;
+    const int units_per_part = a.part_blocks * NSUB;
+    const int u0 = part * units_per_part;
+    if (u0 >= n_units) return;
+    const int u1 = min(u0 + units_per_part, n_units);
+    const int nblk = (ctx + BS - 1) / BS;
+    const bool single = nblk <= a.part_blocks;
+
+    // Q^T fragments: lane holds head (lane & 15) of the group, 8 dims per kk.
+    const int hl = lane & 15;
+    const bool hvalid = hl < G;
+    u32x4_t qf[4];
+    {
+        const uint8_t* qrow = reinterpret_cast<const uint8_t*>(a.q) +
+                              ((int64_t)s * a.num_heads + (int64_t)kvh * G + (hvalid ? hl : 0)) *
+                                  (kHeadDim * 2);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const u32x4_t z = {0u, 0u, 0u, 0u};
+            qf[kk] = hvalid ? *reinterpret_cast<const u32x4_t*>(qrow + 16 * ((lane >> 4) + 4 * kk))
+                            : z;
+        }
+    }
+
+    f32x4_t acc[8];
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) acc[nt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+    float m = -INFINITY, l = 0.f;
+
+    const int first = u0 + w;
+    const int n_my = first < u1 ? (u1 - first + NW - 1) / NW : 0;
+    if (n_my > 0) {
+        const int32_t* bt_row = a.block_tables + (int64_t)s * a.max_blocks;
+        const uint8_t* kpool = a.k_cache + (int64_t)kvh * TILE;
+        const uint8_t* vpool = a.v_cache + (int64_t)kvh * TILE;
+        const int64_t head_stride = (int64_t)a.num_kv_heads * TILE;
+        auto load_ids = [&](int i0) -> int {
+            const int i = i0 + lane;
+            return i < n_my ? bt_row[(first + NW * i) / NSUB] : 0;
+        };
+        auto unit_offset = [&](int ids, int c0, int j) -> int64_t {
+            int pb = __builtin_amdgcn_readlane(ids, j);
+            if (a.num_blocks > 0 && (unsigned)pb >= (unsigned)a.num_blocks) pb = 0;
+            return (int64_t)pb * head_stride + ((first + NW * (c0 + j)) % NSUB) * SUB;
+        };
+        // Units in chunks of 64 per wave: lane j of `ids` holds the block
+        // id of the chunk's unit j (read back with readlane, no reload in
+        // the pipelined loop).
+        for (int c0 = 0; c0 < n_my; c0 += kWave) {
+            const int nc = min(kWave, n_my - c0);
+            const int ids = load_ids(c0);
+            UnitRegs<KVT> A, B;
+            int64_t off = unit_offset(ids, c0, 0);
+            load_unit<KVT>(A, kpool + off, vpool + off, lane);
+            int i = 0;
+            while (true) {
+                const int tok = (first + NW * (c0 + i)) * kSubTokens;
+                if (i + 1 >= nc) {
+                    process_unit<KVT, QT>(A, qf, acc, m, l, tok, ctx, a.qk_scale_log2, lane);
+                    break;
+                }
+                off = unit_offset(ids, c0, i + 1);
+                load_unit<KVT>(B, kpool + off, vpool + off, lane);
+                process_unit<KVT, QT>(A, qf, acc, m, l, tok, ctx, a.qk_scale_log2, lane);
+                ++i;
+                const int tok2 = tok + NW * kSubTokens;
+                if (i + 1 >= nc) {
+                    process_unit<KVT, QT>(B, qf, acc, m, l, tok2, ctx, a.qk_scale_log2, lane);
+                    break;
+                }
+                off = unit_offset(ids, c0, i + 1);
+                load_unit<KVT>(A, kpool + off, vpool + off, lane);
+                process_unit<KVT, QT>(B, qf, acc, m, l, tok2, ctx, a.qk_scale_log2, lane);
+                ++i;
+            }
+        }
+    }
+    // Normaliser of head (lane & 15): sum the four lanes sharing the head.
+    l += xor_shfl(l, 16);
+    l += xor_shfl(l, 32);
+
+    // ---- merge the NW waves through LDS
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sm_acc[w][nt * 4 + i][lane] = acc[nt][i];
+    if (lane < 16) {
+        sm_m[w][lane] = m;
+        sm_l[w][lane] = l;
+    }
+    __syncthreads();
+    if (!hvalid) return;
+    float M = -INFINITY;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, sm_m[ww][hl]);
+    float f[NW];
+    float L = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) {
+        const float mw = sm_m[ww][hl];
+        f[ww] = (mw == -INFINITY) ? 0.f : fast_exp2(mw - M);
+        L += f[ww] * sm_l[ww][hl];
+    }
+    const float invL = 1.0f / L;
+    const int hq = kvh * G + hl;
+    const int64_t pidx = ((int64_t)s * a.num_heads + hq) * a.num_parts + part;
+#pragma unroll
+    for (int k = 0; k < 32 / NW; ++k) {
+        const int idx = w + NW * k;
+        const int dim = 16 * (idx >> 2) + 4 * (lane >> 4) + (idx & 3);
+        float o = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) o += f[ww] * sm_acc[ww][idx][lane];
+        if (single) {
+            uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
+            out[((int64_t)s * a.num_heads + hq) * kHeadDim + dim] =
+                f32_to_bits<QT>(o * invL * a.out_scale);
+        } else {
+            a.ws_out[pidx * kHeadDim + dim] = o * invL;
+        }
+    }
+    if (!single && w == 0 && lane < 16) {
+        a.ws_ml[pidx * 2 + 0] = M;
+        a.ws_ml[pidx * 2 + 1] = L;
+    }
+}
+
+// Merge the partitions of every multi-partition sequence: with per-partition
+// max m_p (log2 units), normaliser l_p and normalised output o_p,
+//   out = sum_p 2^(m_p - M) l_p o_p / sum_p 2^(m_p - M) l_p,  M = max_p m_p.
+// One wave per (query head, sequence); lane owns dims 2*lane, 2*lane+1.
+template <int QT, int BS>
+__global__ __launch_bounds__(kWave) void decode_reduce_kernel(const DecodeArgs a) {
+    const int hq = blockIdx.x, s = blockIdx.y, lane = threadIdx.x;
+    int ctx = a.context_lens[s];
+    ctx = ctx < a.ctx_cap ? ctx : a.ctx_cap;
+    if (ctx <= 0) return;
+    const int nblk = (ctx + BS - 1) / BS;
+    const int np = (nblk + a.part_blocks - 1) / a.part_blocks;
+    if (np <= 1) return;
+    const int64_t base = ((int64_t)s * a.num_heads + hq) * a.num_parts;
+    float M = -INFINITY;
+    for (int p = lane; p < np; p += kWave) M = fmaxf(M, a.ws_ml[(base + p) * 2]);
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) M = fmaxf(M, xor_shfl(M, d));
+    float L = 0.f, o0 = 0.f, o1 = 0.f;
+    for (int p = 0; p < np; ++p) {
+        const float mp = a.ws_ml[(base + p) * 2];
+        const float lp = a.ws_ml[(base + p) * 2 + 1];
+        const float fct = fast_exp2(mp - M) * lp;
+        const float2 op = *reinterpret_cast<const float2*>(a.ws_out + (base + p) * kHeadDim + 2 * lane);
+        L += fct;
+        o0 += fct * op.x;
+        o1 += fct * op.y;
+    }
+    const float sc = a.out_scale / L;
+    uint16_t* out = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)s * a.num_heads + hq) * kHeadDim;
+    const uint32_t packed = (uint32_t)f32_to_bits<QT>(o0 * sc) | ((uint32_t)f32_to_bits<QT>(o1 * sc) << 16);
+    *reinterpret_cast<uint32_t*>(out + 2 * lane) = packed;
+}
+
+// ----------------------------------------------------------------- launch --
+
+constexpr int kWavesPerGroup = 4;
+
+template <int KVT, int QT, int BS>
+static hipError_t launch_mfma(const DecodeArgs& a, hipStream_t st) {
+    dim3 grid(a.num_parts, a.num_kv_heads, a.num_seqs);
+    hipLaunchKernelGGL((paged_decode_mfma_kernel<KVT, QT, BS, kWavesPerGroup>), grid,
+                       dim3(kWavesPerGroup * kWave), 0, st, a);
+    return hipGetLastError();
+}
+
+template <int KVT, int QT>
+static hipError_t launch_mfma_bs(const DecodeArgs& a, int bs, hipStream_t st) {
+    return bs == 16 ? launch_mfma<KVT, QT, 16>(a, st) : launch_mfma<KVT, QT, 32>(a, st);
+}
+
+hipError_t launch_decode_vector(const DecodeArgs& a, int q_dtype, int kv_dtype, int block_size,
+                                hipStream_t st);
+
+hipError_t launch_decode_partitions(const DecodeArgs& a, int q_dtype, int kv_dtype,
+                                    int block_size, int impl, hipStream_t st) {
+    if (a.num_seqs == 0 || a.num_parts == 0) return hipSuccess;
+    if (impl == 2) return launch_decode_vector(a, q_dtype, kv_dtype, block_size, st);
+    if (q_dtype == DT_BF16) {
+        if (kv_dtype == DT_BF16) return launch_mfma_bs<DT_BF16, DT_BF16>(a, block_size, st);
+        return launch_mfma_bs<DT_FP8, DT_BF16>(a, block_size, st);
+    }
+    if (kv_dtype == DT_FP16) return launch_mfma_bs<DT_FP16, DT_FP16>(a, block_size, st);
+    return launch_mfma_bs<DT_FP8, DT_FP16>(a, block_size, st);
+}
+
+hipError_t launch_decode_reduce(const DecodeArgs& a, int q_dtype, int block_size,
+                                hipStream_t st) {
+    if (a.num_seqs == 0 || a.num_parts <= 1) return hipSuccess;
+    dim3 grid(a.num_heads, a.num_seqs);
+    if (q_dtype == DT_BF16) {
+        if (block_size == 16)
+            hipLaunchKernelGGL((decode_reduce_kernel<DT_BF16, 16>), grid, dim3(kWave), 0, st, a);
+        else
+            hipLaunchKernelGGL((decode_reduce_kernel<DT_BF16, 32>), grid, dim3(kWave), 0, st, a);
+    } else {
+        if (block_size == 16)
+            hipLaunchKernelGGL((decode_reduce_kernel<DT_FP16, 16>), grid, dim3(kWave), 0, st, a);
+        else
+            hipLaunchKernelGGL((decode_reduce_kernel<DT_FP16, 32>), grid, dim3(kWave), 0, st, a);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace pkv

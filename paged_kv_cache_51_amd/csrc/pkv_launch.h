@@ -1,0 +1,65 @@
+// pkv_launch.h — host-side launchers between the C ABI (api.hip) and the
+// kernels.  Argument checking happens in api.hip; launchers assume valid
+// arguments.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+struct RacArgs {
+    const void* key;
+    const void* value;
+    void* k_cache;
+    void* v_cache;
+    const int32_t* slot_mapping;
+    int32_t num_tokens;
+    int32_t num_kv_heads;
+    int32_t block_size;
+    int32_t num_blocks;
+    int32_t src_dtype;
+    int32_t kv_dtype;
+    float k_inv;
+    float v_inv;
+};
+
+struct DecodeArgs {
+    void* out;
+    const void* q;
+    const uint8_t* k_cache;
+    const uint8_t* v_cache;
+    const int32_t* block_tables;
+    const int32_t* context_lens;
+    float* ws_out;         // [S][H][P][128] partial outputs (normalised)
+    float* ws_ml;          // [S][H][P][2]   (max in log2 units, normaliser)
+    int32_t max_blocks;    // block-table row length
+    int32_t ctx_cap;       // context clamp: min(max_context_len, max_blocks*bs)
+    int32_t num_seqs;
+    int32_t num_heads;
+    int32_t num_kv_heads;
+    int32_t group;         // num_heads / num_kv_heads
+    int32_t part_blocks;   // blocks per partition
+    int32_t num_parts;     // partitions launched per (seq, kv head)
+    int32_t num_blocks;    // pool size for id clamping (0 = unchecked)
+    float qk_scale_log2;   // scale * k_scale * log2(e)
+    float out_scale;       // v_scale for fp8 pools, else 1
+};
+
+hipError_t launch_reshape_and_cache(const RacArgs& a, hipStream_t st);
+hipError_t launch_decode_slot_mapping(const int32_t* bt, int32_t max_blocks, const int32_t* ctx,
+                                      int32_t num_seqs, int32_t bs, int32_t* slots,
+                                      hipStream_t st);
+hipError_t launch_check_tables(const int32_t* bt, int32_t max_blocks, const int32_t* ctx,
+                               int32_t num_seqs, int32_t bs, int32_t num_blocks, int32_t* bad,
+                               hipStream_t st);
+hipError_t launch_fill_pattern(void* p, int64_t n_bytes, uint32_t pattern, int pattern_bytes,
+                               hipStream_t st);
+
+// Partition kernel (matrix-core or vector implementation) and the merge.
+hipError_t launch_decode_partitions(const DecodeArgs& a, int q_dtype, int kv_dtype,
+                                    int block_size, int impl, hipStream_t st);
+hipError_t launch_decode_reduce(const DecodeArgs& a, int q_dtype, int block_size,
+                                hipStream_t st);
+
+}  // namespace pkv

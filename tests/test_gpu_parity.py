@@ -1,0 +1,361 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bars (set for this build from the method's arithmetic): slot mapping and
+reshape_and_cache bit-exact (whole-pool byte compare); decode attention
+max-abs error <= 2e-2 for bf16/fp16 KV and <= 6e-2 for fp8 KV, against the
+fp64 oracle reading the same pool.  Exact invariants of the paging scheme
+("LLM inference basics and vLLM internals" §4, "vLLM internals (2)" "Block
+table" and "Sharing") are checked bitwise on the GPU output: relabelling
+physical blocks, and sharing prefix blocks instead of private copies.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests import pools
+
+pkv = pytest.importorskip("paged_kv_cache_51_amd")
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+D = 128
+TOL = {oracle.BF16: 2e-2, oracle.FP16: 2e-2, oracle.FP8: 6e-2}
+
+
+def log(*a):
+    print(*a, flush=True)
+
+
+def dev16(bits, dtype):
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.view(torch.bfloat16 if dtype == oracle.BF16 else torch.float16).to(DEV)
+
+
+def dev8(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def devi(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(DEV)
+
+
+def gpu_decode(q_bits, q_dtype, kp, vp, kv_dtype, bt, ctx, Hkv, bs, scale, ks=1.0, vs=1.0,
+               part=0, impl=0, num_blocks=0, max_ctx=None):
+    q = dev16(q_bits, q_dtype)
+    out = torch.full_like(q, float("nan"))
+    mc = int(max(ctx)) if max_ctx is None else max_ctx
+    kd = kp if torch.is_tensor(kp) else dev8(kp)
+    vd = vp if torch.is_tensor(vp) else dev8(vp)
+    pkv.paged_attention_decode(out, q, kd, vd, devi(bt), devi(ctx), mc, Hkv, bs, kv_dtype,
+                               scale, ks, vs, partition_tokens=part, impl=impl,
+                               num_blocks=num_blocks)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy().astype(np.float64)
+
+
+def make_case(lengths, H, Hkv, bs, kv_dtype, q_dtype, seed=0, num_blocks=None, ks=1.0, vs=1.0):
+    _, r_perm, _, r_val = workloads.streams(seed)
+    tabs = workloads.build_tables(lengths, bs, r_perm, num_blocks=num_blocks)
+    kb = [workloads.normal_bits(r_val, (int(c), Hkv, D), q_dtype) for c in lengths]
+    vb = [workloads.normal_bits(r_val, (int(c), Hkv, D), q_dtype) for c in lengths]
+    q = workloads.normal_bits(r_val, (len(lengths), H, D), q_dtype)
+    kp, vp = pools.write_contiguous(kb, vb, tabs.block_tables, tabs.context_lens, Hkv, D, bs,
+                                    tabs.num_blocks, kv_dtype, q_dtype, ks, vs)
+    return tabs, q, kp, vp
+
+
+def check(got, want, kv_dtype, what):
+    err = np.abs(got - want)
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    log(f"  {what}: max-abs {err.max():.3e} mean-abs {err.mean():.3e}")
+    assert err.max() <= TOL[kv_dtype], what
+
+
+SCALE = float(np.float32(1.0 / np.sqrt(D)))
+
+
+# ------------------------------------------------------------ indexing ----
+
+@pytest.mark.parametrize("bs", [16, 32])
+def test_slot_mapping_bit_exact(bs):
+    log(f"slot mapping bs={bs}")
+    cfg, tabs, _, _ = workloads.make("qwen15b", block_size=bs)
+    ctx = tabs.context_lens.copy()
+    ctx[3] = 0                                          # empty context
+    ctx[5] = tabs.block_tables.shape[1] * bs + 1        # past the table
+    got = pkv.decode_slot_mapping(devi(tabs.block_tables), devi(ctx), bs).cpu().numpy()
+    want = oracle.decode_slots(tabs.block_tables, ctx, bs)
+    assert np.array_equal(got.astype(np.int64), want)
+    assert got[3] == -1 and got[5] == -1
+
+
+def test_check_block_tables():
+    log("check block tables")
+    cfg, tabs, _, _ = workloads.make("qwen15b")
+    bt, ctx = tabs.block_tables.copy(), tabs.context_lens.copy()
+    assert pkv.check_block_tables(devi(bt), devi(ctx), 16, tabs.num_blocks) == 0
+    bt[2, 0] = 0                                  # null block inside the context
+    bt[4, (ctx[4] - 1) // 16] = tabs.num_blocks   # out of range, last used entry
+    bt[6, -1] = -5 if (ctx[6] + 15) // 16 < bt.shape[1] else bt[6, -1]   # unused entry: fine
+    ctx[7] = -1
+    assert pkv.check_block_tables(devi(bt), devi(ctx), 16, tabs.num_blocks) == 3
+
+
+# ---------------------------------------------------- reshape_and_cache ----
+
+@pytest.mark.parametrize("src,kv,bs", [
+    (oracle.BF16, oracle.BF16, 16), (oracle.FP16, oracle.FP16, 16),
+    (oracle.BF16, oracle.BF16, 32), (oracle.BF16, oracle.FP8, 16),
+    (oracle.FP16, oracle.FP8, 32),
+])
+def test_reshape_and_cache_bit_exact(src, kv, bs):
+    log(f"reshape_and_cache src={src} kv={kv} bs={bs}")
+    rng = np.random.default_rng(21)
+    Hkv, nb = 2, 40
+    n = oracle.layer_pool_bytes(nb, Hkv, D, bs, kv)
+    k0 = rng.integers(0, 256, n, dtype=np.uint8)          # sentinel background
+    v0 = rng.integers(0, 256, n, dtype=np.uint8)
+    T = 256
+    # distinct slots: two skipped (-1, past the pool), both pool edges, and
+    # T-4 drawn from the interior
+    inner = 1 + rng.permutation(nb * bs - 2)[:T - 4]
+    slots = np.concatenate([[-1, nb * bs, 0, nb * bs - 1], inner]).astype(np.int64)
+    if kv == oracle.FP8 and src == oracle.BF16:
+        allbits = np.arange(65536, dtype=np.uint16)
+        fin = allbits[np.isfinite((allbits.astype(np.uint32) << 16).view(np.float32))]
+        key = np.resize(rng.permutation(fin), (T, Hkv, D)).astype(np.uint16)
+    else:
+        key = workloads.normal_bits(rng, (T, Hkv, D), src)
+    val = workloads.normal_bits(rng, (T, Hkv, D), src)
+    ks, vs = (0.05, 1.0 / 448) if kv == oracle.FP8 else (1.0, 1.0)
+    kd, vd = dev8(k0), dev8(v0)
+    pkv.reshape_and_cache(dev16(key, src), dev16(val, src), kd, vd, devi(slots), bs, nb, kv,
+                          ks, vs)
+    torch.cuda.synchronize()
+    kw, vw = oracle.reshape_and_cache(key, val, src, k0, v0, slots, bs, nb, kv, ks, vs)
+    gk, gv = kd.cpu().numpy(), vd.cpu().numpy()
+    assert np.array_equal(gk, kw), f"K pool differs at {np.flatnonzero(gk != kw)[:8]}"
+    assert np.array_equal(gv, vw), f"V pool differs at {np.flatnonzero(gv != vw)[:8]}"
+
+
+def test_fp8_encoder_exhaustive_fp32_sweep():
+    # every fp32 bit pattern class that matters: all bf16 values times two
+    # scales, plus random fp32, written as fp8 by the GPU and the oracle.
+    log("fp8 encoder sweep")
+    rng = np.random.default_rng(5)
+    Hkv, bs = 1, 16
+    T = 512
+    nb = T // bs + 1
+    n = oracle.layer_pool_bytes(nb, Hkv, D, bs, oracle.FP8)
+    for scale in (1.0, 0.0123):
+        bits = rng.integers(0, 65536, (T, Hkv, D), dtype=np.uint16)
+        bits[(bits & 0x7F80) == 0x7F80] = 0x3F80            # drop inf/NaN inputs
+        slots = np.arange(T, dtype=np.int64) + bs
+        k0 = np.zeros(n, np.uint8)
+        kd, vd = dev8(k0), dev8(k0.copy())
+        pkv.reshape_and_cache(dev16(bits, oracle.BF16), dev16(bits, oracle.BF16), kd, vd,
+                              devi(slots), bs, nb, oracle.FP8, scale, scale)
+        torch.cuda.synchronize()
+        kw, vw = oracle.reshape_and_cache(bits, bits, oracle.BF16, k0, k0, slots, bs, nb,
+                                          oracle.FP8, scale, scale)
+        assert np.array_equal(kd.cpu().numpy(), kw)
+        assert np.array_equal(vd.cpu().numpy(), vw)
+
+
+# --------------------------------------------------------------- decode ----
+
+@pytest.mark.parametrize("kv,q,bs", [
+    (oracle.BF16, oracle.BF16, 16), (oracle.FP16, oracle.FP16, 16),
+    (oracle.BF16, oracle.BF16, 32), (oracle.FP8, oracle.BF16, 16),
+    (oracle.FP8, oracle.FP16, 32),
+])
+@pytest.mark.parametrize("part", [16, 32, 256, 512, 4096])
+def test_decode_tiny(kv, q, bs, part):
+    if part % bs:
+        pytest.skip("partition must be a multiple of the block size")
+    log(f"decode tiny kv={kv} q={q} bs={bs} part={part}")
+    lengths = [1, 17, 64, 200]
+    ks, vs = (0.02, 0.03) if kv == oracle.FP8 else (1.0, 1.0)
+    tabs, qb, kp, vp = make_case(lengths, 12, 2, bs, kv, q, num_blocks=64 if bs == 16 else 40,
+                                 ks=ks, vs=vs)
+    want = oracle.paged_decode(qb, q, kp, vp, kv, tabs.block_tables, tabs.context_lens, 2, bs,
+                               SCALE, ks, vs)
+    got = gpu_decode(qb, q, kp, vp, kv, tabs.block_tables, tabs.context_lens, 2, bs, SCALE,
+                     ks, vs, part=part, num_blocks=tabs.num_blocks)
+    check(got, want, kv, f"tiny part={part}")
+
+
+@pytest.mark.parametrize("H,Hkv", [(4, 4), (8, 2), (28, 4), (16, 2), (32, 2)])
+def test_decode_group_sizes(H, Hkv):
+    log(f"decode group sizes H={H} Hkv={Hkv}")
+    lengths = [5, 16, 33, 130, 300, 47]
+    tabs, qb, kp, vp = make_case(lengths, H, Hkv, 16, oracle.BF16, oracle.BF16, seed=3)
+    want = oracle.paged_decode(qb, oracle.BF16, kp, vp, oracle.BF16, tabs.block_tables,
+                               tabs.context_lens, Hkv, 16, SCALE)
+    for part in (64, 512):
+        got = gpu_decode(qb, oracle.BF16, kp, vp, oracle.BF16, tabs.block_tables,
+                         tabs.context_lens, Hkv, 16, SCALE, part=part,
+                         num_blocks=tabs.num_blocks)
+        check(got, want, oracle.BF16, f"G={H // Hkv} part={part}")
+
+
+def test_decode_zero_and_clamped_context():
+    log("decode zero / clamped context")
+    lengths = [0, 40, 1]
+    tabs, qb, kp, vp = make_case(lengths, 8, 2, 16, oracle.BF16, oracle.BF16, seed=4)
+    got = gpu_decode(qb, oracle.BF16, kp, vp, oracle.BF16, tabs.block_tables,
+                     tabs.context_lens, 2, 16, SCALE, part=16, num_blocks=tabs.num_blocks)
+    assert np.array_equal(got[0], np.zeros((8, D)))
+    want = oracle.paged_decode(qb, oracle.BF16, kp, vp, oracle.BF16, tabs.block_tables,
+                               tabs.context_lens, 2, 16, SCALE)
+    check(got, want, oracle.BF16, "zero ctx")
+    # max_context_len below a sequence's length clamps it (memory-safe)
+    got = gpu_decode(qb, oracle.BF16, kp, vp, oracle.BF16, tabs.block_tables,
+                     tabs.context_lens, 2, 16, SCALE, part=16, num_blocks=tabs.num_blocks,
+                     max_ctx=20)
+    clamped = np.minimum(tabs.context_lens, 20).astype(np.int32)
+    want = oracle.paged_decode(qb, oracle.BF16, kp, vp, oracle.BF16, tabs.block_tables,
+                               clamped, 2, 16, SCALE)
+    check(got, want, oracle.BF16, "clamped ctx")
+
+
+def test_decode_c1_returns_v0_exactly():
+    # closed form: one token -> the output is that token's V (rounded once)
+    log("decode c=1")
+    tabs, qb, kp, vp = make_case([1] * 8, 8, 2, 16, oracle.BF16, oracle.BF16, seed=8)
+    got = gpu_decode(qb, oracle.BF16, kp, vp, oracle.BF16, tabs.block_tables,
+                     tabs.context_lens, 2, 16, SCALE, num_blocks=tabs.num_blocks)
+    want = oracle.paged_decode(qb, oracle.BF16, kp, vp, oracle.BF16, tabs.block_tables,
+                               tabs.context_lens, 2, 16, SCALE)
+    assert np.array_equal(got, want)
+
+
+def test_decode_fp8_every_code():
+    # c = 1 with v_scale 1: the output is the decoded code itself, so every
+    # finite E4M3 code passes through the kernel's fp8 -> 16-bit conversion.
+    log("decode fp8 every code")
+    S, Hkv, H, bs = 16, 1, 1, 16
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    nb = S + 1
+    n = oracle.layer_pool_bytes(nb, Hkv, D, bs, oracle.FP8)
+    kp = np.zeros(n, np.uint8)
+    vp = np.zeros(n, np.uint8)
+    bt = np.arange(1, S + 1, dtype=np.int32)[:, None]
+    ctx = np.ones(S, np.int32)
+    vals = np.resize(codes, S * D).reshape(S, D)
+    for s in range(S):
+        for k in range(D):
+            vp[oracle.pool_offset(s + 1, 0, 0, k, 1, Hkv, D, bs, oracle.FP8)] = vals[s, k]
+    qb = np.zeros((S, H, D), np.uint16)
+    for qdt in (oracle.BF16, oracle.FP16):
+        got = gpu_decode(qb, qdt, kp, vp, oracle.FP8, bt, ctx, Hkv, bs, SCALE, 1.0, 1.0,
+                         num_blocks=nb)
+        want = oracle.e4m3_table()[vals]
+        assert np.array_equal(got[:, 0, :], want)
+
+
+def _relabel(pool, perm, Hkv, bs, eb):
+    tile = Hkv * bs * D * eb
+    src = pool.reshape(len(perm), tile)
+    out = np.empty_like(src)
+    out[perm] = src
+    return out.reshape(-1)
+
+
+@pytest.mark.parametrize("kv", [oracle.BF16, oracle.FP8])
+def test_decode_permutation_bitwise(kv):
+    log(f"decode permutation kv={kv}")
+    lengths = [3, 31, 70, 128, 257, 600]
+    tabs, qb, kp, vp = make_case(lengths, 14, 2, 16, kv, oracle.BF16, seed=9, ks=0.05,
+                                 vs=0.05)
+    base = gpu_decode(qb, oracle.BF16, kp, vp, kv, tabs.block_tables, tabs.context_lens, 2, 16,
+                      SCALE, 0.05, 0.05, part=64, num_blocks=tabs.num_blocks)
+    nb = tabs.num_blocks
+    perm = np.concatenate([[0], 1 + np.random.default_rng(1).permutation(nb - 1)])
+    eb = oracle.elem_bytes(kv)
+    moved = gpu_decode(qb, oracle.BF16, _relabel(kp, perm, 2, 16, eb),
+                       _relabel(vp, perm, 2, 16, eb), kv, perm[tabs.block_tables].astype(np.int32),
+                       tabs.context_lens, 2, 16, SCALE, 0.05, 0.05, part=64, num_blocks=nb)
+    assert np.array_equal(base, moved)
+
+
+def test_decode_shared_prefix_bitwise():
+    # seq 1 reads its first 20 blocks through seq 0's physical blocks
+    # (ref_cnt 2), seq 2 holds private copies; same q, same logical K/V.
+    log("decode shared prefix")
+    Hkv, H, bs, c = 2, 8, 16, 20 * 16 + 9
+    r = np.random.default_rng(12)
+    k = workloads.normal_bits(r, (c, Hkv, D), oracle.BF16)
+    v = workloads.normal_bits(r, (c, Hkv, D), oracle.BF16)
+    q1 = workloads.normal_bits(r, (1, H, D), oracle.BF16)
+    nblk = -(-c // bs)
+    ids = 1 + np.random.default_rng(2).permutation(3 * nblk)
+    bt = np.zeros((3, nblk), np.int32)
+    bt[0] = ids[:nblk]
+    bt[1, :20] = bt[0, :20]
+    bt[1, 20:] = ids[nblk:nblk + nblk - 20]
+    bt[2] = ids[2 * nblk:3 * nblk]
+    ctx = np.full(3, c, np.int32)
+    nb = 3 * nblk + 1
+    kp, vp = pools.write_contiguous([k, k, k], [v, v, v], bt, ctx, Hkv, D, bs, nb, oracle.BF16,
+                                    oracle.BF16)
+    q = np.concatenate([q1, q1, q1])
+    for part in (32, 512):
+        got = gpu_decode(q, oracle.BF16, kp, vp, oracle.BF16, bt, ctx, Hkv, bs, SCALE,
+                         part=part, num_blocks=nb)
+        assert np.array_equal(got[0], got[1]) and np.array_equal(got[0], got[2])
+
+
+def test_decode_step_tiny():
+    """One decode step of the tiny workload: slots from the tables, cache
+    write of the 4 new tokens, then attention — GPU vs oracle end to end."""
+    log("decode step tiny")
+    cfg, tabs, qb, r_val = workloads.make("tiny")
+    Hkv, bs = cfg.num_kv_heads, cfg.block_size
+    ctx = tabs.context_lens
+    # history: every token but the newest, in a NaN pool
+    hist = [workloads.normal_bits(r_val, (int(c) - 1, Hkv, D), oracle.BF16) for c in ctx]
+    histv = [workloads.normal_bits(r_val, (int(c) - 1, Hkv, D), oracle.BF16) for c in ctx]
+    kp, vp = pools.write_contiguous(hist, histv, tabs.block_tables, ctx - 1, Hkv, D, bs,
+                                    tabs.num_blocks, oracle.BF16, oracle.BF16)
+    newk = workloads.normal_bits(r_val, (len(ctx), Hkv, D), oracle.BF16)
+    newv = workloads.normal_bits(r_val, (len(ctx), Hkv, D), oracle.BF16)
+    # oracle step
+    slots = oracle.decode_slots(tabs.block_tables, ctx, bs)
+    assert [int(s) % bs for s in slots] == [0, 0, 15, 7]       # block-boundary cases
+    okp, ovp = oracle.reshape_and_cache(newk, newv, oracle.BF16, kp, vp, slots, bs,
+                                        tabs.num_blocks, oracle.BF16)
+    want = oracle.paged_decode(qb, oracle.BF16, okp, ovp, oracle.BF16, tabs.block_tables, ctx,
+                               Hkv, bs, SCALE)
+    # GPU step
+    kd, vd = dev8(kp), dev8(vp)
+    bt_d, ctx_d = devi(tabs.block_tables), devi(ctx)
+    sl = pkv.decode_slot_mapping(bt_d, ctx_d, bs)
+    pkv.reshape_and_cache(dev16(newk, oracle.BF16), dev16(newv, oracle.BF16), kd, vd, sl, bs,
+                          tabs.num_blocks, oracle.BF16)
+    q = dev16(qb, oracle.BF16)
+    out = torch.empty_like(q)
+    pkv.paged_attention_decode(out, q, kd, vd, bt_d, ctx_d, int(ctx.max()), Hkv, bs,
+                               oracle.BF16, SCALE, num_blocks=tabs.num_blocks)
+    torch.cuda.synchronize()
+    assert np.array_equal(sl.cpu().numpy().astype(np.int64), slots)
+    assert np.array_equal(kd.cpu().numpy(), okp) and np.array_equal(vd.cpu().numpy(), ovp)
+    check(out.float().cpu().numpy().astype(np.float64), want, oracle.BF16, "tiny step")
+
+
+def test_null_block_poison():
+    log("null block poison")
+    pool = pkv.KVPool.allocate(2, 8, 2, D, 16, pkv.BF16)
+    for t in pool.k_layers + pool.v_layers:
+        t.zero_()
+    pool.poison_null_block()
+    torch.cuda.synchronize()
+    tile = 2 * 16 * D * 2
+    for t in pool.k_layers + pool.v_layers:
+        h = t.cpu().numpy()
+        assert (h[:tile].view(np.uint16) == 0x7FC0).all()
+        assert (h[tile:] == 0).all()
+    pool.close()
