@@ -125,8 +125,11 @@ def main():
     bt = torch.from_numpy(tabs.block_tables).to(dev)
     cl = torch.from_numpy(ctx).to(dev)
     slots = torch.empty(S, dtype=torch.int32, device=dev)
-    ws_n = pkv.workspace_bytes(S, H, D, max_ctx, part)
+    part_resolved = part or pkv.default_partition_tokens(S, Hkv, max_ctx, bs)
+    ws_n = pkv.workspace_bytes(S, H, Hkv, D, max_ctx, bs, part_resolved)
     ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=dev)
+    plan = torch.empty(pkv.plan_bytes(S, Hkv, max_ctx, bs, part_resolved), dtype=torch.uint8,
+                       device=dev)
     assert pkv.check_block_tables(bt, cl, bs, nb) == 0
     torch.cuda.synchronize()
     print(f"[bench] inputs resident in {time.time() - t0:.1f}s "
@@ -136,7 +139,9 @@ def main():
     scale = float(np.float32(1.0 / np.sqrt(D)))
 
     def step(ev=None):
+        # per-step work shared by all layers: new-token slots and the work plan
         pkv.decode_slot_mapping(bt, cl, bs, slot_mapping=slots, stream=stream)
+        pkv.build_plan(cl, max_ctx, bt.shape[1], Hkv, bs, part_resolved, plan=plan, stream=stream)
         for layer in range(L):
             pkv.reshape_and_cache(newk[layer], newv[layer], kpools[layer], vpools[layer], slots,
                                   bs, nb, kv_dtype, ks, vs, stream=stream)
@@ -144,15 +149,16 @@ def main():
                 ev[layer][0].record(stream)
             pkv.paged_attention_decode(outs[layer], qs[layer], kpools[layer], vpools[layer], bt,
                                        cl, max_ctx, Hkv, bs, kv_dtype, scale, ks, vs,
-                                       workspace=ws, partition_tokens=part, impl=impl,
-                                       stages=pkv.STAGE_PARTITIONS, num_blocks=nb,
+                                       workspace=ws, partition_tokens=part_resolved, impl=impl,
+                                       stages=pkv.STAGE_PARTITIONS, num_blocks=nb, plan=plan,
                                        stream=stream)
             if ev is not None:
                 ev[layer][1].record(stream)
             pkv.paged_attention_decode(outs[layer], qs[layer], kpools[layer], vpools[layer], bt,
                                        cl, max_ctx, Hkv, bs, kv_dtype, scale, ks, vs,
-                                       workspace=ws, partition_tokens=part, impl=impl,
-                                       stages=pkv.STAGE_REDUCE, num_blocks=nb, stream=stream)
+                                       workspace=ws, partition_tokens=part_resolved, impl=impl,
+                                       stages=pkv.STAGE_REDUCE, num_blocks=nb, plan=plan,
+                                       stream=stream)
 
     for _ in range(args.warmup):
         step()
@@ -178,7 +184,7 @@ def main():
     gbs = step_bytes / (step_ms * 1e-3) / 1e9
     launch_bytes = kv_bytes + qo_bytes
     achieved = launch_bytes / (dec_avg_ms * 1e-3) / 1e9
-    traffic_key = f"{args.config}-{kv_dtype}-bs{bs}-part{part}-impl{impl}"
+    traffic_key = f"{args.config}-{kv_dtype}-bs{bs}-part{part_resolved}-impl{impl}"
     traffic = measured_traffic(traffic_key)
     print(f"[bench] step {step_ms:.3f} ms, {gbs:.0f} GB/s; partition kernel "
           f"{dec_avg_ms * 1e3:.1f} us avg, {achieved:.0f} GB/s ({achieved / PEAK_HBM_GBS:.1%})",
@@ -224,7 +230,7 @@ def main():
             "block_size": bs,
             "kv_dtype": dt_name[kv_dtype],
             "mean_context": float(ctx.mean()),
-            "partition_tokens": part or 512,
+            "partition_tokens": part_resolved,
             "impl": args.impl,
             "parallelism": "single GPU",
         },

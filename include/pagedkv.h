@@ -215,20 +215,55 @@ enum {
 };
 
 typedef struct {
-    int32_t partition_tokens; /* context split size; 0 = library default
-                                 (512); must be a multiple of block_size */
+    int32_t partition_tokens; /* context split size; 0 = the library default
+                                 (pkv_default_partition_tokens); must be a
+                                 multiple of block_size */
     int32_t impl;             /* PKV_IMPL_* */
     int32_t stages;           /* PKV_STAGE_* mask; 0 = both */
     int32_t num_blocks;       /* pool size for id clamping; 0 = unchecked */
+    const void* plan;         /* device plan from paged_attention_plan built
+                                 for the same context_lens, max_context_len,
+                                 max_blocks_per_seq, num_kv_heads, block_size
+                                 and partition_tokens; NULL = build one in
+                                 the workspace */
 } pkv_decode_opts;
 
-/* Workspace bytes for a decode call: per (sequence, query head, partition)
- * one running max, one normaliser and head_dim fp32 partial outputs, with
- * P = ceil(max_context_len / partition_tokens).  Zero when P == 1. */
+/* Default context split.  A sequence's context is cut into partitions of
+ * this many tokens only as far as needed to give the GPU about four
+ * workgroups per compute unit in total (num_seqs * num_kv_heads *
+ * partitions); partial results written while the KV stream is being read
+ * cost far more than their size, so larger partitions are preferred.
+ * Depends on the current device's CU count.  Negative on a bad argument. */
+int32_t pkv_default_partition_tokens(int32_t num_seqs, int32_t num_kv_heads,
+                                     int32_t max_context_len,
+                                     int32_t block_size);
+
+/* Workspace bytes for a decode call: the work plan, plus — when a sequence
+ * can span several partitions (P = ceil(max_context_len / partition) > 1)
+ * — per (sequence, kv head, partition) the group's head_dim fp32 partial
+ * outputs and one 128-byte line of maxima and normalisers.  With a caller
+ * plan (opts->plan) the plan part is not used. */
 int64_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_heads,
-                                        int32_t head_dim,
+                                        int32_t num_kv_heads, int32_t head_dim,
                                         int32_t max_context_len,
+                                        int32_t block_size,
                                         int32_t partition_tokens);
+
+/* Work plan: the list of (sequence, partition) items of a decode, longest
+ * first, so that workgroups dispatched in order form a longest-first
+ * schedule.  Built on the device from context_lens (no host sync); a plan
+ * stays valid while context_lens and the sizes below are unchanged, so one
+ * plan serves every layer of a decode step.  plan: device memory of at
+ * least paged_attention_plan_bytes(...) bytes. */
+int64_t paged_attention_plan_bytes(int32_t num_seqs, int32_t num_kv_heads,
+                                   int32_t max_context_len, int32_t block_size,
+                                   int32_t partition_tokens);
+int32_t paged_attention_plan(const int32_t* context_lens, int32_t num_seqs,
+                             int32_t max_context_len,
+                             int32_t max_blocks_per_seq, int32_t num_kv_heads,
+                             int32_t block_size, int32_t partition_tokens,
+                             void* plan, int64_t plan_bytes,
+                             pkv_stream_t stream);
 
 /* paged_attention_decode: one query token per sequence attends over its
  * whole context through the block table (operation above; [P1] §4, [P2]
@@ -247,7 +282,7 @@ int64_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_heads,
  *   k_scale,
  *   v_scale      : fp8 dequantisation scales (ignored unless kv fp8).
  *   workspace    : >= paged_attention_workspace_bytes(...) bytes of device
- *                  memory (may be NULL when that is 0).
+ *                  memory.
  * num_heads must be a multiple of num_kv_heads, with G = num_heads /
  * num_kv_heads <= 16.  Errors: PKV_ERR_ARG, PKV_ERR_SIZE (workspace),
  * PKV_ERR_UNSUPPORTED (head_dim != 128, dtype pair), PKV_ERR_HIP. */

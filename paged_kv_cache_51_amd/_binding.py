@@ -11,7 +11,8 @@ import os
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-lib_path = os.path.join(HERE, "lib", "libpagedkv.so")
+# PKV_LIB selects another build of the same library (e.g. a tuning variant).
+lib_path = os.environ.get("PKV_LIB") or os.path.join(HERE, "lib", "libpagedkv.so")
 
 BF16, FP16, FP8_E4M3 = 0, 1, 2
 IMPL_AUTO, IMPL_MFMA, IMPL_VECTOR = 0, 1, 2
@@ -22,7 +23,8 @@ EXPORTS = [
     "pkv_last_error", "pkv_version", "pkv_bytes_per_token", "pkv_tile_bytes",
     "pkv_layer_pool_bytes", "kv_pool_create", "kv_pool_destroy", "kv_pool_get_desc",
     "kv_pool_layer", "kv_pool_poison_null_block", "pkv_decode_slot_mapping",
-    "reshape_and_cache", "paged_attention_workspace_bytes", "paged_attention_decode",
+    "reshape_and_cache", "pkv_default_partition_tokens", "paged_attention_workspace_bytes",
+    "paged_attention_plan_bytes", "paged_attention_plan", "paged_attention_decode",
     "paged_attention_decode_ex", "pkv_check_block_tables",
 ]
 
@@ -41,7 +43,8 @@ class PoolDesc(ctypes.Structure):
 
 class DecodeOpts(ctypes.Structure):
     _fields_ = [("partition_tokens", ctypes.c_int32), ("impl", ctypes.c_int32),
-                ("stages", ctypes.c_int32), ("num_blocks", ctypes.c_int32)]
+                ("stages", ctypes.c_int32), ("num_blocks", ctypes.c_int32),
+                ("plan", ctypes.c_void_p)]
 
 
 _lib = None
@@ -70,7 +73,10 @@ def lib():
             "pkv_decode_slot_mapping": (i32, [p, i32, p, i32, i32, p, p]),
             "reshape_and_cache": (i32, [p, p, i32, p, p, p, i32, i32, i32, i32, i32, i32, f32,
                                         f32, p]),
-            "paged_attention_workspace_bytes": (i64, [i32, i32, i32, i32, i32]),
+            "pkv_default_partition_tokens": (i32, [i32, i32, i32, i32]),
+            "paged_attention_workspace_bytes": (i64, [i32, i32, i32, i32, i32, i32, i32]),
+            "paged_attention_plan_bytes": (i64, [i32, i32, i32, i32, i32]),
+            "paged_attention_plan": (i32, [p, i32, i32, i32, i32, i32, i32, p, i64, p]),
             "paged_attention_decode": (i32, [p, p, i32, p, p, p, i32, p, i32, i32, i32, i32,
                                              i32, f32, i32, i32, f32, f32, p, i64, p]),
             "paged_attention_decode_ex": (i32, [p, p, i32, p, p, p, i32, p, i32, i32, i32, i32,
@@ -147,9 +153,35 @@ def layer_pool_bytes(num_blocks, num_kv_heads, head_dim, block_size, kv_dtype):
                                              kv_dtype))
 
 
-def workspace_bytes(num_seqs, num_heads, head_dim, max_context_len, partition_tokens=0):
-    return _check(lib().paged_attention_workspace_bytes(num_seqs, num_heads, head_dim,
-                                                        max_context_len, partition_tokens))
+def default_partition_tokens(num_seqs, num_kv_heads, max_context_len, block_size):
+    return _check(lib().pkv_default_partition_tokens(num_seqs, num_kv_heads, max_context_len,
+                                                     block_size))
+
+
+def workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len, block_size,
+                    partition_tokens=0):
+    return _check(lib().paged_attention_workspace_bytes(num_seqs, num_heads, num_kv_heads,
+                                                        head_dim, max_context_len, block_size,
+                                                        partition_tokens))
+
+
+def plan_bytes(num_seqs, num_kv_heads, max_context_len, block_size, partition_tokens=0):
+    return _check(lib().paged_attention_plan_bytes(num_seqs, num_kv_heads, max_context_len,
+                                                   block_size, partition_tokens))
+
+
+def build_plan(context_lens, max_context_len, max_blocks_per_seq, num_kv_heads, block_size,
+               partition_tokens=0, plan=None, stream=None):
+    """Longest-first work plan on the device (reusable across layers)."""
+    S = context_lens.shape[0]
+    n = plan_bytes(S, num_kv_heads, max_context_len, block_size, partition_tokens)
+    if plan is None:
+        plan = torch.empty(n, dtype=torch.uint8, device=context_lens.device)
+    _check(lib().paged_attention_plan(
+        _ptr(context_lens, "context_lens", torch.int32), S, int(max_context_len),
+        int(max_blocks_per_seq), num_kv_heads, block_size, partition_tokens,
+        _ptr(plan, "plan"), plan.numel() * plan.element_size(), _stream(stream)))
+    return plan
 
 
 class KVPool:
@@ -222,14 +254,15 @@ def reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, block_size, nu
 def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
                            max_context_len, num_kv_heads, block_size, kv_dtype, scale,
                            k_scale=1.0, v_scale=1.0, workspace=None, partition_tokens=0,
-                           impl=IMPL_AUTO, stages=0, num_blocks=0, stream=None):
+                           impl=IMPL_AUTO, stages=0, num_blocks=0, plan=None, stream=None):
     """q/out: [S][H][d] bf16/fp16; k/v_cache: uint8 pools of one layer."""
     S, H, D = q.shape
-    need = workspace_bytes(S, H, D, max_context_len, partition_tokens)
+    need = workspace_bytes(S, H, num_kv_heads, D, max_context_len, block_size, partition_tokens)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    opts = DecodeOpts(partition_tokens, impl, stages, num_blocks)
+    opts = DecodeOpts(partition_tokens, impl, stages, num_blocks,
+                      plan.data_ptr() if plan is not None else None)
     _check(lib().paged_attention_decode_ex(
         _ptr(out, "out"), _ptr(q, "q"), dtype_code(q.dtype), _ptr(k_cache, "k_cache"),
         _ptr(v_cache, "v_cache"), _ptr(block_tables, "block_tables", torch.int32),

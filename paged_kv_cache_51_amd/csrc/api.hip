@@ -3,6 +3,7 @@
 // Every computation runs in the kernels of cache_ops.hip / decode*.hip.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -41,8 +42,62 @@ bool valid_dtype(int32_t dt) { return dt == PKV_BF16 || dt == PKV_FP16 || dt == 
 int32_t elem_size(int32_t dt) { return dt == PKV_FP8_E4M3 ? 1 : 2; }
 bool valid_block_size(int32_t bs) { return bs == 16 || bs == 32; }
 
-constexpr int32_t kDefaultPartitionTokens = 512;
 constexpr int32_t kBuiltHeadDim = 128;
+constexpr int64_t kWorkgroupsPerCu = 4;   // default split target: 4 workgroups per CU
+
+int device_cu_count() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (!cached[dev]) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
+int32_t ctx_cap_of(int32_t max_context_len, int32_t max_blocks, int32_t block_size) {
+    const int64_t table_tokens = (int64_t)max_blocks * block_size;
+    return (int32_t)(table_tokens < max_context_len ? table_tokens : max_context_len);
+}
+
+// Split the context only as far as parallelism needs: about
+// kWorkgroupsPerCu workgroups per CU in total.  Partial results written in
+// the middle of the KV read stream are expensive, so larger is better once
+// the GPU is full; the longest-first plan balances what remains.
+int32_t resolve_partition(int32_t requested, int32_t num_seqs, int32_t num_kv_heads,
+                          int32_t ctx_cap, int32_t block_size) {
+    if (requested > 0) return requested;
+    const int64_t items = std::max<int64_t>(1, (int64_t)num_seqs * num_kv_heads);
+    const int64_t target = kWorkgroupsPerCu * device_cu_count();
+    const int64_t splits = (target + items - 1) / items;
+    int64_t part = (ctx_cap + splits - 1) / splits;
+    part = std::max<int64_t>(block_size, (part + block_size - 1) / block_size * block_size);
+    while ((ctx_cap + part - 1) / part > 65535) part *= 2;
+    return (int32_t)std::min<int64_t>(part, 1 << 30);
+}
+
+int64_t num_parts_of(int32_t ctx_cap, int32_t part) { return std::max<int64_t>(1, (ctx_cap + part - 1) / part); }
+
+int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
+
+int64_t plan_bytes_of(int32_t num_seqs, int64_t P) { return align256(4 * (4 + (int64_t)num_seqs * P)); }
+
+// Workspace: [partial outputs][partial max/normaliser][plan]; the partial
+// areas exist only when some sequence can span several partitions.
+struct WsLayout { int64_t o_bytes, ml_bytes, plan_off, total; };
+WsLayout ws_layout(int32_t S, int32_t H, int32_t Hkv, int32_t D, int64_t P) {
+    WsLayout w{};
+    if (P > 1) {
+        w.o_bytes = align256((int64_t)S * H * P * D * 4);
+        w.ml_bytes = align256((int64_t)S * Hkv * P * 32 * 4);
+    }
+    w.plan_off = w.o_bytes + w.ml_bytes;
+    w.total = w.plan_off + plan_bytes_of(S, P);
+    return w;
+}
 
 // Kernels are built for head_dim 128; layout sizes accept any multiple of 64.
 int32_t check_layout_args(int32_t head_dim, int32_t block_size, int32_t kv_dtype) {
@@ -200,15 +255,53 @@ int32_t reshape_and_cache(const void* key, const void* value, int32_t src_dtype,
     return ok();
 }
 
-int64_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
-                                        int32_t max_context_len, int32_t partition_tokens) {
-    if (num_seqs < 0 || num_heads <= 0 || head_dim <= 0 || max_context_len < 0 || partition_tokens < 0)
-        return fail(PKV_ERR_ARG, "bad workspace query");
-    const int32_t part = partition_tokens ? partition_tokens : kDefaultPartitionTokens;
-    const int64_t P = (max_context_len + part - 1) / part;
+int32_t pkv_default_partition_tokens(int32_t num_seqs, int32_t num_kv_heads,
+                                     int32_t max_context_len, int32_t block_size) {
+    if (num_seqs < 0 || num_kv_heads <= 0 || max_context_len < 0 || !valid_block_size(block_size))
+        return fail(PKV_ERR_ARG, "bad partition query");
     ok();
-    if (P <= 1) return 0;
-    return (int64_t)num_seqs * num_heads * P * (head_dim + 2) * (int64_t)sizeof(float);
+    return resolve_partition(0, num_seqs, num_kv_heads, max_context_len, block_size);
+}
+
+int64_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                        int32_t head_dim, int32_t max_context_len,
+                                        int32_t block_size, int32_t partition_tokens) {
+    if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+        max_context_len < 0 || partition_tokens < 0 || !valid_block_size(block_size))
+        return fail(PKV_ERR_ARG, "bad workspace query");
+    const int32_t part = resolve_partition(partition_tokens, num_seqs, num_kv_heads, max_context_len, block_size);
+    ok();
+    return ws_layout(num_seqs, num_heads, num_kv_heads, head_dim, num_parts_of(max_context_len, part)).total;
+}
+
+int64_t paged_attention_plan_bytes(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len,
+                                   int32_t block_size, int32_t partition_tokens) {
+    if (num_seqs < 0 || num_kv_heads <= 0 || max_context_len < 0 || partition_tokens < 0 ||
+        !valid_block_size(block_size))
+        return fail(PKV_ERR_ARG, "bad plan query");
+    const int32_t part = resolve_partition(partition_tokens, num_seqs, num_kv_heads, max_context_len, block_size);
+    ok();
+    return plan_bytes_of(num_seqs, num_parts_of(max_context_len, part));
+}
+
+int32_t paged_attention_plan(const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,
+                             int32_t max_blocks_per_seq, int32_t num_kv_heads, int32_t block_size,
+                             int32_t partition_tokens, void* plan, int64_t plan_bytes,
+                             pkv_stream_t stream) {
+    if (num_seqs < 0 || num_seqs > 65535 || num_kv_heads <= 0 || max_context_len < 0 ||
+        max_blocks_per_seq < 0 || partition_tokens < 0 || !valid_block_size(block_size))
+        return fail(PKV_ERR_ARG, "bad plan arguments");
+    if (!plan || (num_seqs > 0 && !context_lens)) return fail(PKV_ERR_ARG, "null pointer");
+    const int32_t ctx_cap = ctx_cap_of(max_context_len, max_blocks_per_seq, block_size);
+    const int32_t part = resolve_partition(partition_tokens, num_seqs, num_kv_heads, ctx_cap, block_size);
+    if (part % block_size) return fail(PKV_ERR_ARG, "partition_tokens %d is not a multiple of block_size %d", part, block_size);
+    const int64_t need = plan_bytes_of(num_seqs, num_parts_of(ctx_cap, part));
+    if (plan_bytes < need) return fail(PKV_ERR_SIZE, "plan needs %lld bytes, got %lld", (long long)need, (long long)plan_bytes);
+    (void)hipGetLastError();
+    hipError_t e = pkv::launch_plan(context_lens, num_seqs, ctx_cap, block_size, part / block_size,
+                                    (int32_t*)plan, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "plan launch");
+    return ok();
 }
 
 int32_t paged_attention_decode_ex(void* out, const void* q, int32_t q_dtype, const void* k_cache,
@@ -219,13 +312,13 @@ int32_t paged_attention_decode_ex(void* out, const void* q, int32_t q_dtype, con
                                   int32_t block_size, int32_t kv_dtype, float k_scale,
                                   float v_scale, void* workspace, int64_t workspace_bytes,
                                   const pkv_decode_opts* opts, pkv_stream_t stream) {
-    pkv_decode_opts o{0, PKV_IMPL_AUTO, 0, 0};
+    pkv_decode_opts o{0, PKV_IMPL_AUTO, 0, 0, nullptr};
     if (opts) o = *opts;
     if (int32_t e = check_layout_args(head_dim, block_size, kv_dtype)) return e;
     if (q_dtype != PKV_BF16 && q_dtype != PKV_FP16) return fail(PKV_ERR_ARG, "q_dtype must be bf16 or fp16");
     if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || max_context_len < 0 || max_blocks_per_seq < 0)
         return fail(PKV_ERR_ARG, "bad sizes");
-    if (num_seqs > 65535 || num_kv_heads > 65535) return fail(PKV_ERR_UNSUPPORTED, "num_seqs and num_kv_heads must be <= 65535 (grid limits)");
+    if ((int64_t)num_seqs * num_kv_heads > 0x7fffffff || num_seqs > 65535) return fail(PKV_ERR_UNSUPPORTED, "num_seqs must be <= 65535 and num_seqs * num_kv_heads < 2^31 (grid limits)");
     if (num_heads % num_kv_heads) return fail(PKV_ERR_ARG, "num_heads %d is not a multiple of num_kv_heads %d", num_heads, num_kv_heads);
     const int32_t G = num_heads / num_kv_heads;
     if (G > 16) return fail(PKV_ERR_UNSUPPORTED, "query heads per kv head %d > 16", G);
@@ -239,18 +332,21 @@ int32_t paged_attention_decode_ex(void* out, const void* q, int32_t q_dtype, con
     if (o.impl == PKV_IMPL_VECTOR && G > 8) return fail(PKV_ERR_UNSUPPORTED, "vector kernel supports at most 8 query heads per kv head");
     const int32_t stages = o.stages ? o.stages : (PKV_STAGE_PARTITIONS | PKV_STAGE_REDUCE);
     if (stages & ~(PKV_STAGE_PARTITIONS | PKV_STAGE_REDUCE)) return fail(PKV_ERR_ARG, "bad stages mask");
-    const int32_t part_tokens = o.partition_tokens ? o.partition_tokens : kDefaultPartitionTokens;
-    if (part_tokens < block_size || part_tokens % block_size)
-        return fail(PKV_ERR_ARG, "partition_tokens %d must be a positive multiple of block_size %d", part_tokens, block_size);
+    if (o.partition_tokens < 0) return fail(PKV_ERR_ARG, "partition_tokens < 0");
     if (o.num_blocks < 0) return fail(PKV_ERR_ARG, "num_blocks < 0");
     if (num_seqs > 0 && (!out || !q || !k_cache || !v_cache || !context_lens || (max_blocks_per_seq > 0 && !block_tables)))
         return fail(PKV_ERR_ARG, "null pointer");
 
-    const int64_t table_tokens = (int64_t)max_blocks_per_seq * block_size;
-    const int32_t ctx_cap = (int32_t)(table_tokens < max_context_len ? table_tokens : max_context_len);
-    const int32_t num_parts = (ctx_cap + part_tokens - 1) / part_tokens;
-    const int64_t need = paged_attention_workspace_bytes(num_seqs, num_heads, head_dim, ctx_cap, part_tokens);
-    if (need < 0) return (int32_t)need;
+    const int32_t ctx_cap = ctx_cap_of(max_context_len, max_blocks_per_seq, block_size);
+    const int32_t part_tokens = resolve_partition(o.partition_tokens, num_seqs, num_kv_heads, ctx_cap, block_size);
+    if (part_tokens < block_size || part_tokens % block_size)
+        return fail(PKV_ERR_ARG, "partition_tokens %d must be a positive multiple of block_size %d", part_tokens, block_size);
+    const int64_t num_parts = num_parts_of(ctx_cap, part_tokens);
+    if (num_parts > 65535) return fail(PKV_ERR_UNSUPPORTED, "more than 65535 partitions (raise partition_tokens)");
+    if ((int64_t)num_seqs * num_kv_heads * num_parts > 0x7fffffff)
+        return fail(PKV_ERR_UNSUPPORTED, "too many workgroups (raise partition_tokens)");
+    const WsLayout wl = ws_layout(num_seqs, num_heads, num_kv_heads, head_dim, num_parts);
+    const int64_t need = o.plan ? wl.plan_off : wl.total;
     if (need > 0 && (!workspace || workspace_bytes < need))
         return fail(PKV_ERR_SIZE, "workspace needs %lld bytes, got %lld", (long long)need, (long long)workspace_bytes);
 
@@ -262,7 +358,8 @@ int32_t paged_attention_decode_ex(void* out, const void* q, int32_t q_dtype, con
     a.block_tables = block_tables;
     a.context_lens = context_lens;
     a.ws_out = (float*)workspace;
-    a.ws_ml = need > 0 ? (float*)workspace + (int64_t)num_seqs * num_heads * num_parts * head_dim : nullptr;
+    a.ws_ml = wl.ml_bytes ? (float*)((char*)workspace + wl.o_bytes) : nullptr;
+    a.plan = o.plan ? (const int32_t*)o.plan : (const int32_t*)((char*)workspace + wl.plan_off);
     a.max_blocks = max_blocks_per_seq;
     a.ctx_cap = ctx_cap;
     a.num_seqs = num_seqs;
@@ -270,7 +367,7 @@ int32_t paged_attention_decode_ex(void* out, const void* q, int32_t q_dtype, con
     a.num_kv_heads = num_kv_heads;
     a.group = G;
     a.part_blocks = part_tokens / block_size;
-    a.num_parts = num_parts;
+    a.num_parts = (int32_t)num_parts;
     a.num_blocks = o.num_blocks;
     const float ks = kv_dtype == PKV_FP8_E4M3 ? k_scale : 1.0f;
     a.qk_scale_log2 = (float)((double)scale * (double)ks * 1.4426950408889634);
@@ -278,6 +375,11 @@ int32_t paged_attention_decode_ex(void* out, const void* q, int32_t q_dtype, con
 
     hipStream_t st = (hipStream_t)stream;
     (void)hipGetLastError();
+    if ((stages & PKV_STAGE_PARTITIONS) && !o.plan && num_seqs > 0) {
+        hipError_t e = pkv::launch_plan(context_lens, num_seqs, ctx_cap, block_size, a.part_blocks,
+                                        (int32_t*)a.plan, st);
+        if (e != hipSuccess) return hip_fail(e, "plan launch");
+    }
     if (stages & PKV_STAGE_PARTITIONS) {
         hipError_t e = pkv::launch_decode_partitions(a, q_dtype, kv_dtype, block_size, o.impl, st);
         if (e != hipSuccess) return hip_fail(e, "paged decode launch");

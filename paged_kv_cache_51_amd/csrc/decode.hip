@@ -8,8 +8,8 @@
 // table.  GQA ("LLM inference basics..." §2): the G query heads of a group
 // share one K/V head, so one pass over a K/V tile serves all G of them.
 //
-// Work decomposition (one workgroup of NW waves per (partition, kv head,
-// sequence)):
+// Work decomposition (one workgroup of NW waves per (sequence, kv head,
+// partition) from the work plan of plan.hip):
 //   - a partition is part_blocks consecutive logical blocks; the workgroup
 //     walks its 16-token sub-tiles ("units"), wave w taking units w, w+NW, ...
 //   - per unit a wave loads the K and V sub-tiles (4 + 4 rows of 1 KiB for
@@ -19,10 +19,11 @@
 //     G query heads padded to 16), online softmax in fp32 in the log2 domain,
 //     then O^T += V^T . P^T on eight 16x16x16 MFMAs whose B operand is the
 //     S^T result in place (same lane order);
-//   - the next unit's loads are issued before the current unit is computed
-//     (two register sets);
-//   - waves merge through LDS; a sequence that fits one partition writes its
-//     output directly, otherwise (max, normaliser, normalised output) per
+//   - the next DEPTH-1 units' loads are in flight while a unit is computed
+//     (a ring of register sets);
+//   - waves park their partial results in LDS and the last wave to finish
+//     merges them (no barrier wait); a sequence that fits one partition gets
+//     its output directly, otherwise (max, normaliser, normalised output) per
 //     partition go to the workspace for decode_reduce_kernel.
 #include "pkv_device.h"
 #include "pkv_launch.h"
@@ -72,9 +73,21 @@ __device__ __forceinline__ u32x2_t v_frag(const UnitRegs<KVT>& u, int nt) {
     }
 }
 
+// Rescale threshold (log2 units): the reference max m of a head only moves
+// when a unit's max exceeds it by more than this, so weights stay <= 2^8
+// (exact math for any reference; fp32 / bf16 / fp16 hold 2^8 easily) and the
+// 32 accumulators are rescaled only on such rare jumps.
+constexpr float kRescaleSlack = 8.0f;
+
+// Row stride (floats) of a head's partial output in the merge area: 128
+// dims plus 4 floats of padding to spread heads over LDS banks.
+constexpr int kMergeRow = kHeadDim + 4;
+
+__host__ __device__ constexpr int merge_lds_floats(int nw, int g) { return 4 + 32 * nw + nw * g * kMergeRow; }
+
 // One 16-token unit: logits, online-softmax update, PV accumulation.
 // tok0 = logical position of the unit's first token; ctx = context length;
-// cs = scale * k_scale * log2(e).  m is in log2 units (already scaled).
+// cs = scale * k_scale * log2(e).  m (log2 units) is the head's reference.
 template <int KVT, int QT>
 __device__ __forceinline__ void process_unit(const UnitRegs<KVT>& u, const u32x4_t (&qf)[4],
                                              f32x4_t (&acc)[8], float& m, float& l, int tok0,
@@ -93,28 +106,32 @@ __device__ __forceinline__ void process_unit(const UnitRegs<KVT>& u, const u32x4
     }
     float bm = fmaxf(fmaxf(t[0], t[1]), fmaxf(t[2], t[3]));
     bm = fmaxf(bm, xor_shfl(bm, 16));
-    bm = fmaxf(bm, xor_shfl(bm, 32));
-    const float mn = fmaxf(m, bm);       // finite: every unit holds a valid token
-    const float alpha = (m == -INFINITY) ? 0.f : fast_exp2(m - mn);
+    bm = fmaxf(bm, xor_shfl(bm, 32));     // max of the unit for head lane&15
+    if (__builtin_amdgcn_ballot_w64(bm > m + kRescaleSlack)) {
+        // Some head's max jumped: move every head's reference to its max.
+        const float mn = fmaxf(m, bm);     // finite: every unit holds a valid token
+        const float alpha = (m == -INFINITY) ? 0.f : fast_exp2(m - mn);
+        l *= alpha;
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) acc[nt] *= alpha;
+        m = mn;
+    }
     uint32_t pbits[4];
     float psum = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const float p = valid[i] ? fast_exp2(t[i] - mn) : 0.f;
+        const float p = valid[i] ? fast_exp2(t[i] - m) : 0.f;
         pbits[i] = f32_to_bits<QT>(p);
         psum += bits_to_f32<QT>(pbits[i]);   // normalise with the rounded weights
     }
-    l = l * alpha + psum;
-    m = mn;
+    l += psum;
     u32x2_t pf;
     pf[0] = pbits[0] | (pbits[1] << 16);
     pf[1] = pbits[2] | (pbits[3] << 16);
     if (tok0 + kSubTokens <= ctx) {
 #pragma unroll
-        for (int nt = 0; nt < 8; ++nt) {
-            acc[nt] *= alpha;
+        for (int nt = 0; nt < 8; ++nt)
             acc[nt] = mfma_16x16x16<QT>(v_frag<KVT, QT>(u, nt), pf, acc[nt]);
-        }
     } else {
         // Last unit of the context: rows past the context hold whatever the
         // slot last held (NaN or stale data); a zero weight times NaN would
@@ -123,44 +140,48 @@ __device__ __forceinline__ void process_unit(const UnitRegs<KVT>& u, const u32x4
         vm[0] = (valid[0] ? 0x0000ffffu : 0u) | (valid[1] ? 0xffff0000u : 0u);
         vm[1] = (valid[2] ? 0x0000ffffu : 0u) | (valid[3] ? 0xffff0000u : 0u);
 #pragma unroll
-        for (int nt = 0; nt < 8; ++nt) {
-            acc[nt] *= alpha;
+        for (int nt = 0; nt < 8; ++nt)
             acc[nt] = mfma_16x16x16<QT>(v_frag<KVT, QT>(u, nt) & vm, pf, acc[nt]);
-        }
     }
 }
 
-template <int KVT, int QT, int BS, int NW>
-__global__ __launch_bounds__(NW * kWave) void paged_decode_mfma_kernel(const DecodeArgs a) {
+#ifndef PKV_WAVES_PER_EU
+#define PKV_WAVES_PER_EU 1
+#endif
+template <int KVT, int QT, int BS, int NW, int DEPTH>
+__global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(PKV_WAVES_PER_EU)))
+void paged_decode_mfma_kernel(const DecodeArgs a) {
     constexpr int NSUB = BS / kSubTokens;
     constexpr int64_t SUB = sub_tile_bytes(KVT);
     constexpr int64_t TILE = SUB * NSUB;
-    __shared__ float sm_acc[NW][32][kWave];
-    __shared__ float sm_m[NW][16];
-    __shared__ float sm_l[NW][16];
+    // Dynamic LDS (merge_lds_floats): [counter pad 4][m NW*16][l NW*16]
+    // [acc NW*G rows of kMergeRow floats].
+    extern __shared__ float pkv_smem[];
 
     const int lane = threadIdx.x & (kWave - 1);
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int part = blockIdx.x, kvh = blockIdx.y, s = blockIdx.z;
+    // One workgroup per (plan item, kv head), head fastest: the plan lists
+    // the (sequence, partition) items longest first, so the dispatcher's
+    // greedy in-order placement runs long work first and the heads of one
+    // item spread over consecutive XCDs.
+    const int item = blockIdx.x / a.num_kv_heads;
+    const int kvh = blockIdx.x - item * a.num_kv_heads;
+    const int n_items = a.plan[0];
+    const uint32_t packed = (uint32_t)a.plan[4 + item];   // in bounds; valid if item < n_items
+    if (item >= n_items) return;
+    const int s = (int)(packed >> 16), part = (int)(packed & 0xffffu);
     const int G = a.group;
-
-    int ctx = a.context_lens[s];
-    ctx = ctx < a.ctx_cap ? ctx : a.ctx_cap;
-    if (ctx <= 0) {
-        if (part == 0) {
-            uint16_t* out = reinterpret_cast<uint16_t*>(a.out) +
-                            ((int64_t)s * a.num_heads + (int64_t)kvh * G) * kHeadDim;
-            for (int e = threadIdx.x; e < G * kHeadDim; e += NW * kWave) out[e] = 0;
-        }
-        return;
-    }
-    const int n_units = (ctx + kSubTokens - 1) / kSubTokens;
     const int units_per_part = a.part_blocks * NSUB;
     const int u0 = part * units_per_part;
-    if (u0 >= n_units) return;
-    const int u1 = min(u0 + units_per_part, n_units);
-    const int nblk = (ctx + BS - 1) / BS;
-    const bool single = nblk <= a.part_blocks;
+    const int first = u0 + w;                 // this wave's first unit
+    const int32_t* bt_row = a.block_tables + (int64_t)s * a.max_blocks;
+
+    // Issue every load that does not need the context length at once: the
+    // block ids of this wave's first 64 units (index clamped into the table
+    // row; ids past the context are never used) and the query fragments.
+    // Only one memory round trip then precedes the first K/V unit.
+    int ids0 = 0;
+    if (a.max_blocks > 0) ids0 = bt_row[min(first + NW * lane, a.max_blocks * NSUB - 1) / NSUB];
 
     // Q^T fragments: lane holds head (lane & 15) of the group, 8 dims per kk.
     const int hl = lane & 15;
@@ -178,15 +199,32 @@ __global__ __launch_bounds__(NW * kWave) void paged_decode_mfma_kernel(const Dec
         }
     }
 
+    int ctx = a.context_lens[s];
+    ctx = ctx < a.ctx_cap ? ctx : a.ctx_cap;
+    if (ctx <= 0) {
+        if (part == 0) {
+            uint16_t* out = reinterpret_cast<uint16_t*>(a.out) +
+                            ((int64_t)s * a.num_heads + (int64_t)kvh * G) * kHeadDim;
+            for (int e = threadIdx.x; e < G * kHeadDim; e += NW * kWave) out[e] = 0;
+        }
+        return;
+    }
+    const int n_units = (ctx + kSubTokens - 1) / kSubTokens;
+    if (u0 >= n_units) return;
+    const int u1 = min(u0 + units_per_part, n_units);
+    const int nblk = (ctx + BS - 1) / BS;
+    const bool single = nblk <= a.part_blocks;
+    int* done = reinterpret_cast<int*>(pkv_smem);
+    if (threadIdx.x == 0) *done = 0;
+    __syncthreads();
+
     f32x4_t acc[8];
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) acc[nt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
     float m = -INFINITY, l = 0.f;
 
-    const int first = u0 + w;
     const int n_my = first < u1 ? (u1 - first + NW - 1) / NW : 0;
     if (n_my > 0) {
-        const int32_t* bt_row = a.block_tables + (int64_t)s * a.max_blocks;
         const uint8_t* kpool = a.k_cache + (int64_t)kvh * TILE;
         const uint8_t* vpool = a.v_cache + (int64_t)kvh * TILE;
         const int64_t head_stride = (int64_t)a.num_kv_heads * TILE;
@@ -200,34 +238,54 @@ __global__ __launch_bounds__(NW * kWave) void paged_decode_mfma_kernel(const Dec
             return (int64_t)pb * head_stride + ((first + NW * (c0 + j)) % NSUB) * SUB;
         };
         // Units in chunks of 64 per wave: lane j of `ids` holds the block
-        // id of the chunk's unit j (read back with readlane, no reload in
-        // the pipelined loop).
+        // id of the chunk's unit j (read back with readlane).  Within a chunk
+        // a ring of DEPTH register buffers keeps DEPTH units in flight.  The
+        // steady state only runs while every refill is a real unit, so its
+        // loads are unconditional and their counters static; the drain
+        // refills what is left, so no load is issued past the last unit
+        // (except prologue repeats when the wave has fewer than DEPTH units).
         for (int c0 = 0; c0 < n_my; c0 += kWave) {
             const int nc = min(kWave, n_my - c0);
-            const int ids = load_ids(c0);
-            UnitRegs<KVT> A, B;
-            int64_t off = unit_offset(ids, c0, 0);
-            load_unit<KVT>(A, kpool + off, vpool + off, lane);
+            const int ids = c0 == 0 ? ids0 : load_ids(c0);
+            UnitRegs<KVT> buf[DEPTH];
+            // Unconditional prologue: a conditional load here would make the
+            // compiler's load-counter analysis assume the ring may be half
+            // empty and wait for every outstanding load inside the loop.  With
+            // fewer than DEPTH units the extra slots repeat the last unit.
+#pragma unroll
+            for (int d = 0; d < DEPTH; ++d) {
+                const int64_t off = unit_offset(ids, c0, min(d, nc - 1));
+                load_unit<KVT>(buf[d], kpool + off, vpool + off, lane);
+            }
+            auto tok_of = [&](int j) { return (first + NW * (c0 + j)) * kSubTokens; };
             int i = 0;
-            while (true) {
-                const int tok = (first + NW * (c0 + i)) * kSubTokens;
-                if (i + 1 >= nc) {
-                    process_unit<KVT, QT>(A, qf, acc, m, l, tok, ctx, a.qk_scale_log2, lane);
-                    break;
+            for (; i + 2 * DEPTH <= nc; i += DEPTH) {
+#pragma unroll
+                for (int d = 0; d < DEPTH; ++d) {
+                    process_unit<KVT, QT>(buf[d], qf, acc, m, l, tok_of(i + d), ctx,
+                                          a.qk_scale_log2, lane);
+                    const int64_t off = unit_offset(ids, c0, i + d + DEPTH);
+                    load_unit<KVT>(buf[d], kpool + off, vpool + off, lane);
                 }
-                off = unit_offset(ids, c0, i + 1);
-                load_unit<KVT>(B, kpool + off, vpool + off, lane);
-                process_unit<KVT, QT>(A, qf, acc, m, l, tok, ctx, a.qk_scale_log2, lane);
-                ++i;
-                const int tok2 = tok + NW * kSubTokens;
-                if (i + 1 >= nc) {
-                    process_unit<KVT, QT>(B, qf, acc, m, l, tok2, ctx, a.qk_scale_log2, lane);
-                    break;
+            }
+            // drain: units i .. nc-1 (at most 2*DEPTH-1 of them)
+            const int refills = nc - i - DEPTH;   // < DEPTH; may be negative
+#pragma unroll
+            for (int d = 0; d < DEPTH; ++d) {
+                if (i + d < nc) {
+                    process_unit<KVT, QT>(buf[d], qf, acc, m, l, tok_of(i + d), ctx,
+                                          a.qk_scale_log2, lane);
+                    if (d < refills) {
+                        const int64_t off = unit_offset(ids, c0, i + d + DEPTH);
+                        load_unit<KVT>(buf[d], kpool + off, vpool + off, lane);
+                    }
                 }
-                off = unit_offset(ids, c0, i + 1);
-                load_unit<KVT>(A, kpool + off, vpool + off, lane);
-                process_unit<KVT, QT>(B, qf, acc, m, l, tok2, ctx, a.qk_scale_log2, lane);
-                ++i;
+            }
+#pragma unroll
+            for (int d = 0; d < DEPTH - 1; ++d) {
+                if (d < refills)
+                    process_unit<KVT, QT>(buf[d], qf, acc, m, l, tok_of(i + DEPTH + d), ctx,
+                                          a.qk_scale_log2, lane);
             }
         }
     }
@@ -235,49 +293,73 @@ __global__ __launch_bounds__(NW * kWave) void paged_decode_mfma_kernel(const Dec
     l += xor_shfl(l, 16);
     l += xor_shfl(l, 32);
 
-    // ---- merge the NW waves through LDS
-#pragma unroll
-    for (int nt = 0; nt < 8; ++nt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sm_acc[w][nt * 4 + i][lane] = acc[nt][i];
+    // ---- merge the NW waves: every wave parks its partial (m, l, O for the
+    // G real heads) in LDS and leaves; the last wave to arrive merges them
+    // and writes whole output rows.  No wave waits at a barrier for the
+    // slowest one, so early finishers free their registers at once.
+    float* sm_m = pkv_smem + 4;
+    float* sm_l = sm_m + NW * 16;
+    float* sm_acc = sm_l + NW * 16;
     if (lane < 16) {
-        sm_m[w][lane] = m;
-        sm_l[w][lane] = l;
+        sm_m[w * 16 + lane] = m;
+        sm_l[w * 16 + lane] = l;
     }
-    __syncthreads();
-    if (!hvalid) return;
-    float M = -INFINITY;
+    if (hvalid) {
+        float* row = sm_acc + (w * G + hl) * kMergeRow + 4 * (lane >> 4);
 #pragma unroll
-    for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, sm_m[ww][hl]);
-    float f[NW];
-    float L = 0.f;
-#pragma unroll
-    for (int ww = 0; ww < NW; ++ww) {
-        const float mw = sm_m[ww][hl];
-        f[ww] = (mw == -INFINITY) ? 0.f : fast_exp2(mw - M);
-        L += f[ww] * sm_l[ww][hl];
+        for (int nt = 0; nt < 8; ++nt) *reinterpret_cast<f32x4_t*>(row + 16 * nt) = acc[nt];
     }
-    const float invL = 1.0f / L;
-    const int hq = kvh * G + hl;
-    const int64_t pidx = ((int64_t)s * a.num_heads + hq) * a.num_parts + part;
+    __threadfence_block();
+    int prev = 0;
+    if (lane == 0) prev = atomicAdd(done, 1);
+    prev = __builtin_amdgcn_readfirstlane(prev);
+    if (prev != NW - 1) return;
+    __threadfence_block();
+
+    for (int h = 0; h < G; ++h) {
+        float M = -INFINITY;
 #pragma unroll
-    for (int k = 0; k < 32 / NW; ++k) {
-        const int idx = w + NW * k;
-        const int dim = 16 * (idx >> 2) + 4 * (lane >> 4) + (idx & 3);
-        float o = 0.f;
+        for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, sm_m[ww * 16 + h]);
+        float L = 0.f, o0 = 0.f, o1 = 0.f;
 #pragma unroll
-        for (int ww = 0; ww < NW; ++ww) o += f[ww] * sm_acc[ww][idx][lane];
+        for (int ww = 0; ww < NW; ++ww) {
+            const float mw = sm_m[ww * 16 + h];
+            const float f = (mw == -INFINITY) ? 0.f : fast_exp2(mw - M);
+            const float2 ov = *reinterpret_cast<const float2*>(sm_acc + (ww * G + h) * kMergeRow + 2 * lane);
+            L += f * sm_l[ww * 16 + h];
+            o0 += f * ov.x;
+            o1 += f * ov.y;
+        }
+        const float invL = 1.0f / L;
+        const int hq = kvh * G + h;
         if (single) {
-            uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
-            out[((int64_t)s * a.num_heads + hq) * kHeadDim + dim] =
-                f32_to_bits<QT>(o * invL * a.out_scale);
+            const float sc = invL * a.out_scale;
+            uint16_t* out = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)s * a.num_heads + hq) * kHeadDim;
+            *reinterpret_cast<uint32_t*>(out + 2 * lane) =
+                (uint32_t)f32_to_bits<QT>(o0 * sc) | ((uint32_t)f32_to_bits<QT>(o1 * sc) << 16);
         } else {
-            a.ws_out[pidx * kHeadDim + dim] = o * invL;
+            // record (s, kvh, part): G rows of head_dim floats, contiguous
+            const int64_t rec = ((int64_t)s * a.num_kv_heads + kvh) * a.num_parts + part;
+            *reinterpret_cast<float2*>(a.ws_out + (rec * G + h) * kHeadDim + 2 * lane) =
+                make_float2(o0 * invL, o1 * invL);
         }
     }
-    if (!single && w == 0 && lane < 16) {
-        a.ws_ml[pidx * 2 + 0] = M;
-        a.ws_ml[pidx * 2 + 1] = L;
+    if (!single && lane < 32) {
+        // one full 128-byte line per record: maxima of the G heads at [0, 16),
+        // normalisers at [16, 32)
+        const int h = lane & 15;
+        float M = -INFINITY, L = 0.f;
+        if (h < G) {
+#pragma unroll
+            for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, sm_m[ww * 16 + h]);
+#pragma unroll
+            for (int ww = 0; ww < NW; ++ww) {
+                const float mw = sm_m[ww * 16 + h];
+                L += ((mw == -INFINITY) ? 0.f : fast_exp2(mw - M)) * sm_l[ww * 16 + h];
+            }
+        }
+        const int64_t rec = ((int64_t)s * a.num_kv_heads + kvh) * a.num_parts + part;
+        a.ws_ml[rec * 32 + lane] = (h < G) ? (lane < 16 ? M : L) : 0.f;
     }
 }
 
@@ -294,17 +376,18 @@ __global__ __launch_bounds__(kWave) void decode_reduce_kernel(const DecodeArgs a
     const int nblk = (ctx + BS - 1) / BS;
     const int np = (nblk + a.part_blocks - 1) / a.part_blocks;
     if (np <= 1) return;
-    const int64_t base = ((int64_t)s * a.num_heads + hq) * a.num_parts;
+    const int G = a.group, kvh = hq / G, h = hq - kvh * G;
+    const int64_t base = ((int64_t)s * a.num_kv_heads + kvh) * a.num_parts;
     float M = -INFINITY;
-    for (int p = lane; p < np; p += kWave) M = fmaxf(M, a.ws_ml[(base + p) * 2]);
+    for (int p = lane; p < np; p += kWave) M = fmaxf(M, a.ws_ml[(base + p) * 32 + h]);
 #pragma unroll
     for (int d = 1; d < kWave; d <<= 1) M = fmaxf(M, xor_shfl(M, d));
     float L = 0.f, o0 = 0.f, o1 = 0.f;
     for (int p = 0; p < np; ++p) {
-        const float mp = a.ws_ml[(base + p) * 2];
-        const float lp = a.ws_ml[(base + p) * 2 + 1];
+        const float mp = a.ws_ml[(base + p) * 32 + h];
+        const float lp = a.ws_ml[(base + p) * 32 + 16 + h];
         const float fct = fast_exp2(mp - M) * lp;
-        const float2 op = *reinterpret_cast<const float2*>(a.ws_out + (base + p) * kHeadDim + 2 * lane);
+        const float2 op = *reinterpret_cast<const float2*>(a.ws_out + ((base + p) * G + h) * kHeadDim + 2 * lane);
         L += fct;
         o0 += fct * op.x;
         o1 += fct * op.y;
@@ -317,13 +400,21 @@ __global__ __launch_bounds__(kWave) void decode_reduce_kernel(const DecodeArgs a
 
 // ----------------------------------------------------------------- launch --
 
-constexpr int kWavesPerGroup = 4;
+#ifndef PKV_WAVES_PER_GROUP
+#define PKV_WAVES_PER_GROUP 4
+#endif
+#ifndef PKV_PIPELINE_DEPTH
+#define PKV_PIPELINE_DEPTH 2
+#endif
+constexpr int kWavesPerGroup = PKV_WAVES_PER_GROUP;
+constexpr int kDepth = PKV_PIPELINE_DEPTH;
 
 template <int KVT, int QT, int BS>
 static hipError_t launch_mfma(const DecodeArgs& a, hipStream_t st) {
-    dim3 grid(a.num_parts, a.num_kv_heads, a.num_seqs);
-    hipLaunchKernelGGL((paged_decode_mfma_kernel<KVT, QT, BS, kWavesPerGroup>), grid,
-                       dim3(kWavesPerGroup * kWave), 0, st, a);
+    dim3 grid(a.num_seqs * a.num_kv_heads * a.num_parts);
+    const size_t lds = sizeof(float) * merge_lds_floats(kWavesPerGroup, a.group);
+    hipLaunchKernelGGL((paged_decode_mfma_kernel<KVT, QT, BS, kWavesPerGroup, kDepth>), grid,
+                       dim3(kWavesPerGroup * kWave), lds, st, a);
     return hipGetLastError();
 }
 

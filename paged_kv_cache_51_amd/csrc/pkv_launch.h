@@ -32,7 +32,8 @@ struct DecodeArgs {
     const int32_t* block_tables;
     const int32_t* context_lens;
     float* ws_out;         // [S][H][P][128] partial outputs (normalised)
-    float* ws_ml;          // [S][H][P][2]   (max in log2 units, normaliser)
+    float* ws_ml;          // [S][H_kv][P][32] (max in log2 units, normaliser per head)
+    const int32_t* plan;   // work plan (plan.hip): count, then (seq << 16 | part)
     int32_t max_blocks;    // block-table row length
     int32_t ctx_cap;       // context clamp: min(max_context_len, max_blocks*bs)
     int32_t num_seqs;
@@ -53,6 +54,8 @@ hipError_t launch_decode_slot_mapping(const int32_t* bt, int32_t max_blocks, con
 hipError_t launch_check_tables(const int32_t* bt, int32_t max_blocks, const int32_t* ctx,
                                int32_t num_seqs, int32_t bs, int32_t num_blocks, int32_t* bad,
                                hipStream_t st);
+hipError_t launch_plan(const int32_t* context_lens, int32_t num_seqs, int32_t ctx_cap,
+                       int32_t block_size, int32_t part_blocks, int32_t* plan, hipStream_t st);
 hipError_t launch_fill_pattern(void* p, int64_t n_bytes, uint32_t pattern, int pattern_bytes,
                                hipStream_t st);
 

@@ -40,10 +40,30 @@ def test_sizes_match_oracle():
             assert pkv.tile_bytes(128, bs, dt) == bs * 128 * oracle.elem_bytes(dt)
 
 
-def test_workspace_bytes():
-    assert pkv.workspace_bytes(4, 12, 128, 200, 512) == 0          # one partition
-    assert pkv.workspace_bytes(4, 12, 128, 200, 16) == 4 * 12 * 13 * 130 * 4
-    assert pkv.workspace_bytes(256, 28, 128, 8192, 0) == 256 * 28 * 16 * 130 * 4
+def _a256(x):
+    return (x + 255) // 256 * 256
+
+
+def test_workspace_and_plan_bytes():
+    # one partition: only the plan (count + 3 reserved + one item per sequence)
+    assert pkv.workspace_bytes(4, 12, 2, 128, 200, 16, 512) == _a256(4 * (4 + 4))
+    assert pkv.plan_bytes(4, 2, 200, 16, 512) == _a256(4 * (4 + 4))
+    # 13 partitions: partial outputs [S][H][P][d], one 32-float line per
+    # (sequence, kv head, partition), then the plan
+    P = 13
+    assert pkv.workspace_bytes(4, 12, 2, 128, 200, 16, 16) == (
+        _a256(4 * 12 * P * 128 * 4) + _a256(4 * 2 * P * 32 * 4) + _a256(4 * (4 + 4 * P)))
+
+
+def test_default_partition_heuristic():
+    # no device here: the library assumes 256 compute units (MI355X)
+    cus = 256
+    assert pkv.default_partition_tokens(256, 4, 8192, 16) == 8192    # 1024 items: no split
+    assert pkv.default_partition_tokens(32, 8, 32768, 16) == 8192    # 256 items: 4 splits
+    assert pkv.default_partition_tokens(64, 2, 4096, 16) == 4096 // ((4 * cus + 127) // 128)
+    p = pkv.default_partition_tokens(4, 2, 200, 16)
+    assert p % 16 == 0 and p >= 16
+    assert pkv.default_partition_tokens(128, 32, 4096, 32) == 4096
 
 
 FAKE = ctypes.c_void_p(0x1000)

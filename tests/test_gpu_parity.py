@@ -104,6 +104,34 @@ def test_check_block_tables():
     assert pkv.check_block_tables(devi(bt), devi(ctx), 16, tabs.num_blocks) == 3
 
 
+@pytest.mark.parametrize("cfg,part", [("qwen15b", 0), ("qwen15b", 256), ("qwen7b", 0),
+                                      ("qwen7b", 1024), ("tiny", 16)])
+def test_plan_is_longest_first_permutation(cfg, part):
+    log(f"plan {cfg} part={part}")
+    c, tabs, _, _ = workloads.make(cfg)
+    bs, Hkv = c.block_size, c.num_kv_heads
+    ctx = tabs.context_lens.copy()
+    ctx[1] = 0                                           # an empty sequence gets one item
+    mc = int(ctx.max())
+    plan = pkv.build_plan(devi(ctx), mc, tabs.block_tables.shape[1], Hkv, bs, part)
+    torch.cuda.synchronize()
+    pl = plan.cpu().numpy().view(np.int32)
+    P = part or pkv.default_partition_tokens(len(ctx), Hkv, mc, bs)
+    want = []
+    for s, cl in enumerate(ctx):
+        units = -(-int(cl) // 16)
+        np_ = max(1, -(-(-(-int(cl) // bs)) // (P // bs)))
+        for p in range(np_):
+            want.append((s, p, max(0, min(P // 16, units - p * (P // 16)))))
+    n = int(pl[0])
+    assert n == len(want)
+    items = [(int(e) >> 16 & 0xffff, int(e) & 0xffff) for e in pl[4:4 + n]]
+    assert sorted(items) == sorted((s, p) for s, p, _ in want)
+    size = {(s, p): z for s, p, z in want}
+    sizes = [min(size[it], 4095) for it in items]
+    assert all(a >= b for a, b in zip(sizes, sizes[1:])), "not longest first"
+
+
 # ---------------------------------------------------- reshape_and_cache ----
 
 @pytest.mark.parametrize("src,kv,bs", [
