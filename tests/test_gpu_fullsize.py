@@ -1,0 +1,103 @@
+"""GPU parity at the full workload sizes, in the launch configuration the
+bench times (default partition size, device work plan).
+
+Pools are filled on the device with N(0,1) values (fp8: N(0,1)/scale cast
+by torch), copied back, and the CPU oracle computes a sample of sequences
+one by one; every output of the batch must be finite.  Tolerances as in
+test_gpu_parity: 2e-2 (bf16 / fp16 KV), 6e-2 (fp8 KV).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+
+pkv = pytest.importorskip("paged_kv_cache_51_amd")
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+TOL = {oracle.BF16: 2e-2, oracle.FP16: 2e-2, oracle.FP8: 6e-2}
+
+
+def log(*a):
+    print(*a, flush=True)
+
+
+def run_config(name, kv_dtype=None, block_size=None, samples=(), layer_seed=0):
+    cfg, tabs, _, _ = workloads.make(name, block_size=block_size)
+    kv = cfg.kv_dtype if kv_dtype is None else kv_dtype
+    qdt = cfg.q_dtype if kv == oracle.FP8 else kv
+    bs = block_size or cfg.block_size
+    S, H, Hkv, D = cfg.num_seqs, cfg.num_heads, cfg.num_kv_heads, cfg.head_dim
+    ctx = tabs.context_lens
+    nb = tabs.num_blocks
+    log(f"{name}: kv={kv} bs={bs} S={S} blocks={nb} max_ctx={int(ctx.max())}")
+    scale_fp8 = float(np.float32(8.0 / 448.0))
+    ks = vs = scale_fp8 if kv == oracle.FP8 else 1.0
+    nbytes = pkv.layer_pool_bytes(nb, Hkv, D, bs, kv)
+    kpool = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    vpool = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    workloads.device_fill_normal(kpool, kv, 1000 + layer_seed, scale=scale_fp8)
+    workloads.device_fill_normal(vpool, kv, 2000 + layer_seed, scale=scale_fp8)
+    tq = torch.bfloat16 if qdt == oracle.BF16 else torch.float16
+    g = torch.Generator(device=DEV)
+    g.manual_seed(7 + layer_seed)
+    q = torch.randn(S, H, D, generator=g, device=DEV).to(tq)
+    out = torch.full_like(q, float("nan"))
+    bt = torch.from_numpy(tabs.block_tables).to(DEV)
+    cl = torch.from_numpy(ctx).to(DEV)
+    assert pkv.check_block_tables(bt, cl, bs, nb) == 0
+    mc = int(ctx.max())
+    part = pkv.default_partition_tokens(S, Hkv, mc, bs)
+    plan = pkv.build_plan(cl, mc, bt.shape[1], Hkv, bs, part)
+    scale = float(np.float32(1.0 / np.sqrt(D)))
+    pkv.paged_attention_decode(out, q, kpool, vpool, bt, cl, mc, Hkv, bs, kv, scale, ks, vs,
+                               partition_tokens=part, num_blocks=nb, plan=plan)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy().astype(np.float64)
+    assert np.isfinite(got).all(), "non-finite output"
+    log(f"  partition {part} tokens; copying pools to host")
+    kp, vp = kpool.cpu().numpy(), vpool.cpu().numpy()
+    qb = q.cpu().view(torch.int16).numpy().view(np.uint16)
+    idx = np.array(samples if samples else range(S))
+    want = oracle.paged_decode(qb[idx], qdt, kp, vp, kv, tabs.block_tables[idx], ctx[idx], Hkv, bs,
+                               scale, ks, vs)
+    err = np.abs(got[idx] - want)
+    log(f"  sampled {len(idx)} seqs (ctx {[int(ctx[i]) for i in idx[:8]]}...): "
+        f"max-abs {err.max():.3e} mean-abs {err.mean():.3e}")
+    assert err.max() <= TOL[kv]
+    return part, mc
+
+
+def _extremes(name, n_random, seed=0):
+    cfg, tabs, _, _ = workloads.make(name)
+    ctx = tabs.context_lens
+    r = np.random.default_rng(seed)
+    pick = {int(np.argmax(ctx)), int(np.argmin(ctx))}
+    pick |= set(int(i) for i in r.choice(len(ctx), n_random, replace=False))
+    return sorted(pick)
+
+
+def test_qwen7b_layer_full_size():
+    part, mc = run_config("qwen7b", samples=_extremes("qwen7b", 4))
+    assert part >= mc            # the bench's launch: no context split
+
+
+def test_qwen72b_fp8_full_size():
+    part, mc = run_config("qwen72b", kv_dtype=oracle.FP8, samples=[0])
+    assert part < mc             # split into partitions + reduce
+
+
+def test_qwen72b_bf16_full_size():
+    run_config("qwen72b", kv_dtype=oracle.BF16, samples=[31])
+
+
+def test_qwen15b_full_with_shared_prefix():
+    run_config("qwen15b")        # every sequence, incl. the 8 sharing a prefix
+
+
+@pytest.mark.parametrize("bs", [16, 32])
+def test_llama7b_mha_fp16(bs):
+    run_config("llama7b", block_size=bs, samples=_extremes("llama7b", 6))
