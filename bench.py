@@ -40,7 +40,7 @@ def parse():
     ap.add_argument("--block-size", type=int, default=None, choices=[None, 16, 32])
     ap.add_argument("--layers", type=int, default=None)
     ap.add_argument("--partition-tokens", type=int, default=0)
-    ap.add_argument("--impl", default="auto", choices=["auto", "mfma", "vector"])
+    ap.add_argument("--impl", default="auto", choices=["auto", "mfma", "vector", "persistent"])
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample (0 disables)")
@@ -92,7 +92,8 @@ def main():
     bs = args.block_size or cfg.block_size
     L = args.layers or cfg.num_layers
     S, H, Hkv, D = cfg.num_seqs, cfg.num_heads, cfg.num_kv_heads, cfg.head_dim
-    impl = {"auto": pkv.IMPL_AUTO, "mfma": pkv.IMPL_MFMA, "vector": pkv.IMPL_VECTOR}[args.impl]
+    impl = {"auto": pkv.IMPL_AUTO, "mfma": pkv.IMPL_MFMA, "vector": pkv.IMPL_VECTOR,
+            "persistent": pkv.IMPL_MFMA_PERSISTENT}[args.impl]
     part = args.partition_tokens
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
@@ -238,8 +239,9 @@ def main():
         "seq_layers_per_s": round(S * L / (step_ms * 1e-3), 1),
         "roofline": {
             "bound": "hbm",
-            "kernel": "paged_decode_mfma_kernel" if impl != pkv.IMPL_VECTOR
-                      else "paged_decode_vector_kernel",
+            "kernel": {pkv.IMPL_VECTOR: "paged_decode_vector_kernel",
+                       pkv.IMPL_MFMA_PERSISTENT: "paged_decode_mfma_persistent"}.get(
+                           impl, "paged_decode_mfma_kernel"),
             "achieved": round(achieved, 1),
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",

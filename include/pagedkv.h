@@ -202,8 +202,13 @@ int32_t reshape_and_cache(const void* key, const void* value,
 /* Implementation selector for paged_attention_decode_ex. */
 enum {
     PKV_IMPL_AUTO = 0,    /* matrix-core kernel */
-    PKV_IMPL_MFMA = 1,    /* GQA group on 16x16 MFMA tiles */
-    PKV_IMPL_VECTOR = 2   /* same math on the vector ALU (for comparison) */
+    PKV_IMPL_MFMA = 1,    /* GQA group on 16x16 MFMA tiles, one workgroup
+                             per (item, kv head) of the plan */
+    PKV_IMPL_VECTOR = 2,  /* same math on the vector ALU (for comparison) */
+    PKV_IMPL_MFMA_PERSISTENT = 3  /* MFMA, resident workgroups claiming
+                             plan entries from an atomic counter in the
+                             plan header; a plan must then not be shared
+                             by launches that run concurrently */
 };
 
 /* Which kernels one call launches (bit mask; default both). */

@@ -7,7 +7,7 @@ fallback: if the library is missing or fails to load, importing the binding
 raises.
 """
 from ._binding import (  # noqa: F401
-    BF16, FP16, FP8_E4M3, IMPL_AUTO, IMPL_MFMA, IMPL_VECTOR, STAGE_PARTITIONS, STAGE_REDUCE,
+    BF16, FP16, FP8_E4M3, IMPL_AUTO, IMPL_MFMA, IMPL_VECTOR, IMPL_MFMA_PERSISTENT, STAGE_PARTITIONS, STAGE_REDUCE,
     PagedKVError, KVPool, lib, lib_path, version, last_error, bytes_per_token, tile_bytes,
     layer_pool_bytes, workspace_bytes, default_partition_tokens, plan_bytes, build_plan,
     decode_slot_mapping, reshape_and_cache,

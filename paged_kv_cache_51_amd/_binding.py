@@ -15,7 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.environ.get("PKV_LIB") or os.path.join(HERE, "lib", "libpagedkv.so")
 
 BF16, FP16, FP8_E4M3 = 0, 1, 2
-IMPL_AUTO, IMPL_MFMA, IMPL_VECTOR = 0, 1, 2
+IMPL_AUTO, IMPL_MFMA, IMPL_VECTOR, IMPL_MFMA_PERSISTENT = 0, 1, 2, 3
 STAGE_PARTITIONS, STAGE_REDUCE = 1, 2
 
 # Every symbol include/pagedkv.h declares.

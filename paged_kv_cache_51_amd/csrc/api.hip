@@ -328,7 +328,7 @@ int32_t paged_attention_decode_ex(void* out, const void* q, int32_t q_dtype, con
     if (!std::isfinite(scale)) return fail(PKV_ERR_ARG, "scale must be finite");
     if (kv_dtype == PKV_FP8_E4M3 && !(std::isfinite(k_scale) && std::isfinite(v_scale)))
         return fail(PKV_ERR_ARG, "fp8 scales must be finite");
-    if (o.impl < 0 || o.impl > 2) return fail(PKV_ERR_ARG, "impl %d unknown", o.impl);
+    if (o.impl < 0 || o.impl > 3) return fail(PKV_ERR_ARG, "impl %d unknown", o.impl);
     if (o.impl == PKV_IMPL_VECTOR && G > 8) return fail(PKV_ERR_UNSUPPORTED, "vector kernel supports at most 8 query heads per kv head");
     const int32_t stages = o.stages ? o.stages : (PKV_STAGE_PARTITIONS | PKV_STAGE_REDUCE);
     if (stages & ~(PKV_STAGE_PARTITIONS | PKV_STAGE_REDUCE)) return fail(PKV_ERR_ARG, "bad stages mask");

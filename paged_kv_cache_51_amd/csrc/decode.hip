@@ -28,6 +28,8 @@
 #include "pkv_device.h"
 #include "pkv_launch.h"
 
+#include <algorithm>
+
 namespace pkv {
 
 template <int KVT>
@@ -82,6 +84,9 @@ constexpr float kRescaleSlack = 8.0f;
 // Row stride (floats) of a head's partial output in the merge area: 128
 // dims plus 4 floats of padding to spread heads over LDS banks.
 constexpr int kMergeRow = kHeadDim + 4;
+
+// Plan header ints before the item list: [count][next entry][done][reserved].
+constexpr int kPlanHeader = 4;
 
 __host__ __device__ constexpr int merge_lds_floats(int nw, int g) { return 4 + 32 * nw + nw * g * kMergeRow; }
 
@@ -148,28 +153,16 @@ __device__ __forceinline__ void process_unit(const UnitRegs<KVT>& u, const u32x4
 #ifndef PKV_WAVES_PER_EU
 #define PKV_WAVES_PER_EU 1
 #endif
+// Decode one work entry: kv head `kvh` of plan item (sequence s,
+// partition part), by the NW waves of the calling workgroup.  Every exit
+// before the LDS counter barrier depends only on (s, part), so all waves of
+// the workgroup take it together.
 template <int KVT, int QT, int BS, int NW, int DEPTH>
-__global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(PKV_WAVES_PER_EU)))
-void paged_decode_mfma_kernel(const DecodeArgs a) {
+__device__ __forceinline__ void decode_entry(const DecodeArgs& a, float* pkv_smem, int s, int part,
+                                             int kvh, int lane, int w) {
     constexpr int NSUB = BS / kSubTokens;
     constexpr int64_t SUB = sub_tile_bytes(KVT);
     constexpr int64_t TILE = SUB * NSUB;
-    // Dynamic LDS (merge_lds_floats): [counter pad 4][m NW*16][l NW*16]
-    // [acc NW*G rows of kMergeRow floats].
-    extern __shared__ float pkv_smem[];
-
-    const int lane = threadIdx.x & (kWave - 1);
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    // One workgroup per (plan item, kv head), head fastest: the plan lists
-    // the (sequence, partition) items longest first, so the dispatcher's
-    // greedy in-order placement runs long work first and the heads of one
-    // item spread over consecutive XCDs.
-    const int item = blockIdx.x / a.num_kv_heads;
-    const int kvh = blockIdx.x - item * a.num_kv_heads;
-    const int n_items = a.plan[0];
-    const uint32_t packed = (uint32_t)a.plan[4 + item];   // in bounds; valid if item < n_items
-    if (item >= n_items) return;
-    const int s = (int)(packed >> 16), part = (int)(packed & 0xffffu);
     const int G = a.group;
     const int units_per_part = a.part_blocks * NSUB;
     const int u0 = part * units_per_part;
@@ -363,6 +356,63 @@ void paged_decode_mfma_kernel(const DecodeArgs a) {
     }
 }
 
+// One workgroup per work entry (plan item x kv head, head fastest): the
+// plan lists items longest first, so the dispatcher's greedy in-order
+// placement runs long work first and the heads of an item spread over
+// consecutive XCDs.
+template <int KVT, int QT, int BS, int NW, int DEPTH>
+__global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(PKV_WAVES_PER_EU)))
+void paged_decode_mfma_kernel(const DecodeArgs a) {
+    // Dynamic LDS (merge_lds_floats): [counters 4][m NW*16][l NW*16]
+    // [acc NW*G rows of kMergeRow floats].
+    extern __shared__ float pkv_smem[];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int item = blockIdx.x / a.num_kv_heads;
+    const int kvh = blockIdx.x - item * a.num_kv_heads;
+    const int n_items = a.plan[0];
+    const uint32_t packed = (uint32_t)a.plan[kPlanHeader + item];   // in bounds; valid if item < n_items
+    if (item >= n_items) return;
+    decode_entry<KVT, QT, BS, NW, DEPTH>(a, pkv_smem, (int)(packed >> 16), (int)(packed & 0xffffu),
+                                          kvh, lane, w);
+}
+
+// Persistent form: as many workgroups as fit on the GPU at once, each
+// claiming the next work entry of the longest-first plan from an atomic
+// counter until the plan is exhausted.  CUs (and XCDs) that run faster
+// simply take more entries.  The counters live in the plan header
+// (zeroed by the planner); the last workgroup to leave resets them, so
+// the plan can serve the next launch on the same stream.
+template <int KVT, int QT, int BS, int NW, int DEPTH>
+__global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(PKV_WAVES_PER_EU)))
+void paged_decode_mfma_persistent(const DecodeArgs a) {
+    extern __shared__ float pkv_smem[];
+    int* sm_entry = reinterpret_cast<int*>(pkv_smem) + 1;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    int32_t* counters = const_cast<int32_t*>(a.plan) + 1;   // [0] next entry, [1] workgroups done
+    const int total = a.plan[0] * a.num_kv_heads;
+    for (;;) {
+        if (threadIdx.x == 0) *sm_entry = atomicAdd(&counters[0], 1);
+        __syncthreads();
+        const int k = __builtin_amdgcn_readfirstlane(*sm_entry);
+        __syncthreads();
+        if (k >= total) break;
+        const int item = k / a.num_kv_heads;
+        const int kvh = k - item * a.num_kv_heads;
+        const uint32_t packed = (uint32_t)a.plan[kPlanHeader + item];
+        decode_entry<KVT, QT, BS, NW, DEPTH>(a, pkv_smem, (int)(packed >> 16),
+                                              (int)(packed & 0xffffu), kvh, lane, w);
+    }
+    if (threadIdx.x == 0) {
+        __threadfence();
+        if (atomicAdd(&counters[1], 1) == (int)gridDim.x - 1) {
+            atomicExch(&counters[0], 0);
+            atomicExch(&counters[1], 0);
+        }
+    }
+}
+
 // Merge the partitions of every multi-partition sequence: with per-partition
 // max m_p (log2 units), normaliser l_p and normalised output o_p,
 //   out = sum_p 2^(m_p - M) l_p o_p / sum_p 2^(m_p - M) l_p,  M = max_p m_p.
@@ -410,17 +460,39 @@ constexpr int kWavesPerGroup = PKV_WAVES_PER_GROUP;
 constexpr int kDepth = PKV_PIPELINE_DEPTH;
 
 template <int KVT, int QT, int BS>
-static hipError_t launch_mfma(const DecodeArgs& a, hipStream_t st) {
-    dim3 grid(a.num_seqs * a.num_kv_heads * a.num_parts);
+static hipError_t launch_mfma(const DecodeArgs& a, bool persistent, hipStream_t st) {
     const size_t lds = sizeof(float) * merge_lds_floats(kWavesPerGroup, a.group);
-    hipLaunchKernelGGL((paged_decode_mfma_kernel<KVT, QT, BS, kWavesPerGroup, kDepth>), grid,
-                       dim3(kWavesPerGroup * kWave), lds, st, a);
+    const dim3 block(kWavesPerGroup * kWave);
+    if (!persistent) {
+        const dim3 grid(a.num_seqs * a.num_kv_heads * a.num_parts);
+        hipLaunchKernelGGL((paged_decode_mfma_kernel<KVT, QT, BS, kWavesPerGroup, kDepth>), grid,
+                           block, lds, st, a);
+        return hipGetLastError();
+    }
+    // as many workgroups as can be resident at once (never more than entries)
+    static int per_cu[17] = {0};              // cache by group size (LDS use)
+    int& occ = per_cu[a.group];
+    if (!occ) {
+        hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &occ, reinterpret_cast<const void*>(&paged_decode_mfma_persistent<KVT, QT, BS, kWavesPerGroup, kDepth>),
+            block.x, lds);
+        if (e != hipSuccess || occ <= 0) occ = 1;
+    }
+    int dev = 0, cus = 0;
+    (void)hipGetDevice(&dev);
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        cus = 256;
+    const int64_t entries = (int64_t)a.num_seqs * a.num_kv_heads * a.num_parts;
+    const dim3 grid((unsigned)std::min<int64_t>(entries, (int64_t)occ * cus));
+    hipLaunchKernelGGL((paged_decode_mfma_persistent<KVT, QT, BS, kWavesPerGroup, kDepth>), grid, block,
+                       lds, st, a);
     return hipGetLastError();
 }
 
 template <int KVT, int QT>
-static hipError_t launch_mfma_bs(const DecodeArgs& a, int bs, hipStream_t st) {
-    return bs == 16 ? launch_mfma<KVT, QT, 16>(a, st) : launch_mfma<KVT, QT, 32>(a, st);
+static hipError_t launch_mfma_bs(const DecodeArgs& a, int bs, bool persistent, hipStream_t st) {
+    return bs == 16 ? launch_mfma<KVT, QT, 16>(a, persistent, st)
+                    : launch_mfma<KVT, QT, 32>(a, persistent, st);
 }
 
 hipError_t launch_decode_vector(const DecodeArgs& a, int q_dtype, int kv_dtype, int block_size,
@@ -430,12 +502,13 @@ hipError_t launch_decode_partitions(const DecodeArgs& a, int q_dtype, int kv_dty
                                     int block_size, int impl, hipStream_t st) {
     if (a.num_seqs == 0 || a.num_parts == 0) return hipSuccess;
     if (impl == 2) return launch_decode_vector(a, q_dtype, kv_dtype, block_size, st);
+    const bool persistent = impl == 3;
     if (q_dtype == DT_BF16) {
-        if (kv_dtype == DT_BF16) return launch_mfma_bs<DT_BF16, DT_BF16>(a, block_size, st);
-        return launch_mfma_bs<DT_FP8, DT_BF16>(a, block_size, st);
+        if (kv_dtype == DT_BF16) return launch_mfma_bs<DT_BF16, DT_BF16>(a, block_size, persistent, st);
+        return launch_mfma_bs<DT_FP8, DT_BF16>(a, block_size, persistent, st);
     }
-    if (kv_dtype == DT_FP16) return launch_mfma_bs<DT_FP16, DT_FP16>(a, block_size, st);
-    return launch_mfma_bs<DT_FP8, DT_FP16>(a, block_size, st);
+    if (kv_dtype == DT_FP16) return launch_mfma_bs<DT_FP16, DT_FP16>(a, block_size, persistent, st);
+    return launch_mfma_bs<DT_FP8, DT_FP16>(a, block_size, persistent, st);
 }
 
 hipError_t launch_decode_reduce(const DecodeArgs& a, int q_dtype, int block_size,

@@ -8,7 +8,9 @@
 // kv heads with the head fastest, so the heads of one item land on
 // consecutive XCDs (workgroups go to the 8 XCDs round-robin).
 //
-// Plan layout (int32): [0] item count, [1..3] reserved, [4 + i] item i as
+// Plan layout (int32): [0] item count, [1] next work entry and [2] finished
+// workgroups of the persistent decode (zeroed here, reset by the last
+// workgroup of each launch), [3] reserved, [4 + i] item i as
 // (sequence << 16) | partition.  Built by one workgroup with a counting sort
 // on the item size in 16-token units (sizes above kMaxBucket share the top
 // bucket).
@@ -81,7 +83,12 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
             run += cnt;
         }
     }
-    if (tid == kPlanThreads - 1) plan[0] = scan_tmp[kPlanThreads - 1];
+    if (tid == kPlanThreads - 1) {
+        plan[0] = scan_tmp[kPlanThreads - 1];
+        plan[1] = 0;   // persistent decode: next entry to claim
+        plan[2] = 0;   // persistent decode: workgroups finished
+        plan[3] = 0;
+    }
     __syncthreads();
 
     for (int s = tid; s < num_seqs; s += kPlanThreads) {

@@ -387,3 +387,40 @@ def test_null_block_poison():
         assert (h[:tile].view(np.uint16) == 0x7FC0).all()
         assert (h[tile:] == 0).all()
     pool.close()
+
+
+@pytest.mark.parametrize("cfg,kv", [("tiny", oracle.BF16), ("qwen15b", oracle.BF16),
+                                    ("qwen15b", oracle.FP8)])
+def test_persistent_matches_grid_bitwise_and_reuses_plan(cfg, kv):
+    """The persistent launch (work entries claimed from the plan's atomic
+    counter) runs the same per-entry code as the one-workgroup-per-entry
+    launch: outputs must be bitwise equal, on three launches that share one
+    plan (the last workgroup of each launch resets the counters)."""
+    log(f"persistent vs grid {cfg} kv={kv}")
+    c, tabs, _, r_val = workloads.make(cfg)
+    Hkv, H, bs = c.num_kv_heads, c.num_heads, c.block_size
+    ks = vs = 0.05 if kv == oracle.FP8 else 1.0
+    kb = [workloads.normal_bits(r_val, (int(x), Hkv, D), oracle.BF16) for x in tabs.context_lens]
+    vb = [workloads.normal_bits(r_val, (int(x), Hkv, D), oracle.BF16) for x in tabs.context_lens]
+    qb = workloads.normal_bits(r_val, (len(tabs.context_lens), H, D), oracle.BF16)
+    kp, vp = pools.write_contiguous(kb, vb, tabs.block_tables, tabs.context_lens, Hkv, D, bs,
+                                    tabs.num_blocks, kv, oracle.BF16, ks, vs)
+    want = oracle.paged_decode(qb, oracle.BF16, kp, vp, kv, tabs.block_tables,
+                               tabs.context_lens, Hkv, bs, SCALE, ks, vs)
+    kd, vd, bt, cl = dev8(kp), dev8(vp), devi(tabs.block_tables), devi(tabs.context_lens)
+    q = dev16(qb, oracle.BF16)
+    mc = int(tabs.context_lens.max())
+    plan = pkv.build_plan(cl, mc, bt.shape[1], Hkv, bs)
+    outs = []
+    for impl in (pkv.IMPL_MFMA, pkv.IMPL_MFMA_PERSISTENT, pkv.IMPL_MFMA_PERSISTENT,
+                 pkv.IMPL_MFMA_PERSISTENT):
+        out = torch.full_like(q, float("nan"))
+        pkv.paged_attention_decode(out, q, kd, vd, bt, cl, mc, Hkv, bs, kv, SCALE, ks, vs,
+                                   impl=impl, num_blocks=tabs.num_blocks, plan=plan)
+        torch.cuda.synchronize()
+        outs.append(out.float().cpu().numpy().astype(np.float64))
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
+    check(outs[0], want, kv, f"{cfg} persistent")
+    counters = plan[4:12].cpu().numpy().view(np.int32)
+    assert (counters == 0).all(), "persistent launch left its counters set"
