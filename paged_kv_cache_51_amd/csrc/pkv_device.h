@@ -145,4 +145,21 @@ __device__ __forceinline__ float xor_shfl(float v, int mask) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Dword of lane `src` (any lane of the wave), read by every lane.
+__device__ __forceinline__ uint32_t lane_fetch(uint32_t v, int src) {
+    return (uint32_t)__builtin_amdgcn_ds_bpermute(src << 2, (int)v);
+}
+
+// a.x * b.x + a.y * b.y + c on two packed 16-bit pairs of type DT (vector
+// ALU dot instruction, fp32 accumulate).
+template <int DT>
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+    if constexpr (DT == DT_BF16)
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                               __builtin_bit_cast(bf16x2_t, b), c, false);
+    else
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a), __builtin_bit_cast(f16x2_t, b),
+                                      c, false);
+}
+
 }  // namespace pkv

@@ -424,3 +424,83 @@ def test_persistent_matches_grid_bitwise_and_reuses_plan(cfg, kv):
     check(outs[0], want, kv, f"{cfg} persistent")
     counters = plan[4:12].cpu().numpy().view(np.int32)
     assert (counters == 0).all(), "persistent launch left its counters set"
+
+
+# ---------------------------------------------------- vector-ALU kernel ----
+# The same partition kernel with its per-unit math on the vector ALU (dot2)
+# instead of the matrix cores; held to the same bars against the oracle.
+
+IMPL_VECTOR = 2
+
+
+@pytest.mark.parametrize("kv,q,bs", [
+    (oracle.BF16, oracle.BF16, 16), (oracle.FP16, oracle.FP16, 16),
+    (oracle.BF16, oracle.BF16, 32), (oracle.FP8, oracle.BF16, 16),
+    (oracle.FP8, oracle.FP16, 32),
+])
+@pytest.mark.parametrize("part", [32, 256, 4096])
+def test_vector_decode_tiny(kv, q, bs, part):
+    log(f"vector decode tiny kv={kv} q={q} bs={bs} part={part}")
+    lengths = [1, 17, 64, 200]
+    ks, vs = (0.02, 0.03) if kv == oracle.FP8 else (1.0, 1.0)
+    tabs, qb, kp, vp = make_case(lengths, 12, 2, bs, kv, q, num_blocks=64 if bs == 16 else 40,
+                                 ks=ks, vs=vs)
+    want = oracle.paged_decode(qb, q, kp, vp, kv, tabs.block_tables, tabs.context_lens, 2, bs,
+                               SCALE, ks, vs)
+    got = gpu_decode(qb, q, kp, vp, kv, tabs.block_tables, tabs.context_lens, 2, bs, SCALE,
+                     ks, vs, part=part, impl=IMPL_VECTOR, num_blocks=tabs.num_blocks)
+    check(got, want, kv, f"vector tiny part={part}")
+
+
+@pytest.mark.parametrize("H,Hkv", [(4, 4), (8, 2), (28, 4), (16, 2), (12, 2)])
+def test_vector_group_sizes(H, Hkv):
+    log(f"vector group sizes H={H} Hkv={Hkv}")
+    lengths = [5, 16, 33, 130, 300, 47]
+    tabs, qb, kp, vp = make_case(lengths, H, Hkv, 16, oracle.BF16, oracle.BF16, seed=3)
+    want = oracle.paged_decode(qb, oracle.BF16, kp, vp, oracle.BF16, tabs.block_tables,
+                               tabs.context_lens, Hkv, 16, SCALE)
+    for part in (64, 512):
+        got = gpu_decode(qb, oracle.BF16, kp, vp, oracle.BF16, tabs.block_tables,
+                         tabs.context_lens, Hkv, 16, SCALE, part=part, impl=IMPL_VECTOR,
+                         num_blocks=tabs.num_blocks)
+        check(got, want, oracle.BF16, f"vector G={H // Hkv} part={part}")
+
+
+def test_vector_rejects_groups_above_8():
+    tabs, qb, kp, vp = make_case([20, 3], 32, 2, 16, oracle.BF16, oracle.BF16, seed=5)
+    with pytest.raises(pkv.PagedKVError):
+        gpu_decode(qb, oracle.BF16, kp, vp, oracle.BF16, tabs.block_tables, tabs.context_lens,
+                   2, 16, SCALE, impl=IMPL_VECTOR, num_blocks=tabs.num_blocks)
+
+
+def test_vector_zero_context_and_c1_exact():
+    log("vector zero context / c=1")
+    tabs, qb, kp, vp = make_case([0, 1, 1, 40], 8, 2, 16, oracle.BF16, oracle.BF16, seed=9)
+    got = gpu_decode(qb, oracle.BF16, kp, vp, oracle.BF16, tabs.block_tables,
+                     tabs.context_lens, 2, 16, SCALE, part=16, impl=IMPL_VECTOR,
+                     num_blocks=tabs.num_blocks)
+    want = oracle.paged_decode(qb, oracle.BF16, kp, vp, oracle.BF16, tabs.block_tables,
+                               tabs.context_lens, 2, 16, SCALE)
+    assert np.array_equal(got[0], np.zeros((8, D)))
+    assert np.array_equal(got[1:3], want[1:3])      # one token: its V, exactly
+    check(got, want, oracle.BF16, "vector zero ctx")
+
+
+@pytest.mark.parametrize("cfg,kv", [("qwen15b", oracle.BF16), ("qwen15b", oracle.FP8)])
+def test_vector_workload_shape(cfg, kv):
+    """A whole small workload (all sequences, shared prefixes, default
+    partition and device plan) through the vector kernel."""
+    log(f"vector workload {cfg} kv={kv}")
+    c, tabs, _, r_val = workloads.make(cfg)
+    Hkv, H, bs = c.num_kv_heads, c.num_heads, c.block_size
+    ks = vs = 0.05 if kv == oracle.FP8 else 1.0
+    kb = [workloads.normal_bits(r_val, (int(x), Hkv, D), oracle.BF16) for x in tabs.context_lens]
+    vb = [workloads.normal_bits(r_val, (int(x), Hkv, D), oracle.BF16) for x in tabs.context_lens]
+    qb = workloads.normal_bits(r_val, (len(tabs.context_lens), H, D), oracle.BF16)
+    kp, vp = pools.write_contiguous(kb, vb, tabs.block_tables, tabs.context_lens, Hkv, D, bs,
+                                    tabs.num_blocks, kv, oracle.BF16, ks, vs)
+    want = oracle.paged_decode(qb, oracle.BF16, kp, vp, kv, tabs.block_tables,
+                               tabs.context_lens, Hkv, bs, SCALE, ks, vs)
+    got = gpu_decode(qb, oracle.BF16, kp, vp, kv, tabs.block_tables, tabs.context_lens, Hkv, bs,
+                     SCALE, ks, vs, impl=IMPL_VECTOR, num_blocks=tabs.num_blocks)
+    check(got, want, kv, f"vector {cfg}")
