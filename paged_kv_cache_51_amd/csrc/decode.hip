@@ -228,7 +228,7 @@ static hipError_t launch_mfma(const DecodeArgs& a, bool persistent, hipStream_t 
     const size_t lds = sizeof(float) * merge_lds_floats(kWavesPerGroup, a.group);
     const dim3 block(kWavesPerGroup * kWave);
     if (!persistent) {
-        const dim3 grid(a.num_seqs * a.num_kv_heads * a.num_parts);
+        const dim3 grid((unsigned)grid_workgroups(a));
         hipLaunchKernelGGL((paged_decode_mfma_kernel<KVT, QT, BS, kWavesPerGroup, kDepth>), grid,
                            block, lds, st, a);
         return hipGetLastError();

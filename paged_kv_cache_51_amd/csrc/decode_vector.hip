@@ -170,7 +170,7 @@ static hipError_t launch_vector(const DecodeArgs& a, hipStream_t st) {
     if (a.group > VectorMath<KVT, QT>::kMaxGroup) return hipErrorNotSupported;
     const size_t lds = sizeof(float) * (merge_lds_floats(kWavesPerGroup, a.group) +
                                         VectorMath<KVT, QT>::query_lds_floats(a.group));
-    const dim3 grid(a.num_seqs * a.num_kv_heads * a.num_parts);
+    const dim3 grid((unsigned)grid_workgroups(a));
     hipLaunchKernelGGL((paged_decode_vector_kernel<KVT, QT, BS, kWavesPerGroup, kDepth>), grid,
                        dim3(kWavesPerGroup * kWave), lds, st, a);
     return hipGetLastError();

@@ -504,3 +504,4 @@ def test_vector_workload_shape(cfg, kv):
     got = gpu_decode(qb, oracle.BF16, kp, vp, kv, tabs.block_tables, tabs.context_lens, Hkv, bs,
                      SCALE, ks, vs, impl=IMPL_VECTOR, num_blocks=tabs.num_blocks)
     check(got, want, kv, f"vector {cfg}")
+
