@@ -203,8 +203,11 @@ int32_t reshape_and_cache(const void* key, const void* value,
 enum {
     PKV_IMPL_AUTO = 0,    /* matrix-core kernel */
     PKV_IMPL_MFMA = 1,    /* GQA group on 16x16 MFMA tiles, one workgroup
-                             per (item, kv head) of the plan */
-    PKV_IMPL_VECTOR = 2,  /* same math on the vector ALU (for comparison) */
+                             per (item, kv head) of the plan, the heads of
+                             an item on one XCD */
+    PKV_IMPL_VECTOR = 2,  /* same plan, layout and merge with the per-unit
+                             math on the vector ALU (dot2), for comparison;
+                             G <= 8, else PKV_ERR_UNSUPPORTED */
     PKV_IMPL_MFMA_PERSISTENT = 3  /* MFMA, resident workgroups claiming
                              plan entries from an atomic counter in the
                              plan header; a plan must then not be shared
