@@ -46,6 +46,11 @@ def parse():
                     help="target CPU time of the oracle sample (0 disables)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one device copy of this size (counter calibration)")
+    ap.add_argument("--op", default="decode", choices=["decode", "copy_blocks"],
+                    help="decode: the attention step (default); copy_blocks: copy-on-write "
+                         "block copies over the same pool shape")
+    ap.add_argument("--copy-pairs", type=int, default=2048,
+                    help="copy_blocks: (src, dst) block pairs per call")
     return ap.parse_args()
 
 
@@ -82,6 +87,10 @@ def main():
     import torch
     import paged_kv_cache_51_amd as pkv
     import workloads
+
+    if args.op == "copy_blocks":
+        bench_copy_blocks(args, torch, pkv, workloads)
+        return
 
     dt_names = {"bf16": pkv.BF16, "fp16": pkv.FP16, "fp8": pkv.FP8_E4M3}
     cfg, tabs, _, _ = workloads.make(args.config, seed=args.seed, block_size=args.block_size)
@@ -253,6 +262,82 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
+
+
+def bench_copy_blocks(args, torch, pkv, workloads):
+    """Copy-on-write block copies: one call copies `--copy-pairs` random
+    (src, dst) blocks in every layer's K and V pool of the workload's pool
+    shape.  A step is one call; bytes = pairs x layers x 2 pools x block
+    bytes, read and written."""
+    dt_names = {"bf16": pkv.BF16, "fp16": pkv.FP16, "fp8": pkv.FP8_E4M3}
+    cfg = workloads.CONFIGS[args.config]
+    kv = dt_names[args.kv_dtype] if args.kv_dtype else cfg.kv_dtype
+    bs = args.block_size or cfg.block_size
+    L = args.layers or cfg.num_layers
+    Hkv, D = cfg.num_kv_heads, cfg.head_dim
+    npairs = args.copy_pairs
+    nb = 1 + 4 * npairs                       # room for disjoint sources and destinations
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    pool_bytes = pkv.layer_pool_bytes(nb, Hkv, D, bs, kv)
+    block = pool_bytes // nb
+    ks = [torch.empty(pool_bytes, dtype=torch.uint8, device=dev) for _ in range(L)]
+    vs = [torch.empty(pool_bytes, dtype=torch.uint8, device=dev) for _ in range(L)]
+    for i, t in enumerate(ks + vs):
+        workloads.device_fill_normal(t, kv, 3000 + i, scale=8.0 / 448.0)
+    r = np.random.default_rng(args.seed)
+    perm = r.permutation(np.arange(1, nb))
+    pairs_np = np.stack([perm[:npairs], perm[npairs:2 * npairs]], 1).astype(np.int32)
+    pairs = torch.from_numpy(pairs_np).to(dev)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        pkv.copy_blocks(ks, vs, pairs, nb, Hkv, D, bs, kv, stream=stream)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for k in range(args.steps):
+        evs[k][0].record(stream)
+        pkv.copy_blocks(ks, vs, pairs, nb, Hkv, D, bs, kv, stream=stream)
+        evs[k][1].record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    step_ms = start.elapsed_time(end) / args.steps
+    launch_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    nbytes = npairs * L * 2 * block * 2
+    gbs = nbytes / (step_ms * 1e-3) / 1e9
+    achieved = nbytes / (launch_ms * 1e-3) / 1e9
+    print(f"[bench] copy_blocks: {npairs} pairs x {L} layers x K,V, block {block} B; "
+          f"{launch_ms * 1e3:.1f} us per call, {achieved:.0f} GB/s", file=sys.stderr, flush=True)
+    cpu = None
+    if args.cpu_baseline_seconds > 0:
+        import oracle.blocks as ob
+        hk = [ks[0].cpu().numpy()]
+        hv = [vs[0].cpu().numpy()]
+        n = min(npairs, 256)
+        t0 = time.time()
+        ob.copy_blocks(hk, hv, pairs_np[:n].tolist(), block)
+        dt = time.time() - t0
+        cpu = {"value": round(n * 2 * block * 2 / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
+               "kind": "oracle",
+               "sample": f"layer 0, first {n} of {npairs} pairs, numpy slice copies"}
+    dt_name = {pkv.BF16: "bf16", pkv.FP16: "fp16", pkv.FP8_E4M3: "fp8"}
+    print(json.dumps({
+        "metric": "copy_blocks HBM GB/s (bytes read + written)",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(step_ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "u8", "data": "synthetic",
+        "config": {"workload": f"copy-on-write copies: {npairs} random block pairs x {L} layers "
+                               f"x K and V, {cfg.description.split(':')[0]} pool shape "
+                               f"({Hkv} kv heads, d={D}, {dt_name[kv]}, bs={bs})",
+                   "pairs": npairs, "layers": L, "block_bytes": block,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": "copy_blocks_kernel", "achieved": round(achieved, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": None, "avg_launch_us": round(launch_ms * 1e3, 2),
+                     "algorithmic_bytes_per_launch": nbytes},
+        "cpu_baseline": cpu,
+    }), flush=True)
 
 
 def cpu_baseline(args, tabs, kpool, vpool, q, q_dtype, kv_dtype, Hkv, bs, scale, ks, vs, b_kv,

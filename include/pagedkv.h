@@ -337,6 +337,77 @@ int32_t pkv_check_block_tables(const int32_t* block_tables,
                                int32_t* scratch_dev, int64_t* bad_count,
                                pkv_stream_t stream);
 
+/* ---------------------------------------------------------- block manager --
+ *
+ * Host-side block pool that produces the block tables and slots the calls
+ * above consume ([P1] §4: blocks handed out one at a time as a request
+ * grows, block 0 reserved as the null block, a doubly linked queue of free
+ * blocks, reference counts and copy-on-write for shared blocks; [P2]
+ * "Sharing"; [P1] §5 prefix cache: a full block's hash chains its parent's
+ * hash, its tokens and an extra key, only full blocks are cached, a prompt
+ * recomputes at least its last token, freed blocks keep their content and
+ * are reused least recently freed first, a request returns its blocks last
+ * block first).  Where the order of reuse is open, free blocks holding no
+ * cached content are handed out before a cached block is evicted (the
+ * reading under which [P1] §10's block model prints 0 / 0 / 21,488 hits for
+ * its §9 experiment).
+ *
+ * Sequences are named by caller ids.  Slots are block * block_size +
+ * offset, as pkv_decode_slot_mapping computes them.  Not thread-safe: one
+ * handle, one thread at a time.  Host memory only; no GPU call is made.
+ * Errors: PKV_ERR_ARG (null, unknown or duplicate sequence id, range),
+ * PKV_ERR_SIZE (not enough free blocks: the state is left unchanged). */
+typedef struct pkv_block_manager pkv_block_manager;
+
+/* num_blocks includes the null block (so num_blocks - 1 are usable);
+ * prefix_caching != 0 keeps and reuses the content of full blocks. */
+int32_t pkv_bm_create(int32_t num_blocks, int32_t block_size, int32_t prefix_caching,
+                      pkv_block_manager** out);
+int32_t pkv_bm_destroy(pkv_block_manager* bm);
+/* Free blocks (no cached content + cached content), and the cached ones. */
+int32_t pkv_bm_num_free_blocks(const pkv_block_manager* bm);
+int32_t pkv_bm_num_cached_free_blocks(const pkv_block_manager* bm);
+/* Reference count of a block (the null block reports 1). */
+int32_t pkv_bm_ref_count(const pkv_block_manager* bm, int32_t block);
+int32_t pkv_bm_num_tokens(const pkv_block_manager* bm, int64_t seq_id);
+/* New sequence with a prompt of num_tokens tokens (host array): blocks for
+ * all of them; with the prefix cache, the longest cached run of leading
+ * full blocks is shared instead (*num_cached_tokens, a multiple of
+ * block_size, always < num_tokens), and the prompt's other full blocks are
+ * published.  extra_key separates otherwise equal prompts (salt, adapter). */
+int32_t pkv_bm_add_sequence(pkv_block_manager* bm, int64_t seq_id, const int32_t* tokens,
+                            int32_t num_tokens, uint64_t extra_key,
+                            int32_t* num_cached_tokens);
+/* Append one token: *slot receives its cache slot.  If the last block is
+ * shared and partly filled, it is replaced by a private block first and
+ * (*cow_src, *cow_dst) name the copy to run (pkv_copy_blocks) before the
+ * token is written; otherwise both are -1. */
+int32_t pkv_bm_append_token(pkv_block_manager* bm, int64_t seq_id, int32_t token,
+                            int32_t* slot, int32_t* cow_src, int32_t* cow_dst);
+/* child shares every block of parent (reference counts + 1). */
+int32_t pkv_bm_fork(pkv_block_manager* bm, int64_t parent_id, int64_t child_id);
+/* Drop the sequence; its blocks lose a reference, last block first. */
+int32_t pkv_bm_free_sequence(pkv_block_manager* bm, int64_t seq_id);
+/* The block table as a row of max_blocks ids (host array), padded with the
+ * null block 0; *num_blocks = blocks in use (PKV_ERR_SIZE if > max_blocks). */
+int32_t pkv_bm_block_table(const pkv_block_manager* bm, int64_t seq_id, int32_t* table,
+                           int32_t max_blocks, int32_t* num_blocks);
+/* Slots of positions [first_pos, first_pos + count) (host array). */
+int32_t pkv_bm_slots(const pkv_block_manager* bm, int64_t seq_id, int32_t first_pos,
+                     int32_t count, int32_t* slots);
+
+/* Copy whole blocks (all kv heads, K and V, every layer) from pairs[i][0]
+ * to pairs[i][1] ([P1] §4 copy-on-write): pairs is a device int32 array of
+ * num_pairs (src, dst); k_layers / v_layers are host arrays of num_layers
+ * device pool pointers (layout above).  A pair naming a block outside
+ * [1, num_blocks), or src == dst, is skipped.  Destinations must be distinct
+ * and must not be sources of other pairs in the same call.  Errors:
+ * PKV_ERR_ARG, PKV_ERR_HIP. */
+int32_t pkv_copy_blocks(void* const* k_layers, void* const* v_layers, int32_t num_layers,
+                        int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
+                        int32_t block_size, int32_t kv_dtype, const int32_t* pairs,
+                        int32_t num_pairs, pkv_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

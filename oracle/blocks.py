@@ -1,0 +1,176 @@
+"""Reference model of the block pool — TEST INFRASTRUCTURE ONLY (same rule
+as the rest of oracle/: imported by tests/ only).
+
+A plain, slow model of what the block manager computes, written from the
+pages, sharing no code with the library:
+
+  [P1] "LLM inference basics and vLLM internals" (ttlab.hopto.org),
+       §4 PagedAttention and block management: blocks of 16 tokens handed
+       out one at a time, a per-request table from logical to physical
+       blocks, waste only in a request's last block, one physical block
+       shared by equal prefixes (reference count, copy-on-write), a free
+       queue, block 0 reserved as the null block.
+       §5 prefix cache: a block's hash comes from its parent's hash, its
+       tokens and extra keys, so only prefixes match; only full blocks are
+       cached, hits are whole blocks, the last prompt token is always
+       recomputed; a finished request gives its blocks back with their
+       content, the queue front is reused first (least recently used), and
+       a request gives its blocks back last block first.
+       §9 / §10: the LRU experiment and the block-level model of it.
+  [P2] "vLLM internals (2)" (youngju.dev), "Sharing".
+
+Readings (where the pages leave it open):
+  - free blocks that hold no reusable content (never used, or a partial
+    block, which has no hash) are handed out before any cached block is
+    evicted — the block model of [P1] §10 does this, and it is the reading
+    under which that model prints 0 / 0 / 21,488;
+  - content keys are exact: key(block j) = (key(block j-1), its tokens),
+    rooted at the extra key.  A hash of that chain, as the pages describe,
+    matches exactly these keys up to collisions;
+  - the prompt's full blocks are published when the sequence is added
+    (their K/V is written by the prefill of the same step), appended full
+    blocks when their last token is appended; content already cached under
+    the same key is not published twice.
+"""
+
+
+class BlockPoolModel:
+    """One block pool.  Block ids 1..num_blocks-1 are usable; 0 is null."""
+
+    def __init__(self, num_blocks, block_size, prefix_caching=False):
+        self.bs = block_size
+        self.prefix = prefix_caching
+        self.ref = [0] * num_blocks
+        self.ref[0] = 1                              # the null block stays taken
+        self.clean = list(range(1, num_blocks))      # free, nothing cached; front first
+        self.cached = []                             # free, cached content; front = least recently freed
+        self.key_of = {}                             # block -> content key
+        self.block_of = {}                           # content key -> block
+        self.seqs = {}                               # id -> {"blocks", "tokens", "keys", "root"}
+
+    # -- pool ([P1] §4 free queue; §5 reuse order) --------------------------
+    def free_count(self):
+        return len(self.clean) + len(self.cached)
+
+    num_free_blocks = free_count
+
+    def num_cached_free_blocks(self):
+        return len(self.cached)
+
+    def ref_count(self, b):
+        return self.ref[b]
+
+    def _take(self):
+        if self.clean:
+            b = self.clean.pop(0)
+        else:
+            b = self.cached.pop(0)                   # evict: its content is gone
+            del self.block_of[self.key_of.pop(b)]
+        self.ref[b] = 1
+        return b
+
+    def _release(self, b):
+        self.ref[b] -= 1
+        if self.ref[b] == 0:
+            (self.cached if b in self.key_of else self.clean).append(b)
+
+    def _publish(self, b, key):
+        if key not in self.block_of:
+            self.block_of[key] = b
+            self.key_of[b] = key
+
+    # -- requests -------------------------------------------------------------
+    def add_sequence(self, sid, tokens, extra_key=0):
+        """Blocks for a prompt; returns the number of tokens served from the
+        prefix cache ([P1] §5)."""
+        assert sid not in self.seqs
+        bs, n = self.bs, len(tokens)
+        nblk = -(-n // bs)
+        root = ("root", extra_key)
+        keys, k = [], root
+        for j in range(n // bs):
+            k = (k, tuple(tokens[j * bs:(j + 1) * bs]))
+            keys.append(k)
+        hits = []
+        if self.prefix:
+            for j, k in enumerate(keys):
+                if (j + 1) * bs > n - 1 or k not in self.block_of:
+                    break
+                hits.append(self.block_of[k])
+        free_hits = sum(1 for b in hits if self.ref[b] == 0)
+        need = nblk - len(hits)
+        if need > self.free_count() - free_hits:
+            raise MemoryError("not enough free blocks")
+        blocks = []
+        for b in hits:
+            if self.ref[b] == 0:
+                self.cached.remove(b)
+            self.ref[b] += 1
+            blocks.append(b)
+        for j in range(len(hits), nblk):
+            b = self._take()
+            blocks.append(b)
+            if self.prefix and j < len(keys):
+                self._publish(b, keys[j])
+        self.seqs[sid] = {"blocks": blocks, "tokens": list(tokens), "keys": keys, "root": root}
+        return len(hits) * bs
+
+    def append_token(self, sid, token=0):
+        """Returns (slot, cow_src, cow_dst) ([P1] §4; copy-on-write)."""
+        s = self.seqs[sid]
+        bs = self.bs
+        pos = len(s["tokens"])
+        j, off = divmod(pos, bs)
+        src = dst = -1
+        if off == 0:
+            if self.free_count() < 1:
+                raise MemoryError("no free block")
+            s["blocks"].append(self._take())
+        elif self.ref[s["blocks"][j]] > 1:
+            if self.free_count() < 1:
+                raise MemoryError("no free block for copy-on-write")
+            src = s["blocks"][j]
+            dst = self._take()
+            self._release(src)
+            s["blocks"][j] = dst
+        s["tokens"].append(token)
+        if self.prefix and off == bs - 1:
+            parent = s["keys"][j - 1] if j else s["root"]
+            key = (parent, tuple(s["tokens"][j * bs:(j + 1) * bs]))
+            s["keys"].append(key)
+            self._publish(s["blocks"][j], key)
+        return s["blocks"][j] * bs + off, src, dst
+
+    def fork(self, parent, child):
+        assert child not in self.seqs
+        p = self.seqs[parent]
+        self.seqs[child] = {"blocks": list(p["blocks"]), "tokens": list(p["tokens"]),
+                            "keys": list(p["keys"]), "root": p["root"]}
+        for b in p["blocks"]:
+            self.ref[b] += 1
+
+    def free_sequence(self, sid):
+        s = self.seqs.pop(sid)
+        for b in reversed(s["blocks"]):              # last block first ([P1] §5)
+            self._release(b)
+
+    def block_table(self, sid):
+        return list(self.seqs[sid]["blocks"])
+
+    def slots(self, sid, first, count):
+        bl = self.seqs[sid]["blocks"]
+        return [bl[p // self.bs] * self.bs + p % self.bs for p in range(first, first + count)]
+
+
+def copy_blocks(k_pools, v_pools, pairs, block_bytes):
+    """Copy-on-write copies ([P1] §4): for every (src, dst) pair, the bytes
+    of physical block src (all kv heads) in every layer's K and V pool
+    (numpy uint8 arrays, modified in place) replace those of block dst.
+    Pairs naming block 0, a block outside the pool, or src == dst are
+    skipped."""
+    for pool in list(k_pools) + list(v_pools):
+        nb = len(pool) // block_bytes
+        for src, dst in pairs:
+            if 1 <= src < nb and 1 <= dst < nb and src != dst:
+                pool[dst * block_bytes:(dst + 1) * block_bytes] = \
+                    pool[src * block_bytes:(src + 1) * block_bytes]

@@ -26,6 +26,10 @@ EXPORTS = [
     "reshape_and_cache", "pkv_default_partition_tokens", "paged_attention_workspace_bytes",
     "paged_attention_plan_bytes", "paged_attention_plan", "paged_attention_decode",
     "paged_attention_decode_ex", "pkv_check_block_tables",
+    "pkv_bm_create", "pkv_bm_destroy", "pkv_bm_num_free_blocks", "pkv_bm_num_cached_free_blocks",
+    "pkv_bm_ref_count", "pkv_bm_num_tokens", "pkv_bm_add_sequence", "pkv_bm_append_token",
+    "pkv_bm_fork", "pkv_bm_free_sequence", "pkv_bm_block_table", "pkv_bm_slots",
+    "pkv_copy_blocks",
 ]
 
 
@@ -84,6 +88,21 @@ def lib():
                                                 ctypes.POINTER(DecodeOpts), p]),
             "pkv_check_block_tables": (i32, [p, i32, p, i32, i32, i32, p,
                                              ctypes.POINTER(ctypes.c_int64), p]),
+            "pkv_bm_create": (i32, [i32, i32, i32, ctypes.POINTER(p)]),
+            "pkv_bm_destroy": (i32, [p]),
+            "pkv_bm_num_free_blocks": (i32, [p]),
+            "pkv_bm_num_cached_free_blocks": (i32, [p]),
+            "pkv_bm_ref_count": (i32, [p, i32]),
+            "pkv_bm_num_tokens": (i32, [p, i64]),
+            "pkv_bm_add_sequence": (i32, [p, i64, p, i32, ctypes.c_uint64,
+                                          ctypes.POINTER(i32)]),
+            "pkv_bm_append_token": (i32, [p, i64, i32, ctypes.POINTER(i32), ctypes.POINTER(i32),
+                                          ctypes.POINTER(i32)]),
+            "pkv_bm_fork": (i32, [p, i64, i64]),
+            "pkv_bm_free_sequence": (i32, [p, i64]),
+            "pkv_bm_block_table": (i32, [p, i64, p, i32, ctypes.POINTER(i32)]),
+            "pkv_bm_slots": (i32, [p, i64, i32, i32, p]),
+            "pkv_copy_blocks": (i32, [p, p, i32, i32, i32, i32, i32, i32, p, i32, p]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -283,3 +302,92 @@ def check_block_tables(block_tables, context_lens, block_size, num_blocks, strea
         _ptr(context_lens, "context_lens", torch.int32), context_lens.shape[0], block_size,
         num_blocks, _ptr(scratch, "scratch"), ctypes.byref(bad), _stream(stream)))
     return int(bad.value)
+
+
+class BlockManager:
+    """Host-side block pool (pkv_bm_*): block tables, slots, reference counts,
+    copy-on-write and the prefix cache.  Lists of ints in, lists out."""
+
+    def __init__(self, num_blocks, block_size, prefix_caching=False):
+        h = ctypes.c_void_p()
+        _check(lib().pkv_bm_create(num_blocks, block_size, int(bool(prefix_caching)),
+                                   ctypes.byref(h)))
+        self._h = h
+        self.num_blocks = num_blocks
+        self.block_size = block_size
+
+    def close(self):
+        if self._h:
+            lib().pkv_bm_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def num_free_blocks(self):
+        return _check(lib().pkv_bm_num_free_blocks(self._h))
+
+    def num_cached_free_blocks(self):
+        return _check(lib().pkv_bm_num_cached_free_blocks(self._h))
+
+    def ref_count(self, block):
+        return _check(lib().pkv_bm_ref_count(self._h, block))
+
+    def num_tokens(self, seq_id):
+        return _check(lib().pkv_bm_num_tokens(self._h, seq_id))
+
+    def add_sequence(self, seq_id, tokens, extra_key=0):
+        """Returns the number of prompt tokens served from the prefix cache."""
+        arr = (ctypes.c_int32 * max(len(tokens), 1))(*tokens)
+        hit = ctypes.c_int32(0)
+        _check(lib().pkv_bm_add_sequence(self._h, seq_id, arr, len(tokens),
+                                         ctypes.c_uint64(extra_key), ctypes.byref(hit)))
+        return hit.value
+
+    def append_token(self, seq_id, token=0):
+        """Returns (slot, cow_src, cow_dst); cow_* are -1 unless a shared
+        block was replaced by a private copy."""
+        slot, src, dst = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+        _check(lib().pkv_bm_append_token(self._h, seq_id, token, ctypes.byref(slot),
+                                         ctypes.byref(src), ctypes.byref(dst)))
+        return slot.value, src.value, dst.value
+
+    def fork(self, parent_id, child_id):
+        _check(lib().pkv_bm_fork(self._h, parent_id, child_id))
+
+    def free_sequence(self, seq_id):
+        _check(lib().pkv_bm_free_sequence(self._h, seq_id))
+
+    def block_table(self, seq_id, max_blocks=None):
+        n = ctypes.c_int32(0)
+        rc = lib().pkv_bm_block_table(self._h, seq_id, None, 0, ctypes.byref(n))
+        if rc < 0 and rc != -2:
+            _check(rc)
+        m = n.value if max_blocks is None else max_blocks
+        arr = (ctypes.c_int32 * max(m, 1))()
+        _check(lib().pkv_bm_block_table(self._h, seq_id, arr, m, ctypes.byref(n)))
+        return list(arr[:m])
+
+    def slots(self, seq_id, first_pos, count):
+        arr = (ctypes.c_int32 * max(count, 1))()
+        _check(lib().pkv_bm_slots(self._h, seq_id, first_pos, count, arr))
+        return list(arr[:count])
+
+
+def copy_blocks(k_layers, v_layers, pairs, num_blocks, num_kv_heads, head_dim, block_size,
+                kv_dtype, stream=None):
+    """pkv_copy_blocks: copy whole blocks of every layer's K and V pool.
+    pairs: device int32 tensor [n, 2] of (src, dst)."""
+    n = len(k_layers)
+    if len(v_layers) != n:
+        raise ValueError("k_layers and v_layers differ in length")
+    kp = (ctypes.c_void_p * max(n, 1))(*[_ptr(t, "k_layers", torch.uint8).value for t in k_layers])
+    vp = (ctypes.c_void_p * max(n, 1))(*[_ptr(t, "v_layers", torch.uint8).value for t in v_layers])
+    if pairs.dim() != 2 or pairs.shape[1] != 2:
+        raise ValueError("pairs must be [n, 2]")
+    _check(lib().pkv_copy_blocks(kp, vp, n, num_blocks, num_kv_heads, head_dim, block_size,
+                                 kv_dtype, _ptr(pairs, "pairs", torch.int32), pairs.shape[0],
+                                 _stream(stream)))

@@ -15,7 +15,7 @@
 #include "../../include/pagedkv.h"
 #include "pkv_launch.h"
 
-namespace {
+namespace pkv {
 
 thread_local std::string g_err;
 
@@ -37,6 +37,16 @@ int32_t ok() {
 int32_t hip_fail(hipError_t e, const char* what) {
     return fail(PKV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
+
+const char* last_error() { return g_err.c_str(); }
+
+}  // namespace pkv
+
+namespace {
+
+using pkv::fail;
+using pkv::hip_fail;
+using pkv::ok;
 
 bool valid_dtype(int32_t dt) { return dt == PKV_BF16 || dt == PKV_FP16 || dt == PKV_FP8_E4M3; }
 int32_t elem_size(int32_t dt) { return dt == PKV_FP8_E4M3 ? 1 : 2; }
@@ -118,7 +128,7 @@ struct pkv_pool {
 
 extern "C" {
 
-const char* pkv_last_error(void) { return g_err.c_str(); }
+const char* pkv_last_error(void) { return pkv::last_error(); }
 
 int32_t pkv_version(void) { return 100; }
 

@@ -47,6 +47,12 @@ struct DecodeArgs {
     float out_scale;       // v_scale for fp8 pools, else 1
 };
 
+// Error reporting shared by the extern "C" entry points (api.hip): set the
+// thread-local message and return the code.
+int32_t fail(int32_t code, const char* fmt, ...);
+int32_t ok();
+int32_t hip_fail(hipError_t e, const char* what);
+
 hipError_t launch_reshape_and_cache(const RacArgs& a, hipStream_t st);
 hipError_t launch_decode_slot_mapping(const int32_t* bt, int32_t max_blocks, const int32_t* ctx,
                                       int32_t num_seqs, int32_t bs, int32_t* slots,
