@@ -60,6 +60,9 @@ def lib():
         L.orc_reshape_and_cache.restype = None
         L.orc_reshape_and_cache.argtypes = [p, p, i32, p, p, p, i32, i32, i32, i32, i64,
                                             i32, f32, f32]
+        L.orc_paged_prefill.restype = None
+        L.orc_paged_prefill.argtypes = [p, p, i32, p, p, i32, p, i32, p, p, i32, i32, i32, i32,
+                                        i32, f32, f32, f32]
         L.orc_paged_decode.restype = None
         L.orc_paged_decode.argtypes = [p, p, i32, p, p, i32, p, i32, p, i32, i32, i32, i32,
                                        i32, f32, f32, f32]
@@ -188,6 +191,28 @@ def paged_decode(q_bits, q_dtype, k_pool, v_pool, kv_dtype, block_tables, contex
                            _ptr(bt), bt.shape[1], _ptr(cl), S, H, num_kv_heads, D,
                            block_size, float(np.float32(scale)), float(k_scale),
                            float(v_scale))
+    return out
+
+
+def paged_prefill(q_bits, q_dtype, k_pool, v_pool, kv_dtype, block_tables, context_lens,
+                  query_start, num_kv_heads, block_size, scale, k_scale=1.0, v_scale=1.0):
+    """fp64 multi-token causal attention over the paged cache; q_bits
+    [T][H][d] uint16 (rows of sequence s at query_start[s] ..
+    query_start[s+1]-1) -> [T][H][d] fp64."""
+    q = _c(q_bits, np.uint16)
+    kp = _c(k_pool, np.uint8)
+    vp = _c(v_pool, np.uint8)
+    bt = _c(block_tables, np.int32)
+    cl = _c(context_lens, np.int32)
+    qs = _c(query_start, np.int32)
+    T, H, D = q.shape
+    S = cl.shape[0]
+    assert qs.shape[0] == S + 1 and qs[0] == 0 and qs[-1] == T
+    out = np.zeros((T, H, D), np.float64)
+    lib().orc_paged_prefill(_ptr(out), _ptr(q), q_dtype, _ptr(kp), _ptr(vp), kv_dtype,
+                            _ptr(bt), bt.shape[1], _ptr(cl), _ptr(qs), S, H, num_kv_heads, D,
+                            block_size, float(np.float32(scale)), float(k_scale),
+                            float(v_scale))
     return out
 
 

@@ -27,3 +27,15 @@ def attention(q, k, v, scale):
     w = np.exp(logits)
     w /= w.sum(axis=1, keepdims=True)
     return np.einsum("hc,chd->hd", w, v_rep)
+
+
+def causal_chunk(q, k, v, scale):
+    """The last n = q.shape[0] tokens of a sequence attending causally:
+    q: [n][H][d]; k, v: [c][H_kv][d] with c >= n (the whole context, chunk
+    included).  Token j sits at position c - n + j and sees keys 0 .. that
+    position; each token is the textbook attention over its visible keys."""
+    q = np.asarray(q, np.float64)
+    c = k.shape[0]
+    n = q.shape[0]
+    return np.stack([attention(q[j], k[:c - n + j + 1], v[:c - n + j + 1], scale)
+                     for j in range(n)])

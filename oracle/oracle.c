@@ -281,6 +281,74 @@ void orc_paged_decode(double* out, const uint16_t* q, int q_dtype, const uint8_t
     }
 }
 
+/* Multi-token attention over the paged cache ([P1] §5/§6: the tokens of a
+ * prefill chunk, or those left after a prefix-cache hit, are the last
+ * q_len tokens of their sequence; each attends to every earlier token and
+ * itself).  For query row r of sequence s (rows query_start[s] ..
+ * query_start[s+1]-1), token j = r - query_start[s] sits at position
+ * p = c - q_len + j and its output is the softmax-weighted sum over keys
+ * t = 0 .. p, read through the block table as in orc_paged_decode.  A row
+ * with p < 0 is zero.  Written out directly: one row, one head at a time. */
+void orc_paged_prefill(double* out, const uint16_t* q, int q_dtype, const uint8_t* k_pool,
+                       const uint8_t* v_pool, int kv_dtype, const int32_t* block_tables,
+                       int max_blocks, const int32_t* ctx, const int32_t* query_start,
+                       int num_seqs, int heads, int kv_heads, int head_dim, int block_size,
+                       float scale, float k_scale, float v_scale) {
+    int group = heads / kv_heads;
+    double kdq = kv_dtype == ORC_FP8 ? (double)k_scale : 1.0;
+    double vdq = kv_dtype == ORC_FP8 ? (double)v_scale : 1.0;
+    int64_t rows = query_start[num_seqs];
+    int64_t pairs = rows * heads;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t rh = 0; rh < pairs; ++rh) {
+        int64_t r = rh / heads;
+        int h = (int)(rh % heads), g = h / group;
+        int s = 0;
+        while (query_start[s + 1] <= r) ++s;           /* the sequence owning row r */
+        int q_len = query_start[s + 1] - query_start[s];
+        int j = (int)(r - query_start[s]);
+        int c = ctx[s];
+        int pos = c - q_len + j;
+        double* o = out + rh * head_dim;
+        for (int k = 0; k < head_dim; ++k) o[k] = 0.0;
+        if (pos < 0) continue;
+        int n = pos + 1;                               /* keys 0 .. pos */
+        const int32_t* row = block_tables + (int64_t)s * max_blocks;
+        double* qd = malloc(sizeof(double) * head_dim);
+        double* logit = malloc(sizeof(double) * n);
+        for (int k = 0; k < head_dim; ++k) {
+            uint16_t bits = q[rh * head_dim + k];
+            qd[k] = q_dtype == ORC_BF16 ? orc_bf16_value(bits) : orc_fp16_value(bits);
+        }
+        double mx = -INFINITY;
+        for (int t = 0; t < n; ++t) {
+            int64_t pb = row[t / block_size];
+            double dot = 0.0;
+            for (int k = 0; k < head_dim; ++k) {
+                int64_t off = orc_pool_offset(pb, g, t % block_size, k, 0, kv_heads,
+                                              head_dim, block_size, kv_dtype);
+                dot += qd[k] * (elem_value(k_pool + off, kv_dtype) * kdq);
+            }
+            logit[t] = (double)scale * dot;
+            if (logit[t] > mx) mx = logit[t];
+        }
+        double denom = 0.0;
+        for (int t = 0; t < n; ++t) {
+            double w = exp(logit[t] - mx);
+            denom += w;
+            int64_t pb = row[t / block_size];
+            for (int k = 0; k < head_dim; ++k) {
+                int64_t off = orc_pool_offset(pb, g, t % block_size, k, 1, kv_heads,
+                                              head_dim, block_size, kv_dtype);
+                o[k] += w * (elem_value(v_pool + off, kv_dtype) * vdq);
+            }
+        }
+        for (int k = 0; k < head_dim; ++k) o[k] /= denom;
+        free(qd);
+        free(logit);
+    }
+}
+
 int orc_max_threads(void) {
 #ifdef _OPENMP
     return omp_get_max_threads();
