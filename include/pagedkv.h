@@ -323,6 +323,39 @@ int32_t paged_attention_decode_ex(void* out, const void* q, int32_t q_dtype,
                                   const pkv_decode_opts* opts,
                                   pkv_stream_t stream);
 
+/* ------------------------------------------------------- multi-token --
+ *
+ * paged_attention_prefill: several new tokens per sequence (a chunk of a
+ * chunked prefill, or the tokens left to compute after a prefix-cache hit,
+ * [P1] §5 / §6) attend causally over their paged context: the q_len(s) =
+ * query_start_loc[s+1] - query_start_loc[s] tokens of sequence s are its
+ * last ones, token j at position p = c - q_len(s) + j (c = context_lens[s],
+ * which counts them; their K/V are already in the cache), and
+ *     out[row, h, :] = sum_{t <= p} softmax_t(scale * q[row,h,:] . K_t) V_t,
+ *     row = query_start_loc[s] + j,
+ * with K_t, V_t read through the block table as for decode.  With q_len = 1
+ * for every sequence this is paged_attention_decode.
+ *   q, out          : [num_query_tokens][num_heads][head_dim] q_dtype rows,
+ *                     sequences packed in order.
+ *   query_start_loc : device int32[num_seqs + 1], non-decreasing, from 0;
+ *                     max_query_len >= every q_len(s) (host scalar: grid).
+ * Other arguments as paged_attention_decode; no workspace.  A token whose
+ * position would be < 0 (c < q_len) gets a zero output row.  Errors:
+ * PKV_ERR_ARG, PKV_ERR_UNSUPPORTED (head_dim != 128, dtype pair, G > 16),
+ * PKV_ERR_HIP. */
+int32_t paged_attention_prefill(void* out, const void* q, int32_t q_dtype,
+                                const void* k_cache, const void* v_cache,
+                                const int32_t* block_tables,
+                                int32_t max_blocks_per_seq,
+                                const int32_t* context_lens,
+                                const int32_t* query_start_loc,
+                                int32_t max_query_len, int32_t max_context_len,
+                                int32_t num_seqs, int32_t num_heads,
+                                int32_t num_kv_heads, int32_t head_dim,
+                                float scale, int32_t block_size,
+                                int32_t kv_dtype, float k_scale, float v_scale,
+                                pkv_stream_t stream);
+
 /* ------------------------------------------------------------ validation -- */
 
 /* Count block-table entries that a decode of these context lengths would

@@ -29,7 +29,7 @@ EXPORTS = [
     "pkv_bm_create", "pkv_bm_destroy", "pkv_bm_num_free_blocks", "pkv_bm_num_cached_free_blocks",
     "pkv_bm_ref_count", "pkv_bm_num_tokens", "pkv_bm_add_sequence", "pkv_bm_append_token",
     "pkv_bm_fork", "pkv_bm_free_sequence", "pkv_bm_block_table", "pkv_bm_slots",
-    "pkv_copy_blocks",
+    "pkv_copy_blocks", "paged_attention_prefill",
 ]
 
 
@@ -103,6 +103,8 @@ def lib():
             "pkv_bm_block_table": (i32, [p, i64, p, i32, ctypes.POINTER(i32)]),
             "pkv_bm_slots": (i32, [p, i64, i32, i32, p]),
             "pkv_copy_blocks": (i32, [p, p, i32, i32, i32, i32, i32, i32, p, i32, p]),
+            "paged_attention_prefill": (i32, [p, p, i32, p, p, p, i32, p, p, i32, i32, i32, i32,
+                                              i32, i32, f32, i32, i32, f32, f32, p]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -391,3 +393,21 @@ def copy_blocks(k_layers, v_layers, pairs, num_blocks, num_kv_heads, head_dim, b
     _check(lib().pkv_copy_blocks(kp, vp, n, num_blocks, num_kv_heads, head_dim, block_size,
                                  kv_dtype, _ptr(pairs, "pairs", torch.int32), pairs.shape[0],
                                  _stream(stream)))
+
+
+def paged_attention_prefill(out, q, k_cache, v_cache, block_tables, context_lens, query_start_loc,
+                            max_query_len, max_context_len, num_kv_heads, block_size, kv_dtype,
+                            scale, k_scale=1.0, v_scale=1.0, stream=None):
+    """Multi-token causal attention over the paged cache.  q, out:
+    [num_query_tokens][H][d]; query_start_loc: device int32 [S + 1]."""
+    T, H, D = q.shape
+    S = context_lens.shape[0]
+    if query_start_loc.shape[0] != S + 1:
+        raise ValueError("query_start_loc must have num_seqs + 1 entries")
+    _check(lib().paged_attention_prefill(
+        _ptr(out, "out", q.dtype), _ptr(q, "q"), dtype_code(q.dtype), _ptr(k_cache, "k_cache"),
+        _ptr(v_cache, "v_cache"), _ptr(block_tables, "block_tables", torch.int32),
+        block_tables.shape[1], _ptr(context_lens, "context_lens", torch.int32),
+        _ptr(query_start_loc, "query_start_loc", torch.int32), int(max_query_len),
+        int(max_context_len), S, H, num_kv_heads, D, float(scale), block_size, kv_dtype,
+        float(k_scale), float(v_scale), _stream(stream)))

@@ -401,6 +401,61 @@ int32_t paged_attention_decode_ex(void* out, const void* q, int32_t q_dtype, con
     return ok();
 }
 
+int32_t paged_attention_prefill(void* out, const void* q, int32_t q_dtype, const void* k_cache,
+                                const void* v_cache, const int32_t* block_tables,
+                                int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                const int32_t* query_start_loc, int32_t max_query_len,
+                                int32_t max_context_len, int32_t num_seqs, int32_t num_heads,
+                                int32_t num_kv_heads, int32_t head_dim, float scale,
+                                int32_t block_size, int32_t kv_dtype, float k_scale, float v_scale,
+                                pkv_stream_t stream) {
+    if (int32_t e = check_layout_args(head_dim, block_size, kv_dtype)) return e;
+    if (q_dtype != PKV_BF16 && q_dtype != PKV_FP16) return fail(PKV_ERR_ARG, "q_dtype must be bf16 or fp16");
+    if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || max_context_len < 0 ||
+        max_blocks_per_seq < 0 || max_query_len < 0)
+        return fail(PKV_ERR_ARG, "bad sizes");
+    if (num_heads % num_kv_heads) return fail(PKV_ERR_ARG, "num_heads %d is not a multiple of num_kv_heads %d", num_heads, num_kv_heads);
+    const int32_t G = num_heads / num_kv_heads;
+    if (G > 16) return fail(PKV_ERR_UNSUPPORTED, "query heads per kv head %d > 16", G);
+    if (head_dim != kBuiltHeadDim) return fail(PKV_ERR_UNSUPPORTED, "kernels are built for head_dim 128, got %d", head_dim);
+    if (kv_dtype != PKV_FP8_E4M3 && kv_dtype != q_dtype)
+        return fail(PKV_ERR_UNSUPPORTED, "a 16-bit KV pool must have the query dtype");
+    if (!std::isfinite(scale)) return fail(PKV_ERR_ARG, "scale must be finite");
+    if (kv_dtype == PKV_FP8_E4M3 && !(std::isfinite(k_scale) && std::isfinite(v_scale)))
+        return fail(PKV_ERR_ARG, "fp8 scales must be finite");
+    if (num_seqs > 0 && (!out || !q || !k_cache || !v_cache || !context_lens || !query_start_loc ||
+                         (max_blocks_per_seq > 0 && !block_tables)))
+        return fail(PKV_ERR_ARG, "null pointer");
+    const int32_t tile_tokens = 16 / G;
+    const int64_t max_tiles = ((int64_t)max_query_len + tile_tokens - 1) / tile_tokens;
+    if ((int64_t)num_seqs * max_tiles * num_kv_heads > 0x7fffffff)
+        return fail(PKV_ERR_UNSUPPORTED, "too many workgroups");
+    pkv::DecodeArgs a{};
+    a.out = out;
+    a.q = q;
+    a.k_cache = (const uint8_t*)k_cache;
+    a.v_cache = (const uint8_t*)v_cache;
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.max_blocks = max_blocks_per_seq;
+    a.ctx_cap = ctx_cap_of(max_context_len, max_blocks_per_seq, block_size);
+    a.num_seqs = num_seqs;
+    a.num_heads = num_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.group = G;
+    a.part_blocks = std::max(1, max_blocks_per_seq);   // one partition: the whole context
+    a.num_parts = 1;
+    a.num_blocks = 0;
+    const float ks = kv_dtype == PKV_FP8_E4M3 ? k_scale : 1.0f;
+    a.qk_scale_log2 = (float)((double)scale * (double)ks * 1.4426950408889634);
+    a.out_scale = kv_dtype == PKV_FP8_E4M3 ? v_scale : 1.0f;
+    (void)hipGetLastError();
+    hipError_t e = pkv::launch_prefill(a, q_dtype, kv_dtype, block_size, query_start_loc, tile_tokens,
+                                       (int)max_tiles, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "paged prefill launch");
+    return ok();
+}
+
 int32_t paged_attention_decode(void* out, const void* q, int32_t q_dtype, const void* k_cache,
                                const void* v_cache, const int32_t* block_tables,
                                int32_t max_blocks_per_seq, const int32_t* context_lens,

@@ -32,33 +32,41 @@
 namespace pkv {
 
 // MFMA policy: S^T = K . Q^T on four 16x16x32 MFMAs (rows = 16 tokens,
-// columns = the G heads padded to 16), then O^T += V^T . P^T on eight
-// 16x16x16 MFMAs whose B operand is S^T's lane order.  Lane l holds head
-// l & 15 for the softmax state and rows 4*(l>>4)..+3 of each 16-row tile.
+// columns = the tile's (query token, head) pairs padded to 16; for decode
+// the G heads), then O^T += V^T . P^T on eight 16x16x16 MFMAs whose B
+// operand is S^T's lane order.  Lane l holds column l & 15 for the softmax
+// state and rows 4*(l>>4)..+3 of each 16-row tile.
 template <int KVT, int QT>
 struct MfmaMath {
     static constexpr int kMaxGroup = 16;
     __host__ __device__ static constexpr int query_lds_floats(int) { return 0; }
 
-    u32x4_t qf[4];            // Q^T fragments: 8 dims per kk of head lane & 15
+    u32x4_t qf[4];            // Q^T fragments: 8 dims per kk of column lane & 15
     f32x4_t acc[8];
     float m, l;
-    int hl;
-    bool hvalid;
+    int col;                  // lane & 15: column (token col / G, head col % G)
+    bool cvalid;              // the column holds a real (token, head)
+    int lim;                  // the column sees keys at positions < lim
 
-    __device__ __forceinline__ void load_q(const DecodeArgs& a, int s, int kvh, int lane) {
+    __device__ __forceinline__ void load_q(const DecodeArgs& a, const QueryTile& qt, int kvh,
+                                           int lane) {
         const int G = a.group;
-        hl = lane & 15;
-        hvalid = hl < G;
+        col = lane & 15;
+        cvalid = col < qt.ntok * G;
+        const int j = cvalid ? col / G : 0;
+        const int h = cvalid ? col - j * G : 0;
         const uint8_t* qrow = reinterpret_cast<const uint8_t*>(a.q) +
-                              ((int64_t)s * a.num_heads + (int64_t)kvh * G + (hvalid ? hl : 0)) *
-                                  (kHeadDim * 2);
+                              ((qt.row0 + j) * a.num_heads + (int64_t)kvh * G + h) * (kHeadDim * 2);
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
             const u32x4_t z = {0u, 0u, 0u, 0u};
-            qf[kk] = hvalid ? *reinterpret_cast<const u32x4_t*>(qrow + 16 * ((lane >> 4) + 4 * kk))
+            qf[kk] = cvalid ? *reinterpret_cast<const u32x4_t*>(qrow + 16 * ((lane >> 4) + 4 * kk))
                             : z;
         }
+    }
+    // pos0 = position of the tile's first token: token j sees keys <= pos0 + j
+    __device__ __forceinline__ void limit(int pos0, int G, int) {
+        lim = cvalid ? pos0 + col / G + 1 : 0;
     }
     __device__ __forceinline__ void stage_q(float*, int) {}
 
@@ -78,18 +86,19 @@ struct MfmaMath {
 
         const int tb = tok0 + 4 * (lane >> 4);
         float t[4];
-        bool valid[4];
+        bool valid[4];            // key visible to this lane's column
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            valid[i] = (tb + i) < ctx;
+            valid[i] = (tb + i) < lim;
             t[i] = valid[i] ? st[i] * cs : -INFINITY;
         }
         float bm = fmaxf(fmaxf(t[0], t[1]), fmaxf(t[2], t[3]));
         bm = fmaxf(bm, xor_shfl(bm, 16));
-        bm = fmaxf(bm, xor_shfl(bm, 32));     // max of the unit for head lane&15
+        bm = fmaxf(bm, xor_shfl(bm, 32));     // max of the unit for column lane&15
         if (__builtin_amdgcn_ballot_w64(bm > m + kRescaleSlack)) {
-            // Some head's max jumped: move every head's reference to its max.
-            const float mn = fmaxf(m, bm);     // finite: every unit holds a valid token
+            // Some column's max jumped: move every column's reference to its
+            // max (a column that sees no key of this unit keeps its own).
+            const float mn = fmaxf(m, bm);
             const float alpha = (m == -INFINITY) ? 0.f : fast_exp2(m - mn);
             l *= alpha;
 #pragma unroll
@@ -116,26 +125,29 @@ struct MfmaMath {
             // Last unit of the context: rows past the context hold whatever
             // the slot last held (NaN or stale data); a zero weight times NaN
             // would still poison the sum, so zero those V elements too.
+            bool row[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) row[i] = (tb + i) < ctx;
             u32x2_t vm;
-            vm[0] = (valid[0] ? 0x0000ffffu : 0u) | (valid[1] ? 0xffff0000u : 0u);
-            vm[1] = (valid[2] ? 0x0000ffffu : 0u) | (valid[3] ? 0xffff0000u : 0u);
+            vm[0] = (row[0] ? 0x0000ffffu : 0u) | (row[1] ? 0xffff0000u : 0u);
+            vm[1] = (row[2] ? 0x0000ffffu : 0u) | (row[3] ? 0xffff0000u : 0u);
 #pragma unroll
             for (int nt = 0; nt < 8; ++nt)
                 acc[nt] = mfma_16x16x16<QT>(v_frag<KVT, QT>(u, nt) & vm, pf, acc[nt]);
         }
     }
 
-    __device__ __forceinline__ void park(float* sm_m, float* sm_l, float* sm_acc, int w, int G,
+    __device__ __forceinline__ void park(float* sm_m, float* sm_l, float* sm_acc, int w, int ncols,
                                          int lane) {
-        // normaliser of head lane & 15: sum the four lanes sharing the head
+        // normaliser of column lane & 15: sum the four lanes sharing it
         l += xor_shfl(l, 16);
         l += xor_shfl(l, 32);
         if (lane < 16) {
             sm_m[w * 16 + lane] = m;
             sm_l[w * 16 + lane] = l;
         }
-        if (hvalid) {
-            float* row = sm_acc + (w * G + hl) * kMergeRow + 4 * (lane >> 4);
+        if (cvalid) {
+            float* row = sm_acc + (w * ncols + col) * kMergeRow + 4 * (lane >> 4);
 #pragma unroll
             for (int nt = 0; nt < 8; ++nt) *reinterpret_cast<f32x4_t*>(row + 16 * nt) = acc[nt];
         }
@@ -174,8 +186,9 @@ void paged_decode_mfma_persistent(const DecodeArgs a) {
         const int item = k / a.num_kv_heads;
         const int kvh = k - item * a.num_kv_heads;
         const uint32_t packed = (uint32_t)a.plan[kPlanHeader + item];
-        decode_entry<MfmaMath<KVT, QT>, KVT, QT, BS, NW, DEPTH>(a, pkv_smem, (int)(packed >> 16),
-                                                                 (int)(packed & 0xffffu), kvh, lane, w);
+        const int s = (int)(packed >> 16);
+        decode_entry<MfmaMath<KVT, QT>, KVT, QT, BS, NW, DEPTH>(a, pkv_smem, s, (int)(packed & 0xffffu),
+                                                                 kvh, lane, w, QueryTile{s, 1, 1});
     }
     if (threadIdx.x == 0) {
         __threadfence();
@@ -184,6 +197,64 @@ void paged_decode_mfma_persistent(const DecodeArgs a) {
             atomicExch(&counters[1], 0);
         }
     }
+}
+
+// Multi-token form: workgroup (sequence s, query tile, kv head) attends the
+// tile's tokens to the paged context, causally: token j of a chunk of
+// q_len new tokens sits at position ctx - q_len + j and sees keys up to it.
+// Tiles hold tile_tokens = 16 / G tokens (so the tile's (token, head) pairs
+// fill the 16 MFMA columns), and the last tiles of a chunk, which see the
+// most keys, are dispatched first.  No context split: the tiles give the
+// parallelism.  With q_len = 1 a tile is exactly a decode entry.
+template <int KVT, int QT, int BS, int NW, int DEPTH>
+__global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(PKV_WAVES_PER_EU)))
+void paged_prefill_mfma_kernel(const DecodeArgs a, const int32_t* __restrict__ query_start,
+                               int tile_tokens, int max_tiles) {
+    extern __shared__ float pkv_smem[];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int kvh = blockIdx.x % a.num_kv_heads;
+    const int rest = blockIdx.x / a.num_kv_heads;
+    const int tile = max_tiles - 1 - rest / a.num_seqs;
+    const int s = rest % a.num_seqs;
+    const int q0 = query_start[s];
+    const int q_len = query_start[s + 1] - q0;
+    const int j0 = tile * tile_tokens;
+    if (j0 >= q_len) return;
+    decode_entry<MfmaMath<KVT, QT>, KVT, QT, BS, NW, DEPTH>(
+        a, pkv_smem, s, 0, kvh, lane, w,
+        QueryTile{(int64_t)q0 + j0, min(tile_tokens, q_len - j0), q_len - j0});
+}
+
+template <int KVT, int QT, int BS>
+static hipError_t launch_prefill_t(const DecodeArgs& a, const int32_t* query_start, int tile_tokens,
+                                   int max_tiles, hipStream_t st) {
+    const size_t lds = sizeof(float) * merge_lds_floats(kWavesPerGroup, tile_tokens * a.group);
+    const dim3 grid((unsigned)((int64_t)a.num_seqs * max_tiles * a.num_kv_heads));
+    hipLaunchKernelGGL((paged_prefill_mfma_kernel<KVT, QT, BS, kWavesPerGroup, kDepth>), grid,
+                       dim3(kWavesPerGroup * kWave), lds, st, a, query_start, tile_tokens, max_tiles);
+    return hipGetLastError();
+}
+
+template <int KVT, int QT>
+static hipError_t launch_prefill_bs(const DecodeArgs& a, int bs, const int32_t* query_start,
+                                    int tile_tokens, int max_tiles, hipStream_t st) {
+    return bs == 16 ? launch_prefill_t<KVT, QT, 16>(a, query_start, tile_tokens, max_tiles, st)
+                    : launch_prefill_t<KVT, QT, 32>(a, query_start, tile_tokens, max_tiles, st);
+}
+
+hipError_t launch_prefill(const DecodeArgs& a, int q_dtype, int kv_dtype, int block_size,
+                          const int32_t* query_start, int tile_tokens, int max_tiles,
+                          hipStream_t st) {
+    if (a.num_seqs == 0 || max_tiles == 0) return hipSuccess;
+    if (q_dtype == DT_BF16) {
+        if (kv_dtype == DT_BF16)
+            return launch_prefill_bs<DT_BF16, DT_BF16>(a, block_size, query_start, tile_tokens, max_tiles, st);
+        return launch_prefill_bs<DT_FP8, DT_BF16>(a, block_size, query_start, tile_tokens, max_tiles, st);
+    }
+    if (kv_dtype == DT_FP16)
+        return launch_prefill_bs<DT_FP16, DT_FP16>(a, block_size, query_start, tile_tokens, max_tiles, st);
+    return launch_prefill_bs<DT_FP8, DT_FP16>(a, block_size, query_start, tile_tokens, max_tiles, st);
 }
 
 // Merge the partitions of every multi-partition sequence: with per-partition

@@ -64,15 +64,29 @@ constexpr int kMergeRow = kHeadDim + 4;
 // Plan header ints before the item list: [count][next entry][done][reserved].
 constexpr int kPlanHeader = 4;
 
-__host__ __device__ constexpr int merge_lds_floats(int nw, int g) { return 4 + 32 * nw + nw * g * kMergeRow; }
+__host__ __device__ constexpr int merge_lds_floats(int nw, int ncols) { return 4 + 32 * nw + nw * ncols * kMergeRow; }
+
+// The query side of a work entry: ntok consecutive query tokens of one
+// sequence (1 for decode), stored at rows row0 .. row0 + ntok - 1 of q /
+// out, the first of them at logical position ctx - back (ctx = the
+// sequence's context length, which counts these tokens).  The 16 matrix
+// columns of the entry are the pairs (token j, head h), column c = j*G + h,
+// ncols = ntok * G <= 16; token j attends to keys t <= ctx - back + j.
+struct QueryTile {
+    int64_t row0;
+    int ntok;
+    int back;
+};
 
 // ---------------------------------------------------------------------------
-// Per-unit math.  A policy holds one wave's running state for the G query
-// heads of its kv head (running max m in log2 units, normaliser l, partial
-// output) and provides:
+// Per-unit math.  A policy holds one wave's running state for the columns
+// of its entry (running max m in log2 units, normaliser l, partial output)
+// and provides:
 //   load_q   issue the query loads (before the context length is known),
-//   stage_q  make them usable (after the workgroup's exits, before the
-//            workgroup barrier),
+//   limit    set each column's key limit (first key position it must not
+//            see) once the context length is known,
+//   stage_q  make the queries usable (after the workgroup's exits, before
+//            the workgroup barrier),
 //   begin    reset the running state,
 //   unit     one 16-token unit: logits, online-softmax update, PV,
 //   park     reduce over lanes and store (m, l, O) in the merge area.
@@ -92,13 +106,13 @@ __host__ __device__ constexpr int merge_lds_floats(int nw, int g) { return 4 + 3
 constexpr int kWavesPerGroup = PKV_WAVES_PER_GROUP;
 constexpr int kDepth = PKV_PIPELINE_DEPTH;
 
-// Decode one work entry: kv head `kvh` of plan item (sequence s,
-// partition part), by the NW waves of the calling workgroup.  Every exit
-// before the LDS counter barrier depends only on (s, part), so all waves of
-// the workgroup take it together.
+// Decode one work entry: kv head `kvh` of (sequence s, partition part) for
+// the query tile qt, by the NW waves of the calling workgroup.  Every exit
+// before the LDS counter barrier depends only on (s, part, qt), so all
+// waves of the workgroup take it together.
 template <class Math, int KVT, int QT, int BS, int NW, int DEPTH>
 __device__ __forceinline__ void decode_entry(const DecodeArgs& a, float* pkv_smem, int s, int part,
-                                             int kvh, int lane, int w) {
+                                             int kvh, int lane, int w, const QueryTile& qt) {
     constexpr int NSUB = BS / kSubTokens;
     constexpr int64_t SUB = sub_tile_bytes(KVT);
     constexpr int64_t TILE = SUB * NSUB;
@@ -115,27 +129,36 @@ __device__ __forceinline__ void decode_entry(const DecodeArgs& a, float* pkv_sme
     int ids0 = 0;
     if (a.max_blocks > 0) ids0 = bt_row[min(first + NW * lane, a.max_blocks * NSUB - 1) / NSUB];
 
+    const int ncols = qt.ntok * G;
     Math mt;
-    mt.load_q(a, s, kvh, lane);
+    mt.load_q(a, qt, kvh, lane);
 
     int ctx = a.context_lens[s];
     ctx = ctx < a.ctx_cap ? ctx : a.ctx_cap;
-    if (ctx <= 0) {
+    // keys this tile may see: positions < kv_end (its last token's + 1)
+    const int kv_end = min(ctx, ctx - qt.back + qt.ntok);
+    if (kv_end <= 0) {
         if (part == 0) {
-            uint16_t* out = reinterpret_cast<uint16_t*>(a.out) +
-                            ((int64_t)s * a.num_heads + (int64_t)kvh * G) * kHeadDim;
-            for (int e = threadIdx.x; e < G * kHeadDim; e += NW * kWave) out[e] = 0;
+            // no key at all: zero output (empty context, or tokens placed
+            // before the start of the context)
+            for (int e = threadIdx.x; e < ncols * kHeadDim; e += NW * kWave) {
+                const int c = e / kHeadDim;
+                uint16_t* out = reinterpret_cast<uint16_t*>(a.out) +
+                                ((qt.row0 + c / G) * a.num_heads + (int64_t)kvh * G + c % G) * kHeadDim;
+                out[e % kHeadDim] = 0;
+            }
         }
         return;
     }
-    const int n_units = (ctx + kSubTokens - 1) / kSubTokens;
+    mt.limit(ctx - qt.back, G, lane);
+    const int n_units = (kv_end + kSubTokens - 1) / kSubTokens;
     if (u0 >= n_units) return;
     const int u1 = min(u0 + units_per_part, n_units);
-    const int nblk = (ctx + BS - 1) / BS;
+    const int nblk = (kv_end + BS - 1) / BS;
     const bool single = nblk <= a.part_blocks;
     int* done = reinterpret_cast<int*>(pkv_smem);
     if (threadIdx.x == 0) *done = 0;
-    mt.stage_q(pkv_smem + merge_lds_floats(NW, G), threadIdx.x);
+    mt.stage_q(pkv_smem + merge_lds_floats(NW, ncols), threadIdx.x);
     __syncthreads();
     mt.begin();
 
@@ -209,7 +232,7 @@ __device__ __forceinline__ void decode_entry(const DecodeArgs& a, float* pkv_sme
     float* sm_m = pkv_smem + 4;
     float* sm_l = sm_m + NW * 16;
     float* sm_acc = sm_l + NW * 16;
-    mt.park(sm_m, sm_l, sm_acc, w, G, lane);
+    mt.park(sm_m, sm_l, sm_acc, w, ncols, lane);
     __threadfence_block();
     int prev = 0;
     if (lane == 0) prev = atomicAdd(done, 1);
@@ -217,28 +240,32 @@ __device__ __forceinline__ void decode_entry(const DecodeArgs& a, float* pkv_sme
     if (prev != NW - 1) return;
     __threadfence_block();
 
-    for (int h = 0; h < G; ++h) {
+    for (int c = 0; c < ncols; ++c) {
         float M = -INFINITY;
 #pragma unroll
-        for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, sm_m[ww * 16 + h]);
+        for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, sm_m[ww * 16 + c]);
         float L = 0.f, o0 = 0.f, o1 = 0.f;
 #pragma unroll
         for (int ww = 0; ww < NW; ++ww) {
-            const float mw = sm_m[ww * 16 + h];
+            const float mw = sm_m[ww * 16 + c];
             const float f = (mw == -INFINITY) ? 0.f : fast_exp2(mw - M);
-            const float2 ov = *reinterpret_cast<const float2*>(sm_acc + (ww * G + h) * kMergeRow + 2 * lane);
-            L += f * sm_l[ww * 16 + h];
+            const float2 ov = *reinterpret_cast<const float2*>(sm_acc + (ww * ncols + c) * kMergeRow + 2 * lane);
+            L += f * sm_l[ww * 16 + c];
             o0 += f * ov.x;
             o1 += f * ov.y;
         }
-        const float invL = 1.0f / L;
+        // L = 0 only for a token placed before the start of the context
+        const float invL = L > 0.f ? 1.0f / L : 0.f;
+        const int h = c % G;
         const int hq = kvh * G + h;
         if (single) {
             const float sc = invL * a.out_scale;
-            uint16_t* out = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)s * a.num_heads + hq) * kHeadDim;
+            uint16_t* out = reinterpret_cast<uint16_t*>(a.out) +
+                            ((qt.row0 + c / G) * a.num_heads + hq) * kHeadDim;
             *reinterpret_cast<uint32_t*>(out + 2 * lane) =
                 (uint32_t)f32_to_bits<QT>(o0 * sc) | ((uint32_t)f32_to_bits<QT>(o1 * sc) << 16);
         } else {
+            // (split contexts are decode only: one token, column c = head h)
             // record (s, kvh, part): G rows of head_dim floats, contiguous
             const int64_t rec = ((int64_t)s * a.num_kv_heads + kvh) * a.num_parts + part;
             *reinterpret_cast<float2*>(a.ws_out + (rec * G + h) * kHeadDim + 2 * lane) =
@@ -295,8 +322,9 @@ __device__ __forceinline__ void grid_entry(const DecodeArgs& a, float* pkv_smem)
     // item < n_items
     const uint32_t packed = (uint32_t)a.plan[kPlanHeader + min(item, a.num_seqs * a.num_parts - 1)];
     if (item >= n_items) return;
-    decode_entry<Math, KVT, QT, BS, NW, DEPTH>(a, pkv_smem, (int)(packed >> 16),
-                                                (int)(packed & 0xffffu), kvh, lane, w);
+    const int s = (int)(packed >> 16);
+    decode_entry<Math, KVT, QT, BS, NW, DEPTH>(a, pkv_smem, s, (int)(packed & 0xffffu), kvh, lane, w,
+                                                QueryTile{s, 1, 1});
 }
 
 }  // namespace pkv

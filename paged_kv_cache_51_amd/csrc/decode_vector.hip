@@ -27,14 +27,18 @@ struct VectorMath {
     const u32x4_t* qlds;      // [head][16] chunks of 8 dims
     int G;
 
-    __device__ __forceinline__ void load_q(const DecodeArgs& a, int s, int kvh, int) {
+    // decode only: one query token per entry (columns = the G heads)
+    __device__ __forceinline__ void load_q(const DecodeArgs& a, const QueryTile& qt, int kvh, int) {
         G = a.group;
         const int tid = threadIdx.x;
         const u32x4_t* src = reinterpret_cast<const u32x4_t*>(a.q) +
-                             ((int64_t)s * a.num_heads + (int64_t)kvh * G) * (kHeadDim / 8);
+                             (qt.row0 * a.num_heads + (int64_t)kvh * G) * (kHeadDim / 8);
         const u32x4_t z = {0u, 0u, 0u, 0u};
         qreg = tid < G * (kHeadDim / 8) ? src[tid] : z;
     }
+    // one token at the end of the context: it sees every key (unit() masks
+    // at the context length)
+    __device__ __forceinline__ void limit(int, int, int) {}
     __device__ __forceinline__ void stage_q(float* lds, int tid) {
         u32x4_t* q = reinterpret_cast<u32x4_t*>(lds);
         if (tid < G * (kHeadDim / 8)) q[tid] = qreg;

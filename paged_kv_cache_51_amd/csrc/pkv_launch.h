@@ -70,5 +70,9 @@ hipError_t launch_decode_partitions(const DecodeArgs& a, int q_dtype, int kv_dty
                                     int block_size, int impl, hipStream_t st);
 hipError_t launch_decode_reduce(const DecodeArgs& a, int q_dtype, int block_size,
                                 hipStream_t st);
+// Multi-token attention (query tiles of tile_tokens tokens, causal).
+hipError_t launch_prefill(const DecodeArgs& a, int q_dtype, int kv_dtype, int block_size,
+                          const int32_t* query_start, int tile_tokens, int max_tiles,
+                          hipStream_t st);
 
 }  // namespace pkv
