@@ -46,9 +46,13 @@ def parse():
                     help="target CPU time of the oracle sample (0 disables)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one device copy of this size (counter calibration)")
-    ap.add_argument("--op", default="decode", choices=["decode", "copy_blocks"],
+    ap.add_argument("--op", default="decode", choices=["decode", "copy_blocks", "prefill"],
                     help="decode: the attention step (default); copy_blocks: copy-on-write "
-                         "block copies over the same pool shape")
+                         "block copies over the same pool shape; prefill: multi-token causal "
+                         "attention (the last --q-len tokens of each sequence are new)")
+    ap.add_argument("--q-len", type=int, default=512, help="prefill: new tokens per sequence")
+    ap.add_argument("--num-seqs", type=int, default=0,
+                    help="prefill: sequences (default 16, or the workload's batch if --q-len <= 16)")
     ap.add_argument("--copy-pairs", type=int, default=2048,
                     help="copy_blocks: (src, dst) block pairs per call")
     return ap.parse_args()
@@ -90,6 +94,9 @@ def main():
 
     if args.op == "copy_blocks":
         bench_copy_blocks(args, torch, pkv, workloads)
+        return
+    if args.op == "prefill":
+        bench_prefill(args, torch, pkv, workloads)
         return
 
     dt_names = {"bf16": pkv.BF16, "fp16": pkv.FP16, "fp8": pkv.FP8_E4M3}
@@ -262,6 +269,114 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
+
+
+def bench_prefill(args, torch, pkv, workloads):
+    """Multi-token causal paged attention over the workload's contexts: the
+    last --q-len tokens of each of --num-seqs sequences are new (a chunked
+    prefill step, or a few tokens per sequence after prefix-cache hits).  A
+    step is one paged_attention_prefill call per layer.  Reported: TFLOP/s
+    (4 * d flops per (query row, head, visible key)) and the unique KV +
+    query / output bytes per second; the roofline takes whichever bound
+    the step's intensity puts it under."""
+    dt_names = {"bf16": pkv.BF16, "fp16": pkv.FP16, "fp8": pkv.FP8_E4M3}
+    cfg, tabs_all, _, _ = workloads.make(args.config, seed=args.seed, block_size=args.block_size)
+    kv = dt_names[args.kv_dtype] if args.kv_dtype else cfg.kv_dtype
+    q_dtype = cfg.q_dtype if kv == pkv.FP8_E4M3 else kv
+    bs = args.block_size or cfg.block_size
+    L = args.layers or min(cfg.num_layers, 4)
+    H, Hkv, D = cfg.num_heads, cfg.num_kv_heads, cfg.head_dim
+    qlen = args.q_len
+    S = args.num_seqs or (cfg.num_seqs if qlen <= 16 else min(16, cfg.num_seqs))
+    ctx = tabs_all.context_lens[:S].astype(np.int64)
+    if (ctx < qlen).any():
+        raise SystemExit(f"--q-len {qlen} exceeds a context length ({int(ctx.min())})")
+    bt_np = tabs_all.block_tables[:S]
+    nb = tabs_all.num_blocks
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    pool_bytes = pkv.layer_pool_bytes(nb, Hkv, D, bs, kv)
+    fp8_scale = float(np.float32(8.0 / 448.0))
+    ks = vs = fp8_scale if kv == pkv.FP8_E4M3 else 1.0
+    kpools = [torch.empty(pool_bytes, dtype=torch.uint8, device=dev) for _ in range(L)]
+    vpools = [torch.empty(pool_bytes, dtype=torch.uint8, device=dev) for _ in range(L)]
+    for i in range(L):
+        workloads.device_fill_normal(kpools[i], kv, 1000 + i, scale=fp8_scale)
+        workloads.device_fill_normal(vpools[i], kv, 2000 + i, scale=fp8_scale)
+    tq = torch.bfloat16 if q_dtype == pkv.BF16 else torch.float16
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(args.seed + 17)
+    T = S * qlen
+    qs = [torch.randn(T, H, D, generator=gen, device=dev).to(tq) for _ in range(L)]
+    outs = [torch.empty(T, H, D, dtype=tq, device=dev) for _ in range(L)]
+    bt = torch.from_numpy(np.ascontiguousarray(bt_np)).to(dev)
+    cl = torch.from_numpy(ctx.astype(np.int32)).to(dev)
+    qsl = torch.arange(0, T + 1, qlen, dtype=torch.int32, device=dev)
+    mc = int(ctx.max())
+    scale = float(np.float32(1.0 / np.sqrt(D)))
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        for layer in range(L):
+            if ev is not None:
+                ev[layer][0].record(stream)
+            pkv.paged_attention_prefill(outs[layer], qs[layer], kpools[layer], vpools[layer], bt,
+                                        cl, qsl, qlen, mc, Hkv, bs, kv, scale, ks, vs,
+                                        stream=stream)
+            if ev is not None:
+                ev[layer][1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(L)]
+           for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for k in range(args.steps):
+        step(evs[k])
+    end.record(stream)
+    torch.cuda.synchronize()
+    step_ms = start.elapsed_time(end) / args.steps
+    launch_ms = float(np.mean([evs[k][l][0].elapsed_time(evs[k][l][1])
+                               for k in range(args.steps) for l in range(L)]))
+    b_kv = 1 if kv == pkv.FP8_E4M3 else 2
+    # visible keys of token j (position c - qlen + j): c - qlen + j + 1
+    keys = int(sum(qlen * (c - qlen) + qlen * (qlen + 1) // 2 for c in ctx))
+    flops = 4 * D * H * keys
+    nbytes = int(ctx.sum()) * 2 * Hkv * D * b_kv + T * H * D * 4
+    tflops = flops / (launch_ms * 1e-3) / 1e12
+    gbs = nbytes / (launch_ms * 1e-3) / 1e9
+    peak_tf = {pkv.BF16: 2500.0, pkv.FP16: 2500.0}.get(q_dtype, 2500.0)
+    ridge = peak_tf * 1e12 / (PEAK_HBM_GBS * 1e9)
+    mfma_bound = flops / nbytes > ridge
+    print(f"[bench] prefill: {S} seqs x {qlen} new tokens, contexts {int(ctx.min())}-{int(ctx.max())}; "
+          f"{launch_ms * 1e3:.1f} us per layer, {tflops:.1f} TFLOP/s, {gbs:.0f} GB/s; "
+          f"intensity {flops / nbytes:.0f} flop/B", file=sys.stderr, flush=True)
+    dt_name = {pkv.BF16: "bf16", pkv.FP16: "fp16", pkv.FP8_E4M3: "fp8"}
+    print(json.dumps({
+        "metric": "paged multi-token attention TFLOP/s" if mfma_bound
+                  else "paged multi-token attention HBM GB/s",
+        "value": round(tflops if mfma_bound else gbs, 2 if mfma_bound else 1),
+        "unit": "TFLOP/s" if mfma_bound else "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(step_ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": dt_name[kv] if kv == pkv.FP8_E4M3 else dt_name[q_dtype], "data": "synthetic",
+        "config": {"workload": f"{cfg.description.split(':')[0]}: {S} sequences, the last {qlen} "
+                               f"of {int(ctx.min())}-{int(ctx.max())} context tokens new, {L} layers",
+                   "num_seqs": S, "q_len": qlen, "layers": L, "num_heads": H,
+                   "num_kv_heads": Hkv, "kv_dtype": dt_name[kv], "block_size": bs,
+                   "parallelism": "single GPU"},
+        "tflops": round(tflops, 2), "gbs": round(gbs, 1),
+        "roofline": {"bound": "mfma" if mfma_bound else "hbm", "kernel": "paged_prefill_mfma_kernel",
+                     "achieved": round(tflops if mfma_bound else gbs, 2),
+                     "peak": peak_tf if mfma_bound else PEAK_HBM_GBS,
+                     "unit": "TFLOP/s" if mfma_bound else "GB/s",
+                     "frac": round((tflops / peak_tf) if mfma_bound else (gbs / PEAK_HBM_GBS), 4),
+                     "traffic": None, "avg_launch_us": round(launch_ms * 1e3, 2),
+                     "algorithmic_flops_per_launch": flops, "algorithmic_bytes_per_launch": nbytes},
+        "cpu_baseline": None,
+    }), flush=True)
 
 
 def bench_copy_blocks(args, torch, pkv, workloads):
