@@ -60,6 +60,11 @@ def lib():
         L.orc_reshape_and_cache.restype = None
         L.orc_reshape_and_cache.argtypes = [p, p, i32, p, p, p, i32, i32, i32, i32, i64,
                                             i32, f32, f32]
+        L.orc_paged_decode_tokens.restype = None
+        L.orc_paged_decode_tokens.argtypes = [p, p, i32, p, p, i32, p, i32, p, i32, i32, i32,
+                                              i32, i32, f32, f32, f32]
+        L.orc_move_tokens.restype = None
+        L.orc_move_tokens.argtypes = [p, p, i32, p, i32, i32, i32, i32, i32]
         L.orc_paged_prefill.restype = None
         L.orc_paged_prefill.argtypes = [p, p, i32, p, p, i32, p, i32, p, p, i32, i32, i32, i32,
                                         i32, f32, f32, f32]
@@ -214,6 +219,37 @@ def paged_prefill(q_bits, q_dtype, k_pool, v_pool, kv_dtype, block_tables, conte
                             block_size, float(np.float32(scale)), float(k_scale),
                             float(v_scale))
     return out
+
+
+def paged_decode_tokens(q_bits, q_dtype, k_pool, v_pool, kv_dtype, token_slots, context_lens,
+                        num_kv_heads, block_size, scale, k_scale=1.0, v_scale=1.0):
+    """fp64 decode attention reading logical token t of sequence s from
+    physical slot token_slots[s][t]; q_bits [S][H][d] -> [S][H][d]."""
+    q = _c(q_bits, np.uint16)
+    kp = _c(k_pool, np.uint8)
+    vp = _c(v_pool, np.uint8)
+    ts = _c(token_slots, np.int32)
+    cl = _c(context_lens, np.int32)
+    S, H, D = q.shape
+    out = np.zeros((S, H, D), np.float64)
+    lib().orc_paged_decode_tokens(_ptr(out), _ptr(q), q_dtype, _ptr(kp), _ptr(vp), kv_dtype,
+                                  _ptr(ts), ts.shape[1], _ptr(cl), S, H, num_kv_heads, D,
+                                  block_size, float(np.float32(scale)), float(k_scale),
+                                  float(v_scale))
+    return out
+
+
+def move_tokens(k_pools, v_pools, moves, kv_heads, head_dim, block_size, kv_dtype):
+    """Copies of the pools (lists of uint8 arrays, one per layer) with each
+    token slot moves[i][0] copied to moves[i][1] (K and V, every kv head)."""
+    ks = [np.array(p, np.uint8, copy=True) for p in k_pools]
+    vs = [np.array(p, np.uint8, copy=True) for p in v_pools]
+    mv = _c(np.asarray(moves, np.int32).reshape(-1, 2), np.int32)
+    kp = (ctypes.c_void_p * max(len(ks), 1))(*[a.ctypes.data for a in ks])
+    vp = (ctypes.c_void_p * max(len(vs), 1))(*[a.ctypes.data for a in vs])
+    lib().orc_move_tokens(kp, vp, len(ks), _ptr(mv), mv.shape[0], kv_heads, head_dim, block_size,
+                          kv_dtype)
+    return ks, vs
 
 
 def max_threads():

@@ -118,6 +118,8 @@ class BlockPoolModel:
     def append_token(self, sid, token=0):
         """Returns (slot, cow_src, cow_dst) ([P1] §4; copy-on-write)."""
         s = self.seqs[sid]
+        if "slots" in s:
+            raise ValueError("evicted tokens: repack first")
         bs = self.bs
         pos = len(s["tokens"])
         j, off = divmod(pos, bs)
@@ -144,6 +146,8 @@ class BlockPoolModel:
     def fork(self, parent, child):
         assert child not in self.seqs
         p = self.seqs[parent]
+        if "slots" in p:
+            raise ValueError("evicted tokens: repack first")
         self.seqs[child] = {"blocks": list(p["blocks"]), "tokens": list(p["tokens"]),
                             "keys": list(p["keys"]), "root": p["root"]}
         for b in p["blocks"]:
@@ -156,6 +160,56 @@ class BlockPoolModel:
 
     def block_table(self, sid):
         return list(self.seqs[sid]["blocks"])
+
+    # -- token-level virtualisation ("vToken" page) ---------------------------
+    # A sequence's logical tokens each have a physical slot; normally slot(t)
+    # = blocks[t // bs] * bs + t % bs.  Evicting tokens leaves the survivors
+    # where they are (their slots in logical order form the token table);
+    # repacking moves them so that the table is block-aligned again and the
+    # emptied blocks can be freed.  Readings: a sequence whose blocks are
+    # shared cannot evict (its blocks would change under other readers);
+    # evicted content is no longer the hashed prefix, so the blocks lose
+    # their cached content; repacking fills the sequence's own blocks in
+    # order (all sources are read before any destination is written), frees
+    # the blocks it no longer needs last block first, and a sequence must be
+    # repacked before it grows again.
+    def token_slots(self, sid):
+        s = self.seqs[sid]
+        if "slots" in s:
+            return list(s["slots"])
+        bs = self.bs
+        return [s["blocks"][t // bs] * bs + t % bs for t in range(len(s["tokens"]))]
+
+    def evict_tokens(self, sid, keep):
+        s = self.seqs[sid]
+        assert len(keep) == len(s["tokens"])
+        if any(self.ref[b] != 1 for b in s["blocks"]):
+            raise ValueError("shared blocks")
+        slots = self.token_slots(sid)
+        s["slots"] = [sl for sl, k in zip(slots, keep) if k]
+        s["tokens"] = [t for t, k in zip(s["tokens"], keep) if k]
+        s["keys"] = []
+        for b in s["blocks"]:
+            if b in self.key_of:
+                del self.block_of[self.key_of.pop(b)]
+
+    def repack(self, sid):
+        """Returns the (src_slot, dst_slot) moves that make the table aligned."""
+        s = self.seqs[sid]
+        bs = self.bs
+        cur = self.token_slots(sid)
+        n = len(cur)
+        keep_blocks = -(-n // bs)
+        moves = []
+        for q, src in enumerate(cur):
+            dst = s["blocks"][q // bs] * bs + q % bs
+            if src != dst:
+                moves.append((src, dst))
+        for b in reversed(s["blocks"][keep_blocks:]):
+            self._release(b)
+        s["blocks"] = s["blocks"][:keep_blocks]
+        s.pop("slots", None)
+        return moves
 
     def slots(self, sid, first, count):
         bl = self.seqs[sid]["blocks"]

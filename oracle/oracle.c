@@ -349,6 +349,103 @@ void orc_paged_prefill(double* out, const uint16_t* q, int q_dtype, const uint8_
     }
 }
 
+/* Decode through a per-token table ("vToken" page, "the core idea:
+ * token-level virtualisation"): logical token t of sequence s sits at
+ * physical slot token_slots[s][t] (block slot / block_size, row slot %
+ * block_size), whatever the order of the slots; the result is the same
+ * softmax attention over the c = ctx[s] logical tokens as orc_paged_decode,
+ * whose block table is the special case slot = table[t / bs] * bs + t % bs. */
+void orc_paged_decode_tokens(double* out, const uint16_t* q, int q_dtype, const uint8_t* k_pool,
+                             const uint8_t* v_pool, int kv_dtype, const int32_t* token_slots,
+                             int max_tokens, const int32_t* ctx, int num_seqs, int heads,
+                             int kv_heads, int head_dim, int block_size, float scale,
+                             float k_scale, float v_scale) {
+    int group = heads / kv_heads;
+    double kdq = kv_dtype == ORC_FP8 ? (double)k_scale : 1.0;
+    double vdq = kv_dtype == ORC_FP8 ? (double)v_scale : 1.0;
+    int64_t pairs = (int64_t)num_seqs * heads;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t sh = 0; sh < pairs; ++sh) {
+        int s = (int)(sh / heads), h = (int)(sh % heads), g = h / group;
+        double* o = out + sh * head_dim;
+        for (int k = 0; k < head_dim; ++k) o[k] = 0.0;
+        int c = ctx[s];
+        if (c <= 0) continue;
+        const int32_t* slots = token_slots + (int64_t)s * max_tokens;
+        double* qd = malloc(sizeof(double) * head_dim);
+        double* logit = malloc(sizeof(double) * c);
+        for (int k = 0; k < head_dim; ++k) {
+            uint16_t bits = q[sh * head_dim + k];
+            qd[k] = q_dtype == ORC_BF16 ? orc_bf16_value(bits) : orc_fp16_value(bits);
+        }
+        double mx = -INFINITY;
+        for (int t = 0; t < c; ++t) {
+            int64_t pb = slots[t] / block_size;
+            int row = slots[t] % block_size;
+            double dot = 0.0;
+            for (int k = 0; k < head_dim; ++k) {
+                int64_t off = orc_pool_offset(pb, g, row, k, 0, kv_heads, head_dim, block_size,
+                                              kv_dtype);
+                dot += qd[k] * (elem_value(k_pool + off, kv_dtype) * kdq);
+            }
+            logit[t] = (double)scale * dot;
+            if (logit[t] > mx) mx = logit[t];
+        }
+        double denom = 0.0;
+        for (int t = 0; t < c; ++t) {
+            double w = exp(logit[t] - mx);
+            denom += w;
+            int64_t pb = slots[t] / block_size;
+            int row = slots[t] % block_size;
+            for (int k = 0; k < head_dim; ++k) {
+                int64_t off = orc_pool_offset(pb, g, row, k, 1, kv_heads, head_dim, block_size,
+                                              kv_dtype);
+                o[k] += w * (elem_value(v_pool + off, kv_dtype) * vdq);
+            }
+        }
+        for (int k = 0; k < head_dim; ++k) o[k] /= denom;
+        free(qd);
+        free(logit);
+    }
+}
+
+/* Move whole tokens ("vToken" page, asynchronous repacking: a surviving
+ * token's K and V move to another slot, the logical order is kept by the
+ * token table): for each (src, dst) slot pair, every element of every kv
+ * head of the token's K and V rows is copied, in every layer's pools given.
+ * All sources are read before any destination is written. */
+void orc_move_tokens(uint8_t* const* k_pools, uint8_t* const* v_pools, int num_layers,
+                     const int32_t* moves, int num_moves, int kv_heads, int head_dim,
+                     int block_size, int kv_dtype) {
+    int e = kv_dtype == ORC_FP8 ? 1 : 2;
+    size_t per = (size_t)kv_heads * head_dim * e;
+    uint8_t* tmp = malloc(per * 2 * (size_t)(num_moves > 0 ? num_moves : 1));
+    for (int l = 0; l < num_layers; ++l) {
+        for (int pass = 0; pass < 2; ++pass) {
+            for (int i = 0; i < num_moves; ++i) {
+                int32_t slot = moves[2 * i + pass];           /* pass 0 reads src, pass 1 writes dst */
+                int64_t pb = slot / block_size;
+                int row = slot % block_size;
+                for (int which = 0; which < 2; ++which) {
+                    uint8_t* pool = which ? v_pools[l] : k_pools[l];
+                    uint8_t* t = tmp + ((size_t)i * 2 + which) * per;
+                    for (int g = 0; g < kv_heads; ++g)
+                        for (int k = 0; k < head_dim; ++k) {
+                            int64_t off = orc_pool_offset(pb, g, row, k, which, kv_heads,
+                                                          head_dim, block_size, kv_dtype);
+                            uint8_t* x = t + ((size_t)g * head_dim + k) * e;
+                            for (int b = 0; b < e; ++b) {
+                                if (pass == 0) x[b] = pool[off + b];
+                                else pool[off + b] = x[b];
+                            }
+                        }
+                }
+            }
+        }
+    }
+    free(tmp);
+}
+
 int orc_max_threads(void) {
 #ifdef _OPENMP
     return omp_get_max_threads();
