@@ -60,7 +60,7 @@ def parse():
 
 def kernel_source_hash():
     h = hashlib.sha256()
-    for f in ("decode_core.h", "decode.hip", "pkv_device.h"):
+    for f in ("decode_core.h", "mfma_math.h", "decode.hip", "pkv_device.h"):
         with open(os.path.join(ROOT, "paged_kv_cache_51_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

@@ -429,6 +429,65 @@ int32_t pkv_bm_block_table(const pkv_block_manager* bm, int64_t seq_id, int32_t*
 int32_t pkv_bm_slots(const pkv_block_manager* bm, int64_t seq_id, int32_t first_pos,
                      int32_t count, int32_t* slots);
 
+/* Token-level virtualisation ([P4] "vToken": a token table maps each
+ * logical token to its physical place; tokens dropped by an eviction
+ * policy leave holes; repacking moves survivors so whole blocks can be
+ * freed, keeping the logical order).
+ * pkv_bm_evict_tokens: keep[t] != 0 keeps logical token t (host array of
+ *   num_tokens = the sequence's token count).  Survivors keep their slots,
+ *   in logical order; the sequence must own every block alone
+ *   (PKV_ERR_ARG otherwise); its blocks lose any cached prefix content.
+ *   Until repacked, the sequence cannot grow or fork, and attention must
+ *   read it through pkv_bm_token_slots / paged_attention_decode_tokens.
+ * pkv_bm_repack: host array moves[max_moves][2] receives the (src, dst)
+ *   slot moves that put survivor q at block q / bs, row q % bs of the
+ *   sequence's own blocks; *num_moves = their count (PKV_ERR_SIZE, state
+ *   unchanged, if more than max_moves).  The blocks past the survivors are
+ *   freed at once (last first): run pkv_move_tokens on the stream before
+ *   anything else writes to them.
+ * pkv_bm_token_slots: slot of every logical token (host array of
+ *   max_tokens, padded with 0). */
+int32_t pkv_bm_evict_tokens(pkv_block_manager* bm, int64_t seq_id, const uint8_t* keep,
+                            int32_t num_tokens);
+int32_t pkv_bm_repack(pkv_block_manager* bm, int64_t seq_id, int32_t* moves, int32_t max_moves,
+                      int32_t* num_moves);
+int32_t pkv_bm_token_slots(const pkv_block_manager* bm, int64_t seq_id, int32_t* slots,
+                           int32_t max_tokens, int32_t* num_tokens);
+
+/* Decode through a per-token table ([P4] "vToken"): logical token t of
+ * sequence s is read from physical slot token_slots[s][t] (device int32
+ * [num_seqs][max_tokens_per_seq]; block slot / block_size, row slot %
+ * block_size), for t < min(context_lens[s], max_tokens_per_seq).  Otherwise
+ * as paged_attention_decode (no split, no workspace).  Slots outside
+ * [block_size, num_blocks * block_size) are read as slot block_size.  A
+ * block-aligned table gives exactly the block-table result; a fragmented
+ * one costs element-wise V loads (see DESIGN).  Errors: as
+ * paged_attention_decode. */
+int32_t paged_attention_decode_tokens(void* out, const void* q, int32_t q_dtype,
+                                      const void* k_cache, const void* v_cache,
+                                      const int32_t* token_slots, int32_t max_tokens_per_seq,
+                                      const int32_t* context_lens, int32_t num_seqs,
+                                      int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                      float scale, int32_t block_size, int32_t num_blocks,
+                                      int32_t kv_dtype, float k_scale, float v_scale,
+                                      pkv_stream_t stream);
+
+/* Move whole tokens (K and V rows of every kv head, every layer) from slot
+ * moves[i][0] to slot moves[i][1] ([P4] "vToken" repacking); moves is a
+ * device int32 [num_moves][2].  Every source is read before any
+ * destination is written (through `scratch`, device memory of at least
+ * pkv_move_tokens_scratch_bytes(...) bytes), so moves may chain or swap.
+ * A move naming a slot outside [block_size, num_blocks * block_size) is
+ * skipped; two moves must not share a destination.  Errors: PKV_ERR_ARG,
+ * PKV_ERR_SIZE (scratch), PKV_ERR_UNSUPPORTED (head_dim), PKV_ERR_HIP. */
+int64_t pkv_move_tokens_scratch_bytes(int32_t num_layers, int32_t num_moves,
+                                      int32_t num_kv_heads, int32_t head_dim, int32_t kv_dtype);
+int32_t pkv_move_tokens(void* const* k_layers, void* const* v_layers, int32_t num_layers,
+                        int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
+                        int32_t block_size, int32_t kv_dtype, const int32_t* moves,
+                        int32_t num_moves, void* scratch, int64_t scratch_bytes,
+                        pkv_stream_t stream);
+
 /* Copy whole blocks (all kv heads, K and V, every layer) from pairs[i][0]
  * to pairs[i][1] ([P1] §4 copy-on-write): pairs is a device int32 array of
  * num_pairs (src, dst); k_layers / v_layers are host arrays of num_layers

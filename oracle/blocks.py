@@ -136,7 +136,7 @@ class BlockPoolModel:
             self._release(src)
             s["blocks"][j] = dst
         s["tokens"].append(token)
-        if self.prefix and off == bs - 1:
+        if self.prefix and off == bs - 1 and not s.get("evicted"):
             parent = s["keys"][j - 1] if j else s["root"]
             key = (parent, tuple(s["tokens"][j * bs:(j + 1) * bs]))
             s["keys"].append(key)
@@ -150,6 +150,8 @@ class BlockPoolModel:
             raise ValueError("evicted tokens: repack first")
         self.seqs[child] = {"blocks": list(p["blocks"]), "tokens": list(p["tokens"]),
                             "keys": list(p["keys"]), "root": p["root"]}
+        if p.get("evicted"):
+            self.seqs[child]["evicted"] = True
         for b in p["blocks"]:
             self.ref[b] += 1
 
@@ -169,7 +171,9 @@ class BlockPoolModel:
     # emptied blocks can be freed.  Readings: a sequence whose blocks are
     # shared cannot evict (its blocks would change under other readers);
     # evicted content is no longer the hashed prefix, so the blocks lose
-    # their cached content; repacking fills the sequence's own blocks in
+    # their cached content, and the sequence never publishes content again
+    # (the K/V of its later tokens were computed with the evicted ones in
+    # context, so they match no prompt); repacking fills the sequence's own blocks in
     # order (all sources are read before any destination is written), frees
     # the blocks it no longer needs last block first, and a sequence must be
     # repacked before it grows again.
@@ -189,6 +193,7 @@ class BlockPoolModel:
         s["slots"] = [sl for sl, k in zip(slots, keep) if k]
         s["tokens"] = [t for t, k in zip(s["tokens"], keep) if k]
         s["keys"] = []
+        s["evicted"] = True      # its K/V no longer match any prompt: never published again
         for b in s["blocks"]:
             if b in self.key_of:
                 del self.block_of[self.key_of.pop(b)]

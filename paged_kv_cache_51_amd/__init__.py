@@ -12,5 +12,6 @@ from ._binding import (  # noqa: F401
     layer_pool_bytes, workspace_bytes, default_partition_tokens, plan_bytes, build_plan,
     decode_slot_mapping, reshape_and_cache,
     paged_attention_decode, check_block_tables, torch_dtype, dtype_code, EXPORTS,
-    BlockManager, copy_blocks, paged_attention_prefill,
+    BlockManager, copy_blocks, paged_attention_prefill, paged_attention_decode_tokens,
+    move_tokens,
 )

@@ -29,7 +29,9 @@ EXPORTS = [
     "pkv_bm_create", "pkv_bm_destroy", "pkv_bm_num_free_blocks", "pkv_bm_num_cached_free_blocks",
     "pkv_bm_ref_count", "pkv_bm_num_tokens", "pkv_bm_add_sequence", "pkv_bm_append_token",
     "pkv_bm_fork", "pkv_bm_free_sequence", "pkv_bm_block_table", "pkv_bm_slots",
-    "pkv_copy_blocks", "paged_attention_prefill",
+    "pkv_copy_blocks", "paged_attention_prefill", "pkv_bm_evict_tokens", "pkv_bm_repack",
+    "pkv_bm_token_slots", "paged_attention_decode_tokens", "pkv_move_tokens_scratch_bytes",
+    "pkv_move_tokens",
 ]
 
 
@@ -105,6 +107,13 @@ def lib():
             "pkv_copy_blocks": (i32, [p, p, i32, i32, i32, i32, i32, i32, p, i32, p]),
             "paged_attention_prefill": (i32, [p, p, i32, p, p, p, i32, p, p, i32, i32, i32, i32,
                                               i32, i32, f32, i32, i32, f32, f32, p]),
+            "pkv_bm_evict_tokens": (i32, [p, i64, p, i32]),
+            "pkv_bm_repack": (i32, [p, i64, p, i32, ctypes.POINTER(i32)]),
+            "pkv_bm_token_slots": (i32, [p, i64, p, i32, ctypes.POINTER(i32)]),
+            "paged_attention_decode_tokens": (i32, [p, p, i32, p, p, p, i32, p, i32, i32, i32,
+                                                    i32, f32, i32, i32, i32, f32, f32, p]),
+            "pkv_move_tokens_scratch_bytes": (i64, [i32, i32, i32, i32, i32]),
+            "pkv_move_tokens": (i32, [p, p, i32, i32, i32, i32, i32, i32, p, i32, p, i64, p]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -378,6 +387,33 @@ class BlockManager:
         _check(lib().pkv_bm_slots(self._h, seq_id, first_pos, count, arr))
         return list(arr[:count])
 
+    def evict_tokens(self, seq_id, keep):
+        """keep: sequence of bools over the sequence's logical tokens."""
+        arr = (ctypes.c_uint8 * max(len(keep), 1))(*[1 if k else 0 for k in keep])
+        _check(lib().pkv_bm_evict_tokens(self._h, seq_id, arr, len(keep)))
+
+    def repack(self, seq_id):
+        """Returns the list of (src_slot, dst_slot) moves to run."""
+        n = ctypes.c_int32(0)
+        rc = lib().pkv_bm_repack(self._h, seq_id, None, 0, ctypes.byref(n))
+        if rc >= 0:
+            return []
+        if rc != -2:
+            _check(rc)
+        arr = (ctypes.c_int32 * (2 * n.value))()
+        _check(lib().pkv_bm_repack(self._h, seq_id, arr, n.value, ctypes.byref(n)))
+        return [(arr[2 * i], arr[2 * i + 1]) for i in range(n.value)]
+
+    def token_slots(self, seq_id, max_tokens=None):
+        n = ctypes.c_int32(0)
+        rc = lib().pkv_bm_token_slots(self._h, seq_id, None, 0, ctypes.byref(n))
+        if rc < 0 and rc != -2:
+            _check(rc)
+        m = n.value if max_tokens is None else max_tokens
+        arr = (ctypes.c_int32 * max(m, 1))()
+        _check(lib().pkv_bm_token_slots(self._h, seq_id, arr, m, ctypes.byref(n)))
+        return list(arr[:m])
+
 
 def copy_blocks(k_layers, v_layers, pairs, num_blocks, num_kv_heads, head_dim, block_size,
                 kv_dtype, stream=None):
@@ -411,3 +447,33 @@ def paged_attention_prefill(out, q, k_cache, v_cache, block_tables, context_lens
         _ptr(query_start_loc, "query_start_loc", torch.int32), int(max_query_len),
         int(max_context_len), S, H, num_kv_heads, D, float(scale), block_size, kv_dtype,
         float(k_scale), float(v_scale), _stream(stream)))
+
+
+def paged_attention_decode_tokens(out, q, k_cache, v_cache, token_slots, context_lens,
+                                  num_kv_heads, block_size, num_blocks, kv_dtype, scale,
+                                  k_scale=1.0, v_scale=1.0, stream=None):
+    """Decode reading logical token t of sequence s from slot token_slots[s][t]."""
+    S, H, D = q.shape
+    _check(lib().paged_attention_decode_tokens(
+        _ptr(out, "out", q.dtype), _ptr(q, "q"), dtype_code(q.dtype), _ptr(k_cache, "k_cache"),
+        _ptr(v_cache, "v_cache"), _ptr(token_slots, "token_slots", torch.int32),
+        token_slots.shape[1], _ptr(context_lens, "context_lens", torch.int32), S, H,
+        num_kv_heads, D, float(scale), block_size, num_blocks, kv_dtype, float(k_scale),
+        float(v_scale), _stream(stream)))
+
+
+def move_tokens(k_layers, v_layers, moves, num_blocks, num_kv_heads, head_dim, block_size,
+                kv_dtype, scratch=None, stream=None):
+    """pkv_move_tokens: moves is a device int32 tensor [n, 2] of (src, dst)
+    slots; scratch (uint8, allocated here if None) holds the staged rows."""
+    n = len(k_layers)
+    nm = moves.shape[0]
+    need = _check(lib().pkv_move_tokens_scratch_bytes(n, nm, num_kv_heads, head_dim, kv_dtype))
+    if scratch is None:
+        scratch = torch.empty(max(need, 1), dtype=torch.uint8, device=moves.device)
+    kp = (ctypes.c_void_p * max(n, 1))(*[_ptr(t, "k_layers", torch.uint8).value for t in k_layers])
+    vp = (ctypes.c_void_p * max(n, 1))(*[_ptr(t, "v_layers", torch.uint8).value for t in v_layers])
+    _check(lib().pkv_move_tokens(kp, vp, n, num_blocks, num_kv_heads, head_dim, block_size, kv_dtype,
+                                 _ptr(moves, "moves", torch.int32), nm, _ptr(scratch, "scratch"),
+                                 scratch.numel(), _stream(stream)))
+    return scratch

@@ -456,6 +456,88 @@ int32_t paged_attention_prefill(void* out, const void* q, int32_t q_dtype, const
     return ok();
 }
 
+int32_t paged_attention_decode_tokens(void* out, const void* q, int32_t q_dtype,
+                                      const void* k_cache, const void* v_cache,
+                                      const int32_t* token_slots, int32_t max_tokens_per_seq,
+                                      const int32_t* context_lens, int32_t num_seqs,
+                                      int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                      float scale, int32_t block_size, int32_t num_blocks,
+                                      int32_t kv_dtype, float k_scale, float v_scale,
+                                      pkv_stream_t stream) {
+    if (int32_t e = check_layout_args(head_dim, block_size, kv_dtype)) return e;
+    if (q_dtype != PKV_BF16 && q_dtype != PKV_FP16) return fail(PKV_ERR_ARG, "q_dtype must be bf16 or fp16");
+    if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || max_tokens_per_seq < 0 || num_blocks < 2)
+        return fail(PKV_ERR_ARG, "bad sizes (num_blocks must count the null block and at least one more)");
+    if ((int64_t)num_blocks * block_size >= (1LL << 31)) return fail(PKV_ERR_ARG, "slots must fit int32");
+    if (num_heads % num_kv_heads) return fail(PKV_ERR_ARG, "num_heads %d is not a multiple of num_kv_heads %d", num_heads, num_kv_heads);
+    const int32_t G = num_heads / num_kv_heads;
+    if (G > 16) return fail(PKV_ERR_UNSUPPORTED, "query heads per kv head %d > 16", G);
+    if (head_dim != kBuiltHeadDim) return fail(PKV_ERR_UNSUPPORTED, "kernels are built for head_dim 128, got %d", head_dim);
+    if (kv_dtype != PKV_FP8_E4M3 && kv_dtype != q_dtype)
+        return fail(PKV_ERR_UNSUPPORTED, "a 16-bit KV pool must have the query dtype");
+    if (!std::isfinite(scale)) return fail(PKV_ERR_ARG, "scale must be finite");
+    if (kv_dtype == PKV_FP8_E4M3 && !(std::isfinite(k_scale) && std::isfinite(v_scale)))
+        return fail(PKV_ERR_ARG, "fp8 scales must be finite");
+    if ((int64_t)num_seqs * num_kv_heads > 0x7fffffff) return fail(PKV_ERR_UNSUPPORTED, "too many workgroups");
+    if (num_seqs > 0 && (!out || !q || !k_cache || !v_cache || !context_lens ||
+                         (max_tokens_per_seq > 0 && !token_slots)))
+        return fail(PKV_ERR_ARG, "null pointer");
+    pkv::DecodeArgs a{};
+    a.out = out;
+    a.q = q;
+    a.k_cache = (const uint8_t*)k_cache;
+    a.v_cache = (const uint8_t*)v_cache;
+    a.context_lens = context_lens;
+    a.num_seqs = num_seqs;
+    a.num_heads = num_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.group = G;
+    a.part_blocks = 1;
+    a.num_parts = 1;
+    a.num_blocks = num_blocks;
+    const float ks = kv_dtype == PKV_FP8_E4M3 ? k_scale : 1.0f;
+    a.qk_scale_log2 = (float)((double)scale * (double)ks * 1.4426950408889634);
+    a.out_scale = kv_dtype == PKV_FP8_E4M3 ? v_scale : 1.0f;
+    (void)hipGetLastError();
+    hipError_t e = pkv::launch_decode_tokens(a, q_dtype, kv_dtype, block_size, token_slots,
+                                             max_tokens_per_seq, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "token-table decode launch");
+    return ok();
+}
+
+int64_t pkv_move_tokens_scratch_bytes(int32_t num_layers, int32_t num_moves,
+                                      int32_t num_kv_heads, int32_t head_dim, int32_t kv_dtype) {
+    if (!valid_dtype(kv_dtype) || num_layers < 0 || num_moves < 0 || num_kv_heads <= 0 || head_dim <= 0)
+        return fail(PKV_ERR_ARG, "bad sizes");
+    ok();
+    return (int64_t)num_moves * num_layers * 2 * num_kv_heads * head_dim * elem_size(kv_dtype);
+}
+
+int32_t pkv_move_tokens(void* const* k_layers, void* const* v_layers, int32_t num_layers,
+                        int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
+                        int32_t block_size, int32_t kv_dtype, const int32_t* moves,
+                        int32_t num_moves, void* scratch, int64_t scratch_bytes,
+                        pkv_stream_t stream) {
+    if (int32_t e = check_layout_args(head_dim, block_size, kv_dtype)) return e;
+    if (head_dim != kBuiltHeadDim) return fail(PKV_ERR_UNSUPPORTED, "kernels are built for head_dim 128, got %d", head_dim);
+    if (num_layers < 0 || num_moves < 0 || num_kv_heads <= 0 || num_blocks < 1)
+        return fail(PKV_ERR_ARG, "bad sizes");
+    if ((int64_t)num_blocks * block_size >= (1LL << 31)) return fail(PKV_ERR_ARG, "slots must fit int32");
+    if (num_moves == 0 || num_layers == 0) return ok();
+    if (!k_layers || !v_layers || !moves) return fail(PKV_ERR_ARG, "null pointer");
+    for (int32_t l = 0; l < num_layers; ++l)
+        if (!k_layers[l] || !v_layers[l]) return fail(PKV_ERR_ARG, "null layer pointer");
+    const int64_t need = (int64_t)num_moves * num_layers * 2 * num_kv_heads * head_dim * elem_size(kv_dtype);
+    if (!scratch || scratch_bytes < need)
+        return fail(PKV_ERR_SIZE, "scratch needs %lld bytes, got %lld", (long long)need, (long long)scratch_bytes);
+    (void)hipGetLastError();
+    hipError_t e = pkv::launch_move_tokens(k_layers, v_layers, num_layers, num_blocks, num_kv_heads,
+                                           block_size, kv_dtype, moves, num_moves, scratch,
+                                           (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "move_tokens launch");
+    return ok();
+}
+
 int32_t paged_attention_decode(void* out, const void* q, int32_t q_dtype, const void* k_cache,
                                const void* v_cache, const int32_t* block_tables,
                                int32_t max_blocks_per_seq, const int32_t* context_lens,

@@ -82,6 +82,9 @@ struct Sequence {
     std::vector<int32_t> blocks;   // block table
     std::vector<int32_t> tokens;   // kept only with the prefix cache
     std::vector<uint64_t> chain;   // content hash of each full block so far
+    std::vector<int32_t> slots;    // per-token slots after an eviction (else empty)
+    bool fragmented = false;       // tokens evicted and not yet repacked
+    bool evicted = false;          // ever lost tokens: its K/V match no prompt, never published
     int32_t num_tokens = 0;
     uint64_t seed = 0;
 };
@@ -305,6 +308,7 @@ int32_t pkv_bm_append_token(pkv_block_manager* bm, int64_t seq_id, int32_t token
     if (!bm || !slot) return fail(PKV_ERR_ARG, "null pointer");
     pkv::Sequence* sq = find_seq(bm, seq_id);
     if (!sq) return fail(PKV_ERR_ARG, "unknown sequence %lld", (long long)seq_id);
+    if (sq->fragmented) return fail(PKV_ERR_ARG, "sequence %lld has evicted tokens: repack it first", (long long)seq_id);
     pkv::BlockManager& m = bm->m;
     const int bs = m.block_size;
     const int32_t pos = sq->num_tokens;
@@ -321,7 +325,7 @@ int32_t pkv_bm_append_token(pkv_block_manager* bm, int64_t seq_id, int32_t token
         m.release(src);
         sq->blocks[j] = dst;
     }
-    if (m.prefix_cache) {
+    if (m.prefix_cache && !sq->evicted) {
         sq->tokens.push_back(token);
         if (off == bs - 1) {
             const uint64_t p = j ? sq->chain[j - 1] : sq->seed;
@@ -341,6 +345,7 @@ int32_t pkv_bm_fork(pkv_block_manager* bm, int64_t parent_id, int64_t child_id) 
     if (!bm) return fail(PKV_ERR_ARG, "null handle");
     pkv::Sequence* par = find_seq(bm, parent_id);
     if (!par) return fail(PKV_ERR_ARG, "unknown sequence %lld", (long long)parent_id);
+    if (par->fragmented) return fail(PKV_ERR_ARG, "sequence %lld has evicted tokens: repack it first", (long long)parent_id);
     if (find_seq(bm, child_id)) return fail(PKV_ERR_ARG, "sequence %lld exists", (long long)child_id);
     pkv::Sequence copy;
     try {
@@ -386,8 +391,91 @@ int32_t pkv_bm_slots(const pkv_block_manager* bm, int64_t seq_id, int32_t first_
     const int bs = bm->m.block_size;
     for (int32_t i = 0; i < count; ++i) {
         const int32_t p = first_pos + i;
-        slots[i] = sq->blocks[p / bs] * bs + p % bs;
+        slots[i] = sq->fragmented ? sq->slots[p] : sq->blocks[p / bs] * bs + p % bs;
     }
+    return ok();
+}
+
+// ---- token-level virtualisation ("vToken" page): eviction leaves the
+// survivors where they are (the per-token table lists their slots in
+// logical order); repacking moves them into the sequence's own blocks in
+// order, frees the blocks no longer needed (last first) and makes the table
+// block-aligned again.
+
+int32_t pkv_bm_evict_tokens(pkv_block_manager* bm, int64_t seq_id, const uint8_t* keep,
+                            int32_t num_tokens) {
+    if (!bm || (num_tokens > 0 && !keep)) return fail(PKV_ERR_ARG, "null pointer");
+    pkv::Sequence* sq = find_seq(bm, seq_id);
+    if (!sq) return fail(PKV_ERR_ARG, "unknown sequence %lld", (long long)seq_id);
+    if (num_tokens != sq->num_tokens)
+        return fail(PKV_ERR_ARG, "keep mask covers %d tokens, the sequence holds %d", num_tokens, sq->num_tokens);
+    pkv::BlockManager& m = bm->m;
+    for (int32_t b : sq->blocks)
+        if (m.ref[b] != 1) return fail(PKV_ERR_ARG, "block %d is shared: a shared block cannot lose tokens", b);
+    const int bs = m.block_size;
+    std::vector<int32_t> slots;
+    try {
+        slots.reserve(num_tokens);
+        for (int32_t t = 0; t < num_tokens; ++t)
+            if (keep[t]) slots.push_back(sq->fragmented ? sq->slots[t] : sq->blocks[t / bs] * bs + t % bs);
+    } catch (...) {
+        return fail(PKV_ERR_SIZE, "out of host memory");
+    }
+    // the blocks no longer hold the hashed token runs
+    for (int32_t b : sq->blocks) m.drop_content(b);
+    sq->slots = std::move(slots);
+    sq->tokens.clear();            // only needed to publish, which an evicted sequence never does
+    sq->chain.clear();
+    sq->num_tokens = (int32_t)sq->slots.size();
+    sq->fragmented = true;
+    sq->evicted = true;
+    return ok();
+}
+
+int32_t pkv_bm_repack(pkv_block_manager* bm, int64_t seq_id, int32_t* moves, int32_t max_moves,
+                      int32_t* num_moves) {
+    if (!bm || !num_moves || (max_moves > 0 && !moves)) return fail(PKV_ERR_ARG, "null pointer");
+    pkv::Sequence* sq = find_seq(bm, seq_id);
+    if (!sq) return fail(PKV_ERR_ARG, "unknown sequence %lld", (long long)seq_id);
+    pkv::BlockManager& m = bm->m;
+    const int bs = m.block_size;
+    const int32_t n = sq->num_tokens;
+    int32_t cnt = 0;
+    if (sq->fragmented)
+        for (int32_t q = 0; q < n; ++q) cnt += sq->slots[q] != sq->blocks[q / bs] * bs + q % bs;
+    *num_moves = cnt;
+    if (cnt > max_moves) return fail(PKV_ERR_SIZE, "%d moves, room for %d", cnt, max_moves);
+    if (sq->fragmented) {
+        int32_t i = 0;
+        for (int32_t q = 0; q < n; ++q) {
+            const int32_t dst = sq->blocks[q / bs] * bs + q % bs;
+            if (sq->slots[q] != dst) {
+                moves[2 * i] = sq->slots[q];
+                moves[2 * i + 1] = dst;
+                ++i;
+            }
+        }
+    }
+    const size_t need = (size_t)((n + bs - 1) / bs);
+    for (size_t i = sq->blocks.size(); i-- > need;) m.release(sq->blocks[i]);   // last block first
+    sq->blocks.resize(need);
+    sq->slots.clear();
+    sq->fragmented = false;
+    return ok();
+}
+
+int32_t pkv_bm_token_slots(const pkv_block_manager* bm, int64_t seq_id, int32_t* slots,
+                           int32_t max_tokens, int32_t* num_tokens) {
+    if (!bm || (max_tokens > 0 && !slots)) return fail(PKV_ERR_ARG, "null pointer");
+    const pkv::Sequence* sq = find_seq(const_cast<pkv_block_manager*>(bm), seq_id);
+    if (!sq) return fail(PKV_ERR_ARG, "unknown sequence %lld", (long long)seq_id);
+    if (num_tokens) *num_tokens = sq->num_tokens;
+    if (sq->num_tokens > max_tokens)
+        return fail(PKV_ERR_SIZE, "%d tokens, row has %d", sq->num_tokens, max_tokens);
+    const int bs = bm->m.block_size;
+    for (int32_t t = 0; t < max_tokens; ++t)
+        slots[t] = t >= sq->num_tokens ? 0
+                   : sq->fragmented ? sq->slots[t] : sq->blocks[t / bs] * bs + t % bs;
     return ok();
 }
 

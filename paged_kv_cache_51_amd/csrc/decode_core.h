@@ -106,6 +106,79 @@ struct QueryTile {
 constexpr int kWavesPerGroup = PKV_WAVES_PER_GROUP;
 constexpr int kDepth = PKV_PIPELINE_DEPTH;
 
+// Merge the NW waves of a work entry and store its result: every wave
+// parks its partial (m, l, O for the entry's columns) in LDS and leaves; the
+// last wave to arrive merges them and writes whole output rows (or, for a
+// split context, the partition's record).  No wave waits at a barrier for
+// the slowest one, so early finishers free their registers at once.
+template <class Math, int QT, int NW>
+__device__ __forceinline__ void park_and_store(const DecodeArgs& a, float* pkv_smem, Math& mt, int s,
+                                               int part, int kvh, int lane, int w,
+                                               const QueryTile& qt, int ncols, bool single) {
+    const int G = a.group;
+    int* done = reinterpret_cast<int*>(pkv_smem);   // zeroed before the workgroup barrier
+    float* sm_m = pkv_smem + 4;
+    float* sm_l = sm_m + NW * 16;
+    float* sm_acc = sm_l + NW * 16;
+    mt.park(sm_m, sm_l, sm_acc, w, ncols, lane);
+    __threadfence_block();
+    int prev = 0;
+    if (lane == 0) prev = atomicAdd(done, 1);
+    prev = __builtin_amdgcn_readfirstlane(prev);
+    if (prev != NW - 1) return;
+    __threadfence_block();
+
+    for (int c = 0; c < ncols; ++c) {
+        float M = -INFINITY;
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, sm_m[ww * 16 + c]);
+        float L = 0.f, o0 = 0.f, o1 = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) {
+            const float mw = sm_m[ww * 16 + c];
+            const float f = (mw == -INFINITY) ? 0.f : fast_exp2(mw - M);
+            const float2 ov = *reinterpret_cast<const float2*>(sm_acc + (ww * ncols + c) * kMergeRow + 2 * lane);
+            L += f * sm_l[ww * 16 + c];
+            o0 += f * ov.x;
+            o1 += f * ov.y;
+        }
+        // L = 0 only for a token placed before the start of the context
+        const float invL = L > 0.f ? 1.0f / L : 0.f;
+        const int h = c % G;
+        const int hq = kvh * G + h;
+        if (single) {
+            const float sc = invL * a.out_scale;
+            uint16_t* out = reinterpret_cast<uint16_t*>(a.out) +
+                            ((qt.row0 + c / G) * a.num_heads + hq) * kHeadDim;
+            *reinterpret_cast<uint32_t*>(out + 2 * lane) =
+                (uint32_t)f32_to_bits<QT>(o0 * sc) | ((uint32_t)f32_to_bits<QT>(o1 * sc) << 16);
+        } else {
+            // (split contexts are decode only: one token, column c = head h)
+            // record (s, kvh, part): G rows of head_dim floats, contiguous
+            const int64_t rec = ((int64_t)s * a.num_kv_heads + kvh) * a.num_parts + part;
+            *reinterpret_cast<float2*>(a.ws_out + (rec * G + h) * kHeadDim + 2 * lane) =
+                make_float2(o0 * invL, o1 * invL);
+        }
+    }
+    if (!single && lane < 32) {
+        // one full 128-byte line per record: maxima of the G heads at [0, 16),
+        // normalisers at [16, 32)
+        const int h = lane & 15;
+        float M = -INFINITY, L = 0.f;
+        if (h < G) {
+#pragma unroll
+            for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, sm_m[ww * 16 + h]);
+#pragma unroll
+            for (int ww = 0; ww < NW; ++ww) {
+                const float mw = sm_m[ww * 16 + h];
+                L += ((mw == -INFINITY) ? 0.f : fast_exp2(mw - M)) * sm_l[ww * 16 + h];
+            }
+        }
+        const int64_t rec = ((int64_t)s * a.num_kv_heads + kvh) * a.num_parts + part;
+        a.ws_ml[rec * 32 + lane] = (h < G) ? (lane < 16 ? M : L) : 0.f;
+    }
+}
+
 // Decode one work entry: kv head `kvh` of (sequence s, partition part) for
 // the query tile qt, by the NW waves of the calling workgroup.  Every exit
 // before the LDS counter barrier depends only on (s, part, qt), so all
@@ -225,70 +298,7 @@ __device__ __forceinline__ void decode_entry(const DecodeArgs& a, float* pkv_sme
             }
         }
     }
-    // ---- merge the NW waves: every wave parks its partial (m, l, O for the
-    // G real heads) in LDS and leaves; the last wave to arrive merges them
-    // and writes whole output rows.  No wave waits at a barrier for the
-    // slowest one, so early finishers free their registers at once.
-    float* sm_m = pkv_smem + 4;
-    float* sm_l = sm_m + NW * 16;
-    float* sm_acc = sm_l + NW * 16;
-    mt.park(sm_m, sm_l, sm_acc, w, ncols, lane);
-    __threadfence_block();
-    int prev = 0;
-    if (lane == 0) prev = atomicAdd(done, 1);
-    prev = __builtin_amdgcn_readfirstlane(prev);
-    if (prev != NW - 1) return;
-    __threadfence_block();
-
-    for (int c = 0; c < ncols; ++c) {
-        float M = -INFINITY;
-#pragma unroll
-        for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, sm_m[ww * 16 + c]);
-        float L = 0.f, o0 = 0.f, o1 = 0.f;
-#pragma unroll
-        for (int ww = 0; ww < NW; ++ww) {
-            const float mw = sm_m[ww * 16 + c];
-            const float f = (mw == -INFINITY) ? 0.f : fast_exp2(mw - M);
-            const float2 ov = *reinterpret_cast<const float2*>(sm_acc + (ww * ncols + c) * kMergeRow + 2 * lane);
-            L += f * sm_l[ww * 16 + c];
-            o0 += f * ov.x;
-            o1 += f * ov.y;
-        }
-        // L = 0 only for a token placed before the start of the context
-        const float invL = L > 0.f ? 1.0f / L : 0.f;
-        const int h = c % G;
-        const int hq = kvh * G + h;
-        if (single) {
-            const float sc = invL * a.out_scale;
-            uint16_t* out = reinterpret_cast<uint16_t*>(a.out) +
-                            ((qt.row0 + c / G) * a.num_heads + hq) * kHeadDim;
-            *reinterpret_cast<uint32_t*>(out + 2 * lane) =
-                (uint32_t)f32_to_bits<QT>(o0 * sc) | ((uint32_t)f32_to_bits<QT>(o1 * sc) << 16);
-        } else {
-            // (split contexts are decode only: one token, column c = head h)
-            // record (s, kvh, part): G rows of head_dim floats, contiguous
-            const int64_t rec = ((int64_t)s * a.num_kv_heads + kvh) * a.num_parts + part;
-            *reinterpret_cast<float2*>(a.ws_out + (rec * G + h) * kHeadDim + 2 * lane) =
-                make_float2(o0 * invL, o1 * invL);
-        }
-    }
-    if (!single && lane < 32) {
-        // one full 128-byte line per record: maxima of the G heads at [0, 16),
-        // normalisers at [16, 32)
-        const int h = lane & 15;
-        float M = -INFINITY, L = 0.f;
-        if (h < G) {
-#pragma unroll
-            for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, sm_m[ww * 16 + h]);
-#pragma unroll
-            for (int ww = 0; ww < NW; ++ww) {
-                const float mw = sm_m[ww * 16 + h];
-                L += ((mw == -INFINITY) ? 0.f : fast_exp2(mw - M)) * sm_l[ww * 16 + h];
-            }
-        }
-        const int64_t rec = ((int64_t)s * a.num_kv_heads + kvh) * a.num_parts + part;
-        a.ws_ml[rec * 32 + lane] = (h < G) ? (lane < 16 ? M : L) : 0.f;
-    }
+    park_and_store<Math, QT, NW>(a, pkv_smem, mt, s, part, kvh, lane, w, qt, ncols, single);
 }
 
 // Workgroups of the grid form: the plan's items in groups of 8, each group

@@ -70,6 +70,14 @@ hipError_t launch_decode_partitions(const DecodeArgs& a, int q_dtype, int kv_dty
                                     int block_size, int impl, hipStream_t st);
 hipError_t launch_decode_reduce(const DecodeArgs& a, int q_dtype, int block_size,
                                 hipStream_t st);
+// Decode through a per-token slot table; token moves between slots
+// (decode_tokens.hip).
+hipError_t launch_decode_tokens(const DecodeArgs& a, int q_dtype, int kv_dtype, int block_size,
+                                const int32_t* token_slots, int max_tokens, hipStream_t st);
+hipError_t launch_move_tokens(void* const* k_layers, void* const* v_layers, int num_layers,
+                              int num_blocks, int num_kv_heads, int block_size, int kv_dtype,
+                              const int32_t* moves, int num_moves, void* scratch, hipStream_t st);
+
 // Multi-token attention (query tiles of tile_tokens tokens, causal).
 hipError_t launch_prefill(const DecodeArgs& a, int q_dtype, int kv_dtype, int block_size,
                           const int32_t* query_start, int tile_tokens, int max_tiles,

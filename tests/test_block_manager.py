@@ -236,3 +236,70 @@ def test_oracle_copy_blocks_moves_whole_blocks():
     untouched = np.r_[0:3 * block, 4 * block:5 * block]
     assert np.array_equal(k[0][untouched], k0[untouched])
     assert np.array_equal(v[0][untouched], v0[untouched])
+
+
+@pytest.mark.parametrize("prefix,bs,seed", [(False, 16, 11), (True, 16, 12), (False, 32, 13)])
+def test_evict_and_repack_match_model(prefix, bs, seed):
+    """Token-level virtualisation ("vToken" page): random evictions and
+    repacks interleaved with growth, forks and frees; the library and the
+    model agree on every token table, move list, block table and count."""
+    rng = random.Random(seed)
+    nb = 48
+    lib_ = pkv.BlockManager(nb, bs, prefix)
+    ref = BlockPoolModel(nb, bs, prefix)
+    live, fragmented, next_id = [], set(), 0
+    for step in range(500):
+        op = rng.random()
+        if op < 0.15 or not live:
+            toks = [rng.randrange(5) for _ in range(rng.randrange(1, 70))]
+            try:
+                want = ref.add_sequence(next_id, toks)
+            except MemoryError:
+                with pytest.raises(pkv.PagedKVError):
+                    lib_.add_sequence(next_id, toks)
+            else:
+                assert lib_.add_sequence(next_id, toks) == want
+                live.append(next_id)
+            next_id += 1
+            continue
+        s = rng.choice(live)
+        if op < 0.45:
+            if s in fragmented:
+                with pytest.raises(pkv.PagedKVError):
+                    lib_.append_token(s, 1)
+                continue
+            try:
+                want = ref.append_token(s, rng.randrange(5))
+            except MemoryError:
+                with pytest.raises(pkv.PagedKVError):
+                    lib_.append_token(s, 0)
+            else:
+                assert lib_.append_token(s, ref.seqs[s]["tokens"][-1]) == want
+        elif op < 0.6:
+            n = len(ref.token_slots(s))
+            keep = [rng.random() < 0.6 for _ in range(n)]
+            try:
+                ref.evict_tokens(s, keep)
+            except ValueError:
+                with pytest.raises(pkv.PagedKVError):
+                    lib_.evict_tokens(s, keep)
+            else:
+                lib_.evict_tokens(s, keep)
+                fragmented.add(s)
+        elif op < 0.75:
+            assert lib_.repack(s) == ref.repack(s)
+            fragmented.discard(s)
+        elif op < 0.82 and s not in fragmented:
+            ref.fork(s, next_id)
+            lib_.fork(s, next_id)
+            live.append(next_id)
+            next_id += 1
+        else:
+            live.remove(s)
+            fragmented.discard(s)
+            ref.free_sequence(s)
+            lib_.free_sequence(s)
+        assert lib_.num_free_blocks() == ref.free_count()
+        for x in live:
+            assert lib_.token_slots(x) == ref.token_slots(x)
+            assert lib_.block_table(x) == ref.block_table(x)
