@@ -46,10 +46,13 @@ def parse():
                     help="target CPU time of the oracle sample (0 disables)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one device copy of this size (counter calibration)")
-    ap.add_argument("--op", default="decode", choices=["decode", "copy_blocks", "prefill"],
+    ap.add_argument("--keep", type=float, default=0.5,
+                    help="vtoken: fraction of context tokens an eviction keeps")
+    ap.add_argument("--op", default="decode", choices=["decode", "copy_blocks", "prefill", "vtoken"],
                     help="decode: the attention step (default); copy_blocks: copy-on-write "
                          "block copies over the same pool shape; prefill: multi-token causal "
-                         "attention (the last --q-len tokens of each sequence are new)")
+                         "attention (the last --q-len tokens of each sequence are new); vtoken: "
+                         "decode through a fragmented token table, repack moves, decode after")
     ap.add_argument("--q-len", type=int, default=512, help="prefill: new tokens per sequence")
     ap.add_argument("--num-seqs", type=int, default=0,
                     help="prefill: sequences (default 16, or the workload's batch if --q-len <= 16)")
@@ -97,6 +100,9 @@ def main():
         return
     if args.op == "prefill":
         bench_prefill(args, torch, pkv, workloads)
+        return
+    if args.op == "vtoken":
+        bench_vtoken(args, torch, pkv, workloads)
         return
 
     dt_names = {"bf16": pkv.BF16, "fp16": pkv.FP16, "fp8": pkv.FP8_E4M3}
@@ -375,6 +381,123 @@ def bench_prefill(args, torch, pkv, workloads):
                      "frac": round((tflops / peak_tf) if mfma_bound else (gbs / PEAK_HBM_GBS), 4),
                      "traffic": None, "avg_launch_us": round(launch_ms * 1e3, 2),
                      "algorithmic_flops_per_launch": flops, "algorithmic_bytes_per_launch": nbytes},
+        "cpu_baseline": None,
+    }), flush=True)
+
+
+def bench_vtoken(args, torch, pkv, workloads):
+    """Token-level virtualisation on the workload: every sequence keeps a
+    random --keep fraction of its context (an eviction); time (1) decode
+    through the fragmented token table, (2) the repack moves over all
+    layers, (3) the block-table decode of the repacked sequences.  Bytes:
+    surviving K/V + q/out for the decodes; moved token rows read + written
+    for the repack."""
+    cfg, tabs, _, _ = workloads.make(args.config, seed=args.seed, block_size=args.block_size)
+    dt_names = {"bf16": pkv.BF16, "fp16": pkv.FP16, "fp8": pkv.FP8_E4M3}
+    kv = dt_names[args.kv_dtype] if args.kv_dtype else cfg.kv_dtype
+    q_dtype = cfg.q_dtype if kv == pkv.FP8_E4M3 else kv
+    bs = args.block_size or cfg.block_size
+    L = args.layers or min(cfg.num_layers, 4)
+    S, H, Hkv, D = cfg.num_seqs, cfg.num_heads, cfg.num_kv_heads, cfg.head_dim
+    ctx = tabs.context_lens.astype(np.int64)
+    nb = tabs.num_blocks
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    # the block manager owns the pool: one sequence per row, blocks as allocated
+    bm = pkv.BlockManager(nb, bs)
+    for s in range(S):
+        bm.add_sequence(s, [0] * int(ctx[s]))
+    r = np.random.default_rng(args.seed + 5)
+    for s in range(S):
+        keep = r.random(int(ctx[s])) < args.keep
+        keep[-1] = True
+        bm.evict_tokens(s, keep.tolist())
+    width = int(ctx.max())
+    n_keep = np.array([bm.num_tokens(s) for s in range(S)], np.int64)
+    slots = torch.tensor([bm.token_slots(s, width) for s in range(S)], dtype=torch.int32, device=dev)
+    cl = torch.from_numpy(n_keep.astype(np.int32)).to(dev)
+    pool_bytes = pkv.layer_pool_bytes(nb, Hkv, D, bs, kv)
+    fp8_scale = float(np.float32(8.0 / 448.0))
+    ks = vs = fp8_scale if kv == pkv.FP8_E4M3 else 1.0
+    kpools = [torch.empty(pool_bytes, dtype=torch.uint8, device=dev) for _ in range(L)]
+    vpools = [torch.empty(pool_bytes, dtype=torch.uint8, device=dev) for _ in range(L)]
+    for i in range(L):
+        workloads.device_fill_normal(kpools[i], kv, 1000 + i, scale=fp8_scale)
+        workloads.device_fill_normal(vpools[i], kv, 2000 + i, scale=fp8_scale)
+    tq = torch.bfloat16 if q_dtype == pkv.BF16 else torch.float16
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(args.seed + 9)
+    qs = [torch.randn(S, H, D, generator=gen, device=dev).to(tq) for _ in range(L)]
+    outs = [torch.empty(S, H, D, dtype=tq, device=dev) for _ in range(L)]
+    scale = float(np.float32(1.0 / np.sqrt(D)))
+    stream = torch.cuda.current_stream()
+    b_kv = 1 if kv == pkv.FP8_E4M3 else 2
+    dec_bytes = int(n_keep.sum()) * 2 * Hkv * D * b_kv + S * H * D * 4
+
+    def timed(fn, reps):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    def frag_step():
+        for l in range(L):
+            pkv.paged_attention_decode_tokens(outs[l], qs[l], kpools[l], vpools[l], slots, cl, Hkv, bs,
+                                              nb, kv, scale, ks, vs, stream=stream)
+    frag_ms = timed(frag_step, args.steps) / L
+    moves = []
+    for s in range(S):
+        moves += bm.repack(s)
+    mv = torch.tensor(moves, dtype=torch.int32, device=dev).reshape(-1, 2)
+    need = pkv.lib().pkv_move_tokens_scratch_bytes(L, mv.shape[0], Hkv, D, kv)
+    scratch = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    # repeated for timing (the values the synthetic pools end up with do
+    # not matter here; the decode below only needs the same bytes moved)
+    move_ms = timed(lambda: pkv.move_tokens(kpools, vpools, mv, nb, Hkv, D, bs, kv,
+                                            scratch=scratch, stream=stream), max(1, args.steps // 2))
+    move_bytes = mv.shape[0] * L * 2 * Hkv * D * b_kv * 2
+    mb = -(-width // bs)
+    bt = torch.tensor([bm.block_table(s, mb) for s in range(S)], dtype=torch.int32, device=dev)
+    mc = int(n_keep.max())
+
+    def block_step():
+        for l in range(L):
+            pkv.paged_attention_decode(outs[l], qs[l], kpools[l], vpools[l], bt, cl, mc, Hkv, bs, kv,
+                                       scale, ks, vs, num_blocks=nb, stream=stream)
+    block_ms = timed(block_step, args.steps) / L
+    frag_gbs = dec_bytes / (frag_ms * 1e-3) / 1e9
+    block_gbs = dec_bytes / (block_ms * 1e-3) / 1e9
+    move_gbs = move_bytes / (move_ms * 1e-3) / 1e9
+    print(f"[bench] vtoken: keep {args.keep:.2f} ({int(n_keep.sum())} of {int(ctx.sum())} tokens); "
+          f"fragmented-table decode {frag_ms * 1e3:.1f} us/layer ({frag_gbs:.0f} GB/s), repack "
+          f"{mv.shape[0]} moves x {L} layers {move_ms * 1e3:.1f} us ({move_gbs:.0f} GB/s), "
+          f"block decode after {block_ms * 1e3:.1f} us/layer ({block_gbs:.0f} GB/s)",
+          file=sys.stderr, flush=True)
+    dt_name = {pkv.BF16: "bf16", pkv.FP16: "fp16", pkv.FP8_E4M3: "fp8"}
+    print(json.dumps({
+        "metric": "token-table decode HBM GB/s (surviving K/V + q/out)",
+        "value": round(frag_gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(frag_ms * L, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": dt_name[kv] if kv == pkv.FP8_E4M3 else dt_name[q_dtype], "data": "synthetic",
+        "config": {"workload": f"{cfg.description.split(':')[0]}: each sequence keeps a random "
+                               f"{args.keep:.0%} of its context, {L} layers",
+                   "keep": args.keep, "layers": L, "num_seqs": S, "parallelism": "single GPU"},
+        "repack": {"moves": int(mv.shape[0]), "us": round(move_ms * 1e3, 1),
+                   "gbs_read_plus_write": round(move_gbs, 1)},
+        "after_repack_block_decode": {"us_per_layer": round(block_ms * 1e3, 1),
+                                      "gbs": round(block_gbs, 1)},
+        "roofline": {"bound": "hbm", "kernel": "paged_decode_tokens_kernel",
+                     "achieved": round(frag_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(frag_gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                     "avg_launch_us": round(frag_ms * 1e3, 2),
+                     "algorithmic_bytes_per_launch": dec_bytes},
         "cpu_baseline": None,
     }), flush=True)
 
