@@ -104,9 +104,49 @@ void paged_prefill_mfma_kernel(const DecodeArgs a, const int32_t* __restrict__ q
         QueryTile{(int64_t)q0 + j0, min(tile_tokens, q_len - j0), q_len - j0});
 }
 
+// Wave-per-tile form for longer chunks: workgroup (sequence s, group of NW
+// query tiles, kv head); wave w takes tile NW*group + w and walks all of the
+// keys it sees alone (units in order), so the NW waves read the same K / V
+// units at about the same time and share them through the CU's L1 instead
+// of each tile fetching them from L2.  Each wave merges nothing but itself,
+// in its own LDS area.
+template <int KVT, int QT, int BS, int NW, int DEPTH>
+__global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(PKV_WAVES_PER_EU)))
+void paged_prefill_wave_kernel(const DecodeArgs a, const int32_t* __restrict__ query_start,
+                               int tile_tokens, int max_groups, int lds_per_wave) {
+    extern __shared__ float pkv_smem[];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int kvh = blockIdx.x % a.num_kv_heads;
+    const int rest = blockIdx.x / a.num_kv_heads;
+    const int grp = max_groups - 1 - rest / a.num_seqs;
+    const int s = rest % a.num_seqs;
+    const int q0 = query_start[s];
+    const int q_len = query_start[s + 1] - q0;
+    const int j0 = (grp * NW + w) * tile_tokens;
+    if (j0 >= q_len) return;
+    decode_entry<MfmaMath<KVT, QT>, KVT, QT, BS, 1, DEPTH>(
+        a, pkv_smem + w * lds_per_wave, s, 0, kvh, lane, 0,
+        QueryTile{(int64_t)q0 + j0, min(tile_tokens, q_len - j0), q_len - j0});
+}
+
+#ifndef PKV_PREFILL_DEPTH
+#define PKV_PREFILL_DEPTH 2
+#endif
+
 template <int KVT, int QT, int BS>
 static hipError_t launch_prefill_t(const DecodeArgs& a, const int32_t* query_start, int tile_tokens,
                                    int max_tiles, hipStream_t st) {
+    if (max_tiles > kWavesPerGroup) {
+        const int per_wave = merge_lds_floats(1, tile_tokens * a.group);
+        const int groups = (max_tiles + kWavesPerGroup - 1) / kWavesPerGroup;
+        const size_t lds = sizeof(float) * per_wave * kWavesPerGroup;
+        const dim3 grid((unsigned)((int64_t)a.num_seqs * groups * a.num_kv_heads));
+        hipLaunchKernelGGL((paged_prefill_wave_kernel<KVT, QT, BS, kWavesPerGroup, PKV_PREFILL_DEPTH>), grid,
+                           dim3(kWavesPerGroup * kWave), lds, st, a, query_start, tile_tokens, groups,
+                           per_wave);
+        return hipGetLastError();
+    }
     const size_t lds = sizeof(float) * merge_lds_floats(kWavesPerGroup, tile_tokens * a.group);
     const dim3 grid((unsigned)((int64_t)a.num_seqs * max_tiles * a.num_kv_heads));
     hipLaunchKernelGGL((paged_prefill_mfma_kernel<KVT, QT, BS, kWavesPerGroup, kDepth>), grid,

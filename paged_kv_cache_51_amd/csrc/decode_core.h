@@ -182,7 +182,9 @@ __device__ __forceinline__ void park_and_store(const DecodeArgs& a, float* pkv_s
 // Decode one work entry: kv head `kvh` of (sequence s, partition part) for
 // the query tile qt, by the NW waves of the calling workgroup.  Every exit
 // before the LDS counter barrier depends only on (s, part, qt), so all
-// waves of the workgroup take it together.
+// waves of the workgroup take it together.  With NW = 1 the calling wave
+// works alone (its own entry and its own LDS area, no workgroup barrier),
+// so the waves of one workgroup can run different entries.
 template <class Math, int KVT, int QT, int BS, int NW, int DEPTH>
 __device__ __forceinline__ void decode_entry(const DecodeArgs& a, float* pkv_smem, int s, int part,
                                              int kvh, int lane, int w, const QueryTile& qt) {
@@ -214,7 +216,7 @@ __device__ __forceinline__ void decode_entry(const DecodeArgs& a, float* pkv_sme
         if (part == 0) {
             // no key at all: zero output (empty context, or tokens placed
             // before the start of the context)
-            for (int e = threadIdx.x; e < ncols * kHeadDim; e += NW * kWave) {
+            for (int e = (NW == 1 ? lane : (int)threadIdx.x); e < ncols * kHeadDim; e += NW * kWave) {
                 const int c = e / kHeadDim;
                 uint16_t* out = reinterpret_cast<uint16_t*>(a.out) +
                                 ((qt.row0 + c / G) * a.num_heads + (int64_t)kvh * G + c % G) * kHeadDim;
@@ -230,9 +232,10 @@ __device__ __forceinline__ void decode_entry(const DecodeArgs& a, float* pkv_sme
     const int nblk = (kv_end + BS - 1) / BS;
     const bool single = nblk <= a.part_blocks;
     int* done = reinterpret_cast<int*>(pkv_smem);
-    if (threadIdx.x == 0) *done = 0;
-    mt.stage_q(pkv_smem + merge_lds_floats(NW, ncols), threadIdx.x);
-    __syncthreads();
+    const int ltid = NW == 1 ? lane : (int)threadIdx.x;
+    if (ltid == 0) *done = 0;
+    mt.stage_q(pkv_smem + merge_lds_floats(NW, ncols), ltid);
+    if constexpr (NW > 1) __syncthreads();
     mt.begin();
 
     const int n_my = first < u1 ? (u1 - first + NW - 1) / NW : 0;
