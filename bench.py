@@ -359,6 +359,14 @@ def bench_prefill(args, torch, pkv, workloads):
     print(f"[bench] prefill: {S} seqs x {qlen} new tokens, contexts {int(ctx.min())}-{int(ctx.max())}; "
           f"{launch_ms * 1e3:.1f} us per layer, {tflops:.1f} TFLOP/s, {gbs:.0f} GB/s; "
           f"intensity {flops / nbytes:.0f} flop/B", file=sys.stderr, flush=True)
+    cpu = None
+    if args.cpu_baseline_seconds > 0:
+        cpu = cpu_sample(args, "prefill", lambda n: _prefill_oracle_sample(
+            n, kpools[0], vpools[0], qs[0], bt_np, ctx, qlen, q_dtype, kv, Hkv, bs, scale, ks, vs),
+            lambda n: 4 * D * H * sum(int(ctx[0]) - qlen + j + 1 for j in range(qlen - n, qlen)),
+            "TFLOP/s", 1e12,
+            "layer 0, sequence 0: its last n new tokens (one-token chunks at their positions), "
+            "fp64 C oracle, OpenMP over (row, head)", min(qlen, 256))
     dt_name = {pkv.BF16: "bf16", pkv.FP16: "fp16", pkv.FP8_E4M3: "fp8"}
     print(json.dumps({
         "metric": "paged multi-token attention TFLOP/s" if mfma_bound
@@ -381,7 +389,7 @@ def bench_prefill(args, torch, pkv, workloads):
                      "frac": round((tflops / peak_tf) if mfma_bound else (gbs / PEAK_HBM_GBS), 4),
                      "traffic": None, "avg_launch_us": round(launch_ms * 1e3, 2),
                      "algorithmic_flops_per_launch": flops, "algorithmic_bytes_per_launch": nbytes},
-        "cpu_baseline": None,
+        "cpu_baseline": cpu,
     }), flush=True)
 
 
@@ -446,6 +454,15 @@ def bench_vtoken(args, torch, pkv, workloads):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / reps
 
+    cpu = None
+    if args.cpu_baseline_seconds > 0:
+        slots_np = slots.cpu().numpy()
+        cpu = cpu_sample(args, "vtoken", lambda n: _tokens_oracle_sample(
+            n, kpools[0], vpools[0], qs[0], slots_np, n_keep, q_dtype, kv, Hkv, bs, scale, ks, vs),
+            lambda n: int(n_keep[:n].sum()) * 2 * Hkv * D * b_kv + n * H * D * 4, "GB/s", 1e9,
+            "layer 0, first n sequences through the fragmented token table, fp64 C oracle, "
+            "OpenMP over (seq, head)", S)
+
     def frag_step():
         for l in range(L):
             pkv.paged_attention_decode_tokens(outs[l], qs[l], kpools[l], vpools[l], slots, cl, Hkv, bs,
@@ -498,7 +515,7 @@ def bench_vtoken(args, torch, pkv, workloads):
                      "frac": round(frag_gbs / PEAK_HBM_GBS, 4), "traffic": None,
                      "avg_launch_us": round(frag_ms * 1e3, 2),
                      "algorithmic_bytes_per_launch": dec_bytes},
-        "cpu_baseline": None,
+        "cpu_baseline": cpu,
     }), flush=True)
 
 
@@ -576,6 +593,61 @@ def bench_copy_blocks(args, torch, pkv, workloads):
                      "algorithmic_bytes_per_launch": nbytes},
         "cpu_baseline": cpu,
     }), flush=True)
+
+
+_PKV2ORC = {0: 0, 1: 1, 2: 2}      # library dtype codes -> oracle dtype codes (same values)
+
+
+def cpu_sample(args, what, run, work_of, unit, unit_scale, sample_desc, n_max):
+    """Time run(n) (the oracle on a sample of n units) with n grown until it
+    takes about --cpu-baseline-seconds; report work_of(n) / time."""
+    import oracle
+    run(1)                                       # pulls pools to the host, builds caches
+    t = time.time()
+    run(1)
+    t1 = max(time.time() - t, 1e-6)
+    n = int(min(n_max, max(1, args.cpu_baseline_seconds / t1)))
+    t = time.time()
+    run(n)
+    tn = time.time() - t
+    print(f"[bench] cpu oracle ({what}): n={n} in {tn:.1f}s on {oracle.max_threads()} threads",
+          file=sys.stderr, flush=True)
+    return {"value": round(work_of(n) / tn / unit_scale, 6), "unit": unit,
+            "cores": oracle.max_threads(), "kind": "oracle",
+            "sample": sample_desc.replace(" n ", f" {n} ").replace("first n", f"first {n}")
+                                 .replace("last n", f"last {n}"),
+            "seconds": round(tn, 2)}
+
+
+_HOST = {}
+
+
+def _host(t):
+    key = t.data_ptr()
+    if key not in _HOST:
+        _HOST[key] = t.cpu().numpy()
+    return _HOST[key]
+
+
+def _prefill_oracle_sample(n, kpool, vpool, q, bt, ctx, qlen, q_dtype, kv, Hkv, bs, scale, ks, vs):
+    import oracle
+    import torch
+    qb = q.cpu().view(torch.int16).numpy().view(np.uint16)
+    c0 = int(ctx[0])
+    rows = list(range(qlen - n, qlen))
+    sub_q = qb[rows]
+    sub_ctx = np.array([c0 - qlen + j + 1 for j in rows], np.int32)   # one-token chunks
+    sub_bt = np.repeat(bt[:1], len(rows), axis=0)
+    oracle.paged_prefill(sub_q, _PKV2ORC[q_dtype], _host(kpool), _host(vpool), _PKV2ORC[kv], sub_bt,
+                         sub_ctx, np.arange(len(rows) + 1, dtype=np.int32), Hkv, bs, scale, ks, vs)
+
+
+def _tokens_oracle_sample(n, kpool, vpool, q, slots, n_keep, q_dtype, kv, Hkv, bs, scale, ks, vs):
+    import oracle
+    import torch
+    qb = q[:n].cpu().view(torch.int16).numpy().view(np.uint16)
+    oracle.paged_decode_tokens(qb, _PKV2ORC[q_dtype], _host(kpool), _host(vpool), _PKV2ORC[kv],
+                               slots[:n], n_keep[:n].astype(np.int32), Hkv, bs, scale, ks, vs)
 
 
 def cpu_baseline(args, tabs, kpool, vpool, q, q_dtype, kv_dtype, Hkv, bs, scale, ks, vs, b_kv,

@@ -169,3 +169,44 @@ def test_evict_repack_move_then_block_decode_bitwise(kv):
     torch.cuda.synchronize()
     assert torch.isfinite(a.float()).all()
     assert torch.equal(a, b)
+
+
+def test_decode_tokens_full_size_sampled():
+    """The 7B decode workload (256 sequences, 1K-8K tokens) with every
+    sequence keeping a random 60 % of its context, through the token table
+    at full size; the oracle checks sampled sequences."""
+    c, tabs, _, _ = workloads.make("qwen7b")
+    S, H, Hkv, bs = c.num_seqs, c.num_heads, c.num_kv_heads, c.block_size
+    nb = tabs.num_blocks
+    log("token-table decode, 7B shape, full size")
+    nbytes = pkv.layer_pool_bytes(nb, Hkv, D, bs, oracle.BF16)
+    kd = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    vd = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    workloads.device_fill_normal(kd, oracle.BF16, 61)
+    workloads.device_fill_normal(vd, oracle.BF16, 62)
+    r = np.random.default_rng(63)
+    width = int(tabs.context_lens.max())
+    slots = np.zeros((S, width), np.int32)
+    ctx = np.zeros(S, np.int32)
+    for s in range(S):
+        cl = int(tabs.context_lens[s])
+        full = tabs.block_tables[s][np.arange(cl) // bs] * bs + np.arange(cl) % bs
+        keep = np.nonzero(r.random(cl) < 0.6)[0]
+        slots[s, :len(keep)] = full[keep]
+        ctx[s] = len(keep)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(64)
+    q = torch.randn(S, H, D, generator=g, device=DEV).to(torch.bfloat16)
+    out = torch.full_like(q, float("nan"))
+    pkv.paged_attention_decode_tokens(out, q, kd, vd, devi(slots), devi(ctx), Hkv, bs, nb,
+                                      oracle.BF16, SCALE)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy().astype(np.float64)
+    assert np.isfinite(got).all()
+    idx = sorted({int(np.argmax(ctx)), int(np.argmin(ctx)), 3, 77, 200})
+    qb = q.cpu().view(torch.int16).numpy().view(np.uint16)
+    want = oracle.paged_decode_tokens(qb[idx], oracle.BF16, kd.cpu().numpy(), vd.cpu().numpy(),
+                                      oracle.BF16, slots[idx], ctx[idx], Hkv, bs, SCALE)
+    err = np.abs(got[idx] - want).max()
+    log(f"  sampled {len(idx)} seqs: max-abs {err:.3e}")
+    assert err <= TOL[oracle.BF16]
