@@ -108,10 +108,16 @@ void paged_prefill_mfma_kernel(const DecodeArgs a, const int32_t* __restrict__ q
 // query tiles, kv head); wave w takes tile NW*group + w and walks all of the
 // keys it sees alone (units in order), so the NW waves read the same K / V
 // units at about the same time and share them through the CU's L1 instead
-// of each tile fetching them from L2.  Each wave merges nothing but itself,
-// in its own LDS area.
+// of each tile fetching them from L2.  A tile here holds 32 / G tokens (two
+// 16-column MFMA tiles sharing each unit's K / V fragments).  Each wave
+// merges nothing but itself, in its own LDS area.
+#ifndef PKV_PREFILL_WAVES_PER_EU
+#define PKV_PREFILL_WAVES_PER_EU 2
+#endif
+
+// (two waves per SIMD: the register budget is kept at 256 per lane)
 template <int KVT, int QT, int BS, int NW, int DEPTH>
-__global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(PKV_WAVES_PER_EU)))
+__global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(PKV_PREFILL_WAVES_PER_EU)))
 void paged_prefill_wave_kernel(const DecodeArgs a, const int32_t* __restrict__ query_start,
                                int tile_tokens, int max_groups, int lds_per_wave) {
     extern __shared__ float pkv_smem[];
@@ -125,7 +131,7 @@ void paged_prefill_wave_kernel(const DecodeArgs a, const int32_t* __restrict__ q
     const int q_len = query_start[s + 1] - q0;
     const int j0 = (grp * NW + w) * tile_tokens;
     if (j0 >= q_len) return;
-    decode_entry<MfmaMath<KVT, QT>, KVT, QT, BS, 1, DEPTH>(
+    decode_entry<MfmaMath<KVT, QT, 2>, KVT, QT, BS, 1, DEPTH>(
         a, pkv_smem + w * lds_per_wave, s, 0, kvh, lane, 0,
         QueryTile{(int64_t)q0 + j0, min(tile_tokens, q_len - j0), q_len - j0});
 }
@@ -138,12 +144,15 @@ template <int KVT, int QT, int BS>
 static hipError_t launch_prefill_t(const DecodeArgs& a, const int32_t* query_start, int tile_tokens,
                                    int max_tiles, hipStream_t st) {
     if (max_tiles > kWavesPerGroup) {
-        const int per_wave = merge_lds_floats(1, tile_tokens * a.group);
-        const int groups = (max_tiles + kWavesPerGroup - 1) / kWavesPerGroup;
+        // two 16-column tiles per wave
+        const int tt = 2 * tile_tokens;
+        const int wave_tiles = (max_tiles * tile_tokens + tt - 1) / tt;
+        const int per_wave = merge_lds_floats(1, tt * a.group, 32);
+        const int groups = (wave_tiles + kWavesPerGroup - 1) / kWavesPerGroup;
         const size_t lds = sizeof(float) * per_wave * kWavesPerGroup;
         const dim3 grid((unsigned)((int64_t)a.num_seqs * groups * a.num_kv_heads));
         hipLaunchKernelGGL((paged_prefill_wave_kernel<KVT, QT, BS, kWavesPerGroup, PKV_PREFILL_DEPTH>), grid,
-                           dim3(kWavesPerGroup * kWave), lds, st, a, query_start, tile_tokens, groups,
+                           dim3(kWavesPerGroup * kWave), lds, st, a, query_start, tt, groups,
                            per_wave);
         return hipGetLastError();
     }

@@ -64,7 +64,12 @@ constexpr int kMergeRow = kHeadDim + 4;
 // Plan header ints before the item list: [count][next entry][done][reserved].
 constexpr int kPlanHeader = 4;
 
-__host__ __device__ constexpr int merge_lds_floats(int nw, int ncols) { return 4 + 32 * nw + nw * ncols * kMergeRow; }
+// Merge area of NW waves: [counters 4][m: NW x kcols][l: NW x kcols]
+// [partial outputs: NW x ncols rows of kMergeRow floats]; kcols = the
+// policy's column capacity (16 per tile).
+__host__ __device__ constexpr int merge_lds_floats(int nw, int ncols, int kcols = 16) {
+    return 4 + 2 * nw * kcols + nw * ncols * kMergeRow;
+}
 
 // The query side of a work entry: ntok consecutive query tokens of one
 // sequence (1 for decode), stored at rows row0 .. row0 + ntok - 1 of q /
@@ -116,10 +121,11 @@ __device__ __forceinline__ void park_and_store(const DecodeArgs& a, float* pkv_s
                                                int part, int kvh, int lane, int w,
                                                const QueryTile& qt, int ncols, bool single) {
     const int G = a.group;
+    constexpr int KC = Math::kCols;
     int* done = reinterpret_cast<int*>(pkv_smem);   // zeroed before the workgroup barrier
     float* sm_m = pkv_smem + 4;
-    float* sm_l = sm_m + NW * 16;
-    float* sm_acc = sm_l + NW * 16;
+    float* sm_l = sm_m + NW * KC;
+    float* sm_acc = sm_l + NW * KC;
     mt.park(sm_m, sm_l, sm_acc, w, ncols, lane);
     __threadfence_block();
     int prev = 0;
@@ -131,14 +137,14 @@ __device__ __forceinline__ void park_and_store(const DecodeArgs& a, float* pkv_s
     for (int c = 0; c < ncols; ++c) {
         float M = -INFINITY;
 #pragma unroll
-        for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, sm_m[ww * 16 + c]);
+        for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, sm_m[ww * KC + c]);
         float L = 0.f, o0 = 0.f, o1 = 0.f;
 #pragma unroll
         for (int ww = 0; ww < NW; ++ww) {
-            const float mw = sm_m[ww * 16 + c];
+            const float mw = sm_m[ww * KC + c];
             const float f = (mw == -INFINITY) ? 0.f : fast_exp2(mw - M);
             const float2 ov = *reinterpret_cast<const float2*>(sm_acc + (ww * ncols + c) * kMergeRow + 2 * lane);
-            L += f * sm_l[ww * 16 + c];
+            L += f * sm_l[ww * KC + c];
             o0 += f * ov.x;
             o1 += f * ov.y;
         }
@@ -167,11 +173,11 @@ __device__ __forceinline__ void park_and_store(const DecodeArgs& a, float* pkv_s
         float M = -INFINITY, L = 0.f;
         if (h < G) {
 #pragma unroll
-            for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, sm_m[ww * 16 + h]);
+            for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, sm_m[ww * KC + h]);
 #pragma unroll
             for (int ww = 0; ww < NW; ++ww) {
-                const float mw = sm_m[ww * 16 + h];
-                L += ((mw == -INFINITY) ? 0.f : fast_exp2(mw - M)) * sm_l[ww * 16 + h];
+                const float mw = sm_m[ww * KC + h];
+                L += ((mw == -INFINITY) ? 0.f : fast_exp2(mw - M)) * sm_l[ww * KC + h];
             }
         }
         const int64_t rec = ((int64_t)s * a.num_kv_heads + kvh) * a.num_parts + part;
@@ -234,7 +240,7 @@ __device__ __forceinline__ void decode_entry(const DecodeArgs& a, float* pkv_sme
     int* done = reinterpret_cast<int*>(pkv_smem);
     const int ltid = NW == 1 ? lane : (int)threadIdx.x;
     if (ltid == 0) *done = 0;
-    mt.stage_q(pkv_smem + merge_lds_floats(NW, ncols), ltid);
+    mt.stage_q(pkv_smem + merge_lds_floats(NW, ncols, Math::kCols), ltid);
     if constexpr (NW > 1) __syncthreads();
     mt.begin();
 

@@ -19,6 +19,7 @@ namespace pkv {
 template <int KVT, int QT>
 struct VectorMath {
     static constexpr int kMaxGroup = 8;
+    static constexpr int kCols = 16;
     __host__ __device__ static constexpr int query_lds_floats(int g) { return g * kHeadDim / 2; }
 
     float acc[kMaxGroup][8];  // dim 16nt + (lane & 15), over this row's tokens
