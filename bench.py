@@ -382,7 +382,7 @@ def bench_prefill(args, torch, pkv, workloads):
                    "num_kv_heads": Hkv, "kv_dtype": dt_name[kv], "block_size": bs,
                    "parallelism": "single GPU"},
         "tflops": round(tflops, 2), "gbs": round(gbs, 1),
-        "roofline": {"bound": "mfma" if mfma_bound else "hbm", "kernel": "paged_prefill_wave_kernel" if -(-qlen // (16 // (H // Hkv))) > 4 else "paged_prefill_mfma_kernel",
+        "roofline": {"bound": "mfma" if mfma_bound else "hbm", "kernel": "paged_prefill_staged_kernel" if -(-qlen // (16 // (H // Hkv))) > 4 else "paged_prefill_mfma_kernel",
                      "achieved": round(tflops if mfma_bound else gbs, 2),
                      "peak": peak_tf if mfma_bound else PEAK_HBM_GBS,
                      "unit": "TFLOP/s" if mfma_bound else "GB/s",

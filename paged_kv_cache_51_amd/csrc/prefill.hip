@@ -13,9 +13,10 @@
 
 namespace pkv {
 
-// Multi-token form: workgroup (sequence s, query tile, kv head) attends the
-// tile's tokens to the paged context, causally: token j of a chunk of
-// q_len new tokens sits at position ctx - q_len + j and sees keys up to it.
+// Workgroup form (chunks of at most four 16-column tiles): workgroup
+// (sequence s, query tile, kv head) attends the tile's tokens to the paged
+// context, causally: token j of a chunk of q_len new tokens sits at position
+// ctx - q_len + j and sees keys up to it.  The decode entry body serves it.
 // Tiles hold tile_tokens = 16 / G tokens (so the tile's (token, head) pairs
 // fill the 16 MFMA columns), and the last tiles of a chunk, which see the
 // most keys, are dispatched first.  No context split: the tiles give the
@@ -40,23 +41,199 @@ void paged_prefill_mfma_kernel(const DecodeArgs a, const int32_t* __restrict__ q
         QueryTile{(int64_t)q0 + j0, min(tile_tokens, q_len - j0), q_len - j0});
 }
 
-// Wave-per-tile form for longer chunks: workgroup (sequence s, group of NW
-// query tiles, kv head); wave w takes tile NW*group + w and walks all of the
-// keys it sees alone (units in order), so the NW waves read the same K / V
-// units at about the same time and share them through the CU's L1 instead
-// of each tile fetching them from L2.  A tile here holds 32 / G tokens (two
-// 16-column MFMA tiles sharing each unit's K / V fragments).  Each wave
-// merges nothing but itself, in its own LDS area.
+// Max over the four 16-lane rows of the wave, the result in every lane.
+// permlane16_swap(v, v) returns rows (0, 0, 2, 2) and (1, 1, 3, 3) of v;
+// permlane32_swap(x, x) returns rows (0, 1, 0, 1) and (2, 3, 2, 3) of x.
+// (Every operation here is visible to the compiler: it must place the wait
+// states between a matrix-core result and the vector instructions reading
+// it, which it cannot do for inline assembly.)
+__device__ __forceinline__ float rows_max(float v) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    const float x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// Two fp32 values -> a packed pair of the query type (RNE), low first.
+template <int QT>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    const f32x2_t v = {lo, hi};
+    if constexpr (QT == DT_BF16) return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+    else return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
+}
+
+// 1.0 in both halves of a packed pair of the query type.
+template <int QT>
+__device__ __forceinline__ constexpr uint32_t ones2() {
+    return QT == DT_BF16 ? 0x3f803f80u : 0x3c003c00u;
+}
+
+// ---------------------------------------------------------------------------
+// Staged form, for chunks of more than four 16-column tiles.  Workgroup =
+// (sequence, four consecutive 32-column query tiles, kv head): wave w owns
+// tile w (32 / G tokens, two 16-column MFMA tiles) and the four waves walk
+// the keys together, two 16-token units ("a pair") at a time, sharing every
+// K / V byte through LDS (reading the units into each wave separately
+// moves four times the bytes through the L1 return path, which then bounds
+// the kernel: 405 against 463 TFLOP/s on 16 x 512-token chunks).
+//   - wave w fetches one quarter of each pair (K of unit A / K of unit B /
+//     V of A / V of B for w = 0..3), 16 bytes per lane per 1 KiB pool row,
+//     two pairs ahead in registers, and writes it to one of two LDS stages:
+//     K rows as in the pool, V straight in PV operand order (entry [nt][lane]
+//     = the unit A then unit B halves of dim tile nt); one workgroup barrier
+//     per pair;
+//   - PV runs on 16x16x32 MFMAs whose 32-long contraction covers both units
+//     (16x16x16 runs at half the matrix rate on gfx950): lane group
+//     g = lane >> 4 contributes tokens 4g..4g+3 of unit A and of unit B to
+//     its eight k slots, in V (A operand) and P (B operand) alike;
+//   - pairs that every real column of the wave sees in full (all but the
+//     last one or two on the diagonal) skip the per-key causal and context
+//     masks; the logit scale is folded into the exponent (p = 2^(s*cs - m),
+//     the running max kept on scaled values); row maxima are reduced over
+//     the four 16-lane rows with the gfx950 permlane swaps (VALU, no LDS
+//     round trip); the normaliser is summed from the rounded weights with
+//     packed dot instructions;
+//   - waves whose tile sees fewer keys, or that have no tile, keep fetching
+//     and meeting the barriers; a wave's result needs no merge: it
+//     normalises its columns in registers and writes them out.
+// Same arithmetic as decode otherwise: fp32 logits, log2-domain online
+// softmax with the lazy rescale, weights rounded to the query type.
+
+// LDS bytes of one stage: K [2 units][R rows][64 lanes] x 16 B, V 8 dim
+// tiles x 64 lanes x 16 B (16-bit pools) or [2][R][64] x 16 B raw (fp8).
+__host__ __device__ constexpr int stage_bytes(int kvt) {
+    return 2 * rows_per_sub(kvt) * 1024 + (kvt == DT_FP8 ? 2 * rows_per_sub(kvt) * 1024 : 8 * 1024);
+}
+
+// One unit pair of a stage: logits, online softmax and PV for the wave's two
+// column tiles.
+template <int KVT, int QT, bool MASKED>
+__device__ __forceinline__ void staged_pair(MfmaMath<KVT, QT, 2>& mt, const uint8_t* stage, int tok0,
+                                            int ctx, float cs, int lane) {
+    constexpr int R = rows_per_sub(KVT);
+    const u32x4_t* kl = reinterpret_cast<const u32x4_t*>(stage) + lane;
+    const u32x4_t* vl = reinterpret_cast<const u32x4_t*>(stage + 2 * R * 1024) + lane;
+    // logits
+    f32x4_t st[2][2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) st[u][t] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+        u32x4_t k[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            if constexpr (KVT == DT_FP8) {
+                const u32x4_t row = kl[(u * R + (kk >> 1)) * kWave];
+                k[u] = (kk & 1) ? e4m3x8_to_16<QT>(row[2], row[3]) : e4m3x8_to_16<QT>(row[0], row[1]);
+            } else {
+                k[u] = kl[(u * R + kk) * kWave];
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            st[0][t] = mfma_16x16x32<QT>(k[0], mt.qf[t][kk], st[0][t]);
+            st[1][t] = mfma_16x16x32<QT>(k[1], mt.qf[t][kk], st[1][t]);
+        }
+    }
+    // softmax
+    const int ta = tok0 + 4 * (lane >> 4);
+    bool valid[2][2][4];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) valid[u][t][i] = !MASKED || (ta + 16 * u + i) < mt.lim[t];
+    // scaled logits (log2 units); keys a column must not see get -inf
+    float y[2][8], bm[2];
+    bool jump = false;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) y[t][4 * u + i] = valid[u][t][i] ? st[u][t][i] * cs : -INFINITY;
+        const float mx = fmaxf(fmaxf(fmaxf(y[t][0], y[t][1]), fmaxf(y[t][2], y[t][3])),
+                               fmaxf(fmaxf(y[t][4], y[t][5]), fmaxf(y[t][6], y[t][7])));
+        bm[t] = rows_max(mx);
+        jump |= bm[t] > mt.m[t] + kRescaleSlack;
+    }
+    if (__builtin_amdgcn_ballot_w64(jump)) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const float mn = fmaxf(mt.m[t], bm[t]);
+            const float alpha = (mt.m[t] == -INFINITY) ? 0.f : fast_exp2(mt.m[t] - mn);
+            mt.l[t] *= alpha;
+#pragma unroll
+            for (int nt = 0; nt < 8; ++nt) mt.acc[t][nt] *= alpha;
+            mt.m[t] = mn;
+        }
+    }
+    u32x4_t pf[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        float pv[8];
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float e = fast_exp2(y[t][4 * u + i] - mt.m[t]);
+                pv[4 * u + i] = valid[u][t][i] ? e : 0.f;
+            }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) pf[t][j] = pack2<QT>(pv[2 * j], pv[2 * j + 1]);
+        float lt = mt.l[t];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) lt = dot2<QT>(pf[t][j], ones2<QT>(), lt);
+        mt.l[t] = lt;
+    }
+    // PV
+    u32x4_t vm = {0u, 0u, 0u, 0u};
+    if constexpr (MASKED) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int tb = ta + 16 * u;
+            vm[2 * u] = (tb + 0 < ctx ? 0x0000ffffu : 0u) | (tb + 1 < ctx ? 0xffff0000u : 0u);
+            vm[2 * u + 1] = (tb + 2 < ctx ? 0x0000ffffu : 0u) | (tb + 3 < ctx ? 0xffff0000u : 0u);
+        }
+    }
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) {
+        u32x4_t vv;
+        if constexpr (KVT == DT_FP8) {
+            const u32x2_t x = e4m3x4_to_16<QT>(vl[(nt >> 2) * kWave][nt & 3]);
+            const u32x2_t y = e4m3x4_to_16<QT>(vl[(R + (nt >> 2)) * kWave][nt & 3]);
+            vv = (u32x4_t){x[0], x[1], y[0], y[1]};
+        } else {
+            vv = vl[nt * kWave];
+        }
+        if constexpr (MASKED) vv &= vm;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) mt.acc[t][nt] = mfma_16x16x32<QT>(vv, pf[t], mt.acc[t][nt]);
+    }
+}
+
+// (two waves per SIMD: the register budget is kept at 256 per lane)
 #ifndef PKV_PREFILL_WAVES_PER_EU
 #define PKV_PREFILL_WAVES_PER_EU 2
 #endif
 
-// (two waves per SIMD: the register budget is kept at 256 per lane)
-template <int KVT, int QT, int BS, int NW, int DEPTH>
+template <int KVT, int QT, int BS, int NW>
 __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(PKV_PREFILL_WAVES_PER_EU)))
-void paged_prefill_wave_kernel(const DecodeArgs a, const int32_t* __restrict__ query_start,
-                               int tile_tokens, int max_groups, int lds_per_wave) {
+void paged_prefill_staged_kernel(const DecodeArgs a, const int32_t* __restrict__ query_start,
+                                 int tile_tokens, int max_groups) {
+    static_assert(NW == 4, "one pool-row quarter of a unit pair per wave");
+    constexpr int NSUB = BS / kSubTokens;
+    constexpr int R = rows_per_sub(KVT);
+    constexpr int64_t SUB = sub_tile_bytes(KVT);
+    constexpr int64_t TILE = SUB * NSUB;
+    constexpr int SB = stage_bytes(KVT);
+    using Math = MfmaMath<KVT, QT, 2>;
     extern __shared__ float pkv_smem[];
+    uint8_t* stages = reinterpret_cast<uint8_t*>(pkv_smem);
     const int lane = threadIdx.x & (kWave - 1);
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int kvh = blockIdx.x % a.num_kv_heads;
@@ -65,31 +242,146 @@ void paged_prefill_wave_kernel(const DecodeArgs a, const int32_t* __restrict__ q
     const int s = rest % a.num_seqs;
     const int q0 = query_start[s];
     const int q_len = query_start[s + 1] - q0;
-    const int j0 = (grp * NW + w) * tile_tokens;
-    if (j0 >= q_len) return;
-    decode_entry<MfmaMath<KVT, QT, 2>, KVT, QT, BS, 1, DEPTH>(
-        a, pkv_smem + w * lds_per_wave, s, 0, kvh, lane, 0,
-        QueryTile{(int64_t)q0 + j0, min(tile_tokens, q_len - j0), q_len - j0});
-}
+    const int g0 = grp * NW * tile_tokens;           // the workgroup's first token
+    if (g0 >= q_len) return;                         // (whole workgroup)
+    const int G = a.group;
+    int ctx = a.context_lens[s];
+    ctx = ctx < a.ctx_cap ? ctx : a.ctx_cap;
+    // keys of the workgroup: up to its last token
+    const int kv_end_g = min(ctx, ctx - q_len + min(q_len, g0 + NW * tile_tokens));
 
-#ifndef PKV_PREFILL_DEPTH
-#define PKV_PREFILL_DEPTH 2
-#endif
+    // this wave's tile (it may have none)
+    const int j0 = g0 + w * tile_tokens;
+    const bool has_tile = j0 < q_len;
+    const QueryTile qt{(int64_t)q0 + j0, has_tile ? min(tile_tokens, q_len - j0) : 0, q_len - j0};
+    Math mt;
+    if (has_tile) mt.load_q(a, qt, kvh, lane);
+    const int pos0 = ctx - qt.back;
+    const int kv_end = has_tile ? min(ctx, pos0 + qt.ntok) : 0;
+    mt.limit(pos0, G, lane);
+    mt.begin();
+    const int n_pairs_w = kv_end > 0 ? (kv_end + 2 * kSubTokens - 1) / (2 * kSubTokens) : 0;
+    const int n_free = pos0 + 1 >= kSubTokens ? (pos0 + 1) / kSubTokens : 0;
+
+    if (kv_end_g > 0) {
+        const int n_units = (kv_end_g + kSubTokens - 1) / kSubTokens;
+        const int n_pairs = (n_units + 1) / 2;
+        const int32_t* bt_row = a.block_tables + (int64_t)s * a.max_blocks;
+        // wave w fetches K (w < 2) or V (w >= 2) rows of unit A (w even) or B
+        const uint8_t* pool = ((w >> 1) ? a.v_cache : a.k_cache) + (int64_t)kvh * TILE;
+        const int64_t head_stride = (int64_t)a.num_kv_heads * TILE;
+        // unit fetched by this wave for pair p (indices past the last pair
+        // repeat it; a missing second unit repeats the last unit)
+        auto unit_of = [&](int p) { return min(2 * min(p, n_pairs - 1) + (w & 1), n_units - 1); };
+        auto fetch_at = [&](u32x4_t (&r)[R], int p, int pb) {
+            if (a.num_blocks > 0 && (unsigned)pb >= (unsigned)a.num_blocks) pb = 0;
+            const int u = unit_of(p);
+            const u32x4_t* g = reinterpret_cast<const u32x4_t*>(pool + (int64_t)pb * head_stride + (u % NSUB) * SUB) + lane;
+#pragma unroll
+            for (int i = 0; i < R; ++i) r[i] = g[kWave * i];
+        };
+        auto fetch = [&](u32x4_t (&r)[R], int p) { fetch_at(r, p, bt_row[unit_of(p) / NSUB]); };
+        // block id of pair p as a vector load issued two fetches ahead (a
+        // scalar load would be waited for at once, next to its use)
+        auto id_load = [&](int p) {
+            int z = 0;
+            asm volatile("" : "+v"(z));
+            return bt_row[unit_of(p) / NSUB + z];
+        };
+        // store this wave's quarter of a pair into a stage
+        auto stage_write = [&](const u32x4_t (&r)[R], int st) {
+            uint8_t* base = stages + st * SB;
+            if (w < 2 || KVT == DT_FP8) {
+                // K (or fp8 V) rows as in the pool: [unit][row][lane]
+                u32x4_t* d = reinterpret_cast<u32x4_t*>(base + (w >> 1) * 2 * R * 1024 + (w & 1) * R * 1024) + lane;
+#pragma unroll
+                for (int i = 0; i < R; ++i) d[kWave * i] = r[i];
+            } else {
+                // 16-bit V: row i holds dim tiles 2i (dwords 0, 1) and 2i+1
+                // (dwords 2, 3); unit A fills the low halves, B the high
+                u32x2_t* d = reinterpret_cast<u32x2_t*>(base + 2 * R * 1024) + 2 * lane + (w & 1);
+#pragma unroll
+                for (int i = 0; i < R; ++i) {
+                    d[2 * kWave * (2 * i)] = (u32x2_t){r[i][0], r[i][1]};
+                    d[2 * kWave * (2 * i + 1)] = (u32x2_t){r[i][2], r[i][3]};
+                }
+            }
+        };
+        const float cs = a.qk_scale_log2;
+        auto compute = [&](int p, int st) {
+            if (p < n_pairs_w) {
+                const uint8_t* base = stages + st * SB;
+                if (2 * p + 2 <= n_free)
+                    staged_pair<KVT, QT, false>(mt, base, 2 * p * kSubTokens, ctx, cs, lane);
+                else
+                    staged_pair<KVT, QT, true>(mt, base, 2 * p * kSubTokens, ctx, cs, lane);
+            }
+        };
+
+        u32x4_t r0[R], r1[R];
+        fetch(r0, 0);
+        fetch(r1, 1);
+        int id3 = id_load(3), id4 = id_load(4);
+        stage_write(r0, 0);
+        fetch(r0, 2);
+        __syncthreads();
+        // Fetches, stage writes and barriers are unconditional (indices past
+        // the last pair repeat it; compute skips pairs the wave does not
+        // see), so the load counters the compiler waits on stay static: a
+        // stage write waits only for its own pair, not for the one behind.
+        for (int p = 0; p < n_pairs; p += 2) {
+            compute(p, 0);
+            stage_write(r1, 1);       // pair p + 1
+            fetch_at(r1, p + 3, __builtin_amdgcn_readfirstlane(id3));
+            id3 = id_load(p + 5);
+            __syncthreads();
+            compute(p + 1, 1);
+            stage_write(r0, 0);       // pair p + 2
+            fetch_at(r0, p + 4, __builtin_amdgcn_readfirstlane(id4));
+            id4 = id_load(p + 6);
+            __syncthreads();
+        }
+    }
+    if (!has_tile) return;
+    // normalise and store this wave's columns (column 16t + (lane & 15) of
+    // tile t; lane group g holds dims 16nt + 4g .. +3)
+    const int g = lane >> 4;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        float L = mt.l[t];
+        {
+            const auto a16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(L), __float_as_uint(L), false, false);
+            const float x = __uint_as_float(a16[0]) + __uint_as_float(a16[1]);
+            const auto a32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+            L = __uint_as_float(a32[0]) + __uint_as_float(a32[1]);
+        }
+        if (!mt.cvalid[t]) continue;
+        // L = 0 only for a token placed before the start of the context
+        const float sc = (L > 0.f ? 1.0f / L : 0.f) * a.out_scale;
+        const int c = 16 * t + (lane & 15);
+        uint16_t* out = reinterpret_cast<uint16_t*>(a.out) +
+                        ((qt.row0 + c / G) * a.num_heads + (int64_t)kvh * G + c % G) * kHeadDim + 4 * g;
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) {
+            const f32x4_t o = mt.acc[t][nt];
+            const u32x2_t v = {pack2<QT>(o[0] * sc, o[1] * sc), pack2<QT>(o[2] * sc, o[3] * sc)};
+            *reinterpret_cast<u32x2_t*>(out + 16 * nt) = v;
+        }
+    }
+}
 
 template <int KVT, int QT, int BS>
 static hipError_t launch_prefill_t(const DecodeArgs& a, const int32_t* query_start, int tile_tokens,
                                    int max_tiles, hipStream_t st) {
     if (max_tiles > kWavesPerGroup) {
-        // two 16-column tiles per wave
+        // staged form: 32 columns (two 16-column tiles) per wave
         const int tt = 2 * tile_tokens;
         const int wave_tiles = (max_tiles * tile_tokens + tt - 1) / tt;
-        const int per_wave = merge_lds_floats(1, tt * a.group, 32);
         const int groups = (wave_tiles + kWavesPerGroup - 1) / kWavesPerGroup;
-        const size_t lds = sizeof(float) * per_wave * kWavesPerGroup;
         const dim3 grid((unsigned)((int64_t)a.num_seqs * groups * a.num_kv_heads));
-        hipLaunchKernelGGL((paged_prefill_wave_kernel<KVT, QT, BS, kWavesPerGroup, PKV_PREFILL_DEPTH>), grid,
-                           dim3(kWavesPerGroup * kWave), lds, st, a, query_start, tt, groups,
-                           per_wave);
+        hipLaunchKernelGGL((paged_prefill_staged_kernel<KVT, QT, BS, kWavesPerGroup>), grid,
+                           dim3(kWavesPerGroup * kWave), 2 * stage_bytes(KVT), st, a, query_start, tt,
+                           groups);
         return hipGetLastError();
     }
     const size_t lds = sizeof(float) * merge_lds_floats(kWavesPerGroup, tile_tokens * a.group);

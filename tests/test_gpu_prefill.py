@@ -94,6 +94,50 @@ def test_prefill_tokens_before_context_start_are_zero():
     check(got, want, oracle.BF16, "early tokens")
 
 
+def test_prefill_staged_form_tokens_before_context_start_are_zero():
+    """More than 4 query tiles (the staged kernel), with a chunk
+    longer than its sequence's context."""
+    lengths = [3, 40]
+    q_lens = [40, 30]                              # seq 0: 37 tokens precede its context
+    tabs, kp, vp, qs, q = case(lengths, q_lens, 8, 2, 16, oracle.BF16, oracle.BF16, seed=4)
+    got = gpu_prefill(tabs, kp, vp, qs, q, oracle.BF16, oracle.BF16, 2, 16)
+    want = oracle.paged_prefill(q, oracle.BF16, kp, vp, oracle.BF16, tabs.block_tables,
+                                tabs.context_lens, qs, 2, 16, SCALE)
+    assert np.array_equal(got[:37], np.zeros((37, 8, D)))
+    check(got, want, oracle.BF16, "early tokens, staged form")
+
+
+@pytest.mark.parametrize("kv,qdt,bs", [(oracle.BF16, oracle.BF16, 16), (oracle.FP16, oracle.FP16, 32),
+                                       (oracle.FP8, oracle.BF16, 32), (oracle.FP8, oracle.FP16, 16)])
+@pytest.mark.parametrize("H,Hkv", [(28, 4), (8, 8), (16, 2), (20, 4)])
+def test_prefill_medium(kv, qdt, bs, H, Hkv):
+    """Contexts of several hundred keys: many unit pairs walked without masks,
+    odd and even unit counts, the diagonal pairs masked; chunks ragged
+    against the wave tiles."""
+    G = H // Hkv
+    lengths = [700, 333, 1025, 96]
+    q_lens = [300, 77, 512, 96]
+    ks, vs = (0.02, 0.03) if kv == oracle.FP8 else (1.0, 1.0)
+    log(f"prefill medium kv={kv} q={qdt} bs={bs} G={G}")
+    tabs, kp, vp, qs, q = case(lengths, q_lens, H, Hkv, bs, kv, qdt, seed=10 + G, ks=ks, vs=vs)
+    want = oracle.paged_prefill(q, qdt, kp, vp, kv, tabs.block_tables, tabs.context_lens, qs,
+                                Hkv, bs, SCALE, ks, vs)
+    got = gpu_prefill(tabs, kp, vp, qs, q, qdt, kv, Hkv, bs, ks, vs)
+    check(got, want, kv, f"G={G}")
+
+
+@pytest.mark.parametrize("kv,qdt,bs", [(oracle.BF16, oracle.BF16, 16), (oracle.FP8, oracle.FP16, 16)])
+def test_prefill_repeatable(kv, qdt, bs):
+    """Two launches on the same inputs give the same bits: every step of the
+    kernel is a fixed function of its inputs (no timing-dependent reads)."""
+    lengths = [700, 333, 1025, 96]
+    q_lens = [300, 77, 512, 96]
+    ks, vs = (0.02, 0.03) if kv == oracle.FP8 else (1.0, 1.0)
+    tabs, kp, vp, qs, q = case(lengths, q_lens, 28, 4, bs, kv, qdt, seed=21, ks=ks, vs=vs)
+    runs = [gpu_prefill(tabs, kp, vp, qs, q, qdt, kv, 4, bs, ks, vs) for _ in range(3)]
+    assert np.array_equal(runs[0], runs[1]) and np.array_equal(runs[0], runs[2])
+
+
 def test_prefill_empty_chunks_and_max_query_len_above_need():
     lengths = [30, 9, 50]
     q_lens = [0, 4, 0]
