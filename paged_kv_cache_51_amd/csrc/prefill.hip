@@ -107,10 +107,14 @@ __host__ __device__ constexpr int stage_bytes(int kvt) {
 }
 
 // One unit pair of a stage: logits, online softmax and PV for the wave's two
-// column tiles.
-template <int KVT, int QT, bool MASKED>
+// column tiles.  masked (uniform): apply each column's causal limit; pairs
+// every real column sees in full skip it.  V rows at or past the context
+// end arrive zeroed from the stage writer, so no V mask is needed here.
+// One code path: the branch covers only the logit select (a second copy of
+// the whole pair made the compiler copy the 64 accumulators every pair).
+template <int KVT, int QT>
 __device__ __forceinline__ void staged_pair(MfmaMath<KVT, QT, 2>& mt, const uint8_t* stage, int tok0,
-                                            int ctx, float cs, int lane) {
+                                            bool masked, float cs, int lane) {
     constexpr int R = rows_per_sub(KVT);
     const u32x4_t* kl = reinterpret_cast<const u32x4_t*>(stage) + lane;
     const u32x4_t* vl = reinterpret_cast<const u32x4_t*>(stage + 2 * R * 1024) + lane;
@@ -138,24 +142,28 @@ __device__ __forceinline__ void staged_pair(MfmaMath<KVT, QT, 2>& mt, const uint
             st[1][t] = mfma_16x16x32<QT>(k[1], mt.qf[t][kk], st[1][t]);
         }
     }
-    // softmax
-    const int ta = tok0 + 4 * (lane >> 4);
-    bool valid[2][2][4];
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) valid[u][t][i] = !MASKED || (ta + 16 * u + i) < mt.lim[t];
     // scaled logits (log2 units); keys a column must not see get -inf
-    float y[2][8], bm[2];
-    bool jump = false;
+    float y[2][8];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) y[t][4 * u + i] = valid[u][t][i] ? st[u][t][i] * cs : -INFINITY;
+            for (int i = 0; i < 4; ++i) y[t][4 * u + i] = st[u][t][i] * cs;
+    if (masked) {
+        const int ta = tok0 + 4 * (lane >> 4);   // this lane's keys: ta..ta+3, ta+16..ta+19
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    y[t][4 * u + i] = (ta + 16 * u + i) < mt.lim[t] ? y[t][4 * u + i] : -INFINITY;
+    }
+    float bm[2];
+    bool jump = false;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
         const float mx = fmaxf(fmaxf(fmaxf(y[t][0], y[t][1]), fmaxf(y[t][2], y[t][3])),
                                fmaxf(fmaxf(y[t][4], y[t][5]), fmaxf(y[t][6], y[t][7])));
         bm[t] = rows_max(mx);
@@ -175,14 +183,12 @@ __device__ __forceinline__ void staged_pair(MfmaMath<KVT, QT, 2>& mt, const uint
     u32x4_t pf[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
+        // 2^(-inf - m) = 0 for masked keys; a column that has seen no key
+        // yet (m = -inf) subtracts 0 instead, and all its keys are -inf
+        const float mref = mt.m[t] == -INFINITY ? 0.f : mt.m[t];
         float pv[8];
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float e = fast_exp2(y[t][4 * u + i] - mt.m[t]);
-                pv[4 * u + i] = valid[u][t][i] ? e : 0.f;
-            }
+        for (int j = 0; j < 8; ++j) pv[j] = fast_exp2(y[t][j] - mref);
 #pragma unroll
         for (int j = 0; j < 4; ++j) pf[t][j] = pack2<QT>(pv[2 * j], pv[2 * j + 1]);
         float lt = mt.l[t];
@@ -191,26 +197,16 @@ __device__ __forceinline__ void staged_pair(MfmaMath<KVT, QT, 2>& mt, const uint
         mt.l[t] = lt;
     }
     // PV
-    u32x4_t vm = {0u, 0u, 0u, 0u};
-    if constexpr (MASKED) {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int tb = ta + 16 * u;
-            vm[2 * u] = (tb + 0 < ctx ? 0x0000ffffu : 0u) | (tb + 1 < ctx ? 0xffff0000u : 0u);
-            vm[2 * u + 1] = (tb + 2 < ctx ? 0x0000ffffu : 0u) | (tb + 3 < ctx ? 0xffff0000u : 0u);
-        }
-    }
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) {
         u32x4_t vv;
         if constexpr (KVT == DT_FP8) {
             const u32x2_t x = e4m3x4_to_16<QT>(vl[(nt >> 2) * kWave][nt & 3]);
-            const u32x2_t y = e4m3x4_to_16<QT>(vl[(R + (nt >> 2)) * kWave][nt & 3]);
-            vv = (u32x4_t){x[0], x[1], y[0], y[1]};
+            const u32x2_t z = e4m3x4_to_16<QT>(vl[(R + (nt >> 2)) * kWave][nt & 3]);
+            vv = (u32x4_t){x[0], x[1], z[0], z[1]};
         } else {
             vv = vl[nt * kWave];
         }
-        if constexpr (MASKED) vv &= vm;
 #pragma unroll
         for (int t = 0; t < 2; ++t) mt.acc[t][nt] = mfma_16x16x32<QT>(vv, pf[t], mt.acc[t][nt]);
     }
@@ -288,8 +284,29 @@ void paged_prefill_staged_kernel(const DecodeArgs a, const int32_t* __restrict__
             asm volatile("" : "+v"(z));
             return bt_row[unit_of(p) / NSUB + z];
         };
-        // store this wave's quarter of a pair into a stage
-        auto stage_write = [&](const u32x4_t (&r)[R], int st) {
+        // store this wave's quarter of pair p into a stage; V rows of tokens
+        // at or past the context end are zeroed (they may hold anything, and
+        // a zero weight times NaN would still poison the PV sum)
+        auto stage_write = [&](u32x4_t (&r)[R], int st, int p) {
+            if (w >= 2) {
+                const int t0 = kSubTokens * unit_of(p);
+                if (t0 + kSubTokens > ctx) {
+                    // lane (dim, group g) holds tokens 4g..4g+3 per dim tile
+                    const int tb = t0 + 4 * (lane >> 4);
+                    if constexpr (KVT == DT_FP8) {
+                        const uint32_t mk = (tb + 0 < ctx ? 0x000000ffu : 0u) | (tb + 1 < ctx ? 0x0000ff00u : 0u) |
+                                            (tb + 2 < ctx ? 0x00ff0000u : 0u) | (tb + 3 < ctx ? 0xff000000u : 0u);
+#pragma unroll
+                        for (int i = 0; i < R; ++i) r[i] &= mk;
+                    } else {
+                        const uint32_t m01 = (tb + 0 < ctx ? 0x0000ffffu : 0u) | (tb + 1 < ctx ? 0xffff0000u : 0u);
+                        const uint32_t m23 = (tb + 2 < ctx ? 0x0000ffffu : 0u) | (tb + 3 < ctx ? 0xffff0000u : 0u);
+                        const u32x4_t mk = {m01, m23, m01, m23};
+#pragma unroll
+                        for (int i = 0; i < R; ++i) r[i] &= mk;
+                    }
+                }
+            }
             uint8_t* base = stages + st * SB;
             if (w < 2 || KVT == DT_FP8) {
                 // K (or fp8 V) rows as in the pool: [unit][row][lane]
@@ -309,20 +326,15 @@ void paged_prefill_staged_kernel(const DecodeArgs a, const int32_t* __restrict__
         };
         const float cs = a.qk_scale_log2;
         auto compute = [&](int p, int st) {
-            if (p < n_pairs_w) {
-                const uint8_t* base = stages + st * SB;
-                if (2 * p + 2 <= n_free)
-                    staged_pair<KVT, QT, false>(mt, base, 2 * p * kSubTokens, ctx, cs, lane);
-                else
-                    staged_pair<KVT, QT, true>(mt, base, 2 * p * kSubTokens, ctx, cs, lane);
-            }
+            if (p < n_pairs_w)
+                staged_pair<KVT, QT>(mt, stages + st * SB, 2 * p * kSubTokens, 2 * p + 2 > n_free, cs, lane);
         };
 
         u32x4_t r0[R], r1[R];
         fetch(r0, 0);
         fetch(r1, 1);
         int id3 = id_load(3), id4 = id_load(4);
-        stage_write(r0, 0);
+        stage_write(r0, 0, 0);
         fetch(r0, 2);
         __syncthreads();
         // Fetches, stage writes and barriers are unconditional (indices past
@@ -331,12 +343,12 @@ void paged_prefill_staged_kernel(const DecodeArgs a, const int32_t* __restrict__
         // stage write waits only for its own pair, not for the one behind.
         for (int p = 0; p < n_pairs; p += 2) {
             compute(p, 0);
-            stage_write(r1, 1);       // pair p + 1
+            stage_write(r1, 1, p + 1);
             fetch_at(r1, p + 3, __builtin_amdgcn_readfirstlane(id3));
             id3 = id_load(p + 5);
             __syncthreads();
             compute(p + 1, 1);
-            stage_write(r0, 0);       // pair p + 2
+            stage_write(r0, 0, p + 2);
             fetch_at(r0, p + 4, __builtin_amdgcn_readfirstlane(id4));
             id4 = id_load(p + 6);
             __syncthreads();
