@@ -142,6 +142,18 @@ __device__ __forceinline__ void staged_pair(MfmaMath<KVT, QT, 2>& mt, const uint
             st[1][t] = mfma_16x16x32<QT>(k[1], mt.qf[t][kk], st[1][t]);
         }
     }
+    // PV operands, read before the softmax so their LDS latency hides behind
+    // it (the rescale branch below ends the scheduler's region)
+    u32x4_t vop[8];
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) {
+        if constexpr (KVT == DT_FP8) {
+            // fp8 rows hold four dim tiles each; widened when used
+            vop[nt] = nt < 2 * R ? vl[((nt >> 1) + R * (nt & 1)) * kWave] : (u32x4_t){0u, 0u, 0u, 0u};
+        } else {
+            vop[nt] = vl[nt * kWave];
+        }
+    }
     // scaled logits (log2 units); keys a column must not see get -inf
     float y[2][8];
 #pragma unroll
@@ -201,11 +213,12 @@ __device__ __forceinline__ void staged_pair(MfmaMath<KVT, QT, 2>& mt, const uint
     for (int nt = 0; nt < 8; ++nt) {
         u32x4_t vv;
         if constexpr (KVT == DT_FP8) {
-            const u32x2_t x = e4m3x4_to_16<QT>(vl[(nt >> 2) * kWave][nt & 3]);
-            const u32x2_t z = e4m3x4_to_16<QT>(vl[(R + (nt >> 2)) * kWave][nt & 3]);
+            // vop[2r] = unit A row r, vop[2r + 1] = unit B row r
+            const u32x2_t x = e4m3x4_to_16<QT>(vop[2 * (nt >> 2)][nt & 3]);
+            const u32x2_t z = e4m3x4_to_16<QT>(vop[2 * (nt >> 2) + 1][nt & 3]);
             vv = (u32x4_t){x[0], x[1], z[0], z[1]};
         } else {
-            vv = vl[nt * kWave];
+            vv = vop[nt];
         }
 #pragma unroll
         for (int t = 0; t < 2; ++t) mt.acc[t][nt] = mfma_16x16x32<QT>(vv, pf[t], mt.acc[t][nt]);
