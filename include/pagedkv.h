@@ -461,7 +461,8 @@ int32_t pkv_bm_token_slots(const pkv_block_manager* bm, int64_t seq_id, int32_t*
  * as paged_attention_decode (no split, no workspace).  Slots outside
  * [block_size, num_blocks * block_size) are read as slot block_size.  A
  * block-aligned table gives exactly the block-table result; a fragmented
- * one costs element-wise V loads (see DESIGN).  Errors: as
+ * one costs element-wise V loads (V lanes of the pool layout interleave four
+ * tokens per 16 bytes).  Errors: as
  * paged_attention_decode. */
 int32_t paged_attention_decode_tokens(void* out, const void* q, int32_t q_dtype,
                                       const void* k_cache, const void* v_cache,
