@@ -468,17 +468,28 @@ def bench_vtoken(args, torch, pkv, workloads):
             pkv.paged_attention_decode_tokens(outs[l], qs[l], kpools[l], vpools[l], slots, cl, Hkv, bs,
                                               nb, kv, scale, ks, vs, stream=stream)
     frag_ms = timed(frag_step, args.steps) / L
-    moves = []
+    # the repack, both ways: whole-block rebuild (pkv_repack_blocks, one
+    # chain per sequence) and the same rows as generic token moves
+    tiles, offsets = [], [0]
     for s in range(S):
-        moves += bm.repack(s)
+        tiles += bm.repack_tiles(s)
+        offsets.append(len(tiles))
+    moves = [(src, blk * bs + i) for blk, srcs in tiles for i, src in enumerate(srcs)
+             if src != blk * bs + i]
     mv = torch.tensor(moves, dtype=torch.int32, device=dev).reshape(-1, 2)
+    tl = torch.tensor([[blk] + list(srcs) for blk, srcs in tiles], dtype=torch.int32,
+                      device=dev).reshape(-1, 1 + bs)
+    to = torch.tensor(offsets, dtype=torch.int32, device=dev)
     need = pkv.lib().pkv_move_tokens_scratch_bytes(L, mv.shape[0], Hkv, D, kv)
     scratch = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     # repeated for timing (the values the synthetic pools end up with do
     # not matter here; the decode below only needs the same bytes moved)
     move_ms = timed(lambda: pkv.move_tokens(kpools, vpools, mv, nb, Hkv, D, bs, kv,
                                             scratch=scratch, stream=stream), max(1, args.steps // 2))
+    tile_ms = timed(lambda: pkv.repack_blocks(kpools, vpools, tl, to, nb, Hkv, D, bs, kv,
+                                              stream=stream), max(1, args.steps // 2))
     move_bytes = mv.shape[0] * L * 2 * Hkv * D * b_kv * 2
+    tile_bytes = tl.shape[0] * bs * L * 2 * Hkv * D * b_kv * 2
     mb = -(-width // bs)
     bt = torch.tensor([bm.block_table(s, mb) for s in range(S)], dtype=torch.int32, device=dev)
     mc = int(n_keep.max())
@@ -491,9 +502,11 @@ def bench_vtoken(args, torch, pkv, workloads):
     frag_gbs = dec_bytes / (frag_ms * 1e-3) / 1e9
     block_gbs = dec_bytes / (block_ms * 1e-3) / 1e9
     move_gbs = move_bytes / (move_ms * 1e-3) / 1e9
+    tile_gbs = tile_bytes / (tile_ms * 1e-3) / 1e9
     print(f"[bench] vtoken: keep {args.keep:.2f} ({int(n_keep.sum())} of {int(ctx.sum())} tokens); "
-          f"fragmented-table decode {frag_ms * 1e3:.1f} us/layer ({frag_gbs:.0f} GB/s), repack "
-          f"{mv.shape[0]} moves x {L} layers {move_ms * 1e3:.1f} us ({move_gbs:.0f} GB/s), "
+          f"fragmented-table decode {frag_ms * 1e3:.1f} us/layer ({frag_gbs:.0f} GB/s); repack x {L} "
+          f"layers: {tl.shape[0]} whole blocks rebuilt {tile_ms * 1e3:.1f} us ({tile_gbs:.0f} GB/s "
+          f"read + written), as {mv.shape[0]} token moves {move_ms * 1e3:.1f} us ({move_gbs:.0f} GB/s); "
           f"block decode after {block_ms * 1e3:.1f} us/layer ({block_gbs:.0f} GB/s)",
           file=sys.stderr, flush=True)
     dt_name = {pkv.BF16: "bf16", pkv.FP16: "fp16", pkv.FP8_E4M3: "fp8"}
@@ -506,8 +519,10 @@ def bench_vtoken(args, torch, pkv, workloads):
         "config": {"workload": f"{cfg.description.split(':')[0]}: each sequence keeps a random "
                                f"{args.keep:.0%} of its context, {L} layers",
                    "keep": args.keep, "layers": L, "num_seqs": S, "parallelism": "single GPU"},
-        "repack": {"moves": int(mv.shape[0]), "us": round(move_ms * 1e3, 1),
-                   "gbs_read_plus_write": round(move_gbs, 1)},
+        "repack": {"tiles": int(tl.shape[0]), "tiles_us": round(tile_ms * 1e3, 1),
+                   "tiles_gbs_read_plus_write": round(tile_gbs, 1),
+                   "moves": int(mv.shape[0]), "moves_us": round(move_ms * 1e3, 1),
+                   "moves_gbs_read_plus_write": round(move_gbs, 1)},
         "after_repack_block_decode": {"us_per_layer": round(block_ms * 1e3, 1),
                                       "gbs": round(block_gbs, 1)},
         "roofline": {"bound": "hbm", "kernel": "paged_decode_tokens_kernel",

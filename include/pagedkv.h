@@ -454,6 +454,17 @@ int32_t pkv_bm_repack(pkv_block_manager* bm, int64_t seq_id, int32_t* moves, int
 int32_t pkv_bm_token_slots(const pkv_block_manager* bm, int64_t seq_id, int32_t* slots,
                            int32_t max_tokens, int32_t* num_tokens);
 
+/* pkv_bm_repack_tiles: the same repack as pkv_bm_repack (same state change,
+ * same freed blocks), returned as whole blocks for pkv_repack_blocks: host
+ * array tiles[max_tiles][1 + block_size] receives, for each of the
+ * sequence's remaining blocks that gets at least one moved token, in block
+ * order, the block id followed by the source slot of each of its rows (a
+ * row that keeps its token, or lies past the last survivor, names its own
+ * slot); *num_tiles = their count (PKV_ERR_SIZE, state unchanged, if more
+ * than max_tiles). */
+int32_t pkv_bm_repack_tiles(pkv_block_manager* bm, int64_t seq_id, int32_t* tiles, int32_t max_tiles,
+                            int32_t* num_tiles);
+
 /* Decode through a per-token table ([P4] "vToken"): logical token t of
  * sequence s is read from physical slot token_slots[s][t] (device int32
  * [num_seqs][max_tokens_per_seq]; block slot / block_size, row slot %
@@ -472,6 +483,28 @@ int32_t paged_attention_decode_tokens(void* out, const void* q, int32_t q_dtype,
                                       float scale, int32_t block_size, int32_t num_blocks,
                                       int32_t kv_dtype, float k_scale, float v_scale,
                                       pkv_stream_t stream);
+
+/* Rebuild whole blocks after an eviction ([P4] "vToken", asynchronous
+ * repacking): for every tile t (device int32 tiles[t][1 + block_size]: the
+ * destination block, then the source slot of each of its rows), in every
+ * layer, K and V of every kv head, row i of block tiles[t][0] receives the
+ * token at slot tiles[t][1 + i].  Tiles are grouped in chains (device int32
+ * chain_offsets[num_chains + 1]: chain c is tiles chain_offsets[c] ..
+ * chain_offsets[c + 1] - 1) and a chain's tiles are rebuilt in order,
+ * 16-row sub-tile by sub-tile.  Requirement (what pkv_bm_repack_tiles
+ * produces, one chain per sequence): no source of a sub-tile lies in rows
+ * an earlier sub-tile of its chain writes, and the chains write disjoint
+ * blocks that no other chain reads.  Then every source is read before it is
+ * overwritten and the result equals pkv_move_tokens with the moves (source,
+ * destination) of all rows, without its scratch.  Sub-tiles are stored
+ * whole (no partial writes).  A source slot outside [block_size,
+ * num_blocks * block_size) leaves its row unchanged; a destination block
+ * outside [1, num_blocks) skips its tile.  Errors: PKV_ERR_ARG (null
+ * pointers, bad sizes), PKV_ERR_UNSUPPORTED (head_dim), PKV_ERR_HIP. */
+int32_t pkv_repack_blocks(void* const* k_layers, void* const* v_layers, int32_t num_layers,
+                          int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
+                          int32_t block_size, int32_t kv_dtype, const int32_t* tiles,
+                          const int32_t* chain_offsets, int32_t num_chains, pkv_stream_t stream);
 
 /* Move whole tokens (K and V rows of every kv head, every layer) from slot
  * moves[i][0] to slot moves[i][1] ([P4] "vToken" repacking); moves is a

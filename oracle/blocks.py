@@ -216,6 +216,24 @@ class BlockPoolModel:
         s.pop("slots", None)
         return moves
 
+    def repack_tiles(self, sid):
+        """The same repack as repack(), as whole blocks: [(block, [source
+        slot of each row])] for every remaining block that receives a moved
+        token, in block order; rows that keep their token or lie past the
+        last survivor name their own slot."""
+        s = self.seqs[sid]
+        bs = self.bs
+        cur = self.token_slots(sid)
+        n = len(cur)
+        tiles = []
+        for j in range(-(-n // bs)):
+            b = s["blocks"][j]
+            src = [cur[j * bs + i] if j * bs + i < n else b * bs + i for i in range(bs)]
+            if any(x != b * bs + i for i, x in enumerate(src)):
+                tiles.append((b, src))
+        self.repack(sid)
+        return tiles
+
     def slots(self, sid, first, count):
         bl = self.seqs[sid]["blocks"]
         return [bl[p // self.bs] * self.bs + p % self.bs for p in range(first, first + count)]

@@ -14,4 +14,5 @@ from ._binding import (  # noqa: F401
     paged_attention_decode, check_block_tables, torch_dtype, dtype_code, EXPORTS,
     BlockManager, copy_blocks, paged_attention_prefill, paged_attention_decode_tokens,
     move_tokens,
+    repack_blocks,
 )

@@ -31,7 +31,7 @@ EXPORTS = [
     "pkv_bm_fork", "pkv_bm_free_sequence", "pkv_bm_block_table", "pkv_bm_slots",
     "pkv_copy_blocks", "paged_attention_prefill", "pkv_bm_evict_tokens", "pkv_bm_repack",
     "pkv_bm_token_slots", "paged_attention_decode_tokens", "pkv_move_tokens_scratch_bytes",
-    "pkv_move_tokens",
+    "pkv_move_tokens", "pkv_bm_repack_tiles", "pkv_repack_blocks",
 ]
 
 
@@ -114,6 +114,8 @@ def lib():
                                                     i32, f32, i32, i32, i32, f32, f32, p]),
             "pkv_move_tokens_scratch_bytes": (i64, [i32, i32, i32, i32, i32]),
             "pkv_move_tokens": (i32, [p, p, i32, i32, i32, i32, i32, i32, p, i32, p, i64, p]),
+            "pkv_bm_repack_tiles": (i32, [p, i64, p, i32, ctypes.POINTER(i32)]),
+            "pkv_repack_blocks": (i32, [p, p, i32, i32, i32, i32, i32, i32, p, p, i32, p]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -404,6 +406,20 @@ class BlockManager:
         _check(lib().pkv_bm_repack(self._h, seq_id, arr, n.value, ctypes.byref(n)))
         return [(arr[2 * i], arr[2 * i + 1]) for i in range(n.value)]
 
+    def repack_tiles(self, seq_id):
+        """The same repack as repack(), as whole blocks: a list of
+        (block, [source slot of each row]) in block order."""
+        n = ctypes.c_int32(0)
+        rc = lib().pkv_bm_repack_tiles(self._h, seq_id, None, 0, ctypes.byref(n))
+        if rc >= 0:
+            return []
+        if rc != -2:
+            _check(rc)
+        bs = self.block_size
+        arr = (ctypes.c_int32 * (n.value * (1 + bs)))()
+        _check(lib().pkv_bm_repack_tiles(self._h, seq_id, arr, n.value, ctypes.byref(n)))
+        return [(arr[t * (1 + bs)], list(arr[t * (1 + bs) + 1:(t + 1) * (1 + bs)])) for t in range(n.value)]
+
     def token_slots(self, seq_id, max_tokens=None):
         n = ctypes.c_int32(0)
         rc = lib().pkv_bm_token_slots(self._h, seq_id, None, 0, ctypes.byref(n))
@@ -460,6 +476,20 @@ def paged_attention_decode_tokens(out, q, k_cache, v_cache, token_slots, context
         token_slots.shape[1], _ptr(context_lens, "context_lens", torch.int32), S, H,
         num_kv_heads, D, float(scale), block_size, num_blocks, kv_dtype, float(k_scale),
         float(v_scale), _stream(stream)))
+
+
+def repack_blocks(k_layers, v_layers, tiles, chain_offsets, num_blocks, num_kv_heads, head_dim,
+                  block_size, kv_dtype, stream=None):
+    """pkv_repack_blocks: tiles is a device int32 tensor [n, 1 + block_size]
+    (destination block, then a source slot per row), chain_offsets a device
+    int32 tensor [chains + 1]."""
+    n = len(k_layers)
+    kp = (ctypes.c_void_p * max(n, 1))(*[_ptr(t, "k_layers", torch.uint8).value for t in k_layers])
+    vp = (ctypes.c_void_p * max(n, 1))(*[_ptr(t, "v_layers", torch.uint8).value for t in v_layers])
+    _check(lib().pkv_repack_blocks(kp, vp, n, num_blocks, num_kv_heads, head_dim, block_size, kv_dtype,
+                                   _ptr(tiles, "tiles", torch.int32),
+                                   _ptr(chain_offsets, "chain_offsets", torch.int32),
+                                   chain_offsets.numel() - 1, _stream(stream)))
 
 
 def move_tokens(k_layers, v_layers, moves, num_blocks, num_kv_heads, head_dim, block_size,

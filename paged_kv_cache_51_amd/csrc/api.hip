@@ -538,6 +538,27 @@ int32_t pkv_move_tokens(void* const* k_layers, void* const* v_layers, int32_t nu
     return ok();
 }
 
+int32_t pkv_repack_blocks(void* const* k_layers, void* const* v_layers, int32_t num_layers,
+                          int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
+                          int32_t block_size, int32_t kv_dtype, const int32_t* tiles,
+                          const int32_t* chain_offsets, int32_t num_chains, pkv_stream_t stream) {
+    if (int32_t e = check_layout_args(head_dim, block_size, kv_dtype)) return e;
+    if (head_dim != kBuiltHeadDim) return fail(PKV_ERR_UNSUPPORTED, "kernels are built for head_dim 128, got %d", head_dim);
+    if (num_layers < 0 || num_chains < 0 || num_kv_heads <= 0 || num_blocks < 1)
+        return fail(PKV_ERR_ARG, "bad sizes");
+    if ((int64_t)num_blocks * block_size >= (1LL << 31)) return fail(PKV_ERR_ARG, "slots must fit int32");
+    if (num_chains == 0 || num_layers == 0) return ok();
+    if (!k_layers || !v_layers || !tiles || !chain_offsets) return fail(PKV_ERR_ARG, "null pointer");
+    for (int32_t l = 0; l < num_layers; ++l)
+        if (!k_layers[l] || !v_layers[l]) return fail(PKV_ERR_ARG, "null layer pointer");
+    (void)hipGetLastError();
+    hipError_t e = pkv::launch_repack_blocks(k_layers, v_layers, num_layers, num_blocks, num_kv_heads,
+                                             block_size, kv_dtype, tiles, chain_offsets, num_chains,
+                                             (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "repack_blocks launch");
+    return ok();
+}
+
 int32_t paged_attention_decode(void* out, const void* q, int32_t q_dtype, const void* k_cache,
                                const void* v_cache, const int32_t* block_tables,
                                int32_t max_blocks_per_seq, const int32_t* context_lens,

@@ -464,6 +464,54 @@ int32_t pkv_bm_repack(pkv_block_manager* bm, int64_t seq_id, int32_t* moves, int
     return ok();
 }
 
+// The same repack as tiles: for each of the sequence's first ceil(n / bs)
+// blocks that receives at least one moved token, the block id and the
+// source slot of each of its bs rows (a row that keeps its token, or lies
+// past the last survivor, names its own slot).  Tiles come in block order,
+// which is the order pkv_repack_blocks needs: every source sits at or after
+// the row it moves to.
+int32_t pkv_bm_repack_tiles(pkv_block_manager* bm, int64_t seq_id, int32_t* tiles, int32_t max_tiles,
+                            int32_t* num_tiles) {
+    if (!bm || !num_tiles || (max_tiles > 0 && !tiles)) return fail(PKV_ERR_ARG, "null pointer");
+    pkv::Sequence* sq = find_seq(bm, seq_id);
+    if (!sq) return fail(PKV_ERR_ARG, "unknown sequence %lld", (long long)seq_id);
+    pkv::BlockManager& m = bm->m;
+    const int bs = m.block_size;
+    const int32_t n = sq->num_tokens;
+    const int32_t need = (n + bs - 1) / bs;
+    auto src_of = [&](int32_t j, int32_t i) {
+        const int32_t q = j * bs + i;
+        return q < n ? sq->slots[q] : sq->blocks[j] * bs + i;
+    };
+    int32_t cnt = 0;
+    if (sq->fragmented)
+        for (int32_t j = 0; j < need; ++j)
+            for (int32_t i = 0; i < bs; ++i)
+                if (src_of(j, i) != sq->blocks[j] * bs + i) {
+                    ++cnt;
+                    break;
+                }
+    *num_tiles = cnt;
+    if (cnt > max_tiles) return fail(PKV_ERR_SIZE, "%d tiles, room for %d", cnt, max_tiles);
+    if (sq->fragmented) {
+        int32_t k = 0;
+        for (int32_t j = 0; j < need; ++j) {
+            bool moved = false;
+            for (int32_t i = 0; i < bs && !moved; ++i) moved = src_of(j, i) != sq->blocks[j] * bs + i;
+            if (!moved) continue;
+            int32_t* t = tiles + (int64_t)k * (1 + bs);
+            t[0] = sq->blocks[j];
+            for (int32_t i = 0; i < bs; ++i) t[1 + i] = src_of(j, i);
+            ++k;
+        }
+    }
+    for (size_t i = sq->blocks.size(); i-- > (size_t)need;) m.release(sq->blocks[i]);   // last block first
+    sq->blocks.resize(need);
+    sq->slots.clear();
+    sq->fragmented = false;
+    return ok();
+}
+
 int32_t pkv_bm_token_slots(const pkv_block_manager* bm, int64_t seq_id, int32_t* slots,
                            int32_t max_tokens, int32_t* num_tokens) {
     if (!bm || (max_tokens > 0 && !slots)) return fail(PKV_ERR_ARG, "null pointer");

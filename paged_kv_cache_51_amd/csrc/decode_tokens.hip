@@ -239,6 +239,111 @@ static hipError_t launch_moves_t(MoveArgs a, void* const* kl, void* const* vl, h
     return hipSuccess;
 }
 
+// ---------------------------------------------------------- repack blocks --
+// Whole-block rebuild after an eviction: destination unit (16 rows of a
+// tile's block) gets its K and V sub-tiles assembled from the rows' source
+// slots with the same per-token gather as the token-table decode, then
+// stored whole (16-byte stores of complete pool rows: no partial writes).
+// Workgroup (chain, layer), wave w takes kv heads w, w + 4, ...; a wave
+// walks its chain's units in order, four at a time (gather all four, then
+// store).  No source of a unit lies in rows an earlier unit of the chain
+// writes, so a store can never clobber a source still to be read; the
+// chains of one call touch disjoint blocks.
+
+struct RepackArgs {
+    uint8_t* k[kMoveLayers];
+    uint8_t* v[kMoveLayers];
+    const int32_t* tiles;          // [tile][1 + bs]: destination block, source slot per row
+    const int32_t* chain_offsets;  // [num_chains + 1]
+    int32_t num_kv_heads;
+    int32_t num_blocks;
+};
+
+template <int KVT, int BS>
+__global__ __launch_bounds__(kMoveThreads) void repack_blocks_kernel(const RepackArgs a) {
+    constexpr int NSUB = BS / kSubTokens;
+    constexpr int R = rows_per_sub(KVT);
+    constexpr int64_t SUB = sub_tile_bytes(KVT);
+    constexpr int64_t TILE = SUB * NSUB;
+    constexpr int CH = 4;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int layer = blockIdx.y;
+    const int t0 = a.chain_offsets[blockIdx.x];
+    const int n_units = (a.chain_offsets[blockIdx.x + 1] - t0) * NSUB;
+    if (n_units <= 0) return;
+    const int32_t cap = a.num_blocks * BS;
+    const int64_t head_stride = (int64_t)a.num_kv_heads * TILE;
+    for (int h = w; h < a.num_kv_heads; h += kMoveThreads / kWave) {
+        const uint8_t* kp = a.k[layer] + (int64_t)h * TILE;
+        const uint8_t* vp = a.v[layer] + (int64_t)h * TILE;
+        for (int c0 = 0; c0 < n_units; c0 += CH) {
+            const int nc = min(CH, n_units - c0);
+            // lane l: row l % 16 of chunk unit min(l / 16, nc - 1); a source
+            // outside the pool leaves the row as it is (reads its own slot)
+            const int un = c0 + min(lane >> 4, nc - 1);
+            const int32_t* tile = a.tiles + (int64_t)(t0 + un / NSUB) * (1 + BS);
+            const int32_t dst_block = tile[0];
+            const int row = (un % NSUB) * kSubTokens + (lane & 15);
+            int32_t slot = tile[1 + row];
+            if ((unsigned)(slot - BS) >= (unsigned)(cap - BS)) slot = dst_block * BS + row;
+            const bool dst_ok = (unsigned)(dst_block - 1) < (unsigned)(a.num_blocks - 1);
+            if (!dst_ok) slot = BS;   // (unit skipped below; any valid slot)
+            UnitRegs<KVT> buf[CH];
+#pragma unroll
+            for (int j = 0; j < CH; ++j)
+                gather_unit<KVT, BS>(buf[j], kp, vp, head_stride, slot, min(j, nc - 1), lane);
+#pragma unroll
+            for (int j = 0; j < CH; ++j) {
+                if (j >= nc) continue;
+                const int uj = c0 + j;
+                const int32_t db = __builtin_amdgcn_readlane(dst_block, 16 * j);
+                if ((unsigned)(db - 1) >= (unsigned)(a.num_blocks - 1)) continue;
+                const int64_t off = (int64_t)db * head_stride + (int64_t)h * TILE + (uj % NSUB) * SUB + 16 * lane;
+                u32x4_t* kd = reinterpret_cast<u32x4_t*>(a.k[layer] + off);
+                u32x4_t* vd = reinterpret_cast<u32x4_t*>(a.v[layer] + off);
+#pragma unroll
+                for (int r = 0; r < R; ++r) kd[kWave * r] = buf[j].k[r];
+#pragma unroll
+                for (int r = 0; r < R; ++r) vd[kWave * r] = buf[j].v[r];
+            }
+        }
+    }
+}
+
+template <int KVT, int BS>
+static hipError_t launch_repack_t(RepackArgs a, void* const* kl, void* const* vl, int num_layers,
+                                  int num_chains, hipStream_t st) {
+    for (int l0 = 0; l0 < num_layers; l0 += kMoveLayers) {
+        const int nl = num_layers - l0 < kMoveLayers ? num_layers - l0 : kMoveLayers;
+        for (int i = 0; i < nl; ++i) {
+            a.k[i] = static_cast<uint8_t*>(kl[l0 + i]);
+            a.v[i] = static_cast<uint8_t*>(vl[l0 + i]);
+        }
+        hipLaunchKernelGGL((repack_blocks_kernel<KVT, BS>), dim3(num_chains, nl), dim3(kMoveThreads), 0, st, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_repack_blocks(void* const* k_layers, void* const* v_layers, int num_layers,
+                                int num_blocks, int num_kv_heads, int block_size, int kv_dtype,
+                                const int32_t* tiles, const int32_t* chain_offsets, int num_chains,
+                                hipStream_t st) {
+    if (num_chains == 0 || num_layers == 0) return hipSuccess;
+    RepackArgs a{};
+    a.tiles = tiles;
+    a.chain_offsets = chain_offsets;
+    a.num_kv_heads = num_kv_heads;
+    a.num_blocks = num_blocks;
+    if (kv_dtype == DT_FP8)
+        return block_size == 16 ? launch_repack_t<DT_FP8, 16>(a, k_layers, v_layers, num_layers, num_chains, st)
+                                : launch_repack_t<DT_FP8, 32>(a, k_layers, v_layers, num_layers, num_chains, st);
+    return block_size == 16 ? launch_repack_t<DT_BF16, 16>(a, k_layers, v_layers, num_layers, num_chains, st)
+                            : launch_repack_t<DT_BF16, 32>(a, k_layers, v_layers, num_layers, num_chains, st);
+}
+
 hipError_t launch_move_tokens(void* const* k_layers, void* const* v_layers, int num_layers,
                               int num_blocks, int num_kv_heads, int block_size, int kv_dtype,
                               const int32_t* moves, int num_moves, void* scratch, hipStream_t st) {

@@ -74,6 +74,10 @@ hipError_t launch_decode_reduce(const DecodeArgs& a, int q_dtype, int block_size
 // (decode_tokens.hip).
 hipError_t launch_decode_tokens(const DecodeArgs& a, int q_dtype, int kv_dtype, int block_size,
                                 const int32_t* token_slots, int max_tokens, hipStream_t st);
+hipError_t launch_repack_blocks(void* const* k_layers, void* const* v_layers, int num_layers,
+                                int num_blocks, int num_kv_heads, int block_size, int kv_dtype,
+                                const int32_t* tiles, const int32_t* chain_offsets, int num_chains,
+                                hipStream_t st);
 hipError_t launch_move_tokens(void* const* k_layers, void* const* v_layers, int num_layers,
                               int num_blocks, int num_kv_heads, int block_size, int kv_dtype,
                               const int32_t* moves, int num_moves, void* scratch, hipStream_t st);

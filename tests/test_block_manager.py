@@ -287,7 +287,11 @@ def test_evict_and_repack_match_model(prefix, bs, seed):
                 lib_.evict_tokens(s, keep)
                 fragmented.add(s)
         elif op < 0.75:
-            assert lib_.repack(s) == ref.repack(s)
+            if rng.random() < 0.5:
+                assert lib_.repack(s) == ref.repack(s)
+            else:
+                tiles = ref.repack_tiles(s)
+                assert lib_.repack_tiles(s) == tiles
             fragmented.discard(s)
         elif op < 0.82 and s not in fragmented:
             ref.fork(s, next_id)
@@ -303,3 +307,34 @@ def test_evict_and_repack_match_model(prefix, bs, seed):
         for x in live:
             assert lib_.token_slots(x) == ref.token_slots(x)
             assert lib_.block_table(x) == ref.block_table(x)
+
+
+@pytest.mark.parametrize("bs,seed", [(16, 31), (32, 32)])
+def test_repack_tiles_are_the_repack_moves(bs, seed):
+    """The tile form of a repack names, row for row, the same (source,
+    destination) pairs as the move form, and its tiles come in block order
+    with every source at or after the row it fills (the order the tile
+    kernel relies on)."""
+    rng = random.Random(seed)
+    nb = 64
+    a, b = BlockPoolModel(nb, bs), BlockPoolModel(nb, bs)
+    for sid in range(4):
+        toks = [rng.randrange(9) for _ in range(rng.randrange(20, 120))]
+        a.add_sequence(sid, toks)
+        b.add_sequence(sid, toks)
+    for sid in range(4):
+        for _ in range(2):                          # evict twice before repacking
+            keep = [rng.random() < 0.55 for _ in range(len(a.token_slots(sid)))]
+            a.evict_tokens(sid, keep)
+            b.evict_tokens(sid, keep)
+        order = {blk: j for j, blk in enumerate(a.seqs[sid]["blocks"])}
+        moves = a.repack(sid)
+        tiles = b.repack_tiles(sid)
+        pairs = [(src, blk * bs + i) for blk, srcs in tiles for i, src in enumerate(srcs)
+                 if src != blk * bs + i]
+        assert pairs == moves
+        assert [order[blk] for blk, _ in tiles] == sorted(order[blk] for blk, _ in tiles)
+        for blk, srcs in tiles:
+            for i, src in enumerate(srcs):
+                assert order[src // bs] * bs + src % bs >= order[blk] * bs + i
+        assert a.block_table(sid) == b.block_table(sid)

@@ -129,8 +129,60 @@ def test_move_tokens_bit_exact(kv, bs, Hkv, layers):
         assert np.array_equal(dv.cpu().numpy(), wv)
 
 
-@pytest.mark.parametrize("kv", [oracle.BF16, oracle.FP8])
-def test_evict_repack_move_then_block_decode_bitwise(kv):
+@pytest.mark.parametrize("kv,bs,Hkv,layers", [(oracle.BF16, 16, 4, 2), (oracle.FP8, 32, 2, 3),
+                                              (oracle.FP16, 16, 5, 66), (oracle.FP8, 16, 8, 1)])
+def test_repack_blocks_equal_the_moves(kv, bs, Hkv, layers):
+    """The tile rebuild (pkv_repack_blocks, one chain per sequence) leaves
+    the pools bit for bit as the oracle's moves of the same repack; a row
+    with a source outside the pool keeps its bytes, a tile aimed outside the
+    pool changes nothing."""
+    log(f"repack_blocks kv={kv} bs={bs} Hkv={Hkv} layers={layers}")
+    nb = 80
+    lengths = [300, 77, 160, 33, 250]
+    nbytes = pkv.layer_pool_bytes(nb, Hkv, D, bs, kv)
+    r = np.random.default_rng(17)
+    hk = [r.integers(0, 256, nbytes, dtype=np.uint8) for _ in range(layers)]
+    hv = [r.integers(0, 256, nbytes, dtype=np.uint8) for _ in range(layers)]
+    bm_t, bm_m = pkv.BlockManager(nb, bs), pkv.BlockManager(nb, bs)
+    for s, c in enumerate(lengths):
+        bm_t.add_sequence(s, list(range(c)))
+        bm_m.add_sequence(s, list(range(c)))
+    # blocks no sequence ever held: the extra chain below may write them
+    # (a chain must not write blocks another chain reads)
+    free = [b for b in range(1, nb) if bm_t.ref_count(b) == 0]
+    for s, c in enumerate(lengths):
+        for _ in range(1 + s % 2):
+            keep = [bool(r.random() < 0.5) for _ in range(len(bm_t.token_slots(s)))]
+            bm_t.evict_tokens(s, keep)
+            bm_m.evict_tokens(s, keep)
+    tiles, offsets, moves = [], [0], []
+    for s in range(len(lengths)):
+        tiles += bm_t.repack_tiles(s)
+        offsets.append(len(tiles))
+        moves += bm_m.repack(s)
+    want_k, want_v = oracle.move_tokens(hk, hv, moves, Hkv, D, bs, kv)
+    # a chain of its own: a bad source row (kept as is) and a bad destination
+    b0 = free[0]
+    bad_src = [b0 * bs + i for i in range(bs)]
+    bad_src[3] = 3                                  # inside the null block: not a token slot
+    bad_src[5] = free[1] * bs + 2                   # a real move into the same tile
+    tiles += [(b0, bad_src), (0, [free[2] * bs] * bs), (nb, [free[2] * bs] * bs)]
+    offsets.append(len(tiles))
+    want_k, want_v = oracle.move_tokens(want_k, want_v, [(free[1] * bs + 2, b0 * bs + 5)], Hkv, D, bs, kv)
+    flat = [[blk] + list(src) for blk, src in tiles]
+    ks = [torch.from_numpy(h).to(DEV) for h in hk]
+    vs = [torch.from_numpy(h).to(DEV) for h in hv]
+    pkv.repack_blocks(ks, vs, torch.tensor(flat, dtype=torch.int32, device=DEV),
+                      torch.tensor(offsets, dtype=torch.int32, device=DEV), nb, Hkv, D, bs, kv)
+    torch.cuda.synchronize()
+    for wk, wv, dk, dv in zip(want_k, want_v, ks, vs):
+        assert np.array_equal(dk.cpu().numpy(), wk)
+        assert np.array_equal(dv.cpu().numpy(), wv)
+
+
+@pytest.mark.parametrize("kv,tiles", [(oracle.BF16, False), (oracle.FP8, False), (oracle.BF16, True),
+                                      (oracle.FP8, True)])
+def test_evict_repack_move_then_block_decode_bitwise(kv, tiles):
     bs, Hkv, H, nb = 16, 2, 8, 96
     ks = vs = 0.05 if kv == oracle.FP8 else 1.0
     lengths = [300, 77, 160, 33]
@@ -155,12 +207,21 @@ def test_evict_repack_move_then_block_decode_bitwise(kv):
     a = torch.full_like(q, float("nan"))
     pkv.paged_attention_decode_tokens(a, q, kd, vd, slots, devi(ctx), Hkv, bs, nb, kv, SCALE, ks, vs)
     free_before = bm.num_free_blocks()
-    moves = []
-    for s in range(len(lengths)):
-        moves += bm.repack(s)
+    if tiles:
+        flat, offsets = [], [0]
+        for s in range(len(lengths)):
+            flat += [[blk] + list(src) for blk, src in bm.repack_tiles(s)]
+            offsets.append(len(flat))
+        pkv.repack_blocks([kd], [vd], torch.tensor(flat, dtype=torch.int32, device=DEV),
+                          torch.tensor(offsets, dtype=torch.int32, device=DEV), nb, Hkv, D, bs, kv)
+    else:
+        moves = []
+        for s in range(len(lengths)):
+            moves += bm.repack(s)
+        pkv.move_tokens([kd], [vd], torch.tensor(moves, dtype=torch.int32, device=DEV), nb, Hkv, D, bs,
+                        kv)
     assert bm.num_free_blocks() - free_before == sum(-(-c // bs) - -(-n // bs)
                                                      for c, n in zip(lengths, ctx))
-    pkv.move_tokens([kd], [vd], torch.tensor(moves, dtype=torch.int32, device=DEV), nb, Hkv, D, bs, kv)
     mb = -(-width // bs)
     bt = devi([bm.block_table(s, mb) for s in range(len(lengths))])
     b = torch.full_like(q, float("nan"))
