@@ -12,10 +12,11 @@
 // of its own token instead of taking a whole 16-token sub-tile.  K lanes
 // hold 16 contiguous bytes of one token (the pool layout's K rows), so a K
 // fragment is still four 16-byte loads per lane; V lanes hold 4 tokens of
-// one dim, so a V fragment is gathered element by element (32 two-byte or
-// one-byte loads per lane per unit).  When the table is block-aligned the
-// addresses coincide with the block path's.  Repacking exists to return
-// the table to that state.
+// one dim, so a lane loads the 16-byte chunk holding each of its 4 tokens'
+// values per pool row (16 loads per unit) and picks the token's bytes out
+// with byte permutes.  When the table is block-aligned the addresses
+// coincide with the block path's.  Repacking exists to return the table to
+// that state.
 #include "decode_core.h"
 #include "mfma_math.h"
 
@@ -55,29 +56,56 @@ __device__ __forceinline__ void gather_unit(UnitRegs<KVT>& u, const uint8_t* kpo
 #pragma unroll
         for (int r = 0; r < R; ++r) u.k[r] = *reinterpret_cast<const u32x4_t*>(base + 1024 * r);
     }
-    // V: tokens 4g .. 4g+3 of dim 16nt + (lane & 15), one element each
-    const uint8_t* vb[4];
+    // V: tokens 4g .. 4g+3 of dim d = lane & 15 for each dim tile nt.  A
+    // source token's values for dim d sit in one 16-byte chunk per pool row
+    // (row nt / n, lane d + 16 (row-in-block % 16) / 4), shared with the
+    // three other tokens of its group of 4: load that chunk whole for each
+    // of the 4 tokens and row, then pick the token's bytes out of it.
+    const int d = lane & 15;
+    const u32x4_t* vc[4];
+    int sub[4];                                   // token's place in its group of 4
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int32_t slot = (int32_t)lane_fetch((uint32_t)slot_l, 16 * j + 4 * g + i);
         const int32_t pb = slot / BS, rp = slot - pb * BS;
-        vb[i] = vpool + (int64_t)pb * head_stride + tile_offset_v<KVT>(rp, lane & 15);
+        vc[i] = reinterpret_cast<const u32x4_t*>(vpool + (int64_t)pb * head_stride + (rp >> 4) * sub_tile_bytes(KVT) +
+                                                 16 * (d + 16 * ((rp & 15) >> 2)));
+        sub[i] = rp & 3;
     }
+    u32x4_t c[4][R];
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) {
-        constexpr int n = 4 / E;
-        const int off = 1024 * (nt / n) + 4 * E * (nt % n);   // tile_offset_v(r, k + 16 nt) - (.., k)
-        if constexpr (E == 2) {
-            uint32_t w0 = *reinterpret_cast<const uint16_t*>(vb[0] + off) |
-                          ((uint32_t)*reinterpret_cast<const uint16_t*>(vb[1] + off) << 16);
-            uint32_t w1 = *reinterpret_cast<const uint16_t*>(vb[2] + off) |
-                          ((uint32_t)*reinterpret_cast<const uint16_t*>(vb[3] + off) << 16);
-            u.v[nt >> 1][2 * (nt & 1)] = w0;
-            u.v[nt >> 1][2 * (nt & 1) + 1] = w1;
-        } else {
-            u.v[nt >> 2][nt & 3] = (uint32_t)vb[0][off] | ((uint32_t)vb[1][off] << 8) |
-                                   ((uint32_t)vb[2][off] << 16) | ((uint32_t)vb[3][off] << 24);
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < R; ++r) c[i][r] = vc[i][kWave * r];
+    if constexpr (E == 2) {
+        // chunk dwords: (nt even: tokens 0,1 | 2,3), (nt odd: 0,1 | 2,3);
+        // token i's value is half sub & 1 of dword sub >> 1 (+ 2 if odd)
+        uint32_t sel[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const uint32_t a0 = 2 * (sub[2 * h] & 1), a1 = 4 + 2 * (sub[2 * h + 1] & 1);
+            sel[h] = a0 | ((a0 + 1) << 8) | (a1 << 16) | ((a1 + 1) << 24);
         }
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int odd = 0; odd < 2; ++odd)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const uint32_t lo = (sub[2 * h] >> 1) ? c[2 * h][r][2 * odd + 1] : c[2 * h][r][2 * odd];
+                    const uint32_t hi = (sub[2 * h + 1] >> 1) ? c[2 * h + 1][r][2 * odd + 1] : c[2 * h + 1][r][2 * odd];
+                    u.v[r][2 * odd + h] = __builtin_amdgcn_perm(hi, lo, sel[h]);
+                }
+    } else {
+        // fp8: dword q of a chunk is dim tile 4 row + q, byte = token
+        const uint32_t s01 = sub[0] | ((4 + sub[1]) << 8) | (0x0c0cu << 16);   // bytes 2, 3: zero
+        const uint32_t s23 = (0x0c0cu) | (sub[2] << 16) | ((4 + sub[3]) << 24);
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                u.v[r][q] = __builtin_amdgcn_perm(c[1][r][q], c[0][r][q], s01) |
+                            __builtin_amdgcn_perm(c[3][r][q], c[2][r][q], s23);
     }
 }
 
@@ -245,8 +273,8 @@ static hipError_t launch_moves_t(MoveArgs a, void* const* kl, void* const* vl, h
 // slots with the same per-token gather as the token-table decode, then
 // stored whole (16-byte stores of complete pool rows: no partial writes).
 // Workgroup (chain, layer), wave w takes kv heads w, w + 4, ...; a wave
-// walks its chain's units in order, four at a time (gather all four, then
-// store).  No source of a unit lies in rows an earlier unit of the chain
+// walks its chain's units in order, a few at a time (gather them, then
+// store them).  No source of a unit lies in rows an earlier unit of the chain
 // writes, so a store can never clobber a source still to be read; the
 // chains of one call touch disjoint blocks.
 
@@ -259,13 +287,17 @@ struct RepackArgs {
     int32_t num_blocks;
 };
 
+#ifndef PKV_REPACK_UNITS
+#define PKV_REPACK_UNITS 4
+#endif
+
 template <int KVT, int BS>
 __global__ __launch_bounds__(kMoveThreads) void repack_blocks_kernel(const RepackArgs a) {
     constexpr int NSUB = BS / kSubTokens;
     constexpr int R = rows_per_sub(KVT);
     constexpr int64_t SUB = sub_tile_bytes(KVT);
     constexpr int64_t TILE = SUB * NSUB;
-    constexpr int CH = 4;
+    constexpr int CH = PKV_REPACK_UNITS;   // units gathered before their stores
     const int lane = threadIdx.x & (kWave - 1);
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int layer = blockIdx.y;
@@ -279,7 +311,8 @@ __global__ __launch_bounds__(kMoveThreads) void repack_blocks_kernel(const Repac
         const uint8_t* vp = a.v[layer] + (int64_t)h * TILE;
         for (int c0 = 0; c0 < n_units; c0 += CH) {
             const int nc = min(CH, n_units - c0);
-            // lane l: row l % 16 of chunk unit min(l / 16, nc - 1); a source
+            // lane l: row l % 16 of chunk unit min(l / 16, nc - 1) (lanes past
+            // CH units repeat the last one); a source
             // outside the pool leaves the row as it is (reads its own slot)
             const int un = c0 + min(lane >> 4, nc - 1);
             const int32_t* tile = a.tiles + (int64_t)(t0 + un / NSUB) * (1 + BS);
