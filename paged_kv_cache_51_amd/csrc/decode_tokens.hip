@@ -335,10 +335,12 @@ __global__ __launch_bounds__(kMoveThreads) void repack_blocks_kernel(const Repac
                 const int64_t off = (int64_t)db * head_stride + (int64_t)h * TILE + (uj % NSUB) * SUB + 16 * lane;
                 u32x4_t* kd = reinterpret_cast<u32x4_t*>(a.k[layer] + off);
                 u32x4_t* vd = reinterpret_cast<u32x4_t*>(a.v[layer] + off);
+                // non-temporal: the rebuilt rows are not read again here
+                // (interleaved timing: 3111 -> 3026 us for the 7B repack)
 #pragma unroll
-                for (int r = 0; r < R; ++r) kd[kWave * r] = buf[j].k[r];
+                for (int r = 0; r < R; ++r) __builtin_nontemporal_store(buf[j].k[r], kd + kWave * r);
 #pragma unroll
-                for (int r = 0; r < R; ++r) vd[kWave * r] = buf[j].v[r];
+                for (int r = 0; r < R; ++r) __builtin_nontemporal_store(buf[j].v[r], vd + kWave * r);
             }
         }
     }
