@@ -399,14 +399,14 @@ template <int KVT, int QT, int BS>
 static hipError_t launch_prefill_t(const DecodeArgs& a, const int32_t* query_start, int tile_tokens,
                                    int max_tiles, hipStream_t st) {
     if (max_tiles > kWavesPerGroup) {
-        // staged form: 32 columns (two 16-column tiles) per wave
+        // staged form: 32 columns (two 16-column tiles) per wave, four waves
+        constexpr int NW = 4;
         const int tt = 2 * tile_tokens;
         const int wave_tiles = (max_tiles * tile_tokens + tt - 1) / tt;
-        const int groups = (wave_tiles + kWavesPerGroup - 1) / kWavesPerGroup;
+        const int groups = (wave_tiles + NW - 1) / NW;
         const dim3 grid((unsigned)((int64_t)a.num_seqs * groups * a.num_kv_heads));
-        hipLaunchKernelGGL((paged_prefill_staged_kernel<KVT, QT, BS, kWavesPerGroup>), grid,
-                           dim3(kWavesPerGroup * kWave), 2 * stage_bytes(KVT), st, a, query_start, tt,
-                           groups);
+        hipLaunchKernelGGL((paged_prefill_staged_kernel<KVT, QT, BS, NW>), grid, dim3(NW * kWave),
+                           2 * stage_bytes(KVT), st, a, query_start, tt, groups);
         return hipGetLastError();
     }
     const size_t lds = sizeof(float) * merge_lds_floats(kWavesPerGroup, tile_tokens * a.group);
