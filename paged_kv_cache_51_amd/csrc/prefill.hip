@@ -96,7 +96,17 @@ __device__ __forceinline__ constexpr uint32_t ones2() {
 //     packed dot instructions;
 //   - waves whose tile sees fewer keys, or that have no tile, keep fetching
 //     and meeting the barriers; a wave's result needs no merge: it
-//     normalises its columns in registers and writes them out.
+//     normalises its columns in registers and writes them out;
+//   - work order: longest first.  A workgroup's time is about its
+//     sequence's context length, so the sequences are taken by descending
+//     context (each workgroup ranks them itself from context_lens) and,
+//     within one, the query tiles that see the most keys first; in the
+//     launch order of the grid's (sequence, group) items a band of 8 / H_kv
+//     sequences shares the groups round-robin, so that every workgroup of
+//     one (sequence, kv head) lands on the same XCD and its K / V stays in
+//     that XCD's L2 (blocks go to the XCDs in turn).  Ordered by group
+//     first, as before, contexts of 1-8K left most of the chip idle while
+//     the last long sequences ran (1.2-1.5x the balanced time).
 // Same arithmetic as decode otherwise: fp32 logits, log2-domain online
 // softmax with the lazy rescale, weights rounded to the query type.
 
@@ -225,6 +235,34 @@ __device__ __forceinline__ void staged_pair(MfmaMath<KVT, QT, 2>& mt, const uint
     }
 }
 
+// Sequences ranked above this count keep their own order (the ranking costs
+// each workgroup num_seqs^2 / 256 LDS reads).
+constexpr int kRankSeqsMax = 512;
+static_assert(2 * stage_bytes(DT_FP8) >= 4 * (kRankSeqsMax + 1), "the ranking borrows the stage area");
+
+// The sequence of rank `rank` when the sequences are ordered by descending
+// context length (ties by index).  Whole-workgroup call (barriers); `lds`
+// holds kRankSeqsMax + 1 ints and is free again on return.
+__device__ __forceinline__ int seq_of_rank(const DecodeArgs& a, int rank, int* lds) {
+    const int S = a.num_seqs;
+    if (S > kRankSeqsMax) return rank;
+    for (int i = threadIdx.x; i < S; i += blockDim.x) lds[i] = min(a.context_lens[i], a.ctx_cap);
+    __syncthreads();
+    for (int i = threadIdx.x; i < S; i += blockDim.x) {
+        const int ci = lds[i];
+        int r = 0;
+        for (int j = 0; j < S; ++j) {
+            const int cj = lds[j];
+            r += (cj > ci) | ((cj == ci) & (j < i));
+        }
+        if (r == rank) lds[kRankSeqsMax] = i;        // ranks are a permutation
+    }
+    __syncthreads();
+    const int s = lds[kRankSeqsMax];
+    __syncthreads();
+    return s;
+}
+
 // (two waves per SIMD: the register budget is kept at 256 per lane)
 #ifndef PKV_PREFILL_WAVES_PER_EU
 #define PKV_PREFILL_WAVES_PER_EU 2
@@ -245,10 +283,15 @@ void paged_prefill_staged_kernel(const DecodeArgs a, const int32_t* __restrict__
     uint8_t* stages = reinterpret_cast<uint8_t*>(pkv_smem);
     const int lane = threadIdx.x & (kWave - 1);
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int kvh = blockIdx.x % a.num_kv_heads;
-    const int rest = blockIdx.x / a.num_kv_heads;
-    const int grp = max_groups - 1 - rest / a.num_seqs;
-    const int s = rest % a.num_seqs;
+    const int Hkv = a.num_kv_heads;
+    const int kvh = blockIdx.x % Hkv;
+    const int item = blockIdx.x / Hkv;               // (sequence rank, group) item
+    const int P = (Hkv < 8 && 8 % Hkv == 0) ? 8 / Hkv : 1;
+    const int band = item / (P * max_groups);
+    const int in_band = item - band * P * max_groups;
+    const int bw = min(P, a.num_seqs - band * P);    // sequences in this band
+    const int grp = max_groups - 1 - in_band / bw;
+    const int s = seq_of_rank(a, band * P + in_band % bw, reinterpret_cast<int*>(pkv_smem));
     const int q0 = query_start[s];
     const int q_len = query_start[s + 1] - q0;
     const int g0 = grp * NW * tile_tokens;           // the workgroup's first token

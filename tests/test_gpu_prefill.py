@@ -126,6 +126,36 @@ def test_prefill_medium(kv, qdt, bs, H, Hkv):
     check(got, want, kv, f"G={G}")
 
 
+@pytest.mark.parametrize("H,Hkv", [(28, 4), (7, 1), (12, 3), (16, 2)])
+def test_prefill_work_order_tied_lengths(H, Hkv):
+    """The staged form takes sequences longest context first: equal context
+    lengths (ranked by index), a sequence count that leaves the last band of
+    sequences partial for every H_kv, and chunks of many sizes."""
+    lengths = [300, 300, 128, 700, 300, 700, 45, 128, 128, 900, 45, 300, 5]
+    q_lens = [300, 40, 128, 99, 17, 700, 45, 1, 64, 250, 3, 120, 5]
+    log(f"prefill work order H={H} Hkv={Hkv}")
+    tabs, kp, vp, qs, q = case(lengths, q_lens, H, Hkv, 16, oracle.BF16, oracle.BF16, seed=31 + Hkv)
+    want = oracle.paged_prefill(q, oracle.BF16, kp, vp, oracle.BF16, tabs.block_tables, tabs.context_lens,
+                                qs, Hkv, 16, SCALE)
+    got = gpu_prefill(tabs, kp, vp, qs, q, oracle.BF16, oracle.BF16, Hkv, 16)
+    check(got, want, oracle.BF16, f"H={H} Hkv={Hkv}")
+
+
+def test_prefill_many_sequences_keep_their_order():
+    """More sequences than the staged form ranks (512): they run in their own
+    order, with the same results."""
+    rng = np.random.default_rng(5)
+    S = 520
+    lengths = rng.integers(12, 80, S)
+    q_lens = np.minimum(lengths, rng.integers(1, 40, S))
+    log(f"prefill {S} sequences")
+    tabs, kp, vp, qs, q = case(lengths.tolist(), q_lens.tolist(), 28, 4, 16, oracle.BF16, oracle.BF16, seed=41)
+    want = oracle.paged_prefill(q, oracle.BF16, kp, vp, oracle.BF16, tabs.block_tables, tabs.context_lens,
+                                qs, 4, 16, SCALE)
+    got = gpu_prefill(tabs, kp, vp, qs, q, oracle.BF16, oracle.BF16, 4, 16)
+    check(got, want, oracle.BF16, f"S={S}")
+
+
 @pytest.mark.parametrize("kv,qdt,bs", [(oracle.BF16, oracle.BF16, 16), (oracle.FP8, oracle.FP16, 16)])
 def test_prefill_repeatable(kv, qdt, bs):
     """Two launches on the same inputs give the same bits: every step of the
