@@ -19,8 +19,36 @@ namespace pkv {
 // ctx - q_len + j and sees keys up to it.  The decode entry body serves it.
 // Tiles hold tile_tokens = 16 / G tokens (so the tile's (token, head) pairs
 // fill the 16 MFMA columns), and the last tiles of a chunk, which see the
-// most keys, are dispatched first.  No context split: the tiles give the
+// most keys, are dispatched first, sequences in the staged form's order
+// (longest context first, XCD bands).  No context split: the tiles give the
 // parallelism.  With q_len = 1 a tile is exactly a decode entry.
+// Sequences ranked above this count keep their own order (the ranking costs
+// each workgroup num_seqs^2 / 256 LDS reads).
+constexpr int kRankSeqsMax = 512;
+
+// The sequence of rank `rank` when the sequences are ordered by descending
+// context length (ties by index).  Whole-workgroup call (barriers); `lds`
+// holds kRankSeqsMax + 1 ints and is free again on return.
+__device__ __forceinline__ int seq_of_rank(const DecodeArgs& a, int rank, int* lds) {
+    const int S = a.num_seqs;
+    if (S > kRankSeqsMax) return rank;
+    for (int i = threadIdx.x; i < S; i += blockDim.x) lds[i] = min(a.context_lens[i], a.ctx_cap);
+    __syncthreads();
+    for (int i = threadIdx.x; i < S; i += blockDim.x) {
+        const int ci = lds[i];
+        int r = 0;
+        for (int j = 0; j < S; ++j) {
+            const int cj = lds[j];
+            r += (cj > ci) | ((cj == ci) & (j < i));
+        }
+        if (r == rank) lds[kRankSeqsMax] = i;        // ranks are a permutation
+    }
+    __syncthreads();
+    const int s = lds[kRankSeqsMax];
+    __syncthreads();
+    return s;
+}
+
 template <int KVT, int QT, int BS, int NW, int DEPTH>
 __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(PKV_WAVES_PER_EU)))
 void paged_prefill_mfma_kernel(const DecodeArgs a, const int32_t* __restrict__ query_start,
@@ -28,10 +56,15 @@ void paged_prefill_mfma_kernel(const DecodeArgs a, const int32_t* __restrict__ q
     extern __shared__ float pkv_smem[];
     const int lane = threadIdx.x & (kWave - 1);
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int kvh = blockIdx.x % a.num_kv_heads;
-    const int rest = blockIdx.x / a.num_kv_heads;
-    const int tile = max_tiles - 1 - rest / a.num_seqs;
-    const int s = rest % a.num_seqs;
+    const int Hkv = a.num_kv_heads;
+    const int kvh = blockIdx.x % Hkv;
+    const int item = blockIdx.x / Hkv;               // (sequence rank, tile) item
+    const int P = (Hkv < 8 && 8 % Hkv == 0) ? 8 / Hkv : 1;
+    const int band = item / (P * max_tiles);
+    const int in_band = item - band * P * max_tiles;
+    const int bw = min(P, a.num_seqs - band * P);    // sequences in this band
+    const int tile = max_tiles - 1 - in_band / bw;
+    const int s = seq_of_rank(a, band * P + in_band % bw, reinterpret_cast<int*>(pkv_smem));
     const int q0 = query_start[s];
     const int q_len = query_start[s + 1] - q0;
     const int j0 = tile * tile_tokens;
@@ -115,6 +148,7 @@ __device__ __forceinline__ constexpr uint32_t ones2() {
 __host__ __device__ constexpr int stage_bytes(int kvt) {
     return 2 * rows_per_sub(kvt) * 1024 + (kvt == DT_FP8 ? 2 * rows_per_sub(kvt) * 1024 : 8 * 1024);
 }
+static_assert(2 * stage_bytes(DT_FP8) >= 4 * (kRankSeqsMax + 1), "the ranking borrows the stage area");
 
 // One unit pair of a stage: logits, online softmax and PV for the wave's two
 // column tiles.  masked (uniform): apply each column's causal limit; pairs
@@ -233,34 +267,6 @@ __device__ __forceinline__ void staged_pair(MfmaMath<KVT, QT, 2>& mt, const uint
 #pragma unroll
         for (int t = 0; t < 2; ++t) mt.acc[t][nt] = mfma_16x16x32<QT>(vv, pf[t], mt.acc[t][nt]);
     }
-}
-
-// Sequences ranked above this count keep their own order (the ranking costs
-// each workgroup num_seqs^2 / 256 LDS reads).
-constexpr int kRankSeqsMax = 512;
-static_assert(2 * stage_bytes(DT_FP8) >= 4 * (kRankSeqsMax + 1), "the ranking borrows the stage area");
-
-// The sequence of rank `rank` when the sequences are ordered by descending
-// context length (ties by index).  Whole-workgroup call (barriers); `lds`
-// holds kRankSeqsMax + 1 ints and is free again on return.
-__device__ __forceinline__ int seq_of_rank(const DecodeArgs& a, int rank, int* lds) {
-    const int S = a.num_seqs;
-    if (S > kRankSeqsMax) return rank;
-    for (int i = threadIdx.x; i < S; i += blockDim.x) lds[i] = min(a.context_lens[i], a.ctx_cap);
-    __syncthreads();
-    for (int i = threadIdx.x; i < S; i += blockDim.x) {
-        const int ci = lds[i];
-        int r = 0;
-        for (int j = 0; j < S; ++j) {
-            const int cj = lds[j];
-            r += (cj > ci) | ((cj == ci) & (j < i));
-        }
-        if (r == rank) lds[kRankSeqsMax] = i;        // ranks are a permutation
-    }
-    __syncthreads();
-    const int s = lds[kRankSeqsMax];
-    __syncthreads();
-    return s;
 }
 
 // (two waves per SIMD: the register budget is kept at 256 per lane)
@@ -452,7 +458,8 @@ static hipError_t launch_prefill_t(const DecodeArgs& a, const int32_t* query_sta
                            2 * stage_bytes(KVT), st, a, query_start, tt, groups);
         return hipGetLastError();
     }
-    const size_t lds = sizeof(float) * merge_lds_floats(kWavesPerGroup, tile_tokens * a.group);
+    const size_t lds = std::max(sizeof(float) * merge_lds_floats(kWavesPerGroup, tile_tokens * a.group),
+                                sizeof(int) * (kRankSeqsMax + 1));
     const dim3 grid((unsigned)((int64_t)a.num_seqs * max_tiles * a.num_kv_heads));
     hipLaunchKernelGGL((paged_prefill_mfma_kernel<KVT, QT, BS, kWavesPerGroup, kDepth>), grid,
                        dim3(kWavesPerGroup * kWave), lds, st, a, query_start, tile_tokens, max_tiles);
