@@ -22,6 +22,10 @@ namespace pkv {
 // most keys, are dispatched first, sequences in the staged form's order
 // (longest context first, XCD bands).  No context split: the tiles give the
 // parallelism.  With q_len = 1 a tile is exactly a decode entry.
+#ifndef PKV_PREFILL_WG_NT2
+#define PKV_PREFILL_WG_NT2 1
+#endif
+
 // Sequences ranked above this count keep their own order (the ranking costs
 // each workgroup num_seqs^2 / 256 LDS reads).
 constexpr int kRankSeqsMax = 512;
@@ -49,7 +53,7 @@ __device__ __forceinline__ int seq_of_rank(const DecodeArgs& a, int rank, int* l
     return s;
 }
 
-template <int KVT, int QT, int BS, int NW, int DEPTH>
+template <int KVT, int QT, int BS, int NW, int DEPTH, int NT>
 __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(PKV_WAVES_PER_EU)))
 void paged_prefill_mfma_kernel(const DecodeArgs a, const int32_t* __restrict__ query_start,
                                int tile_tokens, int max_tiles) {
@@ -69,7 +73,7 @@ void paged_prefill_mfma_kernel(const DecodeArgs a, const int32_t* __restrict__ q
     const int q_len = query_start[s + 1] - q0;
     const int j0 = tile * tile_tokens;
     if (j0 >= q_len) return;
-    decode_entry<MfmaMath<KVT, QT>, KVT, QT, BS, NW, DEPTH>(
+    decode_entry<MfmaMath<KVT, QT, NT>, KVT, QT, BS, NW, DEPTH>(
         a, pkv_smem, s, 0, kvh, lane, w,
         QueryTile{(int64_t)q0 + j0, min(tile_tokens, q_len - j0), q_len - j0});
 }
@@ -458,10 +462,21 @@ static hipError_t launch_prefill_t(const DecodeArgs& a, const int32_t* query_sta
                            2 * stage_bytes(KVT), st, a, query_start, tt, groups);
         return hipGetLastError();
     }
+    if (PKV_PREFILL_WG_NT2 && max_tiles >= 2) {
+        // two 16-column tiles per workgroup: its K / V is read once for both
+        const int tt = 2 * tile_tokens;
+        const int tiles2 = (max_tiles + 1) / 2;
+        const size_t lds = std::max(sizeof(float) * merge_lds_floats(kWavesPerGroup, tt * a.group, 32),
+                                    sizeof(int) * (kRankSeqsMax + 1));
+        const dim3 grid((unsigned)((int64_t)a.num_seqs * tiles2 * a.num_kv_heads));
+        hipLaunchKernelGGL((paged_prefill_mfma_kernel<KVT, QT, BS, kWavesPerGroup, kDepth, 2>), grid,
+                           dim3(kWavesPerGroup * kWave), lds, st, a, query_start, tt, tiles2);
+        return hipGetLastError();
+    }
     const size_t lds = std::max(sizeof(float) * merge_lds_floats(kWavesPerGroup, tile_tokens * a.group),
                                 sizeof(int) * (kRankSeqsMax + 1));
     const dim3 grid((unsigned)((int64_t)a.num_seqs * max_tiles * a.num_kv_heads));
-    hipLaunchKernelGGL((paged_prefill_mfma_kernel<KVT, QT, BS, kWavesPerGroup, kDepth>), grid,
+    hipLaunchKernelGGL((paged_prefill_mfma_kernel<KVT, QT, BS, kWavesPerGroup, kDepth, 1>), grid,
                        dim3(kWavesPerGroup * kWave), lds, st, a, query_start, tile_tokens, max_tiles);
     return hipGetLastError();
 }
