@@ -126,8 +126,10 @@ __device__ __forceinline__ constexpr uint32_t ones2() {
 //     its eight k slots, in V (A operand) and P (B operand) alike;
 //   - pairs that every real column of the wave sees in full (all but the
 //     last one or two on the diagonal) skip the per-key causal and context
-//     masks; the logit scale is folded into the exponent (p = 2^(s*cs - m),
-//     the running max kept on scaled values); row maxima are reduced over
+//     masks; the logit scale is applied to the row maxima (max(s) * cs =
+//     max(s * cs) for cs > 0; a negative scale flips the query's signs) and
+//     folded into the exponent as one fused multiply-add, p = 2^(s*cs - m),
+//     with the running max m kept on scaled values; row maxima are reduced over
 //     the four 16-lane rows with the gfx950 permlane swaps (VALU, no LDS
 //     round trip); the normaliser is summed from the rounded weights with
 //     packed dot instructions;
@@ -202,14 +204,16 @@ __device__ __forceinline__ void staged_pair(MfmaMath<KVT, QT, 2>& mt, const uint
             vop[nt] = vl[nt * kWave];
         }
     }
-    // scaled logits (log2 units); keys a column must not see get -inf
+    // raw logits; the scale (cs > 0) goes into the maxima and into the
+    // exponent's fused multiply-add; keys a column must not see are -inf for
+    // the max and get weight 0 below
     float y[2][8];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) y[t][4 * u + i] = st[u][t][i] * cs;
+            for (int i = 0; i < 4; ++i) y[t][4 * u + i] = st[u][t][i];
     if (masked) {
         const int ta = tok0 + 4 * (lane >> 4);   // this lane's keys: ta..ta+3, ta+16..ta+19
 #pragma unroll
@@ -226,7 +230,8 @@ __device__ __forceinline__ void staged_pair(MfmaMath<KVT, QT, 2>& mt, const uint
     for (int t = 0; t < 2; ++t) {
         const float mx = fmaxf(fmaxf(fmaxf(y[t][0], y[t][1]), fmaxf(y[t][2], y[t][3])),
                                fmaxf(fmaxf(y[t][4], y[t][5]), fmaxf(y[t][6], y[t][7])));
-        bm[t] = rows_max(mx);
+        const float rm = rows_max(mx);
+        bm[t] = rm == -INFINITY ? -INFINITY : rm * cs;
         jump |= bm[t] > mt.m[t] + kRescaleSlack;
     }
     if (__builtin_amdgcn_ballot_w64(jump)) {
@@ -248,7 +253,11 @@ __device__ __forceinline__ void staged_pair(MfmaMath<KVT, QT, 2>& mt, const uint
         const float mref = mt.m[t] == -INFINITY ? 0.f : mt.m[t];
         float pv[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) pv[j] = fast_exp2(y[t][j] - mref);
+        for (int j = 0; j < 8; ++j) pv[j] = fast_exp2(fmaf(y[t][j], cs, -mref));
+        if (masked) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) pv[j] = y[t][j] == -INFINITY ? 0.f : pv[j];
+        }
 #pragma unroll
         for (int j = 0; j < 4; ++j) pf[t][j] = pack2<QT>(pv[2 * j], pv[2 * j + 1]);
         float lt = mt.l[t];
@@ -322,6 +331,16 @@ void paged_prefill_staged_kernel(const DecodeArgs a, const int32_t* __restrict__
     const int kv_end = has_tile ? min(ctx, pos0 + qt.ntok) : 0;
     mt.limit(pos0, G, lane);
     mt.begin();
+    // the scale is applied after the max, which needs it positive: a
+    // negative one flips the sign of every query element instead (exact)
+    float cs = a.qk_scale_log2;
+    if (cs < 0.f) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) mt.qf[t][kk] ^= 0x80008000u;
+        cs = -cs;
+    }
     const int n_pairs_w = kv_end > 0 ? (kv_end + 2 * kSubTokens - 1) / (2 * kSubTokens) : 0;
     const int n_free = pos0 + 1 >= kSubTokens ? (pos0 + 1) / kSubTokens : 0;
 
@@ -390,7 +409,6 @@ void paged_prefill_staged_kernel(const DecodeArgs a, const int32_t* __restrict__
                 }
             }
         };
-        const float cs = a.qk_scale_log2;
         auto compute = [&](int p, int st) {
             if (p < n_pairs_w)
                 staged_pair<KVT, QT>(mt, stages + st * SB, 2 * p * kSubTokens, 2 * p + 2 > n_free, cs, lane);

@@ -156,6 +156,26 @@ def test_prefill_many_sequences_keep_their_order():
     check(got, want, oracle.BF16, f"S={S}")
 
 
+@pytest.mark.parametrize("scale", [-SCALE, 0.0, 4.0 * SCALE])
+def test_prefill_staged_form_any_scale(scale):
+    """The staged form applies the scale after the row maxima: a negative
+    scale (query signs flipped), a zero scale (uniform weights over the
+    keys each token sees) and a large one agree with the oracle."""
+    lengths = [300, 77, 130]
+    q_lens = [120, 77, 33]
+    log(f"prefill staged scale={scale}")
+    tabs, kp, vp, qs, q = case(lengths, q_lens, 28, 4, 16, oracle.BF16, oracle.BF16, seed=51)
+    want = oracle.paged_prefill(q, oracle.BF16, kp, vp, oracle.BF16, tabs.block_tables, tabs.context_lens,
+                                qs, 4, 16, scale)
+    qt = dev16(q, oracle.BF16)
+    out = torch.full_like(qt, float("nan"))
+    pkv.paged_attention_prefill(out, qt, torch.from_numpy(kp).to(DEV), torch.from_numpy(vp).to(DEV),
+                                devi(tabs.block_tables), devi(tabs.context_lens), devi(qs), int(max(q_lens)),
+                                int(max(lengths)), 4, 16, oracle.BF16, scale, 1.0, 1.0)
+    torch.cuda.synchronize()
+    check(out.float().cpu().numpy().astype(np.float64), want, oracle.BF16, f"scale={scale}")
+
+
 @pytest.mark.parametrize("kv,qdt,bs", [(oracle.BF16, oracle.BF16, 16), (oracle.FP8, oracle.FP16, 16)])
 def test_prefill_repeatable(kv, qdt, bs):
     """Two launches on the same inputs give the same bits: every step of the
