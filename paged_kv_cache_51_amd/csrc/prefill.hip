@@ -156,14 +156,26 @@ __host__ __device__ constexpr int stage_bytes(int kvt) {
 }
 static_assert(2 * stage_bytes(DT_FP8) >= 4 * (kRankSeqsMax + 1), "the ranking borrows the stage area");
 
+// Type of the staged kernel's LDS stages: an fp8 pool is widened to the
+// query type by the stage writer (each wave converts its quarter of a pair
+// once, instead of every wave converting the whole pair for its MFMAs).
+#ifndef PKV_PREFILL_FP8_WIDEN
+#define PKV_PREFILL_FP8_WIDEN 1
+#endif
+__host__ __device__ constexpr int staged_kvt(int kvt, int qt) {
+    return (kvt == DT_FP8 && PKV_PREFILL_FP8_WIDEN) ? qt : kvt;
+}
+
 // One unit pair of a stage: logits, online softmax and PV for the wave's two
 // column tiles.  masked (uniform): apply each column's causal limit; pairs
 // every real column sees in full skip it.  V rows at or past the context
 // end arrive zeroed from the stage writer, so no V mask is needed here.
 // One code path: the branch covers only the logit select (a second copy of
 // the whole pair made the compiler copy the 64 accumulators every pair).
-template <int KVT, int QT>
-__device__ __forceinline__ void staged_pair(MfmaMath<KVT, QT, 2>& mt, const uint8_t* stage, int tok0,
+// KVT here is the type the stage holds (an fp8 pool is staged as fp8, or
+// already widened to the query type).
+template <int KVT, int QT, class Math>
+__device__ __forceinline__ void staged_pair(Math& mt, const uint8_t* stage, int tok0,
                                             bool masked, float cs, int lane) {
     constexpr int R = rows_per_sub(KVT);
     const u32x4_t* kl = reinterpret_cast<const u32x4_t*>(stage) + lane;
@@ -296,7 +308,9 @@ void paged_prefill_staged_kernel(const DecodeArgs a, const int32_t* __restrict__
     constexpr int R = rows_per_sub(KVT);
     constexpr int64_t SUB = sub_tile_bytes(KVT);
     constexpr int64_t TILE = SUB * NSUB;
-    constexpr int SB = stage_bytes(KVT);
+    constexpr int SKVT = staged_kvt(KVT, QT);         // what the stages hold
+    constexpr int SR = rows_per_sub(SKVT);
+    constexpr int SB = stage_bytes(SKVT);
     using Math = MfmaMath<KVT, QT, 2>;
     extern __shared__ float pkv_smem[];
     uint8_t* stages = reinterpret_cast<uint8_t*>(pkv_smem);
@@ -393,7 +407,26 @@ void paged_prefill_staged_kernel(const DecodeArgs a, const int32_t* __restrict__
                 }
             }
             uint8_t* base = stages + st * SB;
-            if (w < 2 || KVT == DT_FP8) {
+            if constexpr (SKVT != KVT) {
+                // fp8 pool widened here, once per pair: row i of K gives
+                // 16-bit rows 2i (its dims 0..7 per lane) and 2i + 1; dword d
+                // of V row i is dim tile 4i + d, stored as the 16-bit V path
+                // stores it
+                if (w < 2) {
+                    u32x4_t* d = reinterpret_cast<u32x4_t*>(base + (w & 1) * SR * 1024) + lane;
+#pragma unroll
+                    for (int i = 0; i < R; ++i) {
+                        d[kWave * (2 * i)] = e4m3x8_to_16<QT>(r[i][0], r[i][1]);
+                        d[kWave * (2 * i + 1)] = e4m3x8_to_16<QT>(r[i][2], r[i][3]);
+                    }
+                } else {
+                    u32x2_t* d = reinterpret_cast<u32x2_t*>(base + 2 * SR * 1024) + 2 * lane + (w & 1);
+#pragma unroll
+                    for (int i = 0; i < R; ++i)
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) d[2 * kWave * (4 * i + q)] = e4m3x4_to_16<QT>(r[i][q]);
+                }
+            } else if (w < 2 || KVT == DT_FP8) {
                 // K (or fp8 V) rows as in the pool: [unit][row][lane]
                 u32x4_t* d = reinterpret_cast<u32x4_t*>(base + (w >> 1) * 2 * R * 1024 + (w & 1) * R * 1024) + lane;
 #pragma unroll
@@ -411,7 +444,7 @@ void paged_prefill_staged_kernel(const DecodeArgs a, const int32_t* __restrict__
         };
         auto compute = [&](int p, int st) {
             if (p < n_pairs_w)
-                staged_pair<KVT, QT>(mt, stages + st * SB, 2 * p * kSubTokens, 2 * p + 2 > n_free, cs, lane);
+                staged_pair<SKVT, QT>(mt, stages + st * SB, 2 * p * kSubTokens, 2 * p + 2 > n_free, cs, lane);
         };
 
         u32x4_t r0[R], r1[R];
@@ -477,7 +510,7 @@ static hipError_t launch_prefill_t(const DecodeArgs& a, const int32_t* query_sta
         const int groups = (wave_tiles + NW - 1) / NW;
         const dim3 grid((unsigned)((int64_t)a.num_seqs * groups * a.num_kv_heads));
         hipLaunchKernelGGL((paged_prefill_staged_kernel<KVT, QT, BS, NW>), grid, dim3(NW * kWave),
-                           2 * stage_bytes(KVT), st, a, query_start, tt, groups);
+                           2 * stage_bytes(staged_kvt(KVT, QT)), st, a, query_start, tt, groups);
         return hipGetLastError();
     }
     if (PKV_PREFILL_WG_NT2 && max_tiles >= 2) {
