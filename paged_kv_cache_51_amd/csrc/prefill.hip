@@ -30,6 +30,16 @@ namespace pkv {
 // each workgroup num_seqs^2 / 256 LDS reads).
 constexpr int kRankSeqsMax = 512;
 
+// Rank of the sequence at slot j (0 <= j < bw) of band `band` (bands of P
+// sequences, bw of them in this band).  Slot j's workgroups all go to the
+// same XCDs; the slots alternate direction from band to band so that no XCD
+// gets the longer sequence of every band (with slot j = rank offset j,
+// XCDs 0-3 carried 12 % more work than XCDs 4-7 on 1-8K contexts and
+// finished 90 us later).
+__device__ __forceinline__ int band_rank(int band, int j, int P, int bw) {
+    return band * P + ((band & 1) ? bw - 1 - j : j);
+}
+
 // The sequence of rank `rank` when the sequences are ordered by descending
 // context length (ties by index).  Whole-workgroup call (barriers); `lds`
 // holds kRankSeqsMax + 1 ints and is free again on return.
@@ -68,7 +78,7 @@ void paged_prefill_mfma_kernel(const DecodeArgs a, const int32_t* __restrict__ q
     const int in_band = item - band * P * max_tiles;
     const int bw = min(P, a.num_seqs - band * P);    // sequences in this band
     const int tile = max_tiles - 1 - in_band / bw;
-    const int s = seq_of_rank(a, band * P + in_band % bw, reinterpret_cast<int*>(pkv_smem));
+    const int s = seq_of_rank(a, band_rank(band, in_band % bw, P, bw), reinterpret_cast<int*>(pkv_smem));
     const int q0 = query_start[s];
     const int q_len = query_start[s + 1] - q0;
     const int j0 = tile * tile_tokens;
@@ -143,7 +153,8 @@ __device__ __forceinline__ constexpr uint32_t ones2() {
 //     launch order of the grid's (sequence, group) items a band of 8 / H_kv
 //     sequences shares the groups round-robin, so that every workgroup of
 //     one (sequence, kv head) lands on the same XCD and its K / V stays in
-//     that XCD's L2 (blocks go to the XCDs in turn).  Ordered by group
+//     that XCD's L2 (blocks go to the XCDs in turn); successive bands run
+//     in alternating directions to even out the XCDs' work.  Ordered by group
 //     first, as before, contexts of 1-8K left most of the chip idle while
 //     the last long sequences ran (1.2-1.5x the balanced time).
 // Same arithmetic as decode otherwise: fp32 logits, log2-domain online
@@ -324,7 +335,7 @@ void paged_prefill_staged_kernel(const DecodeArgs a, const int32_t* __restrict__
     const int in_band = item - band * P * max_groups;
     const int bw = min(P, a.num_seqs - band * P);    // sequences in this band
     const int grp = max_groups - 1 - in_band / bw;
-    const int s = seq_of_rank(a, band * P + in_band % bw, reinterpret_cast<int*>(pkv_smem));
+    const int s = seq_of_rank(a, band_rank(band, in_band % bw, P, bw), reinterpret_cast<int*>(pkv_smem));
     const int q0 = query_start[s];
     const int q_len = query_start[s + 1] - q0;
     const int g0 = grp * NW * tile_tokens;           // the workgroup's first token
