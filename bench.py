@@ -213,6 +213,25 @@ def main():
           f"{dec_avg_ms * 1e3:.1f} us avg, {achieved:.0f} GB/s ({achieved / PEAK_HBM_GBS:.1%})",
           file=sys.stderr, flush=True)
 
+    # achievable figure: the library's streaming-read probe, one launch over
+    # a contiguous buffer of one decode launch's K / V bytes, outside the
+    # timed region
+    probe_bytes = (launch_bytes + 15) // 16 * 16
+    probe_src = torch.full((probe_bytes,), 1, dtype=torch.uint8, device=dev)
+    sink = pkv.read_probe(probe_src, stream=stream)
+    p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 5
+    torch.cuda.synchronize()
+    p0.record(stream)
+    for _ in range(reps):
+        pkv.read_probe(probe_src, sink=sink, stream=stream)
+    p1.record(stream)
+    torch.cuda.synchronize()
+    probe_gbs = probe_bytes * reps / (p0.elapsed_time(p1) * 1e-3) / 1e9
+    del sink, probe_src
+    print(f"[bench] read-stream probe: {probe_gbs:.0f} GB/s over {probe_bytes / 1e9:.2f} GB "
+          f"(decode kernel at {achieved / probe_gbs:.1%} of it)", file=sys.stderr, flush=True)
+
     if args.copy_probe_mib:
         n = args.copy_probe_mib << 20
         a = torch.empty(n, dtype=torch.uint8, device=dev)
@@ -271,6 +290,14 @@ def main():
             "traffic": traffic,
             "avg_launch_us": round(dec_avg_ms * 1e3, 2),
             "algorithmic_bytes_per_launch": launch_bytes,
+        },
+        "achievable": {
+            "kind": "read-stream probe (pkv_read_probe: non-temporal 16-byte loads, one contiguous "
+                    "slice per workgroup, two workgroups per CU), one launch over a contiguous "
+                    "buffer of one decode launch's bytes",
+            "gbs": round(probe_gbs, 1),
+            "bytes": probe_bytes,
+            "decode_frac_of_probe": round(achieved / probe_gbs, 4),
         },
         "cpu_baseline": cpu,
     }

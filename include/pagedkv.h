@@ -370,6 +370,27 @@ int32_t pkv_check_block_tables(const int32_t* block_tables,
                                int32_t* scratch_dev, int64_t* bad_count,
                                pkv_stream_t stream);
 
+/* ------------------------------------------------------------- measurement --
+ *
+ * Read-stream probe: the HBM read rate a plain stream reaches on this
+ * device, reported beside the decode kernel's rate as the achievable figure
+ * (the 8 TB/s peak is the vendor's).  Not part of the attention path.
+ *
+ * pkv_read_probe_sink_bytes: bytes of the sink buffer pkv_read_probe needs
+ * on the current device (one 16-byte word per probe thread).
+ *
+ * pkv_read_probe: reads the `bytes` bytes at device pointer `src` once
+ * (16-byte words, non-temporal loads, one contiguous slice per workgroup)
+ * and writes the XOR of each thread's words to device buffer `sink`; the
+ * XOR of all sink words equals the XOR of all source words.  bytes: a
+ * multiple of 16 (0: nothing runs); src and sink 16-byte aligned,
+ * caller-owned.  Asynchronous on `stream`.  Errors: PKV_ERR_ARG (null,
+ * alignment, bytes), PKV_ERR_SIZE (sink_bytes below the required size),
+ * PKV_ERR_HIP. */
+int64_t pkv_read_probe_sink_bytes(void);
+int32_t pkv_read_probe(const void* src, int64_t bytes, void* sink, int64_t sink_bytes,
+                       pkv_stream_t stream);
+
 /* ---------------------------------------------------------- block manager --
  *
  * Host-side block pool that produces the block tables and slots the calls

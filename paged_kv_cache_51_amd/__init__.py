@@ -15,4 +15,5 @@ from ._binding import (  # noqa: F401
     BlockManager, copy_blocks, paged_attention_prefill, paged_attention_decode_tokens,
     move_tokens,
     repack_blocks,
+    read_probe,
 )

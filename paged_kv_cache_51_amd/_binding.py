@@ -32,6 +32,7 @@ EXPORTS = [
     "pkv_copy_blocks", "paged_attention_prefill", "pkv_bm_evict_tokens", "pkv_bm_repack",
     "pkv_bm_token_slots", "paged_attention_decode_tokens", "pkv_move_tokens_scratch_bytes",
     "pkv_move_tokens", "pkv_bm_repack_tiles", "pkv_repack_blocks",
+    "pkv_read_probe_sink_bytes", "pkv_read_probe",
 ]
 
 
@@ -90,6 +91,8 @@ def lib():
                                                 ctypes.POINTER(DecodeOpts), p]),
             "pkv_check_block_tables": (i32, [p, i32, p, i32, i32, i32, p,
                                              ctypes.POINTER(ctypes.c_int64), p]),
+            "pkv_read_probe_sink_bytes": (i64, []),
+            "pkv_read_probe": (i32, [p, i64, p, i64, p]),
             "pkv_bm_create": (i32, [i32, i32, i32, ctypes.POINTER(p)]),
             "pkv_bm_destroy": (i32, [p]),
             "pkv_bm_num_free_blocks": (i32, [p]),
@@ -315,6 +318,18 @@ def check_block_tables(block_tables, context_lens, block_size, num_blocks, strea
         _ptr(context_lens, "context_lens", torch.int32), context_lens.shape[0], block_size,
         num_blocks, _ptr(scratch, "scratch"), ctypes.byref(bad), _stream(stream)))
     return int(bad.value)
+
+
+def read_probe(src, sink=None, stream=None):
+    """Read the bytes of device tensor `src` once with the library's
+    streaming-read probe (the achievable HBM read rate); returns the sink
+    tensor (allocated here unless given), one 16-byte XOR word per probe
+    thread."""
+    nbytes = src.numel() * src.element_size()
+    if sink is None:
+        sink = torch.empty(int(lib().pkv_read_probe_sink_bytes()), dtype=torch.uint8, device=src.device)
+    _check(lib().pkv_read_probe(_ptr(src, "src"), nbytes, _ptr(sink, "sink"), sink.numel(), _stream(stream)))
+    return sink
 
 
 class BlockManager:

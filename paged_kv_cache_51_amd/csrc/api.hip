@@ -595,4 +595,22 @@ int32_t pkv_check_block_tables(const int32_t* block_tables, int32_t max_blocks_p
     return ok();
 }
 
+int64_t pkv_read_probe_sink_bytes(void) { return pkv::read_probe_sink_bytes(); }
+
+int32_t pkv_read_probe(const void* src, int64_t bytes, void* sink, int64_t sink_bytes, pkv_stream_t stream) {
+    if (bytes < 0 || bytes % 16 != 0) return fail(PKV_ERR_ARG, "bytes %lld must be a non-negative multiple of 16",
+                                                  (long long)bytes);
+    if (bytes == 0) return ok();
+    if (!src || !sink) return fail(PKV_ERR_ARG, "null pointer");
+    if (((uintptr_t)src | (uintptr_t)sink) % 16 != 0) return fail(PKV_ERR_ARG, "src and sink must be 16-byte aligned");
+    const int64_t need = pkv::read_probe_sink_bytes();
+    if (sink_bytes < need)
+        return fail(PKV_ERR_SIZE, "sink holds %lld bytes, the probe needs %lld", (long long)sink_bytes,
+                    (long long)need);
+    (void)hipGetLastError();
+    hipError_t e = pkv::launch_read_probe(src, bytes / 16, sink, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "read probe launch");
+    return ok();
+}
+
 }  // extern "C"

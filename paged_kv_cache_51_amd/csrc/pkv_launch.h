@@ -64,6 +64,9 @@ hipError_t launch_plan(const int32_t* context_lens, int32_t num_seqs, int32_t ct
                        int32_t block_size, int32_t part_blocks, int32_t* plan, hipStream_t st);
 hipError_t launch_fill_pattern(void* p, int64_t n_bytes, uint32_t pattern, int pattern_bytes,
                                hipStream_t st);
+// Read-stream probe: sink holds read_probe_sink_bytes() bytes.
+int64_t read_probe_sink_bytes();
+hipError_t launch_read_probe(const void* src, int64_t n16, void* sink, hipStream_t st);
 
 // Partition kernel (matrix-core or vector implementation) and the merge.
 hipError_t launch_decode_partitions(const DecodeArgs& a, int q_dtype, int kv_dtype,
