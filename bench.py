@@ -201,6 +201,7 @@ def main():
     dec_avg_ms = float(np.mean(dec_ms))
 
     kv_bytes = int(ctx.astype(np.int64).sum()) * 2 * Hkv * D * b_kv
+    unique_kv_bytes = unique_kv_tokens(tabs.block_tables, ctx, bs, nb) * 2 * Hkv * D * b_kv
     qo_bytes = S * H * D * (2 + 2)
     new_bytes = S * Hkv * D * 2 * (2 + b_kv)
     step_bytes = L * (kv_bytes + qo_bytes + new_bytes)
@@ -209,8 +210,11 @@ def main():
     achieved = launch_bytes / (dec_avg_ms * 1e-3) / 1e9
     traffic_key = f"{args.config}-{kv_dtype}-bs{bs}-part{part_resolved}-impl{impl}"
     traffic = measured_traffic(traffic_key)
+    unique_gbs = (unique_kv_bytes + qo_bytes) / (dec_avg_ms * 1e-3) / 1e9
     print(f"[bench] step {step_ms:.3f} ms, {gbs:.0f} GB/s; partition kernel "
-          f"{dec_avg_ms * 1e3:.1f} us avg, {achieved:.0f} GB/s ({achieved / PEAK_HBM_GBS:.1%})",
+          f"{dec_avg_ms * 1e3:.1f} us avg, {achieved:.0f} GB/s ({achieved / PEAK_HBM_GBS:.1%})"
+          + (f"; unique K/V {unique_kv_bytes / 1e9:.3f} of {kv_bytes / 1e9:.3f} GB: "
+             f"{unique_gbs:.0f} GB/s" if unique_kv_bytes != kv_bytes else ""),
           file=sys.stderr, flush=True)
 
     # achievable figure: the library's streaming-read probe, one launch over
@@ -290,6 +294,11 @@ def main():
             "traffic": traffic,
             "avg_launch_us": round(dec_avg_ms * 1e3, 2),
             "algorithmic_bytes_per_launch": launch_bytes,
+        },
+        "unique_bytes": {
+            "kv_bytes_per_launch": unique_kv_bytes,
+            "gbs": round(unique_gbs, 1),
+            "note": "shared blocks counted once (equal to the logical bytes without sharing)",
         },
         "achievable": {
             "kind": "read-stream probe (pkv_read_probe: non-temporal 16-byte loads, one contiguous "
@@ -690,6 +699,21 @@ def _tokens_oracle_sample(n, kpool, vpool, q, slots, n_keep, q_dtype, kv, Hkv, b
     qb = q[:n].cpu().view(torch.int16).numpy().view(np.uint16)
     oracle.paged_decode_tokens(qb, _PKV2ORC[q_dtype], _host(kpool), _host(vpool), _PKV2ORC[kv],
                                slots[:n], n_keep[:n].astype(np.int32), Hkv, bs, scale, ks, vs)
+
+
+def unique_kv_tokens(block_tables, ctx, bs, num_blocks):
+    """Distinct pool slots a decode over these tables reads: a physical block
+    referenced by several sequences (a shared prefix) counts once, with the
+    most tokens any of them uses in it."""
+    ids, toks = [], []
+    for s, c in enumerate(np.asarray(ctx, dtype=np.int64)):
+        nblk = -(-int(c) // bs)
+        ids.append(block_tables[s, :nblk].astype(np.int64))
+        toks.append(np.minimum(bs, int(c) - bs * np.arange(nblk, dtype=np.int64)))
+    used = np.zeros(num_blocks, dtype=np.int64)
+    if ids:
+        np.maximum.at(used, np.concatenate(ids), np.concatenate(toks))
+    return int(used.sum())
 
 
 def cpu_baseline(args, tabs, kpool, vpool, q, q_dtype, kv_dtype, Hkv, bs, scale, ks, vs, b_kv,

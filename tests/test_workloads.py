@@ -57,3 +57,26 @@ def test_seeded_determinism():
     b = workloads.make("qwen15b", seed=3)
     assert np.array_equal(a[1].block_tables, b[1].block_tables)
     assert np.array_equal(a[2], b[2])
+
+
+def test_unique_kv_tokens_counts_shared_prefix_blocks_once():
+    """bench.py's unique-byte numerator: on the 1.5B workload the first 8
+    sequences share one 256-token prefix, so the distinct slots read are the
+    logical tokens less 7 x 256; without sharing they equal the logical
+    tokens; on the grouped-prefix workload every shared block is full, so
+    the distinct slots are the logical ones less (refs - 1) x block_size per
+    shared block."""
+    import bench
+    cfg, tabs, _, _ = workloads.make("qwen15b", seed=0)
+    ctx = tabs.context_lens
+    assert bench.unique_kv_tokens(tabs.block_tables, ctx, cfg.block_size, tabs.num_blocks) == \
+        int(ctx.sum()) - 7 * 256
+    cfg, tabs, _, _ = workloads.make("qwen7b", seed=0)
+    assert bench.unique_kv_tokens(tabs.block_tables, tabs.context_lens, cfg.block_size,
+                                  tabs.num_blocks) == int(tabs.context_lens.sum())
+    cfg, tabs, _, _ = workloads.make("llama7b", seed=0)
+    bs = cfg.block_size
+    saved = sum((len(m) - 1) * k * bs for m, k in tabs.groups)
+    assert saved > 0
+    assert bench.unique_kv_tokens(tabs.block_tables, tabs.context_lens, bs, tabs.num_blocks) == \
+        int(tabs.context_lens.sum()) - saved
