@@ -742,6 +742,16 @@ def cpu_baseline(args, tabs, kpool, vpool, q, q_dtype, kv_dtype, Hkv, bs, scale,
     qo = n * H * D * 4
     print(f"[bench] cpu oracle: {n} seqs in {tn:.1f}s on {threads} threads "
           f"(host copy {time.time() - t0 - tn - t1:.1f}s)", file=sys.stderr, flush=True)
+    # the same oracle on one core, over a sample of about a third of the time
+    oracle.set_threads(1)
+    try:
+        s1 = run(1)
+        n1 = int(min(n, max(1, args.cpu_baseline_seconds / 3 / max(s1, 1e-6))))
+        sn = run(n1) if n1 > 1 else s1
+    finally:
+        oracle.set_threads(threads)
+    kv1 = int(ctx[:n1].astype(np.int64).sum()) * 2 * Hkv * D * b_kv
+    print(f"[bench] cpu oracle, one core: {n1} seqs in {sn:.1f}s", file=sys.stderr, flush=True)
     return {
         "value": round((kv + qo) / tn / 1e9, 4),
         "unit": "GB/s",
@@ -751,6 +761,14 @@ def cpu_baseline(args, tabs, kpool, vpool, q, q_dtype, kv_dtype, Hkv, bs, scale,
                   f"context tokens), fp64 C oracle, OpenMP over (seq, head)",
         "seq_layers_per_s": round(n / tn, 3),
         "seconds": round(tn, 2),
+        "single_core": {
+            "value": round((kv1 + n1 * H * D * 4) / sn / 1e9, 4),
+            "unit": "GB/s",
+            "cores": 1,
+            "sample": f"layer 0, first {n1} sequences ({int(ctx[:n1].sum())} context tokens)",
+            "seq_layers_per_s": round(n1 / sn, 3),
+            "seconds": round(sn, 2),
+        },
     }
 
 
