@@ -8,6 +8,8 @@
 // 0..ctx - q_len + j, read through the block table exactly as in decode.
 // The per-unit arithmetic is the decode kernel's (decode_core.h,
 // mfma_math.h) with the query columns (token, head) pairs.
+#include <type_traits>
+
 #include "decode_core.h"
 #include "mfma_math.h"
 
@@ -167,15 +169,17 @@ __host__ __device__ constexpr int stage_bytes(int kvt) {
 }
 static_assert(2 * stage_bytes(DT_FP8) >= 4 * (kRankSeqsMax + 1), "the ranking borrows the stage area");
 
-// Type of the staged kernel's LDS stages: an fp8 pool is widened to the
-// query type by the stage writer (each wave converts its quarter of a pair
-// once, instead of every wave converting the whole pair for its MFMAs).
-#ifndef PKV_PREFILL_FP8_WIDEN
-#define PKV_PREFILL_FP8_WIDEN 1
-#endif
-__host__ __device__ constexpr int staged_kvt(int kvt, int qt) {
-    return (kvt == DT_FP8 && PKV_PREFILL_FP8_WIDEN) ? qt : kvt;
+// Type of the staged kernel's LDS stages.  With `widen`, an fp8 pool is
+// widened to the query type by the stage writer (each wave converts its
+// quarter of a pair once, instead of every wave converting the whole pair
+// for its MFMAs).  Measured either way, same code otherwise: widening is
+// 3-3.5 % faster on 32K contexts (72B shape, 64- to 512-token chunks) but
+// 2-9 % slower on 1-8K contexts at 64- to 256-token chunks (7B shape; 2.7 %
+// faster at 512); the launcher widens above kWidenMinContext.
+__host__ __device__ constexpr int staged_kvt(int kvt, int qt, bool widen) {
+    return (kvt == DT_FP8 && widen) ? qt : kvt;
 }
+constexpr int kWidenMinContext = 16384;
 
 // One unit pair of a stage: logits, online softmax and PV for the wave's two
 // column tiles.  masked (uniform): apply each column's causal limit; pairs
@@ -310,7 +314,7 @@ __device__ __forceinline__ void staged_pair(Math& mt, const uint8_t* stage, int 
 #define PKV_PREFILL_WAVES_PER_EU 2
 #endif
 
-template <int KVT, int QT, int BS, int NW>
+template <int KVT, int QT, int BS, int NW, bool WIDEN>
 __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(PKV_PREFILL_WAVES_PER_EU)))
 void paged_prefill_staged_kernel(const DecodeArgs a, const int32_t* __restrict__ query_start,
                                  int tile_tokens, int max_groups) {
@@ -319,7 +323,7 @@ void paged_prefill_staged_kernel(const DecodeArgs a, const int32_t* __restrict__
     constexpr int R = rows_per_sub(KVT);
     constexpr int64_t SUB = sub_tile_bytes(KVT);
     constexpr int64_t TILE = SUB * NSUB;
-    constexpr int SKVT = staged_kvt(KVT, QT);         // what the stages hold
+    constexpr int SKVT = staged_kvt(KVT, QT, WIDEN);  // what the stages hold
     constexpr int SR = rows_per_sub(SKVT);
     constexpr int SB = stage_bytes(SKVT);
     using Math = MfmaMath<KVT, QT, 2>;
@@ -520,8 +524,17 @@ static hipError_t launch_prefill_t(const DecodeArgs& a, const int32_t* query_sta
         const int wave_tiles = (max_tiles * tile_tokens + tt - 1) / tt;
         const int groups = (wave_tiles + NW - 1) / NW;
         const dim3 grid((unsigned)((int64_t)a.num_seqs * groups * a.num_kv_heads));
-        hipLaunchKernelGGL((paged_prefill_staged_kernel<KVT, QT, BS, NW>), grid, dim3(NW * kWave),
-                           2 * stage_bytes(staged_kvt(KVT, QT)), st, a, query_start, tt, groups);
+        auto go = [&](auto widen) {
+            constexpr bool W = decltype(widen)::value;
+            hipLaunchKernelGGL((paged_prefill_staged_kernel<KVT, QT, BS, NW, W>), grid, dim3(NW * kWave),
+                               2 * stage_bytes(staged_kvt(KVT, QT, W)), st, a, query_start, tt, groups);
+        };
+        if constexpr (KVT == DT_FP8) {
+            if (a.ctx_cap > kWidenMinContext) go(std::true_type{});
+            else go(std::false_type{});
+        } else {
+            go(std::false_type{});
+        }
         return hipGetLastError();
     }
     if (PKV_PREFILL_WG_NT2 && max_tiles >= 2) {

@@ -176,6 +176,48 @@ def test_prefill_staged_form_any_scale(scale):
     check(out.float().cpu().numpy().astype(np.float64), want, oracle.BF16, f"scale={scale}")
 
 
+@pytest.mark.parametrize("qdt,bs", [(oracle.BF16, 16), (oracle.FP16, 32)])
+def test_prefill_fp8_both_stage_forms(qdt, bs):
+    """fp8 pools in the staged form: kept fp8 in LDS (maximum context up to
+    16K) and widened to the query type by the stage writer (above 16K,
+    selected here by a longer table and maximum context over the same
+    short sequences): both equal the oracle, and each other bit for bit."""
+    lengths = [700, 333, 1025, 96]
+    q_lens = [300, 77, 512, 96]
+    ks, vs = 0.02, 0.03
+    tabs, kp, vp, qs, q = case(lengths, q_lens, 16, 2, bs, oracle.FP8, qdt, seed=61, ks=ks, vs=vs)
+    want = oracle.paged_prefill(q, qdt, kp, vp, oracle.FP8, tabs.block_tables, tabs.context_lens, qs,
+                                2, bs, SCALE, ks, vs)
+    wide = 20000 // bs + 1
+    bt = np.zeros((len(lengths), wide), dtype=np.int32)
+    bt[:, :tabs.block_tables.shape[1]] = tabs.block_tables
+    outs = []
+    for max_ctx, table in [(int(max(lengths)), tabs.block_tables), (20000, bt)]:
+        qt = dev16(q, qdt)
+        out = torch.full_like(qt, float("nan"))
+        pkv.paged_attention_prefill(out, qt, torch.from_numpy(kp).to(DEV), torch.from_numpy(vp).to(DEV),
+                                    devi(table), devi(tabs.context_lens), devi(qs), int(max(q_lens)), max_ctx,
+                                    2, bs, oracle.FP8, SCALE, ks, vs)
+        torch.cuda.synchronize()
+        outs.append(out.float().cpu().numpy().astype(np.float64))
+        check(outs[-1], want, oracle.FP8, f"max_ctx={max_ctx}")
+    assert np.array_equal(outs[0], outs[1])
+
+
+def test_prefill_fp8_long_context_widened():
+    """One sequence of 17,000 keys (fp8 widened in the stage writer) with a
+    chunk of 24 new tokens, beside a short one."""
+    lengths = [17000, 90]
+    q_lens = [24, 90]
+    ks, vs = 0.02, 0.03
+    log("prefill fp8 17K context")
+    tabs, kp, vp, qs, q = case(lengths, q_lens, 16, 2, 16, oracle.FP8, oracle.BF16, seed=71, ks=ks, vs=vs)
+    want = oracle.paged_prefill(q, oracle.BF16, kp, vp, oracle.FP8, tabs.block_tables, tabs.context_lens,
+                                qs, 2, 16, SCALE, ks, vs)
+    got = gpu_prefill(tabs, kp, vp, qs, q, oracle.BF16, oracle.FP8, 2, 16, ks, vs)
+    check(got, want, oracle.FP8, "17K fp8")
+
+
 @pytest.mark.parametrize("kv,qdt,bs", [(oracle.BF16, oracle.BF16, 16), (oracle.FP8, oracle.FP16, 16)])
 def test_prefill_repeatable(kv, qdt, bs):
     """Two launches on the same inputs give the same bits: every step of the
