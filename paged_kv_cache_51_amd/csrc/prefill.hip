@@ -193,14 +193,15 @@ template <int KVT, int QT, class Math>
 __device__ __forceinline__ void staged_pair(Math& mt, const uint8_t* stage, int tok0,
                                             bool masked, float cs, int lane) {
     constexpr int R = rows_per_sub(KVT);
+    constexpr int NT = Math::kCols / 16;           // 16-column tiles of the wave
     const u32x4_t* kl = reinterpret_cast<const u32x4_t*>(stage) + lane;
     const u32x4_t* vl = reinterpret_cast<const u32x4_t*>(stage + 2 * R * 1024) + lane;
     // logits
-    f32x4_t st[2][2];
+    f32x4_t st[2][NT];
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int t = 0; t < 2; ++t) st[u][t] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+        for (int t = 0; t < NT; ++t) st[u][t] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
         u32x4_t k[2];
@@ -214,7 +215,7 @@ __device__ __forceinline__ void staged_pair(Math& mt, const uint8_t* stage, int 
             }
         }
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
+        for (int t = 0; t < NT; ++t) {
             st[0][t] = mfma_16x16x32<QT>(k[0], mt.qf[t][kk], st[0][t]);
             st[1][t] = mfma_16x16x32<QT>(k[1], mt.qf[t][kk], st[1][t]);
         }
@@ -234,9 +235,9 @@ __device__ __forceinline__ void staged_pair(Math& mt, const uint8_t* stage, int 
     // raw logits; the scale (cs > 0) goes into the maxima and into the
     // exponent's fused multiply-add; keys a column must not see are -inf for
     // the max and get weight 0 below
-    float y[2][8];
+    float y[NT][8];
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
@@ -244,17 +245,17 @@ __device__ __forceinline__ void staged_pair(Math& mt, const uint8_t* stage, int 
     if (masked) {
         const int ta = tok0 + 4 * (lane >> 4);   // this lane's keys: ta..ta+3, ta+16..ta+19
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+        for (int t = 0; t < NT; ++t)
 #pragma unroll
             for (int u = 0; u < 2; ++u)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     y[t][4 * u + i] = (ta + 16 * u + i) < mt.lim[t] ? y[t][4 * u + i] : -INFINITY;
     }
-    float bm[2];
+    float bm[NT];
     bool jump = false;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int t = 0; t < NT; ++t) {
         const float mx = fmaxf(fmaxf(fmaxf(y[t][0], y[t][1]), fmaxf(y[t][2], y[t][3])),
                                fmaxf(fmaxf(y[t][4], y[t][5]), fmaxf(y[t][6], y[t][7])));
         const float rm = rows_max(mx);
@@ -263,7 +264,7 @@ __device__ __forceinline__ void staged_pair(Math& mt, const uint8_t* stage, int 
     }
     if (__builtin_amdgcn_ballot_w64(jump)) {
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
+        for (int t = 0; t < NT; ++t) {
             const float mn = fmaxf(mt.m[t], bm[t]);
             const float alpha = (mt.m[t] == -INFINITY) ? 0.f : fast_exp2(mt.m[t] - mn);
             mt.l[t] *= alpha;
@@ -272,9 +273,9 @@ __device__ __forceinline__ void staged_pair(Math& mt, const uint8_t* stage, int 
             mt.m[t] = mn;
         }
     }
-    u32x4_t pf[2];
+    u32x4_t pf[NT];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int t = 0; t < NT; ++t) {
         // 2^(-inf - m) = 0 for masked keys; a column that has seen no key
         // yet (m = -inf) subtracts 0 instead, and all its keys are -inf
         const float mref = mt.m[t] == -INFINITY ? 0.f : mt.m[t];
@@ -305,17 +306,25 @@ __device__ __forceinline__ void staged_pair(Math& mt, const uint8_t* stage, int 
             vv = vop[nt];
         }
 #pragma unroll
-        for (int t = 0; t < 2; ++t) mt.acc[t][nt] = mfma_16x16x32<QT>(vv, pf[t], mt.acc[t][nt]);
+        for (int t = 0; t < NT; ++t) mt.acc[t][nt] = mfma_16x16x32<QT>(vv, pf[t], mt.acc[t][nt]);
     }
 }
+
+// 16-column tiles per wave of the staged form: 2 (two waves per SIMD).  4
+// tiles (64 columns, half the LDS reads and barriers per MFMA) need 333
+// VGPRs, one wave per SIMD, and measured 35-55 % slower on the multi-token
+// workloads: the second wave is what hides each wave's latencies.
+#ifndef PKV_PREFILL_TILES_PER_WAVE
+#define PKV_PREFILL_TILES_PER_WAVE 2
+#endif
 
 // (two waves per SIMD: the register budget is kept at 256 per lane)
 #ifndef PKV_PREFILL_WAVES_PER_EU
 #define PKV_PREFILL_WAVES_PER_EU 2
 #endif
 
-template <int KVT, int QT, int BS, int NW, bool WIDEN>
-__global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(PKV_PREFILL_WAVES_PER_EU)))
+template <int KVT, int QT, int BS, int NW, bool WIDEN, int NT>
+__global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(NT == 2 ? PKV_PREFILL_WAVES_PER_EU : 1)))
 void paged_prefill_staged_kernel(const DecodeArgs a, const int32_t* __restrict__ query_start,
                                  int tile_tokens, int max_groups) {
     static_assert(NW == 4, "one pool-row quarter of a unit pair per wave");
@@ -326,7 +335,7 @@ void paged_prefill_staged_kernel(const DecodeArgs a, const int32_t* __restrict__
     constexpr int SKVT = staged_kvt(KVT, QT, WIDEN);  // what the stages hold
     constexpr int SR = rows_per_sub(SKVT);
     constexpr int SB = stage_bytes(SKVT);
-    using Math = MfmaMath<KVT, QT, 2>;
+    using Math = MfmaMath<KVT, QT, NT>;
     extern __shared__ float pkv_smem[];
     uint8_t* stages = reinterpret_cast<uint8_t*>(pkv_smem);
     const int lane = threadIdx.x & (kWave - 1);
@@ -365,7 +374,7 @@ void paged_prefill_staged_kernel(const DecodeArgs a, const int32_t* __restrict__
     float cs = a.qk_scale_log2;
     if (cs < 0.f) {
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+        for (int t = 0; t < NT; ++t)
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) mt.qf[t][kk] ^= 0x80008000u;
         cs = -cs;
@@ -491,7 +500,7 @@ void paged_prefill_staged_kernel(const DecodeArgs a, const int32_t* __restrict__
     // tile t; lane group g holds dims 16nt + 4g .. +3)
     const int g = lane >> 4;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int t = 0; t < NT; ++t) {
         float L = mt.l[t];
         {
             const auto a16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(L), __float_as_uint(L), false, false);
@@ -518,15 +527,16 @@ template <int KVT, int QT, int BS>
 static hipError_t launch_prefill_t(const DecodeArgs& a, const int32_t* query_start, int tile_tokens,
                                    int max_tiles, hipStream_t st) {
     if (max_tiles > kWavesPerGroup) {
-        // staged form: 32 columns (two 16-column tiles) per wave, four waves
+        // staged form: 16 * NT columns (NT 16-column tiles) per wave, four waves
         constexpr int NW = 4;
-        const int tt = 2 * tile_tokens;
+        constexpr int NT = PKV_PREFILL_TILES_PER_WAVE;
+        const int tt = NT * tile_tokens;
         const int wave_tiles = (max_tiles * tile_tokens + tt - 1) / tt;
         const int groups = (wave_tiles + NW - 1) / NW;
         const dim3 grid((unsigned)((int64_t)a.num_seqs * groups * a.num_kv_heads));
         auto go = [&](auto widen) {
             constexpr bool W = decltype(widen)::value;
-            hipLaunchKernelGGL((paged_prefill_staged_kernel<KVT, QT, BS, NW, W>), grid, dim3(NW * kWave),
+            hipLaunchKernelGGL((paged_prefill_staged_kernel<KVT, QT, BS, NW, W, NT>), grid, dim3(NW * kWave),
                                2 * stage_bytes(staged_kvt(KVT, QT, W)), st, a, query_start, tt, groups);
         };
         if constexpr (KVT == DT_FP8) {
