@@ -189,7 +189,11 @@ constexpr int kWidenMinContext = 16384;
 // the whole pair made the compiler copy the 64 accumulators every pair).
 // KVT here is the type the stage holds (an fp8 pool is staged as fp8, or
 // already widened to the query type).
-template <int KVT, int QT, class Math>
+//
+// LATE_V: read the PV operands right before the PV MFMAs instead of before
+// the softmax (fewer registers live through the softmax: what lets the fp8
+// form run three waves per SIMD).
+template <int KVT, int QT, bool LATE_V, class Math>
 __device__ __forceinline__ void staged_pair(Math& mt, const uint8_t* stage, int tok0,
                                             bool masked, float cs, int lane) {
     constexpr int R = rows_per_sub(KVT);
@@ -222,16 +226,19 @@ __device__ __forceinline__ void staged_pair(Math& mt, const uint8_t* stage, int 
     }
     // PV operands, read before the softmax so their LDS latency hides behind
     // it (the rescale branch below ends the scheduler's region)
-    u32x4_t vop[8];
+    auto read_v = [&](u32x4_t (&vop)[8]) {
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) {
-        if constexpr (KVT == DT_FP8) {
-            // fp8 rows hold four dim tiles each; widened when used
-            vop[nt] = nt < 2 * R ? vl[((nt >> 1) + R * (nt & 1)) * kWave] : (u32x4_t){0u, 0u, 0u, 0u};
-        } else {
-            vop[nt] = vl[nt * kWave];
+        for (int nt = 0; nt < 8; ++nt) {
+            if constexpr (KVT == DT_FP8) {
+                // fp8 rows hold four dim tiles each; widened when used
+                vop[nt] = nt < 2 * R ? vl[((nt >> 1) + R * (nt & 1)) * kWave] : (u32x4_t){0u, 0u, 0u, 0u};
+            } else {
+                vop[nt] = vl[nt * kWave];
+            }
         }
-    }
+    };
+    u32x4_t vop[8];
+    if constexpr (!LATE_V) read_v(vop);
     // raw logits; the scale (cs > 0) goes into the maxima and into the
     // exponent's fused multiply-add; keys a column must not see are -inf for
     // the max and get weight 0 below
@@ -294,6 +301,7 @@ __device__ __forceinline__ void staged_pair(Math& mt, const uint8_t* stage, int 
         mt.l[t] = lt;
     }
     // PV
+    if constexpr (LATE_V) read_v(vop);
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) {
         u32x4_t vv;
@@ -323,8 +331,16 @@ __device__ __forceinline__ void staged_pair(Math& mt, const uint8_t* stage, int 
 #define PKV_PREFILL_WAVES_PER_EU 2
 #endif
 
+// Waves per SIMD of the staged form: fp8 pools fit three (168 VGPRs, with
+// the PV operands read late and a one-pair fetch ring); 16-bit pools keep
+// two (a 16-bit pair is twice the fetch registers: 32 VGPRs would spill).
+template <int KVT, int NT>
+__host__ __device__ constexpr int staged_waves_per_eu() {
+    return NT != 2 ? 1 : (KVT == DT_FP8 ? 3 : PKV_PREFILL_WAVES_PER_EU);
+}
+
 template <int KVT, int QT, int BS, int NW, bool WIDEN, int NT>
-__global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(NT == 2 ? PKV_PREFILL_WAVES_PER_EU : 1)))
+__global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(staged_waves_per_eu<KVT, NT>())))
 void paged_prefill_staged_kernel(const DecodeArgs a, const int32_t* __restrict__ query_start,
                                  int tile_tokens, int max_groups) {
     static_assert(NW == 4, "one pool-row quarter of a unit pair per wave");
@@ -333,6 +349,7 @@ void paged_prefill_staged_kernel(const DecodeArgs a, const int32_t* __restrict__
     constexpr int64_t SUB = sub_tile_bytes(KVT);
     constexpr int64_t TILE = SUB * NSUB;
     constexpr int SKVT = staged_kvt(KVT, QT, WIDEN);  // what the stages hold
+    constexpr bool kThree = staged_waves_per_eu<KVT, NT>() == 3;
     constexpr int SR = rows_per_sub(SKVT);
     constexpr int SB = stage_bytes(SKVT);
     using Math = MfmaMath<KVT, QT, NT>;
@@ -468,31 +485,51 @@ void paged_prefill_staged_kernel(const DecodeArgs a, const int32_t* __restrict__
         };
         auto compute = [&](int p, int st) {
             if (p < n_pairs_w)
-                staged_pair<SKVT, QT>(mt, stages + st * SB, 2 * p * kSubTokens, 2 * p + 2 > n_free, cs, lane);
+                staged_pair<SKVT, QT, kThree>(mt, stages + st * SB, 2 * p * kSubTokens, 2 * p + 2 > n_free, cs,
+                                             lane);
         };
 
-        u32x4_t r0[R], r1[R];
-        fetch(r0, 0);
-        fetch(r1, 1);
-        int id3 = id_load(3), id4 = id_load(4);
-        stage_write(r0, 0, 0);
-        fetch(r0, 2);
-        __syncthreads();
         // Fetches, stage writes and barriers are unconditional (indices past
         // the last pair repeat it; compute skips pairs the wave does not
         // see), so the load counters the compiler waits on stay static: a
         // stage write waits only for its own pair, not for the one behind.
-        for (int p = 0; p < n_pairs; p += 2) {
-            compute(p, 0);
-            stage_write(r1, 1, p + 1);
-            fetch_at(r1, p + 3, __builtin_amdgcn_readfirstlane(id3));
-            id3 = id_load(p + 5);
+        if constexpr (kThree) {
+            // one pair in flight in registers (three waves per SIMD hide
+            // the shorter lead)
+            u32x4_t r0[R];
+            fetch(r0, 0);
+            int id2 = id_load(2);
+            stage_write(r0, 0, 0);
+            fetch(r0, 1);
             __syncthreads();
-            compute(p + 1, 1);
-            stage_write(r0, 0, p + 2);
-            fetch_at(r0, p + 4, __builtin_amdgcn_readfirstlane(id4));
-            id4 = id_load(p + 6);
+            for (int p = 0; p < n_pairs; ++p) {
+                compute(p, p & 1);
+                stage_write(r0, (p + 1) & 1, p + 1);
+                fetch_at(r0, p + 2, __builtin_amdgcn_readfirstlane(id2));
+                id2 = id_load(p + 3);
+                __syncthreads();
+            }
+        } else {
+            // two pairs in flight in registers
+            u32x4_t r0[R], r1[R];
+            fetch(r0, 0);
+            fetch(r1, 1);
+            int id3 = id_load(3), id4 = id_load(4);
+            stage_write(r0, 0, 0);
+            fetch(r0, 2);
             __syncthreads();
+            for (int p = 0; p < n_pairs; p += 2) {
+                compute(p, 0);
+                stage_write(r1, 1, p + 1);
+                fetch_at(r1, p + 3, __builtin_amdgcn_readfirstlane(id3));
+                id3 = id_load(p + 5);
+                __syncthreads();
+                compute(p + 1, 1);
+                stage_write(r0, 0, p + 2);
+                fetch_at(r0, p + 4, __builtin_amdgcn_readfirstlane(id4));
+                id4 = id_load(p + 6);
+                __syncthreads();
+            }
         }
     }
     if (!has_tile) return;
