@@ -191,11 +191,13 @@ constexpr int kWidenMinContext = 16384;
 // already widened to the query type).
 //
 // LATE_V: read the PV operands right before the PV MFMAs instead of before
-// the softmax (fewer registers live through the softmax: what lets the fp8
-// form run three waves per SIMD).
-template <int KVT, int QT, bool LATE_V, class Math>
+// the softmax (fewer registers live through the softmax: what lets the
+// staged form run three waves per SIMD).  QLDS: this lane's query
+// fragments of k steps 2 and 3 come from LDS (entry [t][kk - 2] at
+// qhi[(2t + kk - 2) * 64]) instead of registers.
+template <int KVT, int QT, bool LATE_V, bool QLDS, class Math>
 __device__ __forceinline__ void staged_pair(Math& mt, const uint8_t* stage, int tok0,
-                                            bool masked, float cs, int lane) {
+                                            bool masked, float cs, int lane, const u32x4_t* qhi) {
     constexpr int R = rows_per_sub(KVT);
     constexpr int NT = Math::kCols / 16;           // 16-column tiles of the wave
     const u32x4_t* kl = reinterpret_cast<const u32x4_t*>(stage) + lane;
@@ -220,8 +222,11 @@ __device__ __forceinline__ void staged_pair(Math& mt, const uint8_t* stage, int 
         }
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            st[0][t] = mfma_16x16x32<QT>(k[0], mt.qf[t][kk], st[0][t]);
-            st[1][t] = mfma_16x16x32<QT>(k[1], mt.qf[t][kk], st[1][t]);
+            u32x4_t qv;
+            if constexpr (QLDS) qv = kk >= 2 ? qhi[(2 * t + kk - 2) * kWave] : mt.qf[t][kk];
+            else qv = mt.qf[t][kk];
+            st[0][t] = mfma_16x16x32<QT>(k[0], qv, st[0][t]);
+            st[1][t] = mfma_16x16x32<QT>(k[1], qv, st[1][t]);
         }
     }
     // PV operands, read before the softmax so their LDS latency hides behind
@@ -331,12 +336,26 @@ __device__ __forceinline__ void staged_pair(Math& mt, const uint8_t* stage, int 
 #define PKV_PREFILL_WAVES_PER_EU 2
 #endif
 
-// Waves per SIMD of the staged form: fp8 pools fit three (168 VGPRs, with
-// the PV operands read late and a one-pair fetch ring); 16-bit pools keep
-// two (a 16-bit pair is twice the fetch registers: 32 VGPRs would spill).
+// Waves per SIMD of the staged form: three (168 VGPRs), with the PV
+// operands read late and a one-pair fetch ring; 16-bit pools (twice the
+// fetch registers of fp8) also keep half of the query fragments in LDS.
+#ifndef PKV_PREFILL_THREE_WAVES_16BIT
+#define PKV_PREFILL_THREE_WAVES_16BIT 1
+#endif
 template <int KVT, int NT>
 __host__ __device__ constexpr int staged_waves_per_eu() {
-    return NT != 2 ? 1 : (KVT == DT_FP8 ? 3 : PKV_PREFILL_WAVES_PER_EU);
+    return NT != 2 ? 1 : ((KVT == DT_FP8 || PKV_PREFILL_THREE_WAVES_16BIT) ? 3 : PKV_PREFILL_WAVES_PER_EU);
+}
+// query fragments of k steps 2, 3 in LDS: 16-bit pools at three waves
+template <int KVT, int NT>
+__host__ __device__ constexpr bool staged_q_in_lds() {
+    return staged_waves_per_eu<KVT, NT>() == 3 && KVT != DT_FP8;
+}
+// LDS bytes of the staged form: two stages, then per wave its query half
+// (two tiles x two k steps x 64 lanes x 16 B)
+template <int KVT, int QT, int NT, bool WIDEN>
+__host__ __device__ constexpr int staged_lds_bytes(int nw) {
+    return 2 * stage_bytes(staged_kvt(KVT, QT, WIDEN)) + (staged_q_in_lds<KVT, NT>() ? nw * NT * 2 * 1024 : 0);
 }
 
 template <int KVT, int QT, int BS, int NW, bool WIDEN, int NT>
@@ -350,6 +369,7 @@ void paged_prefill_staged_kernel(const DecodeArgs a, const int32_t* __restrict__
     constexpr int64_t TILE = SUB * NSUB;
     constexpr int SKVT = staged_kvt(KVT, QT, WIDEN);  // what the stages hold
     constexpr bool kThree = staged_waves_per_eu<KVT, NT>() == 3;
+    constexpr bool kQLds = staged_q_in_lds<KVT, NT>();
     constexpr int SR = rows_per_sub(SKVT);
     constexpr int SB = stage_bytes(SKVT);
     using Math = MfmaMath<KVT, QT, NT>;
@@ -395,6 +415,17 @@ void paged_prefill_staged_kernel(const DecodeArgs a, const int32_t* __restrict__
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) mt.qf[t][kk] ^= 0x80008000u;
         cs = -cs;
+    }
+    // query fragments of k steps 2, 3 to this wave's LDS area (same wave
+    // writes and reads them: no barrier)
+    const u32x4_t* qhi = nullptr;
+    if constexpr (kQLds) {
+        u32x4_t* qa = reinterpret_cast<u32x4_t*>(stages + 2 * SB) + w * (NT * 2 * kWave) + lane;
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) qa[(2 * t + j) * kWave] = mt.qf[t][2 + j];
+        qhi = qa;
     }
     const int n_pairs_w = kv_end > 0 ? (kv_end + 2 * kSubTokens - 1) / (2 * kSubTokens) : 0;
     const int n_free = pos0 + 1 >= kSubTokens ? (pos0 + 1) / kSubTokens : 0;
@@ -485,8 +516,8 @@ void paged_prefill_staged_kernel(const DecodeArgs a, const int32_t* __restrict__
         };
         auto compute = [&](int p, int st) {
             if (p < n_pairs_w)
-                staged_pair<SKVT, QT, kThree>(mt, stages + st * SB, 2 * p * kSubTokens, 2 * p + 2 > n_free, cs,
-                                             lane);
+                staged_pair<SKVT, QT, kThree, kQLds>(mt, stages + st * SB, 2 * p * kSubTokens, 2 * p + 2 > n_free,
+                                                    cs, lane, qhi);
         };
 
         // Fetches, stage writes and barriers are unconditional (indices past
@@ -574,7 +605,7 @@ static hipError_t launch_prefill_t(const DecodeArgs& a, const int32_t* query_sta
         auto go = [&](auto widen) {
             constexpr bool W = decltype(widen)::value;
             hipLaunchKernelGGL((paged_prefill_staged_kernel<KVT, QT, BS, NW, W, NT>), grid, dim3(NW * kWave),
-                               2 * stage_bytes(staged_kvt(KVT, QT, W)), st, a, query_start, tt, groups);
+                               (staged_lds_bytes<KVT, QT, NT, W>(NW)), st, a, query_start, tt, groups);
         };
         if constexpr (KVT == DT_FP8) {
             if (a.ctx_cap > kWidenMinContext) go(std::true_type{});
