@@ -65,8 +65,21 @@ __device__ __forceinline__ int seq_of_rank(const DecodeArgs& a, int rank, int* l
     return s;
 }
 
+// Two-tile workgroups over 16-bit pools: one unit in flight per wave and two
+// waves per SIMD (247-256 VGPRs instead of 277 at one wave): 3-5 % faster on
+// 4- and 8-token chunks.  fp8 pools keep two units in flight at one wave per
+// SIMD (one unit in flight was 59 % slower for them).
+template <int KVT, int NT>
+__host__ __device__ constexpr int small_chunk_waves_per_eu() {
+    return (NT == 2 && KVT != DT_FP8) ? 2 : PKV_WAVES_PER_EU;
+}
+template <int KVT, int NT>
+__host__ __device__ constexpr int small_chunk_depth() {
+    return (NT == 2 && KVT != DT_FP8) ? 1 : kDepth;
+}
+
 template <int KVT, int QT, int BS, int NW, int DEPTH, int NT>
-__global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(PKV_WAVES_PER_EU)))
+__global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(small_chunk_waves_per_eu<KVT, NT>())))
 void paged_prefill_mfma_kernel(const DecodeArgs a, const int32_t* __restrict__ query_start,
                                int tile_tokens, int max_tiles) {
     extern __shared__ float pkv_smem[];
@@ -622,7 +635,7 @@ static hipError_t launch_prefill_t(const DecodeArgs& a, const int32_t* query_sta
         const size_t lds = std::max(sizeof(float) * merge_lds_floats(kWavesPerGroup, tt * a.group, 32),
                                     sizeof(int) * (kRankSeqsMax + 1));
         const dim3 grid((unsigned)((int64_t)a.num_seqs * tiles2 * a.num_kv_heads));
-        hipLaunchKernelGGL((paged_prefill_mfma_kernel<KVT, QT, BS, kWavesPerGroup, kDepth, 2>), grid,
+        hipLaunchKernelGGL((paged_prefill_mfma_kernel<KVT, QT, BS, kWavesPerGroup, small_chunk_depth<KVT, 2>(), 2>), grid,
                            dim3(kWavesPerGroup * kWave), lds, st, a, query_start, tt, tiles2);
         return hipGetLastError();
     }
