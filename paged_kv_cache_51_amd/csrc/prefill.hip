@@ -359,16 +359,19 @@ template <int KVT, int NT>
 __host__ __device__ constexpr int staged_waves_per_eu() {
     return NT != 2 ? 1 : ((KVT == DT_FP8 || PKV_PREFILL_THREE_WAVES_16BIT) ? 3 : PKV_PREFILL_WAVES_PER_EU);
 }
-// query fragments of k steps 2, 3 in LDS: 16-bit pools at three waves
-template <int KVT, int NT>
+// query fragments of k steps 2, 3 in LDS at three waves, except over
+// widened fp8 stages (those fit 168 VGPRs without it and ran 4 % slower
+// with it; fp8 kept as fp8 in the stages spilled up to 12 VGPRs without
+// it, and bs 32 ran 7 % faster with it)
+template <int KVT, int NT, bool WIDEN>
 __host__ __device__ constexpr bool staged_q_in_lds() {
-    return staged_waves_per_eu<KVT, NT>() == 3 && KVT != DT_FP8;
+    return staged_waves_per_eu<KVT, NT>() == 3 && !(KVT == DT_FP8 && WIDEN);
 }
 // LDS bytes of the staged form: two stages, then per wave its query half
 // (two tiles x two k steps x 64 lanes x 16 B)
 template <int KVT, int QT, int NT, bool WIDEN>
 __host__ __device__ constexpr int staged_lds_bytes(int nw) {
-    return 2 * stage_bytes(staged_kvt(KVT, QT, WIDEN)) + (staged_q_in_lds<KVT, NT>() ? nw * NT * 2 * 1024 : 0);
+    return 2 * stage_bytes(staged_kvt(KVT, QT, WIDEN)) + (staged_q_in_lds<KVT, NT, WIDEN>() ? nw * NT * 2 * 1024 : 0);
 }
 
 template <int KVT, int QT, int BS, int NW, bool WIDEN, int NT>
@@ -382,7 +385,7 @@ void paged_prefill_staged_kernel(const DecodeArgs a, const int32_t* __restrict__
     constexpr int64_t TILE = SUB * NSUB;
     constexpr int SKVT = staged_kvt(KVT, QT, WIDEN);  // what the stages hold
     constexpr bool kThree = staged_waves_per_eu<KVT, NT>() == 3;
-    constexpr bool kQLds = staged_q_in_lds<KVT, NT>();
+    constexpr bool kQLds = staged_q_in_lds<KVT, NT, WIDEN>();
     constexpr int SR = rows_per_sub(SKVT);
     constexpr int SB = stage_bytes(SKVT);
     using Math = MfmaMath<KVT, QT, NT>;
