@@ -141,10 +141,16 @@ __device__ __forceinline__ constexpr uint32_t ones2() {
 // the kernel: 405 against 463 TFLOP/s on 16 x 512-token chunks).
 //   - wave w fetches one quarter of each pair (K of unit A / K of unit B /
 //     V of A / V of B for w = 0..3), 16 bytes per lane per 1 KiB pool row,
-//     two pairs ahead in registers, and writes it to one of two LDS stages:
+//     one pair ahead in registers, and writes it to one of two LDS stages:
 //     K rows as in the pool, V straight in PV operand order (entry [nt][lane]
-//     = the unit A then unit B halves of dim tile nt); one workgroup barrier
+//     = the unit A then unit B halves of dim tile nt; fp8 pools are widened
+//     to the query type here for contexts above 16K); one workgroup barrier
 //     per pair;
+//   - three waves per SIMD (168 VGPRs): the PV operands are read from LDS
+//     right before the PV MFMAs, and except over widened fp8 stages the
+//     query fragments of k steps 2 and 3 live in an LDS area of the wave's
+//     own; occupancy is what hides each wave's latencies (one wave per SIMD
+//     ran 35-55 % slower, three waves 4-14 % faster than two);
 //   - PV runs on 16x16x32 MFMAs whose 32-long contraction covers both units
 //     (16x16x16 runs at half the matrix rate on gfx950): lane group
 //     g = lane >> 4 contributes tokens 4g..4g+3 of unit A and of unit B to
