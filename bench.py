@@ -61,26 +61,44 @@ def parse():
     return ap.parse_args()
 
 
-def kernel_source_hash():
+DECODE_SOURCES = ("decode_core.h", "mfma_math.h", "decode.hip", "pkv_device.h")
+PREFILL_SOURCES = ("prefill.hip", "decode_core.h", "mfma_math.h", "pkv_device.h")
+
+
+def kernel_source_hash(files=DECODE_SOURCES):
     h = hashlib.sha256()
-    for f in ("decode_core.h", "mfma_math.h", "decode.hip", "pkv_device.h"):
+    for f in files:
         with open(os.path.join(ROOT, "paged_kv_cache_51_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(config_key):
+def measured_traffic(config_key, table="decode_traffic.json", files=DECODE_SOURCES):
     """HBM traffic per launch from committed rocprofv3 counter runs, only if
     they were taken on the current kernel source."""
-    path = os.path.join(ROOT, "profiles", "decode_traffic.json")
+    path = os.path.join(ROOT, "profiles", table)
     if not os.path.exists(path):
         return None
     with open(path) as f:
         data = json.load(f)
     rec = data.get(config_key)
-    if not rec or rec.get("kernel_hash") != kernel_source_hash():
+    if not rec or rec.get("kernel_hash") != kernel_source_hash(files):
         return None
     return rec.get("bytes_per_launch")
+
+
+def copy_probe(torch, dev, mib):
+    """One device-to-device copy of `mib` MiB (reads and writes exactly that
+    many bytes): the calibration the counter runs scale FETCH_SIZE /
+    WRITE_SIZE by."""
+    n = mib << 20
+    a = torch.empty(n, dtype=torch.uint8, device=dev)
+    b = torch.empty(n, dtype=torch.uint8, device=dev)
+    a.fill_(1)
+    torch.cuda.synchronize()
+    b.copy_(a)
+    torch.cuda.synchronize()
+    del a, b
 
 
 def main():
@@ -237,14 +255,7 @@ def main():
           f"(decode kernel at {achieved / probe_gbs:.1%} of it)", file=sys.stderr, flush=True)
 
     if args.copy_probe_mib:
-        n = args.copy_probe_mib << 20
-        a = torch.empty(n, dtype=torch.uint8, device=dev)
-        b = torch.empty(n, dtype=torch.uint8, device=dev)
-        a.fill_(1)
-        torch.cuda.synchronize()
-        b.copy_(a)
-        torch.cuda.synchronize()
-        del a, b
+        copy_probe(torch, dev, args.copy_probe_mib)
 
     cpu = None
     if args.cpu_baseline_seconds > 0:
@@ -395,6 +406,11 @@ def bench_prefill(args, torch, pkv, workloads):
     print(f"[bench] prefill: {S} seqs x {qlen} new tokens, contexts {int(ctx.min())}-{int(ctx.max())}; "
           f"{launch_ms * 1e3:.1f} us per layer, {tflops:.1f} TFLOP/s, {gbs:.0f} GB/s; "
           f"intensity {flops / nbytes:.0f} flop/B", file=sys.stderr, flush=True)
+    if args.copy_probe_mib:
+        copy_probe(torch, dev, args.copy_probe_mib)
+    kv_name = {pkv.BF16: "bf16", pkv.FP16: "fp16", pkv.FP8_E4M3: "fp8"}[kv]
+    traffic = measured_traffic(f"prefill-{args.config}-{kv_name}-bs{bs}-q{qlen}-s{S}",
+                               "prefill_traffic.json", PREFILL_SOURCES)
     cpu = None
     if args.cpu_baseline_seconds > 0:
         cpu = cpu_sample(args, "prefill", lambda n: _prefill_oracle_sample(
@@ -423,7 +439,7 @@ def bench_prefill(args, torch, pkv, workloads):
                      "peak": peak_tf if mfma_bound else PEAK_HBM_GBS,
                      "unit": "TFLOP/s" if mfma_bound else "GB/s",
                      "frac": round((tflops / peak_tf) if mfma_bound else (gbs / PEAK_HBM_GBS), 4),
-                     "traffic": None, "avg_launch_us": round(launch_ms * 1e3, 2),
+                     "traffic": traffic, "avg_launch_us": round(launch_ms * 1e3, 2),
                      "algorithmic_flops_per_launch": flops, "algorithmic_bytes_per_launch": nbytes},
         "cpu_baseline": cpu,
     }), flush=True)
