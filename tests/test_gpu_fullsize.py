@@ -101,3 +101,80 @@ def test_qwen15b_full_with_shared_prefix():
 @pytest.mark.parametrize("bs", [16, 32])
 def test_llama7b_mha_fp16(bs):
     run_config("llama7b", block_size=bs, samples=_extremes("llama7b", 6))
+
+
+# ---------------------------------------------------------------------------
+# Multi-token (chunked-prefill) attention at the bench's full workloads: the
+# last q_len tokens of each of the first S sequences are new; the launch is
+# the one bench.py times.  Sampled rows (first / middle / last token of the
+# chunk of the longest, the shortest and random sequences) are checked
+# against the oracle as one-token chunks at their positions (the same
+# causal prefix).
+
+
+def run_prefill_config(name, qlen, S, kv_dtype=None, n_random=2, seed=0):
+    cfg, tabs, _, _ = workloads.make(name)
+    kv = cfg.kv_dtype if kv_dtype is None else kv_dtype
+    qdt = cfg.q_dtype if kv == oracle.FP8 else kv
+    bs = cfg.block_size
+    H, Hkv, D = cfg.num_heads, cfg.num_kv_heads, cfg.head_dim
+    ctx = tabs.context_lens[:S].astype(np.int32)
+    bt_np = np.ascontiguousarray(tabs.block_tables[:S])
+    nb = tabs.num_blocks
+    log(f"{name} prefill: kv={kv} S={S} q_len={qlen} contexts {int(ctx.min())}-{int(ctx.max())}")
+    scale_fp8 = float(np.float32(8.0 / 448.0))
+    ks = vs = scale_fp8 if kv == oracle.FP8 else 1.0
+    nbytes = pkv.layer_pool_bytes(nb, Hkv, D, bs, kv)
+    kpool = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    vpool = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    workloads.device_fill_normal(kpool, kv, 3000 + seed, scale=scale_fp8)
+    workloads.device_fill_normal(vpool, kv, 4000 + seed, scale=scale_fp8)
+    tq = torch.bfloat16 if qdt == oracle.BF16 else torch.float16
+    g = torch.Generator(device=DEV)
+    g.manual_seed(11 + seed)
+    T = S * qlen
+    q = torch.randn(T, H, D, generator=g, device=DEV).to(tq)
+    out = torch.full_like(q, float("nan"))
+    qsl = torch.arange(0, T + 1, qlen, dtype=torch.int32, device=DEV)
+    scale = float(np.float32(1.0 / np.sqrt(D)))
+    pkv.paged_attention_prefill(out, q, kpool, vpool, torch.from_numpy(bt_np).to(DEV),
+                                torch.from_numpy(ctx).to(DEV), qsl, qlen, int(ctx.max()), Hkv, bs, kv,
+                                scale, ks, vs)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy().astype(np.float64)
+    assert np.isfinite(got).all(), "non-finite output"
+    r = np.random.default_rng(seed)
+    seqs = {int(np.argmax(ctx)), int(np.argmin(ctx))} | set(int(i) for i in r.choice(S, n_random, replace=False))
+    toks = sorted({0, qlen // 2, qlen - 1})
+    rows = [(s, j) for s in sorted(seqs) for j in toks]
+    log(f"  sampled rows (seq, token): {rows}; copying pools to host")
+    kp, vp = kpool.cpu().numpy(), vpool.cpu().numpy()
+    qb = q.cpu().view(torch.int16).numpy().view(np.uint16)
+    sub_q = qb[[s * qlen + j for s, j in rows]]
+    sub_ctx = np.array([int(ctx[s]) - qlen + j + 1 for s, j in rows], np.int32)
+    sub_bt = np.ascontiguousarray(bt_np[[s for s, _ in rows]])
+    want = oracle.paged_prefill(sub_q, qdt, kp, vp, kv, sub_bt, sub_ctx,
+                                np.arange(len(rows) + 1, dtype=np.int32), Hkv, bs, scale, ks, vs)
+    err = np.abs(got[[s * qlen + j for s, j in rows]] - want)
+    log(f"  max-abs {err.max():.3e} mean-abs {err.mean():.3e}")
+    assert err.max() <= TOL[kv]
+
+
+def test_prefill_qwen7b_16x512_full_size():
+    run_prefill_config("qwen7b", 512, 16)
+
+
+def test_prefill_qwen7b_fp8_16x512_full_size():
+    run_prefill_config("qwen7b", 512, 16, kv_dtype=oracle.FP8)
+
+
+def test_prefill_qwen72b_fp8_8x512_full_size():
+    run_prefill_config("qwen72b", 512, 8, kv_dtype=oracle.FP8, n_random=1)
+
+
+def test_prefill_llama7b_8x512_full_size():
+    run_prefill_config("llama7b", 512, 8)
+
+
+def test_prefill_qwen7b_256x4_full_size():
+    run_prefill_config("qwen7b", 4, 256, n_random=3)
