@@ -143,6 +143,11 @@ typedef struct {
 
 typedef struct pkv_pool pkv_pool;
 
+/* pkv_bytes_per_token of a pool descriptor (its num_layers, num_kv_heads,
+ * head_dim, kv_dtype): the KV bytes one token occupies in that pool over all
+ * layers.  Negative PKV_ERR_ARG for a null descriptor or bad fields. */
+int64_t kv_pool_bytes_per_token(const pkv_pool_desc* desc);
+
 /* Bind caller-allocated device memory as a paged KV pool ([P1] §4 block
  * pool; layout above).  k_layers / v_layers are host arrays of num_layers
  * device pointers, each at least bytes_each bytes, which must be at least

@@ -32,7 +32,7 @@ EXPORTS = [
     "pkv_copy_blocks", "paged_attention_prefill", "pkv_bm_evict_tokens", "pkv_bm_repack",
     "pkv_bm_token_slots", "paged_attention_decode_tokens", "pkv_move_tokens_scratch_bytes",
     "pkv_move_tokens", "pkv_bm_repack_tiles", "pkv_repack_blocks",
-    "pkv_read_probe_sink_bytes", "pkv_read_probe",
+    "pkv_read_probe_sink_bytes", "pkv_read_probe", "kv_pool_bytes_per_token",
 ]
 
 
@@ -92,6 +92,7 @@ def lib():
             "pkv_check_block_tables": (i32, [p, i32, p, i32, i32, i32, p,
                                              ctypes.POINTER(ctypes.c_int64), p]),
             "pkv_read_probe_sink_bytes": (i64, []),
+            "kv_pool_bytes_per_token": (i64, [ctypes.POINTER(PoolDesc)]),
             "pkv_read_probe": (i32, [p, i64, p, i64, p]),
             "pkv_bm_create": (i32, [i32, i32, i32, ctypes.POINTER(p)]),
             "pkv_bm_destroy": (i32, [p]),

@@ -141,6 +141,11 @@ int64_t pkv_bytes_per_token(int32_t num_layers, int32_t num_kv_heads, int32_t he
     return 2LL * num_layers * num_kv_heads * head_dim * elem_size(kv_dtype);
 }
 
+int64_t kv_pool_bytes_per_token(const pkv_pool_desc* desc) {
+    if (!desc) return fail(PKV_ERR_ARG, "null descriptor");
+    return pkv_bytes_per_token(desc->num_layers, desc->num_kv_heads, desc->head_dim, desc->kv_dtype);
+}
+
 int64_t pkv_tile_bytes(int32_t head_dim, int32_t block_size, int32_t kv_dtype) {
     if (int32_t e = check_layout_args(head_dim, block_size, kv_dtype)) return e;
     ok();
