@@ -383,7 +383,7 @@ __host__ __device__ constexpr int staged_lds_bytes(int nw) {
 template <int KVT, int QT, int BS, int NW, bool WIDEN, int NT>
 __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(staged_waves_per_eu<KVT, NT>())))
 void paged_prefill_staged_kernel(const DecodeArgs a, const int32_t* __restrict__ query_start,
-                                 int tile_tokens, int max_groups) {
+                                 int max_groups) {
     static_assert(NW == 4, "one pool-row quarter of a unit pair per wave");
     constexpr int NSUB = BS / kSubTokens;
     constexpr int R = rows_per_sub(KVT);
@@ -410,23 +410,32 @@ void paged_prefill_staged_kernel(const DecodeArgs a, const int32_t* __restrict__
     const int s = seq_of_rank(a, band_rank(band, in_band % bw, P, bw), reinterpret_cast<int*>(pkv_smem));
     const int q0 = query_start[s];
     const int q_len = query_start[s + 1] - q0;
-    const int g0 = grp * NW * tile_tokens;           // the workgroup's first token
-    if (g0 >= q_len) return;                         // (whole workgroup)
+    // Columns: the chunk's (token, head) pairs in order, c = j * G + h, cut
+    // into CW-column waves and NW-wave workgroups across token boundaries
+    // (no padding columns except at the chunk's end)
+    constexpr int CW = 16 * NT;
     const int G = a.group;
+    const int ncs = q_len * G;
+    const int cg0 = grp * NW * CW;                   // the workgroup's first column
+    if (cg0 >= ncs) return;                          // (whole workgroup)
     int ctx = a.context_lens[s];
     ctx = ctx < a.ctx_cap ? ctx : a.ctx_cap;
-    // keys of the workgroup: up to its last token
-    const int kv_end_g = min(ctx, ctx - q_len + min(q_len, g0 + NW * tile_tokens));
+    // keys of the workgroup: up to its last column's token
+    const int kv_end_g = min(ctx, ctx - q_len + (min(ncs, cg0 + NW * CW) - 1) / G + 1);
 
-    // this wave's tile (it may have none)
-    const int j0 = g0 + w * tile_tokens;
-    const bool has_tile = j0 < q_len;
-    const QueryTile qt{(int64_t)q0 + j0, has_tile ? min(tile_tokens, q_len - j0) : 0, q_len - j0};
+    // this wave's columns (it may have none): pairs h0 .. h0 + ncw - 1
+    // counted from head 0 of chunk token j0
+    const int c0w = cg0 + w * CW;
+    const bool has_tile = c0w < ncs;
+    const int j0 = has_tile ? c0w / G : 0;
+    const int h0 = has_tile ? c0w - j0 * G : 0;
+    const int ncw = has_tile ? min(CW, ncs - c0w) : 0;
+    const int64_t row0 = (int64_t)q0 + j0;
     Math mt;
-    if (has_tile) mt.load_q(a, qt, kvh, lane);
-    const int pos0 = ctx - qt.back;
-    const int kv_end = has_tile ? min(ctx, pos0 + qt.ntok) : 0;
-    mt.limit(pos0, G, lane);
+    if (has_tile) mt.load_q_cols(a, row0, h0, ncw, kvh, lane);
+    const int pos0 = ctx - (q_len - j0);             // position of token j0
+    const int kv_end = has_tile ? min(ctx, pos0 + (h0 + ncw - 1) / G + 1) : 0;
+    mt.limit_cols(pos0, h0, G);
     mt.begin();
     // the scale is applied after the max, which needs it positive: a
     // negative one flips the sign of every query element instead (exact)
@@ -601,9 +610,9 @@ void paged_prefill_staged_kernel(const DecodeArgs a, const int32_t* __restrict__
         if (!mt.cvalid[t]) continue;
         // L = 0 only for a token placed before the start of the context
         const float sc = (L > 0.f ? 1.0f / L : 0.f) * a.out_scale;
-        const int c = 16 * t + (lane & 15);
+        const int cl = 16 * t + (lane & 15) + h0;
         uint16_t* out = reinterpret_cast<uint16_t*>(a.out) +
-                        ((qt.row0 + c / G) * a.num_heads + (int64_t)kvh * G + c % G) * kHeadDim + 4 * g;
+                        ((row0 + cl / G) * a.num_heads + (int64_t)kvh * G + cl % G) * kHeadDim + 4 * g;
 #pragma unroll
         for (int nt = 0; nt < 8; ++nt) {
             const f32x4_t o = mt.acc[t][nt];
@@ -617,17 +626,18 @@ template <int KVT, int QT, int BS>
 static hipError_t launch_prefill_t(const DecodeArgs& a, const int32_t* query_start, int tile_tokens,
                                    int max_tiles, hipStream_t st) {
     if (max_tiles > kWavesPerGroup) {
-        // staged form: 16 * NT columns (NT 16-column tiles) per wave, four waves
+        // staged form: 16 * NT columns (NT 16-column tiles) per wave, four
+        // waves; columns packed across tokens (max_tiles * tile_tokens bounds
+        // the longest chunk)
         constexpr int NW = 4;
         constexpr int NT = PKV_PREFILL_TILES_PER_WAVE;
-        const int tt = NT * tile_tokens;
-        const int wave_tiles = (max_tiles * tile_tokens + tt - 1) / tt;
-        const int groups = (wave_tiles + NW - 1) / NW;
+        const int64_t max_cols = (int64_t)max_tiles * tile_tokens * a.group;
+        const int groups = (int)((max_cols + NW * 16 * NT - 1) / (NW * 16 * NT));
         const dim3 grid((unsigned)((int64_t)a.num_seqs * groups * a.num_kv_heads));
         auto go = [&](auto widen) {
             constexpr bool W = decltype(widen)::value;
             hipLaunchKernelGGL((paged_prefill_staged_kernel<KVT, QT, BS, NW, W, NT>), grid, dim3(NW * kWave),
-                               (staged_lds_bytes<KVT, QT, NT, W>(NW)), st, a, query_start, tt, groups);
+                               (staged_lds_bytes<KVT, QT, NT, W>(NW)), st, a, query_start, groups);
         };
         if constexpr (KVT == DT_FP8) {
             if (a.ctx_cap > kWidenMinContext) go(std::true_type{});
