@@ -47,36 +47,6 @@ struct MfmaMath {
             }
         }
     }
-    // Columns packed across token boundaries (the multi-token staged form):
-    // local column c holds the (token, head) pair number h0 + c counted from
-    // head 0 of query row row0, for c < ncols; the rest are padding.
-    __device__ __forceinline__ void load_q_cols(const DecodeArgs& a, int64_t row0, int h0, int ncols, int kvh,
-                                                int lane) {
-        const int G = a.group;
-        col = lane & 15;
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            const int c = 16 * t + col;
-            cvalid[t] = c < ncols;
-            const int cl = cvalid[t] ? c + h0 : 0;
-            const int j = cl / G;
-            const int h = cl - j * G;
-            const uint8_t* qrow = reinterpret_cast<const uint8_t*>(a.q) +
-                                  ((row0 + j) * a.num_heads + (int64_t)kvh * G + h) * (kHeadDim * 2);
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                const u32x4_t z = {0u, 0u, 0u, 0u};
-                qf[t][kk] = cvalid[t] ? *reinterpret_cast<const u32x4_t*>(qrow + 16 * ((lane >> 4) + 4 * kk))
-                                      : z;
-            }
-        }
-    }
-    // pos0 = position of query row row0; column c (pair h0 + c) sees keys up
-    // to its token's position
-    __device__ __forceinline__ void limit_cols(int pos0, int h0, int G) {
-#pragma unroll
-        for (int t = 0; t < NT; ++t) lim[t] = cvalid[t] ? pos0 + (16 * t + col + h0) / G + 1 : 0;
-    }
     // pos0 = position of the entry's first token: token j sees keys <= pos0 + j
     __device__ __forceinline__ void limit(int pos0, int G, int) {
 #pragma unroll

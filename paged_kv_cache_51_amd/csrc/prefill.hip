@@ -342,6 +342,40 @@ __device__ __forceinline__ void staged_pair(Math& mt, const uint8_t* stage, int 
     }
 }
 
+// Columns packed across token boundaries (the staged form): local column c
+// of the wave holds the (token, head) pair number h0 + c counted from head 0
+// of query row row0, for c < ncols; the rest are padding.  Sets the query
+// fragments, the column validity and each column's causal limit (keys at
+// positions < lim; pos0 = position of row0).
+template <class Math>
+__device__ __forceinline__ void load_q_cols(Math& mt, const DecodeArgs& a, int64_t row0, int h0, int ncols,
+                                            int kvh, int lane) {
+    constexpr int NT = Math::kCols / 16;
+    const int G = a.group;
+    mt.col = lane & 15;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        const int c = 16 * t + mt.col;
+        mt.cvalid[t] = c < ncols;
+        const int cl = mt.cvalid[t] ? c + h0 : 0;
+        const int j = cl / G;
+        const int h = cl - j * G;
+        const uint8_t* qrow = reinterpret_cast<const uint8_t*>(a.q) +
+                              ((row0 + j) * a.num_heads + (int64_t)kvh * G + h) * (kHeadDim * 2);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const u32x4_t z = {0u, 0u, 0u, 0u};
+            mt.qf[t][kk] = mt.cvalid[t] ? *reinterpret_cast<const u32x4_t*>(qrow + 16 * ((lane >> 4) + 4 * kk)) : z;
+        }
+    }
+}
+template <class Math>
+__device__ __forceinline__ void limit_cols(Math& mt, int pos0, int h0, int G) {
+    constexpr int NT = Math::kCols / 16;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) mt.lim[t] = mt.cvalid[t] ? pos0 + (16 * t + mt.col + h0) / G + 1 : 0;
+}
+
 // 16-column tiles per wave of the staged form: 2 (two waves per SIMD).  4
 // tiles (64 columns, half the LDS reads and barriers per MFMA) need 333
 // VGPRs, one wave per SIMD, and measured 35-55 % slower on the multi-token
@@ -432,10 +466,10 @@ void paged_prefill_staged_kernel(const DecodeArgs a, const int32_t* __restrict__
     const int ncw = has_tile ? min(CW, ncs - c0w) : 0;
     const int64_t row0 = (int64_t)q0 + j0;
     Math mt;
-    if (has_tile) mt.load_q_cols(a, row0, h0, ncw, kvh, lane);
+    if (has_tile) load_q_cols(mt, a, row0, h0, ncw, kvh, lane);
     const int pos0 = ctx - (q_len - j0);             // position of token j0
     const int kv_end = has_tile ? min(ctx, pos0 + (h0 + ncw - 1) / G + 1) : 0;
-    mt.limit_cols(pos0, h0, G);
+    limit_cols(mt, pos0, h0, G);
     mt.begin();
     // the scale is applied after the max, which needs it positive: a
     // negative one flips the sign of every query element instead (exact)
