@@ -218,6 +218,29 @@ def test_prefill_fp8_long_context_widened():
     check(got, want, oracle.FP8, "17K fp8")
 
 
+@pytest.mark.parametrize("G,Hkv", [(3, 2), (5, 1), (9, 2), (12, 1), (16, 1), (7, 3)])
+def test_prefill_group_sizes_packed_columns(G, Hkv):
+    """Group sizes whose (token, head) pairs do not fill 16-column tiles with
+    whole tokens: the staged form packs them across token boundaries, so a
+    wave starts mid-token and its tokens' causal limits differ per column.
+    Seeded random chunk and context lengths, each dtype pair."""
+    r = np.random.default_rng(100 + G * 10 + Hkv)
+    S = 5
+    lengths = r.integers(40, 420, S)
+    q_lens = np.minimum(lengths, r.integers(1, 160, S))
+    q_lens[0] = lengths[0]                          # one chunk that is the whole context
+    kv, qdt, bs = [(oracle.BF16, oracle.BF16, 16), (oracle.FP16, oracle.FP16, 32),
+                   (oracle.FP8, oracle.BF16, 16)][G % 3]
+    ks, vs = (0.02, 0.03) if kv == oracle.FP8 else (1.0, 1.0)
+    log(f"prefill G={G} Hkv={Hkv} kv={kv} lengths={lengths.tolist()} q_lens={q_lens.tolist()}")
+    tabs, kp, vp, qs, q = case(lengths.tolist(), q_lens.tolist(), G * Hkv, Hkv, bs, kv, qdt,
+                               seed=200 + G, ks=ks, vs=vs)
+    want = oracle.paged_prefill(q, qdt, kp, vp, kv, tabs.block_tables, tabs.context_lens, qs,
+                                Hkv, bs, SCALE, ks, vs)
+    got = gpu_prefill(tabs, kp, vp, qs, q, qdt, kv, Hkv, bs, ks, vs)
+    check(got, want, kv, f"G={G}")
+
+
 @pytest.mark.parametrize("kv,qdt,bs", [(oracle.BF16, oracle.BF16, 16), (oracle.FP8, oracle.FP16, 16)])
 def test_prefill_repeatable(kv, qdt, bs):
     """Two launches on the same inputs give the same bits: every step of the
