@@ -144,8 +144,7 @@ __device__ __forceinline__ constexpr uint32_t ones2() {
 //     one pair ahead in registers, and writes it to one of two LDS stages:
 //     K rows as in the pool, V straight in PV operand order (entry [nt][lane]
 //     = the unit A then unit B halves of dim tile nt; fp8 pools are widened
-//     to the query type here for contexts above 16K); one workgroup barrier
-//     per pair;
+//     to the query type here); one workgroup barrier per pair;
 //   - three waves per SIMD (168 VGPRs): the PV operands are read from LDS
 //     right before the PV MFMAs, and except over widened fp8 stages the
 //     query fragments of k steps 2 and 3 live in an LDS area of the wave's
@@ -191,14 +190,12 @@ static_assert(2 * stage_bytes(DT_FP8) >= 4 * (kRankSeqsMax + 1), "the ranking bo
 // Type of the staged kernel's LDS stages.  With `widen`, an fp8 pool is
 // widened to the query type by the stage writer (each wave converts its
 // quarter of a pair once, instead of every wave converting the whole pair
-// for its MFMAs).  Measured either way, same code otherwise: widening is
-// 3-3.5 % faster on 32K contexts (72B shape, 64- to 512-token chunks) but
-// 2-9 % slower on 1-8K contexts at 64- to 256-token chunks (7B shape; 2.7 %
-// faster at 512); the launcher widens above kWidenMinContext.
+// for its MFMAs).  The launcher widens every fp8 pool: on the three-wave
+// packed-column kernel that was faster or equal on every shape measured
+// (7B 16 x 512 624 -> 573 us, 72B fp8 8 x 512 4637 -> 4397 us).
 __host__ __device__ constexpr int staged_kvt(int kvt, int qt, bool widen) {
     return (kvt == DT_FP8 && widen) ? qt : kvt;
 }
-constexpr int kWidenMinContext = 16384;
 
 // One unit pair of a stage: logits, online softmax and PV for the wave's two
 // column tiles.  masked (uniform): apply each column's causal limit; pairs
@@ -673,12 +670,8 @@ static hipError_t launch_prefill_t(const DecodeArgs& a, const int32_t* query_sta
             hipLaunchKernelGGL((paged_prefill_staged_kernel<KVT, QT, BS, NW, W, NT>), grid, dim3(NW * kWave),
                                (staged_lds_bytes<KVT, QT, NT, W>(NW)), st, a, query_start, groups);
         };
-        if constexpr (KVT == DT_FP8) {
-            if (a.ctx_cap > kWidenMinContext) go(std::true_type{});
-            else go(std::false_type{});
-        } else {
-            go(std::false_type{});
-        }
+        if constexpr (KVT == DT_FP8) go(std::true_type{});
+        else go(std::false_type{});
         return hipGetLastError();
     }
     if (PKV_PREFILL_WG_NT2 && max_tiles >= 2) {

@@ -177,11 +177,11 @@ def test_prefill_staged_form_any_scale(scale):
 
 
 @pytest.mark.parametrize("qdt,bs", [(oracle.BF16, 16), (oracle.FP16, 32)])
-def test_prefill_fp8_both_stage_forms(qdt, bs):
-    """fp8 pools in the staged form: kept fp8 in LDS (maximum context up to
-    16K) and widened to the query type by the stage writer (above 16K,
-    selected here by a longer table and maximum context over the same
-    short sequences): both equal the oracle, and each other bit for bit."""
+def test_prefill_fp8_independent_of_max_context(qdt, bs):
+    """fp8 pools in the staged form (widened to the query type by the stage
+    writer): the result equals the oracle and does not depend on the
+    maximum context passed (a longer table and maximum context over the
+    same short sequences give the same bits)."""
     lengths = [700, 333, 1025, 96]
     q_lens = [300, 77, 512, 96]
     ks, vs = 0.02, 0.03
@@ -205,8 +205,8 @@ def test_prefill_fp8_both_stage_forms(qdt, bs):
 
 
 def test_prefill_fp8_long_context_widened():
-    """One sequence of 17,000 keys (fp8 widened in the stage writer) with a
-    chunk of 24 new tokens, beside a short one."""
+    """One sequence of 17,000 keys (fp8) with a chunk of 24 new tokens,
+    beside a short one."""
     lengths = [17000, 90]
     q_lens = [24, 90]
     ks, vs = 0.02, 0.03
