@@ -397,9 +397,9 @@ __host__ __device__ constexpr int staged_waves_per_eu() {
     return NT != 2 ? 1 : ((KVT == DT_FP8 || PKV_PREFILL_THREE_WAVES_16BIT) ? 3 : PKV_PREFILL_WAVES_PER_EU);
 }
 // query fragments of k steps 2, 3 in LDS at three waves, except over
-// widened fp8 stages (those fit 168 VGPRs without it and ran 4 % slower
-// with it; fp8 kept as fp8 in the stages spilled up to 12 VGPRs without
-// it, and bs 32 ran 7 % faster with it)
+// widened fp8 stages (168 VGPRs with up to 5 spilled without it, but 2-4 %
+// faster than with it; fp8 kept as fp8 in the stages, a form the launcher
+// no longer uses, spilled up to 12 and ran 7 % faster with it)
 template <int KVT, int NT, bool WIDEN>
 __host__ __device__ constexpr bool staged_q_in_lds() {
     return staged_waves_per_eu<KVT, NT>() == 3 && !(KVT == DT_FP8 && WIDEN);
