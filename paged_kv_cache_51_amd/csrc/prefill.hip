@@ -8,8 +8,6 @@
 // 0..ctx - q_len + j, read through the block table exactly as in decode.
 // The per-unit arithmetic is the decode kernel's (decode_core.h,
 // mfma_math.h) with the query columns (token, head) pairs.
-#include <type_traits>
-
 #include "decode_core.h"
 #include "mfma_math.h"
 
@@ -187,14 +185,14 @@ __host__ __device__ constexpr int stage_bytes(int kvt) {
 }
 static_assert(2 * stage_bytes(DT_FP8) >= 4 * (kRankSeqsMax + 1), "the ranking borrows the stage area");
 
-// Type of the staged kernel's LDS stages.  With `widen`, an fp8 pool is
-// widened to the query type by the stage writer (each wave converts its
-// quarter of a pair once, instead of every wave converting the whole pair
-// for its MFMAs).  The launcher widens every fp8 pool: on the three-wave
-// packed-column kernel that was faster or equal on every shape measured
-// (7B 16 x 512 624 -> 573 us, 72B fp8 8 x 512 4637 -> 4397 us).
-__host__ __device__ constexpr int staged_kvt(int kvt, int qt, bool widen) {
-    return (kvt == DT_FP8 && widen) ? qt : kvt;
+// Type of the staged kernel's LDS stages: an fp8 pool is widened to the
+// query type by the stage writer (each wave converts its quarter of a pair
+// once, instead of every wave converting the whole pair for its MFMAs; on
+// the three-wave packed-column kernel that was faster or equal on every
+// shape measured, 7B 16 x 512 624 -> 573 us, 72B fp8 8 x 512 4637 -> 4397
+// us, against fp8 stages widened by each wave).
+__host__ __device__ constexpr int staged_kvt(int kvt, int qt) {
+    return kvt == DT_FP8 ? qt : kvt;
 }
 
 // One unit pair of a stage: logits, online softmax and PV for the wave's two
@@ -203,8 +201,8 @@ __host__ __device__ constexpr int staged_kvt(int kvt, int qt, bool widen) {
 // end arrive zeroed from the stage writer, so no V mask is needed here.
 // One code path: the branch covers only the logit select (a second copy of
 // the whole pair made the compiler copy the 64 accumulators every pair).
-// KVT here is the type the stage holds (an fp8 pool is staged as fp8, or
-// already widened to the query type).
+// KVT here is the type the stage holds: 16-bit (fp8 pools are widened to
+// the query type by the stage writer).
 //
 // LATE_V: read the PV operands right before the PV MFMAs instead of before
 // the softmax (fewer registers live through the softmax: what lets the
@@ -214,6 +212,7 @@ __host__ __device__ constexpr int staged_kvt(int kvt, int qt, bool widen) {
 template <int KVT, int QT, bool LATE_V, bool QLDS, class Math>
 __device__ __forceinline__ void staged_pair(Math& mt, const uint8_t* stage, int tok0,
                                             bool masked, float cs, int lane, const u32x4_t* qhi) {
+    static_assert(KVT != DT_FP8, "stages hold 16-bit K / V");
     constexpr int R = rows_per_sub(KVT);
     constexpr int NT = Math::kCols / 16;           // 16-column tiles of the wave
     const u32x4_t* kl = reinterpret_cast<const u32x4_t*>(stage) + lane;
@@ -228,14 +227,7 @@ __device__ __forceinline__ void staged_pair(Math& mt, const uint8_t* stage, int 
     for (int kk = 0; kk < 4; ++kk) {
         u32x4_t k[2];
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            if constexpr (KVT == DT_FP8) {
-                const u32x4_t row = kl[(u * R + (kk >> 1)) * kWave];
-                k[u] = (kk & 1) ? e4m3x8_to_16<QT>(row[2], row[3]) : e4m3x8_to_16<QT>(row[0], row[1]);
-            } else {
-                k[u] = kl[(u * R + kk) * kWave];
-            }
-        }
+        for (int u = 0; u < 2; ++u) k[u] = kl[(u * R + kk) * kWave];
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             u32x4_t qv;
@@ -249,14 +241,7 @@ __device__ __forceinline__ void staged_pair(Math& mt, const uint8_t* stage, int 
     // it (the rescale branch below ends the scheduler's region)
     auto read_v = [&](u32x4_t (&vop)[8]) {
 #pragma unroll
-        for (int nt = 0; nt < 8; ++nt) {
-            if constexpr (KVT == DT_FP8) {
-                // fp8 rows hold four dim tiles each; widened when used
-                vop[nt] = nt < 2 * R ? vl[((nt >> 1) + R * (nt & 1)) * kWave] : (u32x4_t){0u, 0u, 0u, 0u};
-            } else {
-                vop[nt] = vl[nt * kWave];
-            }
-        }
+        for (int nt = 0; nt < 8; ++nt) vop[nt] = vl[nt * kWave];
     };
     u32x4_t vop[8];
     if constexpr (!LATE_V) read_v(vop);
@@ -324,19 +309,9 @@ __device__ __forceinline__ void staged_pair(Math& mt, const uint8_t* stage, int 
     // PV
     if constexpr (LATE_V) read_v(vop);
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) {
-        u32x4_t vv;
-        if constexpr (KVT == DT_FP8) {
-            // vop[2r] = unit A row r, vop[2r + 1] = unit B row r
-            const u32x2_t x = e4m3x4_to_16<QT>(vop[2 * (nt >> 2)][nt & 3]);
-            const u32x2_t z = e4m3x4_to_16<QT>(vop[2 * (nt >> 2) + 1][nt & 3]);
-            vv = (u32x4_t){x[0], x[1], z[0], z[1]};
-        } else {
-            vv = vop[nt];
-        }
+    for (int nt = 0; nt < 8; ++nt)
 #pragma unroll
-        for (int t = 0; t < NT; ++t) mt.acc[t][nt] = mfma_16x16x32<QT>(vv, pf[t], mt.acc[t][nt]);
-    }
+        for (int t = 0; t < NT; ++t) mt.acc[t][nt] = mfma_16x16x32<QT>(vop[nt], pf[t], mt.acc[t][nt]);
 }
 
 // Columns packed across token boundaries (the staged form): local column c
@@ -396,22 +371,21 @@ template <int KVT, int NT>
 __host__ __device__ constexpr int staged_waves_per_eu() {
     return NT != 2 ? 1 : ((KVT == DT_FP8 || PKV_PREFILL_THREE_WAVES_16BIT) ? 3 : PKV_PREFILL_WAVES_PER_EU);
 }
-// query fragments of k steps 2, 3 in LDS at three waves, except over
-// widened fp8 stages (168 VGPRs with up to 5 spilled without it, but 2-4 %
-// faster than with it; fp8 kept as fp8 in the stages, a form the launcher
-// no longer uses, spilled up to 12 and ran 7 % faster with it)
-template <int KVT, int NT, bool WIDEN>
+// query fragments of k steps 2, 3 in LDS at three waves, except for fp8
+// pools (168 VGPRs with up to 5 spilled without it, but 2-4 % faster than
+// with it)
+template <int KVT, int NT>
 __host__ __device__ constexpr bool staged_q_in_lds() {
-    return staged_waves_per_eu<KVT, NT>() == 3 && !(KVT == DT_FP8 && WIDEN);
+    return staged_waves_per_eu<KVT, NT>() == 3 && KVT != DT_FP8;
 }
 // LDS bytes of the staged form: two stages, then per wave its query half
 // (two tiles x two k steps x 64 lanes x 16 B)
-template <int KVT, int QT, int NT, bool WIDEN>
+template <int KVT, int QT, int NT>
 __host__ __device__ constexpr int staged_lds_bytes(int nw) {
-    return 2 * stage_bytes(staged_kvt(KVT, QT, WIDEN)) + (staged_q_in_lds<KVT, NT, WIDEN>() ? nw * NT * 2 * 1024 : 0);
+    return 2 * stage_bytes(staged_kvt(KVT, QT)) + (staged_q_in_lds<KVT, NT>() ? nw * NT * 2 * 1024 : 0);
 }
 
-template <int KVT, int QT, int BS, int NW, bool WIDEN, int NT>
+template <int KVT, int QT, int BS, int NW, int NT>
 __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(staged_waves_per_eu<KVT, NT>())))
 void paged_prefill_staged_kernel(const DecodeArgs a, const int32_t* __restrict__ query_start,
                                  int max_groups) {
@@ -420,9 +394,9 @@ void paged_prefill_staged_kernel(const DecodeArgs a, const int32_t* __restrict__
     constexpr int R = rows_per_sub(KVT);
     constexpr int64_t SUB = sub_tile_bytes(KVT);
     constexpr int64_t TILE = SUB * NSUB;
-    constexpr int SKVT = staged_kvt(KVT, QT, WIDEN);  // what the stages hold
+    constexpr int SKVT = staged_kvt(KVT, QT);         // what the stages hold
     constexpr bool kThree = staged_waves_per_eu<KVT, NT>() == 3;
-    constexpr bool kQLds = staged_q_in_lds<KVT, NT, WIDEN>();
+    constexpr bool kQLds = staged_q_in_lds<KVT, NT>();
     constexpr int SR = rows_per_sub(SKVT);
     constexpr int SB = stage_bytes(SKVT);
     using Math = MfmaMath<KVT, QT, NT>;
@@ -560,8 +534,8 @@ void paged_prefill_staged_kernel(const DecodeArgs a, const int32_t* __restrict__
 #pragma unroll
                         for (int q = 0; q < 4; ++q) d[2 * kWave * (4 * i + q)] = e4m3x4_to_16<QT>(r[i][q]);
                 }
-            } else if (w < 2 || KVT == DT_FP8) {
-                // K (or fp8 V) rows as in the pool: [unit][row][lane]
+            } else if (w < 2) {
+                // K rows as in the pool: [unit][row][lane]
                 u32x4_t* d = reinterpret_cast<u32x4_t*>(base + (w >> 1) * 2 * R * 1024 + (w & 1) * R * 1024) + lane;
 #pragma unroll
                 for (int i = 0; i < R; ++i) d[kWave * i] = r[i];
@@ -665,13 +639,8 @@ static hipError_t launch_prefill_t(const DecodeArgs& a, const int32_t* query_sta
         const int64_t max_cols = (int64_t)max_tiles * tile_tokens * a.group;
         const int groups = (int)((max_cols + NW * 16 * NT - 1) / (NW * 16 * NT));
         const dim3 grid((unsigned)((int64_t)a.num_seqs * groups * a.num_kv_heads));
-        auto go = [&](auto widen) {
-            constexpr bool W = decltype(widen)::value;
-            hipLaunchKernelGGL((paged_prefill_staged_kernel<KVT, QT, BS, NW, W, NT>), grid, dim3(NW * kWave),
-                               (staged_lds_bytes<KVT, QT, NT, W>(NW)), st, a, query_start, groups);
-        };
-        if constexpr (KVT == DT_FP8) go(std::true_type{});
-        else go(std::false_type{});
+        hipLaunchKernelGGL((paged_prefill_staged_kernel<KVT, QT, BS, NW, NT>), grid, dim3(NW * kWave),
+                           (staged_lds_bytes<KVT, QT, NT>(NW)), st, a, query_start, groups);
         return hipGetLastError();
     }
     if (PKV_PREFILL_WG_NT2 && max_tiles >= 2) {
