@@ -265,20 +265,25 @@ __device__ __forceinline__ void staged_pair(Math& mt, const uint8_t* stage, int 
                 for (int i = 0; i < 4; ++i)
                     y[t][4 * u + i] = (ta + 16 * u + i) < mt.lim[t] ? y[t][4 * u + i] : -INFINITY;
     }
-    float bm[NT];
+    // The rescale test needs only this lane's own maximum: a column's scaled
+    // maximum passes m + slack exactly when one of its lanes' does (cs >= 0
+    // and rounding keep the order; a lane of -inf keys gives -inf, or NaN
+    // when cs = 0, and neither passes).  The column maximum across lanes is
+    // formed only inside the rare rescale branch.
+    float mx[NT];
     bool jump = false;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-        const float mx = fmaxf(fmaxf(fmaxf(y[t][0], y[t][1]), fmaxf(y[t][2], y[t][3])),
-                               fmaxf(fmaxf(y[t][4], y[t][5]), fmaxf(y[t][6], y[t][7])));
-        const float rm = rows_max(mx);
-        bm[t] = rm == -INFINITY ? -INFINITY : rm * cs;
-        jump |= bm[t] > mt.m[t] + kRescaleSlack;
+        mx[t] = fmaxf(fmaxf(fmaxf(y[t][0], y[t][1]), fmaxf(y[t][2], y[t][3])),
+                      fmaxf(fmaxf(y[t][4], y[t][5]), fmaxf(y[t][6], y[t][7])));
+        jump |= mx[t] * cs > mt.m[t] + kRescaleSlack;
     }
     if (__builtin_amdgcn_ballot_w64(jump)) {
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            const float mn = fmaxf(mt.m[t], bm[t]);
+            const float rm = rows_max(mx[t]);
+            const float bm = rm == -INFINITY ? -INFINITY : rm * cs;
+            const float mn = fmaxf(mt.m[t], bm);
             const float alpha = (mt.m[t] == -INFINITY) ? 0.f : fast_exp2(mt.m[t] - mn);
             mt.l[t] *= alpha;
 #pragma unroll
