@@ -58,7 +58,9 @@ __device__ __forceinline__ int seq_of_rank(const DecodeArgs& a, int rank, int* l
         if (r == rank) lds[kRankSeqsMax] = i;        // ranks are a permutation
     }
     __syncthreads();
-    const int s = lds[kRankSeqsMax];
+    // the same word in every lane: a scalar, so that every quantity derived
+    // from the sequence (its lengths, block-table row, loop bounds) is one
+    const int s = __builtin_amdgcn_readfirstlane(lds[kRankSeqsMax]);
     __syncthreads();
     return s;
 }
@@ -195,6 +197,13 @@ __host__ __device__ constexpr int staged_kvt(int kvt, int qt) {
     return kvt == DT_FP8 ? qt : kvt;
 }
 
+// Running maximum of a staged-kernel column that has seen no key yet: finite,
+// so that the exponent subtracts it with no select (-inf would need one to
+// avoid -inf - -inf).  Every finite scaled logit passes it plus the rescale
+// slack, so the first key a column sees replaces it, with alpha =
+// 2^(-FLT_MAX - m) = 0 for the empty sums.
+constexpr float kNoKeyMax = -3.402823466e38f;
+
 // One unit pair of a stage: logits, online softmax and PV for the wave's two
 // column tiles.  masked (uniform): apply each column's causal limit; pairs
 // every real column sees in full skip it.  V rows at or past the context
@@ -284,7 +293,7 @@ __device__ __forceinline__ void staged_pair(Math& mt, const uint8_t* stage, int 
             const float rm = rows_max(mx[t]);
             const float bm = rm == -INFINITY ? -INFINITY : rm * cs;
             const float mn = fmaxf(mt.m[t], bm);
-            const float alpha = (mt.m[t] == -INFINITY) ? 0.f : fast_exp2(mt.m[t] - mn);
+            const float alpha = fast_exp2(mt.m[t] - mn);   // 0 when leaving kNoKeyMax
             mt.l[t] *= alpha;
 #pragma unroll
             for (int nt = 0; nt < 8; ++nt) mt.acc[t][nt] *= alpha;
@@ -294,12 +303,12 @@ __device__ __forceinline__ void staged_pair(Math& mt, const uint8_t* stage, int 
     u32x4_t pf[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-        // 2^(-inf - m) = 0 for masked keys; a column that has seen no key
-        // yet (m = -inf) subtracts 0 instead, and all its keys are -inf
-        const float mref = mt.m[t] == -INFINITY ? 0.f : mt.m[t];
+        // 2^(-inf - m) = 0 for masked keys (the select below covers cs = 0);
+        // m is finite (a column that has seen no key holds kNoKeyMax, and
+        // then all its keys here are -inf)
         float pv[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) pv[j] = fast_exp2(fmaf(y[t][j], cs, -mref));
+        for (int j = 0; j < 8; ++j) pv[j] = fast_exp2(fmaf(y[t][j], cs, -mt.m[t]));
         if (masked) {
 #pragma unroll
             for (int j = 0; j < 8; ++j) pv[j] = y[t][j] == -INFINITY ? 0.f : pv[j];
@@ -418,8 +427,11 @@ void paged_prefill_staged_kernel(const DecodeArgs a, const int32_t* __restrict__
     const int bw = min(P, a.num_seqs - band * P);    // sequences in this band
     const int grp = max_groups - 1 - in_band / bw;
     const int s = seq_of_rank(a, band_rank(band, in_band % bw, P, bw), reinterpret_cast<int*>(pkv_smem));
-    const int q0 = query_start[s];
-    const int q_len = query_start[s + 1] - q0;
+    // the sequence's bounds as scalars (vector loads, since the kernel
+    // writes global memory; without this the pair loop and its block-table
+    // indexing run as per-lane arithmetic)
+    const int q0 = __builtin_amdgcn_readfirstlane(query_start[s]);
+    const int q_len = __builtin_amdgcn_readfirstlane(query_start[s + 1]) - q0;
     // Columns: the chunk's (token, head) pairs in order, c = j * G + h, cut
     // into CW-column waves and NW-wave workgroups across token boundaries
     // (no padding columns except at the chunk's end)
@@ -428,7 +440,7 @@ void paged_prefill_staged_kernel(const DecodeArgs a, const int32_t* __restrict__
     const int ncs = q_len * G;
     const int cg0 = grp * NW * CW;                   // the workgroup's first column
     if (cg0 >= ncs) return;                          // (whole workgroup)
-    int ctx = a.context_lens[s];
+    int ctx = __builtin_amdgcn_readfirstlane(a.context_lens[s]);
     ctx = ctx < a.ctx_cap ? ctx : a.ctx_cap;
     // keys of the workgroup: up to its last column's token
     const int kv_end_g = min(ctx, ctx - q_len + (min(ncs, cg0 + NW * CW) - 1) / G + 1);
@@ -447,6 +459,8 @@ void paged_prefill_staged_kernel(const DecodeArgs a, const int32_t* __restrict__
     const int kv_end = has_tile ? min(ctx, pos0 + (h0 + ncw - 1) / G + 1) : 0;
     limit_cols(mt, pos0, h0, G);
     mt.begin();
+#pragma unroll
+    for (int t = 0; t < NT; ++t) mt.m[t] = kNoKeyMax;
     // the scale is applied after the max, which needs it positive: a
     // negative one flips the sign of every query element instead (exact)
     float cs = a.qk_scale_log2;
@@ -468,11 +482,12 @@ void paged_prefill_staged_kernel(const DecodeArgs a, const int32_t* __restrict__
             for (int j = 0; j < 2; ++j) qa[(2 * t + j) * kWave] = mt.qf[t][2 + j];
         qhi = qa;
     }
-    const int n_pairs_w = kv_end > 0 ? (kv_end + 2 * kSubTokens - 1) / (2 * kSubTokens) : 0;
-    const int n_free = pos0 + 1 >= kSubTokens ? (pos0 + 1) / kSubTokens : 0;
+    // loop bounds as scalars (the divisions by G above are vector code)
+    const int n_pairs_w = __builtin_amdgcn_readfirstlane(kv_end > 0 ? (kv_end + 2 * kSubTokens - 1) / (2 * kSubTokens) : 0);
+    const int n_free = __builtin_amdgcn_readfirstlane(pos0 + 1 >= kSubTokens ? (pos0 + 1) / kSubTokens : 0);
 
     if (kv_end_g > 0) {
-        const int n_units = (kv_end_g + kSubTokens - 1) / kSubTokens;
+        const int n_units = __builtin_amdgcn_readfirstlane((kv_end_g + kSubTokens - 1) / kSubTokens);
         const int n_pairs = (n_units + 1) / 2;
         const int32_t* bt_row = a.block_tables + (int64_t)s * a.max_blocks;
         // wave w fetches K (w < 2) or V (w >= 2) rows of unit A (w even) or B
