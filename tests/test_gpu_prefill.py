@@ -264,6 +264,21 @@ def test_prefill_empty_chunks_and_max_query_len_above_need():
 
 
 @pytest.mark.parametrize("kv", [oracle.BF16, oracle.FP8])
+def test_prefill_staged_form_empty_chunks(kv):
+    # the staged form (13+ query tiles) with sequences that have no new
+    # tokens among them: they take part in the length ranking, and their
+    # workgroups have no columns; one chunk is its whole context
+    lengths = [30, 260, 50, 90, 7, 400]
+    q_lens = [0, 200, 0, 90, 0, 150]
+    tabs, kp, vp, qs, q = case(lengths, q_lens, 28, 4, 16, kv, oracle.BF16, seed=11)
+    log(f"staged empty chunks kv={kv} lengths={lengths} q_lens={q_lens}")
+    got = gpu_prefill(tabs, kp, vp, qs, q, oracle.BF16, kv, 4, 16, max_q=300)
+    want = oracle.paged_prefill(q, oracle.BF16, kp, vp, kv, tabs.block_tables,
+                                tabs.context_lens, qs, 4, 16, SCALE)
+    check(got, want, kv, "staged form, empty chunks")
+
+
+@pytest.mark.parametrize("kv", [oracle.BF16, oracle.FP8])
 def test_one_token_chunks_equal_decode_bitwise(kv):
     """q_len = 1 everywhere: the multi-token kernel is the decode kernel."""
     c, tabs, _, r_val = workloads.make("qwen15b")
