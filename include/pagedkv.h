@@ -108,7 +108,8 @@ typedef void* pkv_stream_t;
 /* ---------------------------------------------------------------- errors -- */
 
 /* Message for the last nonzero return on this thread ("" if none).  The
- * string is owned by the library and valid until the next call. */
+ * string is owned by the library and valid until the next call.  (The pages
+ * define no error channel; this one is the library's.) */
 const char* pkv_last_error(void);
 
 /* Library version as major*10000 + minor*100 + patch. */
@@ -157,6 +158,9 @@ int64_t kv_pool_bytes_per_token(const pkv_pool_desc* desc);
 int32_t kv_pool_create(const pkv_pool_desc* desc, void* const* k_layers,
                        void* const* v_layers, int64_t bytes_each,
                        pkv_pool** out);
+/* Release a handle made by kv_pool_create (NULL is allowed).  The device
+ * memory stays the caller's.  The pages define no such call: it only frees
+ * the handle's host record. */
 int32_t kv_pool_destroy(pkv_pool* pool);
 int32_t kv_pool_get_desc(const pkv_pool* pool, pkv_pool_desc* out);
 /* Device pointers of layer `layer`'s K and V pools. */
@@ -255,7 +259,11 @@ int32_t pkv_default_partition_tokens(int32_t num_seqs, int32_t num_kv_heads,
  * can span several partitions (P = ceil(max_context_len / partition) > 1)
  * — per (sequence, kv head, partition) the group's head_dim fp32 partial
  * outputs and one 128-byte line of maxima and normalisers.  With a caller
- * plan (opts->plan) the plan part is not used. */
+ * plan (opts->plan) the plan part is not used.  The default split size is
+ * resolved from max_context_len here and in the decode call alike, so this
+ * size always suffices for a decode with the same arguments (the decode may
+ * need less when max_blocks_per_seq * block_size < max_context_len).  The
+ * pages define no workspace: it is this library's split-context scratch. */
 int64_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_heads,
                                         int32_t num_kv_heads, int32_t head_dim,
                                         int32_t max_context_len,
@@ -344,8 +352,19 @@ int32_t paged_attention_decode_ex(void* out, const void* q, int32_t q_dtype,
  *                     sequences packed in order.
  *   query_start_loc : device int32[num_seqs + 1], non-decreasing, from 0;
  *                     max_query_len >= every q_len(s) (host scalar: grid).
+ *   max_query_len   : host scalar that sizes the grid; it must be at least
+ *                     every q_len(s).  The rows of a sequence past the first
+ *                     max_query_len are not written (their contents stay
+ *                     undefined): the caller passes the true maximum.
+ *   num_blocks      : pool size; block ids outside [0, num_blocks) are read
+ *                     as the null block 0 instead of faulting (0 =
+ *                     unchecked).
  * Other arguments as paged_attention_decode; no workspace.  A token whose
- * position would be < 0 (c < q_len) gets a zero output row.  Errors:
+ * position would be < 0 (c < q_len) gets a zero output row.  q and the
+ * context's K / V are expected finite: a NaN or infinity in a query row, or
+ * in a key or value a row can see, gives an undefined result in that row
+ * (this kernel is built with the compiler's finite-math assumption for its
+ * min / max; positions a row cannot see may hold anything).  Errors:
  * PKV_ERR_ARG, PKV_ERR_UNSUPPORTED (head_dim != 128, dtype pair, G > 16),
  * PKV_ERR_HIP. */
 int32_t paged_attention_prefill(void* out, const void* q, int32_t q_dtype,
@@ -357,7 +376,7 @@ int32_t paged_attention_prefill(void* out, const void* q, int32_t q_dtype,
                                 int32_t max_query_len, int32_t max_context_len,
                                 int32_t num_seqs, int32_t num_heads,
                                 int32_t num_kv_heads, int32_t head_dim,
-                                float scale, int32_t block_size,
+                                float scale, int32_t block_size, int32_t num_blocks,
                                 int32_t kv_dtype, float k_scale, float v_scale,
                                 pkv_stream_t stream);
 
@@ -432,8 +451,10 @@ int32_t pkv_bm_num_tokens(const pkv_block_manager* bm, int64_t seq_id);
 /* New sequence with a prompt of num_tokens tokens (host array): blocks for
  * all of them; with the prefix cache, the longest cached run of leading
  * full blocks is shared instead (*num_cached_tokens, a multiple of
- * block_size, always < num_tokens), and the prompt's other full blocks are
- * published.  extra_key separates otherwise equal prompts (salt, adapter). */
+ * block_size, always < num_tokens).  Those hit tokens count as computed;
+ * the prompt's other blocks become findable by later prompts only once
+ * pkv_bm_mark_computed covers them.  extra_key separates otherwise equal
+ * prompts (salt, adapter). */
 int32_t pkv_bm_add_sequence(pkv_block_manager* bm, int64_t seq_id, const int32_t* tokens,
                             int32_t num_tokens, uint64_t extra_key,
                             int32_t* num_cached_tokens);
@@ -443,6 +464,19 @@ int32_t pkv_bm_add_sequence(pkv_block_manager* bm, int64_t seq_id, const int32_t
  * token is written; otherwise both are -1. */
 int32_t pkv_bm_append_token(pkv_block_manager* bm, int64_t seq_id, int32_t token,
                             int32_t* slot, int32_t* cow_src, int32_t* cow_dst);
+/* The K/V of the sequence's first num_computed_tokens tokens are written, or
+ * are written by work already enqueued on the stream ahead of any later
+ * reader (a prefill chunk's reshape_and_cache).  With the prefix cache, every
+ * full block that ends inside them becomes findable by later prompts: [P1] §5
+ * caches only full blocks, and with chunked prefill ([P1] §6) a prompt's
+ * blocks fill over several steps, so a block counts as full once its last
+ * token's K/V is computed.  Counts never go back (a smaller value is a no-op);
+ * PKV_ERR_ARG if num_computed_tokens exceeds the sequence's tokens.  A token
+ * appended to a sequence whose every token is computed counts as computed at
+ * once (the decode step that appends it writes its K/V); a block freed before
+ * it was computed is never findable. */
+int32_t pkv_bm_mark_computed(pkv_block_manager* bm, int64_t seq_id, int32_t num_computed_tokens);
+int32_t pkv_bm_num_computed_tokens(const pkv_block_manager* bm, int64_t seq_id);
 /* child shares every block of parent (reference counts + 1). */
 int32_t pkv_bm_fork(pkv_block_manager* bm, int64_t parent_id, int64_t child_id);
 /* Drop the sequence; its blocks lose a reference, last block first. */

@@ -27,9 +27,15 @@ Readings (where the pages leave it open):
   - content keys are exact: key(block j) = (key(block j-1), its tokens),
     rooted at the extra key.  A hash of that chain, as the pages describe,
     matches exactly these keys up to collisions;
-  - the prompt's full blocks are published when the sequence is added
-    (their K/V is written by the prefill of the same step), appended full
-    blocks when their last token is appended; content already cached under
+  - "only full blocks are cached" (§5) is read together with §6's chunked
+    prefill, where a prompt's K/V is computed over several steps: a block
+    counts as full once the K/V of its last token is computed.  So a
+    block becomes findable only when the caller marks the tokens up to its
+    end computed (mark_computed); a prompt's hit blocks are computed from
+    the start, and a token appended to a sequence whose every token is
+    computed counts as computed at once (the decode step that appends it
+    writes its K/V).  A block freed before it was computed was never
+    findable and goes back as a clean block.  Content already cached under
     the same key is not published twice.
 """
 
@@ -108,12 +114,30 @@ class BlockPoolModel:
             self.ref[b] += 1
             blocks.append(b)
         for j in range(len(hits), nblk):
-            b = self._take()
-            blocks.append(b)
-            if self.prefix and j < len(keys):
-                self._publish(b, keys[j])
-        self.seqs[sid] = {"blocks": blocks, "tokens": list(tokens), "keys": keys, "root": root}
+            blocks.append(self._take())
+        self.seqs[sid] = {"blocks": blocks, "tokens": list(tokens), "keys": keys, "root": root,
+                          "computed": len(hits) * bs}
         return len(hits) * bs
+
+    def mark_computed(self, sid, n):
+        """The K/V of the sequence's first n tokens are written: full blocks
+        inside them become findable ([P1] §5, read with §6)."""
+        s = self.seqs[sid]
+        if not 0 <= n <= len(s["tokens"]):
+            raise ValueError("computed count outside the sequence")
+        old = s["computed"]
+        if n <= old:
+            return
+        s["computed"] = n
+        if not self.prefix or s.get("evicted"):
+            return
+        bs = self.bs
+        for j in range(len(s["keys"])):
+            if old < (j + 1) * bs <= n:
+                self._publish(s["blocks"][j], s["keys"][j])
+
+    def num_computed_tokens(self, sid):
+        return self.seqs[sid]["computed"]
 
     def append_token(self, sid, token=0):
         """Returns (slot, cow_src, cow_dst) ([P1] §4; copy-on-write)."""
@@ -135,12 +159,13 @@ class BlockPoolModel:
             dst = self._take()
             self._release(src)
             s["blocks"][j] = dst
+        done = s["computed"] == len(s["tokens"])
         s["tokens"].append(token)
-        if self.prefix and off == bs - 1 and not s.get("evicted"):
+        if off == bs - 1 and not s.get("evicted"):
             parent = s["keys"][j - 1] if j else s["root"]
-            key = (parent, tuple(s["tokens"][j * bs:(j + 1) * bs]))
-            s["keys"].append(key)
-            self._publish(s["blocks"][j], key)
+            s["keys"].append((parent, tuple(s["tokens"][j * bs:(j + 1) * bs])))
+        if done:                                     # a decode step writes the token it appends
+            self.mark_computed(sid, len(s["tokens"]))
         return s["blocks"][j] * bs + off, src, dst
 
     def fork(self, parent, child):
@@ -149,7 +174,8 @@ class BlockPoolModel:
         if "slots" in p:
             raise ValueError("evicted tokens: repack first")
         self.seqs[child] = {"blocks": list(p["blocks"]), "tokens": list(p["tokens"]),
-                            "keys": list(p["keys"]), "root": p["root"]}
+                            "keys": list(p["keys"]), "root": p["root"],
+                            "computed": p["computed"]}
         if p.get("evicted"):
             self.seqs[child]["evicted"] = True
         for b in p["blocks"]:
@@ -193,6 +219,7 @@ class BlockPoolModel:
         s["slots"] = [sl for sl, k in zip(slots, keep) if k]
         s["tokens"] = [t for t, k in zip(s["tokens"], keep) if k]
         s["keys"] = []
+        s["computed"] = len(s["tokens"])
         s["evicted"] = True      # its K/V no longer match any prompt: never published again
         for b in s["blocks"]:
             if b in self.key_of:

@@ -33,6 +33,7 @@ EXPORTS = [
     "pkv_bm_token_slots", "paged_attention_decode_tokens", "pkv_move_tokens_scratch_bytes",
     "pkv_move_tokens", "pkv_bm_repack_tiles", "pkv_repack_blocks",
     "pkv_read_probe_sink_bytes", "pkv_read_probe", "kv_pool_bytes_per_token",
+    "pkv_bm_mark_computed", "pkv_bm_num_computed_tokens",
 ]
 
 
@@ -105,12 +106,14 @@ def lib():
             "pkv_bm_append_token": (i32, [p, i64, i32, ctypes.POINTER(i32), ctypes.POINTER(i32),
                                           ctypes.POINTER(i32)]),
             "pkv_bm_fork": (i32, [p, i64, i64]),
+            "pkv_bm_mark_computed": (i32, [p, i64, i32]),
+            "pkv_bm_num_computed_tokens": (i32, [p, i64]),
             "pkv_bm_free_sequence": (i32, [p, i64]),
             "pkv_bm_block_table": (i32, [p, i64, p, i32, ctypes.POINTER(i32)]),
             "pkv_bm_slots": (i32, [p, i64, i32, i32, p]),
             "pkv_copy_blocks": (i32, [p, p, i32, i32, i32, i32, i32, i32, p, i32, p]),
             "paged_attention_prefill": (i32, [p, p, i32, p, p, p, i32, p, p, i32, i32, i32, i32,
-                                              i32, i32, f32, i32, i32, f32, f32, p]),
+                                              i32, i32, f32, i32, i32, i32, f32, f32, p]),
             "pkv_bm_evict_tokens": (i32, [p, i64, p, i32]),
             "pkv_bm_repack": (i32, [p, i64, p, i32, ctypes.POINTER(i32)]),
             "pkv_bm_token_slots": (i32, [p, i64, p, i32, ctypes.POINTER(i32)]),
@@ -155,6 +158,20 @@ def _ptr(t, name, dtype=None, device=True):
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     return ctypes.c_void_p(t.data_ptr())
+
+
+def _pool_blocks(k_cache, v_cache, num_blocks, num_kv_heads, head_dim, block_size, kv_dtype):
+    """Blocks the two pool tensors hold.  With num_blocks > 0 both must hold
+    at least that many (else ValueError); with 0 the tensors' own capacity is
+    returned, so the kernels can clamp block ids to memory that exists."""
+    per_block = layer_pool_bytes(1, num_kv_heads, head_dim, block_size, kv_dtype)
+    have = min(k_cache.numel() * k_cache.element_size(), v_cache.numel() * v_cache.element_size())
+    if num_blocks > 0:
+        if have < num_blocks * per_block:
+            raise ValueError(f"pool tensors hold {have} bytes, {num_blocks} blocks need "
+                             f"{num_blocks * per_block}")
+        return num_blocks
+    return have // per_block
 
 
 _TORCH = {BF16: torch.bfloat16, FP16: torch.float16}
@@ -278,8 +295,10 @@ def decode_slot_mapping(block_tables, context_lens, block_size, slot_mapping=Non
 
 def reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, block_size, num_blocks,
                       kv_dtype, k_scale=1.0, v_scale=1.0, stream=None):
-    """key/value: [T][H_kv][d] bf16/fp16; caches: uint8 pool tensors."""
+    """key/value: [T][H_kv][d] bf16/fp16; caches: uint8 pool tensors of at
+    least num_blocks blocks (ValueError otherwise)."""
     T, H, D = key.shape
+    _pool_blocks(k_cache, v_cache, num_blocks, H, D, block_size, kv_dtype)
     _check(lib().reshape_and_cache(
         _ptr(key, "key"), _ptr(value, "value"), dtype_code(key.dtype),
         _ptr(k_cache, "k_cache"), _ptr(v_cache, "v_cache"),
@@ -291,8 +310,10 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
                            max_context_len, num_kv_heads, block_size, kv_dtype, scale,
                            k_scale=1.0, v_scale=1.0, workspace=None, partition_tokens=0,
                            impl=IMPL_AUTO, stages=0, num_blocks=0, plan=None, stream=None):
-    """q/out: [S][H][d] bf16/fp16; k/v_cache: uint8 pools of one layer."""
+    """q/out: [S][H][d] bf16/fp16; k/v_cache: uint8 pools of one layer.
+    num_blocks = 0 clamps block ids to the blocks the pool tensors hold."""
     S, H, D = q.shape
+    num_blocks = _pool_blocks(k_cache, v_cache, num_blocks, num_kv_heads, D, block_size, kv_dtype)
     need = workspace_bytes(S, H, num_kv_heads, D, max_context_len, block_size, partition_tokens)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -384,6 +405,14 @@ class BlockManager:
                                          ctypes.byref(src), ctypes.byref(dst)))
         return slot.value, src.value, dst.value
 
+    def mark_computed(self, seq_id, num_computed_tokens):
+        """The K/V of the first num_computed_tokens tokens are written (or
+        enqueued): full blocks inside them become prefix-cache hits."""
+        _check(lib().pkv_bm_mark_computed(self._h, seq_id, num_computed_tokens))
+
+    def num_computed_tokens(self, seq_id):
+        return _check(lib().pkv_bm_num_computed_tokens(self._h, seq_id))
+
     def fork(self, parent_id, child_id):
         _check(lib().pkv_bm_fork(self._h, parent_id, child_id))
 
@@ -465,20 +494,26 @@ def copy_blocks(k_layers, v_layers, pairs, num_blocks, num_kv_heads, head_dim, b
 
 def paged_attention_prefill(out, q, k_cache, v_cache, block_tables, context_lens, query_start_loc,
                             max_query_len, max_context_len, num_kv_heads, block_size, kv_dtype,
-                            scale, k_scale=1.0, v_scale=1.0, stream=None):
+                            scale, k_scale=1.0, v_scale=1.0, num_blocks=0, stream=None):
     """Multi-token causal attention over the paged cache.  q, out:
-    [num_query_tokens][H][d]; query_start_loc: device int32 [S + 1]."""
+    [num_query_tokens][H][d]; query_start_loc: device int32 [S + 1].
+    max_query_len=None reads the longest chunk from query_start_loc (a
+    device-to-host copy, which synchronises).  num_blocks = 0 clamps block
+    ids to the blocks the pool tensors hold."""
     T, H, D = q.shape
     S = context_lens.shape[0]
     if query_start_loc.shape[0] != S + 1:
         raise ValueError("query_start_loc must have num_seqs + 1 entries")
+    if max_query_len is None:
+        max_query_len = int(torch.diff(query_start_loc).max().item()) if S > 0 else 0
+    num_blocks = _pool_blocks(k_cache, v_cache, num_blocks, num_kv_heads, D, block_size, kv_dtype)
     _check(lib().paged_attention_prefill(
         _ptr(out, "out", q.dtype), _ptr(q, "q"), dtype_code(q.dtype), _ptr(k_cache, "k_cache"),
         _ptr(v_cache, "v_cache"), _ptr(block_tables, "block_tables", torch.int32),
         block_tables.shape[1], _ptr(context_lens, "context_lens", torch.int32),
         _ptr(query_start_loc, "query_start_loc", torch.int32), int(max_query_len),
-        int(max_context_len), S, H, num_kv_heads, D, float(scale), block_size, kv_dtype,
-        float(k_scale), float(v_scale), _stream(stream)))
+        int(max_context_len), S, H, num_kv_heads, D, float(scale), block_size, num_blocks,
+        kv_dtype, float(k_scale), float(v_scale), _stream(stream)))
 
 
 def paged_attention_decode_tokens(out, q, k_cache, v_cache, token_slots, context_lens,
@@ -486,6 +521,7 @@ def paged_attention_decode_tokens(out, q, k_cache, v_cache, token_slots, context
                                   k_scale=1.0, v_scale=1.0, stream=None):
     """Decode reading logical token t of sequence s from slot token_slots[s][t]."""
     S, H, D = q.shape
+    _pool_blocks(k_cache, v_cache, num_blocks, num_kv_heads, D, block_size, kv_dtype)
     _check(lib().paged_attention_decode_tokens(
         _ptr(out, "out", q.dtype), _ptr(q, "q"), dtype_code(q.dtype), _ptr(k_cache, "k_cache"),
         _ptr(v_cache, "v_cache"), _ptr(token_slots, "token_slots", torch.int32),

@@ -308,7 +308,8 @@ int32_t paged_attention_plan(const int32_t* context_lens, int32_t num_seqs, int3
         return fail(PKV_ERR_ARG, "bad plan arguments");
     if (!plan || (num_seqs > 0 && !context_lens)) return fail(PKV_ERR_ARG, "null pointer");
     const int32_t ctx_cap = ctx_cap_of(max_context_len, max_blocks_per_seq, block_size);
-    const int32_t part = resolve_partition(partition_tokens, num_seqs, num_kv_heads, ctx_cap, block_size);
+    // the split size comes from max_context_len alone, as in the size queries
+    const int32_t part = resolve_partition(partition_tokens, num_seqs, num_kv_heads, max_context_len, block_size);
     if (part % block_size) return fail(PKV_ERR_ARG, "partition_tokens %d is not a multiple of block_size %d", part, block_size);
     const int64_t need = plan_bytes_of(num_seqs, num_parts_of(ctx_cap, part));
     if (plan_bytes < need) return fail(PKV_ERR_SIZE, "plan needs %lld bytes, got %lld", (long long)need, (long long)plan_bytes);
@@ -353,7 +354,10 @@ int32_t paged_attention_decode_ex(void* out, const void* q, int32_t q_dtype, con
         return fail(PKV_ERR_ARG, "null pointer");
 
     const int32_t ctx_cap = ctx_cap_of(max_context_len, max_blocks_per_seq, block_size);
-    const int32_t part_tokens = resolve_partition(o.partition_tokens, num_seqs, num_kv_heads, ctx_cap, block_size);
+    // The split size comes from max_context_len alone, as in
+    // paged_attention_workspace_bytes / _plan_bytes; the partition count from
+    // the (possibly smaller) clamped context, so it never exceeds theirs.
+    const int32_t part_tokens = resolve_partition(o.partition_tokens, num_seqs, num_kv_heads, max_context_len, block_size);
     if (part_tokens < block_size || part_tokens % block_size)
         return fail(PKV_ERR_ARG, "partition_tokens %d must be a positive multiple of block_size %d", part_tokens, block_size);
     const int64_t num_parts = num_parts_of(ctx_cap, part_tokens);
@@ -412,12 +416,12 @@ int32_t paged_attention_prefill(void* out, const void* q, int32_t q_dtype, const
                                 const int32_t* query_start_loc, int32_t max_query_len,
                                 int32_t max_context_len, int32_t num_seqs, int32_t num_heads,
                                 int32_t num_kv_heads, int32_t head_dim, float scale,
-                                int32_t block_size, int32_t kv_dtype, float k_scale, float v_scale,
-                                pkv_stream_t stream) {
+                                int32_t block_size, int32_t num_blocks, int32_t kv_dtype,
+                                float k_scale, float v_scale, pkv_stream_t stream) {
     if (int32_t e = check_layout_args(head_dim, block_size, kv_dtype)) return e;
     if (q_dtype != PKV_BF16 && q_dtype != PKV_FP16) return fail(PKV_ERR_ARG, "q_dtype must be bf16 or fp16");
     if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || max_context_len < 0 ||
-        max_blocks_per_seq < 0 || max_query_len < 0)
+        max_blocks_per_seq < 0 || max_query_len < 0 || num_blocks < 0)
         return fail(PKV_ERR_ARG, "bad sizes");
     if (num_heads % num_kv_heads) return fail(PKV_ERR_ARG, "num_heads %d is not a multiple of num_kv_heads %d", num_heads, num_kv_heads);
     const int32_t G = num_heads / num_kv_heads;
@@ -450,7 +454,7 @@ int32_t paged_attention_prefill(void* out, const void* q, int32_t q_dtype, const
     a.group = G;
     a.part_blocks = std::max(1, max_blocks_per_seq);   // one partition: the whole context
     a.num_parts = 1;
-    a.num_blocks = 0;
+    a.num_blocks = num_blocks;
     const float ks = kv_dtype == PKV_FP8_E4M3 ? k_scale : 1.0f;
     a.qk_scale_log2 = (float)((double)scale * (double)ks * 1.4426950408889634);
     a.out_scale = kv_dtype == PKV_FP8_E4M3 ? v_scale : 1.0f;

@@ -22,6 +22,16 @@
 //     first, and a request returns its blocks last-block first, so the tail
 //     of a cached prompt is given up before its head.
 //
+// "Only full blocks are cached" is read together with chunked prefill (§6),
+// which computes a prompt's K/V over several steps: a block counts as full
+// once the K/V of its last token is computed.  A block therefore becomes
+// findable only when the caller marks the tokens up to its end computed
+// (pkv_bm_mark_computed, once the step that writes them is enqueued); a
+// prompt's hit blocks are computed from the start, and a token appended to a
+// sequence whose every token is computed counts as computed at once (the
+// decode step that appends it writes its K/V).  A block freed before it was
+// computed was never findable and returns as a clean block.
+//
 // Reading where the pages leave the order open (their own block-level model
 // of the LRU experiment in §10 takes it): a free block that holds no cached
 // content (never used, or a partial block, which has no hash) is handed out
@@ -86,6 +96,7 @@ struct Sequence {
     bool fragmented = false;       // tokens evicted and not yet repacked
     bool evicted = false;          // ever lost tokens: its K/V match no prompt, never published
     int32_t num_tokens = 0;
+    int32_t num_computed = 0;      // leading tokens whose K/V are written
     uint64_t seed = 0;
 };
 
@@ -152,6 +163,17 @@ struct BlockManager {
         parent[b] = p;
         std::memcpy(&content[(size_t)b * block_size], toks, sizeof(int32_t) * (size_t)block_size);
         by_hash.emplace(h, b);
+    }
+    // The K/V of the sequence's first n tokens are written: publish its full
+    // blocks that end inside them and did not end inside the old count.
+    void mark_computed(Sequence& sq, int32_t n) {
+        const int32_t old = sq.num_computed;
+        if (n <= old) return;
+        sq.num_computed = n;
+        if (!prefix_cache || sq.evicted) return;
+        const int32_t bs = block_size;
+        for (int32_t j = old / bs; j < (int32_t)sq.chain.size() && (j + 1) * bs <= n; ++j)
+            publish(sq.blocks[j], sq.chain[j], j ? sq.chain[j - 1] : sq.seed, &sq.tokens[(size_t)j * bs]);
     }
     // The cached block holding (h, p, toks), or -1.
     int32_t lookup(uint64_t h, uint64_t p, const int32_t* toks) const {
@@ -289,14 +311,10 @@ int32_t pkv_bm_add_sequence(pkv_block_manager* bm, int64_t seq_id, const int32_t
         ++m.ref[b];
         sq.blocks.push_back(b);
     }
-    for (int32_t j = (int32_t)hits.size(); j < nblk; ++j) {
-        const int32_t b = m.take();
-        sq.blocks.push_back(b);
-        if (m.prefix_cache && j < nfull)
-            m.publish(b, chain[j], j ? chain[j - 1] : seed, tokens + (int64_t)j * bs);
-    }
+    for (int32_t j = (int32_t)hits.size(); j < nblk; ++j) sq.blocks.push_back(m.take());
     sq.chain = std::move(chain);
     sq.num_tokens = num_tokens;
+    sq.num_computed = (int32_t)hits.size() * bs;   // the hit blocks hold their K/V already
     sq.seed = seed;
     m.seqs.emplace(seq_id, std::move(sq));
     if (num_cached_tokens) *num_cached_tokens = (int32_t)hits.size() * bs;
@@ -329,16 +347,34 @@ int32_t pkv_bm_append_token(pkv_block_manager* bm, int64_t seq_id, int32_t token
         sq->tokens.push_back(token);
         if (off == bs - 1) {
             const uint64_t p = j ? sq->chain[j - 1] : sq->seed;
-            const uint64_t h = pkv::block_hash(p, &sq->tokens[(size_t)j * bs], bs);
-            sq->chain.push_back(h);
-            m.publish(sq->blocks[j], h, p, &sq->tokens[(size_t)j * bs]);
+            sq->chain.push_back(pkv::block_hash(p, &sq->tokens[(size_t)j * bs], bs));
         }
     }
+    const bool all_computed = sq->num_computed == sq->num_tokens;
     ++sq->num_tokens;
+    if (all_computed) m.mark_computed(*sq, sq->num_tokens);   // a decode step writes it
     *slot = sq->blocks[j] * bs + off;
     if (cow_src) *cow_src = src;
     if (cow_dst) *cow_dst = dst;
     return ok();
+}
+
+int32_t pkv_bm_mark_computed(pkv_block_manager* bm, int64_t seq_id, int32_t num_computed_tokens) {
+    if (!bm) return fail(PKV_ERR_ARG, "null handle");
+    pkv::Sequence* sq = find_seq(bm, seq_id);
+    if (!sq) return fail(PKV_ERR_ARG, "unknown sequence %lld", (long long)seq_id);
+    if (num_computed_tokens < 0 || num_computed_tokens > sq->num_tokens)
+        return fail(PKV_ERR_ARG, "computed count %d outside the sequence's %d tokens", num_computed_tokens,
+                    sq->num_tokens);
+    bm->m.mark_computed(*sq, num_computed_tokens);
+    return ok();
+}
+
+int32_t pkv_bm_num_computed_tokens(const pkv_block_manager* bm, int64_t seq_id) {
+    if (!bm) return fail(PKV_ERR_ARG, "null handle");
+    const pkv::Sequence* sq = find_seq(const_cast<pkv_block_manager*>(bm), seq_id);
+    if (!sq) return fail(PKV_ERR_ARG, "unknown sequence %lld", (long long)seq_id);
+    return sq->num_computed;
 }
 
 int32_t pkv_bm_fork(pkv_block_manager* bm, int64_t parent_id, int64_t child_id) {
@@ -427,6 +463,7 @@ int32_t pkv_bm_evict_tokens(pkv_block_manager* bm, int64_t seq_id, const uint8_t
     sq->tokens.clear();            // only needed to publish, which an evicted sequence never does
     sq->chain.clear();
     sq->num_tokens = (int32_t)sq->slots.size();
+    sq->num_computed = sq->num_tokens;
     sq->fragmented = true;
     sq->evicted = true;
     return ok();

@@ -203,6 +203,11 @@ __host__ __device__ constexpr int staged_kvt(int kvt, int qt) {
 // slack, so the first key a column sees replaces it, with alpha =
 // 2^(-FLT_MAX - m) = 0 for the empty sums.
 constexpr float kNoKeyMax = -3.402823466e38f;
+// Logit of a key a column must not see (causal limit, context end): finite,
+// so that kMaskedLogit * cs is finite or -inf for every cs >= 0 (cs = 0
+// included) and never NaN; its weight is set to 0 by a select.  No real
+// logit of finite 16-bit inputs is this value.
+constexpr float kMaskedLogit = -3.402823466e38f;
 
 // One unit pair of a stage: logits, online softmax and PV for the wave's two
 // column tiles.  masked (uniform): apply each column's causal limit; pairs
@@ -261,9 +266,11 @@ __device__ __forceinline__ void staged_pair(Math& mt, const uint8_t* stage, int 
     };
     u32x4_t vop[8];
     if constexpr (!LATE_V) read_v(vop);
-    // raw logits; the scale (cs > 0) goes into the maxima and into the
-    // exponent's fused multiply-add; keys a column must not see are -inf for
-    // the max and get weight 0 below
+    // raw logits; the scale (cs >= 0) goes into the maxima and into the
+    // exponent's fused multiply-add; keys a column must not see hold the
+    // finite kMaskedLogit for the max and get weight 0 below (finite, so
+    // that no product with cs = 0 is ever a NaN: this file is built assuming
+    // none occurs)
     float y[NT][8];
 #pragma unroll
     for (int t = 0; t < NT; ++t)
@@ -279,13 +286,15 @@ __device__ __forceinline__ void staged_pair(Math& mt, const uint8_t* stage, int 
             for (int u = 0; u < 2; ++u)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    y[t][4 * u + i] = (ta + 16 * u + i) < mt.lim[t] ? y[t][4 * u + i] : -INFINITY;
+                    y[t][4 * u + i] = (ta + 16 * u + i) < mt.lim[t] ? y[t][4 * u + i] : kMaskedLogit;
     }
     // The rescale test needs only this lane's own maximum: a column's scaled
     // maximum passes m + slack exactly when one of its lanes' does (cs >= 0
-    // and rounding keep the order; a lane of -inf keys gives -inf, or NaN
-    // when cs = 0, and neither passes).  The column maximum across lanes is
-    // formed only inside the rare rescale branch.
+    // and rounding keep the order).  A lane whose keys are all masked may
+    // pass once, while its column has seen no key (kMaskedLogit * cs >
+    // kNoKeyMax for cs < 1); that rescale multiplies empty sums by 0 and is
+    // harmless.  The column maximum across lanes is formed only inside the
+    // rare rescale branch.
     float mx[NT];
     bool jump = false;
 #pragma unroll
@@ -298,8 +307,7 @@ __device__ __forceinline__ void staged_pair(Math& mt, const uint8_t* stage, int 
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             const float rm = rows_max(mx[t]);
-            const float bm = rm == -INFINITY ? -INFINITY : rm * cs;
-            const float mn = fmaxf(mt.m[t], bm);
+            const float mn = fmaxf(mt.m[t], rm * cs);
             const float alpha = fast_exp2(mt.m[t] - mn);   // 0 when leaving kNoKeyMax
             mt.l[t] *= alpha;
 #pragma unroll
@@ -310,15 +318,14 @@ __device__ __forceinline__ void staged_pair(Math& mt, const uint8_t* stage, int 
     u32x4_t pf[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-        // 2^(-inf - m) = 0 for masked keys (the select below covers cs = 0);
-        // m is finite (a column that has seen no key holds kNoKeyMax, and
-        // then all its keys here are -inf)
+        // masked keys: the select below gives them weight 0 (their exponent
+        // is finite or -inf, never NaN); m is finite
         float pv[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) pv[j] = fast_exp2(fmaf(y[t][j], cs, -mt.m[t]));
         if (masked) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) pv[j] = y[t][j] == -INFINITY ? 0.f : pv[j];
+            for (int j = 0; j < 8; ++j) pv[j] = y[t][j] == kMaskedLogit ? 0.f : pv[j];
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) pf[t][j] = pack2<QT>(pv[2 * j], pv[2 * j + 1]);

@@ -143,3 +143,23 @@ def test_pool_handle_host_side():
     out = pkv._binding.PoolDesc()
     assert L.kv_pool_get_desc(h, ctypes.byref(out)) == 0 and out.num_blocks == 10
     assert L.kv_pool_destroy(h) == 0
+
+
+def test_binding_rejects_pool_tensors_smaller_than_num_blocks():
+    """The binding checks that the pool tensors hold num_blocks blocks before
+    any launch (a larger num_blocks would let slot checks pass for writes
+    past the tensors)."""
+    import torch
+    n = pkv.layer_pool_bytes(8, 2, 128, 16, pkv.BF16)
+    small = torch.zeros(n, dtype=torch.uint8)
+    kv = torch.zeros(1, 2, 128, dtype=torch.bfloat16)
+    slots = torch.zeros(1, dtype=torch.int32)
+    with pytest.raises(ValueError, match="blocks need"):
+        pkv.reshape_and_cache(kv, kv, small, small, slots, 16, 9, pkv.BF16)
+
+
+def test_prefill_rejects_negative_num_blocks():
+    lib = pkv.lib()
+    rc = lib.paged_attention_prefill(None, None, pkv.BF16, None, None, None, 0, None, None, 0, 0, 0,
+                                     8, 2, 128, 0.1, 16, -1, pkv.BF16, 1.0, 1.0, None)
+    assert rc == -1 and "sizes" in pkv.last_error()

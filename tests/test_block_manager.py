@@ -44,6 +44,7 @@ def run_passes(make):
         hits = 0
         for d in order:
             hits += pool.add_sequence(sid, docs[d])
+            pool.mark_computed(sid, len(docs[d]))      # the whole prompt is prefilled
             pool.free_sequence(sid)
             sid += 1
         res.append(hits)
@@ -88,6 +89,7 @@ def test_diagram_request_a_and_b(impl):
     a = list(range(100, 138))
     b = a[:16] + [7, 7, 7, 7, 7]
     assert pool.add_sequence(1, a) == 0
+    pool.mark_computed(1, len(a))
     ta = pool.block_table(1)
     assert len(ta) == 3 and len(ta) * 16 - len(a) == 10
     assert pool.add_sequence(2, b) == 16
@@ -102,6 +104,7 @@ def test_hits_are_whole_blocks_and_leave_the_last_token(impl):
     bm = make(impl, 64, 16, True)
     p = list(range(48))                               # exactly 3 full blocks
     bm.add_sequence(1, p)
+    bm.mark_computed(1, 48)
     bm.free_sequence(1)
     assert bm.add_sequence(2, p) == 32                # last token recomputed
     bm.free_sequence(2)
@@ -115,8 +118,75 @@ def test_extra_key_separates_prompts(impl):
     bm = make(impl, 64, 16, True)
     p = list(range(40))
     bm.add_sequence(1, p, extra_key=5)
+    bm.mark_computed(1, 40)
     assert bm.add_sequence(2, p, extra_key=6) == 0
     assert bm.add_sequence(3, p, extra_key=5) == 32
+
+
+@BOTH
+def test_blocks_are_hits_only_once_computed(impl):
+    """[P1] §5 caches only full blocks; with chunked prefill (§6) a prompt's
+    blocks fill over several steps, so a block is a hit only once the K/V of
+    its last token is computed (mark_computed)."""
+    bm = make(impl, 64, 16, True)
+    p = list(range(100))                              # 6 full blocks + 4 tokens
+    assert bm.add_sequence(1, p) == 0
+    assert bm.num_computed_tokens(1) == 0
+    assert bm.add_sequence(2, p) == 0                 # nothing computed yet: no hit
+    bm.mark_computed(1, 40)                           # first chunk: blocks 0, 1 full
+    assert bm.num_computed_tokens(1) == 40
+    assert bm.add_sequence(3, p) == 32
+    assert bm.num_computed_tokens(3) == 32            # the hit tokens count as computed
+    bm.mark_computed(1, 20)                           # counts never go back
+    assert bm.num_computed_tokens(1) == 40
+    bm.mark_computed(1, 100)
+    assert bm.add_sequence(4, p) == 96
+    ta, t4 = bm.block_table(1), bm.block_table(4)
+    assert t4[:6] == ta[:6] and t4[6] != ta[6]
+
+
+@BOTH
+def test_freed_before_computed_is_never_a_hit(impl):
+    """A request freed before its prefill ran leaves no cached content: its
+    blocks go back clean and a later equal prompt gets no hit."""
+    bm = make(impl, 64, 16, True)
+    p = list(range(64))
+    bm.add_sequence(1, p)
+    bm.mark_computed(1, 16)                           # only block 0 computed
+    bm.free_sequence(1)
+    assert bm.num_cached_free_blocks() == 1
+    assert bm.add_sequence(2, p) == 16
+
+
+@BOTH
+def test_decode_tokens_count_as_computed(impl):
+    """A token appended to a fully computed sequence is written by the same
+    decode step: the block it fills is a hit at once.  Appended to a
+    sequence with uncomputed prompt tokens, it waits for mark_computed."""
+    bm = make(impl, 64, 16, True)
+    p = list(range(30))
+    bm.add_sequence(1, p)
+    bm.mark_computed(1, 30)
+    bm.append_token(1, 30)
+    bm.append_token(1, 31)                            # fills block 1
+    assert bm.num_computed_tokens(1) == 32
+    assert bm.add_sequence(2, list(range(40))) == 32
+    bm.add_sequence(3, [5] * 30)
+    for t in range(2):
+        bm.append_token(3, 5)
+    assert bm.num_computed_tokens(3) == 0
+    assert bm.add_sequence(4, [5] * 40) == 0
+    bm.mark_computed(3, 32)
+    assert bm.add_sequence(5, [5] * 40) == 32
+
+
+def test_mark_computed_errors():
+    bm = pkv.BlockManager(8, 16, True)
+    bm.add_sequence(1, [1, 2, 3])
+    for bad in (lambda: bm.mark_computed(1, 4), lambda: bm.mark_computed(1, -1),
+                lambda: bm.mark_computed(2, 1), lambda: bm.num_computed_tokens(2)):
+        with pytest.raises(pkv.PagedKVError):
+            bad()
 
 
 @BOTH
@@ -195,6 +265,9 @@ def test_random_operations_match_model(prefix, bs, seed):
                 got = lib_.add_sequence(next_id, toks)
                 assert got == want
                 live.append(next_id)
+                if rng.random() < 0.6:                # the whole prompt prefilled at once
+                    ref.mark_computed(next_id, len(toks))
+                    lib_.mark_computed(next_id, len(toks))
             next_id += 1
         elif op < 0.7:
             s = rng.choice(live)
@@ -212,6 +285,12 @@ def test_random_operations_match_model(prefix, bs, seed):
             lib_.fork(s, next_id)
             live.append(next_id)
             next_id += 1
+        elif op < 0.9:
+            s = rng.choice(live)
+            n = rng.randrange(len(ref.seqs[s]["tokens"]) + 1)
+            ref.mark_computed(s, n)
+            lib_.mark_computed(s, n)
+            assert lib_.num_computed_tokens(s) == ref.num_computed_tokens(s)
         else:
             s = live.pop(rng.randrange(len(live)))
             ref.free_sequence(s)
@@ -260,6 +339,9 @@ def test_evict_and_repack_match_model(prefix, bs, seed):
             else:
                 assert lib_.add_sequence(next_id, toks) == want
                 live.append(next_id)
+                if rng.random() < 0.7:
+                    ref.mark_computed(next_id, len(toks))
+                    lib_.mark_computed(next_id, len(toks))
             next_id += 1
             continue
         s = rng.choice(live)

@@ -337,6 +337,32 @@ def test_decode_shared_prefix_bitwise():
         assert np.array_equal(got[0], got[1]) and np.array_equal(got[0], got[2])
 
 
+@pytest.mark.parametrize("part", [64, 0])
+def test_decode_nan_query_row_stays_confined(part):
+    """A NaN in one query row (one sequence, one head) poisons that output
+    row only: the other heads of its kv-head group share every MFMA with it
+    but not a column, and the merge and reduce work per head.  The other
+    rows match the oracle (not bitwise: the NaN column never asks for a
+    rescale, which changes when its neighbours are rescaled)."""
+    log(f"decode NaN query row part={part}")
+    lengths = [40, 300, 129, 1000]
+    H, Hkv = 8, 2
+    tabs, qb, kp, vp = make_case(lengths, H, Hkv, 16, oracle.BF16, oracle.BF16, seed=4)
+    want = oracle.paged_decode(qb, oracle.BF16, kp, vp, oracle.BF16, tabs.block_tables,
+                               tabs.context_lens, Hkv, 16, SCALE)
+    bad = qb.copy()
+    bad[2, 5, 17] = 0x7FC0                                 # a quiet NaN in one element
+    got = gpu_decode(bad, oracle.BF16, kp, vp, oracle.BF16, tabs.block_tables,
+                     tabs.context_lens, Hkv, 16, SCALE, part=part, num_blocks=tabs.num_blocks)
+    assert np.isnan(got[2, 5]).all()
+    mask = np.ones(got.shape[:2], bool)
+    mask[2, 5] = False
+    assert np.isfinite(got[mask]).all()
+    err = float(np.abs(got[mask] - want[mask]).max())
+    log(f"  other rows max-abs {err:.3e}")
+    assert err <= TOL[oracle.BF16]
+
+
 def test_decode_step_tiny():
     """One decode step of the tiny workload: slots from the tables, cache
     write of the 4 new tokens, then attention — GPU vs oracle end to end."""
