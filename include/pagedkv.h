@@ -319,6 +319,32 @@ int32_t paged_attention_decode(void* out, const void* q, int32_t q_dtype,
                                float k_scale, float v_scale, void* workspace,
                                int64_t workspace_bytes, pkv_stream_t stream);
 
+/* Allocation-free decode, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same operation, arguments and kernels as
+ * paged_attention_decode, without the workspace arguments: the work plan and
+ * partition partials live in a static device array of
+ * PKV_NOALLOC_SCRATCH_BYTES bytes that the library holds on every GPU it runs
+ * on until the process ends.  Allocates nothing and calls no allocating
+ * routine.  A call whose workspace (paged_attention_workspace_bytes with the
+ * default split) exceeds that size fails with PKV_ERR_SIZE before anything
+ * is launched.  All calls on one GPU share its array and each fully rewrites
+ * what it reads: calls that overlap on one GPU (concurrent streams, or
+ * threads) race and must be serialised by the caller.  Errors: as
+ * paged_attention_decode. */
+#define PKV_NOALLOC_SCRATCH_BYTES (16ll << 20)
+int32_t paged_attention_decode_noalloc(void* out, const void* q, int32_t q_dtype,
+                                       const void* k_cache, const void* v_cache,
+                                       const int32_t* block_tables,
+                                       int32_t max_blocks_per_seq,
+                                       const int32_t* context_lens,
+                                       int32_t max_context_len, int32_t num_seqs,
+                                       int32_t num_heads, int32_t num_kv_heads,
+                                       int32_t head_dim, float scale,
+                                       int32_t block_size, int32_t kv_dtype,
+                                       float k_scale, float v_scale,
+                                       pkv_stream_t stream);
+
 /* Same as paged_attention_decode with explicit options (NULL = defaults).
  * With opts->num_blocks > 0, block ids outside [0, num_blocks) are read as
  * the null block 0 instead of faulting. */

@@ -33,7 +33,7 @@ EXPORTS = [
     "pkv_bm_token_slots", "paged_attention_decode_tokens", "pkv_move_tokens_scratch_bytes",
     "pkv_move_tokens", "pkv_bm_repack_tiles", "pkv_repack_blocks",
     "pkv_read_probe_sink_bytes", "pkv_read_probe", "kv_pool_bytes_per_token",
-    "pkv_bm_mark_computed", "pkv_bm_num_computed_tokens",
+    "pkv_bm_mark_computed", "pkv_bm_num_computed_tokens", "paged_attention_decode_noalloc",
 ]
 
 
@@ -90,6 +90,8 @@ def lib():
             "paged_attention_decode_ex": (i32, [p, p, i32, p, p, p, i32, p, i32, i32, i32, i32,
                                                 i32, f32, i32, i32, f32, f32, p, i64,
                                                 ctypes.POINTER(DecodeOpts), p]),
+            "paged_attention_decode_noalloc": (i32, [p, p, i32, p, p, p, i32, p, i32, i32, i32,
+                                                     i32, i32, f32, i32, i32, f32, f32, p]),
             "pkv_check_block_tables": (i32, [p, i32, p, i32, i32, i32, p,
                                              ctypes.POINTER(ctypes.c_int64), p]),
             "pkv_read_probe_sink_bytes": (i64, []),
