@@ -27,6 +27,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0   # MI355X published HBM3E bandwidth
+ROTATE_BYTES = 1 << 30  # K/V read between two uses of one pool copy (>> 256 MB cache)
 
 
 def parse():
@@ -145,24 +146,41 @@ def main():
     fp8_scale = float(np.float32(8.0 / 448.0))
     ks = vs = fp8_scale if kv_dtype == pkv.FP8_E4M3 else 1.0
 
-    print(f"[bench] {cfg.description}; layers={L} kv={kv_dtype} bs={bs} blocks={nb}",
-          file=sys.stderr, flush=True)
+    kv_bytes = int(ctx.astype(np.int64).sum()) * 2 * Hkv * D * b_kv
+    # Cache hygiene: the MI355X's 256 MB last-level cache (and 4 MB L2 per
+    # XCD) would hold a small workload's pools between launches.  Each launch
+    # therefore gets its own copy of the layer's pools, queries and outputs,
+    # NP copies in rotation with NP * (K/V bytes) >= ROTATE_BYTES, so that
+    # at least that much other memory is read between two uses of one copy.
+    # A workload of many large layers rotates through its layers as it is.
+    NP = max(L, -(-ROTATE_BYTES // max(kv_bytes, 1)))
+    print(f"[bench] {cfg.description}; layers={L} kv={kv_dtype} bs={bs} blocks={nb} "
+          f"pool copies in rotation={NP}", file=sys.stderr, flush=True)
     t0 = time.time()
     pool_bytes = pkv.layer_pool_bytes(nb, Hkv, D, bs, kv_dtype)
     kpools, vpools = [], []
-    for layer in range(L):
-        k = torch.empty(pool_bytes, dtype=torch.uint8, device=dev)
-        v = torch.empty(pool_bytes, dtype=torch.uint8, device=dev)
-        workloads.device_fill_normal(k, kv_dtype, 1000 + layer, scale=fp8_scale)
-        workloads.device_fill_normal(v, kv_dtype, 2000 + layer, scale=fp8_scale)
-        kpools.append(k)
-        vpools.append(v)
+    if NP > L:
+        # one slab per side, sliced into NP pools
+        kslab = torch.empty(NP * pool_bytes, dtype=torch.uint8, device=dev)
+        vslab = torch.empty(NP * pool_bytes, dtype=torch.uint8, device=dev)
+        workloads.device_fill_normal(kslab, kv_dtype, 1000, scale=fp8_scale)
+        workloads.device_fill_normal(vslab, kv_dtype, 2000, scale=fp8_scale)
+        kpools = [kslab[i * pool_bytes:(i + 1) * pool_bytes] for i in range(NP)]
+        vpools = [vslab[i * pool_bytes:(i + 1) * pool_bytes] for i in range(NP)]
+    else:
+        for layer in range(NP):
+            k = torch.empty(pool_bytes, dtype=torch.uint8, device=dev)
+            v = torch.empty(pool_bytes, dtype=torch.uint8, device=dev)
+            workloads.device_fill_normal(k, kv_dtype, 1000 + layer, scale=fp8_scale)
+            workloads.device_fill_normal(v, kv_dtype, 2000 + layer, scale=fp8_scale)
+            kpools.append(k)
+            vpools.append(v)
     gen = torch.Generator(device=dev)
     gen.manual_seed(args.seed + 7)
-    qs = [torch.randn(S, H, D, generator=gen, device=dev).to(tq) for _ in range(L)]
-    newk = [torch.randn(S, Hkv, D, generator=gen, device=dev).to(tq) for _ in range(L)]
-    newv = [torch.randn(S, Hkv, D, generator=gen, device=dev).to(tq) for _ in range(L)]
-    outs = [torch.empty(S, H, D, dtype=tq, device=dev) for _ in range(L)]
+    qs = [torch.randn(S, H, D, generator=gen, device=dev).to(tq) for _ in range(NP)]
+    newk = [torch.randn(S, Hkv, D, generator=gen, device=dev).to(tq) for _ in range(NP)]
+    newv = [torch.randn(S, Hkv, D, generator=gen, device=dev).to(tq) for _ in range(NP)]
+    outs = [torch.empty(S, H, D, dtype=tq, device=dev) for _ in range(NP)]
     bt = torch.from_numpy(tabs.block_tables).to(dev)
     cl = torch.from_numpy(ctx).to(dev)
     slots = torch.empty(S, dtype=torch.int32, device=dev)
@@ -174,27 +192,33 @@ def main():
     assert pkv.check_block_tables(bt, cl, bs, nb) == 0
     torch.cuda.synchronize()
     print(f"[bench] inputs resident in {time.time() - t0:.1f}s "
-          f"({2 * L * pool_bytes / 2**30:.1f} GiB of pools)", file=sys.stderr, flush=True)
+          f"({2 * NP * pool_bytes / 2**30:.1f} GiB of pools)", file=sys.stderr, flush=True)
 
     stream = torch.cuda.current_stream()
     scale = float(np.float32(1.0 / np.sqrt(D)))
+
+    rot = [0]                  # next pool copy in the rotation
 
     def step(ev=None):
         # per-step work shared by all layers: new-token slots and the work plan
         pkv.decode_slot_mapping(bt, cl, bs, slot_mapping=slots, stream=stream)
         pkv.build_plan(cl, max_ctx, bt.shape[1], Hkv, bs, part_resolved, plan=plan, stream=stream)
-        for layer in range(L):
+        base = rot[0]
+        rot[0] = (base + L) % NP
+        for li in range(L):
+            layer = (base + li) % NP
+            evl = None if ev is None else ev[li]
             pkv.reshape_and_cache(newk[layer], newv[layer], kpools[layer], vpools[layer], slots,
                                   bs, nb, kv_dtype, ks, vs, stream=stream)
-            if ev is not None:
-                ev[layer][0].record(stream)
+            if evl is not None:
+                evl[0].record(stream)
             pkv.paged_attention_decode(outs[layer], qs[layer], kpools[layer], vpools[layer], bt,
                                        cl, max_ctx, Hkv, bs, kv_dtype, scale, ks, vs,
                                        workspace=ws, partition_tokens=part_resolved, impl=impl,
                                        stages=pkv.STAGE_PARTITIONS, num_blocks=nb, plan=plan,
                                        stream=stream)
-            if ev is not None:
-                ev[layer][1].record(stream)
+            if evl is not None:
+                evl[1].record(stream)
             pkv.paged_attention_decode(outs[layer], qs[layer], kpools[layer], vpools[layer], bt,
                                        cl, max_ctx, Hkv, bs, kv_dtype, scale, ks, vs,
                                        workspace=ws, partition_tokens=part_resolved, impl=impl,
@@ -218,7 +242,6 @@ def main():
               for k in range(args.steps) for layer in range(L)]
     dec_avg_ms = float(np.mean(dec_ms))
 
-    kv_bytes = int(ctx.astype(np.int64).sum()) * 2 * Hkv * D * b_kv
     unique_kv_bytes = unique_kv_tokens(tabs.block_tables, ctx, bs, nb) * 2 * Hkv * D * b_kv
     qo_bytes = S * H * D * (2 + 2)
     new_bytes = S * Hkv * D * 2 * (2 + b_kv)
@@ -319,6 +342,15 @@ def main():
             "bytes": probe_bytes,
             "decode_frac_of_probe": round(achieved / probe_gbs, 4),
         },
+        "cache_hygiene": {
+            "pool_copies_in_rotation": NP,
+            "kv_bytes_read_between_reuse": int(NP - 1) * kv_bytes if NP > 1 else 0,
+            "note": "each launch reads its own copy of the layer's pools, q and out; "
+                    f"copies rotate so that >= {ROTATE_BYTES / 1e9:.0f} GB of other K/V is "
+                    "read between two uses of one copy (256 MB last-level cache)"
+                    if NP > L else "layers are distinct pools larger than the caches",
+        },
+        "clocks": gpu_clocks(),
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
@@ -662,6 +694,54 @@ def bench_copy_blocks(args, torch, pkv, workloads):
     }), flush=True)
 
 
+def gpu_clocks():
+    """Current GPU clocks as rocm-smi reports them (a child process, after
+    the timed region), or the reason they are missing."""
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True,
+                           timeout=30)
+        data = json.loads(r.stdout[r.stdout.index("{"):])
+    except Exception as e:            # tool missing, no JSON, timeout
+        return {"error": f"rocm-smi: {type(e).__name__}: {e}"[:200]}
+    out = {}
+    for card, vals in data.items():
+        if isinstance(vals, dict):
+            out[card] = {k.strip(" :"): v for k, v in vals.items() if "clk" in k.lower() or "clock" in k.lower()}
+    return out or {"raw": r.stdout[:400]}
+
+
+def host_info():
+    """The CPU the oracle ran on: model, logical CPUs, and this process's
+    affinity mask."""
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    aff = sorted(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else []
+    runs, start = [], None
+    for c in aff + [None]:
+        if start is None:
+            start = prev = c
+        elif c is None or c != prev + 1:
+            runs.append(f"{start}-{prev}" if prev != start else f"{start}")
+            start = prev = c
+        else:
+            prev = c
+    return {"cpu_model": model, "nproc": os.cpu_count(), "affinity": ",".join(runs),
+            "affinity_cpus": len(aff)}
+
+
+def median3(run, n):
+    """Median of three timings of run(n)."""
+    return float(np.median([run(n) for _ in range(3)]))
+
+
 _PKV2ORC = {0: 0, 1: 1, 2: 2}      # library dtype codes -> oracle dtype codes (same values)
 
 
@@ -673,17 +753,22 @@ def cpu_sample(args, what, run, work_of, unit, unit_scale, sample_desc, n_max):
     t = time.time()
     run(1)
     t1 = max(time.time() - t, 1e-6)
-    n = int(min(n_max, max(1, args.cpu_baseline_seconds / t1)))
-    t = time.time()
-    run(n)
-    tn = time.time() - t
-    print(f"[bench] cpu oracle ({what}): n={n} in {tn:.1f}s on {oracle.max_threads()} threads",
-          file=sys.stderr, flush=True)
+    n = int(min(n_max, max(1, args.cpu_baseline_seconds / 3 / t1)))
+
+    def timed(k):
+        t = time.time()
+        run(k)
+        return time.time() - t
+
+    tn = median3(timed, n)
+    print(f"[bench] cpu oracle ({what}): n={n} in {tn:.1f}s (median of 3) on "
+          f"{oracle.max_threads()} threads", file=sys.stderr, flush=True)
     return {"value": round(work_of(n) / tn / unit_scale, 6), "unit": unit,
             "cores": oracle.max_threads(), "kind": "oracle",
             "sample": sample_desc.replace(" n ", f" {n} ").replace("first n", f"first {n}")
                                  .replace("last n", f"last {n}"),
-            "seconds": round(tn, 2)}
+            "seconds": round(tn, 2), "timing": "median of 3 runs of the sample",
+            "host": host_info()}
 
 
 _HOST = {}
@@ -752,18 +837,18 @@ def cpu_baseline(args, tabs, kpool, vpool, q, q_dtype, kv_dtype, Hkv, bs, scale,
         return time.time() - t
 
     t1 = run(1)
-    n = int(min(len(ctx), max(1, args.cpu_baseline_seconds / max(t1, 1e-6))))
-    tn = run(n) if n > 1 else t1
+    n = int(min(len(ctx), max(1, args.cpu_baseline_seconds / 3 / max(t1, 1e-6))))
+    tn = median3(run, n)
     kv = int(ctx[:n].astype(np.int64).sum()) * 2 * Hkv * D * b_kv
     qo = n * H * D * 4
-    print(f"[bench] cpu oracle: {n} seqs in {tn:.1f}s on {threads} threads "
-          f"(host copy {time.time() - t0 - tn - t1:.1f}s)", file=sys.stderr, flush=True)
+    print(f"[bench] cpu oracle: {n} seqs in {tn:.1f}s (median of 3) on {threads} threads",
+          file=sys.stderr, flush=True)
     # the same oracle on one core, over a sample of about a third of the time
     oracle.set_threads(1)
     try:
         s1 = run(1)
-        n1 = int(min(n, max(1, args.cpu_baseline_seconds / 3 / max(s1, 1e-6))))
-        sn = run(n1) if n1 > 1 else s1
+        n1 = int(min(n, max(1, args.cpu_baseline_seconds / 9 / max(s1, 1e-6))))
+        sn = median3(run, n1)
     finally:
         oracle.set_threads(threads)
     kv1 = int(ctx[:n1].astype(np.int64).sum()) * 2 * Hkv * D * b_kv
@@ -777,6 +862,8 @@ def cpu_baseline(args, tabs, kpool, vpool, q, q_dtype, kv_dtype, Hkv, bs, scale,
                   f"context tokens), fp64 C oracle, OpenMP over (seq, head)",
         "seq_layers_per_s": round(n / tn, 3),
         "seconds": round(tn, 2),
+        "timing": "median of 3 runs of the sample",
+        "host": host_info(),
         "single_core": {
             "value": round((kv1 + n1 * H * D * 4) / sn / 1e9, 4),
             "unit": "GB/s",
