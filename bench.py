@@ -280,6 +280,16 @@ def main():
     if args.copy_probe_mib:
         copy_probe(torch, dev, args.copy_probe_mib)
 
+    # GPU clocks while this workload runs: about 0.6 s of steps are queued
+    # (after the timed region, outside every timing) and rocm-smi is read
+    # while they execute; then once more when the GPU is idle again
+    n_load = int(min(20000, max(1, 600.0 / max(step_ms, 1e-3))))
+    for _ in range(n_load):
+        step()
+    clocks = {"under_load": gpu_clocks(), "load_steps": n_load}
+    torch.cuda.synchronize()
+    clocks["idle_after"] = gpu_clocks()
+
     cpu = None
     if args.cpu_baseline_seconds > 0:
         cpu = cpu_baseline(args, tabs, kpools[0], vpools[0], qs[0], q_dtype, kv_dtype, Hkv, bs,
@@ -350,7 +360,7 @@ def main():
                     "read between two uses of one copy (256 MB last-level cache)"
                     if NP > L else "layers are distinct pools larger than the caches",
         },
-        "clocks": gpu_clocks(),
+        "clocks": clocks,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)

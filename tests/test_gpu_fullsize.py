@@ -85,13 +85,22 @@ def test_qwen7b_layer_full_size():
     assert part >= mc            # the bench's launch: no context split
 
 
+@pytest.mark.parametrize("layer", [13, 27])
+def test_qwen7b_other_layers_full_size(layer):
+    """Layers 13 and 27 of the 28-layer workload (their own pool values)."""
+    run_config("qwen7b", samples=_extremes("qwen7b", 2, seed=layer), layer_seed=layer)
+
+
 def test_qwen72b_fp8_full_size():
-    part, mc = run_config("qwen72b", kv_dtype=oracle.FP8, samples=[0])
+    # every sequence is split (P = 4 partitions of 8192 tokens + the reduce):
+    # six of the 32 checked element-wise
+    part, mc = run_config("qwen72b", kv_dtype=oracle.FP8, samples=[0, 5, 11, 18, 24, 31])
     assert part < mc             # split into partitions + reduce
 
 
 def test_qwen72b_bf16_full_size():
-    run_config("qwen72b", kv_dtype=oracle.BF16, samples=[31])
+    part, mc = run_config("qwen72b", kv_dtype=oracle.BF16, samples=[1, 7, 13, 20, 26, 31])
+    assert part < mc
 
 
 def test_qwen15b_full_with_shared_prefix():
