@@ -69,8 +69,9 @@
  * the A operand of a 16x16x32 matrix-core product S^T = K.Q^T.  In V, lane L
  * holds 4 consecutive tokens of dim L%16 — the A operand of a 16x16x16
  * product O^T = V^T.P^T, whose B operand (P) is in the same lane order as the
- * S^T result.  head_dim must be a multiple of 64 (128 for every shipped
- * kernel), block_size 16 or 32.  Element encodings: bf16 / fp16 bit patterns
+ * S^T result.  head_dim must be a multiple of 64; the cache write and the
+ * block-table decode are built for 64, 128 and 256, every other kernel for
+ * 128.  block_size 16 or 32.  Element encodings: bf16 / fp16 bit patterns
  * unchanged; fp8 = OCP OFP8 E4M3 ("e4m3fn": bias 7, max 448, no infinities,
  * S.1111.111 = NaN) holding round-to-nearest-even(x / scale) saturated to
  * +-448, and dequantised as code * scale.
@@ -197,7 +198,7 @@ int32_t pkv_decode_slot_mapping(const int32_t* block_tables,
  * (resp. v_scale) rounded to fp32 on the host.  Slots < 0 or >= num_blocks *
  * block_size are skipped (padding tokens).  Tokens must have distinct slots.
  * Errors: PKV_ERR_ARG, PKV_ERR_UNSUPPORTED (kv bf16/fp16 must equal
- * src_dtype), PKV_ERR_HIP. */
+ * src_dtype; head_dim not 64, 128 or 256), PKV_ERR_HIP. */
 int32_t reshape_and_cache(const void* key, const void* value,
                           int32_t src_dtype, void* k_cache, void* v_cache,
                           const int32_t* slot_mapping, int32_t num_tokens,
@@ -306,7 +307,8 @@ int32_t paged_attention_plan(const int32_t* context_lens, int32_t num_seqs,
  *                  memory.
  * num_heads must be a multiple of num_kv_heads, with G = num_heads /
  * num_kv_heads <= 16.  Errors: PKV_ERR_ARG, PKV_ERR_SIZE (workspace),
- * PKV_ERR_UNSUPPORTED (head_dim != 128, dtype pair), PKV_ERR_HIP. */
+ * PKV_ERR_UNSUPPORTED (head_dim not 64, 128 or 256 — 128 only with
+ * PKV_IMPL_VECTOR —, dtype pair), PKV_ERR_HIP. */
 int32_t paged_attention_decode(void* out, const void* q, int32_t q_dtype,
                                const void* k_cache, const void* v_cache,
                                const int32_t* block_tables,

@@ -53,6 +53,9 @@ int32_t elem_size(int32_t dt) { return dt == PKV_FP8_E4M3 ? 1 : 2; }
 bool valid_block_size(int32_t bs) { return bs == 16 || bs == 32; }
 
 constexpr int32_t kBuiltHeadDim = 128;
+// head_dim of the cache write and the block-table decode (matrix-core
+// kernels); every other kernel is built for kBuiltHeadDim only
+bool decode_head_dim(int32_t d) { return d == 64 || d == 128 || d == 256; }
 constexpr int64_t kWorkgroupsPerCu = 4;   // default split target: 4 workgroups per CU
 
 int device_cu_count() {
@@ -249,8 +252,8 @@ int32_t reshape_and_cache(const void* key, const void* value, int32_t src_dtype,
         return fail(PKV_ERR_ARG, "num_tokens >= 0, num_kv_heads > 0 and num_blocks > 0 required");
     if ((int64_t)num_blocks * block_size >= (1LL << 31))
         return fail(PKV_ERR_ARG, "num_blocks * block_size must stay below 2^31");
-    if (head_dim != kBuiltHeadDim)
-        return fail(PKV_ERR_UNSUPPORTED, "kernels are built for head_dim 128, got %d", head_dim);
+    if (!decode_head_dim(head_dim))
+        return fail(PKV_ERR_UNSUPPORTED, "reshape_and_cache is built for head_dim 64, 128 and 256, got %d", head_dim);
     if (kv_dtype != PKV_FP8_E4M3 && kv_dtype != src_dtype)
         return fail(PKV_ERR_UNSUPPORTED, "a 16-bit pool must have the source dtype");
     if (num_tokens > 0 && (!key || !value || !k_cache || !v_cache || !slot_mapping))
@@ -262,7 +265,7 @@ int32_t reshape_and_cache(const void* key, const void* value, int32_t src_dtype,
         k_inv = 1.0f / k_scale;   // IEEE fp32 division, correctly rounded
         v_inv = 1.0f / v_scale;
     }
-    pkv::RacArgs a{key, value, k_cache, v_cache, slot_mapping, num_tokens, num_kv_heads,
+    pkv::RacArgs a{key, value, k_cache, v_cache, slot_mapping, num_tokens, num_kv_heads, head_dim,
                    block_size, num_blocks, src_dtype, kv_dtype, k_inv, v_inv};
     (void)hipGetLastError();
     hipError_t e = pkv::launch_reshape_and_cache(a, (hipStream_t)stream);
@@ -338,13 +341,16 @@ int32_t paged_attention_decode_ex(void* out, const void* q, int32_t q_dtype, con
     if (num_heads % num_kv_heads) return fail(PKV_ERR_ARG, "num_heads %d is not a multiple of num_kv_heads %d", num_heads, num_kv_heads);
     const int32_t G = num_heads / num_kv_heads;
     if (G > 16) return fail(PKV_ERR_UNSUPPORTED, "query heads per kv head %d > 16", G);
-    if (head_dim != kBuiltHeadDim) return fail(PKV_ERR_UNSUPPORTED, "kernels are built for head_dim 128, got %d", head_dim);
+    if (!decode_head_dim(head_dim))
+        return fail(PKV_ERR_UNSUPPORTED, "decode is built for head_dim 64, 128 and 256, got %d", head_dim);
     if (kv_dtype != PKV_FP8_E4M3 && kv_dtype != q_dtype)
         return fail(PKV_ERR_UNSUPPORTED, "a 16-bit KV pool must have the query dtype");
     if (!std::isfinite(scale)) return fail(PKV_ERR_ARG, "scale must be finite");
     if (kv_dtype == PKV_FP8_E4M3 && !(std::isfinite(k_scale) && std::isfinite(v_scale)))
         return fail(PKV_ERR_ARG, "fp8 scales must be finite");
     if (o.impl < 0 || o.impl > 3) return fail(PKV_ERR_ARG, "impl %d unknown", o.impl);
+    if (o.impl == PKV_IMPL_VECTOR && head_dim != kBuiltHeadDim)
+        return fail(PKV_ERR_UNSUPPORTED, "the vector kernel is built for head_dim 128");
     if (o.impl == PKV_IMPL_VECTOR && G > 8) return fail(PKV_ERR_UNSUPPORTED, "vector kernel supports at most 8 query heads per kv head");
     const int32_t stages = o.stages ? o.stages : (PKV_STAGE_PARTITIONS | PKV_STAGE_REDUCE);
     if (stages & ~(PKV_STAGE_PARTITIONS | PKV_STAGE_REDUCE)) return fail(PKV_ERR_ARG, "bad stages mask");
@@ -388,6 +394,7 @@ int32_t paged_attention_decode_ex(void* out, const void* q, int32_t q_dtype, con
     a.part_blocks = part_tokens / block_size;
     a.num_parts = (int32_t)num_parts;
     a.num_blocks = o.num_blocks;
+    a.head_dim = head_dim;
     const float ks = kv_dtype == PKV_FP8_E4M3 ? k_scale : 1.0f;
     a.qk_scale_log2 = (float)((double)scale * (double)ks * 1.4426950408889634);
     a.out_scale = kv_dtype == PKV_FP8_E4M3 ? v_scale : 1.0f;
@@ -455,6 +462,7 @@ int32_t paged_attention_prefill(void* out, const void* q, int32_t q_dtype, const
     a.part_blocks = std::max(1, max_blocks_per_seq);   // one partition: the whole context
     a.num_parts = 1;
     a.num_blocks = num_blocks;
+    a.head_dim = head_dim;
     const float ks = kv_dtype == PKV_FP8_E4M3 ? k_scale : 1.0f;
     a.qk_scale_log2 = (float)((double)scale * (double)ks * 1.4426950408889634);
     a.out_scale = kv_dtype == PKV_FP8_E4M3 ? v_scale : 1.0f;
@@ -504,6 +512,7 @@ int32_t paged_attention_decode_tokens(void* out, const void* q, int32_t q_dtype,
     a.part_blocks = 1;
     a.num_parts = 1;
     a.num_blocks = num_blocks;
+    a.head_dim = head_dim;
     const float ks = kv_dtype == PKV_FP8_E4M3 ? k_scale : 1.0f;
     a.qk_scale_log2 = (float)((double)scale * (double)ks * 1.4426950408889634);
     a.out_scale = kv_dtype == PKV_FP8_E4M3 ? v_scale : 1.0f;

@@ -11,18 +11,19 @@
 
 namespace pkv {
 
-// One wave per (token, kv head); lane l owns dims 2l and 2l+1 of the
-// 128-dim row.  K: dims 2l, 2l+1 are adjacent inside one 8-dim group, so one
-// 4-byte (16-bit types) or 2-byte (fp8) store.  V: the two dims live in
-// neighbouring lanes of the V row, so two element stores.
-template <int SRC, int KVT, int BS>
+// One wave per (token, kv head); lane l owns dims k0 = 2l + 128 i and k0 + 1
+// of the D-dim row (D = head_dim: 64, 128 or 256).  K: dims k0, k0 + 1 are
+// adjacent inside one 8-dim group, so one 4-byte (16-bit types) or 2-byte
+// (fp8) store.  V: the two dims live in neighbouring lanes of the V row, so
+// two element stores.
+template <int SRC, int KVT, int BS, int D>
 __global__ __launch_bounds__(64) void reshape_and_cache_kernel(
     const uint16_t* __restrict__ key, const uint16_t* __restrict__ value,
     uint8_t* __restrict__ k_cache, uint8_t* __restrict__ v_cache,
     const int32_t* __restrict__ slot_mapping, int32_t num_kv_heads,
     int64_t num_slots, float k_inv, float v_inv) {
     constexpr int EB = elem_bytes(KVT);
-    constexpr int64_t SUB = sub_tile_bytes(KVT);
+    constexpr int64_t SUB = sub_tile_bytes(KVT, D);
     constexpr int64_t TILE = SUB * (BS / kSubTokens);
     const int t = blockIdx.x, g = blockIdx.y, lane = threadIdx.x;
     const int64_t slot = slot_mapping[t];
@@ -32,11 +33,12 @@ __global__ __launch_bounds__(64) void reshape_and_cache_kernel(
     const int r = row % kSubTokens;
     const int64_t base = (pb * num_kv_heads + g) * TILE + (row / kSubTokens) * SUB;
 
-    const int64_t src = ((int64_t)t * num_kv_heads + g) * kHeadDim + 2 * lane;
+#pragma unroll
+    for (int k0 = 2 * lane; k0 < D; k0 += 2 * kWave) {
+    const int64_t src = ((int64_t)t * num_kv_heads + g) * D + k0;
     const uint32_t kw = *reinterpret_cast<const uint32_t*>(key + src);
     const uint32_t vw = *reinterpret_cast<const uint32_t*>(value + src);
 
-    const int k0 = 2 * lane;
     // K position of (r, k0): group c = k0/8 -> lane r + 16*(c%4), row c/4.
     const int kc = k0 / 8, kkk = kc / 4;
     const int k_lane = r + 16 * (kc % 4);
@@ -62,6 +64,7 @@ __global__ __launch_bounds__(64) void reshape_and_cache_kernel(
         *reinterpret_cast<uint32_t*>(k_cache + base + k_off) = kw;
         *reinterpret_cast<uint16_t*>(v_cache + base + v_off0) = (uint16_t)(vw & 0xffffu);
         *reinterpret_cast<uint16_t*>(v_cache + base + v_off1) = (uint16_t)(vw >> 16);
+    }
     }
 }
 
@@ -117,19 +120,26 @@ __global__ __launch_bounds__(256) void fill_pattern_kernel(uint8_t* __restrict__
 
 // ----------------------------------------------------------------- launch --
 
-template <int SRC, int KVT, int BS>
+template <int SRC, int KVT, int BS, int D>
 static hipError_t launch_rac(const RacArgs& a, hipStream_t st) {
     dim3 grid(a.num_tokens, a.num_kv_heads);
-    hipLaunchKernelGGL((reshape_and_cache_kernel<SRC, KVT, BS>), grid, dim3(64), 0, st,
+    hipLaunchKernelGGL((reshape_and_cache_kernel<SRC, KVT, BS, D>), grid, dim3(64), 0, st,
                        (const uint16_t*)a.key, (const uint16_t*)a.value, (uint8_t*)a.k_cache,
                        (uint8_t*)a.v_cache, a.slot_mapping, a.num_kv_heads,
                        (int64_t)a.num_blocks * BS, a.k_inv, a.v_inv);
     return hipGetLastError();
 }
 
+template <int SRC, int KVT, int D>
+static hipError_t launch_rac_d(const RacArgs& a, hipStream_t st) {
+    return a.block_size == 16 ? launch_rac<SRC, KVT, 16, D>(a, st) : launch_rac<SRC, KVT, 32, D>(a, st);
+}
+
 template <int SRC, int KVT>
 static hipError_t launch_rac_bs(const RacArgs& a, hipStream_t st) {
-    return a.block_size == 16 ? launch_rac<SRC, KVT, 16>(a, st) : launch_rac<SRC, KVT, 32>(a, st);
+    if (a.head_dim == 64) return launch_rac_d<SRC, KVT, 64>(a, st);
+    if (a.head_dim == 256) return launch_rac_d<SRC, KVT, 256>(a, st);
+    return launch_rac_d<SRC, KVT, 128>(a, st);
 }
 
 hipError_t launch_reshape_and_cache(const RacArgs& a, hipStream_t st) {

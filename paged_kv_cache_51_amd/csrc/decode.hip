@@ -32,12 +32,12 @@
 
 namespace pkv {
 
-// Grid form (see grid_entry).
-template <int KVT, int QT, int BS, int NW, int DEPTH>
+// Grid form (see grid_entry).  D = head_dim.
+template <int KVT, int QT, int BS, int NW, int DEPTH, int D = kHeadDim>
 __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(PKV_WAVES_PER_EU)))
 void paged_decode_mfma_kernel(const DecodeArgs a) {
     extern __shared__ float pkv_smem[];
-    grid_entry<MfmaMath<KVT, QT>, KVT, QT, BS, NW, DEPTH>(a, pkv_smem);
+    grid_entry<MfmaMath<KVT, QT, 1, D>, KVT, QT, BS, NW, DEPTH>(a, pkv_smem);
 }
 
 // Persistent form: as many workgroups as fit on the GPU at once, each
@@ -46,7 +46,7 @@ void paged_decode_mfma_kernel(const DecodeArgs a) {
 // simply take more entries.  The counters live in the plan header
 // (zeroed by the planner); the last workgroup to leave resets them, so
 // the plan can serve the next launch on the same stream.
-template <int KVT, int QT, int BS, int NW, int DEPTH>
+template <int KVT, int QT, int BS, int NW, int DEPTH, int D = kHeadDim>
 __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(PKV_WAVES_PER_EU)))
 void paged_decode_mfma_persistent(const DecodeArgs a) {
     extern __shared__ float pkv_smem[];
@@ -65,8 +65,8 @@ void paged_decode_mfma_persistent(const DecodeArgs a) {
         const int kvh = k - item * a.num_kv_heads;
         const uint32_t packed = (uint32_t)a.plan[kPlanHeader + item];
         const int s = (int)(packed >> 16);
-        decode_entry<MfmaMath<KVT, QT>, KVT, QT, BS, NW, DEPTH>(a, pkv_smem, s, (int)(packed & 0xffffu),
-                                                                 kvh, lane, w, QueryTile{s, 1, 1});
+        decode_entry<MfmaMath<KVT, QT, 1, D>, KVT, QT, BS, NW, DEPTH>(a, pkv_smem, s, (int)(packed & 0xffffu),
+                                                                       kvh, lane, w, QueryTile{s, 1, 1});
     }
     if (threadIdx.x == 0) {
         __threadfence();
@@ -80,8 +80,9 @@ void paged_decode_mfma_persistent(const DecodeArgs a) {
 // Merge the partitions of every multi-partition sequence: with per-partition
 // max m_p (log2 units), normaliser l_p and normalised output o_p,
 //   out = sum_p 2^(m_p - M) l_p o_p / sum_p 2^(m_p - M) l_p,  M = max_p m_p.
-// One wave per (query head, sequence); lane owns dims 2*lane, 2*lane+1.
-template <int QT, int BS>
+// One wave per (query head, sequence); lane owns dims e, e + 1 for
+// e = 2 lane + 128 i (D = head_dim).
+template <int QT, int BS, int D = kHeadDim>
 __global__ __launch_bounds__(kWave) void decode_reduce_kernel(const DecodeArgs a) {
     const int hq = blockIdx.x, s = blockIdx.y, lane = threadIdx.x;
     int ctx = a.context_lens[s];
@@ -96,40 +97,54 @@ __global__ __launch_bounds__(kWave) void decode_reduce_kernel(const DecodeArgs a
     for (int p = lane; p < np; p += kWave) M = fmaxf(M, a.ws_ml[(base + p) * 32 + h]);
 #pragma unroll
     for (int d = 1; d < kWave; d <<= 1) M = fmaxf(M, xor_shfl(M, d));
-    float L = 0.f, o0 = 0.f, o1 = 0.f;
+    constexpr int NE = (D + 2 * kWave - 1) / (2 * kWave);   // dim pairs per lane
+    float L = 0.f, o0[NE], o1[NE];
+#pragma unroll
+    for (int i = 0; i < NE; ++i) o0[i] = o1[i] = 0.f;
     for (int p = 0; p < np; ++p) {
         const float mp = a.ws_ml[(base + p) * 32 + h];
         const float lp = a.ws_ml[(base + p) * 32 + 16 + h];
         const float fct = fast_exp2(mp - M) * lp;
-        const float2 op = *reinterpret_cast<const float2*>(a.ws_out + ((base + p) * G + h) * kHeadDim + 2 * lane);
         L += fct;
-        o0 += fct * op.x;
-        o1 += fct * op.y;
+#pragma unroll
+        for (int i = 0; i < NE; ++i) {
+            const int e = 2 * lane + 2 * kWave * i;
+            if (e < D) {
+                const float2 op = *reinterpret_cast<const float2*>(a.ws_out + ((base + p) * G + h) * D + e);
+                o0[i] += fct * op.x;
+                o1[i] += fct * op.y;
+            }
+        }
     }
     const float sc = a.out_scale / L;
-    uint16_t* out = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)s * a.num_heads + hq) * kHeadDim;
-    const uint32_t packed = (uint32_t)f32_to_bits<QT>(o0 * sc) | ((uint32_t)f32_to_bits<QT>(o1 * sc) << 16);
-    *reinterpret_cast<uint32_t*>(out + 2 * lane) = packed;
+    uint16_t* out = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)s * a.num_heads + hq) * D;
+#pragma unroll
+    for (int i = 0; i < NE; ++i) {
+        const int e = 2 * lane + 2 * kWave * i;
+        if (e < D)
+            *reinterpret_cast<uint32_t*>(out + e) =
+                (uint32_t)f32_to_bits<QT>(o0[i] * sc) | ((uint32_t)f32_to_bits<QT>(o1[i] * sc) << 16);
+    }
 }
 
 // ----------------------------------------------------------------- launch --
 
-template <int KVT, int QT, int BS>
+template <int KVT, int QT, int BS, int D>
 static hipError_t launch_mfma(const DecodeArgs& a, bool persistent, hipStream_t st) {
-    const size_t lds = sizeof(float) * merge_lds_floats(kWavesPerGroup, a.group);
+    const size_t lds = sizeof(float) * merge_lds_floats(kWavesPerGroup, a.group, 16, D);
     const dim3 block(kWavesPerGroup * kWave);
     if (!persistent) {
         const dim3 grid((unsigned)grid_workgroups(a));
-        hipLaunchKernelGGL((paged_decode_mfma_kernel<KVT, QT, BS, kWavesPerGroup, kDepth>), grid,
+        hipLaunchKernelGGL((paged_decode_mfma_kernel<KVT, QT, BS, kWavesPerGroup, kDepth, D>), grid,
                            block, lds, st, a);
         return hipGetLastError();
     }
     // as many workgroups as can be resident at once (never more than entries)
-    static int per_cu[17] = {0};              // cache by group size (LDS use)
-    int& occ = per_cu[a.group];
+    static int per_cu[3][17] = {};            // cache by head_dim and group size (LDS use)
+    int& occ = per_cu[D == 64 ? 0 : (D == 128 ? 1 : 2)][a.group];
     if (!occ) {
         hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &occ, reinterpret_cast<const void*>(&paged_decode_mfma_persistent<KVT, QT, BS, kWavesPerGroup, kDepth>),
+            &occ, reinterpret_cast<const void*>(&paged_decode_mfma_persistent<KVT, QT, BS, kWavesPerGroup, kDepth, D>),
             block.x, lds);
         if (e != hipSuccess || occ <= 0) occ = 1;
     }
@@ -139,15 +154,22 @@ static hipError_t launch_mfma(const DecodeArgs& a, bool persistent, hipStream_t 
         cus = 256;
     const int64_t entries = (int64_t)a.num_seqs * a.num_kv_heads * a.num_parts;
     const dim3 grid((unsigned)std::min<int64_t>(entries, (int64_t)occ * cus));
-    hipLaunchKernelGGL((paged_decode_mfma_persistent<KVT, QT, BS, kWavesPerGroup, kDepth>), grid, block,
+    hipLaunchKernelGGL((paged_decode_mfma_persistent<KVT, QT, BS, kWavesPerGroup, kDepth, D>), grid, block,
                        lds, st, a);
     return hipGetLastError();
 }
 
+template <int KVT, int QT, int D>
+static hipError_t launch_mfma_d(const DecodeArgs& a, int bs, bool persistent, hipStream_t st) {
+    return bs == 16 ? launch_mfma<KVT, QT, 16, D>(a, persistent, st)
+                    : launch_mfma<KVT, QT, 32, D>(a, persistent, st);
+}
+
 template <int KVT, int QT>
 static hipError_t launch_mfma_bs(const DecodeArgs& a, int bs, bool persistent, hipStream_t st) {
-    return bs == 16 ? launch_mfma<KVT, QT, 16>(a, persistent, st)
-                    : launch_mfma<KVT, QT, 32>(a, persistent, st);
+    if (a.head_dim == 64) return launch_mfma_d<KVT, QT, 64>(a, bs, persistent, st);
+    if (a.head_dim == 256) return launch_mfma_d<KVT, QT, 256>(a, bs, persistent, st);
+    return launch_mfma_d<KVT, QT, 128>(a, bs, persistent, st);
 }
 
 hipError_t launch_decode_vector(const DecodeArgs& a, int q_dtype, int kv_dtype, int block_size,
@@ -166,21 +188,27 @@ hipError_t launch_decode_partitions(const DecodeArgs& a, int q_dtype, int kv_dty
     return launch_mfma_bs<DT_FP8, DT_FP16>(a, block_size, persistent, st);
 }
 
+template <int QT, int D>
+static void launch_reduce_t(const DecodeArgs& a, int block_size, dim3 grid, hipStream_t st) {
+    if (block_size == 16)
+        hipLaunchKernelGGL((decode_reduce_kernel<QT, 16, D>), grid, dim3(kWave), 0, st, a);
+    else
+        hipLaunchKernelGGL((decode_reduce_kernel<QT, 32, D>), grid, dim3(kWave), 0, st, a);
+}
+
+template <int QT>
+static void launch_reduce_q(const DecodeArgs& a, int block_size, dim3 grid, hipStream_t st) {
+    if (a.head_dim == 64) launch_reduce_t<QT, 64>(a, block_size, grid, st);
+    else if (a.head_dim == 256) launch_reduce_t<QT, 256>(a, block_size, grid, st);
+    else launch_reduce_t<QT, 128>(a, block_size, grid, st);
+}
+
 hipError_t launch_decode_reduce(const DecodeArgs& a, int q_dtype, int block_size,
                                 hipStream_t st) {
     if (a.num_seqs == 0 || a.num_parts <= 1) return hipSuccess;
     dim3 grid(a.num_heads, a.num_seqs);
-    if (q_dtype == DT_BF16) {
-        if (block_size == 16)
-            hipLaunchKernelGGL((decode_reduce_kernel<DT_BF16, 16>), grid, dim3(kWave), 0, st, a);
-        else
-            hipLaunchKernelGGL((decode_reduce_kernel<DT_BF16, 32>), grid, dim3(kWave), 0, st, a);
-    } else {
-        if (block_size == 16)
-            hipLaunchKernelGGL((decode_reduce_kernel<DT_FP16, 16>), grid, dim3(kWave), 0, st, a);
-        else
-            hipLaunchKernelGGL((decode_reduce_kernel<DT_FP16, 32>), grid, dim3(kWave), 0, st, a);
-    }
+    if (q_dtype == DT_BF16) launch_reduce_q<DT_BF16>(a, block_size, grid, st);
+    else launch_reduce_q<DT_FP16>(a, block_size, grid, st);
     return hipGetLastError();
 }
 

@@ -8,15 +8,17 @@
 
 namespace pkv {
 
-template <int KVT>
+// One 16-token unit of one kv head in registers: R pool rows of K and of V
+// (D = head_dim).
+template <int KVT, int D = kHeadDim>
 struct UnitRegs {
-    static constexpr int R = rows_per_sub(KVT);
+    static constexpr int R = rows_per_sub(KVT, D);
     u32x4_t k[R];
     u32x4_t v[R];
 };
 
-template <int KVT>
-__device__ __forceinline__ void load_unit(UnitRegs<KVT>& u, const uint8_t* kbase,
+template <int KVT, int D>
+__device__ __forceinline__ void load_unit(UnitRegs<KVT, D>& u, const uint8_t* kbase,
                                           const uint8_t* vbase, int lane) {
     const u32x4_t* kp = reinterpret_cast<const u32x4_t*>(kbase) + lane;
     const u32x4_t* vp = reinterpret_cast<const u32x4_t*>(vbase) + lane;
@@ -25,14 +27,14 @@ __device__ __forceinline__ void load_unit(UnitRegs<KVT>& u, const uint8_t* kbase
     // 7B shape: 424 -> 380 us per layer (the cache-allocating stream tops
     // out near 6.3 TB/s).
 #pragma unroll
-    for (int r = 0; r < UnitRegs<KVT>::R; ++r) u.k[r] = __builtin_nontemporal_load(kp + kWave * r);
+    for (int r = 0; r < UnitRegs<KVT, D>::R; ++r) u.k[r] = __builtin_nontemporal_load(kp + kWave * r);
 #pragma unroll
-    for (int r = 0; r < UnitRegs<KVT>::R; ++r) u.v[r] = __builtin_nontemporal_load(vp + kWave * r);
+    for (int r = 0; r < UnitRegs<KVT, D>::R; ++r) u.v[r] = __builtin_nontemporal_load(vp + kWave * r);
 }
 
 // K fragment kk (dims 8*((lane>>4) + 4kk) .. +7 of token lane&15).
-template <int KVT, int QT>
-__device__ __forceinline__ u32x4_t k_frag(const UnitRegs<KVT>& u, int kk) {
+template <int KVT, int QT, int D>
+__device__ __forceinline__ u32x4_t k_frag(const UnitRegs<KVT, D>& u, int kk) {
     if constexpr (KVT == DT_FP8) {
         const u32x4_t row = u.k[kk >> 1];
         return (kk & 1) ? e4m3x8_to_16<QT>(row[2], row[3]) : e4m3x8_to_16<QT>(row[0], row[1]);
@@ -42,8 +44,8 @@ __device__ __forceinline__ u32x4_t k_frag(const UnitRegs<KVT>& u, int kk) {
 }
 
 // V fragment nt (tokens 4*(lane>>4) .. +3 of dim 16*nt + (lane&15)).
-template <int KVT, int QT>
-__device__ __forceinline__ u32x2_t v_frag(const UnitRegs<KVT>& u, int nt) {
+template <int KVT, int QT, int D>
+__device__ __forceinline__ u32x2_t v_frag(const UnitRegs<KVT, D>& u, int nt) {
     if constexpr (KVT == DT_FP8) {
         return e4m3x4_to_16<QT>(u.v[nt >> 2][nt & 3]);
     } else {
@@ -61,9 +63,10 @@ __device__ __forceinline__ u32x2_t v_frag(const UnitRegs<KVT>& u, int nt) {
 // 32 accumulators are rescaled only on such rare jumps.
 constexpr float kRescaleSlack = 8.0f;
 
-// Row stride (floats) of a head's partial output in the merge area: 128
-// dims plus 4 floats of padding to spread heads over LDS banks.
-constexpr int kMergeRow = kHeadDim + 4;
+// Row stride (floats) of a head's partial output in the merge area: d dims
+// plus 4 floats of padding to spread heads over LDS banks.
+__host__ __device__ constexpr int merge_row(int d = kHeadDim) { return d + 4; }
+constexpr int kMergeRow = merge_row();
 
 // Plan header ints before the item list: [count][next entry][done][reserved].
 constexpr int kPlanHeader = 4;
@@ -71,8 +74,8 @@ constexpr int kPlanHeader = 4;
 // Merge area of NW waves: [counters 4][m: NW x kcols][l: NW x kcols]
 // [partial outputs: NW x ncols rows of kMergeRow floats]; kcols = the
 // policy's column capacity (16 per tile).
-__host__ __device__ constexpr int merge_lds_floats(int nw, int ncols, int kcols = 16) {
-    return 4 + 2 * nw * kcols + nw * ncols * kMergeRow;
+__host__ __device__ constexpr int merge_lds_floats(int nw, int ncols, int kcols = 16, int d = kHeadDim) {
+    return 4 + 2 * nw * kcols + nw * ncols * merge_row(d);
 }
 
 // The query side of a work entry: ntok consecutive query tokens of one
@@ -126,6 +129,8 @@ __device__ __forceinline__ void park_and_store(const DecodeArgs& a, float* pkv_s
                                                const QueryTile& qt, int ncols, bool single) {
     const int G = a.group;
     constexpr int KC = Math::kCols;
+    constexpr int D = Math::kD;
+    constexpr int MR = merge_row(D);
     int* done = reinterpret_cast<int*>(pkv_smem);   // zeroed before the workgroup barrier
     float* sm_m = pkv_smem + 4;
     float* sm_l = sm_m + NW * KC;
@@ -142,32 +147,39 @@ __device__ __forceinline__ void park_and_store(const DecodeArgs& a, float* pkv_s
         float M = -INFINITY;
 #pragma unroll
         for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, sm_m[ww * KC + c]);
-        float L = 0.f, o0 = 0.f, o1 = 0.f;
+        float f[NW];
+        float L = 0.f;
 #pragma unroll
         for (int ww = 0; ww < NW; ++ww) {
             const float mw = sm_m[ww * KC + c];
-            const float f = (mw == -INFINITY) ? 0.f : fast_exp2(mw - M);
-            const float2 ov = *reinterpret_cast<const float2*>(sm_acc + (ww * ncols + c) * kMergeRow + 2 * lane);
-            L += f * sm_l[ww * KC + c];
-            o0 += f * ov.x;
-            o1 += f * ov.y;
+            f[ww] = (mw == -INFINITY) ? 0.f : fast_exp2(mw - M);
+            L += f[ww] * sm_l[ww * KC + c];
         }
         // L = 0 only for a token placed before the start of the context
         const float invL = L > 0.f ? 1.0f / L : 0.f;
         const int h = c % G;
         const int hq = kvh * G + h;
-        if (single) {
-            const float sc = invL * a.out_scale;
-            uint16_t* out = reinterpret_cast<uint16_t*>(a.out) +
-                            ((qt.row0 + c / G) * a.num_heads + hq) * kHeadDim;
-            *reinterpret_cast<uint32_t*>(out + 2 * lane) =
-                (uint32_t)f32_to_bits<QT>(o0 * sc) | ((uint32_t)f32_to_bits<QT>(o1 * sc) << 16);
-        } else {
-            // (split contexts are decode only: one token, column c = head h)
-            // record (s, kvh, part): G rows of head_dim floats, contiguous
-            const int64_t rec = ((int64_t)s * a.num_kv_heads + kvh) * a.num_parts + part;
-            *reinterpret_cast<float2*>(a.ws_out + (rec * G + h) * kHeadDim + 2 * lane) =
-                make_float2(o0 * invL, o1 * invL);
+        // lane owns dims e, e + 1 for e = 2 lane + 128 i
+#pragma unroll
+        for (int e = 2 * lane; e < D; e += 2 * kWave) {
+            float o0 = 0.f, o1 = 0.f;
+#pragma unroll
+            for (int ww = 0; ww < NW; ++ww) {
+                const float2 ov = *reinterpret_cast<const float2*>(sm_acc + (ww * ncols + c) * MR + e);
+                o0 += f[ww] * ov.x;
+                o1 += f[ww] * ov.y;
+            }
+            if (single) {
+                const float sc = invL * a.out_scale;
+                uint16_t* out = reinterpret_cast<uint16_t*>(a.out) + ((qt.row0 + c / G) * a.num_heads + hq) * D;
+                *reinterpret_cast<uint32_t*>(out + e) =
+                    (uint32_t)f32_to_bits<QT>(o0 * sc) | ((uint32_t)f32_to_bits<QT>(o1 * sc) << 16);
+            } else {
+                // (split contexts are decode only: one token, column c = head h)
+                // record (s, kvh, part): G rows of head_dim floats, contiguous
+                const int64_t rec = ((int64_t)s * a.num_kv_heads + kvh) * a.num_parts + part;
+                *reinterpret_cast<float2*>(a.ws_out + (rec * G + h) * D + e) = make_float2(o0 * invL, o1 * invL);
+            }
         }
     }
     if (!single && lane < 32) {
@@ -199,7 +211,8 @@ template <class Math, int KVT, int QT, int BS, int NW, int DEPTH>
 __device__ __forceinline__ void decode_entry(const DecodeArgs& a, float* pkv_smem, int s, int part,
                                              int kvh, int lane, int w, const QueryTile& qt) {
     constexpr int NSUB = BS / kSubTokens;
-    constexpr int64_t SUB = sub_tile_bytes(KVT);
+    constexpr int D = Math::kD;
+    constexpr int64_t SUB = sub_tile_bytes(KVT, D);
     constexpr int64_t TILE = SUB * NSUB;
     const int G = a.group;
     const int units_per_part = a.part_blocks * NSUB;
@@ -226,11 +239,11 @@ __device__ __forceinline__ void decode_entry(const DecodeArgs& a, float* pkv_sme
         if (part == 0) {
             // no key at all: zero output (empty context, or tokens placed
             // before the start of the context)
-            for (int e = (NW == 1 ? lane : (int)threadIdx.x); e < ncols * kHeadDim; e += NW * kWave) {
-                const int c = e / kHeadDim;
+            for (int e = (NW == 1 ? lane : (int)threadIdx.x); e < ncols * D; e += NW * kWave) {
+                const int c = e / D;
                 uint16_t* out = reinterpret_cast<uint16_t*>(a.out) +
-                                ((qt.row0 + c / G) * a.num_heads + (int64_t)kvh * G + c % G) * kHeadDim;
-                out[e % kHeadDim] = 0;
+                                ((qt.row0 + c / G) * a.num_heads + (int64_t)kvh * G + c % G) * D;
+                out[e % D] = 0;
             }
         }
         return;
@@ -244,7 +257,7 @@ __device__ __forceinline__ void decode_entry(const DecodeArgs& a, float* pkv_sme
     int* done = reinterpret_cast<int*>(pkv_smem);
     const int ltid = NW == 1 ? lane : (int)threadIdx.x;
     if (ltid == 0) *done = 0;
-    mt.stage_q(pkv_smem + merge_lds_floats(NW, ncols, Math::kCols), ltid);
+    mt.stage_q(pkv_smem + merge_lds_floats(NW, ncols, Math::kCols, D), ltid);
     if constexpr (NW > 1) __syncthreads();
     mt.begin();
 
@@ -272,7 +285,7 @@ __device__ __forceinline__ void decode_entry(const DecodeArgs& a, float* pkv_sme
         for (int c0 = 0; c0 < n_my; c0 += kWave) {
             const int nc = min(kWave, n_my - c0);
             const int ids = c0 == 0 ? ids0 : load_ids(c0);
-            UnitRegs<KVT> buf[DEPTH];
+            UnitRegs<KVT, D> buf[DEPTH];
             // Unconditional prologue: a conditional load here would make the
             // compiler's load-counter analysis assume the ring may be half
             // empty and wait for every outstanding load inside the loop.  With

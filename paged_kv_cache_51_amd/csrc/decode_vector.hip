@@ -20,6 +20,7 @@ template <int KVT, int QT>
 struct VectorMath {
     static constexpr int kMaxGroup = 8;
     static constexpr int kCols = 16;
+    static constexpr int kD = kHeadDim;       // built for head_dim 128
     __host__ __device__ static constexpr int query_lds_floats(int g) { return g * kHeadDim / 2; }
 
     float acc[kMaxGroup][8];  // dim 16nt + (lane & 15), over this row's tokens

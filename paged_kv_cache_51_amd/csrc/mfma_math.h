@@ -14,14 +14,17 @@ namespace pkv {
 // 4*(l>>4)..+3 of each 16-row tile.  NT tiles (1 for the partition
 // kernels, 2 for the multi-token wave kernel) share the unit's K and V
 // fragments and the loop around them.
-template <int KVT, int QT, int NT = 1>
+template <int KVT, int QT, int NT = 1, int D = kHeadDim>
 struct MfmaMath {
     static constexpr int kMaxGroup = 16;
     static constexpr int kCols = 16 * NT;     // columns of one entry at most
+    static constexpr int kD = D;              // head_dim
+    static constexpr int KD = D / 32;         // k steps of the logits (32 dims each)
+    static constexpr int NV = D / 16;         // 16-dim tiles of the output
     __host__ __device__ static constexpr int query_lds_floats(int) { return 0; }
 
-    u32x4_t qf[NT][4];        // Q^T fragments: 8 dims per kk of this lane's columns
-    f32x4_t acc[NT][8];
+    u32x4_t qf[NT][KD];       // Q^T fragments: 8 dims per kk of this lane's columns
+    f32x4_t acc[NT][NV];
     float m[NT], l[NT];
     int col;                  // lane & 15; tile t's column is 16t + col
     bool cvalid[NT];          // the column holds a real (token, head)
@@ -38,9 +41,9 @@ struct MfmaMath {
             const int j = cvalid[t] ? c / G : 0;
             const int h = cvalid[t] ? c - j * G : 0;
             const uint8_t* qrow = reinterpret_cast<const uint8_t*>(a.q) +
-                                  ((qt.row0 + j) * a.num_heads + (int64_t)kvh * G + h) * (kHeadDim * 2);
+                                  ((qt.row0 + j) * a.num_heads + (int64_t)kvh * G + h) * (D * 2);
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
+            for (int kk = 0; kk < KD; ++kk) {
                 const u32x4_t z = {0u, 0u, 0u, 0u};
                 qf[t][kk] = cvalid[t] ? *reinterpret_cast<const u32x4_t*>(qrow + 16 * ((lane >> 4) + 4 * kk))
                                       : z;
@@ -58,7 +61,7 @@ struct MfmaMath {
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
 #pragma unroll
-            for (int nt = 0; nt < 8; ++nt) acc[t][nt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+            for (int nt = 0; nt < NV; ++nt) acc[t][nt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
             m[t] = -INFINITY;
             l[t] = 0.f;
         }
@@ -66,12 +69,12 @@ struct MfmaMath {
 
     // tok0 = logical position of the unit's first token; ctx = context
     // length; cs = scale * k_scale * log2(e).
-    __device__ __forceinline__ void unit(const UnitRegs<KVT>& u, int tok0, int ctx, float cs, int lane) {
+    __device__ __forceinline__ void unit(const UnitRegs<KVT, D>& u, int tok0, int ctx, float cs, int lane) {
         f32x4_t st[NT];
 #pragma unroll
         for (int t = 0; t < NT; ++t) st[t] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
+        for (int kk = 0; kk < KD; ++kk) {
             const u32x4_t kf = k_frag<KVT, QT>(u, kk);
 #pragma unroll
             for (int t = 0; t < NT; ++t) st[t] = mfma_16x16x32<QT>(kf, qf[t][kk], st[t]);
@@ -103,7 +106,7 @@ struct MfmaMath {
                 const float alpha = (m[t] == -INFINITY) ? 0.f : fast_exp2(m[t] - mn);
                 l[t] *= alpha;
 #pragma unroll
-                for (int nt = 0; nt < 8; ++nt) acc[t][nt] *= alpha;
+                for (int nt = 0; nt < NV; ++nt) acc[t][nt] *= alpha;
                 m[t] = mn;
             }
         }
@@ -124,7 +127,7 @@ struct MfmaMath {
         }
         if (tok0 + kSubTokens <= ctx) {
 #pragma unroll
-            for (int nt = 0; nt < 8; ++nt) {
+            for (int nt = 0; nt < NV; ++nt) {
                 const u32x2_t vf = v_frag<KVT, QT>(u, nt);
 #pragma unroll
                 for (int t = 0; t < NT; ++t) acc[t][nt] = mfma_16x16x16<QT>(vf, pf[t], acc[t][nt]);
@@ -140,7 +143,7 @@ struct MfmaMath {
             vm[0] = (row[0] ? 0x0000ffffu : 0u) | (row[1] ? 0xffff0000u : 0u);
             vm[1] = (row[2] ? 0x0000ffffu : 0u) | (row[3] ? 0xffff0000u : 0u);
 #pragma unroll
-            for (int nt = 0; nt < 8; ++nt) {
+            for (int nt = 0; nt < NV; ++nt) {
                 const u32x2_t vf = v_frag<KVT, QT>(u, nt) & vm;
 #pragma unroll
                 for (int t = 0; t < NT; ++t) acc[t][nt] = mfma_16x16x16<QT>(vf, pf[t], acc[t][nt]);
@@ -161,9 +164,9 @@ struct MfmaMath {
                 sm_l[w * kCols + 16 * t + lane] = lt;
             }
             if (cvalid[t]) {
-                float* row = sm_acc + (w * ncols + 16 * t + col) * kMergeRow + 4 * (lane >> 4);
+                float* row = sm_acc + (w * ncols + 16 * t + col) * merge_row(D) + 4 * (lane >> 4);
 #pragma unroll
-                for (int nt = 0; nt < 8; ++nt) *reinterpret_cast<f32x4_t*>(row + 16 * nt) = acc[t][nt];
+                for (int nt = 0; nt < NV; ++nt) *reinterpret_cast<f32x4_t*>(row + 16 * nt) = acc[t][nt];
             }
         }
     }

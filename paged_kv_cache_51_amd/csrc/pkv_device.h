@@ -2,7 +2,8 @@
 //
 // Pool layout (tile order, 1 KiB rows of 64 lanes x 16 bytes, K lanes holding
 // 8 dims of one token, V lanes holding 4 tokens of one dim) is defined in
-// include/pagedkv.h; the constants here restate it for head_dim 128.
+// include/pagedkv.h; the constants here restate it (head_dim 128 unless a
+// template says otherwise).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -28,11 +29,13 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 __host__ __device__ constexpr int elem_bytes(int dt) { return dt == DT_FP8 ? 1 : 2; }
 
-// Bytes of one 16-token sub-tile of one pool (K or V) at head_dim 128.
-__host__ __device__ constexpr int sub_tile_bytes(int dt) { return kSubTokens * kHeadDim * elem_bytes(dt); }
+// Bytes of one 16-token sub-tile of one pool (K or V) at head_dim d (a
+// multiple of 64; the kernels are built for 64, 128 and 256).
+__host__ __device__ constexpr int sub_tile_bytes(int dt, int d = kHeadDim) { return kSubTokens * d * elem_bytes(dt); }
 
-// 1 KiB rows per sub-tile: 4 for 16-bit elements, 2 for fp8.
-__host__ __device__ constexpr int rows_per_sub(int dt) { return sub_tile_bytes(dt) / 1024; }
+// 1 KiB rows per sub-tile: d / 32 for 16-bit elements (4 at d = 128), d / 64
+// for fp8.
+__host__ __device__ constexpr int rows_per_sub(int dt, int d = kHeadDim) { return sub_tile_bytes(dt, d) / 1024; }
 
 // ---------------------------------------------------------------- scalars --
 

@@ -16,6 +16,7 @@ struct RacArgs {
     const int32_t* slot_mapping;
     int32_t num_tokens;
     int32_t num_kv_heads;
+    int32_t head_dim;
     int32_t block_size;
     int32_t num_blocks;
     int32_t src_dtype;
@@ -43,6 +44,7 @@ struct DecodeArgs {
     int32_t part_blocks;   // blocks per partition
     int32_t num_parts;     // partitions launched per (seq, kv head)
     int32_t num_blocks;    // pool size for id clamping (0 = unchecked)
+    int32_t head_dim;      // 64, 128 or 256 (decode); 128 elsewhere
     float qk_scale_log2;   // scale * k_scale * log2(e)
     float out_scale;       // v_scale for fp8 pools, else 1
 };

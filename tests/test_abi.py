@@ -98,7 +98,8 @@ def _decode(**kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(H=9), -1),                 # heads not a multiple of kv heads
     (dict(H=34, Hkv=2), -4),         # G = 17 > 16
-    (dict(D=64), -4),                # only head_dim 128 is built
+    (dict(D=192), -4),               # decode is built for head_dim 64, 128, 256
+    (dict(D=64, impl=2), -4),        # vector kernel: head_dim 128 only
     (dict(D=100), -1),               # not a multiple of 64
     (dict(bs=8), -1),
     (dict(kvdt=1), -4),              # fp16 pool with bf16 q
@@ -163,3 +164,19 @@ def test_prefill_rejects_negative_num_blocks():
     rc = lib.paged_attention_prefill(None, None, pkv.BF16, None, None, None, 0, None, None, 0, 0, 0,
                                      8, 2, 128, 0.1, 16, -1, pkv.BF16, 1.0, 1.0, None)
     assert rc == -1 and "sizes" in pkv.last_error()
+
+
+def test_head_dims_outside_the_built_set_are_unsupported():
+    """Cache write and decode are built for head_dim 64, 128 and 256; the
+    multi-token and token-table paths for 128 only (no launch happens)."""
+    lib = pkv.lib()
+    assert lib.reshape_and_cache(None, None, pkv.BF16, None, None, None, 0, 2, 96, 16, 8, pkv.BF16,
+                                 1.0, 1.0, None) == -1          # not a multiple of 64: bad layout
+    assert lib.reshape_and_cache(None, None, pkv.BF16, None, None, None, 0, 2, 192, 16, 8, pkv.BF16,
+                                 1.0, 1.0, None) == -4
+    for d in (64, 256):
+        assert lib.reshape_and_cache(None, None, pkv.BF16, None, None, None, 0, 2, d, 16, 8, pkv.BF16,
+                                     1.0, 1.0, None) == 0       # no tokens: nothing to launch
+        rc = lib.paged_attention_prefill(None, None, pkv.BF16, None, None, None, 0, None, None, 0, 0, 0,
+                                         8, 2, d, 0.1, 16, 0, pkv.BF16, 1.0, 1.0, None)
+        assert rc == -4 and "128" in pkv.last_error()
