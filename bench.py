@@ -708,6 +708,9 @@ def gpu_clocks():
     """Current GPU clocks as rocm-smi reports them (a child process, after
     the timed region), or the reason they are missing."""
     import subprocess
+    if "rocprof" in os.environ.get("LD_PRELOAD", ""):
+        # under the profiler a child process may not start another program
+        return {"error": "not read under rocprofv3"}
     try:
         r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True,
                            timeout=30)
