@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--block-size", type=int, default=None, choices=[None, 16, 32])
     ap.add_argument("--layers", type=int, default=None)
     ap.add_argument("--partition-tokens", type=int, default=0)
+    ap.add_argument("--head-dim", type=int, default=0, choices=[0, 64, 128, 256],
+                    help="decode: override the configuration's head_dim (0 = as configured)")
     ap.add_argument("--impl", default="auto", choices=["auto", "mfma", "vector", "persistent"])
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0,
@@ -126,6 +128,10 @@ def main():
 
     dt_names = {"bf16": pkv.BF16, "fp16": pkv.FP16, "fp8": pkv.FP8_E4M3}
     cfg, tabs, _, _ = workloads.make(args.config, seed=args.seed, block_size=args.block_size)
+    if args.head_dim and args.head_dim != cfg.head_dim:
+        import dataclasses
+        cfg = dataclasses.replace(cfg, head_dim=args.head_dim, description=cfg.description.replace(
+            f"d={cfg.head_dim}", f"d={args.head_dim}"))
     kv_dtype = dt_names[args.kv_dtype] if args.kv_dtype else cfg.kv_dtype
     q_dtype = cfg.q_dtype
     if kv_dtype in (pkv.BF16, pkv.FP16) and kv_dtype != q_dtype:
@@ -249,7 +255,8 @@ def main():
     gbs = step_bytes / (step_ms * 1e-3) / 1e9
     launch_bytes = kv_bytes + qo_bytes
     achieved = launch_bytes / (dec_avg_ms * 1e-3) / 1e9
-    traffic_key = f"{args.config}-{kv_dtype}-bs{bs}-part{part_resolved}-impl{impl}"
+    traffic_key = (f"{args.config}-{kv_dtype}-bs{bs}-part{part_resolved}-impl{impl}"
+                   + (f"-d{D}" if D != 128 else ""))
     traffic = measured_traffic(traffic_key)
     unique_gbs = (unique_kv_bytes + qo_bytes) / (dec_avg_ms * 1e-3) / 1e9
     print(f"[bench] step {step_ms:.3f} ms, {gbs:.0f} GB/s; partition kernel "
@@ -280,15 +287,7 @@ def main():
     if args.copy_probe_mib:
         copy_probe(torch, dev, args.copy_probe_mib)
 
-    # GPU clocks while this workload runs: about 0.6 s of steps are queued
-    # (after the timed region, outside every timing) and rocm-smi is read
-    # while they execute; then once more when the GPU is idle again
-    n_load = int(min(20000, max(1, 600.0 / max(step_ms, 1e-3))))
-    for _ in range(n_load):
-        step()
-    clocks = {"under_load": gpu_clocks(), "load_steps": n_load}
-    torch.cuda.synchronize()
-    clocks["idle_after"] = gpu_clocks()
+    clocks = clocks_under_load(torch, step, step_ms)
 
     cpu = None
     if args.cpu_baseline_seconds > 0:
@@ -450,6 +449,7 @@ def bench_prefill(args, torch, pkv, workloads):
           f"intensity {flops / nbytes:.0f} flop/B", file=sys.stderr, flush=True)
     if args.copy_probe_mib:
         copy_probe(torch, dev, args.copy_probe_mib)
+    clocks = clocks_under_load(torch, step, step_ms)
     kv_name = {pkv.BF16: "bf16", pkv.FP16: "fp16", pkv.FP8_E4M3: "fp8"}[kv]
     traffic = measured_traffic(f"prefill-{args.config}-{kv_name}-bs{bs}-q{qlen}-s{S}",
                                "prefill_traffic.json", PREFILL_SOURCES)
@@ -483,6 +483,7 @@ def bench_prefill(args, torch, pkv, workloads):
                      "frac": round((tflops / peak_tf) if mfma_bound else (gbs / PEAK_HBM_GBS), 4),
                      "traffic": traffic, "avg_launch_us": round(launch_ms * 1e3, 2),
                      "algorithmic_flops_per_launch": flops, "algorithmic_bytes_per_launch": nbytes},
+        "clocks": clocks,
         "cpu_baseline": cpu,
     }), flush=True)
 
@@ -704,23 +705,38 @@ def bench_copy_blocks(args, torch, pkv, workloads):
     }), flush=True)
 
 
+def clocks_under_load(torch, step, step_ms, seconds=1.5):
+    """GPU clocks and power while this workload runs: about `seconds` of
+    steps are queued (after the timed region, outside every timing) and
+    rocm-smi is read while they execute; then once more when the GPU is idle
+    again."""
+    n_load = int(min(20000, max(1, seconds * 1e3 / max(step_ms, 1e-3))))
+    for _ in range(n_load):
+        step()
+    clocks = {"under_load": gpu_clocks(), "load_steps": n_load}
+    torch.cuda.synchronize()
+    clocks["idle_after"] = gpu_clocks()
+    return clocks
+
+
 def gpu_clocks():
-    """Current GPU clocks as rocm-smi reports them (a child process, after
-    the timed region), or the reason they are missing."""
+    """Current GPU clocks and power as rocm-smi reports them (a child
+    process, after the timed region), or the reason they are missing."""
     import subprocess
     if "rocprof" in os.environ.get("LD_PRELOAD", ""):
         # under the profiler a child process may not start another program
         return {"error": "not read under rocprofv3"}
     try:
-        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True,
-                           timeout=30)
+        r = subprocess.run(["rocm-smi", "--showclocks", "--showpower", "--json"],
+                           capture_output=True, text=True, timeout=30)
         data = json.loads(r.stdout[r.stdout.index("{"):])
     except Exception as e:            # tool missing, no JSON, timeout
         return {"error": f"rocm-smi: {type(e).__name__}: {e}"[:200]}
     out = {}
     for card, vals in data.items():
         if isinstance(vals, dict):
-            out[card] = {k.strip(" :"): v for k, v in vals.items() if "clk" in k.lower() or "clock" in k.lower()}
+            out[card] = {k.strip(" :"): v for k, v in vals.items()
+                         if any(w in k.lower() for w in ("clk", "clock", "power"))}
     return out or {"raw": r.stdout[:400]}
 
 
