@@ -41,6 +41,12 @@ def parse():
     ap.add_argument("--block-size", type=int, default=None, choices=[None, 16, 32])
     ap.add_argument("--layers", type=int, default=None)
     ap.add_argument("--partition-tokens", type=int, default=0)
+    ap.add_argument("--event-every", type=int, default=4,
+                    help="decode: HIP events around each launch in every N-th timed step")
+    ap.add_argument("--separate-cache-write", action="store_true",
+                    help="decode: write the new tokens with reshape_and_cache in a launch of "
+                         "their own before each decode launch (default: the decode launch "
+                         "writes them, paged_attention_decode_append)")
     ap.add_argument("--head-dim", type=int, default=0, choices=[0, 64, 128, 256],
                     help="decode: override the configuration's head_dim (0 = as configured)")
     ap.add_argument("--impl", default="auto", choices=["auto", "mfma", "vector", "persistent"])
@@ -61,11 +67,14 @@ def parse():
                     help="prefill: sequences (default 16, or the workload's batch if --q-len <= 16)")
     ap.add_argument("--copy-pairs", type=int, default=2048,
                     help="copy_blocks: (src, dst) block pairs per call")
-    return ap.parse_args()
+    args = ap.parse_args()
+    if args.event_every < 1:
+        raise SystemExit("--event-every must be >= 1")
+    return args
 
 
-DECODE_SOURCES = ("decode_core.h", "mfma_math.h", "decode.hip", "pkv_device.h")
-PREFILL_SOURCES = ("prefill.hip", "decode_core.h", "mfma_math.h", "pkv_device.h")
+DECODE_SOURCES = ("decode_core.h", "mfma_math.h", "decode.hip", "pkv_device.h", "cache_write.h")
+PREFILL_SOURCES = ("prefill.hip", "decode_core.h", "mfma_math.h", "pkv_device.h", "cache_write.h")
 
 
 def kernel_source_hash(files=DECODE_SOURCES):
@@ -205,24 +214,38 @@ def main():
 
     rot = [0]                  # next pool copy in the rotation
 
+    separate = args.separate_cache_write
+
     def step(ev=None):
-        # per-step work shared by all layers: new-token slots and the work plan
-        pkv.decode_slot_mapping(bt, cl, bs, slot_mapping=slots, stream=stream)
+        # per-step work shared by all layers: the work plan (and, for separate
+        # cache writes, the new tokens' slots)
+        if separate:
+            pkv.decode_slot_mapping(bt, cl, bs, slot_mapping=slots, stream=stream)
         pkv.build_plan(cl, max_ctx, bt.shape[1], Hkv, bs, part_resolved, plan=plan, stream=stream)
         base = rot[0]
         rot[0] = (base + L) % NP
         for li in range(L):
             layer = (base + li) % NP
             evl = None if ev is None else ev[li]
-            pkv.reshape_and_cache(newk[layer], newv[layer], kpools[layer], vpools[layer], slots,
-                                  bs, nb, kv_dtype, ks, vs, stream=stream)
+            if separate:
+                pkv.reshape_and_cache(newk[layer], newv[layer], kpools[layer], vpools[layer],
+                                      slots, bs, nb, kv_dtype, ks, vs, stream=stream)
             if evl is not None:
                 evl[0].record(stream)
-            pkv.paged_attention_decode(outs[layer], qs[layer], kpools[layer], vpools[layer], bt,
-                                       cl, max_ctx, Hkv, bs, kv_dtype, scale, ks, vs,
-                                       workspace=ws, partition_tokens=part_resolved, impl=impl,
-                                       stages=pkv.STAGE_PARTITIONS, num_blocks=nb, plan=plan,
-                                       stream=stream)
+            if separate:
+                pkv.paged_attention_decode(outs[layer], qs[layer], kpools[layer], vpools[layer],
+                                           bt, cl, max_ctx, Hkv, bs, kv_dtype, scale, ks, vs,
+                                           workspace=ws, partition_tokens=part_resolved,
+                                           impl=impl, stages=pkv.STAGE_PARTITIONS, num_blocks=nb,
+                                           plan=plan, stream=stream)
+            else:
+                # the partition kernel writes each sequence's new K / V itself
+                pkv.paged_attention_decode_append(outs[layer], qs[layer], newk[layer], newv[layer],
+                                                  kpools[layer], vpools[layer], bt, cl, max_ctx,
+                                                  Hkv, bs, kv_dtype, scale, ks, vs, workspace=ws,
+                                                  partition_tokens=part_resolved, impl=impl,
+                                                  num_blocks=nb, plan=plan, stream=stream,
+                                                  stages=pkv.STAGE_PARTITIONS)
             if evl is not None:
                 evl[1].record(stream)
             pkv.paged_attention_decode(outs[layer], qs[layer], kpools[layer], vpools[layer], bt,
@@ -238,14 +261,18 @@ def main():
            for _ in range(args.steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    # Per-launch events are recorded in every --event-every-th timed step
+    # only: each event pair adds a few microseconds between launches, which
+    # would otherwise count against the step throughput.
+    timed_steps = [k for k in range(args.steps) if k % args.event_every == 0]
     start.record(stream)
     for k in range(args.steps):
-        step(evs[k])
+        step(evs[k] if k % args.event_every == 0 else None)
     end.record(stream)
     torch.cuda.synchronize()
     step_ms = start.elapsed_time(end) / args.steps
     dec_ms = [evs[k][layer][0].elapsed_time(evs[k][layer][1])
-              for k in range(args.steps) for layer in range(L)]
+              for k in timed_steps for layer in range(L)]
     dec_avg_ms = float(np.mean(dec_ms))
 
     unique_kv_bytes = unique_kv_tokens(tabs.block_tables, ctx, bs, nb) * 2 * Hkv * D * b_kv
@@ -253,10 +280,12 @@ def main():
     new_bytes = S * Hkv * D * 2 * (2 + b_kv)
     step_bytes = L * (kv_bytes + qo_bytes + new_bytes)
     gbs = step_bytes / (step_ms * 1e-3) / 1e9
-    launch_bytes = kv_bytes + qo_bytes
+    # the partition kernel's own bytes: K / V, q and out, plus the new
+    # tokens' K / V (read, and written to the pool) when it appends them
+    launch_bytes = kv_bytes + qo_bytes + (0 if separate else new_bytes)
     achieved = launch_bytes / (dec_avg_ms * 1e-3) / 1e9
     traffic_key = (f"{args.config}-{kv_dtype}-bs{bs}-part{part_resolved}-impl{impl}"
-                   + (f"-d{D}" if D != 128 else ""))
+                   + (f"-d{D}" if D != 128 else "") + ("-separate" if separate else "-append"))
     traffic = measured_traffic(traffic_key)
     unique_gbs = (unique_kv_bytes + qo_bytes) / (dec_avg_ms * 1e-3) / 1e9
     print(f"[bench] step {step_ms:.3f} ms, {gbs:.0f} GB/s; partition kernel "
@@ -321,6 +350,8 @@ def main():
             "mean_context": float(ctx.mean()),
             "partition_tokens": part_resolved,
             "impl": args.impl,
+            "cache_write": "separate launch (reshape_and_cache)" if separate
+                           else "in the decode launch (paged_attention_decode_append)",
             "parallelism": "single GPU",
         },
         "pct_of_peak": round(gbs / PEAK_HBM_GBS, 4),
@@ -337,6 +368,9 @@ def main():
             "traffic": traffic,
             "avg_launch_us": round(dec_avg_ms * 1e3, 2),
             "algorithmic_bytes_per_launch": launch_bytes,
+            "launch_timing": f"HIP events on the launch stream around every partition-kernel "
+                             f"launch of {len(timed_steps)} of the {args.steps} timed steps "
+                             f"({len(dec_ms)} launches)",
         },
         "unique_bytes": {
             "kv_bytes_per_launch": unique_kv_bytes,

@@ -364,6 +364,44 @@ int32_t paged_attention_decode_ex(void* out, const void* q, int32_t q_dtype,
                                   const pkv_decode_opts* opts,
                                   pkv_stream_t stream);
 
+/* paged_attention_decode_append: reshape_and_cache of each sequence's new
+ * token followed by paged_attention_decode_ex, in one launch.  Each decode
+ * step appends only the new token's key and value, and attention then sees
+ * every token including it (vToken page, "KV cache basics"): c counts the
+ * new token, which sits at position c - 1.  The workgroup whose partition holds position c - 1 of
+ * (sequence, kv head) writes the token's K / V row to slot
+ * block_tables[s][(c-1) / block_size] * block_size + (c-1) % block_size
+ * exactly as reshape_and_cache would (bit for bit), then reads the pool.
+ *   key, value : [num_seqs][num_kv_heads][head_dim] of q_dtype, the new
+ *                token's K and V (post-RoPE), device memory.
+ *   k_cache,
+ *   v_cache    : one layer's pools, written and read.
+ *   opts       : required, with opts->num_blocks > 0 (the pool size): a
+ *                table entry at or past it gets no write (and is read as
+ *                the null block, as in paged_attention_decode_ex).
+ * Other arguments as paged_attention_decode_ex.  No write happens for a
+ * sequence with c <= 0 or c > min(max_context_len, max_blocks_per_seq *
+ * block_size).  The block receiving the token must not be read by another
+ * sequence of the same call (copy-on-write, [P1] §4, guarantees it: only
+ * unshared blocks are written); otherwise that sequence may see the slot
+ * before or after the write.  Errors: as paged_attention_decode_ex, plus
+ * PKV_ERR_ARG for missing opts / num_blocks, key or value, non-positive fp8
+ * scales, or a stages mask without PKV_STAGE_PARTITIONS. */
+int32_t paged_attention_decode_append(void* out, const void* q, int32_t q_dtype,
+                                      const void* key, const void* value,
+                                      void* k_cache, void* v_cache,
+                                      const int32_t* block_tables,
+                                      int32_t max_blocks_per_seq,
+                                      const int32_t* context_lens,
+                                      int32_t max_context_len, int32_t num_seqs,
+                                      int32_t num_heads, int32_t num_kv_heads,
+                                      int32_t head_dim, float scale,
+                                      int32_t block_size, int32_t kv_dtype,
+                                      float k_scale, float v_scale,
+                                      void* workspace, int64_t workspace_bytes,
+                                      const pkv_decode_opts* opts,
+                                      pkv_stream_t stream);
+
 /* ------------------------------------------------------- multi-token --
  *
  * paged_attention_prefill: several new tokens per sequence (a chunk of a

@@ -11,7 +11,7 @@ from ._binding import (  # noqa: F401
     PagedKVError, KVPool, lib, lib_path, version, last_error, bytes_per_token, tile_bytes,
     layer_pool_bytes, workspace_bytes, default_partition_tokens, plan_bytes, build_plan,
     decode_slot_mapping, reshape_and_cache,
-    paged_attention_decode, check_block_tables, torch_dtype, dtype_code, EXPORTS,
+    paged_attention_decode, paged_attention_decode_append, check_block_tables, torch_dtype, dtype_code, EXPORTS,
     BlockManager, copy_blocks, paged_attention_prefill, paged_attention_decode_tokens,
     move_tokens,
     repack_blocks,

@@ -34,6 +34,7 @@ EXPORTS = [
     "pkv_move_tokens", "pkv_bm_repack_tiles", "pkv_repack_blocks",
     "pkv_read_probe_sink_bytes", "pkv_read_probe", "kv_pool_bytes_per_token",
     "pkv_bm_mark_computed", "pkv_bm_num_computed_tokens", "paged_attention_decode_noalloc",
+    "paged_attention_decode_append",
 ]
 
 
@@ -90,6 +91,9 @@ def lib():
             "paged_attention_decode_ex": (i32, [p, p, i32, p, p, p, i32, p, i32, i32, i32, i32,
                                                 i32, f32, i32, i32, f32, f32, p, i64,
                                                 ctypes.POINTER(DecodeOpts), p]),
+            "paged_attention_decode_append": (i32, [p, p, i32, p, p, p, p, p, i32, p, i32, i32,
+                                                    i32, i32, i32, f32, i32, i32, f32, f32, p,
+                                                    i64, ctypes.POINTER(DecodeOpts), p]),
             "paged_attention_decode_noalloc": (i32, [p, p, i32, p, p, p, i32, p, i32, i32, i32,
                                                      i32, i32, f32, i32, i32, f32, f32, p]),
             "pkv_check_block_tables": (i32, [p, i32, p, i32, i32, i32, p,
@@ -329,6 +333,34 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
         int(max_context_len), S, H, num_kv_heads, D, float(scale), block_size, kv_dtype,
         float(k_scale), float(v_scale), _ptr(workspace, "workspace"), ws_bytes,
         ctypes.byref(opts), _stream(stream)))
+    return out
+
+
+def paged_attention_decode_append(out, q, key, value, k_cache, v_cache, block_tables,
+                                  context_lens, max_context_len, num_kv_heads, block_size,
+                                  kv_dtype, scale, k_scale=1.0, v_scale=1.0, workspace=None,
+                                  partition_tokens=0, impl=IMPL_AUTO, num_blocks=0, plan=None,
+                                  stages=0, stream=None):
+    """reshape_and_cache of every sequence's new token (key/value: [S][H_kv][d]
+    in q's dtype, written to position context_len - 1) and the decode, in one
+    launch.  num_blocks = 0 takes the pool size from the pool tensors."""
+    S, H, D = q.shape
+    if tuple(key.shape) != (S, num_kv_heads, D) or tuple(value.shape) != (S, num_kv_heads, D):
+        raise ValueError(f"key/value must be [{S}][{num_kv_heads}][{D}]")
+    num_blocks = _pool_blocks(k_cache, v_cache, num_blocks, num_kv_heads, D, block_size, kv_dtype)
+    need = workspace_bytes(S, H, num_kv_heads, D, max_context_len, block_size, partition_tokens)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    opts = DecodeOpts(partition_tokens, impl, stages, num_blocks,
+                      plan.data_ptr() if plan is not None else None)
+    _check(lib().paged_attention_decode_append(
+        _ptr(out, "out"), _ptr(q, "q"), dtype_code(q.dtype), _ptr(key, "key", q.dtype),
+        _ptr(value, "value", q.dtype), _ptr(k_cache, "k_cache"), _ptr(v_cache, "v_cache"),
+        _ptr(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+        _ptr(context_lens, "context_lens", torch.int32), int(max_context_len), S, H,
+        num_kv_heads, D, float(scale), block_size, kv_dtype, float(k_scale), float(v_scale),
+        _ptr(workspace, "workspace"), ws_bytes, ctypes.byref(opts), _stream(stream)))
     return out
 
 

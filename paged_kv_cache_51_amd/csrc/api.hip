@@ -323,14 +323,22 @@ int32_t paged_attention_plan(const int32_t* context_lens, int32_t num_seqs, int3
     return ok();
 }
 
-int32_t paged_attention_decode_ex(void* out, const void* q, int32_t q_dtype, const void* k_cache,
-                                  const void* v_cache, const int32_t* block_tables,
-                                  int32_t max_blocks_per_seq, const int32_t* context_lens,
-                                  int32_t max_context_len, int32_t num_seqs, int32_t num_heads,
-                                  int32_t num_kv_heads, int32_t head_dim, float scale,
-                                  int32_t block_size, int32_t kv_dtype, float k_scale,
-                                  float v_scale, void* workspace, int64_t workspace_bytes,
-                                  const pkv_decode_opts* opts, pkv_stream_t stream) {
+// The decode behind paged_attention_decode_ex and _append: `append` (may be
+// null) carries the new token's K / V rows and the inverse fp8 scales.
+struct AppendRows {
+    const void* key;
+    const void* value;
+    float k_inv, v_inv;
+};
+
+static int32_t decode_impl(void* out, const void* q, int32_t q_dtype, const void* k_cache,
+                           const void* v_cache, const int32_t* block_tables,
+                           int32_t max_blocks_per_seq, const int32_t* context_lens,
+                           int32_t max_context_len, int32_t num_seqs, int32_t num_heads,
+                           int32_t num_kv_heads, int32_t head_dim, float scale, int32_t block_size,
+                           int32_t kv_dtype, float k_scale, float v_scale, void* workspace,
+                           int64_t workspace_bytes, const pkv_decode_opts* opts,
+                           const AppendRows* append, pkv_stream_t stream) {
     pkv_decode_opts o{0, PKV_IMPL_AUTO, 0, 0, nullptr};
     if (opts) o = *opts;
     if (int32_t e = check_layout_args(head_dim, block_size, kv_dtype)) return e;
@@ -398,6 +406,12 @@ int32_t paged_attention_decode_ex(void* out, const void* q, int32_t q_dtype, con
     const float ks = kv_dtype == PKV_FP8_E4M3 ? k_scale : 1.0f;
     a.qk_scale_log2 = (float)((double)scale * (double)ks * 1.4426950408889634);
     a.out_scale = kv_dtype == PKV_FP8_E4M3 ? v_scale : 1.0f;
+    if (append) {
+        a.new_key = append->key;
+        a.new_value = append->value;
+        a.k_inv = append->k_inv;
+        a.v_inv = append->v_inv;
+    }
 
     hipStream_t st = (hipStream_t)stream;
     (void)hipGetLastError();
@@ -415,6 +429,49 @@ int32_t paged_attention_decode_ex(void* out, const void* q, int32_t q_dtype, con
         if (e != hipSuccess) return hip_fail(e, "partition reduce launch");
     }
     return ok();
+}
+
+int32_t paged_attention_decode_ex(void* out, const void* q, int32_t q_dtype, const void* k_cache,
+                                  const void* v_cache, const int32_t* block_tables,
+                                  int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                  int32_t max_context_len, int32_t num_seqs, int32_t num_heads,
+                                  int32_t num_kv_heads, int32_t head_dim, float scale,
+                                  int32_t block_size, int32_t kv_dtype, float k_scale,
+                                  float v_scale, void* workspace, int64_t workspace_bytes,
+                                  const pkv_decode_opts* opts, pkv_stream_t stream) {
+    return decode_impl(out, q, q_dtype, k_cache, v_cache, block_tables, max_blocks_per_seq,
+                       context_lens, max_context_len, num_seqs, num_heads, num_kv_heads, head_dim,
+                       scale, block_size, kv_dtype, k_scale, v_scale, workspace, workspace_bytes,
+                       opts, nullptr, stream);
+}
+
+int32_t paged_attention_decode_append(void* out, const void* q, int32_t q_dtype, const void* key,
+                                      const void* value, void* k_cache, void* v_cache,
+                                      const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                      const int32_t* context_lens, int32_t max_context_len,
+                                      int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                      int32_t head_dim, float scale, int32_t block_size,
+                                      int32_t kv_dtype, float k_scale, float v_scale,
+                                      void* workspace, int64_t workspace_bytes,
+                                      const pkv_decode_opts* opts, pkv_stream_t stream) {
+    if (!opts || opts->num_blocks <= 0)
+        return fail(PKV_ERR_ARG, "decode_append needs opts->num_blocks > 0 (the pool size bounds the write)");
+    if (opts->stages && !(opts->stages & PKV_STAGE_PARTITIONS))
+        return fail(PKV_ERR_ARG, "decode_append writes in the partition stage; it cannot be left out");
+    if (valid_block_size(block_size) && (int64_t)opts->num_blocks * block_size >= (1LL << 31))
+        return fail(PKV_ERR_ARG, "num_blocks * block_size must stay below 2^31");
+    if (num_seqs > 0 && (!key || !value)) return fail(PKV_ERR_ARG, "null pointer");
+    AppendRows ap{key, value, 1.0f, 1.0f};
+    if (kv_dtype == PKV_FP8_E4M3) {
+        if (!(std::isfinite(k_scale) && k_scale > 0.f && std::isfinite(v_scale) && v_scale > 0.f))
+            return fail(PKV_ERR_ARG, "fp8 scales must be finite and positive");
+        ap.k_inv = 1.0f / k_scale;   // as reshape_and_cache
+        ap.v_inv = 1.0f / v_scale;
+    }
+    return decode_impl(out, q, q_dtype, k_cache, v_cache, block_tables, max_blocks_per_seq,
+                       context_lens, max_context_len, num_seqs, num_heads, num_kv_heads, head_dim,
+                       scale, block_size, kv_dtype, k_scale, v_scale, workspace, workspace_bytes,
+                       opts, &ap, stream);
 }
 
 int32_t paged_attention_prefill(void* out, const void* q, int32_t q_dtype, const void* k_cache,

@@ -6,66 +6,25 @@
 // table, block 0 is reserved as the null block; vToken page
 // (gotosocial.chinng-lab-srv.dev) "KV cache basics" — each decode step only
 // appends the new token's key and value.
-#include "pkv_device.h"
+#include "cache_write.h"
 #include "pkv_launch.h"
 
 namespace pkv {
 
-// One wave per (token, kv head); lane l owns dims k0 = 2l + 128 i and k0 + 1
-// of the D-dim row (D = head_dim: 64, 128 or 256).  K: dims k0, k0 + 1 are
-// adjacent inside one 8-dim group, so one 4-byte (16-bit types) or 2-byte
-// (fp8) store.  V: the two dims live in neighbouring lanes of the V row, so
-// two element stores.
+// One wave per (token, kv head); the row layout is TokenRow's.
 template <int SRC, int KVT, int BS, int D>
 __global__ __launch_bounds__(64) void reshape_and_cache_kernel(
     const uint16_t* __restrict__ key, const uint16_t* __restrict__ value,
     uint8_t* __restrict__ k_cache, uint8_t* __restrict__ v_cache,
     const int32_t* __restrict__ slot_mapping, int32_t num_kv_heads,
     int64_t num_slots, float k_inv, float v_inv) {
-    constexpr int EB = elem_bytes(KVT);
-    constexpr int64_t SUB = sub_tile_bytes(KVT, D);
-    constexpr int64_t TILE = SUB * (BS / kSubTokens);
     const int t = blockIdx.x, g = blockIdx.y, lane = threadIdx.x;
     const int64_t slot = slot_mapping[t];
     if (slot < 0 || slot >= num_slots) return;
-    const int64_t pb = slot / BS;
-    const int row = (int)(slot % BS);
-    const int r = row % kSubTokens;
-    const int64_t base = (pb * num_kv_heads + g) * TILE + (row / kSubTokens) * SUB;
-
-#pragma unroll
-    for (int k0 = 2 * lane; k0 < D; k0 += 2 * kWave) {
-    const int64_t src = ((int64_t)t * num_kv_heads + g) * D + k0;
-    const uint32_t kw = *reinterpret_cast<const uint32_t*>(key + src);
-    const uint32_t vw = *reinterpret_cast<const uint32_t*>(value + src);
-
-    // K position of (r, k0): group c = k0/8 -> lane r + 16*(c%4), row c/4.
-    const int kc = k0 / 8, kkk = kc / 4;
-    const int k_lane = r + 16 * (kc % 4);
-    const int k_per = 2 / EB;
-    const int64_t k_off = 1024 * (kkk / k_per) + 16 * k_lane + 8 * EB * (kkk % k_per) + EB * (k0 % 8);
-    // V position of (r, k) for k = k0, k0+1: tile nt = k/16, lane k%16 + 16*(r/4).
-    const int v_per = 4 / EB;
-    const int nt = k0 / 16;
-    const int64_t v_off0 = 1024 * (nt / v_per) + 16 * ((k0 % 16) + 16 * (r / 4)) +
-                           4 * EB * (nt % v_per) + EB * (r % 4);
-    const int64_t v_off1 = v_off0 + 16;   // next dim = next lane
-
-    if constexpr (KVT == DT_FP8) {
-        const float k_lo = bits_to_f32<SRC>(kw & 0xffffu) * k_inv;
-        const float k_hi = bits_to_f32<SRC>(kw >> 16) * k_inv;
-        const float v_lo = bits_to_f32<SRC>(vw & 0xffffu) * v_inv;
-        const float v_hi = bits_to_f32<SRC>(vw >> 16) * v_inv;
-        const uint16_t kcode = (uint16_t)(f32_to_e4m3(k_lo) | (f32_to_e4m3(k_hi) << 8));
-        *reinterpret_cast<uint16_t*>(k_cache + base + k_off) = kcode;
-        v_cache[base + v_off0] = (uint8_t)f32_to_e4m3(v_lo);
-        v_cache[base + v_off1] = (uint8_t)f32_to_e4m3(v_hi);
-    } else {
-        *reinterpret_cast<uint32_t*>(k_cache + base + k_off) = kw;
-        *reinterpret_cast<uint16_t*>(v_cache + base + v_off0) = (uint16_t)(vw & 0xffffu);
-        *reinterpret_cast<uint16_t*>(v_cache + base + v_off1) = (uint16_t)(vw >> 16);
-    }
-    }
+    const int64_t src = ((int64_t)t * num_kv_heads + g) * D;
+    TokenRow<D> row;
+    row.load(key + src, value + src, lane);
+    row.template store<SRC, KVT, BS>(k_cache, v_cache, slot, num_kv_heads, g, lane, k_inv, v_inv);
 }
 
 // slot of the newest token (position c-1) of every sequence.

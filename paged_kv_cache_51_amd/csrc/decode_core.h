@@ -3,7 +3,7 @@
 // in flight, and the merge of a workgroup's waves.  The per-unit math is a
 // policy (matrix cores in decode.hip, vector ALU in decode_vector.hip).
 #pragma once
-#include "pkv_device.h"
+#include "cache_write.h"
 #include "pkv_launch.h"
 
 namespace pkv {
@@ -231,8 +231,23 @@ __device__ __forceinline__ void decode_entry(const DecodeArgs& a, float* pkv_sme
     Math mt;
     mt.load_q(a, qt, kvh, lane);
 
-    int ctx = a.context_lens[s];
-    ctx = ctx < a.ctx_cap ? ctx : a.ctx_cap;
+    const int c_full = a.context_lens[s];
+    const int ctx = c_full < a.ctx_cap ? c_full : a.ctx_cap;
+    // Append, first half: wave 0 fetches the new token's K / V row and the
+    // block id of position c - 1 now, beside the query loads, so the write
+    // below adds no memory round trip of its own.  Every partition's wave 0
+    // fetches (512 bytes); only the one holding position c - 1 writes.
+    const bool append = a.new_key != nullptr && qt.ntok == 1 && w == 0;
+    TokenRow<D> new_row;
+    int32_t new_pb = -1;
+    if (append) {
+        const int64_t row = ((int64_t)s * a.num_kv_heads + kvh) * D;
+        new_row.load(reinterpret_cast<const uint16_t*>(a.new_key) + row,
+                     reinterpret_cast<const uint16_t*>(a.new_value) + row, lane);
+        // only when the context is not clamped (the table and
+        // max_context_len cover position c - 1)
+        if (c_full > 0 && c_full == ctx) new_pb = bt_row[(c_full - 1) / BS];
+    }
     // keys this tile may see: positions < kv_end (its last token's + 1)
     const int kv_end = min(ctx, ctx - qt.back + qt.ntok);
     if (kv_end <= 0) {
@@ -257,6 +272,18 @@ __device__ __forceinline__ void decode_entry(const DecodeArgs& a, float* pkv_sme
     int* done = reinterpret_cast<int*>(pkv_smem);
     const int ltid = NW == 1 ? lane : (int)threadIdx.x;
     if (ltid == 0) *done = 0;
+    if (append && u1 == n_units && (unsigned)new_pb < (unsigned)a.num_blocks) {
+        // Append, second half: this workgroup's partition holds position
+        // ctx - 1, the new token, so it writes the token's K / V into its
+        // slot (as reshape_and_cache would) before any wave loads that unit;
+        // the barrier below orders the stores before those loads (waves of
+        // one workgroup share the CU's write-through L1).
+        new_row.template store<QT, KVT, BS>(const_cast<uint8_t*>(a.k_cache),
+                                            const_cast<uint8_t*>(a.v_cache),
+                                            (int64_t)new_pb * BS + (ctx - 1) % BS, a.num_kv_heads,
+                                            kvh, lane, a.k_inv, a.v_inv);
+        if constexpr (NW == 1) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    }
     mt.stage_q(pkv_smem + merge_lds_floats(NW, ncols, Math::kCols, D), ltid);
     if constexpr (NW > 1) __syncthreads();
     mt.begin();

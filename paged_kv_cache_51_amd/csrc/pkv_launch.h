@@ -47,6 +47,15 @@ struct DecodeArgs {
     int32_t head_dim;      // 64, 128 or 256 (decode); 128 elsewhere
     float qk_scale_log2;   // scale * k_scale * log2(e)
     float out_scale;       // v_scale for fp8 pools, else 1
+    // Append (decode only; null = off): the new token's K and V rows
+    // [num_seqs][num_kv_heads][head_dim] in the query dtype, written to the
+    // slot of position c - 1 by the workgroup whose partition holds it,
+    // before that workgroup reads the pool.  The pools are then written
+    // through k_cache / v_cache.
+    const void* new_key;
+    const void* new_value;
+    float k_inv;           // 1 / k_scale for fp8 pools, else 1
+    float v_inv;
 };
 
 // Error reporting shared by the extern "C" entry points (api.hip): set the

@@ -116,6 +116,36 @@ def test_decode_argument_errors(kw, code):
     assert pkv.last_error()
 
 
+def _append(opts=True, **kw):
+    a = dict(out=FAKE, q=FAKE, q_dtype=0, key=FAKE, value=FAKE, k=FAKE, v=FAKE, bt=FAKE, mbps=4,
+             ctx=FAKE, maxc=64, S=2, H=8, Hkv=2, D=128, scale=0.1, bs=16, kvdt=0, ks=1.0,
+             vs=1.0, ws=None, wsb=0)
+    a.update(kw)
+    o = pkv._binding.DecodeOpts(0, 0, kw.get("stages", 0), kw.get("nb", 100))
+    return pkv.lib().paged_attention_decode_append(
+        a["out"], a["q"], a["q_dtype"], a["key"], a["value"], a["k"], a["v"], a["bt"], a["mbps"],
+        a["ctx"], a["maxc"], a["S"], a["H"], a["Hkv"], a["D"], a["scale"], a["bs"], a["kvdt"],
+        a["ks"], a["vs"], a["ws"], a["wsb"], ctypes.byref(o) if opts else None, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(opts=False), -1),          # the pool size is required
+    (dict(nb=0), -1),
+    (dict(nb=1 << 27, bs=32), -1),   # slot numbers would overflow int32
+    (dict(stages=2), -1),            # the write happens in the partition stage
+    (dict(key=None), -1),
+    (dict(value=None), -1),
+    (dict(kvdt=2, ks=0.0), -1),      # fp8 pools need positive scales
+    (dict(kvdt=2, vs=-1.0), -1),
+    (dict(H=9), -1),                 # the decode's own checks follow
+    (dict(D=192), -4),
+    (dict(kvdt=1), -4),
+])
+def test_decode_append_argument_errors(kw, code):
+    assert _append(**kw) == code
+    assert pkv.last_error()
+
+
 def test_reshape_and_cache_argument_errors():
     L = pkv.lib()
     f = lambda **k: L.reshape_and_cache(FAKE, FAKE, k.get("src", 0), FAKE, FAKE, FAKE, 4, 2,
