@@ -1,0 +1,108 @@
+"""GPU: a decode step captured into a HIP graph (through torch.cuda.graph)
+replays with the eager step's results.
+
+The launch shape of every decode entry depends only on host scalars, and
+the work plan, the partition partials and the persistent form's counters
+live in caller memory that each launch fully rewrites (the counters are
+reset by the launch's last workgroup), so a captured step can be replayed
+with new contents in context_lens, block tables, q and the new K / V.  Each
+replay is checked bit for bit against the eager step on the same inputs,
+with eager work and host synchronisations between replays.
+"""
+import numpy as np
+import pytest
+import torch
+
+pkv = pytest.importorskip("paged_kv_cache_51_amd")
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def log(*a):
+    print(*a, flush=True)
+
+
+def randn_pool(nbytes, gen):
+    n = nbytes // 2
+    return torch.randn(n, generator=gen, device=DEV).to(torch.bfloat16).view(torch.uint8)
+
+
+@pytest.mark.parametrize("impl", [pkv.IMPL_MFMA, pkv.IMPL_MFMA_PERSISTENT])
+def test_decode_step_replays_like_eager(impl):
+    S, H, Hkv, D, bs, L = 48, 16, 4, 128, 16, 3
+    part = 128                                   # contexts up to 700: P up to 6, so the reduce runs
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(5)
+    r = np.random.default_rng(5)
+    max_ctx = 700
+    nb = S * (max_ctx // bs + 2) + 1
+    perm = r.permutation(np.arange(1, nb)).astype(np.int32)
+    maxb = max_ctx // bs + 1
+    bt = torch.from_numpy(perm[:S * maxb].reshape(S, maxb).copy()).to(DEV)
+    pool_bytes = pkv.layer_pool_bytes(nb, Hkv, D, bs, pkv.BF16)
+    kp = [randn_pool(pool_bytes, gen) for _ in range(L)]
+    vp = [randn_pool(pool_bytes, gen) for _ in range(L)]
+    cl = torch.empty(S, dtype=torch.int32, device=DEV)
+    q = [torch.empty(S, H, D, dtype=torch.bfloat16, device=DEV) for _ in range(L)]
+    nk = [torch.empty(S, Hkv, D, dtype=torch.bfloat16, device=DEV) for _ in range(L)]
+    nv = [torch.empty(S, Hkv, D, dtype=torch.bfloat16, device=DEV) for _ in range(L)]
+    out = [torch.empty(S, H, D, dtype=torch.bfloat16, device=DEV) for _ in range(L)]
+    ws = torch.empty(pkv.workspace_bytes(S, H, Hkv, D, max_ctx, bs, part), dtype=torch.uint8,
+                     device=DEV)
+    scale = float(np.float32(1.0 / np.sqrt(D)))
+
+    def fill(seed):
+        # new inputs in place (the graph reads these buffers)
+        g = torch.Generator(device=DEV)
+        g.manual_seed(seed)
+        lens = np.random.default_rng(seed).integers(1, max_ctx + 1, S).astype(np.int32)
+        cl.copy_(torch.from_numpy(lens))
+        for t in q + nk + nv:
+            t.copy_(torch.randn(t.shape, generator=g, device=DEV).to(torch.bfloat16))
+
+    def step():
+        for layer in range(L):
+            pkv.paged_attention_decode_append(out[layer], q[layer], nk[layer], nv[layer],
+                                              kp[layer], vp[layer], bt, cl, max_ctx, Hkv, bs,
+                                              pkv.BF16, scale, workspace=ws,
+                                              partition_tokens=part, impl=impl, num_blocks=nb)
+
+    # warm up on a side stream, as torch asks before capture
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fill(1)
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+
+    for rep, seed in enumerate((11, 12, 13)):
+        log(f"  impl={impl} replay {rep} (inputs seed {seed})")
+        # eager reference on copies of the pools (the step writes them)
+        fill(seed)
+        k0 = [t.clone() for t in kp]
+        v0 = [t.clone() for t in vp]
+        step()
+        torch.cuda.synchronize()
+        want = [t.clone() for t in out]
+        k_want = [t.clone() for t in kp]
+        v_want = [t.clone() for t in vp]
+        for t, s in zip(kp + vp, k0 + v0):
+            t.copy_(s)
+        for t in out:
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for layer in range(L):
+            assert torch.equal(out[layer].view(torch.int16), want[layer].view(torch.int16)), \
+                f"replay {rep} layer {layer}: output differs from the eager step"
+            assert torch.equal(kp[layer], k_want[layer]) and torch.equal(vp[layer], v_want[layer])
+        assert torch.isfinite(out[0].float()).all()
