@@ -621,6 +621,7 @@ int32_t pkv_repack_blocks(void* const* k_layers, void* const* v_layers, int32_t 
     if (head_dim != kBuiltHeadDim) return fail(PKV_ERR_UNSUPPORTED, "kernels are built for head_dim 128, got %d", head_dim);
     if (num_layers < 0 || num_chains < 0 || num_kv_heads <= 0 || num_blocks < 1)
         return fail(PKV_ERR_ARG, "bad sizes");
+    if (num_kv_heads > 65535) return fail(PKV_ERR_UNSUPPORTED, "num_kv_heads must be <= 65535 (grid limit)");
     if ((int64_t)num_blocks * block_size >= (1LL << 31)) return fail(PKV_ERR_ARG, "slots must fit int32");
     if (num_chains == 0 || num_layers == 0) return ok();
     if (!k_layers || !v_layers || !tiles || !chain_offsets) return fail(PKV_ERR_ARG, "null pointer");

@@ -272,11 +272,14 @@ static hipError_t launch_moves_t(MoveArgs a, void* const* kl, void* const* vl, h
 // tile's block) gets its K and V sub-tiles assembled from the rows' source
 // slots with the same per-token gather as the token-table decode, then
 // stored whole (16-byte stores of complete pool rows: no partial writes).
-// Workgroup (chain, layer), wave w takes kv heads w, w + 4, ...; a wave
-// walks its chain's units in order, a few at a time (gather them, then
-// store them).  No source of a unit lies in rows an earlier unit of the chain
-// writes, so a store can never clobber a source still to be read; the
-// chains of one call touch disjoint blocks.
+// A repack is a compaction: the survivor that lands in row q comes from a
+// position >= q, so the sources of a unit never lie in rows that an earlier
+// unit of the chain writes, but they may lie in rows a later unit writes.
+// Workgroup (chain, layer, kv head): its four waves take the chain's units in
+// rounds of 4 x CH (wave w gathers units w CH .. w CH + CH - 1 of the round
+// into registers), waits for them and meets the barrier, then every wave
+// stores its units: every store follows the gathers of all units up to its
+// own.  The chains of one call touch disjoint blocks.
 
 struct RepackArgs {
     uint8_t* k[kMoveLayers];
@@ -297,52 +300,65 @@ __global__ __launch_bounds__(kMoveThreads) void repack_blocks_kernel(const Repac
     constexpr int R = rows_per_sub(KVT);
     constexpr int64_t SUB = sub_tile_bytes(KVT);
     constexpr int64_t TILE = SUB * NSUB;
-    constexpr int CH = PKV_REPACK_UNITS;   // units gathered before their stores
+    constexpr int CH = PKV_REPACK_UNITS;   // units one wave gathers per round
+    constexpr int NW = kMoveThreads / kWave;
     const int lane = threadIdx.x & (kWave - 1);
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int layer = blockIdx.y;
+    const int h = blockIdx.z;
     const int t0 = a.chain_offsets[blockIdx.x];
     const int n_units = (a.chain_offsets[blockIdx.x + 1] - t0) * NSUB;
-    if (n_units <= 0) return;
+    if (n_units <= 0) return;                      // (whole workgroup)
     const int32_t cap = a.num_blocks * BS;
     const int64_t head_stride = (int64_t)a.num_kv_heads * TILE;
-    for (int h = w; h < a.num_kv_heads; h += kMoveThreads / kWave) {
-        const uint8_t* kp = a.k[layer] + (int64_t)h * TILE;
-        const uint8_t* vp = a.v[layer] + (int64_t)h * TILE;
-        for (int c0 = 0; c0 < n_units; c0 += CH) {
-            const int nc = min(CH, n_units - c0);
-            // lane l: row l % 16 of chunk unit min(l / 16, nc - 1) (lanes past
-            // CH units repeat the last one); a source
-            // outside the pool leaves the row as it is (reads its own slot)
-            const int un = c0 + min(lane >> 4, nc - 1);
-            const int32_t* tile = a.tiles + (int64_t)(t0 + un / NSUB) * (1 + BS);
-            const int32_t dst_block = tile[0];
-            const int row = (un % NSUB) * kSubTokens + (lane & 15);
-            int32_t slot = tile[1 + row];
-            if ((unsigned)(slot - BS) >= (unsigned)(cap - BS)) slot = dst_block * BS + row;
-            const bool dst_ok = (unsigned)(dst_block - 1) < (unsigned)(a.num_blocks - 1);
-            if (!dst_ok) slot = BS;   // (unit skipped below; any valid slot)
-            UnitRegs<KVT> buf[CH];
+    const uint8_t* kp = a.k[layer] + (int64_t)h * TILE;
+    const uint8_t* vp = a.v[layer] + (int64_t)h * TILE;
+    for (int r0 = 0; r0 < n_units; r0 += NW * CH) {
+        const int c0 = r0 + w * CH;                // this wave's first unit
+        const int nc = max(0, min(CH, n_units - c0));
+        // lane l: row l % 16 of unit c0 + min(l / 16, nc - 1) (lanes past the
+        // wave's units repeat its last one; a wave with none repeats the
+        // chain's last unit); a source outside the pool leaves the row as it
+        // is (reads its own slot)
+        const int un = nc > 0 ? c0 + min(lane >> 4, nc - 1) : n_units - 1;
+        const int32_t* tile = a.tiles + (int64_t)(t0 + un / NSUB) * (1 + BS);
+        const int32_t dst_block = tile[0];
+        const int row = (un % NSUB) * kSubTokens + (lane & 15);
+        int32_t slot = tile[1 + row];
+        if ((unsigned)(slot - BS) >= (unsigned)(cap - BS)) slot = dst_block * BS + row;
+        const bool dst_ok = (unsigned)(dst_block - 1) < (unsigned)(a.num_blocks - 1);
+        if (!dst_ok) slot = BS;   // (unit skipped below; any valid slot)
+        UnitRegs<KVT> buf[CH];
 #pragma unroll
-            for (int j = 0; j < CH; ++j)
-                gather_unit<KVT, BS>(buf[j], kp, vp, head_stride, slot, min(j, nc - 1), lane);
+        for (int j = 0; j < CH; ++j)
+            gather_unit<KVT, BS>(buf[j], kp, vp, head_stride, slot, max(0, min(j, nc - 1)), lane);
+        // Every gather of the round complete (data in registers) before any
+        // wave stores.  The empty asm ties each gathered register, so the
+        // loads can neither stay outstanding at the barrier nor be sunk
+        // below it into the store branch (the compiler did sink them there,
+        // racing with the other waves' stores, without this).
 #pragma unroll
-            for (int j = 0; j < CH; ++j) {
-                if (j >= nc) continue;
-                const int uj = c0 + j;
-                const int32_t db = __builtin_amdgcn_readlane(dst_block, 16 * j);
-                if ((unsigned)(db - 1) >= (unsigned)(a.num_blocks - 1)) continue;
-                const int64_t off = (int64_t)db * head_stride + (int64_t)h * TILE + (uj % NSUB) * SUB + 16 * lane;
-                u32x4_t* kd = reinterpret_cast<u32x4_t*>(a.k[layer] + off);
-                u32x4_t* vd = reinterpret_cast<u32x4_t*>(a.v[layer] + off);
-                // non-temporal: the rebuilt rows are not read again here
-                // (interleaved timing: 3111 -> 3026 us for the 7B repack)
+        for (int j = 0; j < CH; ++j)
 #pragma unroll
-                for (int r = 0; r < R; ++r) __builtin_nontemporal_store(buf[j].k[r], kd + kWave * r);
+            for (int r = 0; r < R; ++r) asm volatile("" : "+v"(buf[j].k[r]), "+v"(buf[j].v[r]));
+        __syncthreads();
 #pragma unroll
-                for (int r = 0; r < R; ++r) __builtin_nontemporal_store(buf[j].v[r], vd + kWave * r);
-            }
+        for (int j = 0; j < CH; ++j) {
+            if (j >= nc) continue;
+            const int uj = c0 + j;
+            const int32_t db = __builtin_amdgcn_readlane(dst_block, 16 * j);
+            if ((unsigned)(db - 1) >= (unsigned)(a.num_blocks - 1)) continue;
+            const int64_t off = (int64_t)db * head_stride + (int64_t)h * TILE + (uj % NSUB) * SUB + 16 * lane;
+            u32x4_t* kd = reinterpret_cast<u32x4_t*>(a.k[layer] + off);
+            u32x4_t* vd = reinterpret_cast<u32x4_t*>(a.v[layer] + off);
+            // non-temporal: the rebuilt rows are not read again here
+#pragma unroll
+            for (int r = 0; r < R; ++r) __builtin_nontemporal_store(buf[j].k[r], kd + kWave * r);
+#pragma unroll
+            for (int r = 0; r < R; ++r) __builtin_nontemporal_store(buf[j].v[r], vd + kWave * r);
         }
+        // no barrier here: the next round's sources lie at or past its own
+        // rows, beyond every row this round writes
     }
 }
 
@@ -355,7 +371,8 @@ static hipError_t launch_repack_t(RepackArgs a, void* const* kl, void* const* vl
             a.k[i] = static_cast<uint8_t*>(kl[l0 + i]);
             a.v[i] = static_cast<uint8_t*>(vl[l0 + i]);
         }
-        hipLaunchKernelGGL((repack_blocks_kernel<KVT, BS>), dim3(num_chains, nl), dim3(kMoveThreads), 0, st, a);
+        hipLaunchKernelGGL((repack_blocks_kernel<KVT, BS>), dim3(num_chains, nl, a.num_kv_heads),
+                           dim3(kMoveThreads), 0, st, a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
