@@ -286,10 +286,13 @@ __device__ __forceinline__ void decode_entry(const DecodeArgs& a, float* pkv_sme
     }
     mt.stage_q(pkv_smem + merge_lds_floats(NW, ncols, Math::kCols, D), ltid);
     if constexpr (NW > 1) __syncthreads();
-    // With an append, no pool load may be moved above the barrier by the
-    // compiler (plain loads have been seen sunk below workgroup barriers;
-    // the asm's memory clobber pins them on this side)
-    if (append) asm volatile("" ::: "memory");
+    // With an append, no wave's pool load may be moved above the barrier by
+    // the compiler (plain loads have been seen sunk below workgroup
+    // barriers; the asm's memory clobber pins them on this side).  The
+    // hardware side needs no wait: waves of one workgroup share the CU's
+    // vector memory path, and the workgroup-scope release of the barrier
+    // orders the stores before the other waves' later loads.
+    if (a.new_key != nullptr) asm volatile("" ::: "memory");
     mt.begin();
 
     const int n_my = first < u1 ? (u1 - first + NW - 1) / NW : 0;
