@@ -129,22 +129,31 @@ __global__ __launch_bounds__(kWave) void decode_reduce_kernel(const DecodeArgs a
 
 // ----------------------------------------------------------------- launch --
 
-template <int KVT, int QT, int BS, int D>
-static hipError_t launch_mfma(const DecodeArgs& a, bool persistent, hipStream_t st) {
-    const size_t lds = sizeof(float) * merge_lds_floats(kWavesPerGroup, a.group, 16, D);
-    const dim3 block(kWavesPerGroup * kWave);
+// Waves per workgroup and units in flight per wave of the partition kernel.
+// 16-bit pools: eight waves, so a workgroup streams its item twice as fast
+// and the end of a launch, when few items are left, is shorter (7B shape
+// 381.9 -> 378.5 us, Llama MHA 722.6 -> 712.4 us per layer, interleaved in
+// one process), as long as partitions are long (>= 2048 tokens: with the
+// 512-token partitions of a small batch, 1.5B shape, eight waves were 10 %
+// slower, each wave holding only a few units), the eight waves' merge area
+// stays within 64 KiB of LDS and head_dim <= 128; fp8 pools: four waves with
+// one unit in flight (72B fp8 334.8 -> 329.6 us; eight waves were 0.6 %
+// slower there).
+template <int KVT, int QT, int BS, int D, int NW, int DEPTH>
+static hipError_t launch_mfma_nw(const DecodeArgs& a, bool persistent, hipStream_t st) {
+    const size_t lds = sizeof(float) * merge_lds_floats(NW, a.group, 16, D);
+    const dim3 block(NW * kWave);
     if (!persistent) {
         const dim3 grid((unsigned)grid_workgroups(a));
-        hipLaunchKernelGGL((paged_decode_mfma_kernel<KVT, QT, BS, kWavesPerGroup, kDepth, D>), grid,
-                           block, lds, st, a);
+        hipLaunchKernelGGL((paged_decode_mfma_kernel<KVT, QT, BS, NW, DEPTH, D>), grid, block, lds, st, a);
         return hipGetLastError();
     }
     // as many workgroups as can be resident at once (never more than entries)
-    static int per_cu[3][17] = {};            // cache by head_dim and group size (LDS use)
-    int& occ = per_cu[D == 64 ? 0 : (D == 128 ? 1 : 2)][a.group];
+    static int per_cu[17] = {};               // cache by group size (LDS use)
+    int& occ = per_cu[a.group];
     if (!occ) {
         hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &occ, reinterpret_cast<const void*>(&paged_decode_mfma_persistent<KVT, QT, BS, kWavesPerGroup, kDepth, D>),
+            &occ, reinterpret_cast<const void*>(&paged_decode_mfma_persistent<KVT, QT, BS, NW, DEPTH, D>),
             block.x, lds);
         if (e != hipSuccess || occ <= 0) occ = 1;
     }
@@ -154,9 +163,23 @@ static hipError_t launch_mfma(const DecodeArgs& a, bool persistent, hipStream_t 
         cus = 256;
     const int64_t entries = (int64_t)a.num_seqs * a.num_kv_heads * a.num_parts;
     const dim3 grid((unsigned)std::min<int64_t>(entries, (int64_t)occ * cus));
-    hipLaunchKernelGGL((paged_decode_mfma_persistent<KVT, QT, BS, kWavesPerGroup, kDepth, D>), grid, block,
-                       lds, st, a);
+    hipLaunchKernelGGL((paged_decode_mfma_persistent<KVT, QT, BS, NW, DEPTH, D>), grid, block, lds, st, a);
     return hipGetLastError();
+}
+
+template <int KVT, int QT, int BS, int D>
+static hipError_t launch_mfma(const DecodeArgs& a, bool persistent, hipStream_t st) {
+    constexpr int NW8 = 2 * kWavesPerGroup;
+    if constexpr (KVT == DT_FP8) {
+        return launch_mfma_nw<KVT, QT, BS, D, kWavesPerGroup, 1>(a, persistent, st);
+    } else if constexpr (D <= 128) {
+        if ((int64_t)a.part_blocks * BS >= 2048 && sizeof(float) * merge_lds_floats(NW8, a.group, 16, D) <= 65536)
+            return launch_mfma_nw<KVT, QT, BS, D, NW8, kDepth>(a, persistent, st);
+        return launch_mfma_nw<KVT, QT, BS, D, kWavesPerGroup, kDepth>(a, persistent, st);
+    } else {
+        // head_dim 256: eight waves would spill (256 VGPRs at most)
+        return launch_mfma_nw<KVT, QT, BS, D, kWavesPerGroup, kDepth>(a, persistent, st);
+    }
 }
 
 template <int KVT, int QT, int D>
