@@ -211,10 +211,16 @@ int32_t reshape_and_cache(const void* key, const void* value,
 
 /* Implementation selector for paged_attention_decode_ex. */
 enum {
-    PKV_IMPL_AUTO = 0,    /* matrix-core kernel */
+    PKV_IMPL_AUTO = 0,    /* matrix-core kernel, waves per workgroup chosen
+                             per workload: eight for 16-bit pools with
+                             head_dim <= 128 and partitions of >= 2048
+                             tokens, else four */
     PKV_IMPL_MFMA = 1,    /* GQA group on 16x16 MFMA tiles, one workgroup
-                             per (item, kv head) of the plan, the heads of
-                             an item on one XCD */
+                             of four waves per (item, kv head) of the plan,
+                             the heads of an item on one XCD: the form whose
+                             results paged_attention_prefill with one-token
+                             chunks and paged_attention_decode_tokens with
+                             an aligned table reproduce bit for bit */
     PKV_IMPL_VECTOR = 2,  /* same plan, layout and merge with the per-unit
                              math on the vector ALU (dot2), for comparison;
                              G <= 8, else PKV_ERR_UNSUPPORTED */

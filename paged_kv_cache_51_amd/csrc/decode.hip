@@ -167,9 +167,13 @@ static hipError_t launch_mfma_nw(const DecodeArgs& a, bool persistent, hipStream
     return hipGetLastError();
 }
 
+// four_waves: the four-wave form whatever the workload (PKV_IMPL_MFMA), the
+// one whose results the multi-token and token-table kernels, which run the
+// same per-wave code with four waves, reproduce bit for bit.
 template <int KVT, int QT, int BS, int D>
-static hipError_t launch_mfma(const DecodeArgs& a, bool persistent, hipStream_t st) {
+static hipError_t launch_mfma(const DecodeArgs& a, bool persistent, bool four_waves, hipStream_t st) {
     constexpr int NW8 = 2 * kWavesPerGroup;
+    if (four_waves) return launch_mfma_nw<KVT, QT, BS, D, kWavesPerGroup, (KVT == DT_FP8 ? 1 : kDepth)>(a, persistent, st);
     if constexpr (KVT == DT_FP8) {
         return launch_mfma_nw<KVT, QT, BS, D, kWavesPerGroup, 1>(a, persistent, st);
     } else if constexpr (D <= 128) {
@@ -183,16 +187,16 @@ static hipError_t launch_mfma(const DecodeArgs& a, bool persistent, hipStream_t 
 }
 
 template <int KVT, int QT, int D>
-static hipError_t launch_mfma_d(const DecodeArgs& a, int bs, bool persistent, hipStream_t st) {
-    return bs == 16 ? launch_mfma<KVT, QT, 16, D>(a, persistent, st)
-                    : launch_mfma<KVT, QT, 32, D>(a, persistent, st);
+static hipError_t launch_mfma_d(const DecodeArgs& a, int bs, bool persistent, bool four, hipStream_t st) {
+    return bs == 16 ? launch_mfma<KVT, QT, 16, D>(a, persistent, four, st)
+                    : launch_mfma<KVT, QT, 32, D>(a, persistent, four, st);
 }
 
 template <int KVT, int QT>
-static hipError_t launch_mfma_bs(const DecodeArgs& a, int bs, bool persistent, hipStream_t st) {
-    if (a.head_dim == 64) return launch_mfma_d<KVT, QT, 64>(a, bs, persistent, st);
-    if (a.head_dim == 256) return launch_mfma_d<KVT, QT, 256>(a, bs, persistent, st);
-    return launch_mfma_d<KVT, QT, 128>(a, bs, persistent, st);
+static hipError_t launch_mfma_bs(const DecodeArgs& a, int bs, bool persistent, bool four, hipStream_t st) {
+    if (a.head_dim == 64) return launch_mfma_d<KVT, QT, 64>(a, bs, persistent, four, st);
+    if (a.head_dim == 256) return launch_mfma_d<KVT, QT, 256>(a, bs, persistent, four, st);
+    return launch_mfma_d<KVT, QT, 128>(a, bs, persistent, four, st);
 }
 
 hipError_t launch_decode_vector(const DecodeArgs& a, int q_dtype, int kv_dtype, int block_size,
@@ -203,12 +207,13 @@ hipError_t launch_decode_partitions(const DecodeArgs& a, int q_dtype, int kv_dty
     if (a.num_seqs == 0 || a.num_parts == 0) return hipSuccess;
     if (impl == 2) return launch_decode_vector(a, q_dtype, kv_dtype, block_size, st);
     const bool persistent = impl == 3;
+    const bool four = impl == 1;
     if (q_dtype == DT_BF16) {
-        if (kv_dtype == DT_BF16) return launch_mfma_bs<DT_BF16, DT_BF16>(a, block_size, persistent, st);
-        return launch_mfma_bs<DT_FP8, DT_BF16>(a, block_size, persistent, st);
+        if (kv_dtype == DT_BF16) return launch_mfma_bs<DT_BF16, DT_BF16>(a, block_size, persistent, four, st);
+        return launch_mfma_bs<DT_FP8, DT_BF16>(a, block_size, persistent, four, st);
     }
-    if (kv_dtype == DT_FP16) return launch_mfma_bs<DT_FP16, DT_FP16>(a, block_size, persistent, st);
-    return launch_mfma_bs<DT_FP8, DT_FP16>(a, block_size, persistent, st);
+    if (kv_dtype == DT_FP16) return launch_mfma_bs<DT_FP16, DT_FP16>(a, block_size, persistent, four, st);
+    return launch_mfma_bs<DT_FP8, DT_FP16>(a, block_size, persistent, four, st);
 }
 
 template <int QT, int D>

@@ -70,7 +70,7 @@ def test_reshape_and_cache_bit_exact(d, kv, bs):
 @pytest.mark.parametrize("d", [64, 256])
 @pytest.mark.parametrize("kv,bs", [(oracle.BF16, 16), (oracle.FP8, 16), (oracle.FP16, 32), (oracle.BF16, 32)])
 @pytest.mark.parametrize("H,Hkv", [(8, 8), (16, 4), (24, 2)])
-@pytest.mark.parametrize("part,impl", [(0, 0), (64, 0), (32, 3)])
+@pytest.mark.parametrize("part,impl", [(0, 0), (64, 0), (32, 3), (4096, 0)])
 def test_decode_matches_oracle(d, kv, bs, H, Hkv, part, impl):
     if part and part % bs:
         pytest.skip("partition must be a multiple of the block size")

@@ -216,6 +216,25 @@ def test_decode_tiny(kv, q, bs, part):
     check(got, want, kv, f"tiny part={part}")
 
 
+@pytest.mark.parametrize("kv,q,bs", [(oracle.BF16, oracle.BF16, 16), (oracle.FP16, oracle.FP16, 32)])
+@pytest.mark.parametrize("H,Hkv", [(28, 4), (16, 2), (8, 8)])
+@pytest.mark.parametrize("part", [2048, 4096])
+def test_decode_long_partitions_both_wave_counts(kv, q, bs, H, Hkv, part):
+    """Partitions of >= 2048 tokens: AUTO runs 16-bit pools with eight waves
+    per workgroup, IMPL_MFMA with four.  Both are held to the oracle on
+    contexts that end on, just before and just after partition and unit
+    boundaries, so every wave's share of the unit ring ends raggedly."""
+    log(f"decode long partitions kv={kv} bs={bs} H={H}/{Hkv} part={part}")
+    lengths = [1, 15, 2047, 2048, 2049, 3001, 4096, 4111, 6000]
+    tabs, qb, kp, vp = make_case(lengths, H, Hkv, bs, kv, q, seed=part + H)
+    want = oracle.paged_decode(qb, q, kp, vp, kv, tabs.block_tables, tabs.context_lens, Hkv, bs,
+                               SCALE)
+    for impl in (pkv.IMPL_AUTO, pkv.IMPL_MFMA):
+        got = gpu_decode(qb, q, kp, vp, kv, tabs.block_tables, tabs.context_lens, Hkv, bs, SCALE,
+                         part=part, impl=impl, num_blocks=tabs.num_blocks)
+        check(got, want, kv, f"part={part} impl={impl}")
+
+
 @pytest.mark.parametrize("H,Hkv", [(4, 4), (8, 2), (28, 4), (16, 2), (32, 2)])
 def test_decode_group_sizes(H, Hkv):
     log(f"decode group sizes H={H} Hkv={Hkv}")
@@ -438,7 +457,9 @@ def test_persistent_matches_grid_bitwise_and_reuses_plan(cfg, kv):
     mc = int(tabs.context_lens.max())
     plan = pkv.build_plan(cl, mc, bt.shape[1], Hkv, bs)
     outs = []
-    for impl in (pkv.IMPL_MFMA, pkv.IMPL_MFMA_PERSISTENT, pkv.IMPL_MFMA_PERSISTENT,
+    # AUTO: the grid launch with the same waves-per-workgroup choice as the
+    # persistent one
+    for impl in (pkv.IMPL_AUTO, pkv.IMPL_MFMA_PERSISTENT, pkv.IMPL_MFMA_PERSISTENT,
                  pkv.IMPL_MFMA_PERSISTENT):
         out = torch.full_like(q, float("nan"))
         pkv.paged_attention_decode(out, q, kd, vd, bt, cl, mc, Hkv, bs, kv, SCALE, ks, vs,

@@ -295,8 +295,10 @@ def test_one_token_chunks_equal_decode_bitwise(kv):
     kd, vd = torch.from_numpy(kp).to(DEV), torch.from_numpy(vp).to(DEV)
     bt, cl = devi(tabs.block_tables), devi(tabs.context_lens)
     a = torch.full_like(q, float("nan"))
+    # the four-wave decode form (the multi-token kernel runs four waves)
     pkv.paged_attention_decode(a, q, kd, vd, bt, cl, mc, Hkv, bs, kv, SCALE, ks, vs,
-                               partition_tokens=-(-mc // bs) * bs, num_blocks=tabs.num_blocks)
+                               partition_tokens=-(-mc // bs) * bs, num_blocks=tabs.num_blocks,
+                               impl=pkv.IMPL_MFMA)
     b = torch.full_like(q, float("nan"))
     pkv.paged_attention_prefill(b, q, kd, vd, bt, cl, devi(np.arange(S + 1)), 1, mc, Hkv, bs, kv,
                                 SCALE, ks, vs)

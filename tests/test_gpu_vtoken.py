@@ -96,8 +96,10 @@ def test_aligned_token_table_equals_block_decode_bitwise(kv):
     kd, vd = torch.from_numpy(kp).to(DEV), torch.from_numpy(vp).to(DEV)
     cl = devi(tabs.context_lens)
     a = torch.full_like(q, float("nan"))
+    # the four-wave decode form (the token-table kernel runs four waves)
     pkv.paged_attention_decode(a, q, kd, vd, devi(tabs.block_tables), cl, mc, Hkv, bs, kv, SCALE,
-                               ks, vs, partition_tokens=-(-mc // bs) * bs, num_blocks=tabs.num_blocks)
+                               ks, vs, partition_tokens=-(-mc // bs) * bs, num_blocks=tabs.num_blocks,
+                               impl=pkv.IMPL_MFMA)
     b = torch.full_like(q, float("nan"))
     pkv.paged_attention_decode_tokens(b, q, kd, vd, devi(slots), cl, Hkv, bs, tabs.num_blocks, kv,
                                       SCALE, ks, vs)
