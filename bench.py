@@ -75,6 +75,7 @@ def parse():
 
 DECODE_SOURCES = ("decode_core.h", "mfma_math.h", "decode.hip", "pkv_device.h", "cache_write.h")
 PREFILL_SOURCES = ("prefill.hip", "decode_core.h", "mfma_math.h", "pkv_device.h", "cache_write.h")
+VTOKEN_SOURCES = ("decode_tokens.hip", "decode_core.h", "mfma_math.h", "pkv_device.h")
 
 
 def kernel_source_hash(files=DECODE_SOURCES):
@@ -628,6 +629,11 @@ def bench_vtoken(args, torch, pkv, workloads):
             pkv.paged_attention_decode(outs[l], qs[l], kpools[l], vpools[l], bt, cl, mc, Hkv, bs, kv,
                                        scale, ks, vs, num_blocks=nb, stream=stream)
     block_ms = timed(block_step, args.steps) / L
+    if args.copy_probe_mib:
+        copy_probe(torch, dev, args.copy_probe_mib)
+    kv_name = {pkv.BF16: "bf16", pkv.FP16: "fp16", pkv.FP8_E4M3: "fp8"}[kv]
+    traffic = measured_traffic(f"vtoken-{args.config}-{kv_name}-bs{bs}-keep{args.keep:.2f}",
+                               "vtoken_traffic.json", VTOKEN_SOURCES)
     frag_gbs = dec_bytes / (frag_ms * 1e-3) / 1e9
     block_gbs = dec_bytes / (block_ms * 1e-3) / 1e9
     move_gbs = move_bytes / (move_ms * 1e-3) / 1e9
@@ -656,7 +662,7 @@ def bench_vtoken(args, torch, pkv, workloads):
                                       "gbs": round(block_gbs, 1)},
         "roofline": {"bound": "hbm", "kernel": "paged_decode_tokens_kernel",
                      "achieved": round(frag_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(frag_gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                     "frac": round(frag_gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
                      "avg_launch_us": round(frag_ms * 1e3, 2),
                      "algorithmic_bytes_per_launch": dec_bytes},
         "cpu_baseline": cpu,
