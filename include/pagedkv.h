@@ -311,8 +311,12 @@ int32_t paged_attention_plan(const int32_t* context_lens, int32_t num_seqs,
  *   v_scale      : fp8 dequantisation scales (ignored unless kv fp8).
  *   workspace    : >= paged_attention_workspace_bytes(...) bytes of device
  *                  memory.
- * num_heads must be a multiple of num_kv_heads, with G = num_heads /
- * num_kv_heads <= 16.  Errors: PKV_ERR_ARG, PKV_ERR_SIZE (workspace),
+ * num_heads must be a multiple of num_kv_heads; G = num_heads /
+ * num_kv_heads may be anything from 1 (MHA) to num_heads (MQA, one kv head
+ * for all query heads: [P1] §2).  Query heads h = g*G .. g*G + G - 1 read kv
+ * head g.  A group of more than 16 heads runs as ceil(G / 16) work entries
+ * of at most 16 heads each, all reading the same K / V (sharing it in the
+ * XCD's L2 when they run together).  Errors: PKV_ERR_ARG, PKV_ERR_SIZE (workspace),
  * PKV_ERR_UNSUPPORTED (head_dim not 64, 128 or 256 — 128 only with
  * PKV_IMPL_VECTOR —, dtype pair), PKV_ERR_HIP. */
 int32_t paged_attention_decode(void* out, const void* q, int32_t q_dtype,
@@ -437,7 +441,7 @@ int32_t paged_attention_decode_append(void* out, const void* q, int32_t q_dtype,
  * in a key or value a row can see, gives an undefined result in that row
  * (this kernel is built with the compiler's finite-math assumption for its
  * min / max; positions a row cannot see may hold anything).  Errors:
- * PKV_ERR_ARG, PKV_ERR_UNSUPPORTED (head_dim != 128, dtype pair, G > 16),
+ * PKV_ERR_ARG, PKV_ERR_UNSUPPORTED (head_dim != 128, dtype pair),
  * PKV_ERR_HIP. */
 int32_t paged_attention_prefill(void* out, const void* q, int32_t q_dtype,
                                 const void* k_cache, const void* v_cache,

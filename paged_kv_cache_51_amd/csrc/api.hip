@@ -99,13 +99,17 @@ int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
 int64_t plan_bytes_of(int32_t num_seqs, int64_t P) { return align256(4 * (4 + (int64_t)num_seqs * P)); }
 
 // Workspace: [partial outputs][partial max/normaliser][plan]; the partial
-// areas exist only when some sequence can span several partitions.
+// areas exist only when some sequence can span several partitions.  Records
+// are per entry head (pkv::set_heads): group rows of D floats each, and one
+// 32-float line of maxima and normalisers.
 struct WsLayout { int64_t o_bytes, ml_bytes, plan_off, total; };
 WsLayout ws_layout(int32_t S, int32_t H, int32_t Hkv, int32_t D, int64_t P) {
     WsLayout w{};
     if (P > 1) {
-        w.o_bytes = align256((int64_t)S * H * P * D * 4);
-        w.ml_bytes = align256((int64_t)S * Hkv * P * 32 * 4);
+        pkv::DecodeArgs e{};
+        pkv::set_heads(e, H, Hkv);
+        w.o_bytes = align256((int64_t)S * e.num_kv_heads * e.group * P * D * 4);
+        w.ml_bytes = align256((int64_t)S * e.num_kv_heads * P * 32 * 4);
     }
     w.plan_off = w.o_bytes + w.ml_bytes;
     w.total = w.plan_off + plan_bytes_of(S, P);
@@ -285,7 +289,8 @@ int64_t paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_heads, int
                                         int32_t head_dim, int32_t max_context_len,
                                         int32_t block_size, int32_t partition_tokens) {
     if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
-        max_context_len < 0 || partition_tokens < 0 || !valid_block_size(block_size))
+        max_context_len < 0 || partition_tokens < 0 || !valid_block_size(block_size) ||
+        num_heads % num_kv_heads)
         return fail(PKV_ERR_ARG, "bad workspace query");
     const int32_t part = resolve_partition(partition_tokens, num_seqs, num_kv_heads, max_context_len, block_size);
     ok();
@@ -345,10 +350,11 @@ static int32_t decode_impl(void* out, const void* q, int32_t q_dtype, const void
     if (q_dtype != PKV_BF16 && q_dtype != PKV_FP16) return fail(PKV_ERR_ARG, "q_dtype must be bf16 or fp16");
     if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || max_context_len < 0 || max_blocks_per_seq < 0)
         return fail(PKV_ERR_ARG, "bad sizes");
-    if ((int64_t)num_seqs * num_kv_heads > 0x7fffffff || num_seqs > 65535) return fail(PKV_ERR_UNSUPPORTED, "num_seqs must be <= 65535 and num_seqs * num_kv_heads < 2^31 (grid limits)");
     if (num_heads % num_kv_heads) return fail(PKV_ERR_ARG, "num_heads %d is not a multiple of num_kv_heads %d", num_heads, num_kv_heads);
     const int32_t G = num_heads / num_kv_heads;
-    if (G > 16) return fail(PKV_ERR_UNSUPPORTED, "query heads per kv head %d > 16", G);
+    pkv::DecodeArgs a{};
+    pkv::set_heads(a, num_heads, num_kv_heads);   // entry heads: column groups of <= 16 query heads
+    if ((int64_t)num_seqs * a.num_kv_heads > 0x7fffffff || num_seqs > 65535) return fail(PKV_ERR_UNSUPPORTED, "num_seqs must be <= 65535 and num_seqs * num_kv_heads < 2^31 (grid limits)");
     if (!decode_head_dim(head_dim))
         return fail(PKV_ERR_UNSUPPORTED, "decode is built for head_dim 64, 128 and 256, got %d", head_dim);
     if (kv_dtype != PKV_FP8_E4M3 && kv_dtype != q_dtype)
@@ -376,14 +382,13 @@ static int32_t decode_impl(void* out, const void* q, int32_t q_dtype, const void
         return fail(PKV_ERR_ARG, "partition_tokens %d must be a positive multiple of block_size %d", part_tokens, block_size);
     const int64_t num_parts = num_parts_of(ctx_cap, part_tokens);
     if (num_parts > 65535) return fail(PKV_ERR_UNSUPPORTED, "more than 65535 partitions (raise partition_tokens)");
-    if ((int64_t)num_seqs * num_kv_heads * num_parts > 0x7fffffff)
+    if ((int64_t)num_seqs * a.num_kv_heads * num_parts > 0x7fffffff)
         return fail(PKV_ERR_UNSUPPORTED, "too many workgroups (raise partition_tokens)");
     const WsLayout wl = ws_layout(num_seqs, num_heads, num_kv_heads, head_dim, num_parts);
     const int64_t need = o.plan ? wl.plan_off : wl.total;
     if (need > 0 && (!workspace || workspace_bytes < need))
         return fail(PKV_ERR_SIZE, "workspace needs %lld bytes, got %lld", (long long)need, (long long)workspace_bytes);
 
-    pkv::DecodeArgs a{};
     a.out = out;
     a.q = q;
     a.k_cache = (const uint8_t*)k_cache;
@@ -396,9 +401,6 @@ static int32_t decode_impl(void* out, const void* q, int32_t q_dtype, const void
     a.max_blocks = max_blocks_per_seq;
     a.ctx_cap = ctx_cap;
     a.num_seqs = num_seqs;
-    a.num_heads = num_heads;
-    a.num_kv_heads = num_kv_heads;
-    a.group = G;
     a.part_blocks = part_tokens / block_size;
     a.num_parts = (int32_t)num_parts;
     a.num_blocks = o.num_blocks;
@@ -488,8 +490,6 @@ int32_t paged_attention_prefill(void* out, const void* q, int32_t q_dtype, const
         max_blocks_per_seq < 0 || max_query_len < 0 || num_blocks < 0)
         return fail(PKV_ERR_ARG, "bad sizes");
     if (num_heads % num_kv_heads) return fail(PKV_ERR_ARG, "num_heads %d is not a multiple of num_kv_heads %d", num_heads, num_kv_heads);
-    const int32_t G = num_heads / num_kv_heads;
-    if (G > 16) return fail(PKV_ERR_UNSUPPORTED, "query heads per kv head %d > 16", G);
     if (head_dim != kBuiltHeadDim) return fail(PKV_ERR_UNSUPPORTED, "kernels are built for head_dim 128, got %d", head_dim);
     if (kv_dtype != PKV_FP8_E4M3 && kv_dtype != q_dtype)
         return fail(PKV_ERR_UNSUPPORTED, "a 16-bit KV pool must have the query dtype");
@@ -499,11 +499,12 @@ int32_t paged_attention_prefill(void* out, const void* q, int32_t q_dtype, const
     if (num_seqs > 0 && (!out || !q || !k_cache || !v_cache || !context_lens || !query_start_loc ||
                          (max_blocks_per_seq > 0 && !block_tables)))
         return fail(PKV_ERR_ARG, "null pointer");
-    const int32_t tile_tokens = 16 / G;
-    const int64_t max_tiles = ((int64_t)max_query_len + tile_tokens - 1) / tile_tokens;
-    if ((int64_t)num_seqs * max_tiles * num_kv_heads > 0x7fffffff)
-        return fail(PKV_ERR_UNSUPPORTED, "too many workgroups");
     pkv::DecodeArgs a{};
+    pkv::set_heads(a, num_heads, num_kv_heads);   // entry heads: column groups of <= 16 query heads
+    const int32_t tile_tokens = 16 / a.group;
+    const int64_t max_tiles = ((int64_t)max_query_len + tile_tokens - 1) / tile_tokens;
+    if ((int64_t)num_seqs * max_tiles * a.num_kv_heads > 0x7fffffff)
+        return fail(PKV_ERR_UNSUPPORTED, "too many workgroups");
     a.out = out;
     a.q = q;
     a.k_cache = (const uint8_t*)k_cache;
@@ -513,9 +514,6 @@ int32_t paged_attention_prefill(void* out, const void* q, int32_t q_dtype, const
     a.max_blocks = max_blocks_per_seq;
     a.ctx_cap = ctx_cap_of(max_context_len, max_blocks_per_seq, block_size);
     a.num_seqs = num_seqs;
-    a.num_heads = num_heads;
-    a.num_kv_heads = num_kv_heads;
-    a.group = G;
     a.part_blocks = std::max(1, max_blocks_per_seq);   // one partition: the whole context
     a.num_parts = 1;
     a.num_blocks = num_blocks;
@@ -544,28 +542,24 @@ int32_t paged_attention_decode_tokens(void* out, const void* q, int32_t q_dtype,
         return fail(PKV_ERR_ARG, "bad sizes (num_blocks must count the null block and at least one more)");
     if ((int64_t)num_blocks * block_size >= (1LL << 31)) return fail(PKV_ERR_ARG, "slots must fit int32");
     if (num_heads % num_kv_heads) return fail(PKV_ERR_ARG, "num_heads %d is not a multiple of num_kv_heads %d", num_heads, num_kv_heads);
-    const int32_t G = num_heads / num_kv_heads;
-    if (G > 16) return fail(PKV_ERR_UNSUPPORTED, "query heads per kv head %d > 16", G);
     if (head_dim != kBuiltHeadDim) return fail(PKV_ERR_UNSUPPORTED, "kernels are built for head_dim 128, got %d", head_dim);
     if (kv_dtype != PKV_FP8_E4M3 && kv_dtype != q_dtype)
         return fail(PKV_ERR_UNSUPPORTED, "a 16-bit KV pool must have the query dtype");
     if (!std::isfinite(scale)) return fail(PKV_ERR_ARG, "scale must be finite");
     if (kv_dtype == PKV_FP8_E4M3 && !(std::isfinite(k_scale) && std::isfinite(v_scale)))
         return fail(PKV_ERR_ARG, "fp8 scales must be finite");
-    if ((int64_t)num_seqs * num_kv_heads > 0x7fffffff) return fail(PKV_ERR_UNSUPPORTED, "too many workgroups");
+    pkv::DecodeArgs a{};
+    pkv::set_heads(a, num_heads, num_kv_heads);   // entry heads: column groups of <= 16 query heads
+    if ((int64_t)num_seqs * a.num_kv_heads > 0x7fffffff) return fail(PKV_ERR_UNSUPPORTED, "too many workgroups");
     if (num_seqs > 0 && (!out || !q || !k_cache || !v_cache || !context_lens ||
                          (max_tokens_per_seq > 0 && !token_slots)))
         return fail(PKV_ERR_ARG, "null pointer");
-    pkv::DecodeArgs a{};
     a.out = out;
     a.q = q;
     a.k_cache = (const uint8_t*)k_cache;
     a.v_cache = (const uint8_t*)v_cache;
     a.context_lens = context_lens;
     a.num_seqs = num_seqs;
-    a.num_heads = num_heads;
-    a.num_kv_heads = num_kv_heads;
-    a.group = G;
     a.part_blocks = 1;
     a.num_parts = 1;
     a.num_blocks = num_blocks;

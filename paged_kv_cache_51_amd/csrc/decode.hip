@@ -32,12 +32,13 @@
 
 namespace pkv {
 
-// Grid form (see grid_entry).  D = head_dim.
-template <int KVT, int QT, int BS, int NW, int DEPTH, int D = kHeadDim>
+// Grid form (see grid_entry).  D = head_dim; PLAIN: cache-allocating K / V
+// loads (load_unit), for kv heads split over several entry heads.
+template <int KVT, int QT, int BS, int NW, int DEPTH, int D = kHeadDim, bool PLAIN = false>
 __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(PKV_WAVES_PER_EU)))
 void paged_decode_mfma_kernel(const DecodeArgs a) {
     extern __shared__ float pkv_smem[];
-    grid_entry<MfmaMath<KVT, QT, 1, D>, KVT, QT, BS, NW, DEPTH>(a, pkv_smem);
+    grid_entry<MfmaMath<KVT, QT, 1, D>, KVT, QT, BS, NW, DEPTH, PLAIN>(a, pkv_smem);
 }
 
 // Persistent form: as many workgroups as fit on the GPU at once, each
@@ -46,7 +47,7 @@ void paged_decode_mfma_kernel(const DecodeArgs a) {
 // simply take more entries.  The counters live in the plan header
 // (zeroed by the planner); the last workgroup to leave resets them, so
 // the plan can serve the next launch on the same stream.
-template <int KVT, int QT, int BS, int NW, int DEPTH, int D = kHeadDim>
+template <int KVT, int QT, int BS, int NW, int DEPTH, int D = kHeadDim, bool PLAIN = false>
 __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(PKV_WAVES_PER_EU)))
 void paged_decode_mfma_persistent(const DecodeArgs a) {
     extern __shared__ float pkv_smem[];
@@ -65,8 +66,8 @@ void paged_decode_mfma_persistent(const DecodeArgs a) {
         const int kvh = k - item * a.num_kv_heads;
         const uint32_t packed = (uint32_t)a.plan[kPlanHeader + item];
         const int s = (int)(packed >> 16);
-        decode_entry<MfmaMath<KVT, QT, 1, D>, KVT, QT, BS, NW, DEPTH>(a, pkv_smem, s, (int)(packed & 0xffffu),
-                                                                       kvh, lane, w, QueryTile{s, 1, 1});
+        decode_entry<MfmaMath<KVT, QT, 1, D>, KVT, QT, BS, NW, DEPTH, PLAIN>(a, pkv_smem, s, (int)(packed & 0xffffu),
+                                                                              kvh, lane, w, QueryTile{s, 1, 1});
     }
     if (threadIdx.x == 0) {
         __threadfence();
@@ -91,7 +92,9 @@ __global__ __launch_bounds__(kWave) void decode_reduce_kernel(const DecodeArgs a
     const int nblk = (ctx + BS - 1) / BS;
     const int np = (nblk + a.part_blocks - 1) / a.part_blocks;
     if (np <= 1) return;
-    const int G = a.group, kvh = hq / G, h = hq - kvh * G;
+    // query head hq -> its entry head kvh and column h in that entry
+    const int G = a.group, ph = hq / a.group_all, r = hq - ph * a.group_all;
+    const int cg = r / G, h = r - cg * G, kvh = ph * a.kv_split + cg;
     const int64_t base = ((int64_t)s * a.num_kv_heads + kvh) * a.num_parts;
     float M = -INFINITY;
     for (int p = lane; p < np; p += kWave) M = fmaxf(M, a.ws_ml[(base + p) * 32 + h]);
@@ -139,13 +142,13 @@ __global__ __launch_bounds__(kWave) void decode_reduce_kernel(const DecodeArgs a
 // stays within 64 KiB of LDS and head_dim <= 128; fp8 pools: four waves with
 // one unit in flight (72B fp8 334.8 -> 329.6 us; eight waves were 0.6 %
 // slower there).
-template <int KVT, int QT, int BS, int D, int NW, int DEPTH>
-static hipError_t launch_mfma_nw(const DecodeArgs& a, bool persistent, hipStream_t st) {
+template <int KVT, int QT, int BS, int D, int NW, int DEPTH, bool PLAIN>
+static hipError_t launch_mfma_nw_t(const DecodeArgs& a, bool persistent, hipStream_t st) {
     const size_t lds = sizeof(float) * merge_lds_floats(NW, a.group, 16, D);
     const dim3 block(NW * kWave);
     if (!persistent) {
         const dim3 grid((unsigned)grid_workgroups(a));
-        hipLaunchKernelGGL((paged_decode_mfma_kernel<KVT, QT, BS, NW, DEPTH, D>), grid, block, lds, st, a);
+        hipLaunchKernelGGL((paged_decode_mfma_kernel<KVT, QT, BS, NW, DEPTH, D, PLAIN>), grid, block, lds, st, a);
         return hipGetLastError();
     }
     // as many workgroups as can be resident at once (never more than entries)
@@ -153,7 +156,7 @@ static hipError_t launch_mfma_nw(const DecodeArgs& a, bool persistent, hipStream
     int& occ = per_cu[a.group];
     if (!occ) {
         hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &occ, reinterpret_cast<const void*>(&paged_decode_mfma_persistent<KVT, QT, BS, NW, DEPTH, D>),
+            &occ, reinterpret_cast<const void*>(&paged_decode_mfma_persistent<KVT, QT, BS, NW, DEPTH, D, PLAIN>),
             block.x, lds);
         if (e != hipSuccess || occ <= 0) occ = 1;
     }
@@ -163,8 +166,16 @@ static hipError_t launch_mfma_nw(const DecodeArgs& a, bool persistent, hipStream
         cus = 256;
     const int64_t entries = (int64_t)a.num_seqs * a.num_kv_heads * a.num_parts;
     const dim3 grid((unsigned)std::min<int64_t>(entries, (int64_t)occ * cus));
-    hipLaunchKernelGGL((paged_decode_mfma_persistent<KVT, QT, BS, NW, DEPTH, D>), grid, block, lds, st, a);
+    hipLaunchKernelGGL((paged_decode_mfma_persistent<KVT, QT, BS, NW, DEPTH, D, PLAIN>), grid, block, lds, st, a);
     return hipGetLastError();
+}
+
+// Cache-allocating K / V loads when a kv head is read by several entry
+// heads (more than 16 query heads per kv head), non-temporal ones otherwise.
+template <int KVT, int QT, int BS, int D, int NW, int DEPTH>
+static hipError_t launch_mfma_nw(const DecodeArgs& a, bool persistent, hipStream_t st) {
+    return a.kv_split > 1 ? launch_mfma_nw_t<KVT, QT, BS, D, NW, DEPTH, true>(a, persistent, st)
+                          : launch_mfma_nw_t<KVT, QT, BS, D, NW, DEPTH, false>(a, persistent, st);
 }
 
 // four_waves: the four-wave form whatever the workload (PKV_IMPL_MFMA), the

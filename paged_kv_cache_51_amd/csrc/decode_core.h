@@ -8,6 +8,23 @@
 
 namespace pkv {
 
+// Entry head kvh of DecodeArgs (a pool kv head, or one column group of a
+// pool kv head with more than 16 query heads): its pool kv head, its first
+// query head and its number of query heads.  "LLM inference basics and
+// vLLM internals" §2: query heads share a kv head in contiguous groups
+// (GQA), all of them in MQA.
+__device__ __forceinline__ int pool_head(const DecodeArgs& a, int kvh) {
+    return a.kv_split == 1 ? kvh : kvh / a.kv_split;
+}
+__device__ __forceinline__ int first_head(const DecodeArgs& a, int kvh) {
+    const int p = pool_head(a, kvh);
+    return p * a.group_all + (kvh - p * a.kv_split) * a.group;
+}
+__device__ __forceinline__ int heads_of(const DecodeArgs& a, int kvh) {
+    const int p = pool_head(a, kvh);
+    return min(a.group, a.group_all - (kvh - p * a.kv_split) * a.group);
+}
+
 // One 16-token unit of one kv head in registers: R pool rows of K and of V
 // (D = head_dim).
 template <int KVT, int D = kHeadDim>
@@ -17,19 +34,30 @@ struct UnitRegs {
     u32x4_t v[R];
 };
 
-template <int KVT, int D>
+// PLAIN = false: non-temporal loads ("nt"): every K / V byte is read once
+// per launch, so it should not displace anything from the caches.  Measured
+// on the 7B shape: 424 -> 380 us per layer (the cache-allocating stream tops
+// out near 6.3 TB/s).  PLAIN = true: cache-allocating loads, for kv heads
+// read by several entry heads (groups of more than 16 query heads), which
+// then find each other's K / V in L2: one kv head, 256 sequences of
+// 1K-8K tokens, 32 query heads 172 -> 142 us, 64 query heads 279 -> 200 us
+// (16 query heads, one entry: 119 us with nt loads, 135 without).
+template <int KVT, int D, bool PLAIN = false>
 __device__ __forceinline__ void load_unit(UnitRegs<KVT, D>& u, const uint8_t* kbase,
                                           const uint8_t* vbase, int lane) {
     const u32x4_t* kp = reinterpret_cast<const u32x4_t*>(kbase) + lane;
     const u32x4_t* vp = reinterpret_cast<const u32x4_t*>(vbase) + lane;
-    // Non-temporal loads ("nt"): every K / V byte is read once per launch,
-    // so it should not displace anything from the caches.  Measured on the
-    // 7B shape: 424 -> 380 us per layer (the cache-allocating stream tops
-    // out near 6.3 TB/s).
+    if constexpr (PLAIN) {
 #pragma unroll
-    for (int r = 0; r < UnitRegs<KVT, D>::R; ++r) u.k[r] = __builtin_nontemporal_load(kp + kWave * r);
+        for (int r = 0; r < UnitRegs<KVT, D>::R; ++r) u.k[r] = kp[kWave * r];
 #pragma unroll
-    for (int r = 0; r < UnitRegs<KVT, D>::R; ++r) u.v[r] = __builtin_nontemporal_load(vp + kWave * r);
+        for (int r = 0; r < UnitRegs<KVT, D>::R; ++r) u.v[r] = vp[kWave * r];
+    } else {
+#pragma unroll
+        for (int r = 0; r < UnitRegs<KVT, D>::R; ++r) u.k[r] = __builtin_nontemporal_load(kp + kWave * r);
+#pragma unroll
+        for (int r = 0; r < UnitRegs<KVT, D>::R; ++r) u.v[r] = __builtin_nontemporal_load(vp + kWave * r);
+    }
 }
 
 // K fragment kk (dims 8*((lane>>4) + 4kk) .. +7 of token lane&15).
@@ -128,6 +156,7 @@ __device__ __forceinline__ void park_and_store(const DecodeArgs& a, float* pkv_s
                                                int part, int kvh, int lane, int w,
                                                const QueryTile& qt, int ncols, bool single) {
     const int G = a.group;
+    const int hq0 = first_head(a, kvh), nh = heads_of(a, kvh);
     constexpr int KC = Math::kCols;
     constexpr int D = Math::kD;
     constexpr int MR = merge_row(D);
@@ -158,7 +187,8 @@ __device__ __forceinline__ void park_and_store(const DecodeArgs& a, float* pkv_s
         // L = 0 only for a token placed before the start of the context
         const float invL = L > 0.f ? 1.0f / L : 0.f;
         const int h = c % G;
-        const int hq = kvh * G + h;
+        if (h >= nh) continue;                    // padding column of a split group
+        const int hq = hq0 + h;
         // lane owns dims e, e + 1 for e = 2 lane + 128 i
 #pragma unroll
         for (int e = 2 * lane; e < D; e += 2 * kWave) {
@@ -206,8 +236,9 @@ __device__ __forceinline__ void park_and_store(const DecodeArgs& a, float* pkv_s
 // before the LDS counter barrier depends only on (s, part, qt), so all
 // waves of the workgroup take it together.  With NW = 1 the calling wave
 // works alone (its own entry and its own LDS area, no workgroup barrier),
-// so the waves of one workgroup can run different entries.
-template <class Math, int KVT, int QT, int BS, int NW, int DEPTH>
+// so the waves of one workgroup can run different entries.  PLAIN: K / V
+// with cache-allocating loads (load_unit).
+template <class Math, int KVT, int QT, int BS, int NW, int DEPTH, bool PLAIN = false>
 __device__ __forceinline__ void decode_entry(const DecodeArgs& a, float* pkv_smem, int s, int part,
                                              int kvh, int lane, int w, const QueryTile& qt) {
     constexpr int NSUB = BS / kSubTokens;
@@ -238,10 +269,11 @@ __device__ __forceinline__ void decode_entry(const DecodeArgs& a, float* pkv_sme
     // below adds no memory round trip of its own.  Every partition's wave 0
     // fetches (512 bytes); only the one holding position c - 1 writes.
     const bool append = a.new_key != nullptr && qt.ntok == 1 && w == 0;
+    const int ph = pool_head(a, kvh);
     TokenRow<D> new_row;
     int32_t new_pb = -1;
     if (append) {
-        const int64_t row = ((int64_t)s * a.num_kv_heads + kvh) * D;
+        const int64_t row = ((int64_t)s * a.pool_kv_heads + ph) * D;
         new_row.load(reinterpret_cast<const uint16_t*>(a.new_key) + row,
                      reinterpret_cast<const uint16_t*>(a.new_value) + row, lane);
         // only when the context is not clamped (the table and
@@ -254,10 +286,12 @@ __device__ __forceinline__ void decode_entry(const DecodeArgs& a, float* pkv_sme
         if (part == 0) {
             // no key at all: zero output (empty context, or tokens placed
             // before the start of the context)
+            const int hq0 = first_head(a, kvh), nh = heads_of(a, kvh);
             for (int e = (NW == 1 ? lane : (int)threadIdx.x); e < ncols * D; e += NW * kWave) {
                 const int c = e / D;
+                if (c % G >= nh) continue;
                 uint16_t* out = reinterpret_cast<uint16_t*>(a.out) +
-                                ((qt.row0 + c / G) * a.num_heads + (int64_t)kvh * G + c % G) * D;
+                                ((qt.row0 + c / G) * a.num_heads + hq0 + c % G) * D;
                 out[e % D] = 0;
             }
         }
@@ -277,11 +311,13 @@ __device__ __forceinline__ void decode_entry(const DecodeArgs& a, float* pkv_sme
         // ctx - 1, the new token, so it writes the token's K / V into its
         // slot (as reshape_and_cache would) before any wave loads that unit;
         // the barrier below orders the stores before those loads (waves of
-        // one workgroup share the CU's write-through L1).
+        // one workgroup share the CU's write-through L1).  Every entry head
+        // of a split pool head writes the same bytes, so each one reads its
+        // own store.
         new_row.template store<QT, KVT, BS>(const_cast<uint8_t*>(a.k_cache),
                                             const_cast<uint8_t*>(a.v_cache),
-                                            (int64_t)new_pb * BS + (ctx - 1) % BS, a.num_kv_heads,
-                                            kvh, lane, a.k_inv, a.v_inv);
+                                            (int64_t)new_pb * BS + (ctx - 1) % BS, a.pool_kv_heads,
+                                            ph, lane, a.k_inv, a.v_inv);
         if constexpr (NW == 1) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     }
     mt.stage_q(pkv_smem + merge_lds_floats(NW, ncols, Math::kCols, D), ltid);
@@ -297,9 +333,9 @@ __device__ __forceinline__ void decode_entry(const DecodeArgs& a, float* pkv_sme
 
     const int n_my = first < u1 ? (u1 - first + NW - 1) / NW : 0;
     if (n_my > 0) {
-        const uint8_t* kpool = a.k_cache + (int64_t)kvh * TILE;
-        const uint8_t* vpool = a.v_cache + (int64_t)kvh * TILE;
-        const int64_t head_stride = (int64_t)a.num_kv_heads * TILE;
+        const uint8_t* kpool = a.k_cache + (int64_t)ph * TILE;
+        const uint8_t* vpool = a.v_cache + (int64_t)ph * TILE;
+        const int64_t head_stride = (int64_t)a.pool_kv_heads * TILE;
         auto load_ids = [&](int i0) -> int {
             const int i = i0 + lane;
             return i < n_my ? bt_row[(first + NW * i) / NSUB] : 0;
@@ -327,7 +363,7 @@ __device__ __forceinline__ void decode_entry(const DecodeArgs& a, float* pkv_sme
 #pragma unroll
             for (int d = 0; d < DEPTH; ++d) {
                 const int64_t off = unit_offset(ids, c0, min(d, nc - 1));
-                load_unit<KVT>(buf[d], kpool + off, vpool + off, lane);
+                load_unit<KVT, D, PLAIN>(buf[d], kpool + off, vpool + off, lane);
             }
             auto tok_of = [&](int j) { return (first + NW * (c0 + j)) * kSubTokens; };
             int i = 0;
@@ -336,7 +372,7 @@ __device__ __forceinline__ void decode_entry(const DecodeArgs& a, float* pkv_sme
                 for (int d = 0; d < DEPTH; ++d) {
                     mt.unit(buf[d], tok_of(i + d), ctx, a.qk_scale_log2, lane);
                     const int64_t off = unit_offset(ids, c0, i + d + DEPTH);
-                    load_unit<KVT>(buf[d], kpool + off, vpool + off, lane);
+                    load_unit<KVT, D, PLAIN>(buf[d], kpool + off, vpool + off, lane);
                 }
             }
             // drain: units i .. nc-1 (at most 2*DEPTH-1 of them)
@@ -347,7 +383,7 @@ __device__ __forceinline__ void decode_entry(const DecodeArgs& a, float* pkv_sme
                     mt.unit(buf[d], tok_of(i + d), ctx, a.qk_scale_log2, lane);
                     if (d < refills) {
                         const int64_t off = unit_offset(ids, c0, i + d + DEPTH);
-                        load_unit<KVT>(buf[d], kpool + off, vpool + off, lane);
+                        load_unit<KVT, D, PLAIN>(buf[d], kpool + off, vpool + off, lane);
                     }
                 }
             }
@@ -378,7 +414,7 @@ __host__ __device__ inline int64_t grid_workgroups(const DecodeArgs& a) {
 // The plan lists items longest first, so the dispatcher's greedy in-order
 // placement runs long work first.  Dynamic LDS: [counters 4][m NW*16]
 // [l NW*16][acc NW*G rows of kMergeRow floats][policy's query area].
-template <class Math, int KVT, int QT, int BS, int NW, int DEPTH>
+template <class Math, int KVT, int QT, int BS, int NW, int DEPTH, bool PLAIN = false>
 __device__ __forceinline__ void grid_entry(const DecodeArgs& a, float* pkv_smem) {
     const int lane = threadIdx.x & (kWave - 1);
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -393,8 +429,8 @@ __device__ __forceinline__ void grid_entry(const DecodeArgs& a, float* pkv_smem)
     const uint32_t packed = (uint32_t)a.plan[kPlanHeader + min(item, a.num_seqs * a.num_parts - 1)];
     if (item >= n_items) return;
     const int s = (int)(packed >> 16);
-    decode_entry<Math, KVT, QT, BS, NW, DEPTH>(a, pkv_smem, s, (int)(packed & 0xffffu), kvh, lane, w,
-                                                QueryTile{s, 1, 1});
+    decode_entry<Math, KVT, QT, BS, NW, DEPTH, PLAIN>(a, pkv_smem, s, (int)(packed & 0xffffu), kvh, lane, w,
+                                                       QueryTile{s, 1, 1});
 }
 
 }  // namespace pkv

@@ -129,8 +129,8 @@ void paged_decode_tokens_kernel(const DecodeArgs a, const int32_t* __restrict__ 
     int ctx = a.context_lens[s];
     ctx = ctx < max_tokens ? ctx : max_tokens;
     if (ctx <= 0) {
-        uint16_t* out = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)s * a.num_heads + (int64_t)kvh * G) * kHeadDim;
-        for (int e = threadIdx.x; e < G * kHeadDim; e += NW * kWave) out[e] = 0;
+        uint16_t* out = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)s * a.num_heads + first_head(a, kvh)) * kHeadDim;
+        for (int e = threadIdx.x; e < heads_of(a, kvh) * kHeadDim; e += NW * kWave) out[e] = 0;
         return;
     }
     mt.limit(ctx - 1, G, lane);
@@ -141,9 +141,9 @@ void paged_decode_tokens_kernel(const DecodeArgs a, const int32_t* __restrict__ 
     mt.begin();
 
     constexpr int64_t TILE = (int64_t)sub_tile_bytes(KVT) * (BS / kSubTokens);
-    const uint8_t* kpool = a.k_cache + (int64_t)kvh * TILE;
-    const uint8_t* vpool = a.v_cache + (int64_t)kvh * TILE;
-    const int64_t head_stride = (int64_t)a.num_kv_heads * TILE;
+    const uint8_t* kpool = a.k_cache + (int64_t)pool_head(a, kvh) * TILE;
+    const uint8_t* vpool = a.v_cache + (int64_t)pool_head(a, kvh) * TILE;
+    const int64_t head_stride = (int64_t)a.pool_kv_heads * TILE;
     const int32_t* row = token_slots + (int64_t)s * max_tokens;
     const int32_t slot_cap = a.num_blocks * BS;   // slots in [BS, slot_cap) are real
     const int n_my = w < n_units ? (n_units - w + NW - 1) / NW : 0;

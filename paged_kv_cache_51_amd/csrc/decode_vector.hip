@@ -34,7 +34,7 @@ struct VectorMath {
         G = a.group;
         const int tid = threadIdx.x;
         const u32x4_t* src = reinterpret_cast<const u32x4_t*>(a.q) +
-                             (qt.row0 * a.num_heads + (int64_t)kvh * G) * (kHeadDim / 8);
+                             (qt.row0 * a.num_heads + (int64_t)first_head(a, kvh)) * (kHeadDim / 8);
         const u32x4_t z = {0u, 0u, 0u, 0u};
         qreg = tid < G * (kHeadDim / 8) ? src[tid] : z;
     }

@@ -33,15 +33,18 @@ struct MfmaMath {
     __device__ __forceinline__ void load_q(const DecodeArgs& a, const QueryTile& qt, int kvh,
                                            int lane) {
         const int G = a.group;
+        const int hq0 = first_head(a, kvh), nh = heads_of(a, kvh);
         col = lane & 15;
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             const int c = 16 * t + col;
-            cvalid[t] = c < qt.ntok * G;
+            // column c = (token c / G, head c % G); heads past nh pad the
+            // last column group of a split kv head
+            cvalid[t] = c < qt.ntok * G && c % G < nh;
             const int j = cvalid[t] ? c / G : 0;
             const int h = cvalid[t] ? c - j * G : 0;
             const uint8_t* qrow = reinterpret_cast<const uint8_t*>(a.q) +
-                                  ((qt.row0 + j) * a.num_heads + (int64_t)kvh * G + h) * (D * 2);
+                                  ((qt.row0 + j) * a.num_heads + hq0 + h) * (D * 2);
 #pragma unroll
             for (int kk = 0; kk < KD; ++kk) {
                 const u32x4_t z = {0u, 0u, 0u, 0u};

@@ -32,15 +32,23 @@ struct DecodeArgs {
     const uint8_t* v_cache;
     const int32_t* block_tables;
     const int32_t* context_lens;
-    float* ws_out;         // [S][H][P][128] partial outputs (normalised)
-    float* ws_ml;          // [S][H_kv][P][32] (max in log2 units, normaliser per head)
+    float* ws_out;         // [S][num_kv_heads][P][group][head_dim] partial outputs (normalised)
+    float* ws_ml;          // [S][num_kv_heads][P][32] (max in log2 units, normaliser per column)
     const int32_t* plan;   // work plan (plan.hip): count, then (seq << 16 | part)
     int32_t max_blocks;    // block-table row length
     int32_t ctx_cap;       // context clamp: min(max_context_len, max_blocks*bs)
     int32_t num_seqs;
     int32_t num_heads;
-    int32_t num_kv_heads;
-    int32_t group;         // num_heads / num_kv_heads
+    // Entry heads.  A pool kv head whose query heads fit one 16-column MFMA
+    // tile is one entry head (kv_split = 1, group = its query heads).  A
+    // larger group (MQA, or GQA above 16 query heads per kv head) is split
+    // into kv_split entry heads of `group` columns each, the last one
+    // possibly fewer; all of them read the same K / V.  Set by set_heads().
+    int32_t num_kv_heads;  // entry heads: pool_kv_heads * kv_split
+    int32_t group;         // query-head columns per entry head (<= 16)
+    int32_t kv_split;      // entry heads per pool kv head
+    int32_t group_all;     // query heads per pool kv head (num_heads / pool_kv_heads)
+    int32_t pool_kv_heads; // kv heads of the pool
     int32_t part_blocks;   // blocks per partition
     int32_t num_parts;     // partitions launched per (seq, kv head)
     int32_t num_blocks;    // pool size for id clamping (0 = unchecked)
@@ -57,6 +65,19 @@ struct DecodeArgs {
     float k_inv;           // 1 / k_scale for fp8 pools, else 1
     float v_inv;
 };
+
+// Entry heads of a (num_heads, num_kv_heads) layout: the fewest entry heads
+// per kv head whose columns fit one 16-column tile, columns spread evenly.
+inline void set_heads(DecodeArgs& a, int32_t num_heads, int32_t num_kv_heads) {
+    const int32_t g_all = num_heads / num_kv_heads;
+    const int32_t split = (g_all + 15) / 16;
+    a.num_heads = num_heads;
+    a.pool_kv_heads = num_kv_heads;
+    a.group_all = g_all;
+    a.kv_split = split;
+    a.group = (g_all + split - 1) / split;
+    a.num_kv_heads = num_kv_heads * split;
+}
 
 // Error reporting shared by the extern "C" entry points (api.hip): set the
 // thread-local message and return the code.

@@ -354,16 +354,18 @@ __device__ __forceinline__ void load_q_cols(Math& mt, const DecodeArgs& a, int64
                                             int kvh, int lane) {
     constexpr int NT = Math::kCols / 16;
     const int G = a.group;
+    const int hq0 = first_head(a, kvh), nh = heads_of(a, kvh);
     mt.col = lane & 15;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
         const int c = 16 * t + mt.col;
-        mt.cvalid[t] = c < ncols;
+        // heads past nh pad the last column group of a split kv head
+        mt.cvalid[t] = c < ncols && (c + h0) % G < nh;
         const int cl = mt.cvalid[t] ? c + h0 : 0;
         const int j = cl / G;
         const int h = cl - j * G;
         const uint8_t* qrow = reinterpret_cast<const uint8_t*>(a.q) +
-                              ((row0 + j) * a.num_heads + (int64_t)kvh * G + h) * (kHeadDim * 2);
+                              ((row0 + j) * a.num_heads + hq0 + h) * (kHeadDim * 2);
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
             const u32x4_t z = {0u, 0u, 0u, 0u};
@@ -507,8 +509,8 @@ void paged_prefill_staged_kernel(const DecodeArgs a, const int32_t* __restrict__
         const int n_pairs = (n_units + 1) / 2;
         const int32_t* bt_row = a.block_tables + (int64_t)s * a.max_blocks;
         // wave w fetches K (w < 2) or V (w >= 2) rows of unit A (w even) or B
-        const uint8_t* pool = ((w >> 1) ? a.v_cache : a.k_cache) + (int64_t)kvh * TILE;
-        const int64_t head_stride = (int64_t)a.num_kv_heads * TILE;
+        const uint8_t* pool = ((w >> 1) ? a.v_cache : a.k_cache) + (int64_t)pool_head(a, kvh) * TILE;
+        const int64_t head_stride = (int64_t)a.pool_kv_heads * TILE;
         // unit fetched by this wave for pair p (indices past the last pair
         // repeat it; a missing second unit repeats the last unit)
         auto unit_of = [&](int p) { return min(2 * min(p, n_pairs - 1) + (w & 1), n_units - 1); };
@@ -653,7 +655,7 @@ void paged_prefill_staged_kernel(const DecodeArgs a, const int32_t* __restrict__
         const float sc = (L > 0.f ? 1.0f / L : 0.f) * a.out_scale;
         const int cl = 16 * t + (lane & 15) + h0;
         uint16_t* out = reinterpret_cast<uint16_t*>(a.out) +
-                        ((row0 + cl / G) * a.num_heads + (int64_t)kvh * G + cl % G) * kHeadDim + 4 * g;
+                        ((row0 + cl / G) * a.num_heads + first_head(a, kvh) + cl % G) * kHeadDim + 4 * g;
 #pragma unroll
         for (int nt = 0; nt < 8; ++nt) {
             const f32x4_t o = mt.acc[t][nt];

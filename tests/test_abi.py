@@ -97,7 +97,7 @@ def _decode(**kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(H=9), -1),                 # heads not a multiple of kv heads
-    (dict(H=34, Hkv=2), -4),         # G = 17 > 16
+    (dict(H=34, Hkv=2), -2),         # G = 17: two entry heads; only the plan's space is missing
     (dict(D=192), -4),               # decode is built for head_dim 64, 128, 256
     (dict(D=64, impl=2), -4),        # vector kernel: head_dim 128 only
     (dict(D=100), -1),               # not a multiple of 64

@@ -183,3 +183,20 @@ def test_nan_poison_never_reaches_output():
     out = oracle.paged_decode(q, oracle.BF16, kp, vp, oracle.BF16, tabs.block_tables,
                               tabs.context_lens, 2, 16, 0.088)
     assert np.isfinite(out).all()
+
+
+@pytest.mark.parametrize("H,Hkv", [(32, 1), (71, 1), (40, 2)])
+def test_mqa_and_wide_groups_match_brute_force(H, Hkv):
+    """MQA (one kv head for every query head) and groups above 16 query
+    heads per kv head ("LLM inference basics and vLLM internals" §2): the
+    oracle's head map h -> h / G against the brute force's head expansion."""
+    lengths = [1, 17, 64, 130]
+    tabs, kb, vb, q, kp, vp = _setup(lengths, H, Hkv, 16, oracle.BF16, oracle.BF16, seed=H)
+    scale = float(np.float32(1 / np.sqrt(D)))
+    got = oracle.paged_decode(q, oracle.BF16, kp, vp, oracle.BF16, tabs.block_tables,
+                              tabs.context_lens, Hkv, 16, scale)
+    for s in range(len(lengths)):
+        want = brute.attention(oracle.decode_values(q[s], oracle.BF16),
+                               oracle.decode_values(kb[s], oracle.BF16),
+                               oracle.decode_values(vb[s], oracle.BF16), scale)
+        np.testing.assert_allclose(got[s], want, rtol=0, atol=1e-12)

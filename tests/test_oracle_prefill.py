@@ -102,3 +102,21 @@ def test_later_keys_do_not_change_earlier_tokens():
     # chunk tokens sit at positions 28..39: those before 34 are unchanged
     assert np.array_equal(a[:6], b[:6])
     assert not np.array_equal(a[6:], b[6:])
+
+
+@pytest.mark.parametrize("H,Hkv", [(32, 1), (40, 2)])
+def test_mqa_and_wide_groups_match_causal_brute_force(H, Hkv):
+    """Multi-token attention with one kv head for all query heads (MQA) or
+    more than 16 query heads per kv head ("LLM inference basics and vLLM
+    internals" §2)."""
+    lengths = [5, 40, 100]
+    q_lens = [5, 9, 33]
+    tabs, kb, vb, _, kp, vp = _setup(lengths, H, Hkv, 16, oracle.BF16, oracle.BF16, seed=H + 1)
+    qs, q = _chunks(q_lens, H, oracle.BF16, 6)
+    got = oracle.paged_prefill(q, oracle.BF16, kp, vp, oracle.BF16, tabs.block_tables,
+                               tabs.context_lens, qs, Hkv, 16, SCALE)
+    for s in range(len(lengths)):
+        qd = oracle.decode_values(q[qs[s]:qs[s + 1]], oracle.BF16)
+        want = brute.causal_chunk(qd, oracle.decode_values(kb[s], oracle.BF16),
+                                  oracle.decode_values(vb[s], oracle.BF16), SCALE)
+        np.testing.assert_allclose(got[qs[s]:qs[s + 1]], want, rtol=0, atol=1e-12)

@@ -137,3 +137,25 @@ def test_model_refuses_eviction_on_shared_blocks():
     m.fork(1, 2)
     with pytest.raises(ValueError):
         m.evict_tokens(1, [True] * 40)
+
+
+@pytest.mark.parametrize("H,Hkv", [(32, 1), (40, 2)])
+def test_survivors_match_contiguous_attention_wide_groups(H, Hkv):
+    """The token-table oracle with MQA / more than 16 query heads per kv
+    head ("LLM inference basics and vLLM internals" §2)."""
+    lengths = [40, 90]
+    tabs, kb, vb, q, kp, vp = _setup(lengths, H, Hkv, 16, oracle.BF16, oracle.BF16, seed=4)
+    r = np.random.default_rng(5)
+    full = table_to_slots(tabs.block_tables, lengths, 16, 128)
+    keep = [np.sort(r.choice(c, size=c // 2, replace=False)) for c in lengths]
+    slots = np.zeros((2, 128), np.int32)
+    for s in range(2):
+        slots[s, :len(keep[s])] = full[s, keep[s]]
+    ctx = np.array([len(k) for k in keep], np.int32)
+    got = oracle.paged_decode_tokens(q, oracle.BF16, kp, vp, oracle.BF16, slots, ctx, Hkv, 16,
+                                     SCALE)
+    for s in range(2):
+        kk = oracle.decode_values(kb[s][keep[s]], oracle.BF16)
+        vv = oracle.decode_values(vb[s][keep[s]], oracle.BF16)
+        want = brute.attention(oracle.decode_values(q[s], oracle.BF16), kk, vv, SCALE)
+        np.testing.assert_allclose(got[s], want, rtol=0, atol=1e-12)
