@@ -213,8 +213,9 @@ int32_t reshape_and_cache(const void* key, const void* value,
 enum {
     PKV_IMPL_AUTO = 0,    /* matrix-core kernel, waves per workgroup chosen
                              per workload: eight for 16-bit pools with
-                             head_dim <= 128 and partitions of >= 2048
-                             tokens, else four */
+                             head_dim <= 128, at most 16 query heads per
+                             kv head and partitions of >= 2048 tokens,
+                             else four */
     PKV_IMPL_MFMA = 1,    /* GQA group on 16x16 MFMA tiles, one workgroup
                              of four waves per (item, kv head) of the plan,
                              the heads of an item on one XCD: the form whose
@@ -314,9 +315,10 @@ int32_t paged_attention_plan(const int32_t* context_lens, int32_t num_seqs,
  * num_heads must be a multiple of num_kv_heads; G = num_heads /
  * num_kv_heads may be anything from 1 (MHA) to num_heads (MQA, one kv head
  * for all query heads: [P1] §2).  Query heads h = g*G .. g*G + G - 1 read kv
- * head g.  A group of more than 16 heads runs as ceil(G / 16) work entries
- * of at most 16 heads each, all reading the same K / V (sharing it in the
- * XCD's L2 when they run together).  Errors: PKV_ERR_ARG, PKV_ERR_SIZE (workspace),
+ * head g.  A work entry holds up to 32 query heads of one kv head (two
+ * 16-column MFMA tiles; 16 at head_dim 256); a larger group runs as several
+ * entries, all reading the same K / V (sharing it in the XCD's L2 when they
+ * run together).  Errors: PKV_ERR_ARG, PKV_ERR_SIZE (workspace),
  * PKV_ERR_UNSUPPORTED (head_dim not 64, 128 or 256 — 128 only with
  * PKV_IMPL_VECTOR —, dtype pair), PKV_ERR_HIP. */
 int32_t paged_attention_decode(void* out, const void* q, int32_t q_dtype,

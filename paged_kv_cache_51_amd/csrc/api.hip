@@ -107,9 +107,9 @@ WsLayout ws_layout(int32_t S, int32_t H, int32_t Hkv, int32_t D, int64_t P) {
     WsLayout w{};
     if (P > 1) {
         pkv::DecodeArgs e{};
-        pkv::set_heads(e, H, Hkv);
+        pkv::set_heads(e, H, Hkv, pkv::decode_max_cols(D));
         w.o_bytes = align256((int64_t)S * e.num_kv_heads * e.group * P * D * 4);
-        w.ml_bytes = align256((int64_t)S * e.num_kv_heads * P * 32 * 4);
+        w.ml_bytes = align256((int64_t)S * e.num_kv_heads * P * pkv::ml_line(e.group) * 4);
     }
     w.plan_off = w.o_bytes + w.ml_bytes;
     w.total = w.plan_off + plan_bytes_of(S, P);
@@ -353,7 +353,8 @@ static int32_t decode_impl(void* out, const void* q, int32_t q_dtype, const void
     if (num_heads % num_kv_heads) return fail(PKV_ERR_ARG, "num_heads %d is not a multiple of num_kv_heads %d", num_heads, num_kv_heads);
     const int32_t G = num_heads / num_kv_heads;
     pkv::DecodeArgs a{};
-    pkv::set_heads(a, num_heads, num_kv_heads);   // entry heads: column groups of <= 16 query heads
+    // entry heads: column groups of <= 32 query heads (<= 16 at head_dim 256)
+    pkv::set_heads(a, num_heads, num_kv_heads, pkv::decode_max_cols(head_dim));
     if ((int64_t)num_seqs * a.num_kv_heads > 0x7fffffff || num_seqs > 65535) return fail(PKV_ERR_UNSUPPORTED, "num_seqs must be <= 65535 and num_seqs * num_kv_heads < 2^31 (grid limits)");
     if (!decode_head_dim(head_dim))
         return fail(PKV_ERR_UNSUPPORTED, "decode is built for head_dim 64, 128 and 256, got %d", head_dim);

@@ -33,12 +33,13 @@
 namespace pkv {
 
 // Grid form (see grid_entry).  D = head_dim; PLAIN: cache-allocating K / V
-// loads (load_unit), for kv heads split over several entry heads.
-template <int KVT, int QT, int BS, int NW, int DEPTH, int D = kHeadDim, bool PLAIN = false>
+// loads (load_unit), for kv heads split over several entry heads; NT: 16-
+// column MFMA tiles per entry (2 for entries of 17-32 query heads).
+template <int KVT, int QT, int BS, int NW, int DEPTH, int D = kHeadDim, bool PLAIN = false, int NT = 1>
 __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(PKV_WAVES_PER_EU)))
 void paged_decode_mfma_kernel(const DecodeArgs a) {
     extern __shared__ float pkv_smem[];
-    grid_entry<MfmaMath<KVT, QT, 1, D>, KVT, QT, BS, NW, DEPTH, PLAIN>(a, pkv_smem);
+    grid_entry<MfmaMath<KVT, QT, NT, D>, KVT, QT, BS, NW, DEPTH, PLAIN>(a, pkv_smem);
 }
 
 // Persistent form: as many workgroups as fit on the GPU at once, each
@@ -47,7 +48,7 @@ void paged_decode_mfma_kernel(const DecodeArgs a) {
 // simply take more entries.  The counters live in the plan header
 // (zeroed by the planner); the last workgroup to leave resets them, so
 // the plan can serve the next launch on the same stream.
-template <int KVT, int QT, int BS, int NW, int DEPTH, int D = kHeadDim, bool PLAIN = false>
+template <int KVT, int QT, int BS, int NW, int DEPTH, int D = kHeadDim, bool PLAIN = false, int NT = 1>
 __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(PKV_WAVES_PER_EU)))
 void paged_decode_mfma_persistent(const DecodeArgs a) {
     extern __shared__ float pkv_smem[];
@@ -66,8 +67,8 @@ void paged_decode_mfma_persistent(const DecodeArgs a) {
         const int kvh = k - item * a.num_kv_heads;
         const uint32_t packed = (uint32_t)a.plan[kPlanHeader + item];
         const int s = (int)(packed >> 16);
-        decode_entry<MfmaMath<KVT, QT, 1, D>, KVT, QT, BS, NW, DEPTH, PLAIN>(a, pkv_smem, s, (int)(packed & 0xffffu),
-                                                                              kvh, lane, w, QueryTile{s, 1, 1});
+        decode_entry<MfmaMath<KVT, QT, NT, D>, KVT, QT, BS, NW, DEPTH, PLAIN>(a, pkv_smem, s, (int)(packed & 0xffffu),
+                                                                               kvh, lane, w, QueryTile{s, 1, 1});
     }
     if (threadIdx.x == 0) {
         __threadfence();
@@ -96,8 +97,9 @@ __global__ __launch_bounds__(kWave) void decode_reduce_kernel(const DecodeArgs a
     const int G = a.group, ph = hq / a.group_all, r = hq - ph * a.group_all;
     const int cg = r / G, h = r - cg * G, kvh = ph * a.kv_split + cg;
     const int64_t base = ((int64_t)s * a.num_kv_heads + kvh) * a.num_parts;
+    const int ML = ml_line(G);
     float M = -INFINITY;
-    for (int p = lane; p < np; p += kWave) M = fmaxf(M, a.ws_ml[(base + p) * 32 + h]);
+    for (int p = lane; p < np; p += kWave) M = fmaxf(M, a.ws_ml[(base + p) * ML + h]);
 #pragma unroll
     for (int d = 1; d < kWave; d <<= 1) M = fmaxf(M, xor_shfl(M, d));
     constexpr int NE = (D + 2 * kWave - 1) / (2 * kWave);   // dim pairs per lane
@@ -105,8 +107,8 @@ __global__ __launch_bounds__(kWave) void decode_reduce_kernel(const DecodeArgs a
 #pragma unroll
     for (int i = 0; i < NE; ++i) o0[i] = o1[i] = 0.f;
     for (int p = 0; p < np; ++p) {
-        const float mp = a.ws_ml[(base + p) * 32 + h];
-        const float lp = a.ws_ml[(base + p) * 32 + 16 + h];
+        const float mp = a.ws_ml[(base + p) * ML + h];
+        const float lp = a.ws_ml[(base + p) * ML + ML / 2 + h];
         const float fct = fast_exp2(mp - M) * lp;
         L += fct;
 #pragma unroll
@@ -142,21 +144,21 @@ __global__ __launch_bounds__(kWave) void decode_reduce_kernel(const DecodeArgs a
 // stays within 64 KiB of LDS and head_dim <= 128; fp8 pools: four waves with
 // one unit in flight (72B fp8 334.8 -> 329.6 us; eight waves were 0.6 %
 // slower there).
-template <int KVT, int QT, int BS, int D, int NW, int DEPTH, bool PLAIN>
+template <int KVT, int QT, int BS, int D, int NW, int DEPTH, bool PLAIN, int NT = 1>
 static hipError_t launch_mfma_nw_t(const DecodeArgs& a, bool persistent, hipStream_t st) {
-    const size_t lds = sizeof(float) * merge_lds_floats(NW, a.group, 16, D);
+    const size_t lds = sizeof(float) * merge_lds_floats(NW, a.group, 16 * NT, D);
     const dim3 block(NW * kWave);
     if (!persistent) {
         const dim3 grid((unsigned)grid_workgroups(a));
-        hipLaunchKernelGGL((paged_decode_mfma_kernel<KVT, QT, BS, NW, DEPTH, D, PLAIN>), grid, block, lds, st, a);
+        hipLaunchKernelGGL((paged_decode_mfma_kernel<KVT, QT, BS, NW, DEPTH, D, PLAIN, NT>), grid, block, lds, st, a);
         return hipGetLastError();
     }
     // as many workgroups as can be resident at once (never more than entries)
-    static int per_cu[17] = {};               // cache by group size (LDS use)
+    static int per_cu[16 * NT + 1] = {};      // cache by group size (LDS use)
     int& occ = per_cu[a.group];
     if (!occ) {
         hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &occ, reinterpret_cast<const void*>(&paged_decode_mfma_persistent<KVT, QT, BS, NW, DEPTH, D, PLAIN>),
+            &occ, reinterpret_cast<const void*>(&paged_decode_mfma_persistent<KVT, QT, BS, NW, DEPTH, D, PLAIN, NT>),
             block.x, lds);
         if (e != hipSuccess || occ <= 0) occ = 1;
     }
@@ -166,7 +168,7 @@ static hipError_t launch_mfma_nw_t(const DecodeArgs& a, bool persistent, hipStre
         cus = 256;
     const int64_t entries = (int64_t)a.num_seqs * a.num_kv_heads * a.num_parts;
     const dim3 grid((unsigned)std::min<int64_t>(entries, (int64_t)occ * cus));
-    hipLaunchKernelGGL((paged_decode_mfma_persistent<KVT, QT, BS, NW, DEPTH, D, PLAIN>), grid, block, lds, st, a);
+    hipLaunchKernelGGL((paged_decode_mfma_persistent<KVT, QT, BS, NW, DEPTH, D, PLAIN, NT>), grid, block, lds, st, a);
     return hipGetLastError();
 }
 
@@ -184,7 +186,20 @@ static hipError_t launch_mfma_nw(const DecodeArgs& a, bool persistent, hipStream
 template <int KVT, int QT, int BS, int D>
 static hipError_t launch_mfma(const DecodeArgs& a, bool persistent, bool four_waves, hipStream_t st) {
     constexpr int NW8 = 2 * kWavesPerGroup;
-    if (four_waves) return launch_mfma_nw<KVT, QT, BS, D, kWavesPerGroup, (KVT == DT_FP8 ? 1 : kDepth)>(a, persistent, st);
+    constexpr int DP = KVT == DT_FP8 ? 1 : kDepth;
+    if constexpr (D <= 128) {
+        // Entries of 17-32 query heads (MQA, wide GQA groups): two MFMA
+        // tiles per wave over one read of the K / V, four waves, one unit in
+        // flight (217 VGPRs, two waves per SIMD; with two units in flight
+        // 265, one wave per SIMD).  One kv head, 256 sequences of 1K-8K
+        // tokens, against 16-column entries sharing the K / V in L2:
+        // 24 heads 172 -> 131 us, 32 heads 142 -> 143 us, 48 heads 171 ->
+        // 162 us, 64 heads 199 -> 179 us, 96 heads 254 -> 224 us.
+        if (a.group > 16)
+            return a.kv_split > 1 ? launch_mfma_nw_t<KVT, QT, BS, D, kWavesPerGroup, 1, true, 2>(a, persistent, st)
+                                  : launch_mfma_nw_t<KVT, QT, BS, D, kWavesPerGroup, 1, false, 2>(a, persistent, st);
+    }
+    if (four_waves) return launch_mfma_nw<KVT, QT, BS, D, kWavesPerGroup, DP>(a, persistent, st);
     if constexpr (KVT == DT_FP8) {
         return launch_mfma_nw<KVT, QT, BS, D, kWavesPerGroup, 1>(a, persistent, st);
     } else if constexpr (D <= 128) {

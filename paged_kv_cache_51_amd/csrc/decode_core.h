@@ -212,10 +212,12 @@ __device__ __forceinline__ void park_and_store(const DecodeArgs& a, float* pkv_s
             }
         }
     }
-    if (!single && lane < 32) {
-        // one full 128-byte line per record: maxima of the G heads at [0, 16),
-        // normalisers at [16, 32)
-        const int h = lane & 15;
+    const int ML = ml_line(G);                // (the launch gives KC >= ML / 2)
+    if (!single && lane < ML) {
+        // one line per record: maxima of the columns at [0, ML / 2),
+        // normalisers at [ML / 2, ML) (entries of <= 16 columns: one
+        // 128-byte line)
+        const int h = lane % (ML / 2);
         float M = -INFINITY, L = 0.f;
         if (h < G) {
 #pragma unroll
@@ -227,7 +229,7 @@ __device__ __forceinline__ void park_and_store(const DecodeArgs& a, float* pkv_s
             }
         }
         const int64_t rec = ((int64_t)s * a.num_kv_heads + kvh) * a.num_parts + part;
-        a.ws_ml[rec * 32 + lane] = (h < G) ? (lane < 16 ? M : L) : 0.f;
+        a.ws_ml[rec * ML + lane] = (h < G) ? (lane < ML / 2 ? M : L) : 0.f;
     }
 }
 

@@ -33,19 +33,21 @@ struct DecodeArgs {
     const int32_t* block_tables;
     const int32_t* context_lens;
     float* ws_out;         // [S][num_kv_heads][P][group][head_dim] partial outputs (normalised)
-    float* ws_ml;          // [S][num_kv_heads][P][32] (max in log2 units, normaliser per column)
+    float* ws_ml;          // [S][num_kv_heads][P][ml_line(group)] (max in log2 units, normaliser per column)
     const int32_t* plan;   // work plan (plan.hip): count, then (seq << 16 | part)
     int32_t max_blocks;    // block-table row length
     int32_t ctx_cap;       // context clamp: min(max_context_len, max_blocks*bs)
     int32_t num_seqs;
     int32_t num_heads;
-    // Entry heads.  A pool kv head whose query heads fit one 16-column MFMA
-    // tile is one entry head (kv_split = 1, group = its query heads).  A
-    // larger group (MQA, or GQA above 16 query heads per kv head) is split
-    // into kv_split entry heads of `group` columns each, the last one
-    // possibly fewer; all of them read the same K / V.  Set by set_heads().
+    // Entry heads.  A pool kv head whose query heads fit the columns one
+    // work entry holds (16: one MFMA tile; the decode partition kernel takes
+    // 32, two tiles, at head_dim <= 128) is one entry head (kv_split = 1,
+    // group = its query heads).  A larger group (MQA, or GQA with many query
+    // heads per kv head) is split into kv_split entry heads of `group`
+    // columns each, the last one possibly fewer; all of them read the same
+    // K / V.  Set by set_heads().
     int32_t num_kv_heads;  // entry heads: pool_kv_heads * kv_split
-    int32_t group;         // query-head columns per entry head (<= 16)
+    int32_t group;         // query-head columns per entry head (<= 16, or <= 32 in decode)
     int32_t kv_split;      // entry heads per pool kv head
     int32_t group_all;     // query heads per pool kv head (num_heads / pool_kv_heads)
     int32_t pool_kv_heads; // kv heads of the pool
@@ -67,10 +69,10 @@ struct DecodeArgs {
 };
 
 // Entry heads of a (num_heads, num_kv_heads) layout: the fewest entry heads
-// per kv head whose columns fit one 16-column tile, columns spread evenly.
-inline void set_heads(DecodeArgs& a, int32_t num_heads, int32_t num_kv_heads) {
+// per kv head whose columns fit max_cols, columns spread evenly.
+inline void set_heads(DecodeArgs& a, int32_t num_heads, int32_t num_kv_heads, int32_t max_cols = 16) {
     const int32_t g_all = num_heads / num_kv_heads;
-    const int32_t split = (g_all + 15) / 16;
+    const int32_t split = (g_all + max_cols - 1) / max_cols;
     a.num_heads = num_heads;
     a.pool_kv_heads = num_kv_heads;
     a.group_all = g_all;
@@ -78,6 +80,14 @@ inline void set_heads(DecodeArgs& a, int32_t num_heads, int32_t num_kv_heads) {
     a.group = (g_all + split - 1) / split;
     a.num_kv_heads = num_kv_heads * split;
 }
+
+// Columns of a decode work entry at head_dim d: two 16-column MFMA tiles up
+// to d = 128, one at 256 (the accumulators of two would not fit).
+inline int32_t decode_max_cols(int32_t head_dim) { return head_dim <= 128 ? 32 : 16; }
+
+// Floats of one partition record's line of maxima and normalisers: 16 + 16
+// for entries of at most 16 columns, 32 + 32 above.
+__host__ __device__ inline int ml_line(int group) { return group > 16 ? 64 : 32; }
 
 // Error reporting shared by the extern "C" entry points (api.hip): set the
 // thread-local message and return the code.

@@ -2,14 +2,14 @@
 basics and vLLM internals" §2: in MQA every query head shares the one K / V
 head; GQA groups them).
 
-A kv head whose group does not fit one 16-column MFMA tile runs as several
-entry heads of at most 16 query heads each, all reading the same K / V (the
-last one may hold fewer heads).  Checked here: decode (grid and persistent,
+A kv head whose group does not fit the columns of one work entry (decode:
+two 16-column MFMA tiles at head_dim <= 128, one at 256; the multi-token and
+token-table kernels: one) runs as several entry heads, all reading the same
+K / V (the last one may hold fewer heads).  Checked here: decode (grid and persistent,
 split and unsplit contexts, bf16 / fp8, head_dim 64 / 128 / 256), the decode
 with the new token's K / V written inside it, the token-table decode and the
-multi-token kernels against the oracle; and, bit for bit, that MQA with 32
-query heads equals GQA with 2 kv heads holding the same K / V (the same
-16-column entries over the same values).
+multi-token kernels against the oracle; and, bit for bit, that MQA equals
+GQA with replicated K / V where both run the same entries.
 """
 import numpy as np
 import pytest
@@ -100,10 +100,13 @@ def test_decode_wide_groups_match_oracle(H, Hkv, d, kv):
 @pytest.mark.parametrize("kv", [oracle.BF16, oracle.FP8])
 @pytest.mark.parametrize("part", [0, 64])
 def test_mqa_equals_gqa_with_replicated_kv_bitwise(kv, part):
-    """32 query heads over one kv head run as two entry heads of 16; GQA
-    with 2 kv heads holding the same values runs the same two 16-column
-    entries: outputs equal bit for bit (decode, token-table decode and
-    multi-token attention)."""
+    """Entries over the same K / V values compute the same bits wherever the
+    values sit.  Decode takes up to 32 query heads per entry at head_dim
+    128: MQA with 32 query heads (one 32-column entry) equals each half of
+    GQA with 64 query heads over 2 kv heads holding the same K / V (two
+    such entries).  The token-table and multi-token kernels take 16 per
+    entry: MQA with 32 query heads (two entries) equals GQA with 2 kv
+    heads and 32 query heads (two entries)."""
     log(f"MQA vs replicated GQA kv={kv} part={part}")
     src, H, d, bs = oracle.BF16, 32, 128, 16
     ks = float(np.float32(4.0 / 448.0)) if kv == oracle.FP8 else 1.0
@@ -117,9 +120,15 @@ def test_mqa_equals_gqa_with_replicated_kv_bitwise(kv, part):
                                         tabs.num_blocks, kv, src, ks, ks)
         kd, vd, bt, cl = dev8(kp), dev8(vp), devi(tabs.block_tables), devi(tabs.context_lens)
         q = dev16(qb, src)
-        a = torch.full_like(q, float("nan"))
-        pkv.paged_attention_decode(a, q, kd, vd, bt, cl, max(lengths), Hkv, bs, kv, 0.09, ks, ks,
+        # decode: the 32 heads once (MQA), or twice over the two kv heads
+        qq = q if Hkv == 1 else torch.cat([q, q], dim=1).contiguous()
+        a = torch.full_like(qq, float("nan"))
+        pkv.paged_attention_decode(a, qq, kd, vd, bt, cl, max(lengths), Hkv, bs, kv, 0.09, ks, ks,
                                    partition_tokens=part or 2048, num_blocks=tabs.num_blocks)
+        if Hkv == 2:
+            torch.cuda.synchronize()
+            assert torch.equal(a[:, :H].view(torch.int16), a[:, H:].view(torch.int16))
+            a = a[:, :H].contiguous()
         slots = np.zeros((len(lengths), max(lengths)), np.int32)
         for s, c in enumerate(lengths):
             slots[s, :c] = [tabs.block_tables[s][t // bs] * bs + t % bs for t in range(c)]
