@@ -100,8 +100,8 @@ int64_t plan_bytes_of(int32_t num_seqs, int64_t P) { return align256(4 * (4 + (i
 
 // Workspace: [partial outputs][partial max/normaliser][plan]; the partial
 // areas exist only when some sequence can span several partitions.  Records
-// are per entry head (pkv::set_heads): group rows of D floats each, and one
-// 32-float line of maxima and normalisers.
+// are per entry head (pkv::set_heads): group rows of D floats each, and a
+// line of ml_line(group) floats of maxima and normalisers.
 struct WsLayout { int64_t o_bytes, ml_bytes, plan_off, total; };
 WsLayout ws_layout(int32_t S, int32_t H, int32_t Hkv, int32_t D, int64_t P) {
     WsLayout w{};

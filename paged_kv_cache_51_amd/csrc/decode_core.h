@@ -9,8 +9,8 @@
 namespace pkv {
 
 // Entry head kvh of DecodeArgs (a pool kv head, or one column group of a
-// pool kv head with more than 16 query heads): its pool kv head, its first
-// query head and its number of query heads.  "LLM inference basics and
+// pool kv head with more query heads than one work entry holds): its pool
+// kv head, its first query head and its number of query heads.  "LLM inference basics and
 // vLLM internals" §2: query heads share a kv head in contiguous groups
 // (GQA), all of them in MQA.
 __device__ __forceinline__ int pool_head(const DecodeArgs& a, int kvh) {
@@ -38,10 +38,10 @@ struct UnitRegs {
 // per launch, so it should not displace anything from the caches.  Measured
 // on the 7B shape: 424 -> 380 us per layer (the cache-allocating stream tops
 // out near 6.3 TB/s).  PLAIN = true: cache-allocating loads, for kv heads
-// read by several entry heads (groups of more than 16 query heads), which
-// then find each other's K / V in L2: one kv head, 256 sequences of
-// 1K-8K tokens, 32 query heads 172 -> 142 us, 64 query heads 279 -> 200 us
-// (16 query heads, one entry: 119 us with nt loads, 135 without).
+// read by several entry heads, which then find each other's K / V in L2.
+// Measured with 16-column entries (one kv head, 256 sequences of 1K-8K
+// tokens): 32 query heads 172 -> 142 us, 64 query heads 279 -> 200 us (16
+// query heads, one entry: 119 us with nt loads, 135 without).
 template <int KVT, int D, bool PLAIN = false>
 __device__ __forceinline__ void load_unit(UnitRegs<KVT, D>& u, const uint8_t* kbase,
                                           const uint8_t* vbase, int lane) {
