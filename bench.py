@@ -49,6 +49,10 @@ def parse():
                          "writes them, paged_attention_decode_append)")
     ap.add_argument("--head-dim", type=int, default=0, choices=[0, 64, 128, 256],
                     help="decode: override the configuration's head_dim (0 = as configured)")
+    ap.add_argument("--heads", type=int, default=0,
+                    help="decode: override the query heads (0 = as configured)")
+    ap.add_argument("--kv-heads", type=int, default=0,
+                    help="decode: override the kv heads (0 = as configured; 1 = MQA)")
     ap.add_argument("--impl", default="auto", choices=["auto", "mfma", "vector", "persistent"])
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0,
@@ -142,6 +146,14 @@ def main():
         import dataclasses
         cfg = dataclasses.replace(cfg, head_dim=args.head_dim, description=cfg.description.replace(
             f"d={cfg.head_dim}", f"d={args.head_dim}"))
+    if args.heads or args.kv_heads:
+        import dataclasses
+        h = args.heads or cfg.num_heads
+        hkv = args.kv_heads or cfg.num_kv_heads
+        if h % hkv:
+            raise SystemExit("--heads must be a multiple of --kv-heads")
+        cfg = dataclasses.replace(cfg, num_heads=h, num_kv_heads=hkv, description=cfg.description.replace(
+            f"{cfg.num_heads} q / {cfg.num_kv_heads} kv heads", f"{h} q / {hkv} kv heads"))
     kv_dtype = dt_names[args.kv_dtype] if args.kv_dtype else cfg.kv_dtype
     q_dtype = cfg.q_dtype
     if kv_dtype in (pkv.BF16, pkv.FP16) and kv_dtype != q_dtype:
@@ -286,7 +298,9 @@ def main():
     launch_bytes = kv_bytes + qo_bytes + (0 if separate else new_bytes)
     achieved = launch_bytes / (dec_avg_ms * 1e-3) / 1e9
     traffic_key = (f"{args.config}-{kv_dtype}-bs{bs}-part{part_resolved}-impl{impl}"
-                   + (f"-d{D}" if D != 128 else "") + ("-separate" if separate else "-append"))
+                   + (f"-d{D}" if D != 128 else "")
+                   + (f"-h{H}-kv{Hkv}" if args.heads or args.kv_heads else "")
+                   + ("-separate" if separate else "-append"))
     traffic = measured_traffic(traffic_key)
     unique_gbs = (unique_kv_bytes + qo_bytes) / (dec_avg_ms * 1e-3) / 1e9
     print(f"[bench] step {step_ms:.3f} ms, {gbs:.0f} GB/s; partition kernel "
