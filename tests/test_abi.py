@@ -210,3 +210,22 @@ def test_head_dims_outside_the_built_set_are_unsupported():
         rc = lib.paged_attention_prefill(None, None, pkv.BF16, None, None, None, 0, None, None, 0, 0, 0,
                                          8, 2, d, 0.1, 16, 0, pkv.BF16, 1.0, 1.0, None)
         assert rc == -4 and "128" in pkv.last_error()
+
+
+@pytest.mark.parametrize("H,Hkv,D,entries,cols", [   # entries per kv head
+    (32, 1, 128, 1, 32),     # MQA, 32 query heads: one two-tile entry
+    (71, 1, 64, 3, 24),      # 71 heads: three entries of 24 columns (the last has 23 real)
+    (64, 2, 128, 1, 32),     # G = 32 per kv head
+    (128, 1, 128, 4, 32),
+    (40, 2, 256, 2, 10),     # head_dim 256: entries of at most 16 columns
+    (17, 1, 256, 2, 9),
+])
+def test_workspace_bytes_wide_groups(H, Hkv, D, entries, cols):
+    """Groups above one entry's columns (MQA, wide GQA): partial records per
+    entry head, `cols` rows each, and a line of 32 floats (entries of <= 16
+    columns) or 64 (wider) of maxima and normalisers."""
+    S, P = 3, 13
+    line = 64 if cols > 16 else 32
+    want = (_a256(S * Hkv * entries * cols * P * D * 4) + _a256(S * Hkv * entries * P * line * 4)
+            + _a256(4 * (4 + S * P)))
+    assert pkv.workspace_bytes(S, H, Hkv, D, 200, 16, 16) == want
