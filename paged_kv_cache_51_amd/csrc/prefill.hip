@@ -78,7 +78,9 @@ __host__ __device__ constexpr int small_chunk_depth() {
     return (NT == 2 && KVT != DT_FP8) ? 1 : kDepth;
 }
 
-template <int KVT, int QT, int BS, int NW, int DEPTH, int NT>
+// PLAIN: cache-allocating K / V loads, for kv heads split over several
+// entry heads (they share the K / V in L2; load_unit in decode_core.h).
+template <int KVT, int QT, int BS, int NW, int DEPTH, int NT, bool PLAIN = false>
 __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(small_chunk_waves_per_eu<KVT, NT>())))
 void paged_prefill_mfma_kernel(const DecodeArgs a, const int32_t* __restrict__ query_start,
                                int tile_tokens, int max_tiles) {
@@ -98,7 +100,7 @@ void paged_prefill_mfma_kernel(const DecodeArgs a, const int32_t* __restrict__ q
     const int q_len = query_start[s + 1] - q0;
     const int j0 = tile * tile_tokens;
     if (j0 >= q_len) return;
-    decode_entry<MfmaMath<KVT, QT, NT>, KVT, QT, BS, NW, DEPTH>(
+    decode_entry<MfmaMath<KVT, QT, NT>, KVT, QT, BS, NW, DEPTH, PLAIN>(
         a, pkv_smem, s, 0, kvh, lane, w,
         QueryTile{(int64_t)q0 + j0, min(tile_tokens, q_len - j0), q_len - j0});
 }
@@ -688,15 +690,23 @@ static hipError_t launch_prefill_t(const DecodeArgs& a, const int32_t* query_sta
         const size_t lds = std::max(sizeof(float) * merge_lds_floats(kWavesPerGroup, tt * a.group, 32),
                                     sizeof(int) * (kRankSeqsMax + 1));
         const dim3 grid((unsigned)((int64_t)a.num_seqs * tiles2 * a.num_kv_heads));
-        hipLaunchKernelGGL((paged_prefill_mfma_kernel<KVT, QT, BS, kWavesPerGroup, small_chunk_depth<KVT, 2>(), 2>), grid,
-                           dim3(kWavesPerGroup * kWave), lds, st, a, query_start, tt, tiles2);
+        if (a.kv_split > 1)
+            hipLaunchKernelGGL((paged_prefill_mfma_kernel<KVT, QT, BS, kWavesPerGroup, small_chunk_depth<KVT, 2>(), 2, true>),
+                               grid, dim3(kWavesPerGroup * kWave), lds, st, a, query_start, tt, tiles2);
+        else
+            hipLaunchKernelGGL((paged_prefill_mfma_kernel<KVT, QT, BS, kWavesPerGroup, small_chunk_depth<KVT, 2>(), 2>),
+                               grid, dim3(kWavesPerGroup * kWave), lds, st, a, query_start, tt, tiles2);
         return hipGetLastError();
     }
     const size_t lds = std::max(sizeof(float) * merge_lds_floats(kWavesPerGroup, tile_tokens * a.group),
                                 sizeof(int) * (kRankSeqsMax + 1));
     const dim3 grid((unsigned)((int64_t)a.num_seqs * max_tiles * a.num_kv_heads));
-    hipLaunchKernelGGL((paged_prefill_mfma_kernel<KVT, QT, BS, kWavesPerGroup, kDepth, 1>), grid,
-                       dim3(kWavesPerGroup * kWave), lds, st, a, query_start, tile_tokens, max_tiles);
+    if (a.kv_split > 1)
+        hipLaunchKernelGGL((paged_prefill_mfma_kernel<KVT, QT, BS, kWavesPerGroup, kDepth, 1, true>), grid,
+                           dim3(kWavesPerGroup * kWave), lds, st, a, query_start, tile_tokens, max_tiles);
+    else
+        hipLaunchKernelGGL((paged_prefill_mfma_kernel<KVT, QT, BS, kWavesPerGroup, kDepth, 1>), grid,
+                           dim3(kWavesPerGroup * kWave), lds, st, a, query_start, tile_tokens, max_tiles);
     return hipGetLastError();
 }
 
