@@ -1,0 +1,25 @@
+"""GPU: the usage example in README.md runs as written (pool, block
+manager, prefill, one decode step with the fused cache write), and its
+decode output is finite."""
+import os
+import re
+
+import pytest
+import torch
+
+pytest.importorskip("paged_kv_cache_51_amd")
+
+pytestmark = pytest.mark.gpu
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_readme_usage_example_runs():
+    text = open(os.path.join(ROOT, "README.md")).read()
+    blocks = re.findall(r"```python\n(.*?)```", text, re.S)
+    assert len(blocks) == 1, "README.md should hold one python example"
+    scope = {}
+    exec(compile(blocks[0], "README.md example", "exec"), scope)
+    torch.cuda.synchronize()
+    out = scope["out"]
+    assert out.shape == (2, 28, 128) and torch.isfinite(out.float()).all()
