@@ -7,7 +7,8 @@
     oracle;
   - one sequence of 262,144 tokens beside a one-token one: the default split
     cuts it into 512 partitions, so the reduce merges that many records per
-    head (bf16 and fp8 pools).
+    head (bf16 and fp8 pools);
+  - a fresh 16,384-token prompt as one multi-token chunk (sampled rows).
 """
 import numpy as np
 import pytest
@@ -98,5 +99,44 @@ def test_decode_262144_token_sequence(kv):
                                kpool.cpu().numpy(), vpool.cpu().numpy(), kv, tabs.block_tables,
                                lengths, Hkv, bs, scale, ks, ks)
     err = float(np.abs(got - want).max())
+    log(f"  max-abs {err:.3e}")
+    assert err <= TOL[kv]
+
+
+@pytest.mark.parametrize("kv", [oracle.BF16, oracle.FP8])
+def test_fresh_prefill_of_16384_tokens(kv):
+    """A whole 16,384-token prompt as one chunk (every token new, causal
+    from position 0) beside a 3-token one: sampled rows against the oracle
+    as one-token chunks at their positions."""
+    H, Hkv, D, bs = 28, 4, 128, 16
+    lengths = np.array([16384, 3], np.int32)
+    q_lens = lengths.copy()
+    r = np.random.default_rng(9)
+    tabs = workloads.build_tables(lengths, bs, r)
+    ks = float(np.float32(8.0 / 448.0)) if kv == oracle.FP8 else 1.0
+    kpool, vpool = filled_pools(tabs.num_blocks, Hkv, D, bs, kv, 51, ks)
+    T = int(q_lens.sum())
+    g = torch.Generator(device=DEV)
+    g.manual_seed(13)
+    q = torch.randn(T, H, D, generator=g, device=DEV).to(torch.bfloat16)
+    qs = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+    out = torch.full_like(q, float("nan"))
+    scale = float(np.float32(1.0 / np.sqrt(D)))
+    pkv.paged_attention_prefill(out, q, kpool, vpool, torch.from_numpy(tabs.block_tables).to(DEV),
+                                torch.from_numpy(lengths).to(DEV), torch.from_numpy(qs).to(DEV),
+                                int(q_lens.max()), int(lengths.max()), Hkv, bs, kv, scale, ks, ks,
+                                num_blocks=tabs.num_blocks)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy().astype(np.float64)
+    assert np.isfinite(got).all()
+    rows = [(0, j) for j in (0, 1, 15, 16, 4097, 8191, 12000, 16382, 16383)] + [(1, 0), (1, 2)]
+    log(f"kv={kv}: rows {rows}")
+    qb = q.cpu().view(torch.int16).numpy().view(np.uint16)
+    sub_q = qb[[qs[s] + j for s, j in rows]]
+    sub_ctx = np.array([j + 1 for _, j in rows], np.int32)       # a fresh prompt: token j at position j
+    sub_bt = np.ascontiguousarray(tabs.block_tables[[s for s, _ in rows]])
+    want = oracle.paged_prefill(sub_q, oracle.BF16, kpool.cpu().numpy(), vpool.cpu().numpy(), kv, sub_bt,
+                                sub_ctx, np.arange(len(rows) + 1, dtype=np.int32), Hkv, bs, scale, ks, ks)
+    err = float(np.abs(got[[qs[s] + j for s, j in rows]] - want).max())
     log(f"  max-abs {err:.3e}")
     assert err <= TOL[kv]
