@@ -83,7 +83,12 @@ void paged_decode_mfma_persistent(const DecodeArgs a) {
 // max m_p (log2 units), normaliser l_p and normalised output o_p,
 //   out = sum_p 2^(m_p - M) l_p o_p / sum_p 2^(m_p - M) l_p,  M = max_p m_p.
 // One wave per (query head, sequence); lane owns dims e, e + 1 for
-// e = 2 lane + 128 i (D = head_dim).
+// e = 2 lane + 128 i (D = head_dim).  Partitions are summed in order p = 0,
+// 1, ... in chunks of kReduceChunk whose records are loaded together; the
+// first chunk's loads are issued with the pass that forms M (they do not
+// depend on it), so a launch of at most kReduceChunk partitions per sequence
+// waits for one memory round trip after the context length.
+constexpr int kReduceChunk = 8;
 template <int QT, int BS, int D = kHeadDim>
 __global__ __launch_bounds__(kWave) void decode_reduce_kernel(const DecodeArgs a) {
     const int hq = blockIdx.x, s = blockIdx.y, lane = threadIdx.x;
@@ -98,26 +103,44 @@ __global__ __launch_bounds__(kWave) void decode_reduce_kernel(const DecodeArgs a
     const int cg = r / G, h = r - cg * G, kvh = ph * a.kv_split + cg;
     const int64_t base = ((int64_t)s * a.num_kv_heads + kvh) * a.num_parts;
     const int ML = ml_line(G);
+    constexpr int NE = (D + 2 * kWave - 1) / (2 * kWave);   // dim pairs per lane
+    // one chunk of records: maxima, normalisers and this lane's output dims
+    // (indices clamped to the last partition; entries past it are not summed)
+    float cm[kReduceChunk], cl[kReduceChunk];
+    float2 co[kReduceChunk][NE];
+    auto load_chunk = [&](int p0) {
+#pragma unroll
+        for (int j = 0; j < kReduceChunk; ++j) {
+            const int64_t rec = base + min(p0 + j, np - 1);
+            cm[j] = a.ws_ml[rec * ML + h];
+            cl[j] = a.ws_ml[rec * ML + ML / 2 + h];
+#pragma unroll
+            for (int i = 0; i < NE; ++i) {
+                const int e = min(2 * lane + 2 * kWave * i, D - 2);
+                co[j][i] = *reinterpret_cast<const float2*>(a.ws_out + (rec * G + h) * D + e);
+            }
+        }
+    };
+    load_chunk(0);
     float M = -INFINITY;
     for (int p = lane; p < np; p += kWave) M = fmaxf(M, a.ws_ml[(base + p) * ML + h]);
 #pragma unroll
     for (int d = 1; d < kWave; d <<= 1) M = fmaxf(M, xor_shfl(M, d));
-    constexpr int NE = (D + 2 * kWave - 1) / (2 * kWave);   // dim pairs per lane
     float L = 0.f, o0[NE], o1[NE];
 #pragma unroll
     for (int i = 0; i < NE; ++i) o0[i] = o1[i] = 0.f;
-    for (int p = 0; p < np; ++p) {
-        const float mp = a.ws_ml[(base + p) * ML + h];
-        const float lp = a.ws_ml[(base + p) * ML + ML / 2 + h];
-        const float fct = fast_exp2(mp - M) * lp;
-        L += fct;
+    for (int p0 = 0; p0 < np; p0 += kReduceChunk) {
+        if (p0 > 0) load_chunk(p0);
 #pragma unroll
-        for (int i = 0; i < NE; ++i) {
-            const int e = 2 * lane + 2 * kWave * i;
-            if (e < D) {
-                const float2 op = *reinterpret_cast<const float2*>(a.ws_out + ((base + p) * G + h) * D + e);
-                o0[i] += fct * op.x;
-                o1[i] += fct * op.y;
+        for (int j = 0; j < kReduceChunk; ++j) {
+            if (p0 + j < np) {
+                const float fct = fast_exp2(cm[j] - M) * cl[j];
+                L += fct;
+#pragma unroll
+                for (int i = 0; i < NE; ++i) {
+                    o0[i] += fct * co[j][i].x;
+                    o1[i] += fct * co[j][i].y;
+                }
             }
         }
     }

@@ -28,11 +28,16 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
                                                            int32_t num_seqs, int32_t ctx_cap,
                                                            int32_t block_size, int32_t part_blocks,
                                                            int32_t* __restrict__ plan) {
+    constexpr int kWaves = kPlanThreads / kWave;
     __shared__ int hist[kMaxBucket + 1];
-    __shared__ int scan_tmp[kPlanThreads];
+    __shared__ int wave_total[kWaves];
     const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1), wid = tid / kWave;
     const int part_units = part_blocks * (block_size / kSubTokens);
     const int nbucket = min(part_units, kMaxBucket) + 1;
+    // The length of this thread's first sequence, read once for both passes
+    // below (every sequence, when there are at most kPlanThreads of them).
+    const int c_first = tid < num_seqs ? context_lens[tid] : 0;
     for (int b = tid; b < nbucket; b += kPlanThreads) hist[b] = 0;
     __syncthreads();
 
@@ -40,7 +45,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
     // a sequence with no context still gets one (empty) item so that its
     // output is written (zeros).
     auto items_of = [&](int s, int& n_units) {
-        const int c = clamp_ctx(context_lens[s], ctx_cap);
+        const int c = clamp_ctx(s == tid ? c_first : context_lens[s], ctx_cap);
         n_units = (c + kSubTokens - 1) / kSubTokens;
         const int nblk = (c + block_size - 1) / block_size;
         return c <= 0 ? 1 : (nblk + part_blocks - 1) / part_blocks;
@@ -59,22 +64,30 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
 
     // Exclusive scan over buckets in decreasing size: bucket b's first slot
     // is the number of items larger than b.  Thread t owns a contiguous run
-    // of buckets taken from the top.
+    // of buckets taken from the top; the runs' sums are scanned in thread
+    // order by shuffles within each wave and the waves' totals in LDS.
     const int per = (nbucket + kPlanThreads - 1) / kPlanThreads;
     int local = 0;
     for (int j = 0; j < per; ++j) {
         const int b = nbucket - 1 - (tid * per + j);
         if (b >= 0) local += hist[b];
     }
-    scan_tmp[tid] = local;
-    __syncthreads();
-    for (int off = 1; off < kPlanThreads; off <<= 1) {
-        const int v = tid >= off ? scan_tmp[tid - off] : 0;
-        __syncthreads();
-        scan_tmp[tid] += v;
-        __syncthreads();
+    int incl = local;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int v = __shfl_up(incl, d);
+        if (lane >= d) incl += v;
     }
-    int run = scan_tmp[tid] - local;          // exclusive prefix of this thread's run
+    if (lane == kWave - 1) wave_total[wid] = incl;
+    __syncthreads();
+    int before = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+        const int t = wave_total[w];
+        before += w < wid ? t : 0;
+        total += t;
+    }
+    int run = before + incl - local;          // exclusive prefix of this thread's run
     for (int j = 0; j < per; ++j) {
         const int b = nbucket - 1 - (tid * per + j);
         if (b >= 0) {
@@ -83,8 +96,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
             run += cnt;
         }
     }
-    if (tid == kPlanThreads - 1) {
-        plan[0] = scan_tmp[kPlanThreads - 1];
+    if (tid == 0) {
+        plan[0] = total;
         plan[1] = 0;   // persistent decode: next entry to claim
         plan[2] = 0;   // persistent decode: workgroups finished
         plan[3] = 0;
