@@ -622,6 +622,53 @@ int32_t paged_attention_decode_tokens(void* out, const void* q, int32_t q_dtype,
                                       int32_t kv_dtype, float k_scale, float v_scale,
                                       pkv_stream_t stream);
 
+/* The same decode over a run list ([P4] "vToken": attention reads every
+ * surviving token through the table; here each pool sub-tile that holds
+ * survivors is read whole and the rows that are not the sequence's keys are
+ * skipped).  Survivors of a random eviction sit in nearly every line of
+ * every tile, so paged_attention_decode_tokens fetches about the whole pool
+ * anyway; a run list fetches the same lines with the block path's whole-row
+ * loads.
+ *
+ * pkv_token_runs_bytes: bytes of the run list of num_seqs sequences of
+ *   at most max_tokens_per_seq table entries (negative on a bad argument).
+ * pkv_token_runs: builds the run list of a token table (arguments as
+ *   paged_attention_decode_tokens; num_seqs <= 65535, max_tokens_per_seq <
+ *   2^27) into `runs` (device memory of at least pkv_token_runs_bytes,
+ *   8-byte aligned; PKV_ERR_SIZE if smaller).  Layout (int32, each area on
+ *   256 bytes): [num_seqs counts n_s][num_seqs lengths 16 n_s][the decode's
+ *   work plan: sequences by decreasing n_s][num_seqs x max_tokens_per_seq
+ *   entries of two int32: (sub-tile, row mask)] (the entries end the
+ *   buffer); entry e < n_s of sequence s holds the pool sub-tile slot / 16
+ *   and a 16-bit mask of its rows that are keys.  An entry takes table
+ *   entries t, t + 1,
+ *   ... (t < min(context_lens[s], max_tokens_per_seq)) while they lie in one
+ *   16-token sub-tile at strictly increasing rows; any other step opens a
+ *   new entry, so the entries list every table entry exactly once (a slot
+ *   listed twice counts twice).  Slots outside [block_size, num_blocks *
+ *   block_size) read as slot block_size.  Built once per step: the table is
+ *   shared by all layers.
+ * paged_attention_decode_runs: attention of each sequence over the keys of
+ *   its run list (`runs` from pkv_token_runs with the same num_seqs,
+ *   max_tokens_per_seq, block_size and num_blocks); otherwise as
+ *   paged_attention_decode_tokens, whose result it equals within rounding
+ *   (the softmax visits the same keys in sub-tile units), and for a
+ *   block-aligned table the block-table decode's on one partition with the
+ *   same waves per workgroup bit for bit (PKV_IMPL_AUTO with partitions of
+ *   >= 2048 tokens: eight waves for 16-bit pools, four for fp8).  Sub-tile
+ *   ids past the pool read block 0.
+ *   Errors: as paged_attention_decode_tokens. */
+int64_t pkv_token_runs_bytes(int32_t num_seqs, int32_t max_tokens_per_seq);
+int32_t pkv_token_runs(const int32_t* token_slots, int32_t max_tokens_per_seq,
+                       const int32_t* context_lens, int32_t num_seqs, int32_t block_size,
+                       int32_t num_blocks, void* runs, int64_t runs_bytes, pkv_stream_t stream);
+int32_t paged_attention_decode_runs(void* out, const void* q, int32_t q_dtype,
+                                    const void* k_cache, const void* v_cache, const void* runs,
+                                    int32_t max_tokens_per_seq, int32_t num_seqs, int32_t num_heads,
+                                    int32_t num_kv_heads, int32_t head_dim, float scale,
+                                    int32_t block_size, int32_t num_blocks, int32_t kv_dtype,
+                                    float k_scale, float v_scale, pkv_stream_t stream);
+
 /* Rebuild whole blocks after an eviction ([P4] "vToken", asynchronous
  * repacking): for every tile t (device int32 tiles[t][1 + block_size]: the
  * destination block, then the source slot of each of its rows), in every

@@ -12,7 +12,8 @@ from ._binding import (  # noqa: F401
     layer_pool_bytes, workspace_bytes, default_partition_tokens, plan_bytes, build_plan,
     decode_slot_mapping, reshape_and_cache,
     paged_attention_decode, paged_attention_decode_append, check_block_tables, torch_dtype, dtype_code, EXPORTS,
-    BlockManager, copy_blocks, paged_attention_prefill, paged_attention_decode_tokens,
+    BlockManager, copy_blocks, paged_attention_prefill, paged_attention_decode_tokens, token_runs_bytes, token_runs,
+    paged_attention_decode_runs,
     move_tokens,
     repack_blocks,
     read_probe,

@@ -34,7 +34,8 @@ EXPORTS = [
     "pkv_move_tokens", "pkv_bm_repack_tiles", "pkv_repack_blocks",
     "pkv_read_probe_sink_bytes", "pkv_read_probe", "kv_pool_bytes_per_token",
     "pkv_bm_mark_computed", "pkv_bm_num_computed_tokens", "paged_attention_decode_noalloc",
-    "paged_attention_decode_append",
+    "paged_attention_decode_append", "pkv_token_runs_bytes", "pkv_token_runs",
+    "paged_attention_decode_runs",
 ]
 
 
@@ -125,6 +126,10 @@ def lib():
             "pkv_bm_token_slots": (i32, [p, i64, p, i32, ctypes.POINTER(i32)]),
             "paged_attention_decode_tokens": (i32, [p, p, i32, p, p, p, i32, p, i32, i32, i32,
                                                     i32, f32, i32, i32, i32, f32, f32, p]),
+            "pkv_token_runs_bytes": (i64, [i32, i32]),
+            "pkv_token_runs": (i32, [p, i32, p, i32, i32, i32, p, i64, p]),
+            "paged_attention_decode_runs": (i32, [p, p, i32, p, p, p, i32, i32, i32, i32, i32,
+                                                  f32, i32, i32, i32, f32, f32, p]),
             "pkv_move_tokens_scratch_bytes": (i64, [i32, i32, i32, i32, i32]),
             "pkv_move_tokens": (i32, [p, p, i32, i32, i32, i32, i32, i32, p, i32, p, i64, p]),
             "pkv_bm_repack_tiles": (i32, [p, i64, p, i32, ctypes.POINTER(i32)]),
@@ -562,6 +567,40 @@ def paged_attention_decode_tokens(out, q, k_cache, v_cache, token_slots, context
         token_slots.shape[1], _ptr(context_lens, "context_lens", torch.int32), S, H,
         num_kv_heads, D, float(scale), block_size, num_blocks, kv_dtype, float(k_scale),
         float(v_scale), _stream(stream)))
+
+
+def token_runs_bytes(num_seqs, max_tokens_per_seq):
+    return _check(lib().pkv_token_runs_bytes(num_seqs, max_tokens_per_seq))
+
+
+def token_runs(token_slots, context_lens, block_size, num_blocks, runs=None, stream=None):
+    """pkv_token_runs: the run list of a token table (device int32
+    [S][max_tokens]); returns the uint8 run-list tensor (allocated if None)."""
+    S, mt = token_slots.shape
+    need = token_runs_bytes(S, mt)
+    if runs is None:
+        runs = torch.empty(max(need, 8), dtype=torch.uint8, device=token_slots.device)
+    _check(lib().pkv_token_runs(_ptr(token_slots, "token_slots", torch.int32), mt,
+                                _ptr(context_lens, "context_lens", torch.int32), S, block_size,
+                                num_blocks, _ptr(runs, "runs"), runs.numel() * runs.element_size(),
+                                _stream(stream)))
+    return runs
+
+
+def paged_attention_decode_runs(out, q, k_cache, v_cache, runs, max_tokens_per_seq, num_kv_heads,
+                                block_size, num_blocks, kv_dtype, scale, k_scale=1.0, v_scale=1.0,
+                                stream=None):
+    """Decode over a run list from token_runs (same max_tokens_per_seq)."""
+    S, H, D = q.shape
+    _pool_blocks(k_cache, v_cache, num_blocks, num_kv_heads, D, block_size, kv_dtype)
+    need = token_runs_bytes(S, max_tokens_per_seq)
+    if runs.numel() * runs.element_size() < need:
+        raise ValueError(f"run list holds {runs.numel() * runs.element_size()} bytes, needs {need}")
+    _check(lib().paged_attention_decode_runs(
+        _ptr(out, "out", q.dtype), _ptr(q, "q"), dtype_code(q.dtype), _ptr(k_cache, "k_cache"),
+        _ptr(v_cache, "v_cache"), _ptr(runs, "runs"), max_tokens_per_seq, S, H, num_kv_heads, D,
+        float(scale), block_size, num_blocks, kv_dtype, float(k_scale), float(v_scale),
+        _stream(stream)))
 
 
 def repack_blocks(k_layers, v_layers, tiles, chain_offsets, num_blocks, num_kv_heads, head_dim,

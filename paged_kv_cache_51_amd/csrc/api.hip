@@ -529,14 +529,15 @@ int32_t paged_attention_prefill(void* out, const void* q, int32_t q_dtype, const
     return ok();
 }
 
-int32_t paged_attention_decode_tokens(void* out, const void* q, int32_t q_dtype,
-                                      const void* k_cache, const void* v_cache,
-                                      const int32_t* token_slots, int32_t max_tokens_per_seq,
-                                      const int32_t* context_lens, int32_t num_seqs,
-                                      int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
-                                      float scale, int32_t block_size, int32_t num_blocks,
-                                      int32_t kv_dtype, float k_scale, float v_scale,
-                                      pkv_stream_t stream) {
+// Checks shared by the token-table decodes; fills the launch arguments.
+// `table` is the token table or the run list (what max_tokens_per_seq
+// sizes).
+static int32_t token_decode_args(pkv::DecodeArgs& a, void* out, const void* q, int32_t q_dtype,
+                                 const void* k_cache, const void* v_cache, const void* table,
+                                 int32_t max_tokens_per_seq, const int32_t* context_lens,
+                                 bool need_context_lens, int32_t num_seqs, int32_t num_heads,
+                                 int32_t num_kv_heads, int32_t head_dim, float scale, int32_t block_size,
+                                 int32_t num_blocks, int32_t kv_dtype, float k_scale, float v_scale) {
     if (int32_t e = check_layout_args(head_dim, block_size, kv_dtype)) return e;
     if (q_dtype != PKV_BF16 && q_dtype != PKV_FP16) return fail(PKV_ERR_ARG, "q_dtype must be bf16 or fp16");
     if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || max_tokens_per_seq < 0 || num_blocks < 2)
@@ -549,11 +550,10 @@ int32_t paged_attention_decode_tokens(void* out, const void* q, int32_t q_dtype,
     if (!std::isfinite(scale)) return fail(PKV_ERR_ARG, "scale must be finite");
     if (kv_dtype == PKV_FP8_E4M3 && !(std::isfinite(k_scale) && std::isfinite(v_scale)))
         return fail(PKV_ERR_ARG, "fp8 scales must be finite");
-    pkv::DecodeArgs a{};
     pkv::set_heads(a, num_heads, num_kv_heads);   // entry heads: column groups of <= 16 query heads
     if ((int64_t)num_seqs * a.num_kv_heads > 0x7fffffff) return fail(PKV_ERR_UNSUPPORTED, "too many workgroups");
-    if (num_seqs > 0 && (!out || !q || !k_cache || !v_cache || !context_lens ||
-                         (max_tokens_per_seq > 0 && !token_slots)))
+    if (num_seqs > 0 && (!out || !q || !k_cache || !v_cache || (need_context_lens && !context_lens) ||
+                         (max_tokens_per_seq > 0 && !table)))
         return fail(PKV_ERR_ARG, "null pointer");
     a.out = out;
     a.q = q;
@@ -568,10 +568,97 @@ int32_t paged_attention_decode_tokens(void* out, const void* q, int32_t q_dtype,
     const float ks = kv_dtype == PKV_FP8_E4M3 ? k_scale : 1.0f;
     a.qk_scale_log2 = (float)((double)scale * (double)ks * 1.4426950408889634);
     a.out_scale = kv_dtype == PKV_FP8_E4M3 ? v_scale : 1.0f;
+    return PKV_OK;
+}
+
+int32_t paged_attention_decode_tokens(void* out, const void* q, int32_t q_dtype,
+                                      const void* k_cache, const void* v_cache,
+                                      const int32_t* token_slots, int32_t max_tokens_per_seq,
+                                      const int32_t* context_lens, int32_t num_seqs,
+                                      int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                      float scale, int32_t block_size, int32_t num_blocks,
+                                      int32_t kv_dtype, float k_scale, float v_scale,
+                                      pkv_stream_t stream) {
+    pkv::DecodeArgs a{};
+    if (int32_t e = token_decode_args(a, out, q, q_dtype, k_cache, v_cache, token_slots, max_tokens_per_seq,
+                                      context_lens, true, num_seqs, num_heads, num_kv_heads, head_dim, scale,
+                                      block_size, num_blocks, kv_dtype, k_scale, v_scale))
+        return e;
     (void)hipGetLastError();
     hipError_t e = pkv::launch_decode_tokens(a, q_dtype, kv_dtype, block_size, token_slots,
                                              max_tokens_per_seq, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "token-table decode launch");
+    return ok();
+}
+
+// Run list: [counts: num_seqs int32][lengths in tokens, 16 x counts][plan
+// of the decode: one item per sequence, longest first][entries: num_seqs x
+// max_tokens_per_seq pairs of int32]; each area starts on 256 bytes.
+struct RunsLayout { int64_t lens16, plan, entries, total; };
+static RunsLayout runs_layout(int32_t num_seqs, int32_t max_tokens_per_seq) {
+    RunsLayout r{};
+    r.lens16 = align256(4LL * num_seqs);
+    r.plan = r.lens16 + align256(4LL * num_seqs);
+    r.entries = r.plan + plan_bytes_of(num_seqs, 1);
+    r.total = r.entries + 8LL * num_seqs * max_tokens_per_seq;
+    return r;
+}
+// the plan sizes items in tokens: 16 per table entry at most
+constexpr int32_t kMaxRunTokens = (1 << 27) - 1;
+
+int64_t pkv_token_runs_bytes(int32_t num_seqs, int32_t max_tokens_per_seq) {
+    if (num_seqs < 0 || max_tokens_per_seq < 0 || max_tokens_per_seq > kMaxRunTokens)
+        return fail(PKV_ERR_ARG, "bad sizes");
+    ok();
+    return runs_layout(num_seqs, max_tokens_per_seq).total;
+}
+
+int32_t pkv_token_runs(const int32_t* token_slots, int32_t max_tokens_per_seq,
+                       const int32_t* context_lens, int32_t num_seqs, int32_t block_size,
+                       int32_t num_blocks, void* runs, int64_t runs_bytes, pkv_stream_t stream) {
+    if (!valid_block_size(block_size)) return fail(PKV_ERR_ARG, "block_size must be 16 or 32");
+    if (num_seqs < 0 || num_seqs > 65535 || max_tokens_per_seq < 0 || max_tokens_per_seq > kMaxRunTokens ||
+        num_blocks < 2)
+        return fail(PKV_ERR_ARG, "bad sizes (num_seqs <= 65535, max_tokens_per_seq < 2^27, num_blocks must "
+                                 "count the null block and at least one more)");
+    if ((int64_t)num_blocks * block_size >= (1LL << 31)) return fail(PKV_ERR_ARG, "slots must fit int32");
+    if (num_seqs == 0) return ok();
+    if (!runs || !context_lens || (max_tokens_per_seq > 0 && !token_slots)) return fail(PKV_ERR_ARG, "null pointer");
+    const RunsLayout rl = runs_layout(num_seqs, max_tokens_per_seq);
+    if (runs_bytes < rl.total)
+        return fail(PKV_ERR_SIZE, "run list needs %lld bytes, got %lld", (long long)rl.total, (long long)runs_bytes);
+    if ((uintptr_t)runs % 8) return fail(PKV_ERR_ARG, "run list must be 8-byte aligned");
+    (void)hipGetLastError();
+    char* rb = (char*)runs;
+    hipError_t e = pkv::launch_token_runs(token_slots, max_tokens_per_seq, context_lens, num_seqs, block_size,
+                                          num_blocks, (int32_t*)rb, (int32_t*)(rb + rl.lens16),
+                                          (int32_t*)(rb + rl.plan), (int2*)(rb + rl.entries), (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "run-list launch");
+    return ok();
+}
+
+int32_t paged_attention_decode_runs(void* out, const void* q, int32_t q_dtype, const void* k_cache,
+                                    const void* v_cache, const void* runs, int32_t max_tokens_per_seq,
+                                    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                    int32_t head_dim, float scale, int32_t block_size, int32_t num_blocks,
+                                    int32_t kv_dtype, float k_scale, float v_scale, pkv_stream_t stream) {
+    pkv::DecodeArgs a{};
+    if (int32_t e = token_decode_args(a, out, q, q_dtype, k_cache, v_cache, runs, max_tokens_per_seq, nullptr,
+                                      false, num_seqs, num_heads, num_kv_heads, head_dim, scale, block_size,
+                                      num_blocks, kv_dtype, k_scale, v_scale))
+        return e;
+    if (num_seqs > 0 && !runs) return fail(PKV_ERR_ARG, "null pointer");
+    if ((uintptr_t)runs % 8) return fail(PKV_ERR_ARG, "run list must be 8-byte aligned");
+    if (num_seqs > 65535 || max_tokens_per_seq > kMaxRunTokens)
+        return fail(PKV_ERR_ARG, "num_seqs <= 65535 and max_tokens_per_seq < 2^27");
+    const RunsLayout rl = runs_layout(num_seqs, max_tokens_per_seq);
+    const char* rb = (const char*)runs;
+    a.plan = (const int32_t*)(rb + rl.plan);
+    (void)hipGetLastError();
+    hipError_t e = pkv::launch_decode_runs(a, q_dtype, kv_dtype, block_size, (const int32_t*)rb,
+                                           (const int2*)(rb + rl.entries), max_tokens_per_seq,
+                                           (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "run-list decode launch");
     return ok();
 }
 

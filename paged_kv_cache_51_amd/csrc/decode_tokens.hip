@@ -16,7 +16,8 @@
 // values per pool row (16 loads per unit) and picks the token's bytes out
 // with byte permutes.  When the table is block-aligned the addresses
 // coincide with the block path's.  Repacking exists to return the table to
-// that state.
+// that state.  The run-list form below reads whole pool sub-tiles instead
+// and skips the rows that are not keys.
 #include "decode_core.h"
 #include "mfma_math.h"
 
@@ -192,6 +193,283 @@ hipError_t launch_decode_tokens(const DecodeArgs& a, int q_dtype, int kv_dtype, 
     }
     if (kv_dtype == DT_FP16) return launch_tokens_bs<DT_FP16, DT_FP16>(a, block_size, token_slots, max_tokens, st);
     return launch_tokens_bs<DT_FP8, DT_FP16>(a, block_size, token_slots, max_tokens, st);
+}
+
+// ------------------------------------------------------------ run lists --
+// The same attention over the pool's sub-tiles instead of single tokens.
+// Tokens evicted at random leave survivors in nearly every 64-byte line of
+// every tile, so the token gather above fetches about the whole pool
+// anyway, with 20 loads per lane and unit where the block path issues 8.
+// A run list reads each sub-tile that holds survivors whole, with the
+// block path's loads, and skips the rows that are not the sequence's keys
+// (their weight is 0 and their V zeroed, as for the tail of a context).
+//
+// Run list of sequence s: entries e = 0 .. n_s - 1, each a pool sub-tile
+// (global index slot / 16: block slot / BS, sub-tile (slot % BS) / 16) and
+// a 16-bit mask of the rows that are keys.  An entry takes consecutive
+// table entries t, t + 1, ... while they lie in one sub-tile at strictly
+// increasing rows (at most 16); any other step starts a new entry, so a
+// slot listed twice counts twice, as in the table.  Table entries outside
+// [BS, num_blocks * BS) read slot BS (block 1, row 0), as the token gather
+// does.
+//
+// One workgroup per sequence walks its table in tiles of kRunTile entries:
+// each thread flags which of its kRunPer entries start an entry, a
+// workgroup scan numbers the starts, every entry ORs its row bit into its
+// entry's mask in LDS, and the starts write their entries.  The tile's last
+// entry may go on in the next tile: it stays open (sub-tile and mask in
+// registers) until a later start or the end closes it.  Also writes
+// lens16[s] = 16 n_s, the run list's length in tokens, from which the plan
+// kernel orders the decode longest first.
+constexpr int kRunThreads = 256;
+constexpr int kRunPer = 4;
+constexpr int kRunTile = kRunThreads * kRunPer;
+
+__global__ __launch_bounds__(kRunThreads) void token_runs_kernel(const int32_t* __restrict__ token_slots,
+                                                                 int max_tokens,
+                                                                 const int32_t* __restrict__ context_lens,
+                                                                 int block_size, int num_blocks,
+                                                                 int32_t* __restrict__ counts,
+                                                                 int32_t* __restrict__ lens16,
+                                                                 int2* __restrict__ entries) {
+    constexpr int kWaves = kRunThreads / kWave;
+    __shared__ uint32_t tmask[kRunTile + 1];      // [0]: the entry open from earlier tiles
+    __shared__ int wave_total[kWaves];
+    __shared__ int last_sub;
+    const int s = blockIdx.x, tid = threadIdx.x;
+    const int lane = tid & (kWave - 1), wid = tid / kWave;
+    int ctx = context_lens[s];
+    ctx = ctx < 0 ? 0 : (ctx < max_tokens ? ctx : max_tokens);
+    const int32_t* row = token_slots + (int64_t)s * max_tokens;
+    int2* out = entries + (int64_t)s * max_tokens;
+    const int32_t cap = num_blocks * block_size;
+    auto slot_at = [&](int t) {
+        const int32_t v = row[t];
+        return (unsigned)(v - block_size) >= (unsigned)(cap - block_size) ? block_size : v;
+    };
+    // uniform state: entries written so far; the open entry (index n_done)
+    int n_done = 0, open_sub = 0;
+    uint32_t open_mask = 0;
+    bool open = false;
+    for (int t0 = 0; t0 < ctx; t0 += kRunTile) {
+        const bool last = t0 + kRunTile >= ctx;
+        const int tb = t0 + kRunPer * tid;
+        int32_t v[kRunPer];
+        bool st[kRunPer];
+        int32_t prev = (tb > 0 && tb <= ctx) ? slot_at(tb - 1) : 0;
+        int cnt = 0;
+#pragma unroll
+        for (int k = 0; k < kRunPer; ++k) {
+            const int t = tb + k;
+            const bool valid = t < ctx;
+            v[k] = valid ? slot_at(t) : 0;
+            st[k] = valid && (t == 0 || (v[k] >> 4) != (prev >> 4) || (v[k] & 15) <= (prev & 15));
+            prev = v[k];
+            cnt += st[k] ? 1 : 0;
+        }
+        // starts before this thread's (thread order = table order) and in all
+        int incl = cnt;
+#pragma unroll
+        for (int d = 1; d < kWave; d <<= 1) {
+            const int y = __shfl_up(incl, d);
+            if (lane >= d) incl += y;
+        }
+        if (lane == kWave - 1) wave_total[wid] = incl;
+        __syncthreads();
+        int before = incl - cnt, T = 0;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const int x = wave_total[w];
+            before += w < wid ? x : 0;
+            T += x;
+        }
+        for (int j = tid; j <= T; j += kRunThreads) tmask[j] = (j == 0 && open) ? open_mask : 0u;
+        __syncthreads();
+        // entry of each table entry, counted in the tile: -1 = the open one
+        int local = before - 1;
+#pragma unroll
+        for (int k = 0; k < kRunPer; ++k) {
+            if (st[k]) ++local;
+            if (tb + k < ctx) atomicOr(&tmask[local + 1], 1u << (v[k] & 15));
+        }
+        __syncthreads();
+        const int base_idx = n_done + (open ? 1 : 0);
+        local = before - 1;
+#pragma unroll
+        for (int k = 0; k < kRunPer; ++k) {
+            if (st[k]) {
+                ++local;
+                // closed by a later start in the tile, or by the end
+                if (local < T - 1 || last) out[base_idx + local] = make_int2(v[k] >> 4, (int)tmask[local + 1]);
+                if (local == T - 1) last_sub = v[k] >> 4;
+            }
+        }
+        if (tid == 0 && open && (T > 0 || last)) out[n_done] = make_int2(open_sub, (int)tmask[0]);
+        __syncthreads();
+        if (T > 0) {
+            open_sub = last_sub;
+            open_mask = tmask[T];
+            n_done = base_idx + T - 1;
+            open = true;
+        } else {
+            open_mask = tmask[0];
+        }
+        __syncthreads();                          // tmask and last_sub are reused
+    }
+    if (tid == 0) {
+        const int n = open ? n_done + 1 : 0;
+        counts[s] = n;
+        lens16[s] = 16 * n;
+    }
+}
+
+hipError_t launch_token_runs(const int32_t* token_slots, int max_tokens, const int32_t* context_lens,
+                             int num_seqs, int block_size, int num_blocks, int32_t* counts,
+                             int32_t* lens16, int32_t* plan, int2* entries, hipStream_t st) {
+    if (num_seqs == 0) return hipSuccess;
+    hipLaunchKernelGGL(token_runs_kernel, dim3(num_seqs), dim3(kRunThreads), 0, st, token_slots, max_tokens,
+                       context_lens, block_size, num_blocks, counts, lens16, entries);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    // longest run list first: one item per sequence (a partition as long
+    // as the longest list), sized in 16-token units
+    return launch_plan(lens16, num_seqs, 16 * max_tokens, kSubTokens, max_tokens > 0 ? max_tokens : 1, plan, st);
+}
+
+// Attention over a run list: one workgroup per (sequence, entry head); wave
+// w takes entries w, w + NW, ... with the block path's ring of whole
+// sub-tile loads, DEPTH in flight.  A block-aligned table gives the block
+// path's result bit for bit (four waves, unsplit context).  PLAIN:
+// cache-allocating loads, for kv heads split over several entry heads.
+template <int KVT, int QT, int BS, int NW, int DEPTH, bool PLAIN>
+__global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(PKV_WAVES_PER_EU)))
+void paged_decode_runs_kernel(const DecodeArgs a, const int32_t* __restrict__ counts,
+                              const int2* __restrict__ entries, int max_tokens) {
+    extern __shared__ float pkv_smem[];
+    constexpr int NSUB = BS / kSubTokens;
+    constexpr int64_t SUB = sub_tile_bytes(KVT);
+    constexpr int64_t TILE = SUB * NSUB;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // the plan's sequences (longest run list first) in groups of 8, each
+    // group expanded over the entry heads with the heads of a sequence on
+    // one XCD, as the block path's grid form
+    const int per_group = 8 * a.num_kv_heads;
+    const int grp = blockIdx.x / per_group;
+    const int rem = blockIdx.x - grp * per_group;
+    const int item = grp * 8 + (rem & 7);
+    const int kvh = rem >> 3;
+    if (item >= a.num_seqs) return;
+    const int s = (int)((uint32_t)a.plan[kPlanHeader + item] >> 16);
+    const QueryTile qt{s, 1, 1};
+    // entry i of this sequence as one 64-bit load: (sub-tile, rows)
+    const uint64_t* ent = reinterpret_cast<const uint64_t*>(entries) + (int64_t)s * max_tokens;
+    auto entry = [&](int i) -> uint64_t { return max_tokens > 0 ? ent[min(i, max_tokens - 1)] : 0ull; };
+    // this wave's first 64 entries load beside the queries and the count
+    const uint64_t e0 = entry(w + NW * lane);
+    MfmaMath<KVT, QT> mt;
+    mt.load_q(a, qt, kvh, lane);
+    const int n_units = __builtin_amdgcn_readfirstlane(counts[s]);
+    if (n_units <= 0) {
+        uint16_t* out = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)s * a.num_heads + first_head(a, kvh)) * kHeadDim;
+        for (int e = threadIdx.x; e < heads_of(a, kvh) * kHeadDim; e += NW * kWave) out[e] = 0;
+        return;
+    }
+    int* done = reinterpret_cast<int*>(pkv_smem);
+    if (threadIdx.x == 0) *done = 0;
+    __syncthreads();
+    mt.begin();
+
+    const uint8_t* kpool = a.k_cache + (int64_t)pool_head(a, kvh) * TILE;
+    const uint8_t* vpool = a.v_cache + (int64_t)pool_head(a, kvh) * TILE;
+    const int64_t head_stride = (int64_t)a.pool_kv_heads * TILE;
+    const int n_my = w < n_units ? (n_units - w + NW - 1) / NW : 0;
+    for (int c0 = 0; c0 < n_my; c0 += kWave) {
+        const int nc = min(kWave, n_my - c0);
+        const uint64_t e = c0 == 0 ? e0 : entry(w + NW * (c0 + lane));
+        const int e_sub = (int)(uint32_t)e, e_rows = (int)(uint32_t)(e >> 32);
+        auto unit_offset = [&](int j) -> int64_t {
+            const int sub = __builtin_amdgcn_readlane(e_sub, j);
+            int pb = sub / NSUB;
+            if ((unsigned)pb >= (unsigned)a.num_blocks) pb = 0;
+            return (int64_t)pb * head_stride + (sub - (sub / NSUB) * NSUB) * SUB;
+        };
+        auto rows_of = [&](int j) { return (uint32_t)__builtin_amdgcn_readlane(e_rows, j); };
+        UnitRegs<KVT> buf[DEPTH];
+#pragma unroll
+        for (int d = 0; d < DEPTH; ++d) {
+            const int64_t off = unit_offset(min(d, nc - 1));
+            load_unit<KVT, kHeadDim, PLAIN>(buf[d], kpool + off, vpool + off, lane);
+        }
+        int i = 0;
+        for (; i + 2 * DEPTH <= nc; i += DEPTH) {
+#pragma unroll
+            for (int d = 0; d < DEPTH; ++d) {
+                mt.unit_rows(buf[d], rows_of(i + d), a.qk_scale_log2, lane);
+                const int64_t off = unit_offset(i + d + DEPTH);
+                load_unit<KVT, kHeadDim, PLAIN>(buf[d], kpool + off, vpool + off, lane);
+            }
+        }
+        const int refills = nc - i - DEPTH;       // < DEPTH; may be negative
+#pragma unroll
+        for (int d = 0; d < DEPTH; ++d) {
+            if (i + d < nc) {
+                mt.unit_rows(buf[d], rows_of(i + d), a.qk_scale_log2, lane);
+                if (d < refills) {
+                    const int64_t off = unit_offset(i + d + DEPTH);
+                    load_unit<KVT, kHeadDim, PLAIN>(buf[d], kpool + off, vpool + off, lane);
+                }
+            }
+        }
+#pragma unroll
+        for (int d = 0; d < DEPTH - 1; ++d)
+            if (d < refills) mt.unit_rows(buf[d], rows_of(i + DEPTH + d), a.qk_scale_log2, lane);
+    }
+    park_and_store<MfmaMath<KVT, QT>, QT, NW>(a, pkv_smem, mt, s, 0, kvh, lane, w, qt, a.group, true);
+}
+
+template <int KVT, int QT, int BS, int NW, int DP>
+static hipError_t launch_runs_nw(const DecodeArgs& a, const int32_t* counts, const int2* entries,
+                                 int max_tokens, hipStream_t st) {
+    const size_t lds = sizeof(float) * merge_lds_floats(NW, a.group);
+    const dim3 grid((unsigned)(((int64_t)a.num_seqs + 7) / 8 * 8 * a.num_kv_heads)), block(NW * kWave);
+    if (a.kv_split > 1)
+        hipLaunchKernelGGL((paged_decode_runs_kernel<KVT, QT, BS, NW, DP, true>), grid, block, lds,
+                           st, a, counts, entries, max_tokens);
+    else
+        hipLaunchKernelGGL((paged_decode_runs_kernel<KVT, QT, BS, NW, DP, false>), grid, block, lds,
+                           st, a, counts, entries, max_tokens);
+    return hipGetLastError();
+}
+
+// Waves per workgroup as the block path's partition kernel on unsplit
+// contexts: eight for 16-bit pools (a sequence's list streams in half the
+// time, so the end of the launch is shorter), four with one sub-tile in
+// flight for fp8.
+template <int KVT, int QT, int BS>
+static hipError_t launch_runs_t(const DecodeArgs& a, const int32_t* counts, const int2* entries,
+                                int max_tokens, hipStream_t st) {
+    if constexpr (KVT == DT_FP8)
+        return launch_runs_nw<KVT, QT, BS, kWavesPerGroup, 1>(a, counts, entries, max_tokens, st);
+    else
+        return launch_runs_nw<KVT, QT, BS, 2 * kWavesPerGroup, kDepth>(a, counts, entries, max_tokens, st);
+}
+
+template <int KVT, int QT>
+static hipError_t launch_runs_bs(const DecodeArgs& a, int bs, const int32_t* c, const int2* e, int mt,
+                                 hipStream_t st) {
+    return bs == 16 ? launch_runs_t<KVT, QT, 16>(a, c, e, mt, st) : launch_runs_t<KVT, QT, 32>(a, c, e, mt, st);
+}
+
+hipError_t launch_decode_runs(const DecodeArgs& a, int q_dtype, int kv_dtype, int block_size,
+                              const int32_t* counts, const int2* entries, int max_tokens, hipStream_t st) {
+    if (a.num_seqs == 0) return hipSuccess;
+    if (q_dtype == DT_BF16) {
+        if (kv_dtype == DT_BF16) return launch_runs_bs<DT_BF16, DT_BF16>(a, block_size, counts, entries, max_tokens, st);
+        return launch_runs_bs<DT_FP8, DT_BF16>(a, block_size, counts, entries, max_tokens, st);
+    }
+    if (kv_dtype == DT_FP16) return launch_runs_bs<DT_FP16, DT_FP16>(a, block_size, counts, entries, max_tokens, st);
+    return launch_runs_bs<DT_FP8, DT_FP16>(a, block_size, counts, entries, max_tokens, st);
 }
 
 // ------------------------------------------------------------ move tokens --

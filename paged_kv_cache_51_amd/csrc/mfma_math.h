@@ -73,6 +73,20 @@ struct MfmaMath {
     // tok0 = logical position of the unit's first token; ctx = context
     // length; cs = scale * k_scale * log2(e).
     __device__ __forceinline__ void unit(const UnitRegs<KVT, D>& u, int tok0, int ctx, float cs, int lane) {
+        unit_impl<false>(u, tok0, ctx, 0xffffu, cs, lane);
+    }
+    // A pool sub-tile of which only some rows hold keys of the sequence:
+    // row r is a key when bit r of the wave-uniform rows16 is set, and is
+    // skipped otherwise (weight 0, V zeroed: the row may hold anything).
+    // Every real column sees every key.  With all 16 bits set the result
+    // is unit()'s on a unit wholly inside the context, bit for bit.
+    __device__ __forceinline__ void unit_rows(const UnitRegs<KVT, D>& u, uint32_t rows16, float cs, int lane) {
+        unit_impl<true>(u, 0, 0, rows16, cs, lane);
+    }
+
+    template <bool ROWS>
+    __device__ __forceinline__ void unit_impl(const UnitRegs<KVT, D>& u, int tok0, int ctx, uint32_t rows16,
+                                              float cs, int lane) {
         f32x4_t st[NT];
 #pragma unroll
         for (int t = 0; t < NT; ++t) st[t] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
@@ -84,6 +98,7 @@ struct MfmaMath {
         }
 
         const int tb = tok0 + 4 * (lane >> 4);
+        const uint32_t rows4 = (rows16 >> (4 * (lane >> 4))) & 0xfu;   // this lane's rows (ROWS)
         float x[NT][4];
         bool valid[NT][4];        // key visible to this lane's column
         float bm[NT];
@@ -92,7 +107,8 @@ struct MfmaMath {
         for (int t = 0; t < NT; ++t) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                valid[t][i] = (tb + i) < lim[t];
+                if constexpr (ROWS) valid[t][i] = cvalid[t] && ((rows4 >> i) & 1u);
+                else valid[t][i] = (tb + i) < lim[t];
                 x[t][i] = valid[t][i] ? st[t][i] * cs : -INFINITY;
             }
             bm[t] = fmaxf(fmaxf(x[t][0], x[t][1]), fmaxf(x[t][2], x[t][3]));
@@ -128,7 +144,7 @@ struct MfmaMath {
             pf[t][0] = pbits[0] | (pbits[1] << 16);
             pf[t][1] = pbits[2] | (pbits[3] << 16);
         }
-        if (tok0 + kSubTokens <= ctx) {
+        if (ROWS ? rows16 == 0xffffu : tok0 + kSubTokens <= ctx) {
 #pragma unroll
             for (int nt = 0; nt < NV; ++nt) {
                 const u32x2_t vf = v_frag<KVT, QT>(u, nt);
@@ -139,9 +155,10 @@ struct MfmaMath {
             // Last unit of the context: rows past the context hold whatever
             // the slot last held (NaN or stale data); a zero weight times NaN
             // would still poison the sum, so zero those V elements too.
+            // (ROWS: rows whose bit is clear, which another token may hold)
             bool row[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) row[i] = (tb + i) < ctx;
+            for (int i = 0; i < 4; ++i) row[i] = ROWS ? ((rows4 >> i) & 1u) != 0 : (tb + i) < ctx;
             u32x2_t vm;
             vm[0] = (row[0] ? 0x0000ffffu : 0u) | (row[1] ? 0xffff0000u : 0u);
             vm[1] = (row[2] ? 0x0000ffffu : 0u) | (row[3] ? 0xffff0000u : 0u);

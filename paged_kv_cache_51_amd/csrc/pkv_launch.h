@@ -119,6 +119,12 @@ hipError_t launch_decode_reduce(const DecodeArgs& a, int q_dtype, int block_size
 // (decode_tokens.hip).
 hipError_t launch_decode_tokens(const DecodeArgs& a, int q_dtype, int kv_dtype, int block_size,
                                 const int32_t* token_slots, int max_tokens, hipStream_t st);
+// Run lists of a token table, and decode through them (decode_tokens.hip).
+hipError_t launch_token_runs(const int32_t* token_slots, int max_tokens, const int32_t* context_lens,
+                             int num_seqs, int block_size, int num_blocks, int32_t* counts,
+                             int32_t* lens16, int32_t* plan, int2* entries, hipStream_t st);
+hipError_t launch_decode_runs(const DecodeArgs& a, int q_dtype, int kv_dtype, int block_size,
+                              const int32_t* counts, const int2* entries, int max_tokens, hipStream_t st);
 hipError_t launch_repack_blocks(void* const* k_layers, void* const* v_layers, int num_layers,
                                 int num_blocks, int num_kv_heads, int block_size, int kv_dtype,
                                 const int32_t* tiles, const int32_t* chain_offsets, int num_chains,

@@ -229,3 +229,39 @@ def test_workspace_bytes_wide_groups(H, Hkv, D, entries, cols):
     want = (_a256(S * Hkv * entries * cols * P * D * 4) + _a256(S * Hkv * entries * P * line * 4)
             + _a256(4 * (4 + S * P)))
     assert pkv.workspace_bytes(S, H, Hkv, D, 200, 16, 16) == want
+
+
+def test_token_run_list_sizes_and_argument_errors():
+    """Run lists ("vToken" page, decode through a token table): size query,
+    and every argument error before a launch (no GPU touched)."""
+    L = pkv.lib()
+    assert pkv.token_runs_bytes(3, 10) == 3 * 256 + 3 * 10 * 8   # counts, lengths, plan, entries
+    assert pkv.token_runs_bytes(65, 0) == 3 * 512
+    assert L.pkv_token_runs_bytes(1, 1 << 27) == -1                 # lengths in tokens must fit int32
+    assert L.pkv_token_runs_bytes(-1, 4) == -1
+    # pkv_token_runs(slots, max_tokens, ctx, S, bs, nb, runs, runs_bytes, stream)
+    f = lambda **k: L.pkv_token_runs(k.get("slots", FAKE), k.get("mt", 10), k.get("ctx", FAKE),
+                                     k.get("S", 3), k.get("bs", 16), k.get("nb", 8),
+                                     k.get("runs", FAKE), k.get("nbytes", 1008), None)
+    assert f(bs=8) == -1
+    assert f(nb=1) == -1
+    assert f(S=-1) == -1
+    assert f(runs=None) == -1
+    assert f(nbytes=1007) == -2
+    assert f(S=65536) == -1
+    assert f(runs=ctypes.c_void_p(0x1004)) == -1          # not 8-byte aligned
+    assert f(nb=1 << 27, bs=32) == -1                     # slots would overflow int32
+    assert f(S=0, runs=None) == 0                         # nothing to do
+    # paged_attention_decode_runs(out, q, qt, k, v, runs, mt, S, H, Hkv, D, scale, bs, nb, kv, ks, vs, st)
+    g = lambda **k: L.paged_attention_decode_runs(FAKE, FAKE, k.get("qt", 0), FAKE, FAKE,
+                                                  k.get("runs", FAKE), 10, 3, k.get("H", 8), 2,
+                                                  k.get("D", 128), k.get("scale", 0.1), 16,
+                                                  k.get("nb", 8), k.get("kv", 0), 1.0, 1.0, None)
+    assert g(qt=2) == -1
+    assert g(H=7) == -1
+    assert g(D=64) == -4
+    assert g(nb=1) == -1
+    assert g(kv=1) == -4
+    assert g(scale=float("nan")) == -1
+    assert g(runs=None) == -1
+    assert g(runs=ctypes.c_void_p(0x1004)) == -1

@@ -3,7 +3,10 @@ per-token table against the oracle (fragmented tables, every dtype); an
 aligned table equal bit for bit to the block-table decode; token moves
 bit-exact against the oracle (chains, swaps, skipped moves, > 64 layers);
 evict -> repack -> move -> block decode equal bit for bit to the decode of
-the fragmented table before repacking."""
+the fragmented table before repacking.  Run lists (the table as pool
+sub-tiles with row masks) bit-exact against the rule written out; the
+run-list decode against the oracle with NaN in every evicted row, equal bit
+for bit to the block decode on aligned tables."""
 import numpy as np
 import pytest
 import torch
@@ -273,3 +276,172 @@ def test_decode_tokens_full_size_sampled():
     err = np.abs(got[idx] - want).max()
     log(f"  sampled {len(idx)} seqs: max-abs {err:.3e}")
     assert err <= TOL[oracle.BF16]
+
+
+# ------------------------------------------------------------ run lists --
+
+def runs_reference(slots, ctx, bs, num_blocks):
+    """The run rule written out with plain loops: consecutive table entries
+    share an entry while they lie in one 16-token sub-tile at strictly
+    increasing rows; slots outside [bs, num_blocks * bs) read as slot bs."""
+    cap = num_blocks * bs
+    out = []
+    for s in range(slots.shape[0]):
+        ent, prev = [], None
+        for t in range(max(0, min(int(ctx[s]), slots.shape[1]))):
+            v = int(slots[s, t])
+            v = v if bs <= v < cap else bs
+            if prev is not None and v >> 4 == prev >> 4 and (v & 15) > (prev & 15):
+                ent[-1][1] |= 1 << (v & 15)
+            else:
+                ent.append([v >> 4, 1 << (v & 15)])
+            prev = v
+        out.append(ent)
+    return out
+
+
+def read_runs(runs, S, width):
+    """Counts at the start of the run list, entries at its end."""
+    h = runs.cpu().numpy()
+    counts = h[:4 * S].view(np.int32)
+    off = pkv.token_runs_bytes(S, width) - 8 * S * width
+    ent = h[off:off + 8 * S * width].view(np.int32).reshape(S, width, 2)
+    return [[[int(x), int(m)] for x, m in ent[s, :counts[s]]] for s in range(S)]
+
+
+def poison_evicted(kp, vp, tabs, slots, ctx, kv, qdt, Hkv, bs):
+    """NaN into every slot a sequence held before eviction and no longer
+    lists: the run decode reads those rows and must skip them."""
+    kept = {int(v) for s in range(len(ctx)) for v in slots[s, :ctx[s]]}
+    held = {int(slot) for _, _, slot in pools.all_slots(tabs.block_tables, tabs.context_lens, bs)}
+    gone = np.array(sorted(held - kept), np.int64)
+    if len(gone) == 0:
+        return kp, vp
+    nan = 0x7FC0 if qdt == oracle.BF16 else 0x7E00    # (E4M3 encodes it as its NaN, 0x7F)
+    bits = np.full((len(gone), Hkv, D), nan, np.uint16)
+    return oracle.reshape_and_cache(bits, bits, qdt, kp, vp, gone, bs, tabs.num_blocks, kv)
+
+
+@pytest.mark.parametrize("bs", [16, 32])
+def test_token_runs_bit_exact(bs):
+    """Run lists equal the rule written out: fragmented tables, a slot listed
+    twice, rows out of order, slots outside the pool, a table longer than the
+    context and a context longer than the table, an empty sequence."""
+    nb = 70
+    r = np.random.default_rng(31 + bs)
+    width = 300
+    S = 7
+    slots = r.integers(bs, nb * bs, (S, width)).astype(np.int32)
+    for s in range(S):
+        base = r.integers(1, nb - 20) * bs
+        run = np.sort(r.choice(np.arange(base, base + 20 * bs), width, replace=False))
+        slots[s] = run if s % 2 == 0 else slots[s]
+    slots[0, 10:14] = slots[0, 9]                    # the same slot listed again
+    slots[2, 40:48] = slots[2, 40:48][::-1]          # rows out of order
+    slots[4, [3, 7, 8]] = [0, 5, nb * bs + 3]        # null block, inside it, past the pool
+    slots[4, 20] = -7
+    ctx = np.array([width, 0, 255, 1, 300, 17, 1000], np.int32)
+    want = runs_reference(slots, ctx, bs, nb)
+    runs = pkv.token_runs(devi(slots), devi(ctx), bs, nb)
+    torch.cuda.synchronize()
+    got = read_runs(runs, S, width)
+    for s in range(S):
+        assert got[s] == want[s], f"sequence {s}"
+
+
+@pytest.mark.parametrize("kv,qdt,bs", [(oracle.BF16, oracle.BF16, 16), (oracle.FP16, oracle.FP16, 32),
+                                       (oracle.FP8, oracle.BF16, 16), (oracle.FP8, oracle.FP16, 32)])
+@pytest.mark.parametrize("H,Hkv", [(12, 2), (8, 8), (32, 2)])
+def test_decode_runs_fragmented(kv, qdt, bs, H, Hkv):
+    """Run-list decode of fragmented tables against the oracle, with NaN in
+    every evicted row (read with the sub-tile, never used); and within
+    rounding of the token gather."""
+    log(f"run-list decode kv={kv} bs={bs} G={H // Hkv}")
+    ks, vs = (0.02, 0.03) if kv == oracle.FP8 else (1.0, 1.0)
+    lengths = [1, 17, 64, 200, 333, 50]
+    tabs, kp, vp, slots, ctx, q = fragmented_case(lengths, H, Hkv, bs, kv, qdt, 0.55, 7, ks, vs)
+    kp, vp = poison_evicted(kp, vp, tabs, slots, ctx, kv, qdt, Hkv, bs)
+    want = oracle.paged_decode_tokens(q, qdt, kp, vp, kv, slots, ctx, Hkv, bs, SCALE, ks, vs)
+    qt = dev16(q, qdt)
+    kd, vd = torch.from_numpy(kp).to(DEV), torch.from_numpy(vp).to(DEV)
+    ts, cl = devi(slots), devi(ctx)
+    runs = pkv.token_runs(ts, cl, bs, tabs.num_blocks)
+    out = torch.full_like(qt, float("nan"))
+    pkv.paged_attention_decode_runs(out, qt, kd, vd, runs, slots.shape[1], Hkv, bs, tabs.num_blocks, kv,
+                                    SCALE, ks, vs)
+    gat = torch.full_like(qt, float("nan"))
+    pkv.paged_attention_decode_tokens(gat, qt, kd, vd, ts, cl, Hkv, bs, tabs.num_blocks, kv, SCALE, ks, vs)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy().astype(np.float64)
+    assert np.isfinite(got).all()
+    err = np.abs(got - want).max()
+    log(f"  max-abs {err:.3e}")
+    assert err <= TOL[kv]
+    assert np.abs(got - gat.float().cpu().numpy()).max() <= TOL[kv]
+
+
+@pytest.mark.parametrize("kv", [oracle.BF16, oracle.FP8])
+def test_aligned_runs_equal_block_decode_bitwise(kv):
+    """A block-aligned table's run list is the block table: the run decode
+    gives the unsplit block decode's output bit for bit (same waves per
+    workgroup: eight for 16-bit pools, four for fp8, which is what the
+    default form takes with partitions of >= 2048 tokens)."""
+    c, tabs, _, r_val = workloads.make("qwen15b")
+    Hkv, H, bs = c.num_kv_heads, c.num_heads, c.block_size
+    ks = vs = 0.05 if kv == oracle.FP8 else 1.0
+    kb = [workloads.normal_bits(r_val, (int(x), Hkv, D), oracle.BF16) for x in tabs.context_lens]
+    vb = [workloads.normal_bits(r_val, (int(x), Hkv, D), oracle.BF16) for x in tabs.context_lens]
+    S = len(tabs.context_lens)
+    qb = workloads.normal_bits(r_val, (S, H, D), oracle.BF16)
+    kp, vp = pools.write_contiguous(kb, vb, tabs.block_tables, tabs.context_lens, Hkv, D, bs,
+                                    tabs.num_blocks, kv, oracle.BF16, ks, vs)
+    mc = int(tabs.context_lens.max())
+    slots = np.zeros((S, mc), np.int32)
+    for s, cl in enumerate(tabs.context_lens):
+        slots[s, :cl] = [tabs.block_tables[s][t // bs] * bs + t % bs for t in range(cl)]
+    q = dev16(qb, oracle.BF16)
+    kd, vd = torch.from_numpy(kp).to(DEV), torch.from_numpy(vp).to(DEV)
+    cl = devi(tabs.context_lens)
+    a = torch.full_like(q, float("nan"))
+    assert mc >= 2048
+    pkv.paged_attention_decode(a, q, kd, vd, devi(tabs.block_tables), cl, mc, Hkv, bs, kv, SCALE,
+                               ks, vs, partition_tokens=-(-mc // bs) * bs, num_blocks=tabs.num_blocks)
+    runs = pkv.token_runs(devi(slots), cl, bs, tabs.num_blocks)
+    b = torch.full_like(q, float("nan"))
+    pkv.paged_attention_decode_runs(b, q, kd, vd, runs, mc, Hkv, bs, tabs.num_blocks, kv, SCALE, ks, vs)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_decode_runs_repeated_slots_and_empty():
+    """A slot listed twice counts twice (as in the oracle's definition), an
+    empty sequence gives zeros, and a second call reusing the run buffer for
+    a smaller table gives the same result as a fresh one."""
+    bs, Hkv, H, kv, qdt = 16, 2, 8, oracle.BF16, oracle.BF16
+    lengths = [90, 40, 129]
+    tabs, kp, vp, slots, ctx, q = fragmented_case(lengths, H, Hkv, bs, kv, qdt, 0.7, 3)
+    slots = np.concatenate([slots, np.zeros((3, 8), np.int32)], axis=1)
+    for s in range(3):
+        c = ctx[s]
+        slots[s, c:c + 5] = slots[s, [0, 0, c // 2, c - 1, c // 3]]   # repeats, out of order
+        ctx[s] = c + 5
+    ctx[1] = 0
+    want = oracle.paged_decode_tokens(q, qdt, kp, vp, kv, slots, ctx, Hkv, bs, SCALE)
+    qt = dev16(q, qdt)
+    kd, vd = torch.from_numpy(kp).to(DEV), torch.from_numpy(vp).to(DEV)
+    runs = pkv.token_runs(devi(slots), devi(ctx), bs, tabs.num_blocks)
+    out = torch.full_like(qt, float("nan"))
+    pkv.paged_attention_decode_runs(out, qt, kd, vd, runs, slots.shape[1], Hkv, bs, tabs.num_blocks, kv,
+                                    SCALE)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy().astype(np.float64)
+    assert np.all(got[1] == 0)
+    assert np.abs(got - want).max() <= TOL[kv]
+    # the same buffer, a narrower table of the first sequence only
+    narrow = np.ascontiguousarray(slots[:1, :ctx[0]])
+    pkv.token_runs(devi(narrow), devi(ctx[:1]), bs, tabs.num_blocks, runs=runs)
+    one = torch.full_like(qt[:1], float("nan"))
+    pkv.paged_attention_decode_runs(one, qt[:1].contiguous(), kd, vd, runs, narrow.shape[1], Hkv, bs,
+                                    tabs.num_blocks, kv, SCALE)
+    torch.cuda.synchronize()
+    assert torch.equal(one[0], out[0])
