@@ -649,8 +649,9 @@ int32_t paged_attention_decode_tokens(void* out, const void* q, int32_t q_dtype,
  *   block_size) read as slot block_size.  Built once per step: the table is
  *   shared by all layers.
  * paged_attention_decode_runs: attention of each sequence over the keys of
- *   its run list (`runs` from pkv_token_runs with the same num_seqs,
- *   max_tokens_per_seq, block_size and num_blocks); otherwise as
+ *   its run list (`runs`, runs_bytes long, from pkv_token_runs with the same
+ *   num_seqs, max_tokens_per_seq, block_size and num_blocks; PKV_ERR_SIZE if
+ *   runs_bytes < pkv_token_runs_bytes); otherwise as
  *   paged_attention_decode_tokens, whose result it equals within rounding
  *   (the softmax visits the same keys in sub-tile units), and for a
  *   block-aligned table the block-table decode's on one partition with the
@@ -664,7 +665,8 @@ int32_t pkv_token_runs(const int32_t* token_slots, int32_t max_tokens_per_seq,
                        int32_t num_blocks, void* runs, int64_t runs_bytes, pkv_stream_t stream);
 int32_t paged_attention_decode_runs(void* out, const void* q, int32_t q_dtype,
                                     const void* k_cache, const void* v_cache, const void* runs,
-                                    int32_t max_tokens_per_seq, int32_t num_seqs, int32_t num_heads,
+                                    int64_t runs_bytes, int32_t max_tokens_per_seq,
+                                    int32_t num_seqs, int32_t num_heads,
                                     int32_t num_kv_heads, int32_t head_dim, float scale,
                                     int32_t block_size, int32_t num_blocks, int32_t kv_dtype,
                                     float k_scale, float v_scale, pkv_stream_t stream);

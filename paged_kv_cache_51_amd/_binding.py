@@ -128,8 +128,8 @@ def lib():
                                                     i32, f32, i32, i32, i32, f32, f32, p]),
             "pkv_token_runs_bytes": (i64, [i32, i32]),
             "pkv_token_runs": (i32, [p, i32, p, i32, i32, i32, p, i64, p]),
-            "paged_attention_decode_runs": (i32, [p, p, i32, p, p, p, i32, i32, i32, i32, i32,
-                                                  f32, i32, i32, i32, f32, f32, p]),
+            "paged_attention_decode_runs": (i32, [p, p, i32, p, p, p, i64, i32, i32, i32, i32,
+                                                  i32, f32, i32, i32, i32, f32, f32, p]),
             "pkv_move_tokens_scratch_bytes": (i64, [i32, i32, i32, i32, i32]),
             "pkv_move_tokens": (i32, [p, p, i32, i32, i32, i32, i32, i32, p, i32, p, i64, p]),
             "pkv_bm_repack_tiles": (i32, [p, i64, p, i32, ctypes.POINTER(i32)]),
@@ -593,12 +593,10 @@ def paged_attention_decode_runs(out, q, k_cache, v_cache, runs, max_tokens_per_s
     """Decode over a run list from token_runs (same max_tokens_per_seq)."""
     S, H, D = q.shape
     _pool_blocks(k_cache, v_cache, num_blocks, num_kv_heads, D, block_size, kv_dtype)
-    need = token_runs_bytes(S, max_tokens_per_seq)
-    if runs.numel() * runs.element_size() < need:
-        raise ValueError(f"run list holds {runs.numel() * runs.element_size()} bytes, needs {need}")
     _check(lib().paged_attention_decode_runs(
         _ptr(out, "out", q.dtype), _ptr(q, "q"), dtype_code(q.dtype), _ptr(k_cache, "k_cache"),
-        _ptr(v_cache, "v_cache"), _ptr(runs, "runs"), max_tokens_per_seq, S, H, num_kv_heads, D,
+        _ptr(v_cache, "v_cache"), _ptr(runs, "runs"), runs.numel() * runs.element_size(),
+        max_tokens_per_seq, S, H, num_kv_heads, D,
         float(scale), block_size, num_blocks, kv_dtype, float(k_scale), float(v_scale),
         _stream(stream)))
 

@@ -638,8 +638,9 @@ int32_t pkv_token_runs(const int32_t* token_slots, int32_t max_tokens_per_seq,
 }
 
 int32_t paged_attention_decode_runs(void* out, const void* q, int32_t q_dtype, const void* k_cache,
-                                    const void* v_cache, const void* runs, int32_t max_tokens_per_seq,
-                                    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                    const void* v_cache, const void* runs, int64_t runs_bytes,
+                                    int32_t max_tokens_per_seq, int32_t num_seqs, int32_t num_heads,
+                                    int32_t num_kv_heads,
                                     int32_t head_dim, float scale, int32_t block_size, int32_t num_blocks,
                                     int32_t kv_dtype, float k_scale, float v_scale, pkv_stream_t stream) {
     pkv::DecodeArgs a{};
@@ -652,6 +653,8 @@ int32_t paged_attention_decode_runs(void* out, const void* q, int32_t q_dtype, c
     if (num_seqs > 65535 || max_tokens_per_seq > kMaxRunTokens)
         return fail(PKV_ERR_ARG, "num_seqs <= 65535 and max_tokens_per_seq < 2^27");
     const RunsLayout rl = runs_layout(num_seqs, max_tokens_per_seq);
+    if (num_seqs > 0 && runs_bytes < rl.total)
+        return fail(PKV_ERR_SIZE, "run list of %lld bytes, needs %lld", (long long)runs_bytes, (long long)rl.total);
     const char* rb = (const char*)runs;
     a.plan = (const int32_t*)(rb + rl.plan);
     (void)hipGetLastError();

@@ -361,6 +361,7 @@ void paged_decode_runs_kernel(const DecodeArgs a, const int32_t* __restrict__ co
     const int kvh = rem >> 3;
     if (item >= a.num_seqs) return;
     const int s = (int)((uint32_t)a.plan[kPlanHeader + item] >> 16);
+    if (s >= a.num_seqs) return;              // a list built for other sizes
     const QueryTile qt{s, 1, 1};
     // entry i of this sequence as one 64-bit load: (sub-tile, rows)
     const uint64_t* ent = reinterpret_cast<const uint64_t*>(entries) + (int64_t)s * max_tokens;

@@ -252,9 +252,11 @@ def test_token_run_list_sizes_and_argument_errors():
     assert f(runs=ctypes.c_void_p(0x1004)) == -1          # not 8-byte aligned
     assert f(nb=1 << 27, bs=32) == -1                     # slots would overflow int32
     assert f(S=0, runs=None) == 0                         # nothing to do
-    # paged_attention_decode_runs(out, q, qt, k, v, runs, mt, S, H, Hkv, D, scale, bs, nb, kv, ks, vs, st)
+    # paged_attention_decode_runs(out, q, qt, k, v, runs, runs_bytes, mt, S, H, Hkv, D, scale, bs, nb,
+    #                             kv, ks, vs, st)
     g = lambda **k: L.paged_attention_decode_runs(FAKE, FAKE, k.get("qt", 0), FAKE, FAKE,
-                                                  k.get("runs", FAKE), 10, 3, k.get("H", 8), 2,
+                                                  k.get("runs", FAKE), k.get("nbytes", 1008), 10, 3,
+                                                  k.get("H", 8), 2,
                                                   k.get("D", 128), k.get("scale", 0.1), 16,
                                                   k.get("nb", 8), k.get("kv", 0), 1.0, 1.0, None)
     assert g(qt=2) == -1
@@ -265,3 +267,4 @@ def test_token_run_list_sizes_and_argument_errors():
     assert g(scale=float("nan")) == -1
     assert g(runs=None) == -1
     assert g(runs=ctypes.c_void_p(0x1004)) == -1
+    assert g(nbytes=1007) == -2

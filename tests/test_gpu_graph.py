@@ -5,7 +5,8 @@ The launch shape of every decode entry depends only on host scalars, and
 the work plan, the partition partials and the persistent form's counters
 live in caller memory that each launch fully rewrites (the counters are
 reset by the launch's last workgroup), so a captured step can be replayed
-with new contents in context_lens, block tables, q and the new K / V.  Each
+with new contents in context_lens, block tables, q and the new K / V (and a
+token-table step over run lists with new tables).  Each
 replay is checked bit for bit against the eager step on the same inputs,
 with eager work and host synchronisations between replays.
 """
@@ -105,4 +106,80 @@ def test_decode_step_replays_like_eager(impl):
             assert torch.equal(out[layer].view(torch.int16), want[layer].view(torch.int16)), \
                 f"replay {rep} layer {layer}: output differs from the eager step"
             assert torch.equal(kp[layer], k_want[layer]) and torch.equal(vp[layer], v_want[layer])
+        assert torch.isfinite(out[0].float()).all()
+
+
+def test_run_list_decode_step_replays_like_eager():
+    """A token-table step over run lists (the list built once, then the
+    decode of each layer) captured and replayed on new tables, lengths and
+    queries: every replay equals the eager step bit for bit."""
+    S, H, Hkv, D, bs, L = 40, 8, 2, 128, 16, 2
+    width = 600
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(7)
+    nb = S * (width // bs + 2) + 1
+    pool_bytes = pkv.layer_pool_bytes(nb, Hkv, D, bs, pkv.BF16)
+    kp = [randn_pool(pool_bytes, gen) for _ in range(L)]
+    vp = [randn_pool(pool_bytes, gen) for _ in range(L)]
+    slots = torch.empty(S, width, dtype=torch.int32, device=DEV)
+    cl = torch.empty(S, dtype=torch.int32, device=DEV)
+    q = [torch.empty(S, H, D, dtype=torch.bfloat16, device=DEV) for _ in range(L)]
+    out = [torch.empty(S, H, D, dtype=torch.bfloat16, device=DEV) for _ in range(L)]
+    runs = torch.empty(pkv.token_runs_bytes(S, width), dtype=torch.uint8, device=DEV)
+    scale = float(np.float32(1.0 / np.sqrt(D)))
+
+    def fill(seed):
+        # a fresh eviction: each sequence keeps a random subset of its own
+        # blocks' slots, in order (new table, new lengths, new queries)
+        r = np.random.default_rng(seed)
+        perm = r.permutation(np.arange(1, nb)).astype(np.int64)
+        tab = np.zeros((S, width), np.int32)
+        lens = np.zeros(S, np.int32)
+        per = width // bs + 1
+        for s in range(S):
+            c = int(r.integers(1, width + 1))
+            full = np.array([perm[s * per + t // bs] * bs + t % bs for t in range(c)], np.int64)
+            keep = full[r.random(c) < 0.6] if c > 1 else full
+            keep = keep if len(keep) else full[-1:]
+            tab[s, :len(keep)] = keep
+            lens[s] = len(keep)
+        slots.copy_(torch.from_numpy(tab))
+        cl.copy_(torch.from_numpy(lens))
+        g = torch.Generator(device=DEV)
+        g.manual_seed(seed)
+        for t in q:
+            t.copy_(torch.randn(t.shape, generator=g, device=DEV).to(torch.bfloat16))
+
+    def step():
+        pkv.token_runs(slots, cl, bs, nb, runs=runs)
+        for layer in range(L):
+            pkv.paged_attention_decode_runs(out[layer], q[layer], kp[layer], vp[layer], runs, width, Hkv, bs,
+                                            nb, pkv.BF16, scale)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fill(1)
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    for rep, seed in enumerate((21, 22, 23)):
+        log(f"  run lists replay {rep} (inputs seed {seed})")
+        fill(seed)
+        step()
+        torch.cuda.synchronize()
+        want = [t.clone() for t in out]
+        for t in out:
+            t.fill_(float("nan"))
+        runs.fill_(0xFF)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for layer in range(L):
+            assert torch.equal(out[layer].view(torch.int16), want[layer].view(torch.int16)), \
+                f"replay {rep} layer {layer}: output differs from the eager step"
         assert torch.isfinite(out[0].float()).all()
