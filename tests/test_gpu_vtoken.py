@@ -351,7 +351,7 @@ def test_token_runs_bit_exact(bs):
 
 @pytest.mark.parametrize("kv,qdt,bs", [(oracle.BF16, oracle.BF16, 16), (oracle.FP16, oracle.FP16, 32),
                                        (oracle.FP8, oracle.BF16, 16), (oracle.FP8, oracle.FP16, 32)])
-@pytest.mark.parametrize("H,Hkv", [(12, 2), (8, 8), (32, 2)])
+@pytest.mark.parametrize("H,Hkv", [(12, 2), (8, 8), (32, 2), (40, 1)])
 def test_decode_runs_fragmented(kv, qdt, bs, H, Hkv):
     """Run-list decode of fragmented tables against the oracle, with NaN in
     every evicted row (read with the sub-tile, never used); and within
