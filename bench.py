@@ -618,12 +618,15 @@ def bench_vtoken(args, torch, pkv, workloads):
     # row masks, built once per step (the table is shared by all layers)
     runs = torch.empty(pkv.token_runs_bytes(S, width), dtype=torch.uint8, device=dev)
     runs_build_ms = timed(lambda: pkv.token_runs(slots, cl, bs, nb, runs=runs, stream=stream), args.steps)
-    n_entries = int(runs[:4 * S].view(torch.int32).sum().item())
+    counts = runs[:4 * S].view(torch.int32).cpu().numpy()
+    n_entries = int(counts[counts >= 0].sum())         # sub-tiles the run lists read
+    n_marked = int((counts < 0).sum())                  # sequences left to the token gather
 
     def runs_layers():
         for l in range(L):
             pkv.paged_attention_decode_runs(outs[l], qs[l], kpools[l], vpools[l], runs, width, Hkv, bs, nb,
-                                            kv, scale, ks, vs, stream=stream)
+                                            kv, scale, ks, vs, token_slots=slots, context_lens=cl,
+                                            stream=stream)
     runs_ms = timed(runs_layers, args.steps) / L
 
     def runs_step():
@@ -683,7 +686,8 @@ def bench_vtoken(args, torch, pkv, workloads):
           f"read + written), as {mv.shape[0]} token moves {move_ms * 1e3:.1f} us ({move_gbs:.0f} GB/s); "
           f"block decode after {block_ms * 1e3:.1f} us/layer ({block_gbs:.0f} GB/s)",
           file=sys.stderr, flush=True)
-    print(f"[bench] vtoken run lists: {n_entries} sub-tiles ({sub_bytes / 1e9:.2f} GB read per layer); "
+    print(f"[bench] vtoken run lists: {n_entries} sub-tiles ({sub_bytes / 1e9:.2f} GB read per layer), "
+          f"{n_marked} of {S} sequences token by token (fewer than {pkv.RUNS_MIN_KEYS} keys per sub-tile); "
           f"build {runs_build_ms * 1e3:.1f} us per step, decode {runs_ms * 1e3:.1f} us/layer ({runs_gbs:.0f} "
           f"GB/s surviving, {sub_bytes / (runs_ms * 1e-3) / 1e9:.0f} GB/s of sub-tiles read); step of "
           f"{L} layers {runs_step_ms * 1e3:.1f} us ({runs_step_gbs:.0f} GB/s)", file=sys.stderr, flush=True)
@@ -705,6 +709,7 @@ def bench_vtoken(args, torch, pkv, workloads):
                                       "gbs": round(block_gbs, 1)},
         "step": "run lists built once (pkv_token_runs), then paged_attention_decode_runs per layer",
         "run_lists": {"entries": n_entries, "sub_tile_bytes_per_layer": sub_bytes,
+                      "sequences_token_by_token": n_marked, "min_keys_per_entry": pkv.RUNS_MIN_KEYS,
                       "build_us_per_step": round(runs_build_ms * 1e3, 2),
                       "sub_tile_gbs": round(sub_bytes / (runs_ms * 1e-3) / 1e9, 1)},
         "token_gather_decode": {"kernel": "paged_decode_tokens_kernel",

@@ -647,11 +647,20 @@ int32_t paged_attention_decode_tokens(void* out, const void* q, int32_t q_dtype,
  *   new entry, so the entries list every table entry exactly once (a slot
  *   listed twice counts twice).  Slots outside [block_size, num_blocks *
  *   block_size) read as slot block_size.  Built once per step: the table is
- *   shared by all layers.
+ *   shared by all layers.  min_keys_per_entry (0..16): a sequence whose
+ *   list holds fewer keys than this per entry on average (sparse survivors,
+ *   whole sub-tiles mostly skipped) is marked for the token gather instead
+ *   (count -1 - n_s); 0 marks none.  Measured crossover on the Qwen2.5-7B
+ *   decode shape: about 5 (10 % of tokens kept: gather 212 us / layer, run
+ *   list 308 us; 25 %: 353 / 373 us; 50 %: 463 / 376 us).
  * paged_attention_decode_runs: attention of each sequence over the keys of
  *   its run list (`runs`, runs_bytes long, from pkv_token_runs with the same
  *   num_seqs, max_tokens_per_seq, block_size and num_blocks; PKV_ERR_SIZE if
- *   runs_bytes < pkv_token_runs_bytes); otherwise as
+ *   runs_bytes < pkv_token_runs_bytes), and of the sequences the list marked
+ *   for the gather token by token through token_slots / context_lens (the
+ *   table the list was built from; a second launch).  Pass both as NULL only
+ *   for a list built with min_keys_per_entry = 0 (marked sequences are then
+ *   left unwritten).  Otherwise as
  *   paged_attention_decode_tokens, whose result it equals within rounding
  *   (the softmax visits the same keys in sub-tile units), and for a
  *   block-aligned table the block-table decode's on one partition with the
@@ -662,10 +671,12 @@ int32_t paged_attention_decode_tokens(void* out, const void* q, int32_t q_dtype,
 int64_t pkv_token_runs_bytes(int32_t num_seqs, int32_t max_tokens_per_seq);
 int32_t pkv_token_runs(const int32_t* token_slots, int32_t max_tokens_per_seq,
                        const int32_t* context_lens, int32_t num_seqs, int32_t block_size,
-                       int32_t num_blocks, void* runs, int64_t runs_bytes, pkv_stream_t stream);
+                       int32_t num_blocks, int32_t min_keys_per_entry, void* runs,
+                       int64_t runs_bytes, pkv_stream_t stream);
 int32_t paged_attention_decode_runs(void* out, const void* q, int32_t q_dtype,
                                     const void* k_cache, const void* v_cache, const void* runs,
-                                    int64_t runs_bytes, int32_t max_tokens_per_seq,
+                                    int64_t runs_bytes, const int32_t* token_slots,
+                                    const int32_t* context_lens, int32_t max_tokens_per_seq,
                                     int32_t num_seqs, int32_t num_heads,
                                     int32_t num_kv_heads, int32_t head_dim, float scale,
                                     int32_t block_size, int32_t num_blocks, int32_t kv_dtype,

@@ -13,7 +13,7 @@ from ._binding import (  # noqa: F401
     decode_slot_mapping, reshape_and_cache,
     paged_attention_decode, paged_attention_decode_append, check_block_tables, torch_dtype, dtype_code, EXPORTS,
     BlockManager, copy_blocks, paged_attention_prefill, paged_attention_decode_tokens, token_runs_bytes, token_runs,
-    paged_attention_decode_runs,
+    paged_attention_decode_runs, RUNS_MIN_KEYS,
     move_tokens,
     repack_blocks,
     read_probe,

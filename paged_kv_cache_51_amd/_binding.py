@@ -127,9 +127,9 @@ def lib():
             "paged_attention_decode_tokens": (i32, [p, p, i32, p, p, p, i32, p, i32, i32, i32,
                                                     i32, f32, i32, i32, i32, f32, f32, p]),
             "pkv_token_runs_bytes": (i64, [i32, i32]),
-            "pkv_token_runs": (i32, [p, i32, p, i32, i32, i32, p, i64, p]),
-            "paged_attention_decode_runs": (i32, [p, p, i32, p, p, p, i64, i32, i32, i32, i32,
-                                                  i32, f32, i32, i32, i32, f32, f32, p]),
+            "pkv_token_runs": (i32, [p, i32, p, i32, i32, i32, i32, p, i64, p]),
+            "paged_attention_decode_runs": (i32, [p, p, i32, p, p, p, i64, p, p, i32, i32, i32,
+                                                  i32, i32, f32, i32, i32, i32, f32, f32, p]),
             "pkv_move_tokens_scratch_bytes": (i64, [i32, i32, i32, i32, i32]),
             "pkv_move_tokens": (i32, [p, p, i32, i32, i32, i32, i32, i32, p, i32, p, i64, p]),
             "pkv_bm_repack_tiles": (i32, [p, i64, p, i32, ctypes.POINTER(i32)]),
@@ -573,7 +573,13 @@ def token_runs_bytes(num_seqs, max_tokens_per_seq):
     return _check(lib().pkv_token_runs_bytes(num_seqs, max_tokens_per_seq))
 
 
-def token_runs(token_slots, context_lens, block_size, num_blocks, runs=None, stream=None):
+# Keys per run-list entry below which a sequence is decoded token by token
+# (the measured crossover on the Qwen2.5-7B decode shape, pagedkv.h).
+RUNS_MIN_KEYS = 5
+
+
+def token_runs(token_slots, context_lens, block_size, num_blocks, runs=None,
+               min_keys_per_entry=RUNS_MIN_KEYS, stream=None):
     """pkv_token_runs: the run list of a token table (device int32
     [S][max_tokens]); returns the uint8 run-list tensor (allocated if None)."""
     S, mt = token_slots.shape
@@ -582,20 +588,23 @@ def token_runs(token_slots, context_lens, block_size, num_blocks, runs=None, str
         runs = torch.empty(max(need, 8), dtype=torch.uint8, device=token_slots.device)
     _check(lib().pkv_token_runs(_ptr(token_slots, "token_slots", torch.int32), mt,
                                 _ptr(context_lens, "context_lens", torch.int32), S, block_size,
-                                num_blocks, _ptr(runs, "runs"), runs.numel() * runs.element_size(),
-                                _stream(stream)))
+                                num_blocks, int(min_keys_per_entry), _ptr(runs, "runs"),
+                                runs.numel() * runs.element_size(), _stream(stream)))
     return runs
 
 
 def paged_attention_decode_runs(out, q, k_cache, v_cache, runs, max_tokens_per_seq, num_kv_heads,
                                 block_size, num_blocks, kv_dtype, scale, k_scale=1.0, v_scale=1.0,
-                                stream=None):
-    """Decode over a run list from token_runs (same max_tokens_per_seq)."""
+                                token_slots=None, context_lens=None, stream=None):
+    """Decode over a run list from token_runs (same max_tokens_per_seq); the
+    sequences it marked for the gather read token_slots / context_lens (the
+    table the list was built from; both None only for min_keys_per_entry=0)."""
     S, H, D = q.shape
     _pool_blocks(k_cache, v_cache, num_blocks, num_kv_heads, D, block_size, kv_dtype)
     _check(lib().paged_attention_decode_runs(
         _ptr(out, "out", q.dtype), _ptr(q, "q"), dtype_code(q.dtype), _ptr(k_cache, "k_cache"),
         _ptr(v_cache, "v_cache"), _ptr(runs, "runs"), runs.numel() * runs.element_size(),
+        _ptr(token_slots, "token_slots", torch.int32), _ptr(context_lens, "context_lens", torch.int32),
         max_tokens_per_seq, S, H, num_kv_heads, D,
         float(scale), block_size, num_blocks, kv_dtype, float(k_scale), float(v_scale),
         _stream(stream)))

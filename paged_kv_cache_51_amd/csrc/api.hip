@@ -586,7 +586,7 @@ int32_t paged_attention_decode_tokens(void* out, const void* q, int32_t q_dtype,
         return e;
     (void)hipGetLastError();
     hipError_t e = pkv::launch_decode_tokens(a, q_dtype, kv_dtype, block_size, token_slots,
-                                             max_tokens_per_seq, (hipStream_t)stream);
+                                             max_tokens_per_seq, nullptr, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "token-table decode launch");
     return ok();
 }
@@ -615,8 +615,10 @@ int64_t pkv_token_runs_bytes(int32_t num_seqs, int32_t max_tokens_per_seq) {
 
 int32_t pkv_token_runs(const int32_t* token_slots, int32_t max_tokens_per_seq,
                        const int32_t* context_lens, int32_t num_seqs, int32_t block_size,
-                       int32_t num_blocks, void* runs, int64_t runs_bytes, pkv_stream_t stream) {
+                       int32_t num_blocks, int32_t min_keys_per_entry, void* runs, int64_t runs_bytes,
+                       pkv_stream_t stream) {
     if (!valid_block_size(block_size)) return fail(PKV_ERR_ARG, "block_size must be 16 or 32");
+    if (min_keys_per_entry < 0 || min_keys_per_entry > 16) return fail(PKV_ERR_ARG, "min_keys_per_entry must be 0..16");
     if (num_seqs < 0 || num_seqs > 65535 || max_tokens_per_seq < 0 || max_tokens_per_seq > kMaxRunTokens ||
         num_blocks < 2)
         return fail(PKV_ERR_ARG, "bad sizes (num_seqs <= 65535, max_tokens_per_seq < 2^27, num_blocks must "
@@ -631,7 +633,7 @@ int32_t pkv_token_runs(const int32_t* token_slots, int32_t max_tokens_per_seq,
     (void)hipGetLastError();
     char* rb = (char*)runs;
     hipError_t e = pkv::launch_token_runs(token_slots, max_tokens_per_seq, context_lens, num_seqs, block_size,
-                                          num_blocks, (int32_t*)rb, (int32_t*)(rb + rl.lens16),
+                                          num_blocks, min_keys_per_entry, (int32_t*)rb, (int32_t*)(rb + rl.lens16),
                                           (int32_t*)(rb + rl.plan), (int2*)(rb + rl.entries), (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "run-list launch");
     return ok();
@@ -639,6 +641,7 @@ int32_t pkv_token_runs(const int32_t* token_slots, int32_t max_tokens_per_seq,
 
 int32_t paged_attention_decode_runs(void* out, const void* q, int32_t q_dtype, const void* k_cache,
                                     const void* v_cache, const void* runs, int64_t runs_bytes,
+                                    const int32_t* token_slots, const int32_t* context_lens,
                                     int32_t max_tokens_per_seq, int32_t num_seqs, int32_t num_heads,
                                     int32_t num_kv_heads,
                                     int32_t head_dim, float scale, int32_t block_size, int32_t num_blocks,
@@ -648,6 +651,8 @@ int32_t paged_attention_decode_runs(void* out, const void* q, int32_t q_dtype, c
                                       false, num_seqs, num_heads, num_kv_heads, head_dim, scale, block_size,
                                       num_blocks, kv_dtype, k_scale, v_scale))
         return e;
+    if ((token_slots == nullptr) != (context_lens == nullptr))
+        return fail(PKV_ERR_ARG, "token_slots and context_lens go together (both or neither)");
     if (num_seqs > 0 && !runs) return fail(PKV_ERR_ARG, "null pointer");
     if ((uintptr_t)runs % 8) return fail(PKV_ERR_ARG, "run list must be 8-byte aligned");
     if (num_seqs > 65535 || max_tokens_per_seq > kMaxRunTokens)
@@ -662,6 +667,13 @@ int32_t paged_attention_decode_runs(void* out, const void* q, int32_t q_dtype, c
                                            (const int2*)(rb + rl.entries), max_tokens_per_seq,
                                            (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "run-list decode launch");
+    if (token_slots) {
+        // the sequences the run list marked for the token gather
+        a.context_lens = context_lens;
+        e = pkv::launch_decode_tokens(a, q_dtype, kv_dtype, block_size, token_slots, max_tokens_per_seq,
+                                      (const int32_t*)rb, (hipStream_t)stream);
+        if (e != hipSuccess) return hip_fail(e, "token-table decode launch");
+    }
     return ok();
 }
 

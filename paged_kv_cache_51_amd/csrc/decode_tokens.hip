@@ -113,16 +113,20 @@ __device__ __forceinline__ void gather_unit(UnitRegs<KVT>& u, const uint8_t* kpo
 // One workgroup per (sequence, kv head); wave w takes units w, w + NW, ...
 // in chunks of 4 (one slot load per lane per chunk, then four units of
 // loads in flight), no context split.
+// only_marked (a run list's counts, or null): decode only the sequences
+// the run list marked for the gather (negative count), leave the others to
+// the run-list decode.
 template <int KVT, int QT, int BS, int NW>
 __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(PKV_WAVES_PER_EU)))
 void paged_decode_tokens_kernel(const DecodeArgs a, const int32_t* __restrict__ token_slots,
-                                int max_tokens) {
+                                int max_tokens, const int32_t* __restrict__ only_marked) {
     extern __shared__ float pkv_smem[];
     constexpr int CH = 4;
     const int lane = threadIdx.x & (kWave - 1);
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int s = blockIdx.x / a.num_kv_heads;
     const int kvh = blockIdx.x - s * a.num_kv_heads;
+    if (only_marked != nullptr && only_marked[s] >= 0) return;
     const int G = a.group;
     const QueryTile qt{s, 1, 1};
     MfmaMath<KVT, QT> mt;
@@ -170,29 +174,32 @@ void paged_decode_tokens_kernel(const DecodeArgs a, const int32_t* __restrict__ 
 
 template <int KVT, int QT, int BS>
 static hipError_t launch_tokens_t(const DecodeArgs& a, const int32_t* token_slots, int max_tokens,
-                                  hipStream_t st) {
+                                  const int32_t* only_marked, hipStream_t st) {
     const size_t lds = sizeof(float) * merge_lds_floats(kWavesPerGroup, a.group);
     hipLaunchKernelGGL((paged_decode_tokens_kernel<KVT, QT, BS, kWavesPerGroup>),
                        dim3(a.num_seqs * a.num_kv_heads), dim3(kWavesPerGroup * kWave), lds, st, a,
-                       token_slots, max_tokens);
+                       token_slots, max_tokens, only_marked);
     return hipGetLastError();
 }
 
 template <int KVT, int QT>
 static hipError_t launch_tokens_bs(const DecodeArgs& a, int bs, const int32_t* ts, int mt,
-                                   hipStream_t st) {
-    return bs == 16 ? launch_tokens_t<KVT, QT, 16>(a, ts, mt, st) : launch_tokens_t<KVT, QT, 32>(a, ts, mt, st);
+                                   const int32_t* om, hipStream_t st) {
+    return bs == 16 ? launch_tokens_t<KVT, QT, 16>(a, ts, mt, om, st)
+                    : launch_tokens_t<KVT, QT, 32>(a, ts, mt, om, st);
 }
 
 hipError_t launch_decode_tokens(const DecodeArgs& a, int q_dtype, int kv_dtype, int block_size,
-                                const int32_t* token_slots, int max_tokens, hipStream_t st) {
+                                const int32_t* token_slots, int max_tokens, const int32_t* only_marked,
+                                hipStream_t st) {
     if (a.num_seqs == 0) return hipSuccess;
+    const int32_t* om = only_marked;
     if (q_dtype == DT_BF16) {
-        if (kv_dtype == DT_BF16) return launch_tokens_bs<DT_BF16, DT_BF16>(a, block_size, token_slots, max_tokens, st);
-        return launch_tokens_bs<DT_FP8, DT_BF16>(a, block_size, token_slots, max_tokens, st);
+        if (kv_dtype == DT_BF16) return launch_tokens_bs<DT_BF16, DT_BF16>(a, block_size, token_slots, max_tokens, om, st);
+        return launch_tokens_bs<DT_FP8, DT_BF16>(a, block_size, token_slots, max_tokens, om, st);
     }
-    if (kv_dtype == DT_FP16) return launch_tokens_bs<DT_FP16, DT_FP16>(a, block_size, token_slots, max_tokens, st);
-    return launch_tokens_bs<DT_FP8, DT_FP16>(a, block_size, token_slots, max_tokens, st);
+    if (kv_dtype == DT_FP16) return launch_tokens_bs<DT_FP16, DT_FP16>(a, block_size, token_slots, max_tokens, om, st);
+    return launch_tokens_bs<DT_FP8, DT_FP16>(a, block_size, token_slots, max_tokens, om, st);
 }
 
 // ------------------------------------------------------------ run lists --
@@ -220,7 +227,10 @@ hipError_t launch_decode_tokens(const DecodeArgs& a, int q_dtype, int kv_dtype, 
 // entry may go on in the next tile: it stays open (sub-tile and mask in
 // registers) until a later start or the end closes it.  Also writes
 // lens16[s] = 16 n_s, the run list's length in tokens, from which the plan
-// kernel orders the decode longest first.
+// kernel orders the decode longest first.  With min_keys > 0, a sequence
+// whose list holds fewer than min_keys keys per entry on average (sparse
+// survivors: whole sub-tiles would be mostly skipped rows) is marked for
+// the token gather instead: counts[s] = -1 - n_s, lens16[s] = 0.
 constexpr int kRunThreads = 256;
 constexpr int kRunPer = 4;
 constexpr int kRunTile = kRunThreads * kRunPer;
@@ -228,7 +238,7 @@ constexpr int kRunTile = kRunThreads * kRunPer;
 __global__ __launch_bounds__(kRunThreads) void token_runs_kernel(const int32_t* __restrict__ token_slots,
                                                                  int max_tokens,
                                                                  const int32_t* __restrict__ context_lens,
-                                                                 int block_size, int num_blocks,
+                                                                 int block_size, int num_blocks, int min_keys,
                                                                  int32_t* __restrict__ counts,
                                                                  int32_t* __restrict__ lens16,
                                                                  int2* __restrict__ entries) {
@@ -318,17 +328,18 @@ __global__ __launch_bounds__(kRunThreads) void token_runs_kernel(const int32_t* 
     }
     if (tid == 0) {
         const int n = open ? n_done + 1 : 0;
-        counts[s] = n;
-        lens16[s] = 16 * n;
+        const bool sparse = min_keys > 0 && n > 0 && (int64_t)ctx < (int64_t)min_keys * n;
+        counts[s] = sparse ? -1 - n : n;
+        lens16[s] = sparse ? 0 : 16 * n;
     }
 }
 
 hipError_t launch_token_runs(const int32_t* token_slots, int max_tokens, const int32_t* context_lens,
-                             int num_seqs, int block_size, int num_blocks, int32_t* counts,
+                             int num_seqs, int block_size, int num_blocks, int min_keys, int32_t* counts,
                              int32_t* lens16, int32_t* plan, int2* entries, hipStream_t st) {
     if (num_seqs == 0) return hipSuccess;
     hipLaunchKernelGGL(token_runs_kernel, dim3(num_seqs), dim3(kRunThreads), 0, st, token_slots, max_tokens,
-                       context_lens, block_size, num_blocks, counts, lens16, entries);
+                       context_lens, block_size, num_blocks, min_keys, counts, lens16, entries);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     // longest run list first: one item per sequence (a partition as long
@@ -371,7 +382,8 @@ void paged_decode_runs_kernel(const DecodeArgs a, const int32_t* __restrict__ co
     MfmaMath<KVT, QT> mt;
     mt.load_q(a, qt, kvh, lane);
     const int n_units = __builtin_amdgcn_readfirstlane(counts[s]);
-    if (n_units <= 0) {
+    if (n_units < 0) return;                  // marked for the token gather
+    if (n_units == 0) {
         uint16_t* out = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)s * a.num_heads + first_head(a, kvh)) * kHeadDim;
         for (int e = threadIdx.x; e < heads_of(a, kvh) * kHeadDim; e += NW * kWave) out[e] = 0;
         return;

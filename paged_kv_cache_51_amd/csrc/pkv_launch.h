@@ -118,10 +118,11 @@ hipError_t launch_decode_reduce(const DecodeArgs& a, int q_dtype, int block_size
 // Decode through a per-token slot table; token moves between slots
 // (decode_tokens.hip).
 hipError_t launch_decode_tokens(const DecodeArgs& a, int q_dtype, int kv_dtype, int block_size,
-                                const int32_t* token_slots, int max_tokens, hipStream_t st);
+                                const int32_t* token_slots, int max_tokens, const int32_t* only_marked,
+                                hipStream_t st);
 // Run lists of a token table, and decode through them (decode_tokens.hip).
 hipError_t launch_token_runs(const int32_t* token_slots, int max_tokens, const int32_t* context_lens,
-                             int num_seqs, int block_size, int num_blocks, int32_t* counts,
+                             int num_seqs, int block_size, int num_blocks, int min_keys, int32_t* counts,
                              int32_t* lens16, int32_t* plan, int2* entries, hipStream_t st);
 hipError_t launch_decode_runs(const DecodeArgs& a, int q_dtype, int kv_dtype, int block_size,
                               const int32_t* counts, const int2* entries, int max_tokens, hipStream_t st);

@@ -239,10 +239,12 @@ def test_token_run_list_sizes_and_argument_errors():
     assert pkv.token_runs_bytes(65, 0) == 3 * 512
     assert L.pkv_token_runs_bytes(1, 1 << 27) == -1                 # lengths in tokens must fit int32
     assert L.pkv_token_runs_bytes(-1, 4) == -1
-    # pkv_token_runs(slots, max_tokens, ctx, S, bs, nb, runs, runs_bytes, stream)
+    # pkv_token_runs(slots, max_tokens, ctx, S, bs, nb, min_keys, runs, runs_bytes, stream)
     f = lambda **k: L.pkv_token_runs(k.get("slots", FAKE), k.get("mt", 10), k.get("ctx", FAKE),
-                                     k.get("S", 3), k.get("bs", 16), k.get("nb", 8),
+                                     k.get("S", 3), k.get("bs", 16), k.get("nb", 8), k.get("mk", 5),
                                      k.get("runs", FAKE), k.get("nbytes", 1008), None)
+    assert f(mk=-1) == -1
+    assert f(mk=17) == -1
     assert f(bs=8) == -1
     assert f(nb=1) == -1
     assert f(S=-1) == -1
@@ -252,10 +254,11 @@ def test_token_run_list_sizes_and_argument_errors():
     assert f(runs=ctypes.c_void_p(0x1004)) == -1          # not 8-byte aligned
     assert f(nb=1 << 27, bs=32) == -1                     # slots would overflow int32
     assert f(S=0, runs=None) == 0                         # nothing to do
-    # paged_attention_decode_runs(out, q, qt, k, v, runs, runs_bytes, mt, S, H, Hkv, D, scale, bs, nb,
-    #                             kv, ks, vs, st)
+    # paged_attention_decode_runs(out, q, qt, k, v, runs, runs_bytes, slots, ctx, mt, S, H, Hkv, D,
+    #                             scale, bs, nb, kv, ks, vs, st)
     g = lambda **k: L.paged_attention_decode_runs(FAKE, FAKE, k.get("qt", 0), FAKE, FAKE,
-                                                  k.get("runs", FAKE), k.get("nbytes", 1008), 10, 3,
+                                                  k.get("runs", FAKE), k.get("nbytes", 1008),
+                                                  k.get("slots", FAKE), k.get("ctx", FAKE), 10, 3,
                                                   k.get("H", 8), 2,
                                                   k.get("D", 128), k.get("scale", 0.1), 16,
                                                   k.get("nb", 8), k.get("kv", 0), 1.0, 1.0, None)
@@ -268,3 +271,5 @@ def test_token_run_list_sizes_and_argument_errors():
     assert g(runs=None) == -1
     assert g(runs=ctypes.c_void_p(0x1004)) == -1
     assert g(nbytes=1007) == -2
+    assert g(slots=None) == -1                            # the table and its lengths go together
+    assert g(ctx=None) == -1

@@ -154,7 +154,7 @@ def test_run_list_decode_step_replays_like_eager():
         pkv.token_runs(slots, cl, bs, nb, runs=runs)
         for layer in range(L):
             pkv.paged_attention_decode_runs(out[layer], q[layer], kp[layer], vp[layer], runs, width, Hkv, bs,
-                                            nb, pkv.BF16, scale)
+                                            nb, pkv.BF16, scale, token_slots=slots, context_lens=cl)
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())

@@ -288,7 +288,7 @@ def runs_reference(slots, ctx, bs, num_blocks):
     out = []
     for s in range(slots.shape[0]):
         ent, prev = [], None
-        for t in range(max(0, min(int(ctx[s]), slots.shape[1]))):
+        for t in range(table_len(ctx[s], slots.shape[1])):
             v = int(slots[s, t])
             v = v if bs <= v < cap else bs
             if prev is not None and v >> 4 == prev >> 4 and (v & 15) > (prev & 15):
@@ -300,13 +300,22 @@ def runs_reference(slots, ctx, bs, num_blocks):
     return out
 
 
+def table_len(c, width):
+    return max(0, min(int(c), width))
+
+
+def read_counts(runs, S):
+    return runs.cpu().numpy()[:4 * S].view(np.int32).copy()
+
+
 def read_runs(runs, S, width):
     """Counts at the start of the run list, entries at its end."""
     h = runs.cpu().numpy()
     counts = h[:4 * S].view(np.int32)
     off = pkv.token_runs_bytes(S, width) - 8 * S * width
     ent = h[off:off + 8 * S * width].view(np.int32).reshape(S, width, 2)
-    return [[[int(x), int(m)] for x, m in ent[s, :counts[s]]] for s in range(S)]
+    n = [int(c) if c >= 0 else -1 - int(c) for c in counts]
+    return [[[int(x), int(m)] for x, m in ent[s, :n[s]]] for s in range(S)]
 
 
 def poison_evicted(kp, vp, tabs, slots, ctx, kv, qdt, Hkv, bs):
@@ -342,21 +351,31 @@ def test_token_runs_bit_exact(bs):
     slots[4, 20] = -7
     ctx = np.array([width, 0, 255, 1, 300, 17, 1000], np.int32)
     want = runs_reference(slots, ctx, bs, nb)
-    runs = pkv.token_runs(devi(slots), devi(ctx), bs, nb)
-    torch.cuda.synchronize()
-    got = read_runs(runs, S, width)
-    for s in range(S):
-        assert got[s] == want[s], f"sequence {s}"
+    for mk in (0, 5, 16):
+        runs = pkv.token_runs(devi(slots), devi(ctx), bs, nb, min_keys_per_entry=mk)
+        torch.cuda.synchronize()
+        got = read_runs(runs, S, width)
+        counts = read_counts(runs, S)
+        for s in range(S):
+            assert got[s] == want[s], f"sequence {s}"
+            n, c = len(want[s]), table_len(ctx[s], width)
+            marked = mk > 0 and n > 0 and c < mk * n        # fewer than mk keys per entry
+            assert counts[s] == (-1 - n if marked else n), f"sequence {s} count, min keys {mk}"
+        if mk == 16:
+            assert (counts < 0).sum() >= 3                  # the scattered tables
 
 
 @pytest.mark.parametrize("kv,qdt,bs", [(oracle.BF16, oracle.BF16, 16), (oracle.FP16, oracle.FP16, 32),
                                        (oracle.FP8, oracle.BF16, 16), (oracle.FP8, oracle.FP16, 32)])
 @pytest.mark.parametrize("H,Hkv", [(12, 2), (8, 8), (32, 2), (40, 1)])
-def test_decode_runs_fragmented(kv, qdt, bs, H, Hkv):
+@pytest.mark.parametrize("min_keys", [0, 5, 16])
+def test_decode_runs_fragmented(kv, qdt, bs, H, Hkv, min_keys):
     """Run-list decode of fragmented tables against the oracle, with NaN in
     every evicted row (read with the sub-tile, never used); and within
-    rounding of the token gather."""
-    log(f"run-list decode kv={kv} bs={bs} G={H // Hkv}")
+    rounding of the token gather.  min_keys 0: every sequence over its run
+    list; 5: the sparse ones token by token; 16: nearly all token by
+    token."""
+    log(f"run-list decode kv={kv} bs={bs} G={H // Hkv} min_keys={min_keys}")
     ks, vs = (0.02, 0.03) if kv == oracle.FP8 else (1.0, 1.0)
     lengths = [1, 17, 64, 200, 333, 50]
     tabs, kp, vp, slots, ctx, q = fragmented_case(lengths, H, Hkv, bs, kv, qdt, 0.55, 7, ks, vs)
@@ -365,10 +384,10 @@ def test_decode_runs_fragmented(kv, qdt, bs, H, Hkv):
     qt = dev16(q, qdt)
     kd, vd = torch.from_numpy(kp).to(DEV), torch.from_numpy(vp).to(DEV)
     ts, cl = devi(slots), devi(ctx)
-    runs = pkv.token_runs(ts, cl, bs, tabs.num_blocks)
+    runs = pkv.token_runs(ts, cl, bs, tabs.num_blocks, min_keys_per_entry=min_keys)
     out = torch.full_like(qt, float("nan"))
     pkv.paged_attention_decode_runs(out, qt, kd, vd, runs, slots.shape[1], Hkv, bs, tabs.num_blocks, kv,
-                                    SCALE, ks, vs)
+                                    SCALE, ks, vs, token_slots=ts, context_lens=cl)
     gat = torch.full_like(qt, float("nan"))
     pkv.paged_attention_decode_tokens(gat, qt, kd, vd, ts, cl, Hkv, bs, tabs.num_blocks, kv, SCALE, ks, vs)
     torch.cuda.synchronize()
@@ -406,7 +425,7 @@ def test_aligned_runs_equal_block_decode_bitwise(kv):
     assert mc >= 2048
     pkv.paged_attention_decode(a, q, kd, vd, devi(tabs.block_tables), cl, mc, Hkv, bs, kv, SCALE,
                                ks, vs, partition_tokens=-(-mc // bs) * bs, num_blocks=tabs.num_blocks)
-    runs = pkv.token_runs(devi(slots), cl, bs, tabs.num_blocks)
+    runs = pkv.token_runs(devi(slots), cl, bs, tabs.num_blocks, min_keys_per_entry=0)
     b = torch.full_like(q, float("nan"))
     pkv.paged_attention_decode_runs(b, q, kd, vd, runs, mc, Hkv, bs, tabs.num_blocks, kv, SCALE, ks, vs)
     torch.cuda.synchronize()
@@ -429,19 +448,21 @@ def test_decode_runs_repeated_slots_and_empty():
     want = oracle.paged_decode_tokens(q, qdt, kp, vp, kv, slots, ctx, Hkv, bs, SCALE)
     qt = dev16(q, qdt)
     kd, vd = torch.from_numpy(kp).to(DEV), torch.from_numpy(vp).to(DEV)
-    runs = pkv.token_runs(devi(slots), devi(ctx), bs, tabs.num_blocks)
+    ts, cl = devi(slots), devi(ctx)
+    runs = pkv.token_runs(ts, cl, bs, tabs.num_blocks)
     out = torch.full_like(qt, float("nan"))
     pkv.paged_attention_decode_runs(out, qt, kd, vd, runs, slots.shape[1], Hkv, bs, tabs.num_blocks, kv,
-                                    SCALE)
+                                    SCALE, token_slots=ts, context_lens=cl)
     torch.cuda.synchronize()
     got = out.float().cpu().numpy().astype(np.float64)
     assert np.all(got[1] == 0)
     assert np.abs(got - want).max() <= TOL[kv]
     # the same buffer, a narrower table of the first sequence only
     narrow = np.ascontiguousarray(slots[:1, :ctx[0]])
-    pkv.token_runs(devi(narrow), devi(ctx[:1]), bs, tabs.num_blocks, runs=runs)
+    nt, nc = devi(narrow), devi(ctx[:1])
+    pkv.token_runs(nt, nc, bs, tabs.num_blocks, runs=runs)
     one = torch.full_like(qt[:1], float("nan"))
     pkv.paged_attention_decode_runs(one, qt[:1].contiguous(), kd, vd, runs, narrow.shape[1], Hkv, bs,
-                                    tabs.num_blocks, kv, SCALE)
+                                    tabs.num_blocks, kv, SCALE, token_slots=nt, context_lens=nc)
     torch.cuda.synchronize()
     assert torch.equal(one[0], out[0])
