@@ -1,6 +1,7 @@
 """GPU: the usage example in README.md runs as written (pool, block
-manager, prefill, one decode step with the fused cache write), and its
-decode output is finite."""
+manager, prefill, one decode step with the fused cache write, a token-level
+eviction and a decode through the token table), and its last decode output
+is finite."""
 import os
 import re
 
