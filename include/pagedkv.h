@@ -658,9 +658,12 @@ int32_t paged_attention_decode_tokens(void* out, const void* q, int32_t q_dtype,
  *   num_seqs, max_tokens_per_seq, block_size and num_blocks; PKV_ERR_SIZE if
  *   runs_bytes < pkv_token_runs_bytes), and of the sequences the list marked
  *   for the gather token by token through token_slots / context_lens (the
- *   table the list was built from; a second launch).  Pass both as NULL only
- *   for a list built with min_keys_per_entry = 0 (marked sequences are then
- *   left unwritten).  Otherwise as
+ *   table the list was built from; a second launch, in which the workgroups
+ *   of unmarked sequences leave at once: 4-9 us on the Qwen2.5-7B decode
+ *   shape when none is marked).  Pass both as NULL only for a list built
+ *   with min_keys_per_entry = 0 (marked sequences are then left unwritten):
+ *   a caller that knows its survivors are dense skips the second launch
+ *   that way.  Otherwise as
  *   paged_attention_decode_tokens, whose result it equals within rounding
  *   (the softmax visits the same keys in sub-tile units), and for a
  *   block-aligned table the block-table decode's on one partition with the
