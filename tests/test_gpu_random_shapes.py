@@ -1,0 +1,143 @@
+"""GPU: seeded random shapes against the oracle.
+
+Each case draws a configuration the fixed-shape tests may not hit together:
+kv dtype (bf16, fp16, fp8 with a bf16 or fp16 query), block size 16 or 32,
+1-8 kv heads, group sizes from MHA to wide GQA / MQA (up to 33 query heads
+per kv head), 1-11 sequences with lengths at block boundaries, zero-length
+and random ones, and an automatic or explicit partition length.  On the
+same NaN-poisoned pools it checks, against the fp64 oracle:
+  - the decode in its three forms (default, four-wave, persistent);
+  - the decode with each sequence's new token written inside the launch
+    (the pool bit for bit against the oracle's reshape_and_cache);
+  - multi-token causal attention of a random trailing chunk per sequence;
+  - the token-table decode over run lists (and the gather for sparse
+    sequences) after a random eviction.
+Cases are small enough for the oracle to finish in well under a second.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests import pools
+
+pkv = pytest.importorskip("paged_kv_cache_51_amd")
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+D = 128
+TOL = {oracle.BF16: 2e-2, oracle.FP16: 2e-2, oracle.FP8: 6e-2}
+PKV_DT = {oracle.BF16: pkv.BF16, oracle.FP16: pkv.FP16, oracle.FP8: pkv.FP8_E4M3}
+
+
+def log(*a):
+    print(*a, flush=True)
+
+
+def dev16(bits, dtype):
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.view(torch.bfloat16 if dtype == oracle.BF16 else torch.float16).to(DEV)
+
+
+def devi(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(DEV)
+
+
+def draw_case(seed):
+    r = np.random.default_rng(7000 + seed)
+    kv = [oracle.BF16, oracle.FP16, oracle.FP8][r.integers(3)]
+    qdt = kv if kv != oracle.FP8 else [oracle.BF16, oracle.FP16][r.integers(2)]
+    bs = int(r.choice([16, 32]))
+    G = int(r.choice([1, 2, 3, 5, 6, 7, 8, 12, 16, 20, 33]))
+    Hkv = int(r.choice([h for h in (1, 2, 4, 8) if h * G <= 66]))
+    S = int(r.integers(1, 12))
+    pick = [1, bs - 1, bs, bs + 1, 2 * bs, 3 * bs - 1] + list(r.integers(1, 600, 6))
+    lengths = [int(r.choice(pick)) for _ in range(S)]
+    part = int(r.choice([0, 0, bs, 4 * bs, 16 * bs]))
+    ks, vs = (float(np.float32(r.uniform(0.01, 0.05))), float(np.float32(r.uniform(0.01, 0.05)))) \
+        if kv == oracle.FP8 else (1.0, 1.0)
+    scale = float(np.float32(r.choice([1.0 / np.sqrt(D), 0.05, 0.2])))
+    return r, kv, qdt, bs, G, Hkv, lengths, part, ks, vs, scale
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_shape(seed):
+    r, kv, qdt, bs, G, Hkv, lengths, part, ks, vs, scale = draw_case(seed)
+    H, S = G * Hkv, len(lengths)
+    log(f"case {seed}: kv={kv} q={qdt} bs={bs} G={G} Hkv={Hkv} S={S} part={part} lengths={lengths}")
+    # contexts of the decode count the token the step appends (position c - 1)
+    tabs = workloads.build_tables(lengths, bs, np.random.default_rng(100 + seed))
+    nb = tabs.num_blocks
+    ctx = tabs.context_lens
+    hist = ctx - 1                                   # tokens already in the cache
+    kb = [workloads.normal_bits(r, (int(c), Hkv, D), qdt) for c in ctx]
+    vb = [workloads.normal_bits(r, (int(c), Hkv, D), qdt) for c in ctx]
+    kp_hist, vp_hist = pools.write_contiguous([k[:-1] for k in kb], [v[:-1] for v in vb],
+                                              tabs.block_tables, hist, Hkv, D, bs, nb, kv, qdt, ks, vs)
+    nk = np.stack([k[-1] for k in kb])
+    nv = np.stack([v[-1] for v in vb])
+    slots = oracle.decode_slots(tabs.block_tables, ctx, bs)
+    kp, vp = oracle.reshape_and_cache(nk, nv, qdt, kp_hist, vp_hist, slots, bs, nb, kv, ks, vs)
+    q = workloads.normal_bits(r, (S, H, D), qdt)
+    want = oracle.paged_decode(q, qdt, kp, vp, kv, tabs.block_tables, ctx, Hkv, bs, scale, ks, vs)
+    tol = TOL[kv]
+    qt = dev16(q, qdt)
+    bt, cl = devi(tabs.block_tables), devi(ctx)
+    mc = int(ctx.max())
+    kd, vd = torch.from_numpy(kp).to(DEV), torch.from_numpy(vp).to(DEV)
+    kvt = PKV_DT[kv]
+
+    # decode, three forms
+    for impl in (pkv.IMPL_AUTO, pkv.IMPL_MFMA, pkv.IMPL_MFMA_PERSISTENT):
+        out = torch.full_like(qt, float("nan"))
+        pkv.paged_attention_decode(out, qt, kd, vd, bt, cl, mc, Hkv, bs, kvt, scale, ks, vs,
+                                   partition_tokens=part, impl=impl, num_blocks=nb)
+        torch.cuda.synchronize()
+        err = float(np.abs(out.float().cpu().numpy() - want).max())
+        assert err <= tol, f"decode impl {impl}: max-abs {err}"
+
+    # the same step with the new tokens written by the decode launch
+    ka, va = torch.from_numpy(kp_hist).to(DEV), torch.from_numpy(vp_hist).to(DEV)
+    out = torch.full_like(qt, float("nan"))
+    pkv.paged_attention_decode_append(out, qt, dev16(nk, qdt), dev16(nv, qdt), ka, va, bt, cl, mc, Hkv, bs,
+                                      kvt, scale, ks, vs, partition_tokens=part, num_blocks=nb)
+    torch.cuda.synchronize()
+    assert np.array_equal(ka.cpu().numpy(), kp) and np.array_equal(va.cpu().numpy(), vp), "append pools"
+    err = float(np.abs(out.float().cpu().numpy() - want).max())
+    assert err <= tol, f"decode with append: max-abs {err}"
+
+    # multi-token attention: a random trailing chunk of each sequence
+    qlen = [int(r.integers(1, min(int(c), 40) + 1)) for c in ctx]
+    qs = np.concatenate([[0], np.cumsum(qlen)]).astype(np.int32)
+    qp = workloads.normal_bits(r, (int(qs[-1]), H, D), qdt)
+    want_p = oracle.paged_prefill(qp, qdt, kp, vp, kv, tabs.block_tables, ctx, qs, Hkv, bs, scale, ks, vs)
+    qpt = dev16(qp, qdt)
+    outp = torch.full_like(qpt, float("nan"))
+    pkv.paged_attention_prefill(outp, qpt, kd, vd, bt, cl, devi(qs), max(qlen), mc, Hkv, bs, kvt, scale,
+                                ks, vs, num_blocks=nb)
+    torch.cuda.synchronize()
+    err = float(np.abs(outp.float().cpu().numpy() - want_p).max())
+    assert err <= tol, f"multi-token: max-abs {err}"
+
+    # token table after a random eviction, over run lists (sparse sequences
+    # by the gather)
+    keep = float(r.choice([0.1, 0.4, 0.7, 1.0]))
+    width = mc
+    table = np.zeros((S, width), np.int32)
+    tlen = np.zeros(S, np.int32)
+    for s, c in enumerate(ctx):
+        full = [oracle.slot_of_position(tabs.block_tables[s], p, bs) for p in range(int(c))]
+        kept = [x for x in full if r.random() < keep] or full[-1:]
+        table[s, :len(kept)] = kept
+        tlen[s] = len(kept)
+    want_t = oracle.paged_decode_tokens(q, qdt, kp, vp, kv, table, tlen, Hkv, bs, scale, ks, vs)
+    tt, tl = devi(table), devi(tlen)
+    runs = pkv.token_runs(tt, tl, bs, nb)
+    outt = torch.full_like(qt, float("nan"))
+    pkv.paged_attention_decode_runs(outt, qt, kd, vd, runs, width, Hkv, bs, nb, kvt, scale, ks, vs,
+                                    token_slots=tt, context_lens=tl)
+    torch.cuda.synchronize()
+    err = float(np.abs(outt.float().cpu().numpy() - want_t).max())
+    assert err <= tol, f"token table (keep {keep}): max-abs {err}"
