@@ -3,8 +3,9 @@
 Each case draws a configuration the fixed-shape tests may not hit together:
 kv dtype (bf16, fp16, fp8 with a bf16 or fp16 query), block size 16 or 32,
 1-8 kv heads, group sizes from MHA to wide GQA / MQA (up to 33 query heads
-per kv head), 1-11 sequences with lengths at block boundaries, zero-length
-and random ones, and an automatic or explicit partition length.  On the
+per kv head), 1-11 sequences with lengths at block boundaries (from a
+single token) and random ones, and an automatic or explicit partition
+length.  On the
 same NaN-poisoned pools it checks, against the fp64 oracle:
   - the decode in its three forms (default, four-wave, persistent);
   - the decode with each sequence's new token written inside the launch
@@ -141,3 +142,43 @@ def test_random_shape(seed):
     torch.cuda.synchronize()
     err = float(np.abs(outt.float().cpu().numpy() - want_t).max())
     assert err <= tol, f"token table (keep {keep}): max-abs {err}"
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_random_shape_head_dims(seed):
+    """head_dim 64 and 256 (the cache write and the block-table decode are
+    built for them): random configurations as above, decode in its three
+    forms and with the fused cache write."""
+    r, kv, qdt, bs, G, Hkv, lengths, part, ks, vs, scale = draw_case(100 + seed)
+    d = int(r.choice([64, 256]))
+    H, S = G * Hkv, len(lengths)
+    log(f"case {seed}: d={d} kv={kv} q={qdt} bs={bs} G={G} Hkv={Hkv} S={S} part={part} lengths={lengths}")
+    tabs = workloads.build_tables(lengths, bs, np.random.default_rng(200 + seed))
+    nb, ctx = tabs.num_blocks, tabs.context_lens
+    kb = [workloads.normal_bits(r, (int(c), Hkv, d), qdt) for c in ctx]
+    vb = [workloads.normal_bits(r, (int(c), Hkv, d), qdt) for c in ctx]
+    kp_hist, vp_hist = pools.write_contiguous([k[:-1] for k in kb], [v[:-1] for v in vb],
+                                              tabs.block_tables, ctx - 1, Hkv, d, bs, nb, kv, qdt, ks, vs)
+    nk, nv = np.stack([k[-1] for k in kb]), np.stack([v[-1] for v in vb])
+    slots = oracle.decode_slots(tabs.block_tables, ctx, bs)
+    kp, vp = oracle.reshape_and_cache(nk, nv, qdt, kp_hist, vp_hist, slots, bs, nb, kv, ks, vs)
+    q = workloads.normal_bits(r, (S, H, d), qdt)
+    want = oracle.paged_decode(q, qdt, kp, vp, kv, tabs.block_tables, ctx, Hkv, bs, scale, ks, vs)
+    qt, bt, cl, mc = dev16(q, qdt), devi(tabs.block_tables), devi(ctx), int(ctx.max())
+    kd, vd = torch.from_numpy(kp).to(DEV), torch.from_numpy(vp).to(DEV)
+    kvt = PKV_DT[kv]
+    for impl in (pkv.IMPL_AUTO, pkv.IMPL_MFMA, pkv.IMPL_MFMA_PERSISTENT):
+        out = torch.full_like(qt, float("nan"))
+        pkv.paged_attention_decode(out, qt, kd, vd, bt, cl, mc, Hkv, bs, kvt, scale, ks, vs,
+                                   partition_tokens=part, impl=impl, num_blocks=nb)
+        torch.cuda.synchronize()
+        err = float(np.abs(out.float().cpu().numpy() - want).max())
+        assert err <= TOL[kv], f"decode impl {impl}: max-abs {err}"
+    ka, va = torch.from_numpy(kp_hist).to(DEV), torch.from_numpy(vp_hist).to(DEV)
+    out = torch.full_like(qt, float("nan"))
+    pkv.paged_attention_decode_append(out, qt, dev16(nk, qdt), dev16(nv, qdt), ka, va, bt, cl, mc, Hkv, bs,
+                                      kvt, scale, ks, vs, partition_tokens=part, num_blocks=nb)
+    torch.cuda.synchronize()
+    assert np.array_equal(ka.cpu().numpy(), kp) and np.array_equal(va.cpu().numpy(), vp), "append pools"
+    err = float(np.abs(out.float().cpu().numpy() - want).max())
+    assert err <= TOL[kv], f"decode with append: max-abs {err}"
