@@ -209,3 +209,59 @@ def test_prefill_llama7b_8x512_full_size():
 
 def test_prefill_qwen7b_256x4_full_size():
     run_prefill_config("qwen7b", 4, 256, n_random=3)
+
+
+@pytest.mark.parametrize("keep", [0.5, 0.1])
+def test_vtoken_qwen7b_full_size(keep):
+    """The bench's token-table workload: the 7B shape, one layer, every
+    sequence keeps a random fraction of its context through the block
+    manager's eviction; decode over run lists (half kept) or by the gather
+    the run lists hand sparse sequences to (a tenth kept), every output
+    finite, sampled sequences against the oracle."""
+    cfg, tabs, _, _ = workloads.make("qwen7b")
+    kv, qdt = cfg.kv_dtype, cfg.q_dtype
+    S, H, Hkv, D, bs = cfg.num_seqs, cfg.num_heads, cfg.num_kv_heads, cfg.head_dim, cfg.block_size
+    ctx = tabs.context_lens.astype(np.int64)
+    nb = tabs.num_blocks
+    bm = pkv.BlockManager(nb, bs)
+    for s in range(S):
+        bm.add_sequence(s, [0] * int(ctx[s]))
+    r = np.random.default_rng(5)
+    for s in range(S):
+        k = r.random(int(ctx[s])) < keep
+        k[-1] = True
+        bm.evict_tokens(s, k.tolist())
+    width = int(ctx.max())
+    n_keep = np.array([bm.num_tokens(s) for s in range(S)], np.int32)
+    table = np.array([bm.token_slots(s, width) for s in range(S)], np.int32)
+    log(f"vtoken keep {keep}: {int(n_keep.sum())} of {int(ctx.sum())} tokens")
+    nbytes = pkv.layer_pool_bytes(nb, Hkv, D, bs, kv)
+    kpool = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    vpool = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    workloads.device_fill_normal(kpool, kv, 1300)
+    workloads.device_fill_normal(vpool, kv, 2300)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(9)
+    q = torch.randn(S, H, D, generator=g, device=DEV).to(torch.bfloat16)
+    tt = torch.from_numpy(table).to(DEV)
+    tl = torch.from_numpy(n_keep).to(DEV)
+    scale = float(np.float32(1.0 / np.sqrt(D)))
+    runs = pkv.token_runs(tt, tl, bs, nb)
+    out = torch.full_like(q, float("nan"))
+    pkv.paged_attention_decode_runs(out, q, kpool, vpool, runs, width, Hkv, bs, nb, kv, scale,
+                                    token_slots=tt, context_lens=tl)
+    torch.cuda.synchronize()
+    counts = runs[:4 * S].view(torch.int32).cpu().numpy()
+    marked = int((counts < 0).sum())
+    log(f"  {marked} of {S} sequences by the gather")
+    assert (marked == 0) if keep == 0.5 else (marked == S)
+    got = out.float().cpu().numpy().astype(np.float64)
+    assert np.isfinite(got).all(), "non-finite output"
+    kp, vp = kpool.cpu().numpy(), vpool.cpu().numpy()
+    qb = q.cpu().view(torch.int16).numpy().view(np.uint16)
+    idx = np.array(sorted({int(np.argmax(n_keep)), int(np.argmin(n_keep))} |
+                          set(int(i) for i in r.choice(S, 10, replace=False))))
+    want = oracle.paged_decode_tokens(qb[idx], qdt, kp, vp, kv, table[idx], n_keep[idx], Hkv, bs, scale)
+    err = np.abs(got[idx] - want)
+    log(f"  checked {len(idx)} of {S} seqs: max-abs {err.max():.3e}")
+    assert err.max() <= TOL[kv]
