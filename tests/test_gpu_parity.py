@@ -1,6 +1,6 @@
 """GPU parity: the HIP path through the C ABI against the CPU oracle.
 
-Bars (set for this build from the method's arithmetic): slot mapping and
+Bars (derived from the method's arithmetic): slot mapping and
 reshape_and_cache bit-exact (whole-pool byte compare); decode attention
 max-abs error <= 2e-2 for bf16/fp16 KV and <= 6e-2 for fp8 KV, against the
 fp64 oracle reading the same pool.  Exact invariants of the paging scheme

@@ -4,7 +4,7 @@ This module only draws random numbers and lays out who owns which physical
 block; it holds none of the attention, cache-write, slot or fp8 arithmetic.
 Both the HIP path and the CPU oracle receive what it produces.
 
-Workload shapes are the five named configurations of the task (the pages'
+Workload shapes are five named configurations (the pages'
 model shapes: Qwen2.5-1.5B/7B/72B from "LLM inference basics and vLLM
 internals" §2's table, and the Llama-2-7B MHA shape from the vToken page's
 "KV cache basics").  The pages measure on ShareGPT/Alpaca request traces that
