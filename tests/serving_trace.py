@@ -1,0 +1,290 @@
+"""A random serving trace driven through the host block manager.
+
+The block manager (prefix cache on) serves a random mix of requests — new
+prompts, half of them sharing a prefix with an earlier prompt ("LLM
+inference basics and vLLM internals" §5: whole-block prefix hits), decode
+steps (appends, with copy-on-write after forks, §4), forks, frees, and token
+evictions followed by a repack (the "vToken" page).  A backend moves the
+data the manager's answers call for — it writes only the tokens a prompt did
+not hit, runs the copy-on-write copies before the step's writes, repacks
+evicted sequences — and attends.  After every decode step, and after each
+eviction and repack, every output is compared with contiguous textbook
+attention over that sequence's own K / V in logical order (oracle/brute.py),
+so tables, hits, copies, writes, repacks and the attention are checked
+together.
+
+A token's K / V is a fixed function of the tokens up to it (a chained key
+seeds its values), so a prompt that hits cached blocks finds exactly the
+values it would have written itself.
+
+Two backends: OracleBackend (numpy pools and the oracle's data movement and
+attention, for the host logic on the CPU) and KernelBackend (the library's
+kernels on the GPU).
+"""
+import numpy as np
+
+import oracle
+from oracle import brute
+import workloads
+
+D, HKV, H, BS, L, NB = 128, 2, 8, 16, 2, 700
+SCALE = float(np.float32(1.0 / np.sqrt(D)))
+NAN_BF16 = 0x7FC0
+MAX_LIVE = 9
+
+
+def bf16_f64(bits):
+    """Exact values of bf16 bits (the upper half of an fp32)."""
+    return (np.asarray(bits).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def chain(key, tok):
+    return hash((key, tok)) & ((1 << 62) - 1)
+
+
+class Truth:
+    """The K / V of a token, a fixed function of its chained key: bits
+    ([L][H_kv][d] bf16) and their exact values."""
+
+    def __init__(self):
+        self.cache = {}
+
+    def kv(self, key):
+        if key not in self.cache:
+            r = np.random.default_rng(key)
+            kb = workloads.normal_bits(r, (L, HKV, D), oracle.BF16)
+            vb = workloads.normal_bits(r, (L, HKV, D), oracle.BF16)
+            self.cache[key] = (kb, vb, bf16_f64(kb), bf16_f64(vb))
+        return self.cache[key]
+
+
+class OracleBackend:
+    """Pools as numpy bytes, moved and read by the oracle."""
+
+    tol = 1e-9
+
+    def __init__(self):
+        n = oracle.layer_pool_bytes(NB, HKV, D, BS, oracle.BF16)
+        poison = np.full(n // 2, NAN_BF16, np.uint16).view(np.uint8)
+        self.k = [poison.copy() for _ in range(L)]
+        self.v = [poison.copy() for _ in range(L)]
+
+    def write(self, layer, kb, vb, slots):
+        self.k[layer], self.v[layer] = oracle.reshape_and_cache(
+            kb, vb, oracle.BF16, self.k[layer], self.v[layer], np.asarray(slots, np.int64), BS, NB, oracle.BF16)
+
+    def copy_blocks(self, pairs):
+        moves = [(s * BS + r, d * BS + r) for s, d in pairs for r in range(BS)]
+        self.k, self.v = oracle.move_tokens(self.k, self.v, moves, HKV, D, BS, oracle.BF16)
+
+    def repack(self, tiles):
+        moves = [(src, blk * BS + r) for blk, srcs in tiles for r, src in enumerate(srcs)]
+        self.k, self.v = oracle.move_tokens(self.k, self.v, moves, HKV, D, BS, oracle.BF16)
+
+    def decode(self, layer, q, tables, lens):
+        return oracle.paged_decode(q, oracle.BF16, self.k[layer], self.v[layer], oracle.BF16,
+                                   np.asarray(tables, np.int32), np.asarray(lens, np.int32), HKV, BS, SCALE)
+
+    def decode_tokens(self, layer, q, table, lens):
+        return {"table": oracle.paged_decode_tokens(q, oracle.BF16, self.k[layer], self.v[layer], oracle.BF16,
+                                                    np.asarray(table, np.int32), np.asarray(lens, np.int32),
+                                                    HKV, BS, SCALE)}
+
+
+class KernelBackend:
+    """Pools on the GPU, moved and read by the library's kernels (every call
+    through the C ABI; outputs start as NaN)."""
+
+    tol = 2e-2
+
+    def __init__(self, pkv, torch):
+        self.pkv, self.torch = pkv, torch
+        n = pkv.layer_pool_bytes(NB, HKV, D, BS, pkv.BF16)
+        mk = lambda: torch.full((n // 2,), NAN_BF16, dtype=torch.int16, device="cuda").view(torch.uint8)
+        self.k = [mk() for _ in range(L)]
+        self.v = [mk() for _ in range(L)]
+
+    def _bf16(self, bits):
+        t = self.torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+        return t.view(self.torch.bfloat16).to("cuda")
+
+    def _i32(self, a):
+        return self.torch.tensor(np.asarray(a, np.int32), dtype=self.torch.int32, device="cuda")
+
+    def _out(self, S):
+        return self.torch.full((S, H, D), float("nan"), dtype=self.torch.bfloat16, device="cuda")
+
+    def _host(self, out):
+        self.torch.cuda.synchronize()
+        return out.float().cpu().numpy().astype(np.float64)
+
+    def write(self, layer, kb, vb, slots):
+        self.pkv.reshape_and_cache(self._bf16(kb), self._bf16(vb), self.k[layer], self.v[layer],
+                                   self._i32(slots), BS, NB, self.pkv.BF16)
+
+    def copy_blocks(self, pairs):
+        self.pkv.copy_blocks(self.k, self.v, self._i32(pairs), NB, HKV, D, BS, self.pkv.BF16)
+
+    def repack(self, tiles):
+        flat = self._i32([[blk] + list(srcs) for blk, srcs in tiles])
+        self.pkv.repack_blocks(self.k, self.v, flat, self._i32([0, len(tiles)]), NB, HKV, D, BS, self.pkv.BF16)
+
+    def decode(self, layer, q, tables, lens):
+        out = self._out(len(lens))
+        cl = self._i32(lens)
+        self.pkv.paged_attention_decode(out, self._bf16(q), self.k[layer], self.v[layer], self._i32(tables), cl,
+                                        int(max(lens)), HKV, BS, self.pkv.BF16, SCALE, num_blocks=NB,
+                                        partition_tokens=64)
+        return self._host(out)
+
+    def decode_tokens(self, layer, q, table, lens):
+        pkv = self.pkv
+        tt, cl, qt = self._i32(table), self._i32(lens), self._bf16(q)
+        width = tt.shape[1]
+        res = {}
+        out = self._out(len(lens))
+        pkv.paged_attention_decode_tokens(out, qt, self.k[layer], self.v[layer], tt, cl, HKV, BS, NB, pkv.BF16,
+                                          SCALE)
+        res["gather"] = self._host(out)
+        for min_keys in (0, pkv.RUNS_MIN_KEYS):
+            runs = pkv.token_runs(tt, cl, BS, NB, min_keys_per_entry=min_keys)
+            out = self._out(len(lens))
+            pkv.paged_attention_decode_runs(out, qt, self.k[layer], self.v[layer], runs, width, HKV, BS, NB,
+                                            pkv.BF16, SCALE, token_slots=tt, context_lens=cl)
+            res[f"runs (min keys {min_keys})"] = self._host(out)
+        return res
+
+
+def check(got, q, seqs, sids, layer, tol, label):
+    """Each sequence's output against contiguous attention over its own
+    tokens' K / V in logical order."""
+    for i, sid in enumerate(sids):
+        kv = seqs[sid]["kv"]
+        k = np.stack([t[2][layer] for t in kv])
+        v = np.stack([t[3][layer] for t in kv])
+        want = brute.attention(bf16_f64(q[i]), k, v, SCALE)
+        err = float(np.abs(got[i] - want).max())
+        assert err <= tol, f"{label} layer {layer}: sequence {sid} ({len(kv)} tokens) max-abs {err}"
+
+
+def run_trace(seed, pkv, dev, num_ops=70, log=print):
+    """Drive num_ops random requests; returns counts of what ran."""
+    r = np.random.default_rng(seed)
+    truth = Truth()
+    bm = pkv.BlockManager(NB, BS, prefix_caching=True)
+    seqs = {}                 # sid -> {"keys": chained key per token, "kv": Truth.kv per token, "evicted"}
+    prompts = []              # prompts seen so far (prefix sources)
+    next_sid = 0
+    stats = dict(prompts=0, hit_tokens=0, steps=0, cow=0, forks=0, frees=0, evictions=0, repacked_tiles=0)
+
+    def write(triples):
+        """(sid, position, slot) triples: their K / V into every layer."""
+        if not triples:
+            return
+        slots = [sl for _, _, sl in triples]
+        for layer in range(L):
+            kb = np.stack([seqs[s]["kv"][p][0][layer] for s, p, _ in triples])
+            vb = np.stack([seqs[s]["kv"][p][1][layer] for s, p, _ in triples])
+            dev.write(layer, kb, vb, slots)
+
+    def decode_all(sids, label):
+        maxb = max(-(-bm.num_tokens(s) // BS) for s in sids)
+        tables = [bm.block_table(s, maxb) for s in sids]
+        lens = [bm.num_tokens(s) for s in sids]
+        assert lens == [len(seqs[s]["kv"]) for s in sids]
+        for layer in range(L):
+            q = workloads.normal_bits(r, (len(sids), H, D), oracle.BF16)
+            check(dev.decode(layer, q, tables, lens), q, seqs, sids, layer, dev.tol, label)
+
+    for op_i in range(num_ops):
+        live = list(seqs)
+        growable = [s for s in live if not seqs[s]["evicted"]]
+        u = r.random()
+        if u < 0.3 or not live:
+            if len(live) >= MAX_LIVE:
+                continue
+            n = int(r.integers(20, 260))
+            if prompts and r.random() < 0.5:
+                src = prompts[int(r.integers(len(prompts)))]
+                k = int(r.integers(1, len(src) + 1))
+                toks = list(src[:k]) + [int(x) for x in r.integers(0, 1000, max(0, n - k))]
+            else:
+                toks = [int(x) for x in r.integers(0, 1000, n)]
+            sid = next_sid
+            next_sid += 1
+            hit = bm.add_sequence(sid, toks)
+            assert hit % BS == 0 and 0 <= hit <= len(toks)
+            keys, key = [], seed
+            for t in toks:
+                key = chain(key, t)
+                keys.append(key)
+            seqs[sid] = {"keys": keys, "kv": [truth.kv(kk) for kk in keys], "evicted": False}
+            prompts.append(toks)
+            write([(sid, hit + i, sl) for i, sl in enumerate(bm.slots(sid, hit, len(toks) - hit))])
+            bm.mark_computed(sid, len(toks))
+            decode_all([sid], f"op {op_i} prompt ({hit} of {len(toks)} tokens hit)")
+            stats["prompts"] += 1
+            stats["hit_tokens"] += hit
+        elif u < 0.65 and growable:
+            # one decode step for a random subset: copy-on-write copies, then
+            # the new tokens' K / V, then attention
+            batch = sorted(set(int(x) for x in r.choice(growable, int(r.integers(1, len(growable) + 1)))))
+            pairs, writes = [], []
+            for sid in batch:
+                tok = int(r.integers(0, 1000))
+                slot, src, dst = bm.append_token(sid, tok)
+                s = seqs[sid]
+                key = chain(s["keys"][-1], tok)
+                s["keys"].append(key)
+                s["kv"].append(truth.kv(key))
+                if src >= 0:
+                    pairs.append((src, dst))
+                writes.append((sid, len(s["kv"]) - 1, slot))
+            if pairs:
+                dev.copy_blocks(pairs)
+                stats["cow"] += len(pairs)
+            write(writes)
+            decode_all(batch, f"op {op_i} decode step")
+            stats["steps"] += 1
+        elif u < 0.75 and growable:
+            parent = int(r.choice(growable))
+            child = next_sid
+            next_sid += 1
+            bm.fork(parent, child)
+            p = seqs[parent]
+            seqs[child] = {"keys": list(p["keys"]), "kv": list(p["kv"]), "evicted": False}
+            stats["forks"] += 1
+        elif u < 0.85 and live:
+            sid = int(r.choice(live))
+            bm.free_sequence(sid)
+            del seqs[sid]
+            stats["frees"] += 1
+        else:
+            # drop about half of a sequence's tokens (it must own its blocks
+            # alone), attend through the token table, repack, attend through
+            # the block table
+            alone = [s for s in growable
+                     if all(bm.ref_count(b) == 1 for b in bm.block_table(s, -(-bm.num_tokens(s) // BS)))]
+            if not alone:
+                continue
+            sid = int(r.choice(alone))
+            s = seqs[sid]
+            keep = [bool(x) for x in (r.random(len(s["kv"])) < float(r.choice([0.2, 0.5, 0.9])))]
+            keep[-1] = True
+            bm.evict_tokens(sid, keep)
+            s["kv"] = [kv for kv, k in zip(s["kv"], keep) if k]
+            s["keys"] = [kk for kk, k in zip(s["keys"], keep) if k]
+            m = len(s["kv"])
+            table = [bm.token_slots(sid, m)]
+            for layer in range(L):
+                q = workloads.normal_bits(r, (1, H, D), oracle.BF16)
+                for path, got in dev.decode_tokens(layer, q, table, [m]).items():
+                    check(got, q, seqs, [sid], layer, dev.tol, f"op {op_i} evicted, {path}")
+            tiles = bm.repack_tiles(sid)
+            if tiles:
+                dev.repack(tiles)
+            stats["repacked_tiles"] += len(tiles)
+            decode_all([sid], f"op {op_i} after repack")
+            stats["evictions"] += 1
+    log(f"seed {seed}: {stats}")
+    return stats
