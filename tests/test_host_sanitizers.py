@@ -1,7 +1,8 @@
 """The library's host code under AddressSanitizer and
 UndefinedBehaviorSanitizer, on the CPU: the block manager (free queues,
 reference counts, prefix-cache hashes, token tables) and the argument
-checks and size queries of every entry point.  A sanitized copy of the
+checks and size queries of every entry point, and random serving traces
+through the block manager.  A sanitized copy of the
 library is built in a temporary directory (host code instrumented, device
 code as usual) and the ABI and block-manager suites run against it in a
 child process with the ASan runtime preloaded; any report fails the test."""
@@ -28,7 +29,8 @@ def test_abi_and_block_manager_under_asan_ubsan(tmp_path):
         "UBSAN_OPTIONS": "print_stacktrace=1",
     })
     r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-p", "no:cacheprovider",
-                        "tests/test_abi.py", "tests/test_block_manager.py"],
+                        "tests/test_abi.py", "tests/test_block_manager.py",
+                        "tests/test_serving_trace_host.py"],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=900)
     out = r.stdout + r.stderr
     assert "AddressSanitizer" not in out and "runtime error:" not in out, out[-4000:]
