@@ -27,10 +27,23 @@ import oracle
 from oracle import brute
 import workloads
 
-D, HKV, H, BS, L, NB = 128, 2, 8, 16, 2, 700
+D, HKV, H, L, NB = 128, 2, 8, 2, 700
 SCALE = float(np.float32(1.0 / np.sqrt(D)))
 NAN_BF16 = 0x7FC0
+NAN_E4M3 = 0x7F
 MAX_LIVE = 9
+
+
+class Cfg:
+    """Pool block size and kv dtype (bf16, or fp8 e4m3 written from bf16
+    with per-tensor scales); queries are bf16."""
+
+    def __init__(self, block_size=16, kv_dtype=oracle.BF16, k_scale=1.0, v_scale=1.0):
+        self.bs, self.kv = block_size, kv_dtype
+        self.ks, self.vs = float(np.float32(k_scale)), float(np.float32(v_scale))
+
+    def __repr__(self):
+        return f"bs={self.bs} kv={'fp8' if self.kv == oracle.FP8 else 'bf16'}"
 
 
 def bf16_f64(bits):
@@ -42,11 +55,24 @@ def chain(key, tok):
     return hash((key, tok)) & ((1 << 62) - 1)
 
 
-class Truth:
-    """The K / V of a token, a fixed function of its chained key: bits
-    ([L][H_kv][d] bf16) and their exact values."""
+def stored_values(bits, kv, scale):
+    """What the pool holds for bf16 source bits, as exact values: the bf16
+    values, or the fp8 e4m3 code of fp32(x) * fp32(1 / scale) (the oracle's
+    encoder) decoded and times the scale."""
+    x = bf16_f64(bits)
+    if kv == oracle.BF16:
+        return x
+    inv = np.float32(1.0) / np.float32(scale)
+    codes = oracle.e4m3_encode(x.astype(np.float32) * inv)
+    return oracle.e4m3_table()[codes.astype(np.int64)] * scale
 
-    def __init__(self):
+
+class Truth:
+    """The K / V of a token, a fixed function of its chained key: source
+    bits ([L][H_kv][d] bf16) and the exact values the pool holds."""
+
+    def __init__(self, cfg):
+        self.cfg = cfg
         self.cache = {}
 
     def kv(self, key):
@@ -54,55 +80,65 @@ class Truth:
             r = np.random.default_rng(key)
             kb = workloads.normal_bits(r, (L, HKV, D), oracle.BF16)
             vb = workloads.normal_bits(r, (L, HKV, D), oracle.BF16)
-            self.cache[key] = (kb, vb, bf16_f64(kb), bf16_f64(vb))
+            c = self.cfg
+            self.cache[key] = (kb, vb, stored_values(kb, c.kv, c.ks), stored_values(vb, c.kv, c.vs))
         return self.cache[key]
+
+
+def poisoned_pool(cfg):
+    n = oracle.layer_pool_bytes(NB, HKV, D, cfg.bs, cfg.kv)
+    if cfg.kv == oracle.FP8:
+        return np.full(n, NAN_E4M3, np.uint8)
+    return np.full(n // 2, NAN_BF16, np.uint16).view(np.uint8)
 
 
 class OracleBackend:
     """Pools as numpy bytes, moved and read by the oracle."""
 
-    tol = 1e-9
-
-    def __init__(self):
-        n = oracle.layer_pool_bytes(NB, HKV, D, BS, oracle.BF16)
-        poison = np.full(n // 2, NAN_BF16, np.uint16).view(np.uint8)
-        self.k = [poison.copy() for _ in range(L)]
-        self.v = [poison.copy() for _ in range(L)]
+    def __init__(self, cfg):
+        self.c = cfg
+        self.tol = 1e-9
+        self.k = [poisoned_pool(cfg) for _ in range(L)]
+        self.v = [poisoned_pool(cfg) for _ in range(L)]
 
     def write(self, layer, kb, vb, slots):
+        c = self.c
         self.k[layer], self.v[layer] = oracle.reshape_and_cache(
-            kb, vb, oracle.BF16, self.k[layer], self.v[layer], np.asarray(slots, np.int64), BS, NB, oracle.BF16)
+            kb, vb, oracle.BF16, self.k[layer], self.v[layer], np.asarray(slots, np.int64), c.bs, NB, c.kv,
+            c.ks, c.vs)
 
     def copy_blocks(self, pairs):
-        moves = [(s * BS + r, d * BS + r) for s, d in pairs for r in range(BS)]
-        self.k, self.v = oracle.move_tokens(self.k, self.v, moves, HKV, D, BS, oracle.BF16)
+        bs = self.c.bs
+        moves = [(s * bs + r, d * bs + r) for s, d in pairs for r in range(bs)]
+        self.k, self.v = oracle.move_tokens(self.k, self.v, moves, HKV, D, bs, self.c.kv)
 
     def repack(self, tiles):
-        moves = [(src, blk * BS + r) for blk, srcs in tiles for r, src in enumerate(srcs)]
-        self.k, self.v = oracle.move_tokens(self.k, self.v, moves, HKV, D, BS, oracle.BF16)
+        bs = self.c.bs
+        moves = [(src, blk * bs + r) for blk, srcs in tiles for r, src in enumerate(srcs)]
+        self.k, self.v = oracle.move_tokens(self.k, self.v, moves, HKV, D, bs, self.c.kv)
 
     def decode(self, layer, q, tables, lens):
-        return oracle.paged_decode(q, oracle.BF16, self.k[layer], self.v[layer], oracle.BF16,
-                                   np.asarray(tables, np.int32), np.asarray(lens, np.int32), HKV, BS, SCALE)
+        c = self.c
+        return oracle.paged_decode(q, oracle.BF16, self.k[layer], self.v[layer], c.kv, np.asarray(tables, np.int32),
+                                   np.asarray(lens, np.int32), HKV, c.bs, SCALE, c.ks, c.vs)
 
     def decode_tokens(self, layer, q, table, lens):
-        return {"table": oracle.paged_decode_tokens(q, oracle.BF16, self.k[layer], self.v[layer], oracle.BF16,
+        c = self.c
+        return {"table": oracle.paged_decode_tokens(q, oracle.BF16, self.k[layer], self.v[layer], c.kv,
                                                     np.asarray(table, np.int32), np.asarray(lens, np.int32),
-                                                    HKV, BS, SCALE)}
+                                                    HKV, c.bs, SCALE, c.ks, c.vs)}
 
 
 class KernelBackend:
     """Pools on the GPU, moved and read by the library's kernels (every call
     through the C ABI; outputs start as NaN)."""
 
-    tol = 2e-2
-
-    def __init__(self, pkv, torch):
-        self.pkv, self.torch = pkv, torch
-        n = pkv.layer_pool_bytes(NB, HKV, D, BS, pkv.BF16)
-        mk = lambda: torch.full((n // 2,), NAN_BF16, dtype=torch.int16, device="cuda").view(torch.uint8)
-        self.k = [mk() for _ in range(L)]
-        self.v = [mk() for _ in range(L)]
+    def __init__(self, pkv, torch, cfg):
+        self.pkv, self.torch, self.c = pkv, torch, cfg
+        self.tol = 6e-2 if cfg.kv == oracle.FP8 else 2e-2
+        self.dt = pkv.FP8_E4M3 if cfg.kv == oracle.FP8 else pkv.BF16
+        self.k = [torch.from_numpy(poisoned_pool(cfg)).to("cuda") for _ in range(L)]
+        self.v = [torch.from_numpy(poisoned_pool(cfg)).to("cuda") for _ in range(L)]
 
     def _bf16(self, bits):
         t = self.torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
@@ -119,38 +155,39 @@ class KernelBackend:
         return out.float().cpu().numpy().astype(np.float64)
 
     def write(self, layer, kb, vb, slots):
+        c = self.c
         self.pkv.reshape_and_cache(self._bf16(kb), self._bf16(vb), self.k[layer], self.v[layer],
-                                   self._i32(slots), BS, NB, self.pkv.BF16)
+                                   self._i32(slots), c.bs, NB, self.dt, c.ks, c.vs)
 
     def copy_blocks(self, pairs):
-        self.pkv.copy_blocks(self.k, self.v, self._i32(pairs), NB, HKV, D, BS, self.pkv.BF16)
+        self.pkv.copy_blocks(self.k, self.v, self._i32(pairs), NB, HKV, D, self.c.bs, self.dt)
 
     def repack(self, tiles):
         flat = self._i32([[blk] + list(srcs) for blk, srcs in tiles])
-        self.pkv.repack_blocks(self.k, self.v, flat, self._i32([0, len(tiles)]), NB, HKV, D, BS, self.pkv.BF16)
+        self.pkv.repack_blocks(self.k, self.v, flat, self._i32([0, len(tiles)]), NB, HKV, D, self.c.bs, self.dt)
 
     def decode(self, layer, q, tables, lens):
+        c = self.c
         out = self._out(len(lens))
-        cl = self._i32(lens)
-        self.pkv.paged_attention_decode(out, self._bf16(q), self.k[layer], self.v[layer], self._i32(tables), cl,
-                                        int(max(lens)), HKV, BS, self.pkv.BF16, SCALE, num_blocks=NB,
-                                        partition_tokens=64)
+        self.pkv.paged_attention_decode(out, self._bf16(q), self.k[layer], self.v[layer], self._i32(tables),
+                                        self._i32(lens), int(max(lens)), HKV, c.bs, self.dt, SCALE, c.ks, c.vs,
+                                        num_blocks=NB, partition_tokens=4 * c.bs)
         return self._host(out)
 
     def decode_tokens(self, layer, q, table, lens):
-        pkv = self.pkv
+        pkv, c = self.pkv, self.c
         tt, cl, qt = self._i32(table), self._i32(lens), self._bf16(q)
         width = tt.shape[1]
         res = {}
         out = self._out(len(lens))
-        pkv.paged_attention_decode_tokens(out, qt, self.k[layer], self.v[layer], tt, cl, HKV, BS, NB, pkv.BF16,
-                                          SCALE)
+        pkv.paged_attention_decode_tokens(out, qt, self.k[layer], self.v[layer], tt, cl, HKV, c.bs, NB, self.dt,
+                                          SCALE, c.ks, c.vs)
         res["gather"] = self._host(out)
         for min_keys in (0, pkv.RUNS_MIN_KEYS):
-            runs = pkv.token_runs(tt, cl, BS, NB, min_keys_per_entry=min_keys)
+            runs = pkv.token_runs(tt, cl, c.bs, NB, min_keys_per_entry=min_keys)
             out = self._out(len(lens))
-            pkv.paged_attention_decode_runs(out, qt, self.k[layer], self.v[layer], runs, width, HKV, BS, NB,
-                                            pkv.BF16, SCALE, token_slots=tt, context_lens=cl)
+            pkv.paged_attention_decode_runs(out, qt, self.k[layer], self.v[layer], runs, width, HKV, c.bs, NB,
+                                            self.dt, SCALE, c.ks, c.vs, token_slots=tt, context_lens=cl)
             res[f"runs (min keys {min_keys})"] = self._host(out)
         return res
 
@@ -167,10 +204,11 @@ def check(got, q, seqs, sids, layer, tol, label):
         assert err <= tol, f"{label} layer {layer}: sequence {sid} ({len(kv)} tokens) max-abs {err}"
 
 
-def run_trace(seed, pkv, dev, num_ops=70, log=print):
+def run_trace(seed, pkv, dev, cfg, num_ops=70, log=print):
     """Drive num_ops random requests; returns counts of what ran."""
     r = np.random.default_rng(seed)
-    truth = Truth()
+    truth = Truth(cfg)
+    BS = cfg.bs
     bm = pkv.BlockManager(NB, BS, prefix_caching=True)
     seqs = {}                 # sid -> {"keys": chained key per token, "kv": Truth.kv per token, "evicted"}
     prompts = []              # prompts seen so far (prefix sources)
@@ -286,5 +324,5 @@ def run_trace(seed, pkv, dev, num_ops=70, log=print):
             stats["repacked_tiles"] += len(tiles)
             decode_all([sid], f"op {op_i} after repack")
             stats["evictions"] += 1
-    log(f"seed {seed}: {stats}")
+    log(f"seed {seed} {cfg}: {stats}")
     return stats
