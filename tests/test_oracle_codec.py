@@ -82,7 +82,8 @@ def test_e4m3_encode_matches_torch_on_all_bf16(scale):
     x = (bits << 16).view(np.float32)
     x = x[np.isfinite(x)]
     inv = np.float32(1.0) / np.float32(scale)
-    xs = (x * inv).astype(np.float32)
+    with np.errstate(over="ignore"):                 # large inputs overflow to inf, dropped next
+        xs = (x * inv).astype(np.float32)
     xs = xs[np.isfinite(xs)]
     assert np.array_equal(oracle.e4m3_encode(xs), _torch_e4m3(xs))
 
@@ -94,6 +95,7 @@ def test_e4m3_encode_matches_torch_random_fp32():
     assert np.array_equal(oracle.e4m3_encode(x), _torch_e4m3(x))
 
 
+@pytest.mark.filterwarnings("ignore:invalid value encountered:RuntimeWarning")   # the NaN codes
 def test_bf16_and_fp16_decode_exhaustive():
     bits = np.arange(65536, dtype=np.uint16)
     want16 = bits.view(np.float16).astype(np.float64)
