@@ -2,16 +2,20 @@
 
 The block manager (prefix cache on) serves a random mix of requests — new
 prompts, half of them sharing a prefix with an earlier prompt ("LLM
-inference basics and vLLM internals" §5: whole-block prefix hits), decode
-steps (appends, with copy-on-write after forks, §4), forks, frees, and token
-evictions followed by a repack (the "vToken" page).  A backend moves the
-data the manager's answers call for — it writes only the tokens a prompt did
-not hit, runs the copy-on-write copies before the step's writes, repacks
-evicted sequences — and attends.  After every decode step, and after each
-eviction and repack, every output is compared with contiguous textbook
-attention over that sequence's own K / V in logical order (oracle/brute.py),
-so tables, hits, copies, writes, repacks and the attention are checked
-together.
+inference basics and vLLM internals" §5: whole-block prefix hits), prefilled
+in random chunks (§6: chunked prefill; a block becomes a hit only once the
+chunk that fills it is marked computed, so later prompts, and prompts freed
+half-way, exercise that rule), decode steps (appends, with copy-on-write
+after forks, §4), forks, frees, and token evictions followed by a repack
+(the "vToken" page).  A backend moves the data the manager's answers call
+for — it writes only the tokens a prompt did not hit, runs the copy-on-write
+copies before the step's writes, repacks evicted sequences — and attends.
+Each chunk's tokens attend causally over everything written so far
+(multi-token attention); after every completed prompt, decode step,
+eviction and repack, every sequence's decode output is compared too, each
+against textbook attention over that sequence's own K / V in logical order
+(oracle/brute.py), so tables, hits, copies, writes, repacks and the
+attention are checked together.
 
 A token's K / V is a fixed function of the tokens up to it (a chained key
 seeds its values), so a prompt that hits cached blocks finds exactly the
@@ -122,6 +126,13 @@ class OracleBackend:
         return oracle.paged_decode(q, oracle.BF16, self.k[layer], self.v[layer], c.kv, np.asarray(tables, np.int32),
                                    np.asarray(lens, np.int32), HKV, c.bs, SCALE, c.ks, c.vs)
 
+    def prefill(self, layer, q, table, ctx):
+        c = self.c
+        n = q.shape[0]
+        return oracle.paged_prefill(q, oracle.BF16, self.k[layer], self.v[layer], c.kv, np.asarray([table], np.int32),
+                                    np.asarray([ctx], np.int32), np.asarray([0, n], np.int32), HKV, c.bs, SCALE,
+                                    c.ks, c.vs)
+
     def decode_tokens(self, layer, q, table, lens):
         c = self.c
         return {"table": oracle.paged_decode_tokens(q, oracle.BF16, self.k[layer], self.v[layer], c.kv,
@@ -174,6 +185,15 @@ class KernelBackend:
                                         num_blocks=NB, partition_tokens=4 * c.bs)
         return self._host(out)
 
+    def prefill(self, layer, q, table, ctx):
+        c = self.c
+        n = q.shape[0]
+        out = self.torch.full((n, H, D), float("nan"), dtype=self.torch.bfloat16, device="cuda")
+        self.pkv.paged_attention_prefill(out, self._bf16(q), self.k[layer], self.v[layer], self._i32([table]),
+                                         self._i32([ctx]), self._i32([0, n]), n, ctx, HKV, c.bs, self.dt, SCALE,
+                                         c.ks, c.vs, num_blocks=NB)
+        return self._host(out)
+
     def decode_tokens(self, layer, q, table, lens):
         pkv, c = self.pkv, self.c
         tt, cl, qt = self._i32(table), self._i32(lens), self._bf16(q)
@@ -210,10 +230,13 @@ def run_trace(seed, pkv, dev, cfg, num_ops=70, log=print):
     truth = Truth(cfg)
     BS = cfg.bs
     bm = pkv.BlockManager(NB, BS, prefix_caching=True)
-    seqs = {}                 # sid -> {"keys": chained key per token, "kv": Truth.kv per token, "evicted"}
+    # sid -> {"keys": chained key per token, "kv": Truth.kv per token,
+    #         "done": tokens whose K / V are written, "evicted"}
+    seqs = {}
     prompts = []              # prompts seen so far (prefix sources)
     next_sid = 0
-    stats = dict(prompts=0, hit_tokens=0, steps=0, cow=0, forks=0, frees=0, evictions=0, repacked_tiles=0)
+    stats = dict(prompts=0, hit_tokens=0, chunks=0, steps=0, cow=0, forks=0, frees=0, evictions=0,
+                 repacked_tiles=0, freed_mid_prefill=0)
 
     def write(triples):
         """(sid, position, slot) triples: their K / V into every layer."""
@@ -234,11 +257,36 @@ def run_trace(seed, pkv, dev, cfg, num_ops=70, log=print):
             q = workloads.normal_bits(r, (len(sids), H, D), oracle.BF16)
             check(dev.decode(layer, q, tables, lens), q, seqs, sids, layer, dev.tol, label)
 
+    def prefill_chunk(sid, label):
+        """Write the next chunk of a prompt (the whole rest, or a random
+        part), attend with its tokens as queries over everything written so
+        far (multi-token causal attention), then mark it computed."""
+        s = seqs[sid]
+        p0, n_all = s["done"], len(s["kv"])
+        n = n_all - p0 if r.random() < 0.4 else int(r.integers(1, n_all - p0 + 1))
+        p1 = p0 + n
+        write([(sid, p0 + i, sl) for i, sl in enumerate(bm.slots(sid, p0, n))])
+        table = bm.block_table(sid, -(-n_all // BS))
+        for layer in range(L):
+            q = workloads.normal_bits(r, (n, H, D), oracle.BF16)
+            got = dev.prefill(layer, q, table, p1)
+            k = np.stack([t[2][layer] for t in s["kv"][:p1]])
+            v = np.stack([t[3][layer] for t in s["kv"][:p1]])
+            want = brute.causal_chunk(bf16_f64(q), k, v, SCALE)
+            err = float(np.abs(got - want).max())
+            assert err <= dev.tol, f"{label} layer {layer}: chunk {p0}..{p1} of sequence {sid} max-abs {err}"
+        bm.mark_computed(sid, p1)
+        s["done"] = p1
+        stats["chunks"] += 1
+        if p1 == n_all:
+            decode_all([sid], f"{label}, prompt complete")
+
     for op_i in range(num_ops):
         live = list(seqs)
-        growable = [s for s in live if not seqs[s]["evicted"]]
+        growable = [s for s in live if not seqs[s]["evicted"] and seqs[s]["done"] == len(seqs[s]["kv"])]
+        prefilling = [s for s in live if seqs[s]["done"] < len(seqs[s]["kv"])]
         u = r.random()
-        if u < 0.3 or not live:
+        if u < 0.25 or not live:
             if len(live) >= MAX_LIVE:
                 continue
             n = int(r.integers(20, 260))
@@ -256,13 +304,15 @@ def run_trace(seed, pkv, dev, cfg, num_ops=70, log=print):
             for t in toks:
                 key = chain(key, t)
                 keys.append(key)
-            seqs[sid] = {"keys": keys, "kv": [truth.kv(kk) for kk in keys], "evicted": False}
+            assert hit < len(toks)                 # the last token is always computed
+            seqs[sid] = {"keys": keys, "kv": [truth.kv(kk) for kk in keys], "done": hit, "evicted": False}
             prompts.append(toks)
-            write([(sid, hit + i, sl) for i, sl in enumerate(bm.slots(sid, hit, len(toks) - hit))])
-            bm.mark_computed(sid, len(toks))
-            decode_all([sid], f"op {op_i} prompt ({hit} of {len(toks)} tokens hit)")
             stats["prompts"] += 1
             stats["hit_tokens"] += hit
+            prefill_chunk(sid, f"op {op_i} prompt ({hit} of {len(toks)} tokens hit)")
+        elif u < 0.35 and prefilling:
+            sid = int(r.choice(prefilling))
+            prefill_chunk(sid, f"op {op_i} next chunk")
         elif u < 0.65 and growable:
             # one decode step for a random subset: copy-on-write copies, then
             # the new tokens' K / V, then attention
@@ -275,6 +325,7 @@ def run_trace(seed, pkv, dev, cfg, num_ops=70, log=print):
                 key = chain(s["keys"][-1], tok)
                 s["keys"].append(key)
                 s["kv"].append(truth.kv(key))
+                s["done"] += 1                     # the step writes it
                 if src >= 0:
                     pairs.append((src, dst))
                 writes.append((sid, len(s["kv"]) - 1, slot))
@@ -290,11 +341,12 @@ def run_trace(seed, pkv, dev, cfg, num_ops=70, log=print):
             next_sid += 1
             bm.fork(parent, child)
             p = seqs[parent]
-            seqs[child] = {"keys": list(p["keys"]), "kv": list(p["kv"]), "evicted": False}
+            seqs[child] = {"keys": list(p["keys"]), "kv": list(p["kv"]), "done": p["done"], "evicted": False}
             stats["forks"] += 1
         elif u < 0.85 and live:
             sid = int(r.choice(live))
             bm.free_sequence(sid)
+            stats["freed_mid_prefill"] += sid in prefilling
             del seqs[sid]
             stats["frees"] += 1
         else:
@@ -311,6 +363,7 @@ def run_trace(seed, pkv, dev, cfg, num_ops=70, log=print):
             keep[-1] = True
             bm.evict_tokens(sid, keep)
             s["kv"] = [kv for kv, k in zip(s["kv"], keep) if k]
+            s["done"] = len(s["kv"])
             s["keys"] = [kk for kk, k in zip(s["keys"], keep) if k]
             m = len(s["kv"])
             table = [bm.token_slots(sid, m)]

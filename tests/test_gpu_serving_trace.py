@@ -1,7 +1,8 @@
 """GPU: random serving traces through the host block manager, the data moved
 and read by the library's kernels (reshape_and_cache, copy_blocks,
 repack_blocks, the block-table decode, the token-table gather and run-list
-decodes), every output checked against contiguous attention over each
+decodes, multi-token attention of each prefill chunk), every output checked
+against contiguous attention over each
 sequence's own K / V (the driver and its checks are in tests/serving_trace.py):
 bf16 pools of 16- and 32-token blocks, and fp8 pools written from bf16."""
 import pytest
