@@ -31,7 +31,7 @@ import oracle
 from oracle import brute
 import workloads
 
-D, HKV, H, L, NB = 128, 2, 8, 2, 700
+D, L, NB = 128, 2, 700
 SCALE = float(np.float32(1.0 / np.sqrt(D)))
 NAN_BF16 = 0x7FC0
 NAN_E4M3 = 0x7F
@@ -39,15 +39,16 @@ MAX_LIVE = 9
 
 
 class Cfg:
-    """Pool block size and kv dtype (bf16, or fp8 e4m3 written from bf16
-    with per-tensor scales); queries are bf16."""
+    """Pool block size, kv dtype (bf16, or fp8 e4m3 written from bf16 with
+    per-tensor scales) and head counts; queries are bf16."""
 
-    def __init__(self, block_size=16, kv_dtype=oracle.BF16, k_scale=1.0, v_scale=1.0):
+    def __init__(self, block_size=16, kv_dtype=oracle.BF16, k_scale=1.0, v_scale=1.0, heads=8, kv_heads=2):
         self.bs, self.kv = block_size, kv_dtype
         self.ks, self.vs = float(np.float32(k_scale)), float(np.float32(v_scale))
+        self.h, self.hkv = heads, kv_heads
 
     def __repr__(self):
-        return f"bs={self.bs} kv={'fp8' if self.kv == oracle.FP8 else 'bf16'}"
+        return f"bs={self.bs} kv={'fp8' if self.kv == oracle.FP8 else 'bf16'} heads={self.h}/{self.hkv}"
 
 
 def bf16_f64(bits):
@@ -82,15 +83,15 @@ class Truth:
     def kv(self, key):
         if key not in self.cache:
             r = np.random.default_rng(key)
-            kb = workloads.normal_bits(r, (L, HKV, D), oracle.BF16)
-            vb = workloads.normal_bits(r, (L, HKV, D), oracle.BF16)
+            kb = workloads.normal_bits(r, (L, self.cfg.hkv, D), oracle.BF16)
+            vb = workloads.normal_bits(r, (L, self.cfg.hkv, D), oracle.BF16)
             c = self.cfg
             self.cache[key] = (kb, vb, stored_values(kb, c.kv, c.ks), stored_values(vb, c.kv, c.vs))
         return self.cache[key]
 
 
 def poisoned_pool(cfg):
-    n = oracle.layer_pool_bytes(NB, HKV, D, cfg.bs, cfg.kv)
+    n = oracle.layer_pool_bytes(NB, cfg.hkv, D, cfg.bs, cfg.kv)
     if cfg.kv == oracle.FP8:
         return np.full(n, NAN_E4M3, np.uint8)
     return np.full(n // 2, NAN_BF16, np.uint16).view(np.uint8)
@@ -114,30 +115,30 @@ class OracleBackend:
     def copy_blocks(self, pairs):
         bs = self.c.bs
         moves = [(s * bs + r, d * bs + r) for s, d in pairs for r in range(bs)]
-        self.k, self.v = oracle.move_tokens(self.k, self.v, moves, HKV, D, bs, self.c.kv)
+        self.k, self.v = oracle.move_tokens(self.k, self.v, moves, self.c.hkv, D, bs, self.c.kv)
 
     def repack(self, tiles):
         bs = self.c.bs
         moves = [(src, blk * bs + r) for blk, srcs in tiles for r, src in enumerate(srcs)]
-        self.k, self.v = oracle.move_tokens(self.k, self.v, moves, HKV, D, bs, self.c.kv)
+        self.k, self.v = oracle.move_tokens(self.k, self.v, moves, self.c.hkv, D, bs, self.c.kv)
 
     def decode(self, layer, q, tables, lens):
         c = self.c
         return oracle.paged_decode(q, oracle.BF16, self.k[layer], self.v[layer], c.kv, np.asarray(tables, np.int32),
-                                   np.asarray(lens, np.int32), HKV, c.bs, SCALE, c.ks, c.vs)
+                                   np.asarray(lens, np.int32), self.c.hkv, c.bs, SCALE, c.ks, c.vs)
 
     def prefill(self, layer, q, table, ctx):
         c = self.c
         n = q.shape[0]
         return oracle.paged_prefill(q, oracle.BF16, self.k[layer], self.v[layer], c.kv, np.asarray([table], np.int32),
-                                    np.asarray([ctx], np.int32), np.asarray([0, n], np.int32), HKV, c.bs, SCALE,
-                                    c.ks, c.vs)
+                                    np.asarray([ctx], np.int32), np.asarray([0, n], np.int32), c.hkv, c.bs,
+                                    SCALE, c.ks, c.vs)
 
     def decode_tokens(self, layer, q, table, lens):
         c = self.c
         return {"table": oracle.paged_decode_tokens(q, oracle.BF16, self.k[layer], self.v[layer], c.kv,
                                                     np.asarray(table, np.int32), np.asarray(lens, np.int32),
-                                                    HKV, c.bs, SCALE, c.ks, c.vs)}
+                                                    self.c.hkv, c.bs, SCALE, c.ks, c.vs)}
 
 
 class KernelBackend:
@@ -159,7 +160,7 @@ class KernelBackend:
         return self.torch.tensor(np.asarray(a, np.int32), dtype=self.torch.int32, device="cuda")
 
     def _out(self, S):
-        return self.torch.full((S, H, D), float("nan"), dtype=self.torch.bfloat16, device="cuda")
+        return self.torch.full((S, self.c.h, D), float("nan"), dtype=self.torch.bfloat16, device="cuda")
 
     def _host(self, out):
         self.torch.cuda.synchronize()
@@ -171,27 +172,28 @@ class KernelBackend:
                                    self._i32(slots), c.bs, NB, self.dt, c.ks, c.vs)
 
     def copy_blocks(self, pairs):
-        self.pkv.copy_blocks(self.k, self.v, self._i32(pairs), NB, HKV, D, self.c.bs, self.dt)
+        self.pkv.copy_blocks(self.k, self.v, self._i32(pairs), NB, self.c.hkv, D, self.c.bs, self.dt)
 
     def repack(self, tiles):
         flat = self._i32([[blk] + list(srcs) for blk, srcs in tiles])
-        self.pkv.repack_blocks(self.k, self.v, flat, self._i32([0, len(tiles)]), NB, HKV, D, self.c.bs, self.dt)
+        self.pkv.repack_blocks(self.k, self.v, flat, self._i32([0, len(tiles)]), NB, self.c.hkv, D, self.c.bs,
+                               self.dt)
 
     def decode(self, layer, q, tables, lens):
         c = self.c
         out = self._out(len(lens))
         self.pkv.paged_attention_decode(out, self._bf16(q), self.k[layer], self.v[layer], self._i32(tables),
-                                        self._i32(lens), int(max(lens)), HKV, c.bs, self.dt, SCALE, c.ks, c.vs,
+                                        self._i32(lens), int(max(lens)), c.hkv, c.bs, self.dt, SCALE, c.ks, c.vs,
                                         num_blocks=NB, partition_tokens=4 * c.bs)
         return self._host(out)
 
     def prefill(self, layer, q, table, ctx):
         c = self.c
         n = q.shape[0]
-        out = self.torch.full((n, H, D), float("nan"), dtype=self.torch.bfloat16, device="cuda")
+        out = self.torch.full((n, self.c.h, D), float("nan"), dtype=self.torch.bfloat16, device="cuda")
         self.pkv.paged_attention_prefill(out, self._bf16(q), self.k[layer], self.v[layer], self._i32([table]),
-                                         self._i32([ctx]), self._i32([0, n]), n, ctx, HKV, c.bs, self.dt, SCALE,
-                                         c.ks, c.vs, num_blocks=NB)
+                                         self._i32([ctx]), self._i32([0, n]), n, ctx, c.hkv, c.bs, self.dt,
+                                         SCALE, c.ks, c.vs, num_blocks=NB)
         return self._host(out)
 
     def decode_tokens(self, layer, q, table, lens):
@@ -200,13 +202,13 @@ class KernelBackend:
         width = tt.shape[1]
         res = {}
         out = self._out(len(lens))
-        pkv.paged_attention_decode_tokens(out, qt, self.k[layer], self.v[layer], tt, cl, HKV, c.bs, NB, self.dt,
+        pkv.paged_attention_decode_tokens(out, qt, self.k[layer], self.v[layer], tt, cl, c.hkv, c.bs, NB, self.dt,
                                           SCALE, c.ks, c.vs)
         res["gather"] = self._host(out)
         for min_keys in (0, pkv.RUNS_MIN_KEYS):
             runs = pkv.token_runs(tt, cl, c.bs, NB, min_keys_per_entry=min_keys)
             out = self._out(len(lens))
-            pkv.paged_attention_decode_runs(out, qt, self.k[layer], self.v[layer], runs, width, HKV, c.bs, NB,
+            pkv.paged_attention_decode_runs(out, qt, self.k[layer], self.v[layer], runs, width, c.hkv, c.bs, NB,
                                             self.dt, SCALE, c.ks, c.vs, token_slots=tt, context_lens=cl)
             res[f"runs (min keys {min_keys})"] = self._host(out)
         return res
@@ -254,7 +256,7 @@ def run_trace(seed, pkv, dev, cfg, num_ops=70, log=print):
         lens = [bm.num_tokens(s) for s in sids]
         assert lens == [len(seqs[s]["kv"]) for s in sids]
         for layer in range(L):
-            q = workloads.normal_bits(r, (len(sids), H, D), oracle.BF16)
+            q = workloads.normal_bits(r, (len(sids), cfg.h, D), oracle.BF16)
             check(dev.decode(layer, q, tables, lens), q, seqs, sids, layer, dev.tol, label)
 
     def prefill_chunk(sid, label):
@@ -268,7 +270,7 @@ def run_trace(seed, pkv, dev, cfg, num_ops=70, log=print):
         write([(sid, p0 + i, sl) for i, sl in enumerate(bm.slots(sid, p0, n))])
         table = bm.block_table(sid, -(-n_all // BS))
         for layer in range(L):
-            q = workloads.normal_bits(r, (n, H, D), oracle.BF16)
+            q = workloads.normal_bits(r, (n, cfg.h, D), oracle.BF16)
             got = dev.prefill(layer, q, table, p1)
             k = np.stack([t[2][layer] for t in s["kv"][:p1]])
             v = np.stack([t[3][layer] for t in s["kv"][:p1]])
@@ -368,7 +370,7 @@ def run_trace(seed, pkv, dev, cfg, num_ops=70, log=print):
             m = len(s["kv"])
             table = [bm.token_slots(sid, m)]
             for layer in range(L):
-                q = workloads.normal_bits(r, (1, H, D), oracle.BF16)
+                q = workloads.normal_bits(r, (1, cfg.h, D), oracle.BF16)
                 for path, got in dev.decode_tokens(layer, q, table, [m]).items():
                     check(got, q, seqs, [sid], layer, dev.tol, f"op {op_i} evicted, {path}")
             tiles = bm.repack_tiles(sid)
